@@ -1,0 +1,174 @@
+"""CPU oracle for the depth-routing read of Attention Residuals (AttnRes), its
+multi-head form (MHAR) and its low-rank-key form (LR-AttnRes).
+
+TEST INFRASTRUCTURE ONLY.  This module is the slow, plain reference that the
+HIP kernels are checked against.  Only the tests, the smoke check and the
+benchmark's CPU-baseline leg may import it; the library never does.  It shares
+no code with the HIP path: its inputs come from the seeded generators in
+``synth`` and nothing else.
+
+Everything is NumPy in float64.  Inputs are the storage-rounded values
+(float32 or bfloat16 numbers) upcast exactly.  There is no online softmax, no
+caching, no blocking and no fusion: each function is the plain definition.
+
+What is computed, and where the pages define it
+------------------------------------------------
+"Multi-Head Attention Residuals", section 2.2 (Eq. 2) and section 2.3 (Eq. 3):
+at a routing site with learned static query q in R^d split into H contiguous
+heads of width d/H, head h scores every source s_i by q_h . RMSNorm(s_i)_[h],
+takes a softmax over the sources and mixes the h-th slice of the sources.
+H = 1 is single-head AttnRes (Eq. 2).
+
+"Low-Rank Attention Residuals", section 3.2-3.3 (Eq. 8-11): the key of a
+source is its last r coordinates, RMS-normalised over those r coordinates
+(slice first, then normalise; Eq. 13 "slice"), scored against q in R^r; the
+value is still the full d-wide source.  r = d is plain AttnRes.
+
+Backward: "Multi-Head Attention Residuals", Appendix E (backward paragraph and
+Figure 10) gives the closed form: with P_{n,h} = <dout_h, s_{n,h}>,
+S_h = sum_n w_{n,h} P_{n,h} and dl_{n,h} = w_{n,h} (P_{n,h} - S_h), the source
+gradient is r_n dk - (r_n^3 / d) <dk, s_n> s_n + w_n dout with dk = dl q and
+r_n the inverse RMS.  "Low-Rank Attention Residuals", Appendix B.3 (Lemma 2,
+Eq. 20; Corollary 2.1, Eq. 21) gives the same decomposition for sliced keys,
+with the norm taken over the r key coordinates.
+
+Readings where the pages are open (each also listed in the design doc):
+  R1  RMS over the full key width, then the per-head slice (Eq. 3 normalises
+      the whole source; the fused kernel of Appendix E takes mean(v*v) over
+      the row).  For LR keys the RMS is over the r key coordinates.
+  R2  eps = 1e-6 inside the square root: (mean(k^2) + eps)^(-1/2).
+  R3  No RMSNorm gain (LR pages: parameter-free norm).  A gain would fold
+      into q for the forward ("Low-Rank Attention Residuals", Eq. 17).
+  R5  LR with H > 1: q in R^r is split into H slices of width r/H; head h
+      scores the h-th slice of the normalised r-wide key and mixes the h-th
+      d/H slice of the value.  Requires H | r.  r = d gives MHAR.
+  R6  Sites read a growing prefix of the bank; the trivial one-source site
+      is included.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+EPS = 1e-6
+
+
+def key_slice(x: np.ndarray, r: int) -> np.ndarray:
+    """The routing key of a source: its last r coordinates ("Low-Rank Attention
+    Residuals", section 3.3, Eq. 11).  r == d gives the whole source."""
+    return x[..., x.shape[-1] - r:]
+
+
+def inv_rms(key: np.ndarray, eps: float = EPS) -> np.ndarray:
+    """(mean of key^2 over the last axis + eps)^(-1/2) (parameter-free RMSNorm,
+    "Low-Rank Attention Residuals", Eq. 13 slice form)."""
+    return 1.0 / np.sqrt(np.mean(key * key, axis=-1) + eps)
+
+
+def route_forward(sources, q, heads: int, r: int, eps: float = EPS):
+    """One routing read.
+
+    sources: [N, T, d]  (committed rows, then a transient source if any)
+    q:       [r]        static query of the site
+    Returns out [T, d], alpha [N, T, H], lse [T, H].
+    """
+    src = np.asarray(sources, dtype=np.float64)
+    q = np.asarray(q, dtype=np.float64)
+    N, T, d = src.shape
+    H = heads
+    kk, kv = r // H, d // H
+    key = key_slice(src, r)                                   # [N, T, r]
+    khat = key * inv_rms(key, eps)[..., None]                 # RMSNorm(key)
+    logits = np.einsum("nthk,hk->nth", khat.reshape(N, T, H, kk), q.reshape(H, kk))
+    m = logits.max(axis=0)
+    lse = m + np.log(np.exp(logits - m).sum(axis=0))
+    alpha = np.exp(logits - lse)                              # softmax over sources
+    out = np.einsum("nth,nthk->thk", alpha, src.reshape(N, T, H, kv)).reshape(T, d)
+    return out, alpha, lse
+
+
+def route_backward(sources, q, heads: int, r: int, dout, eps: float = EPS):
+    """Gradient of <dout, out> for one routing read.
+
+    Returns dsources [N, T, d] and dq [r].
+    """
+    src = np.asarray(sources, dtype=np.float64)
+    q = np.asarray(q, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    N, T, d = src.shape
+    H = heads
+    kk, kv = r // H, d // H
+    _, alpha, _ = route_forward(src, q, H, r, eps)
+    key = key_slice(src, r)
+    rinv = inv_rms(key, eps)                                  # [N, T]
+    khat = key * rinv[..., None]
+
+    # Softmax coupling: P, S and the logit gradient (Appendix E, Figure 10).
+    P = np.einsum("thk,nthk->nth", dout.reshape(T, H, kv), src.reshape(N, T, H, kv))
+    S = np.einsum("nth,nth->th", alpha, P)
+    dlogit = alpha * (P - S)
+
+    # Query gradient: logits are q_h . khat_[h].
+    dq = np.einsum("nth,nthk->hk", dlogit, khat.reshape(N, T, H, kk)).reshape(r)
+
+    # Key path through the RMSNorm (Eq. 21 / Appendix E closed form).
+    dkhat = (dlogit[..., None] * q.reshape(H, kk)).reshape(N, T, r)
+    proj = np.einsum("ntj,ntj->nt", dkhat, key)
+    dkey = rinv[..., None] * dkhat - (rinv ** 3 / r)[..., None] * proj[..., None] * key
+
+    # Value path: w_{n,h} dout_h on the h-th slice.
+    dsrc = (alpha[..., None] * dout.reshape(T, H, kv)).reshape(N, T, d)
+    dsrc[..., d - r:] += dkey
+    return dsrc, dq
+
+
+def run_schedule(rows, extras, queries, douts, nsrc, heads: int, r: int, eps: float = EPS):
+    """Forward every site in order, then backward every site in reverse.
+
+    rows:    [R, T, d]   committed bank rows
+    extras:  list of length S; None or [T, d] transient source of that site
+    queries: [S, r]
+    douts:   [S, T, d]   upstream gradient of each site's output
+    nsrc:    S ints; site s reads rows [0, nsrc[s]) (then its extra, if any)
+
+    The loss whose gradients are returned is sum_s <dout_s, out_s>, with every
+    bank row, query and transient source an independent input.
+    Returns a dict: out [S,T,d], alpha (list of [N_s,T,H]), lse [S,T,H],
+    dbank [R,T,d], dq [S,r], dextra (list of None or [T,d]).
+    """
+    rows = np.asarray(rows, dtype=np.float64)
+    R, T, d = rows.shape
+    S = len(nsrc)
+    outs, alphas, lses = [], [], []
+    for s in range(S):
+        src = _site_sources(rows, extras[s], nsrc[s])
+        o, a, l = route_forward(src, queries[s], heads, r, eps)
+        outs.append(o)
+        alphas.append(a)
+        lses.append(l)
+
+    dbank = np.zeros_like(rows)
+    dq = np.zeros((S, r))
+    dextra = [None] * S
+    for s in reversed(range(S)):
+        src = _site_sources(rows, extras[s], nsrc[s])
+        dsrc, dq[s] = route_backward(src, queries[s], heads, r, douts[s], eps)
+        n = nsrc[s]
+        dbank[:n] += dsrc[:n]
+        if extras[s] is not None:
+            dextra[s] = dsrc[n]
+    return {
+        "out": np.stack(outs) if outs else np.zeros((0, T, d)),
+        "alpha": alphas,
+        "lse": np.stack(lses) if lses else np.zeros((0, T, heads)),
+        "dbank": dbank,
+        "dq": dq,
+        "dextra": dextra,
+    }
+
+
+def _site_sources(rows, extra, n):
+    src = rows[:n]
+    if extra is not None:
+        src = np.concatenate([src, np.asarray(extra, dtype=np.float64)[None]], axis=0)
+    return src

@@ -1,0 +1,94 @@
+"""Seeded random draws for a workload.
+
+Recipe (one numpy PCG64 stream per item, so any row, query or gradient can be
+regenerated on its own and in any order):
+
+  root = SeedSequence(seed); groups = root.spawn(5), in this order:
+    0 scales   - one stream; c_n ~ U(0.5, 2) per bank row (all 1 if the
+                 workload has no per-source scale)
+    1 rows     - spawn(rows): bank row n = c_n * Z, Z ~ N(0, 1), shape [T, d]
+    2 extras   - spawn(sites): transient source of site s ~ N(0, 1), [T, d]
+    3 queries  - spawn(sites): q_s ~ N(0, 0.02^2), shape [r]
+    4 douts    - spawn(sites): upstream gradient of site s ~ N(0, 1), [T, d]
+
+Values are drawn in float32 and then rounded to the storage dtype (bf16 with
+round-to-nearest-even), so every consumer sees exactly the same numbers.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .workloads import Workload
+
+QUERY_STD = 0.02
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even); returns float32."""
+    return (bf16_bits(x).astype(np.uint32) << 16).view(np.float32)
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) of float32 values, round-to-nearest-even."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))
+    return ((b + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def sample_tokens(tokens: int, count: int, seed: int = 1234) -> np.ndarray:
+    """A sorted seeded token subset that always includes the first and last token."""
+    count = min(count, tokens)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    pick = set(rng.choice(tokens, size=count, replace=False).tolist())
+    pick.update({0, tokens - 1})
+    return np.array(sorted(pick), dtype=np.int64)
+
+
+class Inputs:
+    """Lazily drawn, storage-rounded inputs of one workload (float32 arrays)."""
+
+    def __init__(self, w: Workload):
+        self.w = w
+        root = np.random.SeedSequence(w.seed)
+        g_scale, g_rows, g_extra, g_query, g_dout = root.spawn(5)
+        self._scale_seed = g_scale
+        self._row_seeds = g_rows.spawn(max(w.rows, 1))
+        self._extra_seeds = g_extra.spawn(max(w.sites, 1))
+        self._query_seeds = g_query.spawn(max(w.sites, 1))
+        self._dout_seeds = g_dout.spawn(max(w.sites, 1))
+        rng = np.random.Generator(np.random.PCG64(self._scale_seed))
+        c = rng.uniform(0.5, 2.0, size=max(w.rows, 1))
+        self.scales = c if w.source_scale else np.ones_like(c)
+
+    def _round(self, x: np.ndarray) -> np.ndarray:
+        x = x.astype(np.float32, copy=False)
+        return bf16_round(x) if self.w.dtype == "bf16" else x
+
+    @staticmethod
+    def _normal(seed, shape) -> np.ndarray:
+        rng = np.random.Generator(np.random.PCG64(seed))
+        return rng.standard_normal(size=shape, dtype=np.float32)
+
+    def row(self, n: int) -> np.ndarray:
+        w = self.w
+        z = self._normal(self._row_seeds[n], (w.tokens, w.d))
+        z *= np.float32(self.scales[n])
+        return self._round(z)
+
+    def extra(self, s: int):
+        w = self.w
+        if not w.extra[s]:
+            return None
+        return self._round(self._normal(self._extra_seeds[s], (w.tokens, w.d)))
+
+    def query(self, s: int) -> np.ndarray:
+        q = self._normal(self._query_seeds[s], (self.w.r,)) * np.float32(QUERY_STD)
+        return self._round(q)
+
+    def dout(self, s: int) -> np.ndarray:
+        w = self.w
+        return self._round(self._normal(self._dout_seeds[s], (w.tokens, w.d)))
+
+    def queries(self) -> np.ndarray:
+        return np.stack([self.query(s) for s in range(self.w.sites)])

@@ -1,0 +1,365 @@
+"""Pins of the CPU oracle to facts fixed by the pages and by mathematics.
+
+Each test checks the oracle against something other than itself: hand-derived
+worked examples (tests/golden), an independently written single-head routine,
+closed-form special cases, invariances the pages state, and central finite
+differences of the forward.  A plausible mistake in the oracle (per-head
+instead of full-width RMS, a wrong softmax axis, first-r instead of last-r
+keys, a dropped key-path term, a missed accumulation across sites) fails at
+least one of them.
+"""
+
+import ast
+import json
+import math
+import operator
+import os
+
+import numpy as np
+import pytest
+
+from oracle import inv_rms, route_backward, route_forward, run_schedule
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
+
+
+# --------------------------------------------------------------------------
+# exact-expression reader for the golden fixture (numbers, + - * /, log, sqrt)
+_OPS = {ast.Add: operator.add, ast.Sub: operator.sub, ast.Mult: operator.mul,
+        ast.Div: operator.truediv, ast.USub: operator.neg, ast.UAdd: operator.pos}
+_FUNCS = {"log": math.log, "sqrt": math.sqrt}
+
+
+def _ev(node):
+    if isinstance(node, ast.Expression):
+        return _ev(node.body)
+    if isinstance(node, ast.Constant) and isinstance(node.value, (int, float)):
+        return float(node.value)
+    if isinstance(node, ast.BinOp) and type(node.op) in _OPS:
+        return _OPS[type(node.op)](_ev(node.left), _ev(node.right))
+    if isinstance(node, ast.UnaryOp) and type(node.op) in _OPS:
+        return _OPS[type(node.op)](_ev(node.operand))
+    if (isinstance(node, ast.Call) and isinstance(node.func, ast.Name)
+            and node.func.id in _FUNCS and len(node.args) == 1):
+        return _FUNCS[node.func.id](_ev(node.args[0]))
+    raise ValueError(f"unsupported expression node {ast.dump(node)}")
+
+
+def num(x):
+    if isinstance(x, list):
+        return np.array([num(v) for v in x], dtype=np.float64)
+    if isinstance(x, (int, float)):
+        return float(x)
+    return _ev(ast.parse(str(x), mode="eval"))
+
+
+def load_cases():
+    with open(GOLDEN) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", load_cases(), ids=lambda c: c["name"])
+def test_worked_example_exact(case):
+    src = num(case["sources"])[:, None, :]          # [N, T=1, d]
+    q = num(case["q"])
+    H, r = case["heads"], case["r"]
+    out, alpha, lse = route_forward(src, q, H, r, eps=0.0)
+    np.testing.assert_allclose(out[0], num(case["out"]), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(alpha[:, 0, :], num(case["alpha"]), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse[0], num(case["lse"]), rtol=0, atol=1e-13)
+    dsrc, dq = route_backward(src, q, H, r, num(case["dout"])[None, :], eps=0.0)
+    np.testing.assert_allclose(dq, num(case["dq"]), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dsrc[:, 0, :], num(case["dsources"]), rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("case", load_cases(), ids=lambda c: c["name"])
+def test_worked_example_default_eps_is_close(case):
+    # eps = 1e-6 rescales unit-RMS keys by (1 + 1e-6)^(-1/2): a ~1e-6 relative change.
+    src = num(case["sources"])[:, None, :]
+    q = num(case["q"])
+    out, alpha, _ = route_forward(src, q, case["heads"], case["r"])
+    np.testing.assert_allclose(out[0], num(case["out"]), rtol=0, atol=1e-5)
+    np.testing.assert_allclose(alpha[:, 0, :], num(case["alpha"]), rtol=0, atol=1e-5)
+
+
+# --------------------------------------------------------------------------
+# I1: H = 1 is single-head AttnRes (Eq. 2), written here independently with
+# scalar loops; LR keys follow "Low-Rank Attention Residuals" Eq. 8-11.
+def single_head_reference(sources, q, r, eps):
+    N, T, d = sources.shape
+    out = np.zeros((T, d))
+    alpha = np.zeros((N, T))
+    for t in range(T):
+        logits = []
+        for n in range(N):
+            key = [float(sources[n, t, j]) for j in range(d - r, d)]
+            rms = math.sqrt(sum(v * v for v in key) / r + eps)
+            logits.append(sum(float(q[j]) * key[j] / rms for j in range(r)))
+        top = max(logits)
+        ex = [math.exp(v - top) for v in logits]
+        z = sum(ex)
+        for n in range(N):
+            alpha[n, t] = ex[n] / z
+            for j in range(d):
+                out[t, j] += alpha[n, t] * float(sources[n, t, j])
+    return out, alpha
+
+
+@pytest.mark.parametrize("d,r", [(16, 16), (16, 6)])
+def test_single_head_matches_independent_eq2(d, r):
+    rng = np.random.default_rng(1)
+    src = rng.standard_normal((5, 7, d)) * rng.uniform(0.5, 2.0, (5, 1, 1))
+    q = rng.standard_normal(r) * 0.7
+    out, alpha, _ = route_forward(src, q, 1, r)
+    ref_out, ref_alpha = single_head_reference(src, q, r, 1e-6)
+    np.testing.assert_allclose(out, ref_out, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(alpha[:, :, 0], ref_alpha, rtol=0, atol=1e-14)
+
+
+def test_heads_are_independent_single_head_reads_with_shared_rms():
+    # Eq. 3: head h scores and mixes only the h-th slice, with the RMS taken
+    # over the whole key (reading R1).  With every source rescaled to a
+    # full-width RMS of 1 and eps = 0 the normalisation is the identity, so
+    # each head must be a plain softmax of q_h . s_[h] over the sources.
+    rng = np.random.default_rng(2)
+    N, T, d, H = 4, 3, 12, 3
+    src = rng.standard_normal((N, T, d))
+    src /= np.sqrt(np.mean(src ** 2, axis=-1, keepdims=True))
+    q = rng.standard_normal(d)
+    out, alpha, _ = route_forward(src, q, H, d, eps=0.0)
+    kv = d // H
+    for h in range(H):
+        sl = slice(h * kv, (h + 1) * kv)
+        logits = np.einsum("ntk,k->nt", src[:, :, sl], q[sl])
+        a = np.exp(logits - logits.max(0))
+        a /= a.sum(0)
+        np.testing.assert_allclose(alpha[:, :, h], a, rtol=0, atol=1e-14)
+        np.testing.assert_allclose(out[:, sl], np.einsum("nt,ntk->tk", a, src[:, :, sl]),
+                                   rtol=0, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+def test_zero_query_is_uniform_mean():
+    rng = np.random.default_rng(3)
+    src = rng.standard_normal((6, 5, 8))
+    out, alpha, lse = route_forward(src, np.zeros(8), 2, 8)
+    np.testing.assert_allclose(alpha, np.full_like(alpha, 1 / 6), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(out, src.mean(0), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, np.full_like(lse, math.log(6)), rtol=0, atol=1e-14)
+    neff = np.exp(-(alpha * np.log(alpha)).sum(0))  # "Low-Rank Attention Residuals" Eq. 14
+    np.testing.assert_allclose(neff, 6.0, rtol=1e-13)
+
+
+def test_one_source_is_identity():
+    rng = np.random.default_rng(4)
+    src = rng.standard_normal((1, 5, 8))
+    q = rng.standard_normal(8)
+    dout = rng.standard_normal((5, 8))
+    out, alpha, _ = route_forward(src, q, 4, 8)
+    np.testing.assert_array_equal(alpha, np.ones_like(alpha))
+    np.testing.assert_allclose(out, src[0], rtol=0, atol=1e-15)
+    dsrc, dq = route_backward(src, q, 4, 8, dout)
+    np.testing.assert_allclose(dsrc[0], dout, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(dq, 0.0, atol=1e-15)
+
+
+def test_alpha_is_a_distribution_over_sources():
+    rng = np.random.default_rng(5)
+    src = rng.standard_normal((9, 11, 24)) * 3
+    q = rng.standard_normal(24) * 2
+    _, alpha, lse = route_forward(src, q, 4, 24)
+    assert (alpha >= 0).all()
+    np.testing.assert_allclose(alpha.sum(0), 1.0, rtol=0, atol=1e-12)
+    # lse is the log-normaliser of the logits: alpha = exp(logit - lse)
+    assert np.isfinite(lse).all()
+
+
+def test_full_width_lr_equals_full_routing():
+    rng = np.random.default_rng(6)
+    src = rng.standard_normal((4, 3, 16))
+    q = rng.standard_normal(16)
+    a = route_forward(src, q, 2, 16)
+    b = route_forward(src.copy(), q.copy(), 2, 16)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+# --------------------------------------------------------------------------
+# I8: LR slice support ("Low-Rank Attention Residuals", Eq. 16, Corollary 2.1).
+def test_lr_slice_support():
+    rng = np.random.default_rng(7)
+    N, T, d, r, H = 4, 5, 16, 8, 2
+    src = rng.standard_normal((N, T, d))
+    q = rng.standard_normal(r)
+    dout = rng.standard_normal((T, d))
+    out, alpha, _ = route_forward(src, q, H, r)
+    dsrc, _ = route_backward(src, q, H, r, dout)
+    kv = d // H
+    # outside the key coordinates only the direct value gradient remains
+    for j in range(d - r):
+        h = j // kv
+        np.testing.assert_allclose(dsrc[:, :, j], alpha[:, :, h] * dout[None, :, j],
+                                   rtol=0, atol=1e-14)
+    # a perturbation outside the key leaves alpha unchanged and moves out by alpha*u
+    u = np.zeros((T, d))
+    u[:, : d - r] = rng.standard_normal((T, d - r))
+    src2 = src.copy()
+    src2[2] += u
+    out2, alpha2, _ = route_forward(src2, q, H, r)
+    np.testing.assert_allclose(alpha2, alpha, rtol=0, atol=1e-15)
+    shift = (alpha[2][:, :, None] * u.reshape(T, H, kv)).reshape(T, d)
+    np.testing.assert_allclose(out2 - out, shift, rtol=0, atol=1e-13)
+    # a perturbation inside the key does move alpha (keys are the last r)
+    src3 = src.copy()
+    src3[2, :, d - r:] += 1.0
+    _, alpha3, _ = route_forward(src3, q, H, r)
+    assert np.abs(alpha3 - alpha).max() > 1e-3
+
+
+# I9: rotation covariance ("Low-Rank Attention Residuals", Prop. 1, Eq. 18-19),
+# with a block-diagonal per-head rotation so that head slices are preserved.
+def test_headwise_rotation_covariance():
+    rng = np.random.default_rng(8)
+    N, T, d, H = 5, 4, 12, 3
+    kv = d // H
+    R = np.zeros((d, d))
+    for h in range(H):
+        Qm, _ = np.linalg.qr(rng.standard_normal((kv, kv)))
+        R[h * kv:(h + 1) * kv, h * kv:(h + 1) * kv] = Qm
+    src = rng.standard_normal((N, T, d))
+    q = rng.standard_normal(d)
+    dout = rng.standard_normal((T, d))
+    out, alpha, _ = route_forward(src, q, H, d)
+    outR, alphaR, _ = route_forward(src @ R.T, R @ q, H, d)
+    np.testing.assert_allclose(alphaR, alpha, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(outR, out @ R.T, rtol=0, atol=1e-12)
+    dsrc, dq = route_backward(src, q, H, d, dout)
+    dsrcR, dqR = route_backward(src @ R.T, R @ q, H, d, dout @ R.T)
+    np.testing.assert_allclose(dsrcR, dsrc @ R.T, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dqR, R @ dq, rtol=0, atol=1e-12)
+
+
+# I10: permuting the sources permutes alpha and gradients, leaves out unchanged.
+def test_source_permutation_equivariance():
+    rng = np.random.default_rng(9)
+    src = rng.standard_normal((6, 3, 8))
+    q = rng.standard_normal(8)
+    dout = rng.standard_normal((3, 8))
+    perm = np.array([3, 0, 5, 1, 4, 2])
+    out, alpha, lse = route_forward(src, q, 2, 8)
+    outP, alphaP, lseP = route_forward(src[perm], q, 2, 8)
+    np.testing.assert_allclose(outP, out, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(alphaP, alpha[perm], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lseP, lse, rtol=0, atol=1e-14)
+    dsrc, dq = route_backward(src, q, 2, 8, dout)
+    dsrcP, dqP = route_backward(src[perm], q, 2, 8, dout)
+    np.testing.assert_allclose(dsrcP, dsrc[perm], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(dqP, dq, rtol=0, atol=1e-14)
+
+
+# I11: RMS-normalised keys make alpha invariant to a per-source scale.
+def test_source_scale_invariance_of_alpha():
+    rng = np.random.default_rng(10)
+    src = rng.standard_normal((4, 3, 8))
+    q = rng.standard_normal(8)
+    _, alpha, _ = route_forward(src, q, 2, 8, eps=0.0)
+    scaled = src * np.array([0.5, 2.0, 7.0, 0.1])[:, None, None]
+    _, alpha2, _ = route_forward(scaled, q, 2, 8, eps=0.0)
+    np.testing.assert_allclose(alpha2, alpha, rtol=0, atol=1e-14)
+    _, alpha3, _ = route_forward(scaled, q, 2, 8)  # eps = 1e-6: O(eps / rms^2) change
+    np.testing.assert_allclose(alpha3, alpha, rtol=0, atol=1e-4)
+
+
+def test_zero_row_is_finite():
+    src = np.zeros((3, 2, 8))
+    src[1] = 1.0
+    q = np.arange(8.0)
+    out, alpha, _ = route_forward(src, q, 2, 8)
+    dsrc, dq = route_backward(src, q, 2, 8, np.ones((2, 8)))
+    for x in (out, alpha, dsrc, dq):
+        assert np.isfinite(x).all()
+    assert inv_rms(np.zeros(8)) == pytest.approx(1e3)
+
+
+# --------------------------------------------------------------------------
+# I6: the backward of the whole schedule equals central finite differences of
+# L = sum_s <dout_s, out_s>, for every bank element, query and transient source.
+def _schedule_loss(rows, extras, queries, douts, nsrc, H, r):
+    total = 0.0
+    for s in range(len(nsrc)):
+        src = rows[: nsrc[s]]
+        if extras[s] is not None:
+            src = np.concatenate([src, extras[s][None]], 0)
+        out, _, _ = route_forward(src, queries[s], H, r)
+        total += float(np.sum(douts[s] * out))
+    return total
+
+
+@pytest.mark.parametrize("kind", ["full", "lowrank_block"])
+def test_schedule_backward_matches_finite_differences(kind):
+    rng = np.random.default_rng(11)
+    T, d, H = 2, 8, 2
+    if kind == "full":
+        r, nsrc, has_extra = 8, [1, 2, 3], [0, 0, 0]
+    else:
+        r, nsrc, has_extra = 4, [1, 1, 2, 3], [1, 1, 1, 0]
+    R, S = max(nsrc), len(nsrc)
+    rows = rng.standard_normal((R, T, d)) * rng.uniform(0.5, 2.0, (R, 1, 1))
+    extras = [rng.standard_normal((T, d)) if e else None for e in has_extra]
+    queries = rng.standard_normal((S, r)) * 0.8
+    douts = rng.standard_normal((S, T, d))
+    res = run_schedule(rows, extras, queries, douts, nsrc, H, r)
+    h = 1e-6
+
+    def fd(arr, idx):
+        old = arr[idx]
+        arr[idx] = old + h
+        lp = _schedule_loss(rows, extras, queries, douts, nsrc, H, r)
+        arr[idx] = old - h
+        lm = _schedule_loss(rows, extras, queries, douts, nsrc, H, r)
+        arr[idx] = old
+        return (lp - lm) / (2 * h)
+
+    g = np.zeros_like(rows)
+    for idx in np.ndindex(rows.shape):
+        g[idx] = fd(rows, idx)
+    np.testing.assert_allclose(res["dbank"], g, rtol=1e-6, atol=1e-8)
+    gq = np.zeros_like(queries)
+    for idx in np.ndindex(queries.shape):
+        gq[idx] = fd(queries, idx)
+    np.testing.assert_allclose(res["dq"], gq, rtol=1e-6, atol=1e-8)
+    for s, e in enumerate(extras):
+        if e is None:
+            assert res["dextra"][s] is None
+            continue
+        ge = np.zeros_like(e)
+        for idx in np.ndindex(e.shape):
+            ge[idx] = fd(e, idx)
+        np.testing.assert_allclose(res["dextra"][s], ge, rtol=1e-6, atol=1e-8)
+
+
+def test_gradient_decomposition_value_plus_routing_feedback():
+    # "Low-Rank Attention Residuals" Eq. 15 / Lemma 2 (Eq. 20): for H = 1,
+    # grad_{o_i} = alpha_i g + alpha_i <g, o_i - h> grad z_i, with grad z_i
+    # the gradient of the score (Eq. 21 for sliced keys), evaluated by FD.
+    rng = np.random.default_rng(12)
+    N, d, r = 4, 10, 6
+    src = rng.standard_normal((N, 1, d))
+    q = rng.standard_normal(r)
+    g = rng.standard_normal((1, d))
+    out, alpha, _ = route_forward(src, q, 1, r)
+    dsrc, _ = route_backward(src, q, 1, r, g)
+
+    def score(x):
+        k = x[d - r:]
+        return float(q @ (k / math.sqrt(np.mean(k * k) + 1e-6)))
+
+    for i in range(N):
+        gz = np.zeros(d)
+        for j in range(d):
+            xp, xm = src[i, 0].copy(), src[i, 0].copy()
+            xp[j] += 1e-6
+            xm[j] -= 1e-6
+            gz[j] = (score(xp) - score(xm)) / 2e-6
+        expect = alpha[i, 0, 0] * g[0] + alpha[i, 0, 0] * float(g[0] @ (src[i, 0] - out[0])) * gz
+        np.testing.assert_allclose(dsrc[i, 0], expect, rtol=1e-6, atol=1e-8)
