@@ -1,0 +1,223 @@
+/*
+ * attnres.h - C ABI of libattnres: the depth-routing read of Attention
+ * Residuals (AttnRes), its multi-head form (MHAR) and its low-rank-key form
+ * (LR-AttnRes), forward and backward, on AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes
+ * -------------------------
+ * A bank holds committed sources s_0, s_1, ... (rows of T tokens x d values).
+ * A routing site with static query q (r values, split into H heads of r/H)
+ * reads the first N rows of the bank, plus optionally one transient source
+ * (e.g. the partial sum of the current block), and for every token and head h
+ *
+ *   key_n    = last r coordinates of s_n            (r == d: the whole source)
+ *   khat_n   = key_n * (mean(key_n^2) + eps)^(-1/2) (RMSNorm over the key, no gain)
+ *   l_{n,h}  = q_[h] . khat_n[h]                    (h-th r/H slice)
+ *   a_{.,h}  = softmax over the sources of l_{.,h}
+ *   out_[h]  = sum_n a_{n,h} s_n[h]                 (h-th d/H slice of the value)
+ *
+ * "Multi-Head Attention Residuals", section 2.3 (Eq. 3; H = 1 is Eq. 2 of
+ * section 2.2); "Low-Rank Attention Residuals", section 3.2-3.3 (Eq. 8-11).
+ * The backward gives, for the loss sum_sites <dout_site, out_site>, the
+ * gradient of every bank row (accumulated over all sites that read it), of
+ * every site query and of every transient source: "Multi-Head Attention
+ * Residuals" Appendix E (backward paragraph, Figure 10); "Low-Rank Attention
+ * Residuals" Appendix B.3 (Eq. 20-21).  Readings of open points: the RMS is
+ * over the whole key and then sliced per head; eps sits inside the square
+ * root; there is no norm gain; with r < d and H > 1 head h scores the h-th
+ * r/H slice of the normalised key and mixes the h-th d/H slice of the value.
+ *
+ * Ownership and memory
+ * --------------------
+ * Every tensor is device memory allocated and owned by the caller; the library
+ * allocates no device memory (rows, drows and dout_rows may be NULL when
+ * tokens == 0).  The handle is a small host object.  Layouts are
+ * row-major and contiguous; all device pointers must be 16-byte aligned.
+ *   rows       [max_rows,  T, d]  storage dtype  bank (row n = source n)
+ *   drows      [max_rows,  T, d]  float32        gradient of each bank row
+ *   dout_rows  [max_sites, T, d]  storage dtype  upstream gradient of each site
+ *   workspace  attnres_workspace_bytes(cfg) bytes: cached inverse RMS, cached
+ *              logits, saved softmax weights and log-sum-exp, backward
+ *              coefficients and query-gradient partials.
+ * The storage dtype (bank, queries, transient sources, dout, out) is bf16 or
+ * float32; all arithmetic is float32.
+ *
+ * Call order per microbatch (checked; a call out of order returns
+ * ATTNRES_ERR_ORDER and launches nothing)
+ * -----------------------------------------------------------------------
+ *   attnres_bank_reset
+ *   attnres_bank_set_queries            (the site schedule and its queries)
+ *   for each site s = 0..S-1:           append rows until nsrc[s] are committed,
+ *     attnres_bank_append ...           then
+ *     attnres_route_fwd(s)
+ *   for each site s = S-1..0:           strictly reverse order
+ *     attnres_route_bwd(s)
+ * After attnres_route_bwd(s) returns (in stream order) the gradient of every
+ * bank row first read by site s is final in drows: rows [nsrc[s-1], nsrc[s])
+ * (nsrc[-1] = 0).  Rows never read by any site are not written.
+ *
+ * All kernels are enqueued on the caller's stream and run asynchronously; a
+ * kernel fault is reported by the caller's next synchronisation.  Results are
+ * deterministic: no atomics, every reduction has a fixed order.  A handle is
+ * not thread-safe; distinct handles are independent.
+ *
+ * Errors: every call returns a status; ATTNRES_OK is 0.  On failure
+ * attnres_last_error() returns a message (thread-local, valid until the next
+ * call on the same thread).  Argument, shape and order checks happen before
+ * any kernel is enqueued, and a failed call leaves the handle unchanged.
+ */
+#ifndef ATTNRES_H
+#define ATTNRES_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct attnres_bank_s* attnres_bank_t;
+
+/* A hipStream_t (NULL = the default stream). */
+typedef void* attnres_stream_t;
+
+typedef enum {
+  ATTNRES_OK = 0,
+  ATTNRES_ERR_INVALID = 1,     /* null pointer, bad shape or value, misaligned pointer */
+  ATTNRES_ERR_CAPACITY = 2,    /* more rows or sites than configured, workspace too small */
+  ATTNRES_ERR_ORDER = 3,       /* call out of the documented order */
+  ATTNRES_ERR_UNSUPPORTED = 4, /* shape this build does not handle (see attnres_bank_create) */
+  ATTNRES_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed */
+} attnres_status_t;
+
+typedef enum { ATTNRES_F32 = 0, ATTNRES_BF16 = 1 } attnres_dtype_t;
+
+typedef struct {
+  int64_t tokens;    /* T: tokens per microbatch (batch x sequence, flattened), >= 0 */
+  int32_t d;         /* value width */
+  int32_t r;         /* key width: r == d for full-width keys, r < d keys on the last r coordinates */
+  int32_t heads;     /* H routing heads; H | d and H | r */
+  int32_t max_rows;  /* bank capacity in rows (committed sources) */
+  int32_t max_sites; /* routing sites per microbatch */
+  int32_t dtype;     /* attnres_dtype_t: storage dtype */
+  float eps;         /* RMSNorm epsilon, inside the square root (1e-6) */
+} attnres_config_t;
+
+/* Bytes of device workspace a bank with this configuration needs (0 if the
+ * configuration is invalid; see attnres_last_error). */
+size_t attnres_workspace_bytes(const attnres_config_t* cfg);
+
+/* Create a bank over caller-owned device buffers (layouts above).
+ * Shapes supported by this build: with c = 16 / sizeof(storage dtype)
+ * elements per 16-byte chunk, d, r, d/H and r/H must be multiples of c;
+ * otherwise ATTNRES_ERR_UNSUPPORTED.  H | d, H | r, 1 <= r <= d, heads >= 1,
+ * max_rows >= 1, max_sites >= 1, eps > 0, else ATTNRES_ERR_INVALID.
+ * workspace_bytes must be at least attnres_workspace_bytes(cfg). */
+attnres_status_t attnres_bank_create(const attnres_config_t* cfg, void* rows, float* drows,
+                                     void* dout_rows, void* workspace, size_t workspace_bytes,
+                                     attnres_bank_t* out);
+
+/* Start a new microbatch: no committed rows, no queries, no forward state. */
+attnres_status_t attnres_bank_reset(attnres_bank_t bank);
+
+/* Register the site schedule and the static queries of this microbatch
+ * (queries are input-independent, "Low-Rank Attention Residuals" section 3.4
+ * and section 4.8).  Must follow attnres_bank_reset / create, before the first
+ * append.
+ *   n_sites          1..max_sites
+ *   nsrc[n_sites]    host array: committed rows read by each site;
+ *                    1 <= nsrc[s] <= max_rows and non-decreasing in s
+ *   has_extra        host array [n_sites] of 0/1 (site reads one transient
+ *                    source), or NULL for none
+ *   queries          device [n_sites, r] storage dtype; must stay unchanged
+ *                    until the backward of site 0 has run
+ * Each later append scores its row against every registered query that will
+ * read it, so the route itself streams the bank only to mix it. */
+attnres_status_t attnres_bank_set_queries(attnres_bank_t bank, int32_t n_sites,
+                                          const int32_t* nsrc, const int32_t* has_extra,
+                                          const void* queries);
+
+/* Commit the next bank row n (returned in *row_out if not NULL) and cache its
+ * per-token inverse RMS over the key coordinates and its per-head logits
+ * ("key projections") against every registered query of a site that reads
+ * row n.  src: device [T, d] storage dtype copied into row n, or NULL when the
+ * caller already wrote row n of `rows`.  The shared bank is written once per
+ * source and read in place by every site ("Multi-Head Attention Residuals",
+ * Appendix E, shared source buffer). */
+attnres_status_t attnres_bank_append(attnres_bank_t bank, const void* src, attnres_stream_t stream,
+                                     int32_t* row_out);
+
+/* Forward of site `site` (sites in increasing order, all rows it reads
+ * committed).  extra: device [T, d] transient source when has_extra[site],
+ * else NULL; it must stay unchanged until the backward of this site.  Writes
+ * out [T, d] (storage dtype) and saves the softmax weights alpha
+ * [n, T, H] and log-sum-exp [T, H] (float32, n = nsrc[site] + has_extra[site],
+ * transient source last) in the workspace; see attnres_site_saved. */
+attnres_status_t attnres_route_fwd(attnres_bank_t bank, int32_t site, const void* extra, void* out,
+                                   attnres_stream_t stream);
+
+/* Backward of site `site`: sites in strictly decreasing order, after the
+ * forward of every registered site.
+ *   extra    the same pointer as passed to attnres_route_fwd for this site
+ *   dout     device [T, d] storage dtype gradient of this site's output,
+ *            copied into slot `site` of dout_rows; NULL if the caller already
+ *            wrote that slot.  Slots of later sites are read again here, so
+ *            they must be unchanged since their own backward.
+ *   dq       device float32 [r]: gradient of this site's query (overwritten)
+ *   d_extra  device float32 [T, d]: gradient of the transient source
+ *            (overwritten) when the site has one, else NULL
+ * Bank-row gradients are accumulated over all sites and written once per row
+ * into drows (see the call order above). */
+attnres_status_t attnres_route_bwd(attnres_bank_t bank, int32_t site, const void* extra,
+                                   const void* dout, float* dq, float* d_extra,
+                                   attnres_stream_t stream);
+
+/* Device pointers to what the forward of `site` saved: alpha [n, T, H] and
+ * lse [T, H] (float32), n = *n_src.  Valid after attnres_route_fwd(site) in
+ * stream order, until the next reset.  Any output pointer may be NULL. */
+attnres_status_t attnres_site_saved(attnres_bank_t bank, int32_t site, const float** alpha,
+                                    const float** lse, int32_t* n_src);
+
+/* Device pointer to the cached inverse RMS [T] (float32) of committed row n. */
+attnres_status_t attnres_row_rinv(attnres_bank_t bank, int32_t row, const float** rinv);
+
+/* Tiling the bank chose (for byte accounting and profiling): out[0..4] =
+ * tokens per tile and 16-byte chunks per thread of the forward / finalize
+ * kernels, the same two for the backward site pass, and the number of
+ * query-gradient partial rows the site pass writes. */
+attnres_status_t attnres_bank_tiling(attnres_bank_t bank, int32_t* out5);
+
+/* Kernel kinds reported by the launch trace. */
+typedef enum {
+  ATTNRES_KERNEL_SCORE = 0,     /* append (and transient-source) scoring */
+  ATTNRES_KERNEL_FWD = 1,       /* forward softmax + mix */
+  ATTNRES_KERNEL_BWD_SITE = 2,  /* backward site pass */
+  ATTNRES_KERNEL_DQ_REDUCE = 3, /* query-gradient reduction */
+  ATTNRES_KERNEL_FINALIZE = 4,  /* bank-row and transient-source gradients */
+  ATTNRES_KERNEL_KINDS = 5
+} attnres_kernel_t;
+
+/* Launch trace.  While enabled, every kernel the bank enqueues is bracketed by
+ * two HIP events recorded on the same stream (the events are created by the
+ * library and kept until destroy).  attnres_trace_read waits for the recorded
+ * events and writes, per kernel kind, the summed elapsed milliseconds
+ * (ms[ATTNRES_KERNEL_KINDS]) and launch counts (launches[...]), then clears
+ * the record.  Enabling or disabling also clears it.  Either output may be
+ * NULL. */
+attnres_status_t attnres_trace_enable(attnres_bank_t bank, int32_t enable);
+attnres_status_t attnres_trace_read(attnres_bank_t bank, double* ms, int64_t* launches);
+
+/* Message describing the last failed call on this thread ("" if none). */
+const char* attnres_last_error(void);
+
+/* Destroy the handle (the caller's buffers are untouched).  NULL is ignored. */
+void attnres_bank_destroy(attnres_bank_t bank);
+
+/* ABI version of this header: 1. */
+int32_t attnres_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTNRES_H */

@@ -70,25 +70,43 @@ class Inputs:
         rng = np.random.Generator(np.random.PCG64(seed))
         return rng.standard_normal(size=shape, dtype=np.float32)
 
-    def row(self, n: int) -> np.ndarray:
+    # unrounded float32 draws -------------------------------------------------
+    def _row_raw(self, n: int) -> np.ndarray:
         w = self.w
         z = self._normal(self._row_seeds[n], (w.tokens, w.d))
         z *= np.float32(self.scales[n])
-        return self._round(z)
+        return z
+
+    def _extra_raw(self, s: int) -> np.ndarray:
+        w = self.w
+        return self._normal(self._extra_seeds[s], (w.tokens, w.d))
+
+    def _query_raw(self, s: int) -> np.ndarray:
+        return self._normal(self._query_seeds[s], (self.w.r,)) * np.float32(QUERY_STD)
+
+    def _dout_raw(self, s: int) -> np.ndarray:
+        w = self.w
+        return self._normal(self._dout_seeds[s], (w.tokens, w.d))
+
+    # storage-rounded values as float32 -----------------------------------------
+    def row(self, n: int) -> np.ndarray:
+        return self._round(self._row_raw(n))
 
     def extra(self, s: int):
-        w = self.w
-        if not w.extra[s]:
+        if not self.w.extra[s]:
             return None
-        return self._round(self._normal(self._extra_seeds[s], (w.tokens, w.d)))
+        return self._round(self._extra_raw(s))
 
     def query(self, s: int) -> np.ndarray:
-        q = self._normal(self._query_seeds[s], (self.w.r,)) * np.float32(QUERY_STD)
-        return self._round(q)
+        return self._round(self._query_raw(s))
 
     def dout(self, s: int) -> np.ndarray:
-        w = self.w
-        return self._round(self._normal(self._dout_seeds[s], (w.tokens, w.d)))
+        return self._round(self._dout_raw(s))
+
+    # raw storage (bf16 bit patterns as uint16, or float32) for upload ----------
+    def storage(self, kind: str, i: int) -> np.ndarray:
+        x = getattr(self, f"_{kind}_raw")(i)
+        return bf16_bits(x) if self.w.dtype == "bf16" else x
 
     def queries(self) -> np.ndarray:
         return np.stack([self.query(s) for s in range(self.w.sites)])

@@ -1,0 +1,145 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header
+declares, and rejects bad arguments and out-of-order calls before it would
+enqueue any kernel (so these calls never touch a device)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from transformer_depth_wise_amd import attnres as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attnres.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(A.LIB_PATH):
+        from transformer_depth_wise_amd.build import build
+        build()
+    return A.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attnres_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declarations_are_exported(lib):
+    names = declared_functions()
+    assert len(names) == len(A.EXPORTS)
+    assert set(names) == set(A.EXPORTS)
+    for n in names:
+        assert getattr(lib, n) is not None
+    assert A.attnres_abi_version() == 1
+
+
+def cfg(**kw):
+    base = dict(tokens=256, d=1280, r=1280, heads=8, max_rows=73, max_sites=73,
+                dtype=A.ATTNRES_BF16, eps=1e-6)
+    base.update(kw)
+    return A.make_config(**base)
+
+
+FAKE = 0x10000  # aligned, never dereferenced by the checks below
+
+
+def fake_bank(c):
+    n = A.attnres_workspace_bytes(c)
+    return A.attnres_bank_create(c, FAKE, FAKE, FAKE, FAKE, n)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(heads=3), A.ATTNRES_ERR_INVALID),          # H must divide d
+    (dict(r=2000), A.ATTNRES_ERR_INVALID),           # r > d
+    (dict(d=1284, r=1284, heads=4), A.ATTNRES_ERR_UNSUPPORTED),  # not 16-byte chunks
+    (dict(heads=0), A.ATTNRES_ERR_INVALID),
+    (dict(dtype=7), A.ATTNRES_ERR_INVALID),
+    (dict(tokens=-1), A.ATTNRES_ERR_INVALID),
+    (dict(eps=0.0), A.ATTNRES_ERR_INVALID),
+    (dict(max_rows=0), A.ATTNRES_ERR_INVALID),
+])
+def test_bad_config_rejected(lib, kw, status):
+    c = cfg(**kw)
+    assert lib.attnres_workspace_bytes(ctypes.byref(c)) == 0
+    with pytest.raises(A.AttnResError) as e:
+        A.attnres_bank_create(c, FAKE, FAKE, FAKE, FAKE, 1 << 40)
+    assert e.value.status == status
+
+
+def test_workspace_size_and_capacity(lib):
+    c = cfg()
+    n = A.attnres_workspace_bytes(c)
+    # saved per-site slots: logits, alpha and P, [sites][rows+1][T][H] fp32
+    assert n >= 3 * 4 * 73 * 74 * 256 * 8
+    with pytest.raises(A.AttnResError) as e:
+        A.attnres_bank_create(c, FAKE, FAKE, FAKE, FAKE, n - 1)
+    assert e.value.status == A.ATTNRES_ERR_CAPACITY
+    with pytest.raises(A.AttnResError) as e:
+        A.attnres_bank_create(c, FAKE + 8, FAKE, FAKE, FAKE, n)
+    assert e.value.status == A.ATTNRES_ERR_INVALID
+
+
+def test_call_order_is_enforced(lib):
+    b = fake_bank(cfg())
+    try:
+        with pytest.raises(A.AttnResError) as e:
+            A.attnres_bank_append(b, None, stream=0)
+        assert e.value.status == A.ATTNRES_ERR_ORDER
+        with pytest.raises(A.AttnResError) as e:
+            A.attnres_route_fwd(b, 0, None, FAKE, stream=0)
+        assert e.value.status == A.ATTNRES_ERR_ORDER
+        # bad schedules
+        with pytest.raises(A.AttnResError) as e:
+            A.attnres_bank_set_queries(b, [2, 1], None, FAKE)
+        assert e.value.status == A.ATTNRES_ERR_INVALID
+        with pytest.raises(A.AttnResError) as e:
+            A.attnres_bank_set_queries(b, [1, 74], None, FAKE)
+        assert e.value.status == A.ATTNRES_ERR_CAPACITY
+        with pytest.raises(A.AttnResError) as e:
+            A.attnres_bank_set_queries(b, list(range(1, 75)), None, FAKE)
+        assert e.value.status == A.ATTNRES_ERR_CAPACITY
+        A.attnres_bank_set_queries(b, [1, 2, 3], None, FAKE)
+        with pytest.raises(A.AttnResError) as e:
+            A.attnres_bank_set_queries(b, [1, 2, 3], None, FAKE)
+        assert e.value.status == A.ATTNRES_ERR_ORDER
+        # forward of site 0 before its row is committed, or of site 1 first
+        with pytest.raises(A.AttnResError) as e:
+            A.attnres_route_fwd(b, 0, None, FAKE, stream=0)
+        assert e.value.status == A.ATTNRES_ERR_ORDER
+        with pytest.raises(A.AttnResError) as e:
+            A.attnres_route_fwd(b, 1, None, FAKE, stream=0)
+        assert e.value.status == A.ATTNRES_ERR_ORDER
+        # backward before every forward
+        with pytest.raises(A.AttnResError) as e:
+            A.attnres_route_bwd(b, 2, None, None, FAKE, None, stream=0)
+        assert e.value.status == A.ATTNRES_ERR_ORDER
+        # saved state of a site that has not run
+        with pytest.raises(A.AttnResError) as e:
+            A.attnres_site_saved(b, 0)
+        assert e.value.status == A.ATTNRES_ERR_ORDER
+        with pytest.raises(A.AttnResError) as e:
+            A.attnres_row_rinv(b, 0)
+        assert e.value.status == A.ATTNRES_ERR_INVALID
+        # reset clears the schedule: queries may be registered again
+        A.attnres_bank_reset(b)
+        A.attnres_bank_set_queries(b, [1, 1], [1, 1], FAKE)
+        with pytest.raises(A.AttnResError) as e:  # extra required by this schedule
+            A.attnres_route_fwd(b, 0, None, FAKE, stream=0)
+        assert e.value.status == A.ATTNRES_ERR_ORDER or e.value.status == A.ATTNRES_ERR_INVALID
+    finally:
+        A.attnres_bank_destroy(b)
+    assert A.last_error() != ""
+
+
+def test_misaligned_queries_rejected(lib):
+    b = fake_bank(cfg())
+    try:
+        with pytest.raises(A.AttnResError) as e:
+            A.attnres_bank_set_queries(b, [1], None, FAKE + 2)
+        assert e.value.status == A.ATTNRES_ERR_INVALID
+    finally:
+        A.attnres_bank_destroy(b)

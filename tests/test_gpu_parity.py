@@ -1,0 +1,119 @@
+"""HIP path vs the CPU oracle, element by element, on seeded inputs.
+
+Tolerances: max |x - x_ref| / max |x_ref| per tensor <= 1e-5 (fp32 storage)
+or 2e-2 (bf16 storage) for out, lse, bank gradients, query gradients and
+transient-source gradients; softmax weights within 1e-3 absolute.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import inv_rms, key_slice
+from synth import Inputs, get_workload, sample_tokens
+
+from gpu_harness import compare, log, max_rel, run_gpu, run_ref
+
+pytestmark = pytest.mark.gpu
+
+# Small token counts that the oracle finishes in seconds, each spanning
+# several tiles with a ragged tail (tile sizes: 64 / 16 / 8 / 8 / 2 tokens).
+REDUCED = ["tiny", "tiny@T37", "mhar100m@T200", "mhar350m@T100", "mhar1b@T77",
+           "lr_h1@T9", "lr_h8@T9"]
+
+
+@pytest.mark.parametrize("name", REDUCED)
+def test_schedule_matches_oracle(name):
+    w = get_workload(name)
+    inp = Inputs(w)
+    log(f"[parity] {w.describe()}")
+    got = run_gpu(w, inp)
+    ref = run_ref(w, inp)
+    compare(w, got, ref, label="full-schedule")
+    rinv_ref = np.stack([inv_rms(key_slice(inp.row(n).astype(np.float64), w.r), w.eps)
+                         for n in range(w.rows)])
+    assert max_rel(got["rinv"], rinv_ref) <= 1e-5
+
+
+@pytest.mark.parametrize("name", ["mhar100m", "mhar350m", "mhar1b", "lr_h1", "lr_h8"])
+def test_full_size_sampled_tokens(name):
+    """Full benchmark shapes: sampled tokens against the oracle; dq through a
+    second run whose upstream gradients are zero outside the sampled tokens."""
+    w = get_workload(name)
+    inp = Inputs(w)
+    toks = sample_tokens(w.tokens, 24)
+    log(f"[full-size] {w.describe()} sampled tokens={len(toks)}")
+    got = run_gpu(w, inp, tokens=toks)
+    ref = run_ref(w, inp, tokens=toks)
+    compare(w, got, ref, check_dq=False, label="sampled")
+    bank = got.pop("_bank")
+    log(f"[full-size] {name}: dq with upstream gradients masked to the sampled tokens")
+    got2 = run_gpu(w, inp, tokens=toks, dout_tokens=toks, bank=bank)
+    ref2 = run_ref(w, inp, tokens=toks, dout_tokens=toks)
+    err = max_rel(got2["dq"], ref2["dq"])
+    log(f"  dq (masked) max-rel={err:.3e}")
+    assert err <= 2e-2
+
+
+def test_deterministic_bitwise():
+    w = get_workload("mhar100m@T200")
+    inp = Inputs(w)
+    a = run_gpu(w, inp)
+    b = run_gpu(w, inp, bank=a["_bank"])
+    for k in ("out", "lse", "dbank", "dq"):
+        np.testing.assert_array_equal(a[k], b[k])
+    for x, y in zip(a["alpha"], b["alpha"]):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_one_source_site_is_identity():
+    w = get_workload("tiny").with_sites(1)
+    inp = Inputs(w)
+    got = run_gpu(w, inp)
+    np.testing.assert_array_equal(got["alpha"][0], 1.0)
+    np.testing.assert_allclose(got["out"][0], inp.row(0), rtol=0, atol=1e-6)
+    np.testing.assert_allclose(got["dbank"][0], inp.dout(0), rtol=0, atol=1e-6)
+    # dq = sum_t a (P - S) khat = 0 exactly; the kernel forms it as the
+    # difference of two fp32 sums of terms |P_t| * |khat_t|, so the residual is
+    # bounded by a few fp32 ulps of that scale.
+    x, g = inp.row(0).astype(np.float64), inp.dout(0).astype(np.float64)
+    khat = x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + w.eps)
+    scale = float(np.sum(np.abs(np.sum(g * x, axis=1)) * np.abs(khat).max(axis=1)))
+    assert np.abs(got["dq"]).max() <= 1e-6 * scale
+
+
+def test_single_token_and_empty():
+    w = get_workload("mhar1b").with_tokens(1).with_sites(4)
+    inp = Inputs(w)
+    compare(w, run_gpu(w, inp), run_ref(w, inp), label="T=1")
+    w0 = get_workload("tiny").with_tokens(0)
+    got = run_gpu(w0, Inputs(w0))
+    assert got["out"].shape == (5, 0, 64)
+    np.testing.assert_array_equal(got["dq"], 0.0)
+
+
+def test_zero_row_and_query():
+    """A zero bank row (RMS = sqrt(eps)) and a zero query stay finite and exact."""
+    import torch
+    from transformer_depth_wise_amd.attnres import Bank
+    from transformer_depth_wise_amd.schedule import run_microbatch
+    from oracle import run_schedule
+    T, d, H = 24, 64, 4
+    rng = np.random.default_rng(5)
+    rows = rng.standard_normal((3, T, d)).astype(np.float32)
+    rows[1] = 0.0
+    q = (rng.standard_normal((3, d)) * 0.5).astype(np.float32)
+    q[2] = 0.0
+    douts = rng.standard_normal((3, T, d)).astype(np.float32)
+    bank = Bank(T, d, d, H, 3, 3, "f32")
+    bank.rows.copy_(torch.from_numpy(rows))
+    bank.dout_rows.copy_(torch.from_numpy(douts))
+    outs = torch.empty((3, T, d), device="cuda")
+    dqs = torch.empty((3, d), device="cuda")
+    run_microbatch(bank, [1, 2, 3], [0, 0, 0], torch.from_numpy(q).cuda(), outs, dqs)
+    torch.cuda.synchronize()
+    ref = run_schedule(rows.astype(np.float64), [None] * 3, q.astype(np.float64),
+                       douts.astype(np.float64), [1, 2, 3], H, d)
+    assert max_rel(outs.cpu().numpy(), ref["out"]) <= 1e-5
+    assert max_rel(bank.drows.cpu().numpy(), ref["dbank"]) <= 1e-5
+    assert max_rel(dqs.cpu().numpy(), ref["dq"]) <= 1e-5
+    np.testing.assert_allclose(bank.saved(2)[0].cpu().numpy(), 1.0 / 3.0, rtol=0, atol=1e-7)

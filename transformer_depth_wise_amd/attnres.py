@@ -1,0 +1,300 @@
+"""ctypes binding of libattnres (include/attnres.h).
+
+The functions below carry the C names and only marshal arguments: every step
+of the routing path runs in the library's HIP kernels.  ``Bank`` keeps the
+device buffers of one bank as torch tensors (torch is used for device memory
+and streams only).  Importing this module fails loudly when the library has
+not been built; there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_float, c_int32, c_int64, c_size_t, c_void_p
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattnres.so")
+
+ATTNRES_OK = 0
+ATTNRES_ERR_INVALID = 1
+ATTNRES_ERR_CAPACITY = 2
+ATTNRES_ERR_ORDER = 3
+ATTNRES_ERR_UNSUPPORTED = 4
+ATTNRES_ERR_HIP = 5
+ATTNRES_F32 = 0
+ATTNRES_BF16 = 1
+
+STATUS_NAMES = {0: "OK", 1: "ERR_INVALID", 2: "ERR_CAPACITY", 3: "ERR_ORDER",
+                4: "ERR_UNSUPPORTED", 5: "ERR_HIP"}
+
+# Every symbol the header declares, in header order.
+EXPORTS = (
+    "attnres_workspace_bytes",
+    "attnres_bank_create",
+    "attnres_bank_reset",
+    "attnres_bank_set_queries",
+    "attnres_bank_append",
+    "attnres_route_fwd",
+    "attnres_route_bwd",
+    "attnres_site_saved",
+    "attnres_row_rinv",
+    "attnres_bank_tiling",
+    "attnres_trace_enable",
+    "attnres_trace_read",
+    "attnres_last_error",
+    "attnres_bank_destroy",
+    "attnres_abi_version",
+)
+
+
+class Config(ctypes.Structure):
+    _fields_ = [
+        ("tokens", c_int64),
+        ("d", c_int32),
+        ("r", c_int32),
+        ("heads", c_int32),
+        ("max_rows", c_int32),
+        ("max_sites", c_int32),
+        ("dtype", c_int32),
+        ("eps", c_float),
+    ]
+
+
+class AttnResError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libattnres is not built ({path} missing); run "
+                          f"`python -m transformer_depth_wise_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, fp = c_void_p, c_int32, POINTER(c_float)
+    cfgp = POINTER(Config)
+    sig = {
+        "attnres_workspace_bytes": (c_size_t, [cfgp]),
+        "attnres_bank_create": (i32, [cfgp, vp, vp, vp, vp, c_size_t, POINTER(vp)]),
+        "attnres_bank_reset": (i32, [vp]),
+        "attnres_bank_set_queries": (i32, [vp, i32, POINTER(i32), POINTER(i32), vp]),
+        "attnres_bank_append": (i32, [vp, vp, vp, POINTER(i32)]),
+        "attnres_route_fwd": (i32, [vp, i32, vp, vp, vp]),
+        "attnres_route_bwd": (i32, [vp, i32, vp, vp, vp, vp, vp]),
+        "attnres_site_saved": (i32, [vp, i32, POINTER(vp), POINTER(vp), POINTER(i32)]),
+        "attnres_row_rinv": (i32, [vp, i32, POINTER(vp)]),
+        "attnres_bank_tiling": (i32, [vp, POINTER(i32)]),
+        "attnres_trace_enable": (i32, [vp, i32]),
+        "attnres_trace_read": (i32, [vp, POINTER(ctypes.c_double), POINTER(c_int64)]),
+        "attnres_last_error": (ctypes.c_char_p, []),
+        "attnres_bank_destroy": (None, [vp]),
+        "attnres_abi_version": (i32, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    del fp
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load_library().attnres_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != ATTNRES_OK:
+        raise AttnResError(status, last_error())
+
+
+def _ptr(x):
+    """Device address of a tensor (or an int / None) as a c_void_p."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return c_void_p(x)
+    return c_void_p(x.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+# ---------------------------------------------------------------------------
+# C-named wrappers (status -> exception)
+
+def make_config(tokens, d, r, heads, max_rows, max_sites, dtype, eps=1e-6) -> Config:
+    return Config(int(tokens), int(d), int(r), int(heads), int(max_rows), int(max_sites),
+                  int(dtype), float(eps))
+
+
+def attnres_workspace_bytes(cfg: Config) -> int:
+    n = load_library().attnres_workspace_bytes(ctypes.byref(cfg))
+    if n == 0:
+        raise AttnResError(ATTNRES_ERR_INVALID, last_error())
+    return int(n)
+
+
+def attnres_bank_create(cfg: Config, rows, drows, dout_rows, workspace, workspace_bytes: int):
+    h = c_void_p()
+    _check(load_library().attnres_bank_create(ctypes.byref(cfg), _ptr(rows), _ptr(drows),
+                                              _ptr(dout_rows), _ptr(workspace),
+                                              int(workspace_bytes), ctypes.byref(h)))
+    return h
+
+
+def attnres_bank_reset(bank) -> None:
+    _check(load_library().attnres_bank_reset(bank))
+
+
+def attnres_bank_set_queries(bank, nsrc, has_extra, queries) -> None:
+    n = len(nsrc)
+    ns = (c_int32 * n)(*[int(v) for v in nsrc])
+    he = (c_int32 * n)(*[int(v) for v in has_extra]) if has_extra is not None else None
+    _check(load_library().attnres_bank_set_queries(bank, n, ns, he, _ptr(queries)))
+
+
+def attnres_bank_append(bank, src=None, stream=None) -> int:
+    row = c_int32(-1)
+    _check(load_library().attnres_bank_append(bank, _ptr(src), _stream(stream), ctypes.byref(row)))
+    return row.value
+
+
+def attnres_route_fwd(bank, site: int, extra, out, stream=None) -> None:
+    _check(load_library().attnres_route_fwd(bank, int(site), _ptr(extra), _ptr(out), _stream(stream)))
+
+
+def attnres_route_bwd(bank, site: int, extra, dout, dq, d_extra=None, stream=None) -> None:
+    _check(load_library().attnres_route_bwd(bank, int(site), _ptr(extra), _ptr(dout), _ptr(dq),
+                                            _ptr(d_extra), _stream(stream)))
+
+
+def attnres_site_saved(bank, site: int):
+    a, l, n = c_void_p(), c_void_p(), c_int32()
+    _check(load_library().attnres_site_saved(bank, int(site), ctypes.byref(a), ctypes.byref(l),
+                                             ctypes.byref(n)))
+    return a.value, l.value, n.value
+
+
+def attnres_row_rinv(bank, row: int) -> int:
+    p = c_void_p()
+    _check(load_library().attnres_row_rinv(bank, int(row), ctypes.byref(p)))
+    return p.value
+
+
+def attnres_bank_tiling(bank):
+    out = (c_int32 * 5)()
+    _check(load_library().attnres_bank_tiling(bank, out))
+    keys = ("tile_tokens", "chunks_per_thread", "site_tile_tokens", "site_chunks_per_thread",
+            "dq_parts")
+    return dict(zip(keys, [int(v) for v in out]))
+
+
+KERNEL_KINDS = ("score", "fwd", "bwd_site", "dq_reduce", "finalize")
+
+
+def attnres_trace_enable(bank, enable: bool) -> None:
+    _check(load_library().attnres_trace_enable(bank, 1 if enable else 0))
+
+
+def attnres_trace_read(bank):
+    """{kernel kind: (total ms, launches)} of the launches traced since the last read."""
+    n = len(KERNEL_KINDS)
+    ms = (ctypes.c_double * n)()
+    cnt = (c_int64 * n)()
+    _check(load_library().attnres_trace_read(bank, ms, cnt))
+    return {k: (float(ms[i]), int(cnt[i])) for i, k in enumerate(KERNEL_KINDS)}
+
+
+def attnres_bank_destroy(bank) -> None:
+    load_library().attnres_bank_destroy(bank)
+
+
+def attnres_abi_version() -> int:
+    return int(load_library().attnres_abi_version())
+
+
+# ---------------------------------------------------------------------------
+class Bank:
+    """One bank with its caller-owned device buffers held as torch tensors."""
+
+    def __init__(self, tokens, d, r, heads, max_rows, max_sites, dtype="bf16", eps=1e-6,
+                 device="cuda"):
+        import torch
+        self.torch = torch
+        self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
+        self.cdtype = ATTNRES_BF16 if dtype == "bf16" else ATTNRES_F32
+        self.T, self.d, self.r, self.H = int(tokens), int(d), int(r), int(heads)
+        self.max_rows, self.max_sites = int(max_rows), int(max_sites)
+        self.cfg = make_config(tokens, d, r, heads, max_rows, max_sites, self.cdtype, eps)
+        self.ws_bytes = attnres_workspace_bytes(self.cfg)
+        self.rows = torch.empty((max_rows, self.T, d), dtype=self.tdtype, device=device)
+        self.drows = torch.empty((max_rows, self.T, d), dtype=torch.float32, device=device)
+        self.dout_rows = torch.empty((max_sites, self.T, d), dtype=self.tdtype, device=device)
+        self.workspace = torch.empty((self.ws_bytes,), dtype=torch.uint8, device=device)
+        self.handle = attnres_bank_create(self.cfg, self.rows, self.drows, self.dout_rows,
+                                          self.workspace, self.ws_bytes)
+
+    def close(self):
+        if getattr(self, "handle", None) is not None:
+            attnres_bank_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def reset(self):
+        attnres_bank_reset(self.handle)
+
+    def set_queries(self, nsrc, has_extra, queries):
+        self.nsrc = list(nsrc)
+        self.has_extra = list(has_extra) if has_extra is not None else [0] * len(nsrc)
+        self.queries = queries  # keep alive
+        attnres_bank_set_queries(self.handle, nsrc, has_extra, queries)
+
+    def append(self, src=None, stream=None) -> int:
+        return attnres_bank_append(self.handle, src, stream)
+
+    def route_fwd(self, site, extra, out, stream=None):
+        attnres_route_fwd(self.handle, site, extra, out, stream)
+
+    def route_bwd(self, site, extra, dout, dq, d_extra=None, stream=None):
+        attnres_route_bwd(self.handle, site, extra, dout, dq, d_extra, stream)
+
+    def _ws_view(self, ptr, count):
+        off = ptr - self.workspace.data_ptr()
+        assert 0 <= off and off + 4 * count <= self.ws_bytes
+        return self.workspace[off:off + 4 * count].view(self.torch.float32)
+
+    def saved(self, site):
+        """(alpha [n, T, H], lse [T, H]) float32 views of what the forward saved."""
+        a, l, n = attnres_site_saved(self.handle, site)
+        alpha = self._ws_view(a, n * self.T * self.H).view(n, self.T, self.H)
+        lse = self._ws_view(l, self.T * self.H).view(self.T, self.H)
+        return alpha, lse
+
+    def tiling(self):
+        return attnres_bank_tiling(self.handle)
+
+    def trace(self, enable: bool):
+        attnres_trace_enable(self.handle, enable)
+
+    def trace_read(self):
+        return attnres_trace_read(self.handle)
+
+    def rinv(self, row):
+        p = attnres_row_rinv(self.handle, row)
+        return self._ws_view(p, self.T)

@@ -1,0 +1,542 @@
+// Host side of libattnres: argument and order checks, workspace layout, and
+// the launch sequence of each call of the C ABI declared in include/attnres.h.
+
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/attnres.h"
+#include "attnres_internal.h"
+
+using attnres::FinalizeJob;
+using attnres::Geom;
+using attnres::SiteArrays;
+
+namespace {
+
+thread_local std::string g_error;
+
+attnres_status_t fail(attnres_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return st;
+}
+
+attnres_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(ATTNRES_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Layout {
+  size_t rinv, rinvx, logits, alpha, pcoef, ssum, lse, dqpart, total;
+  int64_t site_stride;  // floats
+};
+
+int dq_parts_cap() { return 1024; }
+
+Layout make_layout(const attnres_config_t& c) {
+  Layout L{};
+  const size_t T = (size_t)c.tokens;
+  const size_t slot = ((size_t)c.max_rows + 1) * T * (size_t)c.heads;
+  size_t off = 0;
+  L.rinv = off;
+  off += align256(4 * (size_t)c.max_rows * T);
+  L.rinvx = off;
+  off += align256(4 * (size_t)c.max_sites * T);
+  L.logits = off;
+  off += align256(4 * slot * c.max_sites);
+  L.alpha = off;
+  off += align256(4 * slot * c.max_sites);
+  L.pcoef = off;
+  off += align256(4 * slot * c.max_sites);
+  L.ssum = off;
+  off += align256(4 * (size_t)c.max_sites * T * c.heads);
+  L.lse = off;
+  off += align256(4 * (size_t)c.max_sites * T * c.heads);
+  L.dqpart = off;
+  off += align256(4 * (size_t)dq_parts_cap() * c.r);
+  L.total = off;
+  L.site_stride = (int64_t)slot;
+  return L;
+}
+
+attnres_status_t check_config(const attnres_config_t* c) {
+  if (!c) return fail(ATTNRES_ERR_INVALID, "config is NULL");
+  if (c->tokens < 0) return fail(ATTNRES_ERR_INVALID, "tokens must be >= 0 (got %lld)", (long long)c->tokens);
+  if (c->dtype != ATTNRES_F32 && c->dtype != ATTNRES_BF16)
+    return fail(ATTNRES_ERR_INVALID, "dtype must be ATTNRES_F32 or ATTNRES_BF16 (got %d)", c->dtype);
+  if (c->heads < 1) return fail(ATTNRES_ERR_INVALID, "heads must be >= 1 (got %d)", c->heads);
+  if (c->d < 1 || c->r < 1 || c->r > c->d)
+    return fail(ATTNRES_ERR_INVALID, "need 1 <= r <= d (got d=%d r=%d)", c->d, c->r);
+  if (c->d % c->heads || c->r % c->heads)
+    return fail(ATTNRES_ERR_INVALID, "heads=%d must divide d=%d and r=%d", c->heads, c->d, c->r);
+  if (c->max_rows < 1 || c->max_sites < 1)
+    return fail(ATTNRES_ERR_INVALID, "max_rows and max_sites must be >= 1");
+  if (!(c->eps > 0.f)) return fail(ATTNRES_ERR_INVALID, "eps must be > 0");
+  const int pc = c->dtype == ATTNRES_F32 ? 4 : 8;
+  if (c->d % pc || c->r % pc || (c->d / c->heads) % pc || (c->r / c->heads) % pc)
+    return fail(ATTNRES_ERR_UNSUPPORTED,
+                "d, r, d/H and r/H must be multiples of %d elements (16-byte chunks); got d=%d r=%d H=%d",
+                pc, c->d, c->r, c->heads);
+  const int64_t T = c->tokens;
+  if (T > ((int64_t)1 << 31) / c->d)
+    return fail(ATTNRES_ERR_UNSUPPORTED, "tokens * d must stay below 2^31 per row");
+  return ATTNRES_OK;
+}
+
+// Tiling of the streaming kernels: `cpt` 16-byte chunks per thread, `tt`
+// tokens per tile, picked to waste the fewest thread slots (cpt from the
+// compiled set, tt * H <= threads so that one thread owns each (token, head)).
+Geom make_geom(const attnres_config_t& c, const int* cpts, int ncpts) {
+  Geom g{};
+  g.T = c.tokens;
+  g.d = c.d;
+  g.r = c.r;
+  g.H = c.heads;
+  g.kv = c.d / c.heads;
+  g.kk = c.r / c.heads;
+  g.pc = c.dtype == ATTNRES_F32 ? 4 : 8;
+  g.cpr = c.d / g.pc;
+  g.kvc = g.kv / g.pc;
+  g.kkc = g.kk / g.pc;
+  g.key_c0 = (c.d - c.r) / g.pc;
+  g.eps = c.eps;
+  double best = 2.0;
+  for (int i = 0; i < ncpts; ++i) {
+    const int cpt = cpts[i];
+    int tt = attnres::kThreads * cpt / g.cpr;
+    if (tt > 64) tt = 64;
+    if (tt * g.H > attnres::kThreads) tt = attnres::kThreads / g.H;
+    if (tt < 1) continue;
+    const double waste = 1.0 - (double)tt * g.cpr / ((double)attnres::kThreads * cpt);
+    if (waste < best - 1e-9) {
+      best = waste;
+      g.cpt = cpt;
+      g.tt = tt;
+    }
+  }
+  g.ntiles = g.tt > 0 ? (g.T + g.tt - 1) / g.tt : 0;
+  return g;
+}
+
+}  // namespace
+
+struct attnres_bank_s {
+  attnres_config_t cfg;
+  Geom g_main;  // forward and finalize
+  Geom g_site;  // backward site pass (fewer chunks per thread: more registers per chunk)
+  Layout lay;
+  char* rows;
+  float* drows;
+  char* dout_rows;
+  char* ws;
+  size_t esz;
+  // microbatch state
+  int n_sites;
+  std::vector<int> nsrc, has_extra;
+  const void* queries;
+  bool queries_set;
+  int rows_committed;
+  int fwd_next;
+  int bwd_next;  // next site to run backward; -1 before the backward phase
+  bool bwd_done;  // backward of site 0 has run: only reset is allowed
+  std::vector<const void*> extra_ptr;
+  // launch trace
+  struct TraceRec {
+    int kind;
+    hipEvent_t a, b;
+  };
+  bool trace_on;
+  std::vector<TraceRec> trace;
+  std::vector<hipEvent_t> event_pool;
+
+  float* f(size_t off) const { return reinterpret_cast<float*>(ws + off); }
+  char* row_ptr(int n) const { return rows + (size_t)n * cfg.tokens * cfg.d * esz; }
+  char* dout_ptr(int s) const { return dout_rows + (size_t)s * cfg.tokens * cfg.d * esz; }
+  float* rinv(int n) const { return f(lay.rinv) + (size_t)n * cfg.tokens; }
+  float* rinvx(int s) const { return f(lay.rinvx) + (size_t)s * cfg.tokens; }
+  float* site_logits(int s) const { return f(lay.logits) + (size_t)s * lay.site_stride; }
+  float* site_alpha(int s) const { return f(lay.alpha) + (size_t)s * lay.site_stride; }
+  float* site_pcoef(int s) const { return f(lay.pcoef) + (size_t)s * lay.site_stride; }
+  float* site_ssum(int s) const { return f(lay.ssum) + (size_t)s * cfg.tokens * cfg.heads; }
+  float* site_lse(int s) const { return f(lay.lse) + (size_t)s * cfg.tokens * cfg.heads; }
+
+  void clear_microbatch() {
+    n_sites = 0;
+    nsrc.clear();
+    has_extra.clear();
+    queries = nullptr;
+    queries_set = false;
+    rows_committed = 0;
+    fwd_next = 0;
+    bwd_next = -1;
+    bwd_done = false;
+    extra_ptr.clear();
+  }
+};
+
+namespace {
+
+hipEvent_t take_event(attnres_bank_s* b) {
+  if (!b->event_pool.empty()) {
+    hipEvent_t e = b->event_pool.back();
+    b->event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Brackets one kernel launch with events when the trace is on.
+struct TraceScope {
+  attnres_bank_s* b;
+  int kind;
+  hipStream_t st;
+  hipEvent_t a = nullptr;
+  TraceScope(attnres_bank_s* b_, int kind_, hipStream_t st_) : b(b_), kind(kind_), st(st_) {
+    if (b->trace_on && (a = take_event(b)) != nullptr && hipEventRecord(a, st) != hipSuccess) {
+      b->event_pool.push_back(a);
+      a = nullptr;
+    }
+  }
+  void done() {
+    if (!a) return;
+    hipEvent_t e = take_event(b);
+    if (e && hipEventRecord(e, st) == hipSuccess) {
+      b->trace.push_back({kind, a, e});
+    } else {
+      b->event_pool.push_back(a);
+      if (e) b->event_pool.push_back(e);
+    }
+    a = nullptr;
+  }
+};
+
+void trace_clear(attnres_bank_s* b) {
+  for (auto& r : b->trace) {
+    b->event_pool.push_back(r.a);
+    b->event_pool.push_back(r.b);
+  }
+  b->trace.clear();
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t attnres_abi_version(void) { return 1; }
+
+attnres_status_t attnres_trace_enable(attnres_bank_t b, int32_t enable) {
+  if (!b) return fail(ATTNRES_ERR_INVALID, "bank is NULL");
+  trace_clear(b);
+  b->trace_on = enable != 0;
+  return ATTNRES_OK;
+}
+
+attnres_status_t attnres_trace_read(attnres_bank_t b, double* ms, int64_t* launches) {
+  if (!b) return fail(ATTNRES_ERR_INVALID, "bank is NULL");
+  double tot[ATTNRES_KERNEL_KINDS] = {0};
+  int64_t cnt[ATTNRES_KERNEL_KINDS] = {0};
+  for (auto& r : b->trace) {
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e != hipSuccess) return hip_fail(e, "trace event wait");
+    float t = 0.f;
+    e = hipEventElapsedTime(&t, r.a, r.b);
+    if (e != hipSuccess) return hip_fail(e, "trace elapsed time");
+    tot[r.kind] += t;
+    cnt[r.kind] += 1;
+  }
+  trace_clear(b);
+  for (int k = 0; k < ATTNRES_KERNEL_KINDS; ++k) {
+    if (ms) ms[k] = tot[k];
+    if (launches) launches[k] = cnt[k];
+  }
+  return ATTNRES_OK;
+}
+
+const char* attnres_last_error(void) { return g_error.c_str(); }
+
+size_t attnres_workspace_bytes(const attnres_config_t* cfg) {
+  if (check_config(cfg) != ATTNRES_OK) return 0;
+  return make_layout(*cfg).total;
+}
+
+attnres_status_t attnres_bank_create(const attnres_config_t* cfg, void* rows, float* drows,
+                                     void* dout_rows, void* workspace, size_t workspace_bytes,
+                                     attnres_bank_t* out) {
+  attnres_status_t st = check_config(cfg);
+  if (st != ATTNRES_OK) return st;
+  if (!out) return fail(ATTNRES_ERR_INVALID, "out handle pointer is NULL");
+  if (!workspace || (cfg->tokens > 0 && (!rows || !drows || !dout_rows)))
+    return fail(ATTNRES_ERR_INVALID, "rows, drows, dout_rows and workspace must be non-NULL");
+  if (!aligned16(rows) || !aligned16(drows) || !aligned16(dout_rows) || !aligned16(workspace))
+    return fail(ATTNRES_ERR_INVALID, "device buffers must be 16-byte aligned");
+  const Layout lay = make_layout(*cfg);
+  if (workspace_bytes < lay.total)
+    return fail(ATTNRES_ERR_CAPACITY, "workspace has %zu bytes, needs %zu", workspace_bytes, lay.total);
+  static const int kMainCpts[] = {4, 5, 8, 7, 2};
+  static const int kSiteCpts[] = {4, 5, 2};
+  attnres_bank_s* b = new (std::nothrow) attnres_bank_s();
+  if (!b) return fail(ATTNRES_ERR_CAPACITY, "host allocation of the handle failed");
+  b->cfg = *cfg;
+  b->g_main = make_geom(*cfg, kMainCpts, 5);
+  b->g_site = make_geom(*cfg, kSiteCpts, 3);
+  if (b->g_main.tt < 1 || b->g_site.tt < 1) {
+    delete b;
+    return fail(ATTNRES_ERR_UNSUPPORTED, "row of %d chunks is too wide for one tile", cfg->d);
+  }
+  b->lay = lay;
+  b->rows = static_cast<char*>(rows);
+  b->drows = drows;
+  b->dout_rows = static_cast<char*>(dout_rows);
+  b->ws = static_cast<char*>(workspace);
+  b->esz = cfg->dtype == ATTNRES_F32 ? 4 : 2;
+  b->trace_on = false;
+  b->clear_microbatch();
+  *out = b;
+  return ATTNRES_OK;
+}
+
+void attnres_bank_destroy(attnres_bank_t bank) {
+  if (!bank) return;
+  trace_clear(bank);
+  for (hipEvent_t e : bank->event_pool) hipEventDestroy(e);
+  delete bank;
+}
+
+attnres_status_t attnres_bank_reset(attnres_bank_t b) {
+  if (!b) return fail(ATTNRES_ERR_INVALID, "bank is NULL");
+  b->clear_microbatch();
+  return ATTNRES_OK;
+}
+
+attnres_status_t attnres_bank_set_queries(attnres_bank_t b, int32_t n_sites, const int32_t* nsrc,
+                                          const int32_t* has_extra, const void* queries) {
+  if (!b) return fail(ATTNRES_ERR_INVALID, "bank is NULL");
+  if (b->queries_set || b->rows_committed > 0)
+    return fail(ATTNRES_ERR_ORDER, "set_queries must come right after reset (once per microbatch)");
+  if (n_sites < 1 || n_sites > b->cfg.max_sites)
+    return fail(ATTNRES_ERR_CAPACITY, "n_sites=%d outside [1, max_sites=%d]", n_sites, b->cfg.max_sites);
+  if (!nsrc || !queries) return fail(ATTNRES_ERR_INVALID, "nsrc and queries must be non-NULL");
+  if (!aligned16(queries)) return fail(ATTNRES_ERR_INVALID, "queries must be 16-byte aligned");
+  for (int s = 0; s < n_sites; ++s) {
+    if (nsrc[s] < 1 || nsrc[s] > b->cfg.max_rows)
+      return fail(ATTNRES_ERR_CAPACITY, "nsrc[%d]=%d outside [1, max_rows=%d]", s, nsrc[s], b->cfg.max_rows);
+    if (s > 0 && nsrc[s] < nsrc[s - 1])
+      return fail(ATTNRES_ERR_INVALID, "nsrc must be non-decreasing (nsrc[%d]=%d < nsrc[%d]=%d)", s,
+                  nsrc[s], s - 1, nsrc[s - 1]);
+    if (has_extra && has_extra[s] != 0 && has_extra[s] != 1)
+      return fail(ATTNRES_ERR_INVALID, "has_extra[%d] must be 0 or 1", s);
+  }
+  b->n_sites = n_sites;
+  b->nsrc.assign(nsrc, nsrc + n_sites);
+  b->has_extra.assign(n_sites, 0);
+  if (has_extra)
+    for (int s = 0; s < n_sites; ++s) b->has_extra[s] = has_extra[s];
+  b->queries = queries;
+  b->queries_set = true;
+  b->extra_ptr.assign(n_sites, nullptr);
+  return ATTNRES_OK;
+}
+
+attnres_status_t attnres_bank_append(attnres_bank_t b, const void* src, attnres_stream_t stream,
+                                     int32_t* row_out) {
+  if (!b) return fail(ATTNRES_ERR_INVALID, "bank is NULL");
+  if (!b->queries_set) return fail(ATTNRES_ERR_ORDER, "append before set_queries");
+  if (b->bwd_next >= 0 || b->bwd_done)
+    return fail(ATTNRES_ERR_ORDER, "append during or after the backward phase");
+  if (b->rows_committed >= b->cfg.max_rows)
+    return fail(ATTNRES_ERR_CAPACITY, "bank is full (max_rows=%d)", b->cfg.max_rows);
+  if (src && !aligned16(src)) return fail(ATTNRES_ERR_INVALID, "src must be 16-byte aligned");
+  const int n = b->rows_committed;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t bytes = (size_t)b->cfg.tokens * b->cfg.d * b->esz;
+  char* dst = b->row_ptr(n);
+  if (src && src != dst && bytes) {
+    hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st);
+    if (e != hipSuccess) return hip_fail(e, "append copy");
+  }
+  // Sites reading row n form the suffix of the schedule with nsrc > n.
+  int s_lo = 0;
+  while (s_lo < b->n_sites && b->nsrc[s_lo] <= n) ++s_lo;
+  TraceScope ts(b, ATTNRES_KERNEL_SCORE, st);
+  hipError_t e = attnres::launch_score(b->g_main, b->cfg.dtype, dst, b->queries, s_lo, b->n_sites, n,
+                                       b->rinv(n), b->f(b->lay.logits), b->lay.site_stride, st);
+  ts.done();
+  if (e != hipSuccess) return hip_fail(e, "append score kernel");
+  b->rows_committed = n + 1;
+  if (row_out) *row_out = n;
+  return ATTNRES_OK;
+}
+
+attnres_status_t attnres_route_fwd(attnres_bank_t b, int32_t site, const void* extra, void* out,
+                                   attnres_stream_t stream) {
+  if (!b) return fail(ATTNRES_ERR_INVALID, "bank is NULL");
+  if (!b->queries_set) return fail(ATTNRES_ERR_ORDER, "route_fwd before set_queries");
+  if (b->bwd_next >= 0 || b->bwd_done)
+    return fail(ATTNRES_ERR_ORDER, "route_fwd during or after the backward phase");
+  if (site != b->fwd_next)
+    return fail(ATTNRES_ERR_ORDER, "route_fwd(site=%d) out of order: next forward site is %d", site,
+                b->fwd_next);
+  if (site >= b->n_sites) return fail(ATTNRES_ERR_ORDER, "site %d is not registered", site);
+  const int n_rows = b->nsrc[site];
+  if (b->rows_committed < n_rows)
+    return fail(ATTNRES_ERR_ORDER, "site %d reads %d rows but only %d are committed", site, n_rows,
+                b->rows_committed);
+  // With no tokens every tensor is empty and may be NULL.
+  const bool empty = b->cfg.tokens == 0;
+  if (!empty && (extra != nullptr) != (b->has_extra[site] != 0))
+    return fail(ATTNRES_ERR_INVALID, "site %d: extra must be %s", site,
+                b->has_extra[site] ? "non-NULL" : "NULL");
+  if (!empty && !out) return fail(ATTNRES_ERR_INVALID, "out is NULL");
+  if (!aligned16(out) || (extra && !aligned16(extra)))
+    return fail(ATTNRES_ERR_INVALID, "out and extra must be 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (extra) {
+    TraceScope ts(b, ATTNRES_KERNEL_SCORE, st);
+    hipError_t e = attnres::launch_score(b->g_main, b->cfg.dtype, extra, b->queries, site, site + 1,
+                                         n_rows, b->rinvx(site), b->f(b->lay.logits),
+                                         b->lay.site_stride, st);
+    ts.done();
+    if (e != hipSuccess) return hip_fail(e, "route_fwd score kernel (transient source)");
+  }
+  const int64_t row_stride = b->cfg.tokens * (int64_t)b->cfg.d;
+  TraceScope ts(b, ATTNRES_KERNEL_FWD, st);
+  hipError_t e = attnres::launch_fwd(b->g_main, b->cfg.dtype, b->rows, row_stride, extra, n_rows,
+                                     b->site_logits(site), b->site_alpha(site), b->site_lse(site),
+                                     out, st);
+  ts.done();
+  if (e != hipSuccess) return hip_fail(e, "route_fwd kernel");
+  b->extra_ptr[site] = extra;
+  b->fwd_next = site + 1;
+  return ATTNRES_OK;
+}
+
+attnres_status_t attnres_route_bwd(attnres_bank_t b, int32_t site, const void* extra,
+                                   const void* dout, float* dq, float* d_extra,
+                                   attnres_stream_t stream) {
+  if (!b) return fail(ATTNRES_ERR_INVALID, "bank is NULL");
+  if (!b->queries_set || b->fwd_next != b->n_sites)
+    return fail(ATTNRES_ERR_ORDER, "route_bwd before the forward of every registered site");
+  if (b->bwd_done)
+    return fail(ATTNRES_ERR_ORDER, "backward phase already complete; reset for a new microbatch");
+  const int expect = b->bwd_next < 0 ? b->n_sites - 1 : b->bwd_next;
+  if (site != expect)
+    return fail(ATTNRES_ERR_ORDER, "route_bwd(site=%d) out of order: next backward site is %d", site,
+                expect);
+  if (extra != b->extra_ptr[site])
+    return fail(ATTNRES_ERR_ORDER, "site %d: extra differs from the pointer given to route_fwd", site);
+  if (!dq) return fail(ATTNRES_ERR_INVALID, "dq is NULL");
+  if (b->cfg.tokens > 0 && (d_extra != nullptr) != (b->has_extra[site] != 0))
+    return fail(ATTNRES_ERR_INVALID, "site %d: d_extra must be %s", site,
+                b->has_extra[site] ? "non-NULL" : "NULL");
+  if ((dout && !aligned16(dout)) || (d_extra && !aligned16(d_extra)) || !aligned16(dq))
+    return fail(ATTNRES_ERR_INVALID, "dout, dq and d_extra must be 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const attnres_config_t& c = b->cfg;
+  char* slot = b->dout_ptr(site);
+  const size_t bytes = (size_t)c.tokens * c.d * b->esz;
+  if (dout && dout != slot && bytes) {
+    hipError_t e = hipMemcpyAsync(slot, dout, bytes, hipMemcpyDeviceToDevice, st);
+    if (e != hipSuccess) return hip_fail(e, "route_bwd dout copy");
+  }
+  const int n_rows = b->nsrc[site];
+  const int64_t row_stride = c.tokens * (int64_t)c.d;
+  const int parts = attnres::bwd_site_parts(b->g_site);
+  {
+    TraceScope ts(b, ATTNRES_KERNEL_BWD_SITE, st);
+    hipError_t e = attnres::launch_bwd_site(
+        b->g_site, c.dtype, b->rows, row_stride, extra, n_rows, b->site_alpha(site), b->rinv(0),
+        extra ? b->rinvx(site) : nullptr, slot, b->site_pcoef(site), b->site_ssum(site),
+        b->f(b->lay.dqpart), parts, st);
+    ts.done();
+    if (e != hipSuccess) return hip_fail(e, "route_bwd site kernel");
+    // With no tokens there are no parts and the reduction writes zeros.
+    TraceScope tr(b, ATTNRES_KERNEL_DQ_REDUCE, st);
+    e = attnres::launch_dq_reduce(b->f(b->lay.dqpart), c.tokens > 0 ? parts : 0, c.r, dq, st);
+    tr.done();
+    if (e != hipSuccess) return hip_fail(e, "route_bwd dq reduction");
+  }
+  // Rows first read by this site are final once every later site has run.
+  std::vector<FinalizeJob> jobs;
+  const int lo = site > 0 ? b->nsrc[site - 1] : 0;
+  for (int n = lo; n < n_rows; ++n) {
+    FinalizeJob j{};
+    j.x = b->row_ptr(n);
+    j.rinv = b->rinv(n);
+    j.dst = b->drows + (size_t)n * c.tokens * c.d;
+    j.slot = n;
+    j.s0 = site;
+    j.s1 = b->n_sites;
+    jobs.push_back(j);
+  }
+  if (extra) {
+    FinalizeJob j{};
+    j.x = extra;
+    j.rinv = b->rinvx(site);
+    j.dst = d_extra;
+    j.slot = n_rows;
+    j.s0 = site;
+    j.s1 = site + 1;
+    jobs.push_back(j);
+  }
+  SiteArrays sa{};
+  sa.logits = b->f(b->lay.logits);
+  sa.alpha = b->f(b->lay.alpha);
+  sa.pcoef = b->f(b->lay.pcoef);
+  sa.ssum = b->f(b->lay.ssum);
+  sa.lse = b->f(b->lay.lse);
+  sa.site_stride = b->lay.site_stride;
+  sa.th_stride = c.tokens * (int64_t)c.heads;
+  TraceScope tf(b, ATTNRES_KERNEL_FINALIZE, st);
+  hipError_t e = attnres::launch_finalize(b->g_main, c.dtype, jobs.data(), (int)jobs.size(), sa,
+                                          b->dout_rows, row_stride, b->queries, st);
+  tf.done();
+  if (e != hipSuccess) return hip_fail(e, "route_bwd finalize kernel");
+  b->bwd_next = site - 1;
+  if (site == 0) b->bwd_done = true;
+  return ATTNRES_OK;
+}
+
+attnres_status_t attnres_site_saved(attnres_bank_t b, int32_t site, const float** alpha,
+                                    const float** lse, int32_t* n_src) {
+  if (!b) return fail(ATTNRES_ERR_INVALID, "bank is NULL");
+  if (!b->queries_set || site < 0 || site >= b->n_sites)
+    return fail(ATTNRES_ERR_INVALID, "site %d is not registered", site);
+  if (site >= b->fwd_next) return fail(ATTNRES_ERR_ORDER, "site %d has not run forward", site);
+  if (alpha) *alpha = b->site_alpha(site);
+  if (lse) *lse = b->site_lse(site);
+  if (n_src) *n_src = b->nsrc[site] + b->has_extra[site];
+  return ATTNRES_OK;
+}
+
+attnres_status_t attnres_bank_tiling(attnres_bank_t b, int32_t* out5) {
+  if (!b || !out5) return fail(ATTNRES_ERR_INVALID, "bank and out5 must be non-NULL");
+  out5[0] = b->g_main.tt;
+  out5[1] = b->g_main.cpt;
+  out5[2] = b->g_site.tt;
+  out5[3] = b->g_site.cpt;
+  out5[4] = attnres::bwd_site_parts(b->g_site);
+  return ATTNRES_OK;
+}
+
+attnres_status_t attnres_row_rinv(attnres_bank_t b, int32_t row, const float** rinv) {
+  if (!b) return fail(ATTNRES_ERR_INVALID, "bank is NULL");
+  if (row < 0 || row >= b->rows_committed)
+    return fail(ATTNRES_ERR_INVALID, "row %d is not committed", row);
+  if (rinv) *rinv = b->rinv(row);
+  return ATTNRES_OK;
+}
+
+}  // extern "C"
