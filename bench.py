@@ -31,13 +31,12 @@ HBM_PEAK_GBPS = 8000.0
 # ---------------------------------------------------------------------------
 # Algorithmic bytes per kernel launch (what each kernel must move in HBM).
 def kernel_bytes(w, parts: int):
-    """Total algorithmic bytes per kernel kind over one microbatch."""
+    """Total algorithmic bytes per kernel kind over one microbatch (see DESIGN.md)."""
     b, T, d, r, H, S = w.elem_bytes, w.tokens, w.d, w.r, w.heads, w.sites
     nsrc, extra = list(w.nsrc), list(w.extra)
     out = {"score": 0, "fwd": 0, "bwd_site": 0, "dq_reduce": 0, "finalize": 0}
     launches = {k: 0 for k in out}
-    rows = max(nsrc)
-    for n in range(rows):  # append of row n: key coords in, rinv + logits out
+    for n in range(max(nsrc)):  # append of row n: key coordinates in; rinv + projections out
         readers = sum(1 for s in range(S) if nsrc[s] > n)
         out["score"] += T * r * b + 4 * T + 4 * readers * T * H
         launches["score"] += 1
@@ -46,17 +45,19 @@ def kernel_bytes(w, parts: int):
         if extra[s]:
             out["score"] += T * r * b + 4 * T + 4 * T * H
             launches["score"] += 1
-        out["fwd"] += N * T * d * b + 8 * N * T * H + 4 * T * H + T * d * b
-        out["bwd_site"] += (N * T * d * b + T * d * b + 8 * N * T * H + 4 * N * T
-                            + 4 * T * H + 4 * parts * r)
+        # rows; projections + rinv in; alpha + lse + out written
+        out["fwd"] += N * T * d * b + 4 * N * T * H + 4 * N * T + 4 * N * T * H + 4 * T * H + T * d * b
+        # rows + dout; alpha, rinv, lse in; dl, radial, dq parts out
+        out["bwd_site"] += (N * T * d * b + T * d * b + 4 * N * T * H + 4 * N * T + 4 * T * H
+                            + 4 * N * T * H + 4 * N * T + 4 * parts * r)
         out["dq_reduce"] += 4 * parts * r + 4 * r
         launches["fwd"] += 1
         launches["bwd_site"] += 1
         launches["dq_reduce"] += 1
         lo = nsrc[s - 1] if s > 0 else 0
         jobs = [S - s] * (nsrc[s] - lo) + ([1] if extra[s] else [])
-        for ns in jobs:  # one source gathered from ns sites
-            out["finalize"] += ns * T * d * b + 16 * ns * T * H + T * r * b + 4 * T + 4 * T * d
+        for ns in jobs:  # one source gathered from ns sites: dout, alpha, dl, radial; key, rinv; grad
+            out["finalize"] += ns * T * d * b + 8 * ns * T * H + 4 * ns * T + T * r * b + 4 * T + 4 * T * d
         launches["finalize"] += 1
     return out, launches
 
@@ -103,6 +104,33 @@ def cpu_baseline(name: str, tokens: int, full_tokens: int):
                    f"{len(os.sched_getaffinity(0))} cores visible); measured {dt:.2f} s, "
                    f"scaled linearly in tokens"),
     }
+
+
+def bandwidth_probe(torch, gib: float = 2.0, reps: int = 10):
+    """Practical HBM ceiling: 16-byte-load read stream and copy over `gib` GiB."""
+    from transformer_depth_wise_amd.attnres import (attnres_probe_copy, attnres_probe_read,
+                                                    attnres_probe_sink_words)
+    n = int(gib * (1 << 30))
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(attnres_probe_sink_words(), dtype=torch.int32, device="cuda")
+    out = {}
+    for name, fn, nbytes in (("read", lambda: attnres_probe_read(src, n, sink), n),
+                             ("copy", lambda: attnres_probe_copy(src, dst, n), 2 * n)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[f"{name}_gbps"] = round(nbytes / ms / 1e6, 1)
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -165,6 +193,7 @@ def main():
     ms = ev0.elapsed_time(ev1) / args.steps
     print(f"[bench] {args.steps} steps: {ms:.3f} ms/microbatch", file=sys.stderr, flush=True)
 
+    result_probe = bandwidth_probe(torch)
     parts = bank.tiling()["dq_parts"]
     alg, launches = kernel_bytes(w, parts)
     total_bytes = sum(alg.values())
@@ -190,6 +219,7 @@ def main():
         "achieved_gbps": round(total_bytes / ms / 1e6, 1),
         "pct_of_peak": round(100.0 * total_bytes / ms / 1e6 / HBM_PEAK_GBPS, 1),
         "alg_bytes_per_microbatch": total_bytes,
+        "probe": result_probe,
     }
 
     if not args.no_trace:

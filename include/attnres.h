@@ -207,6 +207,19 @@ typedef enum {
 attnres_status_t attnres_trace_enable(attnres_bank_t bank, int32_t enable);
 attnres_status_t attnres_trace_read(attnres_bank_t bank, double* ms, int64_t* launches);
 
+/* Bandwidth probes giving the practical HBM ceiling with the same 16-byte
+ * vector loads as the routing kernels (grid-stride loops, whole 16-byte words
+ * only; a tail under 16 bytes is ignored).  Enqueued on `stream`.
+ *   attnres_probe_read   reads `bytes` of src; writes attnres_probe_sink_words()
+ *                        uint32 words to sink (device)
+ *   attnres_probe_copy   copies `bytes` from src to dst (non-overlapping)
+ * Pointers must be 16-byte aligned; ATTNRES_ERR_INVALID otherwise. */
+int32_t attnres_probe_sink_words(void);
+attnres_status_t attnres_probe_read(const void* src, size_t bytes, uint32_t* sink,
+                                    attnres_stream_t stream);
+attnres_status_t attnres_probe_copy(const void* src, void* dst, size_t bytes,
+                                    attnres_stream_t stream);
+
 /* Message describing the last failed call on this thread ("" if none). */
 const char* attnres_last_error(void);
 

@@ -21,9 +21,18 @@ REDUCED = ["tiny", "tiny@T37", "mhar100m@T200", "mhar350m@T100", "mhar1b@T77",
            "lr_h1@T9", "lr_h8@T9"]
 
 
-@pytest.mark.parametrize("name", REDUCED)
+def _workload(name):
+    if name == "bf16_kk24":
+        # r/H = 24 is not a multiple of 32: exercises the vector-ALU append
+        from synth import Workload, full_schedule
+        nsrc, extra = full_schedule(3)
+        return Workload("bf16_kk24", 50, 192, 8, 192, nsrc, extra, "bf16", True)
+    return get_workload(name)
+
+
+@pytest.mark.parametrize("name", REDUCED + ["bf16_kk24"])
 def test_schedule_matches_oracle(name):
-    w = get_workload(name)
+    w = _workload(name)
     inp = Inputs(w)
     log(f"[parity] {w.describe()}")
     got = run_gpu(w, inp)

@@ -41,6 +41,9 @@ EXPORTS = (
     "attnres_bank_tiling",
     "attnres_trace_enable",
     "attnres_trace_read",
+    "attnres_probe_sink_words",
+    "attnres_probe_read",
+    "attnres_probe_copy",
     "attnres_last_error",
     "attnres_bank_destroy",
     "attnres_abi_version",
@@ -92,6 +95,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "attnres_bank_tiling": (i32, [vp, POINTER(i32)]),
         "attnres_trace_enable": (i32, [vp, i32]),
         "attnres_trace_read": (i32, [vp, POINTER(ctypes.c_double), POINTER(c_int64)]),
+        "attnres_probe_sink_words": (i32, []),
+        "attnres_probe_read": (i32, [vp, c_size_t, vp, vp]),
+        "attnres_probe_copy": (i32, [vp, vp, c_size_t, vp]),
         "attnres_last_error": (ctypes.c_char_p, []),
         "attnres_bank_destroy": (None, [vp]),
         "attnres_abi_version": (i32, []),
@@ -214,6 +220,18 @@ def attnres_trace_read(bank):
     cnt = (c_int64 * n)()
     _check(load_library().attnres_trace_read(bank, ms, cnt))
     return {k: (float(ms[i]), int(cnt[i])) for i, k in enumerate(KERNEL_KINDS)}
+
+
+def attnres_probe_sink_words() -> int:
+    return int(load_library().attnres_probe_sink_words())
+
+
+def attnres_probe_read(src, nbytes: int, sink, stream=None) -> None:
+    _check(load_library().attnres_probe_read(_ptr(src), int(nbytes), _ptr(sink), _stream(stream)))
+
+
+def attnres_probe_copy(src, dst, nbytes: int, stream=None) -> None:
+    _check(load_library().attnres_probe_copy(_ptr(src), _ptr(dst), int(nbytes), _stream(stream)))
 
 
 def attnres_bank_destroy(bank) -> None:

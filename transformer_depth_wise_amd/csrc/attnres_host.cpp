@@ -38,35 +38,35 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Layout {
-  size_t rinv, rinvx, logits, alpha, pcoef, ssum, lse, dqpart, total;
-  int64_t site_stride;  // floats
+  size_t rinv, rinvx, proj, alpha, dl, radial, lse, dqpart, total;
+  int64_t site_stride;  // floats per site of proj / alpha / dl: (max_rows + 1) * T * H
+  int64_t rad_stride;   // floats per site of radial: (max_rows + 1) * T
 };
 
-int dq_parts_cap() { return 1024; }
+int dq_parts_cap() { return 512; }
 
 Layout make_layout(const attnres_config_t& c) {
   Layout L{};
   const size_t T = (size_t)c.tokens;
-  const size_t slot = ((size_t)c.max_rows + 1) * T * (size_t)c.heads;
+  const size_t srcs = (size_t)c.max_rows + 1;  // bank rows + one transient source
+  const size_t slot = srcs * T * (size_t)c.heads;
   size_t off = 0;
-  L.rinv = off;
-  off += align256(4 * (size_t)c.max_rows * T);
-  L.rinvx = off;
-  off += align256(4 * (size_t)c.max_sites * T);
-  L.logits = off;
-  off += align256(4 * slot * c.max_sites);
-  L.alpha = off;
-  off += align256(4 * slot * c.max_sites);
-  L.pcoef = off;
-  off += align256(4 * slot * c.max_sites);
-  L.ssum = off;
-  off += align256(4 * (size_t)c.max_sites * T * c.heads);
-  L.lse = off;
-  off += align256(4 * (size_t)c.max_sites * T * c.heads);
-  L.dqpart = off;
-  off += align256(4 * (size_t)dq_parts_cap() * c.r);
+  auto take = [&](size_t floats) {
+    const size_t at = off;
+    off += align256(4 * floats);
+    return at;
+  };
+  L.rinv = take((size_t)c.max_rows * T);
+  L.rinvx = take((size_t)c.max_sites * T);
+  L.proj = take(slot * c.max_sites);
+  L.alpha = take(slot * c.max_sites);
+  L.dl = take(slot * c.max_sites);
+  L.radial = take(srcs * T * c.max_sites);
+  L.lse = take((size_t)c.max_sites * T * c.heads);
+  L.dqpart = take((size_t)dq_parts_cap() * c.r);
   L.total = off;
   L.site_stride = (int64_t)slot;
+  L.rad_stride = (int64_t)(srcs * T);
   return L;
 }
 
@@ -126,6 +126,27 @@ Geom make_geom(const attnres_config_t& c, const int* cpts, int ncpts) {
     }
   }
   g.ntiles = g.tt > 0 ? (g.T + g.tt - 1) / g.tt : 0;
+  g.wave_tokens = 0;
+  return g;
+}
+
+// Backward site pass: prefer the layout in which every wave owns whole
+// tokens (tw tokens = 64 * cpt chunks, tw * H <= 64, 4 waves per tile);
+// otherwise the work-group-wide layout.
+Geom make_site_geom(const attnres_config_t& c) {
+  static const int kSiteCpts[] = {4, 5, 2};
+  Geom g = make_geom(c, kSiteCpts, 3);
+  for (int i = 0; i < 3; ++i) {
+    const int cpt = kSiteCpts[i];
+    if ((64 * cpt) % g.cpr != 0) continue;
+    const int tw = 64 * cpt / g.cpr;
+    if (tw < 1 || tw * g.H > 64) continue;
+    g.cpt = cpt;
+    g.wave_tokens = tw;
+    g.tt = 4 * tw;
+    g.ntiles = (g.T + g.tt - 1) / g.tt;
+    break;
+  }
   return g;
 }
 
@@ -165,10 +186,10 @@ struct attnres_bank_s {
   char* dout_ptr(int s) const { return dout_rows + (size_t)s * cfg.tokens * cfg.d * esz; }
   float* rinv(int n) const { return f(lay.rinv) + (size_t)n * cfg.tokens; }
   float* rinvx(int s) const { return f(lay.rinvx) + (size_t)s * cfg.tokens; }
-  float* site_logits(int s) const { return f(lay.logits) + (size_t)s * lay.site_stride; }
+  float* site_proj(int s) const { return f(lay.proj) + (size_t)s * lay.site_stride; }
   float* site_alpha(int s) const { return f(lay.alpha) + (size_t)s * lay.site_stride; }
-  float* site_pcoef(int s) const { return f(lay.pcoef) + (size_t)s * lay.site_stride; }
-  float* site_ssum(int s) const { return f(lay.ssum) + (size_t)s * cfg.tokens * cfg.heads; }
+  float* site_dl(int s) const { return f(lay.dl) + (size_t)s * lay.site_stride; }
+  float* site_radial(int s) const { return f(lay.radial) + (size_t)s * lay.rad_stride; }
   float* site_lse(int s) const { return f(lay.lse) + (size_t)s * cfg.tokens * cfg.heads; }
 
   void clear_microbatch() {
@@ -286,12 +307,11 @@ attnres_status_t attnres_bank_create(const attnres_config_t* cfg, void* rows, fl
   if (workspace_bytes < lay.total)
     return fail(ATTNRES_ERR_CAPACITY, "workspace has %zu bytes, needs %zu", workspace_bytes, lay.total);
   static const int kMainCpts[] = {4, 5, 8, 7, 2};
-  static const int kSiteCpts[] = {4, 5, 2};
   attnres_bank_s* b = new (std::nothrow) attnres_bank_s();
   if (!b) return fail(ATTNRES_ERR_CAPACITY, "host allocation of the handle failed");
   b->cfg = *cfg;
   b->g_main = make_geom(*cfg, kMainCpts, 5);
-  b->g_site = make_geom(*cfg, kSiteCpts, 3);
+  b->g_site = make_site_geom(*cfg);
   if (b->g_main.tt < 1 || b->g_site.tt < 1) {
     delete b;
     return fail(ATTNRES_ERR_UNSUPPORTED, "row of %d chunks is too wide for one tile", cfg->d);
@@ -372,7 +392,7 @@ attnres_status_t attnres_bank_append(attnres_bank_t b, const void* src, attnres_
   while (s_lo < b->n_sites && b->nsrc[s_lo] <= n) ++s_lo;
   TraceScope ts(b, ATTNRES_KERNEL_SCORE, st);
   hipError_t e = attnres::launch_score(b->g_main, b->cfg.dtype, dst, b->queries, s_lo, b->n_sites, n,
-                                       b->rinv(n), b->f(b->lay.logits), b->lay.site_stride, st);
+                                       b->rinv(n), b->f(b->lay.proj), b->lay.site_stride, st);
   ts.done();
   if (e != hipSuccess) return hip_fail(e, "append score kernel");
   b->rows_committed = n + 1;
@@ -406,7 +426,7 @@ attnres_status_t attnres_route_fwd(attnres_bank_t b, int32_t site, const void* e
   if (extra) {
     TraceScope ts(b, ATTNRES_KERNEL_SCORE, st);
     hipError_t e = attnres::launch_score(b->g_main, b->cfg.dtype, extra, b->queries, site, site + 1,
-                                         n_rows, b->rinvx(site), b->f(b->lay.logits),
+                                         n_rows, b->rinvx(site), b->f(b->lay.proj),
                                          b->lay.site_stride, st);
     ts.done();
     if (e != hipSuccess) return hip_fail(e, "route_fwd score kernel (transient source)");
@@ -414,8 +434,8 @@ attnres_status_t attnres_route_fwd(attnres_bank_t b, int32_t site, const void* e
   const int64_t row_stride = b->cfg.tokens * (int64_t)b->cfg.d;
   TraceScope ts(b, ATTNRES_KERNEL_FWD, st);
   hipError_t e = attnres::launch_fwd(b->g_main, b->cfg.dtype, b->rows, row_stride, extra, n_rows,
-                                     b->site_logits(site), b->site_alpha(site), b->site_lse(site),
-                                     out, st);
+                                     b->site_proj(site), b->rinv(0), b->rinvx(site),
+                                     b->site_alpha(site), b->site_lse(site), out, st);
   ts.done();
   if (e != hipSuccess) return hip_fail(e, "route_fwd kernel");
   b->extra_ptr[site] = extra;
@@ -457,9 +477,9 @@ attnres_status_t attnres_route_bwd(attnres_bank_t b, int32_t site, const void* e
   {
     TraceScope ts(b, ATTNRES_KERNEL_BWD_SITE, st);
     hipError_t e = attnres::launch_bwd_site(
-        b->g_site, c.dtype, b->rows, row_stride, extra, n_rows, b->site_alpha(site), b->rinv(0),
-        extra ? b->rinvx(site) : nullptr, slot, b->site_pcoef(site), b->site_ssum(site),
-        b->f(b->lay.dqpart), parts, st);
+        b->g_site, c.dtype, b->rows, row_stride, extra, n_rows, b->site_alpha(site),
+        b->site_lse(site), b->rinv(0), extra ? b->rinvx(site) : nullptr, slot, b->site_dl(site),
+        b->site_radial(site), b->f(b->lay.dqpart), parts, st);
     ts.done();
     if (e != hipSuccess) return hip_fail(e, "route_bwd site kernel");
     // With no tokens there are no parts and the reduction writes zeros.
@@ -492,12 +512,13 @@ attnres_status_t attnres_route_bwd(attnres_bank_t b, int32_t site, const void* e
     jobs.push_back(j);
   }
   SiteArrays sa{};
-  sa.logits = b->f(b->lay.logits);
+  sa.proj = b->f(b->lay.proj);
   sa.alpha = b->f(b->lay.alpha);
-  sa.pcoef = b->f(b->lay.pcoef);
-  sa.ssum = b->f(b->lay.ssum);
+  sa.dl = b->f(b->lay.dl);
+  sa.radial = b->f(b->lay.radial);
   sa.lse = b->f(b->lay.lse);
   sa.site_stride = b->lay.site_stride;
+  sa.rad_stride = b->lay.rad_stride;
   sa.th_stride = c.tokens * (int64_t)c.heads;
   TraceScope tf(b, ATTNRES_KERNEL_FINALIZE, st);
   hipError_t e = attnres::launch_finalize(b->g_main, c.dtype, jobs.data(), (int)jobs.size(), sa,
@@ -519,6 +540,24 @@ attnres_status_t attnres_site_saved(attnres_bank_t b, int32_t site, const float*
   if (lse) *lse = b->site_lse(site);
   if (n_src) *n_src = b->nsrc[site] + b->has_extra[site];
   return ATTNRES_OK;
+}
+
+int32_t attnres_probe_sink_words(void) { return attnres::probe_blocks(); }
+
+attnres_status_t attnres_probe_read(const void* src, size_t bytes, uint32_t* sink,
+                                    attnres_stream_t stream) {
+  if ((bytes >= 16 && !src) || !sink || !aligned16(src) || !aligned16(sink))
+    return fail(ATTNRES_ERR_INVALID, "probe_read: src/sink must be non-NULL and 16-byte aligned");
+  hipError_t e = attnres::launch_probe_read(src, bytes, sink, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTNRES_OK : hip_fail(e, "probe_read kernel");
+}
+
+attnres_status_t attnres_probe_copy(const void* src, void* dst, size_t bytes,
+                                    attnres_stream_t stream) {
+  if (bytes >= 16 && (!src || !dst || !aligned16(src) || !aligned16(dst)))
+    return fail(ATTNRES_ERR_INVALID, "probe_copy: src/dst must be non-NULL and 16-byte aligned");
+  hipError_t e = attnres::launch_probe_copy(src, dst, bytes, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTNRES_OK : hip_fail(e, "probe_copy kernel");
 }
 
 attnres_status_t attnres_bank_tiling(attnres_bank_t b, int32_t* out5) {

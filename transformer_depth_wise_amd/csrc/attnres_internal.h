@@ -27,37 +27,40 @@ struct Geom {
   int32_t tt;    // tokens per tile of the streaming kernels
   int32_t cpt;   // chunks per thread of the streaming kernels
   int64_t ntiles;  // ceil(T / tt)
+  int32_t wave_tokens;  // backward site pass: tokens owned by each wave (0: work-group-wide layout)
   float eps;
 };
 
 // Per-site saved state lives in site-major slots of the workspace:
-//   logits / alpha / P : [site][max_rows + 1][T][H]  (source index, then token, head)
-//   ssum / lse         : [site][T][H]
+//   proj          : [site][max_rows + 1][H][T]  raw per-head key projections
+//                   q_h . key_[h] (the logit is this times the inverse RMS)
+//   alpha / dl    : [site][max_rows + 1][T][H]  softmax weights, a (P - S)
+//   radial        : [site][max_rows + 1][T]     sum_h dl_h * logit_h
+//   lse           : [site][T][H]
+// Source index n of a site is bank row n, index nsrc[site] its transient source.
 struct SiteArrays {
-  float* logits;
+  float* proj;
   float* alpha;
-  float* pcoef;
-  float* ssum;
+  float* dl;
+  float* radial;
   float* lse;
-  int64_t site_stride;  // floats between consecutive sites of logits/alpha/pcoef
-  int64_t th_stride;    // floats between consecutive sites of ssum/lse = T*H
+  int64_t site_stride;  // floats between consecutive sites of proj / alpha / dl
+  int64_t rad_stride;   // floats between consecutive sites of radial = (max_rows + 1) * T
+  int64_t th_stride;    // floats between consecutive sites of lse = T * H
 };
 
-// Bank row n of the logits/alpha/pcoef slot of a site starts at
-// base + site*site_stride + n*T*H.
-
 hipError_t launch_score(const Geom& g, int dtype, const void* x, const void* queries, int s_lo,
-                        int s_hi, int slot, float* rinv_out, float* logits,
+                        int s_hi, int slot, float* rinv_out, float* proj,
                         int64_t site_stride, hipStream_t st);
 
 hipError_t launch_fwd(const Geom& g, int dtype, const void* rows, int64_t row_stride,
-                      const void* extra, int n_rows, const float* logits, float* alpha,
-                      float* lse, void* out, hipStream_t st);
+                      const void* extra, int n_rows, const float* proj, const float* rinv_rows,
+                      const float* rinv_x, float* alpha, float* lse, void* out, hipStream_t st);
 
 hipError_t launch_bwd_site(const Geom& g, int dtype, const void* rows, int64_t row_stride,
-                           const void* extra, int n_rows, const float* alpha,
+                           const void* extra, int n_rows, const float* alpha, const float* lse,
                            const float* rinv_rows, const float* rinv_extra, const void* dout,
-                           float* pcoef, float* ssum, float* dq_part, int parts,
+                           float* dl, float* radial, float* dq_part, int parts,
                            hipStream_t st);
 
 hipError_t launch_dq_reduce(const float* dq_part, int parts, int r, float* dq, hipStream_t st);
@@ -78,6 +81,11 @@ hipError_t launch_finalize(const Geom& g, int dtype, const FinalizeJob* jobs, in
 
 // Number of dq partial rows the site pass writes for this geometry.
 int bwd_site_parts(const Geom& g);
+
+// Bandwidth probes (attnres_probe.hip).
+int probe_blocks();
+hipError_t launch_probe_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t st);
+hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
 
 // Dynamic LDS bytes of each kernel (host-side checks before launch).
 size_t lds_fwd(const Geom& g, int n_src);

@@ -7,9 +7,11 @@
 // the bank, with the per-(token, head) scalars of the softmax staged in LDS.
 //
 //   k_score     append time: inverse RMS of the key coordinates of a row and
-//               its per-head logits against every static query that will
-//               read it (queries are input-independent, "Low-Rank Attention
-//               Residuals" section 3.4), so the forward only has to mix.
+//               its per-head key projections q_h . key_[h] against every
+//               static query that will read it (queries are input-independent,
+//               "Low-Rank Attention Residuals" section 3.4), so the forward
+//               only has to mix; the logit is the projection times the inverse
+//               RMS.  k_score_mfma is the matrix-core form for bf16 rows.
 //   k_fwd       softmax over the cached logits, then the per-head mix of the
 //               full-width values (Eq. 3); saves alpha and log-sum-exp.
 //   k_bwd_site  one pass over the rows the site read: per-head
@@ -89,6 +91,47 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// Load of streamed data (bank rows, upstream gradients) that the kernel reads
+// exactly once: non-temporal, so it does not evict reusable lines.
+__device__ __forceinline__ uint4 ld_stream(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Sum over the 4 lanes of a quad (two DPP quad permutations).
+__device__ __forceinline__ float quad_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+  return v;
+}
+
+// <a, b> over one 16-byte chunk with fp32 accumulation.
+template <typename T>
+__device__ __forceinline__ float dot_chunk(const uint4& a, const uint4& b);
+
+template <>
+__device__ __forceinline__ float dot_chunk<bf16_t>(const uint4& a, const uint4& b) {
+  // bf16 x bf16 products are exact in fp32; v_dot2c_f32_bf16 adds two at a time
+  float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x),
+                                            __builtin_bit_cast(bf16x2_t, b.x), 0.f, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.y),
+                                      __builtin_bit_cast(bf16x2_t, b.y), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.z),
+                                      __builtin_bit_cast(bf16x2_t, b.z), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w),
+                                      __builtin_bit_cast(bf16x2_t, b.w), s, false);
+  return s;
+}
+
+template <>
+__device__ __forceinline__ float dot_chunk<float>(const uint4& a, const uint4& b) {
+  return __uint_as_float(a.x) * __uint_as_float(b.x) + __uint_as_float(a.y) * __uint_as_float(b.y) +
+         __uint_as_float(a.z) * __uint_as_float(b.z) + __uint_as_float(a.w) * __uint_as_float(b.w);
+}
+
 // Position of one chunk slot of a thread inside a [tt x cpr] tile of chunks:
 // slot j of thread `tid` is chunk q = tid + j * kThreads, token q / cpr.
 struct Slot {
@@ -116,8 +159,9 @@ __device__ __forceinline__ Slot make_slot(const Geom& g, int tid, int j) {
 }
 
 // ---------------------------------------------------------------------------
-// Append: inverse RMS of the key and per-head logits against the queries of
-// sites [s_lo, s_hi), stored at source index `slot` of each site's logits.
+// Append: inverse RMS of the key and per-head key projections against the
+// queries of sites [s_lo, s_hi), stored at source index `slot` of each site's
+// projection slot.  Vector-ALU form (fp32 rows, or r/H not a multiple of 32).
 // Grid: ceil(T / kScoreTile) work-groups; the key coordinates of a tile are
 // staged in LDS as fp32, each thread owns (head, site) items with the site
 // index fastest, so a wave reads the same LDS words (broadcast) while its
@@ -126,7 +170,7 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void k_score(Geom g, const T* __restrict__ x,
                                                      const T* __restrict__ Q, int s_lo, int s_hi,
                                                      int slot, float* __restrict__ rinv_out,
-                                                     float* __restrict__ logits,
+                                                     float* __restrict__ proj,
                                                      int64_t site_stride) {
   using V = Vec<T>;
   extern __shared__ float sm[];
@@ -183,95 +227,220 @@ __global__ __launch_bounds__(kThreads) void k_score(Geom g, const T* __restrict_
         for (int e = 0; e < V::N; ++e) acc[tau] += qf[e] * kp[e];
       }
     }
-    float* dst = logits + (int64_t)s * site_stride + ((int64_t)slot * g.T + t0) * g.H + h;
+    float* dst = proj + (int64_t)s * site_stride + ((int64_t)slot * g.H + h) * g.T + t0;
 #pragma unroll
     for (int tau = 0; tau < kScoreTile; ++tau)
-      if (t0 + tau < g.T) dst[(int64_t)tau * g.H] = acc[tau] * srinv[tau];
+      if (t0 + tau < g.T) dst[tau] = acc[tau];
   }
+}
+
+// Append on the matrix cores (bf16 storage, r/H a multiple of 32).  Per head
+// the projections are a dense contraction [tokens x r/H] . [r/H x sites], so
+// each wave computes a 16-token x 16-site block per v_mfma_f32_16x16x32_bf16:
+// A = 16 token rows of the key slice (lane l holds row l%16, k-group l/16 of
+// 8 values), B = 16 query rows (same k mapping), D = 16x16 fp32 with lane l
+// holding column (site) l%16, rows (tokens) 4*(l/16)..+3.  The inverse RMS is
+// accumulated from the same A fragments, so the row is read once.
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+constexpr int kMfmaSiteBlocks = 8;  // 16-site blocks accumulated per pass over the row
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+__global__ __launch_bounds__(kThreads) void k_score_mfma(Geom g, const bf16_t* __restrict__ x,
+                                                          const bf16_t* __restrict__ Q, int s_lo,
+                                                          int s_hi, int slot,
+                                                          float* __restrict__ rinv_out,
+                                                          float* __restrict__ proj,
+                                                          int64_t site_stride) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = lane & 15, kg = lane >> 4;
+  const int64_t tw = (int64_t)blockIdx.x * 64 + wave * 16;  // first token of this wave
+  const int64_t t = tw + row;                                // token of this lane's A row
+  const bool tok_ok = t < g.T;
+  const bf16_t* xr = x + (tok_ok ? t : 0) * g.d + (g.d - g.r);
+  const int ns = s_hi - s_lo;
+  const int ksteps = g.kk / 32;
+  const int ngroups = ns > 0 ? (ns + 16 * kMfmaSiteBlocks - 1) / (16 * kMfmaSiteBlocks) : 1;
+  float ss = 0.f;
+  for (int grp = 0; grp < ngroups; ++grp) {
+    const int sg0 = s_lo + grp * 16 * kMfmaSiteBlocks;
+    const int rem = s_hi - sg0;
+    const int nsb = rem > 0 ? min(kMfmaSiteBlocks, (rem + 15) / 16) : 0;
+    for (int h = 0; h < g.H; ++h) {
+      f32x4_t acc[kMfmaSiteBlocks];
+#pragma unroll
+      for (int sb = 0; sb < kMfmaSiteBlocks; ++sb) acc[sb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < ksteps; ++ks) {
+        const int k0 = h * g.kk + ks * 32 + kg * 8;
+        const uint4 av = tok_ok ? ld_stream(reinterpret_cast<const uint4*>(xr + k0)) : zero4();
+        if (grp == 0) {
+          float f[8];
+          Vec<bf16_t>::unpack(av, f);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+        }
+        const bf16x8_t a = as_bf16x8(av);
+#pragma unroll
+        for (int sb = 0; sb < kMfmaSiteBlocks; ++sb) {
+          if (sb < nsb) {
+            const int s = sg0 + sb * 16 + row;
+            const uint4 bv =
+                s < s_hi ? *reinterpret_cast<const uint4*>(Q + (int64_t)s * g.r + k0) : zero4();
+            acc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(bv), acc[sb], 0, 0, 0);
+          }
+        }
+      }
+      // lane (kg, row) holds tokens tw+4kg..+3 of site `row`: one 16-byte
+      // store into the token-fastest [slot][head][token] layout
+      const int64_t tq = tw + kg * 4;
+      const bool vec = (g.T & 3) == 0 && tq + 3 < g.T;
+#pragma unroll
+      for (int sb = 0; sb < kMfmaSiteBlocks; ++sb) {
+        if (sb >= nsb) continue;
+        const int s = sg0 + sb * 16 + row;
+        if (s >= s_hi) continue;
+        float* dst = proj + (int64_t)s * site_stride + ((int64_t)slot * g.H + h) * g.T + tq;
+        if (vec) {
+          *reinterpret_cast<float4*>(dst) = make_float4(acc[sb][0], acc[sb][1], acc[sb][2], acc[sb][3]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (tq + j < g.T) dst[j] = acc[sb][j];
+        }
+      }
+    }
+  }
+  // the four k-groups holding this token row
+  ss += __shfl_xor(ss, 16, 64);
+  ss += __shfl_xor(ss, 32, 64);
+  if (kg == 0 && tok_ok) rinv_out[t] = rsqrtf(ss / (float)g.r + g.eps);
 }
 
 // ---------------------------------------------------------------------------
 // Forward of one site: softmax over the cached logits of the tile's
 // (token, head) pairs, then out = sum_n alpha_n * s_n per head slice.
 // Grid: ceil(T / tt) work-groups.  Source n < n_rows is bank row n, source
-// n_rows (if extra) the transient source.
+// n_rows (if extra) the transient source.  The first two sources are
+// requested before the softmax prologue so that their loads overlap it; the
+// stream then keeps three sources in flight.
 template <typename T, int CPT>
 __global__ __launch_bounds__(kThreads) void k_fwd(Geom g, const T* __restrict__ rows,
                                                    int64_t row_stride, const T* __restrict__ extra,
-                                                   int n_rows, const float* __restrict__ logits,
+                                                   int n_rows, const float* __restrict__ proj,
+                                                   const float* __restrict__ rinv_rows,
+                                                   const float* __restrict__ rinv_x,
                                                    float* __restrict__ alpha,
                                                    float* __restrict__ lse, T* __restrict__ out) {
   using V = Vec<T>;
   constexpr int N = V::N;
-  extern __shared__ float sa[];  // [n_src][tt][H]
+  constexpr int DEPTH = 3;  // sources in flight
+  extern __shared__ float sa[];  // [n_src][tt][H]: logits, then softmax weights
   const int n_src = n_rows + (extra != nullptr ? 1 : 0);
   const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)blockIdx.x * g.tt;
   const int tv = (int)min((int64_t)g.tt, g.T - t0);
   const int pairs = g.tt * g.H;
-  const int vpairs = tv * g.H;
 
-  for (int i = tid; i < n_src * pairs; i += kThreads) {
-    const int n = i / pairs, p = i - n * pairs;
-    sa[i] = (p < vpairs) ? logits[((int64_t)n * g.T + t0) * g.H + p] : 0.f;
-  }
-  __syncthreads();
-  for (int p = tid; p < pairs; p += kThreads) {
-    float m = -INFINITY;
-    for (int n = 0; n < n_src; ++n) m = fmaxf(m, sa[n * pairs + p]);
-    float l = 0.f;
-    for (int n = 0; n < n_src; ++n) l += expf(sa[n * pairs + p] - m);
-    const float ls = m + logf(l);
-    for (int n = 0; n < n_src; ++n) sa[n * pairs + p] = expf(sa[n * pairs + p] - ls);
-    if (p < vpairs) lse[t0 * g.H + p] = ls;
-  }
-  __syncthreads();
-  for (int i = tid; i < n_src * pairs; i += kThreads) {
-    const int n = i / pairs, p = i - n * pairs;
-    if (p < vpairs) alpha[((int64_t)n * g.T + t0) * g.H + p] = sa[i];
-  }
-
+  // Slots outside the tile's valid tokens load the tile's first chunk (valid
+  // memory) and are never stored, so every load is unconditional.
   Slot sl[CPT];
   bool ok[CPT];
+  int qa[CPT], ai[CPT];
 #pragma unroll
   for (int j = 0; j < CPT; ++j) {
     sl[j] = make_slot(g, tid, j);
     ok[j] = sl[j].own && sl[j].tau < tv;
+    qa[j] = ok[j] ? sl[j].q : 0;
+    ai[j] = sl[j].tau * g.H + sl[j].hv;
   }
+  auto tile_of = [&](int n) {
+    const T* src = (n < n_rows) ? rows + (int64_t)n * row_stride : extra;
+    return reinterpret_cast<const uint4*>(src + t0 * g.d);
+  };
+  uint4 buf[DEPTH][CPT];
+#pragma unroll
+  for (int d = 0; d < DEPTH - 1; ++d) {
+    if (d < n_src) {
+      const uint4* sp = tile_of(d);
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) buf[d][j] = ld_stream(sp + qa[j]);
+    }
+  }
+
+  // logit = inverse RMS of the source * cached per-head key projection
+  // (projections are stored [source][head][token])
+#pragma unroll 4
+  for (int i = tid; i < n_src * pairs; i += kThreads) {
+    const int n = i / pairs, p = i - n * pairs;
+    const int tau = p / g.H, h = p - tau * g.H;
+    float v = 0.f;
+    if (tau < tv) {
+      const int64_t t = t0 + tau;
+      const float ri = (n < n_rows) ? rinv_rows[(int64_t)n * g.T + t] : rinv_x[t];
+      v = ri * proj[((int64_t)n * g.H + h) * g.T + t];
+    }
+    sa[i] = v;
+  }
+  __syncthreads();
+  // Softmax over the sources: `sub` threads per (token, head) pair take the
+  // sources round-robin and combine with a fixed butterfly.
+  {
+    int sub = 1;
+    while (sub < 64 && 2 * sub * pairs <= kThreads) sub *= 2;
+    const int p = tid / sub, k = tid - p * sub;
+    const bool live = p < pairs;
+    const int pc = live ? p : 0;
+    float m = -INFINITY;
+    for (int n = k; n < n_src; n += sub) m = fmaxf(m, sa[n * pairs + pc]);
+    for (int o = 1; o < sub; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    float l = 0.f;
+    for (int n = k; n < n_src; n += sub) l += expf(sa[n * pairs + pc] - m);
+    for (int o = 1; o < sub; o <<= 1) l += __shfl_xor(l, o, 64);
+    const float ls = m + logf(l);
+    __syncthreads();  // every max/sum read of sa is done before it is overwritten
+    if (live) {
+      for (int n = k; n < n_src; n += sub) sa[n * pairs + p] = expf(sa[n * pairs + p] - ls);
+      if (k == 0 && p / g.H < tv) lse[t0 * g.H + p] = ls;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < n_src * pairs; i += kThreads) {
+    const int n = i / pairs, p = i - n * pairs;
+    if (p / g.H < tv) alpha[((int64_t)n * g.T + t0) * g.H + p] = sa[i];
+  }
+
   float acc[CPT][N];
 #pragma unroll
   for (int j = 0; j < CPT; ++j)
 #pragma unroll
     for (int e = 0; e < N; ++e) acc[j][e] = 0.f;
-
-  uint4 cur[CPT];
-  {
-    const uint4* sp = reinterpret_cast<const uint4*>((n_rows > 0 ? rows : extra) + t0 * g.d);
+  // The row loop is unrolled by the pipeline depth so the buffers rotate by
+  // index, not by register moves.
+  for (int i = 0; i < n_src; i += DEPTH) {
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) cur[j] = ok[j] ? sp[sl[j].q] : zero4();
-  }
-  for (int n = 0; n < n_src; ++n) {
-    uint4 nxt[CPT];
-    if (n + 1 < n_src) {
-      const T* src = (n + 1 < n_rows) ? rows + (int64_t)(n + 1) * row_stride : extra;
-      const uint4* sp = reinterpret_cast<const uint4*>(src + t0 * g.d);
+    for (int d = 0; d < DEPTH; ++d) {
+      const int n = i + d;
+      if (n < n_src) {
+        const int nf = n + DEPTH - 1;
+        if (nf < n_src) {
+          const uint4* sp = tile_of(nf);
 #pragma unroll
-      for (int j = 0; j < CPT; ++j) nxt[j] = ok[j] ? sp[sl[j].q] : zero4();
-    } else {
+          for (int j = 0; j < CPT; ++j) buf[(d + DEPTH - 1) % DEPTH][j] = ld_stream(sp + qa[j]);
+        }
+        const float* an = sa + n * pairs;
 #pragma unroll
-      for (int j = 0; j < CPT; ++j) nxt[j] = zero4();
+        for (int j = 0; j < CPT; ++j) {
+          const float a = an[ai[j]];
+          float f[N];
+          V::unpack(buf[d][j], f);
+#pragma unroll
+          for (int e = 0; e < N; ++e) acc[j][e] += a * f[e];
+        }
+      }
     }
-    const float* an = sa + n * pairs;
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const float a = an[sl[j].tau * g.H + sl[j].hv];
-      float f[N];
-      V::unpack(cur[j], f);
-#pragma unroll
-      for (int e = 0; e < N; ++e) acc[j][e] += a * f[e];
-    }
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) cur[j] = nxt[j];
   }
   uint4* op = reinterpret_cast<uint4*>(out + t0 * g.d);
 #pragma unroll
@@ -281,32 +450,38 @@ __global__ __launch_bounds__(kThreads) void k_fwd(Geom g, const T* __restrict__ 
 
 // ---------------------------------------------------------------------------
 // Backward, site pass.  For every source n and (token, head):
-//   P_{n,h} = <dout_h, s_{n,h}>  (stored for the finalize gather)
-//   S_h     = sum_n a_{n,h} P_{n,h}
+//   P_{n,h} = <dout_h, s_{n,h}>,   S_h = sum_n a_{n,h} P_{n,h}
 // and the query gradient dq_[h] = sum_t sum_n a (P - S) rho_n^-1 key_n[h],
 // which needs S before any dl is known.  It is split exactly as
 //   dq = sum_t [ sum_n a P rho^-1 key_n ]  -  sum_t S_t W_t,
 //   W_t = sum_n a rho^-1 key_n  (per token, in registers),
 // so the rows are streamed once (the pages' kernel streams them twice).
-// Per row, per-chunk partial dots go to LDS and one thread per (token, head)
-// sums its head's chunks in a fixed order.  Persistent grid of `parts`
-// work-groups, each writing one [r] partial of dq.
+// Per row, each lane dots its 16-byte chunk with the upstream gradient; the
+// 4 lanes of a quad (4 chunks of one head) combine by DPP, quad leaders put
+// the sums in LDS and one thread per (token, head) adds its head's quads in a
+// fixed order.  After the tile the coefficients the finalize gather needs are
+// formed here: dl = a (P - S) and, per (source, token), the radial sum
+// sum_h dl_h * l_h with l = log(a) + lse (the logit).  Persistent grid of
+// `parts` work-groups, each writing one [r] partial of dq.
 template <typename T, int CPT>
 __global__ __launch_bounds__(kThreads) void k_bwd_site(
     Geom g, const T* __restrict__ rows, int64_t row_stride, const T* __restrict__ extra,
-    int n_rows, const float* __restrict__ alpha, const float* __restrict__ rinv_rows,
-    const float* __restrict__ rinv_x, const T* __restrict__ dout, float* __restrict__ pcoef,
-    float* __restrict__ ssum, float* __restrict__ dq_part) {
+    int n_rows, const float* __restrict__ alpha, const float* __restrict__ lse_site,
+    const float* __restrict__ rinv_rows, const float* __restrict__ rinv_x,
+    const T* __restrict__ dout, float* __restrict__ dl_out, float* __restrict__ rad_out,
+    float* __restrict__ dq_part) {
   using V = Vec<T>;
   constexpr int N = V::N;
   extern __shared__ float sm[];
   const int n_src = n_rows + (extra != nullptr ? 1 : 0);
   const int pairs = g.tt * g.H;
-  float* s_alpha = sm;                     // [n_src][tt][H]
-  float* s_rinv = s_alpha + n_src * pairs;  // [n_src][tt]
-  float* s_part = s_rinv + n_src * g.tt;    // [tt * cpr]
-  float* s_P = s_part + g.tt * g.cpr;       // [tt][H]
-  float* s_S = s_P + pairs;                 // [tt][H]
+  const bool quad = (g.kvc & 3) == 0;
+  float* s_alpha = sm;                       // [n_src][tt][H]
+  float* s_P = s_alpha + n_src * pairs;      // [n_src][tt][H]
+  float* s_rinv = s_P + n_src * pairs;       // [n_src][tt]
+  float* s_part = s_rinv + n_src * g.tt;     // [tt * cpr] (or a quarter with quads)
+  float* s_S = s_part + g.tt * g.cpr;        // [tt][H]
+  float* s_lse = s_S + pairs;                // [tt][H]
   const int tid = threadIdx.x;
 
   Slot sl[CPT];
@@ -319,13 +494,29 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
 #pragma unroll
     for (int e = 0; e < N; ++e) dq[j][e] = 0.f;
 
+  auto tile_of = [&](int n, int64_t t0) {
+    const T* src = (n < n_rows) ? rows + (int64_t)n * row_stride : extra;
+    return reinterpret_cast<const uint4*>(src + t0 * g.d);
+  };
+
   for (int64_t tile = blockIdx.x; tile < g.ntiles; tile += gridDim.x) {
     const int64_t t0 = tile * g.tt;
     const int tv = (int)min((int64_t)g.tt, g.T - t0);
-    const int vpairs = tv * g.H;
+    bool ok[CPT];
+    uint4 dov[CPT], cur[CPT];
+    {
+      const uint4* dp = reinterpret_cast<const uint4*>(dout + t0 * g.d);
+      const uint4* sp = tile_of(0, t0);
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        ok[j] = sl[j].own && sl[j].tau < tv;
+        dov[j] = ok[j] ? ld_stream(dp + sl[j].q) : zero4();
+        cur[j] = ok[j] ? ld_stream(sp + sl[j].q) : zero4();
+      }
+    }
     for (int i = tid; i < n_src * pairs; i += kThreads) {
       const int n = i / pairs, p = i - n * pairs;
-      s_alpha[i] = (p < vpairs) ? alpha[((int64_t)n * g.T + t0) * g.H + p] : 0.f;
+      s_alpha[i] = (p / g.H < tv) ? alpha[((int64_t)n * g.T + t0) * g.H + p] : 0.f;
     }
     for (int i = tid; i < n_src * g.tt; i += kThreads) {
       const int n = i / g.tt, tau = i - n * g.tt;
@@ -333,57 +524,45 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
       if (tau < tv) v = (n < n_rows) ? rinv_rows[(int64_t)n * g.T + t0 + tau] : rinv_x[t0 + tau];
       s_rinv[i] = v;
     }
-    bool ok[CPT];
-    float dov[CPT][N];
+    for (int p = tid; p < pairs; p += kThreads) s_lse[p] = (p / g.H < tv) ? lse_site[t0 * g.H + p] : 0.f;
     float W[CPT][N];
-    {
-      const uint4* dp = reinterpret_cast<const uint4*>(dout + t0 * g.d);
 #pragma unroll
-      for (int j = 0; j < CPT; ++j) {
-        ok[j] = sl[j].own && sl[j].tau < tv;
-        V::unpack(ok[j] ? dp[sl[j].q] : zero4(), dov[j]);
+    for (int j = 0; j < CPT; ++j)
 #pragma unroll
-        for (int e = 0; e < N; ++e) W[j][e] = 0.f;
-      }
-    }
+      for (int e = 0; e < N; ++e) W[j][e] = 0.f;
     float S_acc = 0.f;
     __syncthreads();
 
-    uint4 cur[CPT];
-    {
-      const uint4* sp = reinterpret_cast<const uint4*>((n_rows > 0 ? rows : extra) + t0 * g.d);
-#pragma unroll
-      for (int j = 0; j < CPT; ++j) cur[j] = ok[j] ? sp[sl[j].q] : zero4();
-    }
     for (int n = 0; n < n_src; ++n) {
       uint4 nxt[CPT];
       if (n + 1 < n_src) {
-        const T* src = (n + 1 < n_rows) ? rows + (int64_t)(n + 1) * row_stride : extra;
-        const uint4* sp = reinterpret_cast<const uint4*>(src + t0 * g.d);
+        const uint4* sp = tile_of(n + 1, t0);
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) nxt[j] = ok[j] ? sp[sl[j].q] : zero4();
+        for (int j = 0; j < CPT; ++j) nxt[j] = ok[j] ? ld_stream(sp + sl[j].q) : zero4();
       } else {
 #pragma unroll
         for (int j = 0; j < CPT; ++j) nxt[j] = zero4();
       }
-      float xv[CPT][N];
 #pragma unroll
       for (int j = 0; j < CPT; ++j) {
-        V::unpack(cur[j], xv[j]);
-        float part = 0.f;
-#pragma unroll
-        for (int e = 0; e < N; ++e) part += dov[j][e] * xv[j][e];
-        if (sl[j].own) s_part[sl[j].q] = part;
+        float part = dot_chunk<T>(dov[j], cur[j]);
+        if (quad) {
+          part = quad_sum(part);
+          if (sl[j].own && (sl[j].q & 3) == 0) s_part[sl[j].q >> 2] = part;
+        } else if (sl[j].own) {
+          s_part[sl[j].q] = part;
+        }
       }
       __syncthreads();
       if (tid < pairs) {
         const int tau = tid / g.H, h = tid - tau * g.H;
-        const float* pp = s_part + tau * g.cpr + h * g.kvc;
+        const int sh = quad ? 2 : 0;
+        const float* pp = s_part + ((tau * g.cpr + h * g.kvc) >> sh);
+        const int cnt = g.kvc >> sh;
         float P = 0.f;
-        for (int c = 0; c < g.kvc; ++c) P += pp[c];
-        s_P[tid] = P;
+        for (int c = 0; c < cnt; ++c) P += pp[c];
+        s_P[n * pairs + tid] = P;
         S_acc += s_alpha[n * pairs + tid] * P;
-        if (tid < vpairs) pcoef[((int64_t)n * g.T + t0) * g.H + tid] = P;
       }
       __syncthreads();
 #pragma unroll
@@ -391,20 +570,19 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
         if (!sl[j].key) continue;
         const int pi = sl[j].tau * g.H + sl[j].hk;
         const float cw = s_alpha[n * pairs + pi] * s_rinv[n * g.tt + sl[j].tau];
-        const float cu = cw * s_P[pi];
+        const float cu = cw * s_P[n * pairs + pi];
+        float xv[N];
+        V::unpack(cur[j], xv);
 #pragma unroll
         for (int e = 0; e < N; ++e) {
-          W[j][e] += cw * xv[j][e];
-          dq[j][e] += cu * xv[j][e];
+          W[j][e] += cw * xv[e];
+          dq[j][e] += cu * xv[e];
         }
       }
 #pragma unroll
       for (int j = 0; j < CPT; ++j) cur[j] = nxt[j];
     }
-    if (tid < pairs) {
-      s_S[tid] = S_acc;
-      if (tid < vpairs) ssum[t0 * g.H + tid] = S_acc;
-    }
+    if (tid < pairs) s_S[tid] = S_acc;
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
@@ -412,6 +590,22 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
       const float sv = s_S[sl[j].tau * g.H + sl[j].hk];
 #pragma unroll
       for (int e = 0; e < N; ++e) dq[j][e] -= sv * W[j][e];
+    }
+    // coefficients of the finalize gather
+    for (int i = tid; i < n_src * g.tt; i += kThreads) {
+      const int n = i / g.tt, tau = i - n * g.tt;
+      if (tau >= tv) continue;
+      const int base = n * pairs + tau * g.H;
+      float* dst = dl_out + ((int64_t)n * g.T + t0 + tau) * g.H;
+      float c = 0.f;
+      for (int h = 0; h < g.H; ++h) {
+        const float a = s_alpha[base + h];
+        const float dl = a * (s_P[base + h] - s_S[tau * g.H + h]);
+        const float lg = a > 0.f ? logf(a) + s_lse[tau * g.H + h] : 0.f;
+        c += dl * lg;
+        dst[h] = dl;
+      }
+      rad_out[(int64_t)n * g.T + t0 + tau] = c;
     }
     __syncthreads();
   }
@@ -434,18 +628,231 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
 }
 
 // ---------------------------------------------------------------------------
+// Backward site pass, wave-owned tokens: the same computation as k_bwd_site,
+// laid out so that every wave owns whole tokens (tw tokens = 64 * CPT
+// chunks, lane l holding chunks l + 64 j).  All cross-lane exchange stays
+// inside the wave (DPP quads, then a wave-private LDS region), so the row
+// loop has no work-group barrier and the waves of a work-group stream
+// independently.  A work-group tile is 4 * tw tokens.
+__device__ __forceinline__ void wave_lds_fence() {
+  // LDS operations of one wave execute in order; this only stops the
+  // compiler from moving LDS accesses across the exchange point.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+template <typename T, int CPT>
+__global__ __launch_bounds__(kThreads) void k_bwd_site_w(
+    Geom g, const T* __restrict__ rows, int64_t row_stride, const T* __restrict__ extra,
+    int n_rows, const float* __restrict__ alpha, const float* __restrict__ lse_site,
+    const float* __restrict__ rinv_rows, const float* __restrict__ rinv_x,
+    const T* __restrict__ dout, float* __restrict__ dl_out, float* __restrict__ rad_out,
+    float* __restrict__ dq_part) {
+  using V = Vec<T>;
+  constexpr int N = V::N;
+  extern __shared__ float sm[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n_src = n_rows + (extra != nullptr ? 1 : 0);
+  const int tw = g.wave_tokens;
+  const int pw = tw * g.H;  // (token, head) pairs of this wave, <= 64
+  const bool quad = (g.kvc & 3) == 0;
+  const int part_len = quad ? (tw * g.cpr) >> 2 : tw * g.cpr;
+  const int fw = 2 * n_src * pw + n_src * tw + part_len + 2 * pw;
+  float* w_alpha = sm + wave * fw;      // [n_src][tw][H]
+  float* w_P = w_alpha + n_src * pw;    // [n_src][tw][H]
+  float* w_rinv = w_P + n_src * pw;     // [n_src][tw]
+  float* w_part = w_rinv + n_src * tw;  // quad (or chunk) partial dots
+  float* w_S = w_part + part_len;       // [tw][H]
+  float* w_lse = w_S + pw;              // [tw][H]
+
+  int tau[CPT], hv[CPT], hk[CPT], kc[CPT], q[CPT];
+  bool key[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    q[j] = lane + 64 * j;
+    tau[j] = q[j] / g.cpr;
+    const int c = q[j] - tau[j] * g.cpr;
+    hv[j] = c / g.kvc;
+    key[j] = c >= g.key_c0;
+    kc[j] = key[j] ? c - g.key_c0 : 0;
+    hk[j] = kc[j] / g.kkc;
+  }
+  float dq[CPT][N];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j)
+#pragma unroll
+    for (int e = 0; e < N; ++e) dq[j][e] = 0.f;
+
+  for (int64_t tile = blockIdx.x; tile < g.ntiles; tile += gridDim.x) {
+    const int64_t t0 = tile * g.tt + (int64_t)wave * tw;  // first token of this wave
+    const int tv = (int)max((int64_t)0, min((int64_t)tw, g.T - t0));
+    // Loads are based at the wave's first token, or at the tile's first token
+    // (always < T) when the wave has no valid token.
+    const int64_t tb = tv > 0 ? t0 : tile * g.tt;
+    auto tile_of = [&](int n) {
+      const T* src = (n < n_rows) ? rows + (int64_t)n * row_stride : extra;
+      return reinterpret_cast<const uint4*>(src + tb * g.d);
+    };
+    // Chunks of tokens past the end load chunk 0 at tb (valid memory); their
+    // weights are zero and their results are never stored.
+    int qa[CPT];
+    uint4 dov[CPT], buf[2][CPT];
+    {
+      const uint4* dp = reinterpret_cast<const uint4*>(dout + tb * g.d);
+      const uint4* sp = tile_of(0);
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        qa[j] = tau[j] < tv ? q[j] : 0;
+        dov[j] = ld_stream(dp + qa[j]);
+        buf[0][j] = ld_stream(sp + qa[j]);
+      }
+    }
+#pragma unroll 4
+    for (int i = lane; i < n_src * pw; i += 64) {
+      const int n = i / pw, p = i - n * pw;
+      w_alpha[i] = (p / g.H < tv) ? alpha[((int64_t)n * g.T + t0) * g.H + p] : 0.f;
+    }
+    for (int i = lane; i < n_src * tw; i += 64) {
+      const int n = i / tw, t = i - n * tw;
+      float v = 0.f;
+      if (t < tv) v = (n < n_rows) ? rinv_rows[(int64_t)n * g.T + t0 + t] : rinv_x[t0 + t];
+      w_rinv[i] = v;
+    }
+    for (int p = lane; p < pw; p += 64) w_lse[p] = (p / g.H < tv) ? lse_site[t0 * g.H + p] : 0.f;
+    float W[CPT][N];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j)
+#pragma unroll
+      for (int e = 0; e < N; ++e) W[j][e] = 0.f;
+    float S_acc = 0.f;
+    wave_lds_fence();
+
+    for (int i = 0; i < n_src; i += 2) {
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const int n = i + d;
+        if (n >= n_src) break;
+        if (n + 1 < n_src) {
+          const uint4* sp = tile_of(n + 1);
+#pragma unroll
+          for (int j = 0; j < CPT; ++j) buf[d ^ 1][j] = ld_stream(sp + qa[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+          float part = dot_chunk<T>(dov[j], buf[d][j]);
+          if (quad) {
+            part = quad_sum(part);
+            if ((q[j] & 3) == 0) w_part[q[j] >> 2] = part;
+          } else {
+            w_part[q[j]] = part;
+          }
+        }
+        wave_lds_fence();
+        if (lane < pw) {
+          const int t = lane / g.H, h = lane - t * g.H;
+          const int sh = quad ? 2 : 0;
+          const float* pp = w_part + ((t * g.cpr + h * g.kvc) >> sh);
+          const int cnt = g.kvc >> sh;
+          float P = 0.f;
+          for (int c = 0; c < cnt; ++c) P += pp[c];
+          w_P[n * pw + lane] = P;
+          S_acc += w_alpha[n * pw + lane] * P;
+        }
+        wave_lds_fence();
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+          if (!key[j]) continue;
+          const int pi = tau[j] * g.H + hk[j];
+          const float cw = w_alpha[n * pw + pi] * w_rinv[n * tw + tau[j]];
+          const float cu = cw * w_P[n * pw + pi];
+          float xv[N];
+          V::unpack(buf[d][j], xv);
+#pragma unroll
+          for (int e = 0; e < N; ++e) {
+            W[j][e] += cw * xv[e];
+            dq[j][e] += cu * xv[e];
+          }
+        }
+      }
+    }
+    if (lane < pw) w_S[lane] = S_acc;
+    wave_lds_fence();
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      if (!key[j]) continue;
+      const float sv = w_S[tau[j] * g.H + hk[j]];
+#pragma unroll
+      for (int e = 0; e < N; ++e) dq[j][e] -= sv * W[j][e];
+    }
+    // coefficients of the finalize gather
+    for (int i = lane; i < n_src * tw; i += 64) {
+      const int n = i / tw, t = i - n * tw;
+      if (t >= tv) continue;
+      const int base = n * pw + t * g.H;
+      float* dst = dl_out + ((int64_t)n * g.T + t0 + t) * g.H;
+      float c = 0.f;
+      for (int h = 0; h < g.H; ++h) {
+        const float a = w_alpha[base + h];
+        const float dl = a * (w_P[base + h] - w_S[t * g.H + h]);
+        const float lg = a > 0.f ? logf(a) + w_lse[t * g.H + h] : 0.f;
+        c += dl * lg;
+        dst[h] = dl;
+      }
+      rad_out[(int64_t)n * g.T + t0 + t] = c;
+    }
+    wave_lds_fence();
+  }
+
+  // This work-group's part of dq: its 4 * tw token rows summed in a fixed order.
+  __syncthreads();
+  float* s_red = sm;  // [4 * tw][r]
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    if (!key[j]) continue;
+    float* dst = s_red + (wave * tw + tau[j]) * g.r + kc[j] * N;
+#pragma unroll
+    for (int e = 0; e < N; ++e) dst[e] = dq[j][e];
+  }
+  __syncthreads();
+  for (int k = tid; k < g.r; k += kThreads) {
+    float s = 0.f;
+    for (int t = 0; t < g.tt; ++t) s += s_red[t * g.r + k];
+    dq_part[(int64_t)blockIdx.x * g.r + k] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Sum the [parts, r] query-gradient partials in a fixed order.
-__global__ __launch_bounds__(kThreads) void k_dq_reduce(const float* __restrict__ part, int parts,
-                                                         int r, float* __restrict__ dq) {
-  __shared__ float red[kThreads / 64][64];
+// One 1024-thread work-group per 64 columns: wave w sums rows w, w+16, ...
+// with four independent accumulators, then wave 0 adds the 16 wave sums.
+constexpr int kReduceThreads = 1024;
+__global__ __launch_bounds__(kReduceThreads) void k_dq_reduce(const float* __restrict__ part,
+                                                               int parts, int r,
+                                                               float* __restrict__ dq) {
+  constexpr int W = kReduceThreads / 64;
+  __shared__ float red[W][64];
   const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
   const int col = blockIdx.x * 64 + lane;
-  float s = 0.f;
-  if (col < r)
-    for (int i = grp; i < parts; i += kThreads / 64) s += part[(int64_t)i * r + col];
-  red[grp][lane] = s;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  if (col < r) {
+    int i = grp;
+    for (; i + 3 * W < parts; i += 4 * W) {
+      a0 += part[(int64_t)i * r + col];
+      a1 += part[(int64_t)(i + W) * r + col];
+      a2 += part[(int64_t)(i + 2 * W) * r + col];
+      a3 += part[(int64_t)(i + 3 * W) * r + col];
+    }
+    for (; i < parts; i += W) a0 += part[(int64_t)i * r + col];
+  }
+  red[grp][lane] = (a0 + a1) + (a2 + a3);
   __syncthreads();
-  if (grp == 0 && col < r) dq[col] = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
+  if (grp == 0 && col < r) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) s += red[w][lane];
+    dq[col] = s;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -454,8 +861,10 @@ __global__ __launch_bounds__(kThreads) void k_dq_reduce(const float* __restrict_
 // token t, value head hv(j), key head hk(j) of coordinate j:
 //   grad[j] = sum_s a_{s,hv} dout_s[j]
 //           + [j in key] ( sum_s rho^-1 dl_{s,hk} q_s[j - (d - r)]
-//                          - rho^-2 / r * (sum_{s,h} dl_{s,h} l_{s,h}) key[j] )
-// with dl = a (P - S).  Sites are processed in batches that fit in LDS.
+//                          - rho^-2 / r * (sum_s c_s) key[j] )
+// with dl = a (P - S) and c_s = sum_h dl_{s,h} l_{s,h} from the site pass.
+// Sites are processed in batches whose coefficients fit in LDS; each batch's
+// first upstream-gradient tile is requested before its coefficients.
 // Grid: (ceil(T / tt), jobs).
 constexpr int kMaxJobs = 8;
 struct FinalizeArgs {
@@ -472,14 +881,12 @@ __global__ __launch_bounds__(kThreads) void k_finalize(Geom g, FinalizeArgs fa, 
   extern __shared__ float sm[];
   const FinalizeJob job = fa.job[blockIdx.y];
   const int pairs = g.tt * g.H;
-  float* cA = sm;                 // [batch][tt][H]  alpha
-  float* cQ = cA + batch * pairs;  // [batch][tt][H]  rho^-1 * dl
-  float* cR = cQ + batch * pairs;  // [batch][tt][H]  dl * logit
-  float* s_rad = cR + batch * pairs;  // [tt]
+  float* cA = sm;                     // [batch][tt][H]  alpha
+  float* cQ = cA + batch * pairs;     // [batch][tt][H]  rho^-1 * dl
+  float* s_rad = cQ + batch * pairs;  // [tt]
   const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)blockIdx.x * g.tt;
   const int tv = (int)min((int64_t)g.tt, g.T - t0);
-  const int vpairs = tv * g.H;
 
   Slot sl[CPT];
   bool ok[CPT];
@@ -493,67 +900,82 @@ __global__ __launch_bounds__(kThreads) void k_finalize(Geom g, FinalizeArgs fa, 
   for (int j = 0; j < CPT; ++j)
 #pragma unroll
     for (int e = 0; e < N; ++e) acc[j][e] = 0.f;
-  float rad = 0.f;  // thread tau < tt: sum of dl * logit over sites and heads
+  float rad = 0.f;  // thread tau < tt: sum over sites of the radial sums
 
+  auto dout_of = [&](int s) {
+    return reinterpret_cast<const uint4*>(dout_rows + (int64_t)s * dout_stride + t0 * g.d);
+  };
+  // Slots outside the valid tokens load the tile's first chunk (valid memory,
+  // zero weight, never stored), so every load is unconditional.
+  int qa[CPT], ka[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    qa[j] = ok[j] ? sl[j].q : 0;
+    ka[j] = sl[j].kc;
+  }
   for (int b0 = job.s0; b0 < job.s1; b0 += batch) {
     const int nb = min(batch, job.s1 - b0);
+    uint4 buf[2][CPT], qb[2][CPT];
+    {
+      const uint4* dp = dout_of(b0);
+      const uint4* qs = reinterpret_cast<const uint4*>(Q + (int64_t)b0 * g.r);
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        buf[0][j] = ld_stream(dp + qa[j]);
+        qb[0][j] = qs[ka[j]];
+      }
+    }
     for (int i = tid; i < nb * pairs; i += kThreads) {
       const int k = i / pairs, p = i - k * pairs;
-      float a = 0.f, q = 0.f, rr = 0.f;
-      if (p < vpairs) {
-        const int s = b0 + k;
-        const int64_t idx = (int64_t)s * sa.site_stride + ((int64_t)job.slot * g.T + t0) * g.H + p;
+      const int tau = p / g.H;
+      float a = 0.f, q = 0.f;
+      if (tau < tv) {
+        const int64_t idx =
+            (int64_t)(b0 + k) * sa.site_stride + ((int64_t)job.slot * g.T + t0) * g.H + p;
         a = sa.alpha[idx];
-        const float dl = a * (sa.pcoef[idx] - sa.ssum[(int64_t)s * sa.th_stride + t0 * g.H + p]);
-        q = job.rinv[t0 + p / g.H] * dl;
-        rr = dl * sa.logits[idx];
+        q = job.rinv[t0 + tau] * sa.dl[idx];
       }
       cA[i] = a;
       cQ[i] = q;
-      cR[i] = rr;
+    }
+    if (tid < tv) {
+      for (int k = 0; k < nb; ++k)
+        rad += sa.radial[(int64_t)(b0 + k) * sa.rad_stride + (int64_t)job.slot * g.T + t0 + tid];
     }
     __syncthreads();
-    if (tid < g.tt) {
-      for (int k = 0; k < nb; ++k)
-        for (int h = 0; h < g.H; ++h) rad += cR[(k * g.tt + tid) * g.H + h];
-    }
-    uint4 cur[CPT];
-    {
-      const uint4* dp = reinterpret_cast<const uint4*>(dout_rows + (int64_t)b0 * dout_stride + t0 * g.d);
+    for (int i = 0; i < nb; i += 2) {
 #pragma unroll
-      for (int j = 0; j < CPT; ++j) cur[j] = ok[j] ? dp[sl[j].q] : zero4();
-    }
-    for (int k = 0; k < nb; ++k) {
-      const int s = b0 + k;
-      uint4 nxt[CPT];
-      if (k + 1 < nb) {
-        const uint4* dp =
-            reinterpret_cast<const uint4*>(dout_rows + (int64_t)(s + 1) * dout_stride + t0 * g.d);
+      for (int d = 0; d < 2; ++d) {
+        const int k = i + d;
+        if (k >= nb) break;
+        const int s = b0 + k;
+        if (k + 1 < nb) {
+          // query chunks are shared by every token of the tile: cache hits
+          const uint4* dp = dout_of(s + 1);
+          const uint4* qs = reinterpret_cast<const uint4*>(Q + (int64_t)(s + 1) * g.r);
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) nxt[j] = ok[j] ? dp[sl[j].q] : zero4();
-      } else {
+          for (int j = 0; j < CPT; ++j) {
+            buf[d ^ 1][j] = ld_stream(dp + qa[j]);
+            qb[d ^ 1][j] = qs[ka[j]];
+          }
+        }
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) nxt[j] = zero4();
-      }
-      const uint4* qs = reinterpret_cast<const uint4*>(Q + (int64_t)s * g.r);
+        for (int j = 0; j < CPT; ++j) {
+          const int base = (k * g.tt + sl[j].tau) * g.H;
+          const float a = cA[base + sl[j].hv];
+          float f[N];
+          V::unpack(buf[d][j], f);
 #pragma unroll
-      for (int j = 0; j < CPT; ++j) {
-        const int base = (k * g.tt + sl[j].tau) * g.H;
-        const float a = cA[base + sl[j].hv];
-        float f[N];
-        V::unpack(cur[j], f);
+          for (int e = 0; e < N; ++e) acc[j][e] += a * f[e];
+          if (sl[j].key) {
+            const float b = cQ[base + sl[j].hk];
+            float qf[N];
+            V::unpack(qb[d][j], qf);
 #pragma unroll
-        for (int e = 0; e < N; ++e) acc[j][e] += a * f[e];
-        if (sl[j].key) {
-          const float b = cQ[base + sl[j].hk];
-          float qf[N];
-          V::unpack(qs[sl[j].kc], qf);
-#pragma unroll
-          for (int e = 0; e < N; ++e) acc[j][e] += b * qf[e];
+            for (int e = 0; e < N; ++e) acc[j][e] += b * qf[e];
+          }
         }
       }
-#pragma unroll
-      for (int j = 0; j < CPT; ++j) cur[j] = nxt[j];
     }
     __syncthreads();
   }
@@ -584,10 +1006,11 @@ __global__ __launch_bounds__(kThreads) void k_finalize(Geom g, FinalizeArgs fa, 
 
 // ---------------------------------------------------------------------------
 template <typename T>
-using FwdFn = void (*)(Geom, const T*, int64_t, const T*, int, const float*, float*, float*, T*);
+using FwdFn = void (*)(Geom, const T*, int64_t, const T*, int, const float*, const float*,
+                       const float*, float*, float*, T*);
 template <typename T>
 using SiteFn = void (*)(Geom, const T*, int64_t, const T*, int, const float*, const float*,
-                        const float*, const T*, float*, float*, float*);
+                        const float*, const float*, const T*, float*, float*, float*);
 template <typename T>
 using FinFn = void (*)(Geom, FinalizeArgs, SiteArrays, int, const T*, int64_t, const T*);
 
@@ -603,7 +1026,15 @@ FwdFn<T> pick_fwd(int cpt) {
   return nullptr;
 }
 template <typename T>
-SiteFn<T> pick_site(int cpt) {
+SiteFn<T> pick_site(int cpt, bool wave_tokens) {
+  if (wave_tokens) {
+    switch (cpt) {
+      case 2: return k_bwd_site_w<T, 2>;
+      case 4: return k_bwd_site_w<T, 4>;
+      case 5: return k_bwd_site_w<T, 5>;
+    }
+    return nullptr;
+  }
   switch (cpt) {
     case 2: return k_bwd_site<T, 2>;
     case 4: return k_bwd_site<T, 4>;
@@ -627,7 +1058,7 @@ constexpr size_t kMaxLds = 64 * 1024;
 
 int finalize_batch(const Geom& g) {
   const int pairs = g.tt * g.H;
-  int b = (int)((kMaxLds / sizeof(float) - g.tt) / (3 * (size_t)pairs));
+  int b = (int)((kMaxLds / sizeof(float) - g.tt) / (2 * (size_t)pairs));
   return b < 1 ? 1 : b;
 }
 
@@ -637,43 +1068,57 @@ int finalize_batch(const Geom& g) {
 size_t lds_score(const Geom& g) { return sizeof(float) * ((size_t)kScoreTile * g.r + kScoreTile); }
 size_t lds_fwd(const Geom& g, int n_src) { return sizeof(float) * (size_t)n_src * g.tt * g.H; }
 size_t lds_bwd_site(const Geom& g, int n_src) {
+  if (g.wave_tokens > 0) {
+    const size_t tw = g.wave_tokens, pw = tw * g.H;
+    const size_t part = (g.kvc % 4 == 0) ? tw * g.cpr / 4 : tw * g.cpr;
+    const size_t fw = 2 * (size_t)n_src * pw + (size_t)n_src * tw + part + 2 * pw;
+    const size_t a = 4 * fw, b = (size_t)g.tt * g.r;
+    return sizeof(float) * (a > b ? a : b);
+  }
   const size_t pairs = (size_t)g.tt * g.H;
-  const size_t a = (size_t)n_src * pairs + (size_t)n_src * g.tt + (size_t)g.tt * g.cpr + 2 * pairs;
+  const size_t a = 2 * (size_t)n_src * pairs + (size_t)n_src * g.tt + (size_t)g.tt * g.cpr + 2 * pairs;
   const size_t b = (size_t)g.tt * g.r;
   return sizeof(float) * (a > b ? a : b);
 }
 size_t lds_finalize(const Geom& g, int n_sites) {
   int b = finalize_batch(g);
   if (n_sites < b) b = n_sites < 1 ? 1 : n_sites;
-  return sizeof(float) * (3 * (size_t)b * g.tt * g.H + g.tt);
+  return sizeof(float) * (2 * (size_t)b * g.tt * g.H + g.tt);
 }
 
 int bwd_site_parts(const Geom& g) {
-  const int64_t cap = 1024;
+  const int64_t cap = 512;
   return (int)(g.ntiles < cap ? g.ntiles : cap);
 }
 
 hipError_t launch_score(const Geom& g, int dtype, const void* x, const void* queries, int s_lo,
-                        int s_hi, int slot, float* rinv_out, float* logits, int64_t site_stride,
+                        int s_hi, int slot, float* rinv_out, float* proj, int64_t site_stride,
                         hipStream_t st) {
   if (g.T == 0) return hipSuccess;
+  if (dtype != 0 && g.kk % 32 == 0) {
+    const dim3 grid((unsigned)((g.T + 63) / 64));
+    hipLaunchKernelGGL(k_score_mfma, grid, dim3(kThreads), 0, st, g,
+                       static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(queries), s_lo,
+                       s_hi, slot, rinv_out, proj, site_stride);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((g.T + kScoreTile - 1) / kScoreTile));
   const size_t lds = lds_score(g);
   if (lds > kMaxLds) return hipErrorInvalidConfiguration;
   if (dtype == 0)
     hipLaunchKernelGGL(k_score<float>, grid, dim3(kThreads), lds, st, g,
                        static_cast<const float*>(x), static_cast<const float*>(queries), s_lo, s_hi,
-                       slot, rinv_out, logits, site_stride);
+                       slot, rinv_out, proj, site_stride);
   else
     hipLaunchKernelGGL(k_score<bf16_t>, grid, dim3(kThreads), lds, st, g,
                        static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(queries), s_lo,
-                       s_hi, slot, rinv_out, logits, site_stride);
+                       s_hi, slot, rinv_out, proj, site_stride);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd(const Geom& g, int dtype, const void* rows, int64_t row_stride,
-                      const void* extra, int n_rows, const float* logits, float* alpha, float* lse,
-                      void* out, hipStream_t st) {
+                      const void* extra, int n_rows, const float* proj, const float* rinv_rows,
+                      const float* rinv_x, float* alpha, float* lse, void* out, hipStream_t st) {
   if (g.T == 0) return hipSuccess;
   const int n_src = n_rows + (extra ? 1 : 0);
   const size_t lds = lds_fwd(g, n_src);
@@ -683,22 +1128,22 @@ hipError_t launch_fwd(const Geom& g, int dtype, const void* rows, int64_t row_st
     auto fn = pick_fwd<float>(g.cpt);
     if (!fn) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(fn, grid, dim3(kThreads), lds, st, g, static_cast<const float*>(rows),
-                       row_stride, static_cast<const float*>(extra), n_rows, logits, alpha, lse,
-                       static_cast<float*>(out));
+                       row_stride, static_cast<const float*>(extra), n_rows, proj, rinv_rows,
+                       rinv_x, alpha, lse, static_cast<float*>(out));
   } else {
     auto fn = pick_fwd<bf16_t>(g.cpt);
     if (!fn) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(fn, grid, dim3(kThreads), lds, st, g, static_cast<const bf16_t*>(rows),
-                       row_stride, static_cast<const bf16_t*>(extra), n_rows, logits, alpha, lse,
-                       static_cast<bf16_t*>(out));
+                       row_stride, static_cast<const bf16_t*>(extra), n_rows, proj, rinv_rows,
+                       rinv_x, alpha, lse, static_cast<bf16_t*>(out));
   }
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_site(const Geom& g, int dtype, const void* rows, int64_t row_stride,
-                           const void* extra, int n_rows, const float* alpha,
+                           const void* extra, int n_rows, const float* alpha, const float* lse,
                            const float* rinv_rows, const float* rinv_extra, const void* dout,
-                           float* pcoef, float* ssum, float* dq_part, int parts,
+                           float* dl, float* radial, float* dq_part, int parts,
                            hipStream_t st) {
   if (g.T == 0) return hipSuccess;
   const int n_src = n_rows + (extra ? 1 : 0);
@@ -706,24 +1151,24 @@ hipError_t launch_bwd_site(const Geom& g, int dtype, const void* rows, int64_t r
   if (lds > kMaxLds || parts < 1) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)parts);
   if (dtype == 0) {
-    auto fn = pick_site<float>(g.cpt);
+    auto fn = pick_site<float>(g.cpt, g.wave_tokens > 0);
     if (!fn) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(fn, grid, dim3(kThreads), lds, st, g, static_cast<const float*>(rows),
-                       row_stride, static_cast<const float*>(extra), n_rows, alpha, rinv_rows,
-                       rinv_extra, static_cast<const float*>(dout), pcoef, ssum, dq_part);
+                       row_stride, static_cast<const float*>(extra), n_rows, alpha, lse, rinv_rows,
+                       rinv_extra, static_cast<const float*>(dout), dl, radial, dq_part);
   } else {
-    auto fn = pick_site<bf16_t>(g.cpt);
+    auto fn = pick_site<bf16_t>(g.cpt, g.wave_tokens > 0);
     if (!fn) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(fn, grid, dim3(kThreads), lds, st, g, static_cast<const bf16_t*>(rows),
-                       row_stride, static_cast<const bf16_t*>(extra), n_rows, alpha, rinv_rows,
-                       rinv_extra, static_cast<const bf16_t*>(dout), pcoef, ssum, dq_part);
+                       row_stride, static_cast<const bf16_t*>(extra), n_rows, alpha, lse, rinv_rows,
+                       rinv_extra, static_cast<const bf16_t*>(dout), dl, radial, dq_part);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_dq_reduce(const float* dq_part, int parts, int r, float* dq, hipStream_t st) {
   const dim3 grid((unsigned)((r + 63) / 64));
-  hipLaunchKernelGGL(k_dq_reduce, grid, dim3(kThreads), 0, st, dq_part, parts, r, dq);
+  hipLaunchKernelGGL(k_dq_reduce, grid, dim3(kReduceThreads), 0, st, dq_part, parts, r, dq);
   return hipGetLastError();
 }
 
@@ -736,7 +1181,7 @@ hipError_t launch_finalize(const Geom& g, int dtype, const FinalizeJob* jobs, in
     if (jobs[i].s1 - jobs[i].s0 > max_sites) max_sites = jobs[i].s1 - jobs[i].s0;
   int batch = finalize_batch(g);
   if (max_sites < batch) batch = max_sites;
-  const size_t lds = sizeof(float) * (3 * (size_t)batch * g.tt * g.H + g.tt);
+  const size_t lds = sizeof(float) * (2 * (size_t)batch * g.tt * g.H + g.tt);
   if (lds > kMaxLds) return hipErrorInvalidConfiguration;
   for (int j0 = 0; j0 < njobs; j0 += kMaxJobs) {
     FinalizeArgs fa{};
