@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 # Small token counts that the oracle finishes in seconds, each spanning
 # several tiles with a ragged tail (tile sizes: 64 / 16 / 8 / 8 / 2 tokens).
 REDUCED = ["tiny", "tiny@T37", "mhar100m@T200", "mhar350m@T100", "mhar1b@T77",
-           "lr_h1@T9", "lr_h8@T9"]
+           "mhar1b@T100", "lr_h1@T9", "lr_h8@T9", "lr_h8@T12"]
 
 
 def _workload(name):

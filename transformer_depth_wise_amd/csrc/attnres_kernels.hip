@@ -249,74 +249,90 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
+// A work-group owns 16 tokens and its 4 waves split the heads (wave w takes
+// heads w, w+4, ...).  Per head a wave holds its A fragments (this lane's KS
+// 16-byte pieces of the key slice, from HBM), loaded one head ahead, and
+// loops over the 16-site blocks with a single accumulator per block; query
+// fragments are small and shared by every tile, so they come from L2.  The
+// per-wave sums of squares meet in LDS for the inverse RMS.  r/H = KS * 32.
+template <int KS>
 __global__ __launch_bounds__(kThreads) void k_score_mfma(Geom g, const bf16_t* __restrict__ x,
                                                           const bf16_t* __restrict__ Q, int s_lo,
                                                           int s_hi, int slot,
                                                           float* __restrict__ rinv_out,
                                                           float* __restrict__ proj,
                                                           int64_t site_stride) {
+  __shared__ float s_ss[kThreads / 64][16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int kWaves = kThreads / 64;
   const int row = lane & 15, kg = lane >> 4;
-  const int64_t tw = (int64_t)blockIdx.x * 64 + wave * 16;  // first token of this wave
-  const int64_t t = tw + row;                                // token of this lane's A row
+  const int64_t tw = (int64_t)blockIdx.x * 16;  // first token of the work-group
+  const int64_t t = tw + row;                   // token of this lane's A row
   const bool tok_ok = t < g.T;
   const bf16_t* xr = x + (tok_ok ? t : 0) * g.d + (g.d - g.r);
   const int ns = s_hi - s_lo;
-  const int ksteps = g.kk / 32;
-  const int ngroups = ns > 0 ? (ns + 16 * kMfmaSiteBlocks - 1) / (16 * kMfmaSiteBlocks) : 1;
+  const int nsb = (ns + 15) / 16;
+  // lane (kg, row) of the accumulator holds tokens tw+4kg..+3 of site `row`
+  const int64_t tq = tw + kg * 4;
+  const bool vec = (g.T & 3) == 0 && tq + 3 < g.T;
+
+  auto fetch_a = [&](int h, uint4* a) {
+    const bf16_t* p = xr + h * g.kk + kg * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      a[ks] = tok_ok ? ld_stream(reinterpret_cast<const uint4*>(p + ks * 32)) : zero4();
+  };
+
   float ss = 0.f;
-  for (int grp = 0; grp < ngroups; ++grp) {
-    const int sg0 = s_lo + grp * 16 * kMfmaSiteBlocks;
-    const int rem = s_hi - sg0;
-    const int nsb = rem > 0 ? min(kMfmaSiteBlocks, (rem + 15) / 16) : 0;
-    for (int h = 0; h < g.H; ++h) {
-      f32x4_t acc[kMfmaSiteBlocks];
+  uint4 a_cur[KS], a_nxt[KS];
+  if (wave < g.H) fetch_a(wave, a_cur);
+  for (int h = wave; h < g.H; h += kWaves) {
+    if (h + kWaves < g.H) fetch_a(h + kWaves, a_nxt);
 #pragma unroll
-      for (int sb = 0; sb < kMfmaSiteBlocks; ++sb) acc[sb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      for (int ks = 0; ks < ksteps; ++ks) {
-        const int k0 = h * g.kk + ks * 32 + kg * 8;
-        const uint4 av = tok_ok ? ld_stream(reinterpret_cast<const uint4*>(xr + k0)) : zero4();
-        if (grp == 0) {
-          float f[8];
-          Vec<bf16_t>::unpack(av, f);
+    for (int ks = 0; ks < KS; ++ks) {
+      float f[8];
+      Vec<bf16_t>::unpack(a_cur[ks], f);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
-        }
-        const bf16x8_t a = as_bf16x8(av);
+      for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+    }
+    for (int sb = 0; sb < nsb; ++sb) {
+      const int s = s_lo + sb * 16 + row;
+      const bool s_ok = s < s_hi;
+      const bf16_t* qp = Q + (int64_t)(s_ok ? s : s_lo) * g.r + h * g.kk + kg * 8;
+      uint4 b[KS];
 #pragma unroll
-        for (int sb = 0; sb < kMfmaSiteBlocks; ++sb) {
-          if (sb < nsb) {
-            const int s = sg0 + sb * 16 + row;
-            const uint4 bv =
-                s < s_hi ? *reinterpret_cast<const uint4*>(Q + (int64_t)s * g.r + k0) : zero4();
-            acc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(bv), acc[sb], 0, 0, 0);
-          }
-        }
-      }
-      // lane (kg, row) holds tokens tw+4kg..+3 of site `row`: one 16-byte
-      // store into the token-fastest [slot][head][token] layout
-      const int64_t tq = tw + kg * 4;
-      const bool vec = (g.T & 3) == 0 && tq + 3 < g.T;
+      for (int ks = 0; ks < KS; ++ks) b[ks] = *reinterpret_cast<const uint4*>(qp + ks * 32);
+      f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int sb = 0; sb < kMfmaSiteBlocks; ++sb) {
-        if (sb >= nsb) continue;
-        const int s = sg0 + sb * 16 + row;
-        if (s >= s_hi) continue;
+      for (int ks = 0; ks < KS; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a_cur[ks]), as_bf16x8(b[ks]), acc,
+                                                      0, 0, 0);
+      if (s_ok) {
+        // one 16-byte store into the token-fastest [slot][head][token] layout
         float* dst = proj + (int64_t)s * site_stride + ((int64_t)slot * g.H + h) * g.T + tq;
         if (vec) {
-          *reinterpret_cast<float4*>(dst) = make_float4(acc[sb][0], acc[sb][1], acc[sb][2], acc[sb][3]);
+          *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
         } else {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            if (tq + j < g.T) dst[j] = acc[sb][j];
+            if (tq + j < g.T) dst[j] = acc[j];
         }
       }
     }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) a_cur[ks] = a_nxt[ks];
   }
-  // the four k-groups holding this token row
+  // the four k-groups of this wave holding the token row, then the waves
   ss += __shfl_xor(ss, 16, 64);
   ss += __shfl_xor(ss, 32, 64);
-  if (kg == 0 && tok_ok) rinv_out[t] = rsqrtf(ss / (float)g.r + g.eps);
+  if (kg == 0) s_ss[wave][row] = ss;
+  __syncthreads();
+  if (wave == 0 && kg == 0 && tok_ok) {
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) tot += s_ss[w][row];
+    rinv_out[t] = rsqrtf(tot / (float)g.r + g.eps);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -336,7 +352,7 @@ __global__ __launch_bounds__(kThreads) void k_fwd(Geom g, const T* __restrict__ 
                                                    float* __restrict__ lse, T* __restrict__ out) {
   using V = Vec<T>;
   constexpr int N = V::N;
-  constexpr int DEPTH = 3;  // sources in flight
+  constexpr int DEPTH = 2;  // sources in flight (the next one prefetched)
   extern __shared__ float sa[];  // [n_src][tt][H]: logits, then softmax weights
   const int n_src = n_rows + (extra != nullptr ? 1 : 0);
   const int tid = threadIdx.x;
@@ -371,22 +387,50 @@ __global__ __launch_bounds__(kThreads) void k_fwd(Geom g, const T* __restrict__ 
   }
 
   // logit = inverse RMS of the source * cached per-head key projection
-  // (projections are stored [source][head][token])
-#pragma unroll 4
-  for (int i = tid; i < n_src * pairs; i += kThreads) {
-    const int n = i / pairs, p = i - n * pairs;
-    const int tau = p / g.H, h = p - tau * g.H;
-    float v = 0.f;
-    if (tau < tv) {
-      const int64_t t = t0 + tau;
-      const float ri = (n < n_rows) ? rinv_rows[(int64_t)n * g.T + t] : rinv_x[t];
-      v = ri * proj[((int64_t)n * g.H + h) * g.T + t];
+  // (projections are stored [source][head][token]).  With 4-aligned token
+  // runs every thread moves 16-byte words: 4 tokens of one (source, head).
+  const bool vec = (g.tt & 3) == 0 && (g.T & 3) == 0;
+  if (vec) {
+    const int q4 = g.tt >> 2;
+#pragma unroll 2
+    for (int i = tid; i < n_src * g.H * q4; i += kThreads) {
+      const int n = i / (g.H * q4), r = i - n * g.H * q4;
+      const int h = r / q4, k4 = r - h * q4;
+      const int64_t t = t0 + 4 * k4;
+      const int lim = tv - 4 * k4;  // valid tokens of this word (T % 4 == 0: all or none)
+      float4 ri = make_float4(0.f, 0.f, 0.f, 0.f), pr = ri;
+      if (lim > 0) {
+        const float* rr = (n < n_rows) ? rinv_rows + (int64_t)n * g.T : rinv_x;
+        ri = *reinterpret_cast<const float4*>(rr + t);
+        pr = *reinterpret_cast<const float4*>(proj + ((int64_t)n * g.H + h) * g.T + t);
+      }
+      float* d = sa + n * pairs + (4 * k4) * g.H + h;
+      d[0] = lim > 0 ? ri.x * pr.x : 0.f;
+      d[g.H] = lim > 1 ? ri.y * pr.y : 0.f;
+      d[2 * g.H] = lim > 2 ? ri.z * pr.z : 0.f;
+      d[3 * g.H] = lim > 3 ? ri.w * pr.w : 0.f;
     }
-    sa[i] = v;
+  } else {
+#pragma unroll 4
+    for (int i = tid; i < n_src * pairs; i += kThreads) {
+      const int n = i / pairs, p = i - n * pairs;
+      const int tau = p / g.H, h = p - tau * g.H;
+      float v = 0.f;
+      if (tau < tv) {
+        const int64_t t = t0 + tau;
+        const float ri = (n < n_rows) ? rinv_rows[(int64_t)n * g.T + t] : rinv_x[t];
+        v = ri * proj[((int64_t)n * g.H + h) * g.T + t];
+      }
+      sa[i] = v;
+    }
   }
   __syncthreads();
   // Softmax over the sources: `sub` threads per (token, head) pair take the
-  // sources round-robin and combine with a fixed butterfly.
+  // sources round-robin and combine with a fixed butterfly.  The weights and
+  // lse are stored after the row loop: on this GPU stores and loads share one
+  // completion counter, so stores ahead of the stream would delay it.
+  float lse_v = 0.f;
+  int lse_p = -1;
   {
     int sub = 1;
     while (sub < 64 && 2 * sub * pairs <= kThreads) sub *= 2;
@@ -403,14 +447,11 @@ __global__ __launch_bounds__(kThreads) void k_fwd(Geom g, const T* __restrict__ 
     __syncthreads();  // every max/sum read of sa is done before it is overwritten
     if (live) {
       for (int n = k; n < n_src; n += sub) sa[n * pairs + p] = expf(sa[n * pairs + p] - ls);
-      if (k == 0 && p / g.H < tv) lse[t0 * g.H + p] = ls;
+      lse_v = ls;
     }
+    lse_p = (live && k == 0 && p / g.H < tv) ? p : -1;
   }
   __syncthreads();
-  for (int i = tid; i < n_src * pairs; i += kThreads) {
-    const int n = i / pairs, p = i - n * pairs;
-    if (p / g.H < tv) alpha[((int64_t)n * g.T + t0) * g.H + p] = sa[i];
-  }
 
   float acc[CPT][N];
 #pragma unroll
@@ -446,6 +487,21 @@ __global__ __launch_bounds__(kThreads) void k_fwd(Geom g, const T* __restrict__ 
 #pragma unroll
   for (int j = 0; j < CPT; ++j)
     if (ok[j]) op[sl[j].q] = V::pack(acc[j]);
+  if (lse_p >= 0) lse[t0 * g.H + lse_p] = lse_v;
+  if ((g.H & 3) == 0 && (g.T & 3) == 0) {
+    const int p4 = pairs >> 2;
+    for (int i = tid; i < n_src * p4; i += kThreads) {
+      const int n = i / p4, r = i - n * p4;
+      if ((4 * r) / g.H < tv)  // a word never straddles two tokens when H % 4 == 0
+        *reinterpret_cast<float4*>(alpha + ((int64_t)n * g.T + t0) * g.H + 4 * r) =
+            *reinterpret_cast<const float4*>(sa + n * pairs + 4 * r);
+    }
+  } else {
+    for (int i = tid; i < n_src * pairs; i += kThreads) {
+      const int n = i / pairs, p = i - n * pairs;
+      if (p / g.H < tv) alpha[((int64_t)n * g.T + t0) * g.H + p] = sa[i];
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -708,10 +764,22 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site_w(
         buf[0][j] = ld_stream(sp + qa[j]);
       }
     }
+    if ((g.H & 3) == 0) {  // 16-byte words, each within one token
+      const int p4 = pw >> 2;
+#pragma unroll 2
+      for (int i = lane; i < n_src * p4; i += 64) {
+        const int n = i / p4, r = i - n * p4;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if ((4 * r) / g.H < tv)
+          v = *reinterpret_cast<const float4*>(alpha + ((int64_t)n * g.T + t0) * g.H + 4 * r);
+        *reinterpret_cast<float4*>(w_alpha + n * pw + 4 * r) = v;
+      }
+    } else {
 #pragma unroll 4
-    for (int i = lane; i < n_src * pw; i += 64) {
-      const int n = i / pw, p = i - n * pw;
-      w_alpha[i] = (p / g.H < tv) ? alpha[((int64_t)n * g.T + t0) * g.H + p] : 0.f;
+      for (int i = lane; i < n_src * pw; i += 64) {
+        const int n = i / pw, p = i - n * pw;
+        w_alpha[i] = (p / g.H < tv) ? alpha[((int64_t)n * g.T + t0) * g.H + p] : 0.f;
+      }
     }
     for (int i = lane; i < n_src * tw; i += 64) {
       const int n = i / tw, t = i - n * tw;
@@ -785,19 +853,31 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site_w(
 #pragma unroll
       for (int e = 0; e < N; ++e) dq[j][e] -= sv * W[j][e];
     }
-    // coefficients of the finalize gather
+    // coefficients of the finalize gather, 16-byte stores when H % 4 == 0
     for (int i = lane; i < n_src * tw; i += 64) {
       const int n = i / tw, t = i - n * tw;
       if (t >= tv) continue;
       const int base = n * pw + t * g.H;
       float* dst = dl_out + ((int64_t)n * g.T + t0 + t) * g.H;
       float c = 0.f;
-      for (int h = 0; h < g.H; ++h) {
-        const float a = w_alpha[base + h];
-        const float dl = a * (w_P[base + h] - w_S[t * g.H + h]);
-        const float lg = a > 0.f ? logf(a) + w_lse[t * g.H + h] : 0.f;
-        c += dl * lg;
-        dst[h] = dl;
+      for (int h0 = 0; h0 < g.H; h0 += 4) {
+        float dv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int h = h0 + u;
+          dv[u] = 0.f;
+          if (h < g.H) {
+            const float a = w_alpha[base + h];
+            dv[u] = a * (w_P[base + h] - w_S[t * g.H + h]);
+            const float lg = a > 0.f ? logf(a) + w_lse[t * g.H + h] : 0.f;
+            c += dv[u] * lg;
+          }
+        }
+        if ((g.H & 3) == 0) {
+          *reinterpret_cast<float4*>(dst + h0) = make_float4(dv[0], dv[1], dv[2], dv[3]);
+        } else {
+          for (int u = 0; u < 4 && h0 + u < g.H; ++u) dst[h0 + u] = dv[u];
+        }
       }
       rad_out[(int64_t)n * g.T + t0 + t] = c;
     }
@@ -883,7 +963,8 @@ __global__ __launch_bounds__(kThreads) void k_finalize(Geom g, FinalizeArgs fa, 
   const int pairs = g.tt * g.H;
   float* cA = sm;                     // [batch][tt][H]  alpha
   float* cQ = cA + batch * pairs;     // [batch][tt][H]  rho^-1 * dl
-  float* s_rad = cQ + batch * pairs;  // [tt]
+  float* s_radb = cQ + batch * pairs; // [batch][tt]     radial sums of the batch
+  float* s_rad = s_radb + batch * g.tt;  // [tt]
   const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)blockIdx.x * g.tt;
   const int tv = (int)min((int64_t)g.tt, g.T - t0);
@@ -925,24 +1006,50 @@ __global__ __launch_bounds__(kThreads) void k_finalize(Geom g, FinalizeArgs fa, 
         qb[0][j] = qs[ka[j]];
       }
     }
-    for (int i = tid; i < nb * pairs; i += kThreads) {
-      const int k = i / pairs, p = i - k * pairs;
-      const int tau = p / g.H;
-      float a = 0.f, q = 0.f;
-      if (tau < tv) {
-        const int64_t idx =
-            (int64_t)(b0 + k) * sa.site_stride + ((int64_t)job.slot * g.T + t0) * g.H + p;
-        a = sa.alpha[idx];
-        q = job.rinv[t0 + tau] * sa.dl[idx];
+    if ((g.H & 3) == 0 && (g.T & 3) == 0) {  // 16-byte words, each within one token
+      const int p4 = pairs >> 2;
+#pragma unroll 2
+      for (int i = tid; i < nb * p4; i += kThreads) {
+        const int k = i / p4, r = i - k * p4;
+        const int tau = (4 * r) / g.H;
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), q = a;
+        if (tau < tv) {
+          const int64_t idx =
+              (int64_t)(b0 + k) * sa.site_stride + ((int64_t)job.slot * g.T + t0) * g.H + 4 * r;
+          a = *reinterpret_cast<const float4*>(sa.alpha + idx);
+          const float4 dl = *reinterpret_cast<const float4*>(sa.dl + idx);
+          const float ri = job.rinv[t0 + tau];
+          q = make_float4(ri * dl.x, ri * dl.y, ri * dl.z, ri * dl.w);
+        }
+        *reinterpret_cast<float4*>(cA + k * pairs + 4 * r) = a;
+        *reinterpret_cast<float4*>(cQ + k * pairs + 4 * r) = q;
       }
-      cA[i] = a;
-      cQ[i] = q;
+    } else {
+      for (int i = tid; i < nb * pairs; i += kThreads) {
+        const int k = i / pairs, p = i - k * pairs;
+        const int tau = p / g.H;
+        float a = 0.f, q = 0.f;
+        if (tau < tv) {
+          const int64_t idx =
+              (int64_t)(b0 + k) * sa.site_stride + ((int64_t)job.slot * g.T + t0) * g.H + p;
+          a = sa.alpha[idx];
+          q = job.rinv[t0 + tau] * sa.dl[idx];
+        }
+        cA[i] = a;
+        cQ[i] = q;
+      }
     }
-    if (tid < tv) {
-      for (int k = 0; k < nb; ++k)
-        rad += sa.radial[(int64_t)(b0 + k) * sa.rad_stride + (int64_t)job.slot * g.T + t0 + tid];
+    // radial sums of the batch: one value per (site, token), then a fixed-order
+    // sum per token
+    for (int i = tid; i < nb * g.tt; i += kThreads) {
+      const int k = i / g.tt, tau = i - k * g.tt;
+      s_radb[i] = tau < tv ? sa.radial[(int64_t)(b0 + k) * sa.rad_stride +
+                                       (int64_t)job.slot * g.T + t0 + tau]
+                           : 0.f;
     }
     __syncthreads();
+    if (tid < g.tt)
+      for (int k = 0; k < nb; ++k) rad += s_radb[k * g.tt + tid];
     for (int i = 0; i < nb; i += 2) {
 #pragma unroll
       for (int d = 0; d < 2; ++d) {
@@ -1058,7 +1165,7 @@ constexpr size_t kMaxLds = 64 * 1024;
 
 int finalize_batch(const Geom& g) {
   const int pairs = g.tt * g.H;
-  int b = (int)((kMaxLds / sizeof(float) - g.tt) / (2 * (size_t)pairs));
+  int b = (int)((kMaxLds / sizeof(float) - g.tt) / (2 * (size_t)pairs + g.tt));
   return b < 1 ? 1 : b;
 }
 
@@ -1083,7 +1190,7 @@ size_t lds_bwd_site(const Geom& g, int n_src) {
 size_t lds_finalize(const Geom& g, int n_sites) {
   int b = finalize_batch(g);
   if (n_sites < b) b = n_sites < 1 ? 1 : n_sites;
-  return sizeof(float) * (2 * (size_t)b * g.tt * g.H + g.tt);
+  return sizeof(float) * (2 * (size_t)b * g.tt * g.H + (size_t)b * g.tt + g.tt);
 }
 
 int bwd_site_parts(const Geom& g) {
@@ -1095,11 +1202,27 @@ hipError_t launch_score(const Geom& g, int dtype, const void* x, const void* que
                         int s_hi, int slot, float* rinv_out, float* proj, int64_t site_stride,
                         hipStream_t st) {
   if (g.T == 0) return hipSuccess;
-  if (dtype != 0 && g.kk % 32 == 0) {
-    const dim3 grid((unsigned)((g.T + 63) / 64));
-    hipLaunchKernelGGL(k_score_mfma, grid, dim3(kThreads), 0, st, g,
-                       static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(queries), s_lo,
-                       s_hi, slot, rinv_out, proj, site_stride);
+  if (dtype != 0 && g.kk % 32 == 0 && g.kk <= 256) {
+    const int ks = g.kk / 32;
+    const dim3 grid((unsigned)((g.T + 15) / 16));
+    const bf16_t* xb = static_cast<const bf16_t*>(x);
+    const bf16_t* qb = static_cast<const bf16_t*>(queries);
+    switch (ks) {
+#define ATTNRES_SCORE_KS(K)                                                                  \
+  case K:                                                                                    \
+    hipLaunchKernelGGL(k_score_mfma<K>, grid, dim3(kThreads), 0, st, g, xb, qb, s_lo, s_hi, \
+                       slot, rinv_out, proj, site_stride);                                   \
+    break;
+      ATTNRES_SCORE_KS(1)
+      ATTNRES_SCORE_KS(2)
+      ATTNRES_SCORE_KS(3)
+      ATTNRES_SCORE_KS(4)
+      ATTNRES_SCORE_KS(5)
+      ATTNRES_SCORE_KS(6)
+      ATTNRES_SCORE_KS(7)
+      ATTNRES_SCORE_KS(8)
+#undef ATTNRES_SCORE_KS
+    }
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((g.T + kScoreTile - 1) / kScoreTile));
@@ -1181,7 +1304,7 @@ hipError_t launch_finalize(const Geom& g, int dtype, const FinalizeJob* jobs, in
     if (jobs[i].s1 - jobs[i].s0 > max_sites) max_sites = jobs[i].s1 - jobs[i].s0;
   int batch = finalize_batch(g);
   if (max_sites < batch) batch = max_sites;
-  const size_t lds = sizeof(float) * (2 * (size_t)batch * g.tt * g.H + g.tt);
+  const size_t lds = sizeof(float) * (2 * (size_t)batch * g.tt * g.H + (size_t)batch * g.tt + g.tt);
   if (lds > kMaxLds) return hipErrorInvalidConfiguration;
   for (int j0 = 0; j0 < njobs; j0 += kMaxJobs) {
     FinalizeArgs fa{};
