@@ -14,9 +14,13 @@ Prints one JSON line (see the design doc for the byte model behind the GB/s).
 from __future__ import annotations
 
 import argparse
+import collections
+import csv
+import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -26,6 +30,15 @@ if ROOT not in sys.path:
 
 METRIC = "routing ms/microbatch fwd+bwd and achieved HBM GB/s (% of peak), 1 MI355X"
 HBM_PEAK_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+# Sources whose change makes a stored counter summary stale.
+KERNEL_SOURCES = ("transformer_depth_wise_amd/csrc/attnres_kernels.hip",
+                  "transformer_depth_wise_amd/csrc/attnres_internal.h",
+                  "transformer_depth_wise_amd/csrc/attnres_host.cpp")
+# Kernel symbol -> kernel kind reported by the library trace.
+KERNEL_KIND = (("k_score", "score"), ("k_fwd", "fwd"), ("k_bwd_site", "bwd_site"),
+               ("k_dq_reduce", "dq_reduce"), ("k_finalize", "finalize"),
+               ("k_probe_copy", "probe_copy"), ("k_probe_read", "probe_read"))
 
 
 # ---------------------------------------------------------------------------
@@ -106,11 +119,14 @@ def cpu_baseline(name: str, tokens: int, full_tokens: int):
     }
 
 
-def bandwidth_probe(torch, gib: float = 2.0, reps: int = 10):
-    """Practical HBM ceiling: 16-byte-load read stream and copy over `gib` GiB."""
+PROBE_BYTES = 2 << 30  # bytes each bandwidth probe reads
+
+
+def bandwidth_probe(torch, reps: int = 10):
+    """Practical HBM ceiling: 16-byte-load read stream and copy of PROBE_BYTES."""
     from transformer_depth_wise_amd.attnres import (attnres_probe_copy, attnres_probe_read,
                                                     attnres_probe_sink_words)
-    n = int(gib * (1 << 30))
+    n = PROBE_BYTES
     src = torch.empty(n, dtype=torch.uint8, device="cuda")
     src.fill_(1)
     dst = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -133,6 +149,74 @@ def bandwidth_probe(torch, gib: float = 2.0, reps: int = 10):
     return out
 
 
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counters_path(workload: str) -> str:
+    return os.path.join(PROFILES, f"{workload}_hbm_counters.txt")
+
+
+def kind_of(kernel_name: str):
+    for sym, kind in KERNEL_KIND:
+        if re.search(r"\b" + sym + r"(_\w+)?\b", kernel_name):  # k_score_mfma, k_bwd_site_w
+            return kind
+    return None
+
+
+def summarize_counters(pmc_dir: str, workload: str, copy_bytes: int, command: str) -> str:
+    """Per-kernel HBM bytes per dispatch from a FETCH_SIZE run and a WRITE_SIZE
+    run of rocprofv3 (CSV output), each calibrated by the reading of the same
+    counter for the copy probe, which moves `copy_bytes` in and out."""
+    per = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        path = os.path.join(pmc_dir, f"pmc_{counter}", "run_counter_collection.csv")
+        tot, disp = collections.defaultdict(float), collections.defaultdict(set)
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                kind = kind_of(row["Kernel_Name"])
+                if kind is None or row["Counter_Name"] != counter:
+                    continue
+                tot[kind] += float(row["Counter_Value"])
+                disp[kind].add(row["Dispatch_Id"])
+        per[counter] = {k: (tot[k] / len(disp[k]), len(disp[k])) for k in tot}
+    scale = {c: copy_bytes / (per[c]["probe_copy"][0] * 1024.0) for c in per}
+    lines = [f"# HBM traffic per dispatch, {workload}: rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB)",
+             f"# command: {command}",
+             f"# calibration: copy probe of {copy_bytes} bytes in + out reads "
+             f"FETCH_SIZE x{scale['FETCH_SIZE']:.4f}, WRITE_SIZE x{scale['WRITE_SIZE']:.4f}",
+             f"source_hash {source_hash()}",
+             f"scale FETCH_SIZE {scale['FETCH_SIZE']:.6f} WRITE_SIZE {scale['WRITE_SIZE']:.6f}",
+             "# kind dispatches fetch_kib write_kib fetch_bytes_calibrated write_bytes_calibrated"]
+    for kind in sorted(per["FETCH_SIZE"]):
+        fk, n = per["FETCH_SIZE"][kind]
+        wk = per["WRITE_SIZE"].get(kind, (0.0, 0))[0]
+        lines.append(f"kernel {kind} {n} {fk:.1f} {wk:.1f} "
+                     f"{fk * 1024 * scale['FETCH_SIZE']:.0f} {wk * 1024 * scale['WRITE_SIZE']:.0f}")
+    return "\n".join(lines) + "\n"
+
+
+def load_counters(workload: str):
+    """Calibrated (fetch, write) bytes per dispatch per kernel kind from the
+    stored summary, or None when it is missing or the kernels changed since."""
+    path = counters_path(workload)
+    if not os.path.exists(path):
+        return None
+    out, stamp = {}, None
+    with open(path) as f:
+        for line in f:
+            p = line.split()
+            if p and p[0] == "source_hash":
+                stamp = p[1]
+            elif p and p[0] == "kernel":
+                out[p[1]] = (float(p[5]), float(p[6]))
+    return out if stamp == source_hash() else None
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,7 +226,19 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true")
+    ap.add_argument("--counters", metavar="DIR",
+                    help="summarize rocprofv3 FETCH_SIZE/WRITE_SIZE runs of this bench found "
+                         "in DIR/pmc_<counter>/ into profiles/ and exit (no GPU use)")
+    ap.add_argument("--counters-command", default="", help="command recorded in the summary")
     args = ap.parse_args()
+
+    if args.counters:
+        text = summarize_counters(args.counters, args.workload, PROBE_BYTES,
+                                  args.counters_command)
+        with open(counters_path(args.workload), "w") as f:
+            f.write(text)
+        print(text, end="")
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures the routing path on one GPU only: the kernel is per-token "
@@ -239,9 +335,15 @@ def main():
                        "gbps": round(alg[k] * args.steps / tms / 1e6, 1)}
         dom = max(kern, key=lambda k: kern[k]["ms_per_microbatch"])
         a = kern[dom]["gbps"]
+        n_launch = kern[dom]["launches_per_microbatch"]
+        counters = load_counters(w.name)
+        traffic = None
+        if counters is not None and dom in counters:
+            traffic = int(sum(counters[dom]))
         result["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": a,
                               "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                              "frac": round(a / HBM_PEAK_GBPS, 3), "traffic": None}
+                              "frac": round(a / HBM_PEAK_GBPS, 3), "traffic": traffic,
+                              "alg_bytes_per_launch": int(alg[dom] / n_launch)}
         result["kernels"] = kern
         print(f"[bench] per-kernel: {json.dumps(kern)}", file=sys.stderr, flush=True)
 
