@@ -166,6 +166,17 @@ __device__ __forceinline__ Slot make_slot(const Geom& g, int tid, int j) {
 // staged in LDS as fp32, each thread owns (head, site) items with the site
 // index fastest, so a wave reads the same LDS words (broadcast) while its
 // lanes stream different query rows from L2.
+// Work-groups are dispatched round-robin over the 8 XCDs, each with its own
+// L2.  Renumbering them so that each XCD's share is one contiguous range of
+// tiles lets neighbouring tiles share the 128-byte lines of the small
+// per-token arrays (inverse RMS, projections, radial sums) in one L2 instead
+// of each XCD fetching a whole line for a 32-byte run.
+__device__ __forceinline__ int64_t xcd_order(int64_t b, int64_t n) {
+  constexpr int64_t kXcds = 8;
+  const int64_t q = n / kXcds, rem = n % kXcds, x = b % kXcds, k = b / kXcds;
+  return x * q + (x < rem ? x : rem) + k;
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_score(Geom g, const T* __restrict__ x,
                                                      const T* __restrict__ Q, int s_lo, int s_hi,
@@ -177,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void k_score(Geom g, const T* __restrict_
   float* keys = sm;                      // [kScoreTile][r]
   float* srinv = sm + kScoreTile * g.r;  // [kScoreTile]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t t0 = (int64_t)blockIdx.x * kScoreTile;
+  const int64_t t0 = xcd_order(blockIdx.x, gridDim.x) * kScoreTile;
   const int kc = g.r / V::N;
 
   for (int tau = wave; tau < kScoreTile; tau += kThreads / 64) {
@@ -266,7 +277,7 @@ __global__ __launch_bounds__(kThreads) void k_score_mfma(Geom g, const bf16_t* _
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int kWaves = kThreads / 64;
   const int row = lane & 15, kg = lane >> 4;
-  const int64_t tw = (int64_t)blockIdx.x * 16;  // first token of the work-group
+  const int64_t tw = xcd_order(blockIdx.x, gridDim.x) * 16;  // first token of the work-group
   const int64_t t = tw + row;                   // token of this lane's A row
   const bool tok_ok = t < g.T;
   const bf16_t* xr = x + (tok_ok ? t : 0) * g.d + (g.d - g.r);
@@ -356,7 +367,7 @@ __global__ __launch_bounds__(kThreads) void k_fwd(Geom g, const T* __restrict__ 
   extern __shared__ float sa[];  // [n_src][tt][H]: logits, then softmax weights
   const int n_src = n_rows + (extra != nullptr ? 1 : 0);
   const int tid = threadIdx.x;
-  const int64_t t0 = (int64_t)blockIdx.x * g.tt;
+  const int64_t t0 = xcd_order(blockIdx.x, gridDim.x) * g.tt;
   const int tv = (int)min((int64_t)g.tt, g.T - t0);
   const int pairs = g.tt * g.H;
 
@@ -555,7 +566,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
     return reinterpret_cast<const uint4*>(src + t0 * g.d);
   };
 
-  for (int64_t tile = blockIdx.x; tile < g.ntiles; tile += gridDim.x) {
+  for (int64_t tile = xcd_order(blockIdx.x, gridDim.x); tile < g.ntiles; tile += gridDim.x) {
     const int64_t t0 = tile * g.tt;
     const int tv = (int)min((int64_t)g.tt, g.T - t0);
     bool ok[CPT];
@@ -740,7 +751,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site_w(
 #pragma unroll
     for (int e = 0; e < N; ++e) dq[j][e] = 0.f;
 
-  for (int64_t tile = blockIdx.x; tile < g.ntiles; tile += gridDim.x) {
+  for (int64_t tile = xcd_order(blockIdx.x, gridDim.x); tile < g.ntiles; tile += gridDim.x) {
     const int64_t t0 = tile * g.tt + (int64_t)wave * tw;  // first token of this wave
     const int tv = (int)max((int64_t)0, min((int64_t)tw, g.T - t0));
     // Loads are based at the wave's first token, or at the tile's first token
@@ -959,14 +970,17 @@ __global__ __launch_bounds__(kThreads) void k_finalize(Geom g, FinalizeArgs fa, 
   using V = Vec<T>;
   constexpr int N = V::N;
   extern __shared__ float sm[];
-  const FinalizeJob job = fa.job[blockIdx.y];
+  const int64_t lin = xcd_order((int64_t)blockIdx.y * gridDim.x + blockIdx.x,
+                                (int64_t)gridDim.x * gridDim.y);
+  const int64_t tile = lin % gridDim.x;
+  const FinalizeJob job = fa.job[lin / gridDim.x];
   const int pairs = g.tt * g.H;
   float* cA = sm;                     // [batch][tt][H]  alpha
   float* cQ = cA + batch * pairs;     // [batch][tt][H]  rho^-1 * dl
   float* s_radb = cQ + batch * pairs; // [batch][tt]     radial sums of the batch
   float* s_rad = s_radb + batch * g.tt;  // [tt]
   const int tid = threadIdx.x;
-  const int64_t t0 = (int64_t)blockIdx.x * g.tt;
+  const int64_t t0 = tile * g.tt;
   const int tv = (int)min((int64_t)g.tt, g.T - t0);
 
   Slot sl[CPT];
