@@ -9,4 +9,5 @@ from .attnres_oracle import (  # noqa: F401
     route_backward,
     route_forward,
     run_schedule,
+    source_inv_rms,
 )

@@ -37,8 +37,20 @@ Readings where the pages are open (each also listed in the design doc):
       the whole source; the fused kernel of Appendix E takes mean(v*v) over
       the row).  For LR keys the RMS is over the r key coordinates.
   R2  eps = 1e-6 inside the square root: (mean(k^2) + eps)^(-1/2).
-  R3  No RMSNorm gain (LR pages: parameter-free norm).  A gain would fold
-      into q for the forward ("Low-Rank Attention Residuals", Eq. 17).
+  R3  The routing RMSNorm is parameter-free unless a gain g in R^r is given
+      per site; then the normalised key is multiplied by g coordinate-wise
+      ("Multi-Head Attention Residuals", Appendix E, Figures 9-10: the key
+      is the normalised row times g) and the gain gradient is returned.
+      The forward then equals the gain-free read with query q * g
+      ("Low-Rank Attention Residuals", Appendix B.1, Eq. 17).  The fused
+      kernel of Figure 9 rounds the normalised key to the storage dtype
+      before the gain; the oracle keeps it exact.
+  R7  norm="full" is the full-width-RMS control ("Low-Rank Attention
+      Residuals", section 4.4, Eq. 13 control): the RMS is taken over all d
+      coordinates of the source, the key is still its last r coordinates.
+      Its source gradient is Appendix B.3, Eq. 22: the radial term has
+      divisor d and reaches every coordinate.  For r = d it coincides with
+      the default norm="slice".
   R5  LR with H > 1: q in R^r is split into H slices of width r/H; head h
       scores the h-th slice of the normalised r-wide key and mixes the h-th
       d/H slice of the value.  Requires H | r.  r = d gives MHAR.
@@ -65,11 +77,25 @@ def inv_rms(key: np.ndarray, eps: float = EPS) -> np.ndarray:
     return 1.0 / np.sqrt(np.mean(key * key, axis=-1) + eps)
 
 
-def route_forward(sources, q, heads: int, r: int, eps: float = EPS):
+def source_inv_rms(src, r: int, eps: float = EPS, norm: str = "slice"):
+    """Inverse RMS of each source: over its r key coordinates (norm="slice",
+    Eq. 11 / Eq. 13 slice) or over all d coordinates (norm="full", Eq. 13
+    control)."""
+    if norm == "slice":
+        return inv_rms(key_slice(src, r), eps)
+    if norm == "full":
+        return inv_rms(src, eps)
+    raise ValueError(f"norm must be 'slice' or 'full', got {norm!r}")
+
+
+def route_forward(sources, q, heads: int, r: int, eps: float = EPS, gain=None,
+                  norm: str = "slice"):
     """One routing read.
 
     sources: [N, T, d]  (committed rows, then a transient source if any)
     q:       [r]        static query of the site
+    gain:    [r] or None  RMSNorm gain on the normalised key (R3)
+    norm:    "slice" (RMS over the key) or "full" (RMS over all d, R7)
     Returns out [T, d], alpha [N, T, H], lse [T, H].
     """
     src = np.asarray(sources, dtype=np.float64)
@@ -78,7 +104,9 @@ def route_forward(sources, q, heads: int, r: int, eps: float = EPS):
     H = heads
     kk, kv = r // H, d // H
     key = key_slice(src, r)                                   # [N, T, r]
-    khat = key * inv_rms(key, eps)[..., None]                 # RMSNorm(key)
+    khat = key * source_inv_rms(src, r, eps, norm)[..., None]  # RMSNorm(key)
+    if gain is not None:
+        khat = khat * np.asarray(gain, dtype=np.float64)
     logits = np.einsum("nthk,hk->nth", khat.reshape(N, T, H, kk), q.reshape(H, kk))
     m = logits.max(axis=0)
     lse = m + np.log(np.exp(logits - m).sum(axis=0))
@@ -87,10 +115,11 @@ def route_forward(sources, q, heads: int, r: int, eps: float = EPS):
     return out, alpha, lse
 
 
-def route_backward(sources, q, heads: int, r: int, dout, eps: float = EPS):
+def route_backward(sources, q, heads: int, r: int, dout, eps: float = EPS, gain=None,
+                   norm: str = "slice"):
     """Gradient of <dout, out> for one routing read.
 
-    Returns dsources [N, T, d] and dq [r].
+    Returns dsources [N, T, d] and dq [r]; with a gain also dgain [r].
     """
     src = np.asarray(sources, dtype=np.float64)
     q = np.asarray(q, dtype=np.float64)
@@ -98,31 +127,39 @@ def route_backward(sources, q, heads: int, r: int, dout, eps: float = EPS):
     N, T, d = src.shape
     H = heads
     kk, kv = r // H, d // H
-    _, alpha, _ = route_forward(src, q, H, r, eps)
+    g = np.ones(r) if gain is None else np.asarray(gain, dtype=np.float64)
+    _, alpha, _ = route_forward(src, q, H, r, eps, gain, norm)
     key = key_slice(src, r)
-    rinv = inv_rms(key, eps)                                  # [N, T]
-    khat = key * rinv[..., None]
+    rinv = source_inv_rms(src, r, eps, norm)                  # [N, T]
+    khat = key * rinv[..., None]                              # normalised key, before the gain
 
     # Softmax coupling: P, S and the logit gradient (Appendix E, Figure 10).
     P = np.einsum("thk,nthk->nth", dout.reshape(T, H, kv), src.reshape(N, T, H, kv))
     S = np.einsum("nth,nth->th", alpha, P)
     dlogit = alpha * (P - S)
 
-    # Query gradient: logits are q_h . khat_[h].
-    dq = np.einsum("nth,nthk->hk", dlogit, khat.reshape(N, T, H, kk)).reshape(r)
+    # Query and gain gradients: logits are sum_j q_j g_j khat_j over head h.
+    dqg = np.einsum("nth,nthk->hk", dlogit, khat.reshape(N, T, H, kk)).reshape(r)
+    dq = g * dqg
+    dgain = q * dqg
 
-    # Key path through the RMSNorm (Eq. 21 / Appendix E closed form).
-    dkhat = (dlogit[..., None] * q.reshape(H, kk)).reshape(N, T, r)
-    proj = np.einsum("ntj,ntj->nt", dkhat, key)
-    dkey = rinv[..., None] * dkhat - (rinv ** 3 / r)[..., None] * proj[..., None] * key
-
-    # Value path: w_{n,h} dout_h on the h-th slice.
-    dsrc = (alpha[..., None] * dout.reshape(T, H, kv)).reshape(N, T, d)
-    dsrc[..., d - r:] += dkey
+    # Key path through the RMSNorm (Eq. 21 / Eq. 22 / Appendix E closed form),
+    # driven by dk = dlogit * (q * g) on the key coordinates.
+    dk = (dlogit[..., None] * (q * g).reshape(H, kk)).reshape(N, T, r)
+    proj = np.einsum("ntj,ntj->nt", dk, key)
+    dsrc = (alpha[..., None] * dout.reshape(T, H, kv)).reshape(N, T, d)  # value path
+    dsrc[..., d - r:] += rinv[..., None] * dk
+    if norm == "slice":   # RMS over the r key coordinates: radial term on the key
+        dsrc[..., d - r:] -= (rinv ** 3 / r)[..., None] * proj[..., None] * key
+    else:                 # RMS over all d coordinates: radial term on the whole source
+        dsrc -= (rinv ** 3 / d)[..., None] * proj[..., None] * src
+    if gain is not None:
+        return dsrc, dq, dgain
     return dsrc, dq
 
 
-def run_schedule(rows, extras, queries, douts, nsrc, heads: int, r: int, eps: float = EPS):
+def run_schedule(rows, extras, queries, douts, nsrc, heads: int, r: int, eps: float = EPS,
+                 gains=None, norm: str = "slice"):
     """Forward every site in order, then backward every site in reverse.
 
     rows:    [R, T, d]   committed bank rows
@@ -130,11 +167,14 @@ def run_schedule(rows, extras, queries, douts, nsrc, heads: int, r: int, eps: fl
     queries: [S, r]
     douts:   [S, T, d]   upstream gradient of each site's output
     nsrc:    S ints; site s reads rows [0, nsrc[s]) (then its extra, if any)
+    gains:   None or [S, r] RMSNorm gain of each site (R3)
+    norm:    "slice" or "full" (R7)
 
     The loss whose gradients are returned is sum_s <dout_s, out_s>, with every
     bank row, query and transient source an independent input.
     Returns a dict: out [S,T,d], alpha (list of [N_s,T,H]), lse [S,T,H],
-    dbank [R,T,d], dq [S,r], dextra (list of None or [T,d]).
+    dbank [R,T,d], dq [S,r], dextra (list of None or [T,d]) and, with gains,
+    dgain [S,r].
     """
     rows = np.asarray(rows, dtype=np.float64)
     R, T, d = rows.shape
@@ -142,7 +182,8 @@ def run_schedule(rows, extras, queries, douts, nsrc, heads: int, r: int, eps: fl
     outs, alphas, lses = [], [], []
     for s in range(S):
         src = _site_sources(rows, extras[s], nsrc[s])
-        o, a, l = route_forward(src, queries[s], heads, r, eps)
+        g = None if gains is None else gains[s]
+        o, a, l = route_forward(src, queries[s], heads, r, eps, g, norm)
         outs.append(o)
         alphas.append(a)
         lses.append(l)
@@ -150,9 +191,14 @@ def run_schedule(rows, extras, queries, douts, nsrc, heads: int, r: int, eps: fl
     dbank = np.zeros_like(rows)
     dq = np.zeros((S, r))
     dextra = [None] * S
+    dgain = None if gains is None else np.zeros((S, r))
     for s in reversed(range(S)):
         src = _site_sources(rows, extras[s], nsrc[s])
-        dsrc, dq[s] = route_backward(src, queries[s], heads, r, douts[s], eps)
+        if gains is None:
+            dsrc, dq[s] = route_backward(src, queries[s], heads, r, douts[s], eps, None, norm)
+        else:
+            dsrc, dq[s], dgain[s] = route_backward(src, queries[s], heads, r, douts[s], eps,
+                                                   gains[s], norm)
         n = nsrc[s]
         dbank[:n] += dsrc[:n]
         if extras[s] is not None:
@@ -164,6 +210,7 @@ def run_schedule(rows, extras, queries, douts, nsrc, heads: int, r: int, eps: fl
         "dbank": dbank,
         "dq": dq,
         "dextra": dextra,
+        **({} if gains is None else {"dgain": dgain}),
     }
 
 

@@ -63,13 +63,19 @@ def test_worked_example_exact(case):
     src = num(case["sources"])[:, None, :]          # [N, T=1, d]
     q = num(case["q"])
     H, r = case["heads"], case["r"]
-    out, alpha, lse = route_forward(src, q, H, r, eps=0.0)
+    gain = num(case["gain"]) if "gain" in case else None
+    norm = case.get("norm", "slice")
+    out, alpha, lse = route_forward(src, q, H, r, eps=0.0, gain=gain, norm=norm)
     np.testing.assert_allclose(out[0], num(case["out"]), rtol=0, atol=1e-13)
     np.testing.assert_allclose(alpha[:, 0, :], num(case["alpha"]), rtol=0, atol=1e-13)
     np.testing.assert_allclose(lse[0], num(case["lse"]), rtol=0, atol=1e-13)
-    dsrc, dq = route_backward(src, q, H, r, num(case["dout"])[None, :], eps=0.0)
+    res = route_backward(src, q, H, r, num(case["dout"])[None, :], eps=0.0, gain=gain,
+                         norm=norm)
+    dsrc, dq = res[0], res[1]
     np.testing.assert_allclose(dq, num(case["dq"]), rtol=0, atol=1e-13)
     np.testing.assert_allclose(dsrc[:, 0, :], num(case["dsources"]), rtol=0, atol=1e-13)
+    if gain is not None:
+        np.testing.assert_allclose(res[2], num(case["dgain"]), rtol=0, atol=1e-13)
 
 
 @pytest.mark.parametrize("case", load_cases(), ids=lambda c: c["name"])
@@ -77,7 +83,9 @@ def test_worked_example_default_eps_is_close(case):
     # eps = 1e-6 rescales unit-RMS keys by (1 + 1e-6)^(-1/2): a ~1e-6 relative change.
     src = num(case["sources"])[:, None, :]
     q = num(case["q"])
-    out, alpha, _ = route_forward(src, q, case["heads"], case["r"])
+    gain = num(case["gain"]) if "gain" in case else None
+    out, alpha, _ = route_forward(src, q, case["heads"], case["r"], gain=gain,
+                                  norm=case.get("norm", "slice"))
     np.testing.assert_allclose(out[0], num(case["out"]), rtol=0, atol=1e-5)
     np.testing.assert_allclose(alpha[:, 0, :], num(case["alpha"]), rtol=0, atol=1e-5)
 
@@ -284,39 +292,49 @@ def test_zero_row_is_finite():
 # --------------------------------------------------------------------------
 # I6: the backward of the whole schedule equals central finite differences of
 # L = sum_s <dout_s, out_s>, for every bank element, query and transient source.
-def _schedule_loss(rows, extras, queries, douts, nsrc, H, r):
+def _schedule_loss(rows, extras, queries, douts, nsrc, H, r, gains=None, norm="slice"):
     total = 0.0
     for s in range(len(nsrc)):
         src = rows[: nsrc[s]]
         if extras[s] is not None:
             src = np.concatenate([src, extras[s][None]], 0)
-        out, _, _ = route_forward(src, queries[s], H, r)
+        g = None if gains is None else gains[s]
+        out, _, _ = route_forward(src, queries[s], H, r, gain=g, norm=norm)
         total += float(np.sum(douts[s] * out))
     return total
 
 
-@pytest.mark.parametrize("kind", ["full", "lowrank_block"])
+# kind -> (r, nsrc, has_extra, with gains, norm)
+FD_CASES = {
+    "full": (8, [1, 2, 3], [0, 0, 0], False, "slice"),
+    "lowrank_block": (4, [1, 1, 2, 3], [1, 1, 1, 0], False, "slice"),
+    "full_gain": (8, [1, 2, 3], [0, 0, 0], True, "slice"),
+    "lowrank_block_gain": (4, [1, 1, 2, 3], [1, 1, 1, 0], True, "slice"),
+    "lowrank_block_full_rms": (4, [1, 1, 2, 3], [1, 1, 1, 0], False, "full"),
+    "lowrank_block_gain_full_rms": (4, [1, 1, 2, 3], [1, 1, 1, 0], True, "full"),
+}
+
+
+@pytest.mark.parametrize("kind", list(FD_CASES))
 def test_schedule_backward_matches_finite_differences(kind):
     rng = np.random.default_rng(11)
     T, d, H = 2, 8, 2
-    if kind == "full":
-        r, nsrc, has_extra = 8, [1, 2, 3], [0, 0, 0]
-    else:
-        r, nsrc, has_extra = 4, [1, 1, 2, 3], [1, 1, 1, 0]
+    r, nsrc, has_extra, with_gain, norm = FD_CASES[kind]
     R, S = max(nsrc), len(nsrc)
     rows = rng.standard_normal((R, T, d)) * rng.uniform(0.5, 2.0, (R, 1, 1))
     extras = [rng.standard_normal((T, d)) if e else None for e in has_extra]
     queries = rng.standard_normal((S, r)) * 0.8
     douts = rng.standard_normal((S, T, d))
-    res = run_schedule(rows, extras, queries, douts, nsrc, H, r)
+    gains = rng.uniform(0.5, 1.5, (S, r)) if with_gain else None
+    res = run_schedule(rows, extras, queries, douts, nsrc, H, r, gains=gains, norm=norm)
     h = 1e-6
 
     def fd(arr, idx):
         old = arr[idx]
         arr[idx] = old + h
-        lp = _schedule_loss(rows, extras, queries, douts, nsrc, H, r)
+        lp = _schedule_loss(rows, extras, queries, douts, nsrc, H, r, gains, norm)
         arr[idx] = old - h
-        lm = _schedule_loss(rows, extras, queries, douts, nsrc, H, r)
+        lm = _schedule_loss(rows, extras, queries, douts, nsrc, H, r, gains, norm)
         arr[idx] = old
         return (lp - lm) / (2 * h)
 
@@ -336,6 +354,13 @@ def test_schedule_backward_matches_finite_differences(kind):
         for idx in np.ndindex(e.shape):
             ge[idx] = fd(e, idx)
         np.testing.assert_allclose(res["dextra"][s], ge, rtol=1e-6, atol=1e-8)
+    if gains is None:
+        assert "dgain" not in res
+    else:
+        gg = np.zeros_like(gains)
+        for idx in np.ndindex(gains.shape):
+            gg[idx] = fd(gains, idx)
+        np.testing.assert_allclose(res["dgain"], gg, rtol=1e-6, atol=1e-8)
 
 
 def test_gradient_decomposition_value_plus_routing_feedback():
@@ -363,3 +388,87 @@ def test_gradient_decomposition_value_plus_routing_feedback():
             gz[j] = (score(xp) - score(xm)) / 2e-6
         expect = alpha[i, 0, 0] * g[0] + alpha[i, 0, 0] * float(g[0] @ (src[i, 0] - out[0])) * gz
         np.testing.assert_allclose(dsrc[i, 0], expect, rtol=1e-6, atol=1e-8)
+
+
+# --------------------------------------------------------------------------
+# I12: a routing RMSNorm gain folds into the static query ("Low-Rank Attention
+# Residuals", Appendix B.1, Eq. 17): reading with (q, g) equals reading with
+# q * g and no gain, and a unit gain changes nothing.
+def test_gain_folds_into_query():
+    rng = np.random.default_rng(13)
+    N, T, d, r, H = 5, 4, 16, 8, 2
+    src = rng.standard_normal((N, T, d))
+    q = rng.standard_normal(r)
+    g = rng.uniform(0.25, 2.0, r)
+    dout = rng.standard_normal((T, d))
+    for norm in ("slice", "full"):
+        a = route_forward(src, q, H, r, gain=g, norm=norm)
+        b = route_forward(src, q * g, H, r, norm=norm)
+        for x, y in zip(a, b):
+            np.testing.assert_allclose(x, y, rtol=0, atol=1e-13)
+        dsrc_g, dq_g, dg = route_backward(src, q, H, r, dout, gain=g, norm=norm)
+        dsrc_f, dq_f = route_backward(src, q * g, H, r, dout, norm=norm)
+        np.testing.assert_allclose(dsrc_g, dsrc_f, rtol=0, atol=1e-13)
+        # chain rule through the product q * g: d/dq = g * d/d(qg), d/dg = q * d/d(qg)
+        np.testing.assert_allclose(dq_g, g * dq_f, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(dg, q * dq_f, rtol=0, atol=1e-13)
+        one = route_backward(src, q, H, r, dout, gain=np.ones(r), norm=norm)
+        plain = route_backward(src, q, H, r, dout, norm=norm)
+        np.testing.assert_array_equal(one[0], plain[0])
+        np.testing.assert_array_equal(one[1], plain[1])
+
+
+# I13: with r = d the full-width-RMS control is the default read ("Low-Rank
+# Attention Residuals", Eq. 13: both constructions coincide when P_r = I).
+def test_full_rms_control_equals_slice_at_full_width():
+    rng = np.random.default_rng(14)
+    src = rng.standard_normal((4, 3, 12))
+    q = rng.standard_normal(12)
+    dout = rng.standard_normal((3, 12))
+    for x, y in zip(route_forward(src, q, 3, 12, norm="full"), route_forward(src, q, 3, 12)):
+        np.testing.assert_array_equal(x, y)
+    a = route_backward(src, q, 3, 12, dout, norm="full")
+    b = route_backward(src, q, 3, 12, dout)
+    np.testing.assert_allclose(a[0], b[0], rtol=0, atol=1e-14)
+    np.testing.assert_array_equal(a[1], b[1])
+    with pytest.raises(ValueError):
+        route_forward(src, q, 3, 12, norm="per-head")
+
+
+# I14: outside the key coordinates the control's gradient is the value
+# gradient plus a term parallel to the source's own unselected coordinates
+# ("Low-Rank Attention Residuals", Corollary 2.2, Eq. 22); a perturbation
+# there that keeps the full-width norm leaves the weights unchanged, one
+# that changes the norm moves them (unlike the slice norm, Corollary 2.1).
+def test_full_rms_control_radial_dependence_outside_slice():
+    rng = np.random.default_rng(15)
+    N, T, d, r, H = 4, 3, 12, 4, 2
+    src = rng.standard_normal((N, T, d))
+    q = rng.standard_normal(r)
+    dout = rng.standard_normal((T, d))
+    out, alpha, _ = route_forward(src, q, H, r, norm="full")
+    dsrc, _ = route_backward(src, q, H, r, dout, norm="full")
+    kv = d // H
+    outside = d - r
+    value = np.stack([alpha[:, :, j // kv] * dout[None, :, j] for j in range(outside)], -1)
+    rest = dsrc[..., :outside] - value                       # [N, T, d - r]
+    x = src[..., :outside]
+    for n in range(N):
+        for t in range(T):
+            c = float(rest[n, t] @ x[n, t]) / float(x[n, t] @ x[n, t])
+            np.testing.assert_allclose(rest[n, t], c * x[n, t], rtol=0, atol=1e-12)
+            assert abs(c) > 1e-6
+    # a norm-preserving rotation of the unselected coordinates leaves alpha alone
+    Qm, _ = np.linalg.qr(rng.standard_normal((outside, outside)))
+    src2 = src.copy()
+    src2[1, :, :outside] = src[1, :, :outside] @ Qm.T
+    _, alpha2, _ = route_forward(src2, q, H, r, norm="full")
+    np.testing.assert_allclose(alpha2, alpha, rtol=0, atol=1e-14)
+    # scaling them changes the full-width norm and so the weights
+    src3 = src.copy()
+    src3[1, :, :outside] *= 3.0
+    _, alpha3, _ = route_forward(src3, q, H, r, norm="full")
+    _, alpha3s, _ = route_forward(src3, q, H, r, norm="slice")
+    _, alpha_s, _ = route_forward(src, q, H, r, norm="slice")
+    assert np.abs(alpha3 - alpha).max() > 1e-3
+    np.testing.assert_allclose(alpha3s, alpha_s, rtol=0, atol=1e-15)
