@@ -11,8 +11,9 @@
  * (e.g. the partial sum of the current block), and for every token and head h
  *
  *   key_n    = last r coordinates of s_n            (r == d: the whole source)
- *   khat_n   = key_n * (mean(key_n^2) + eps)^(-1/2) (RMSNorm over the key, no gain)
- *   l_{n,h}  = q_[h] . khat_n[h]                    (h-th r/H slice)
+ *   khat_n   = key_n * (mean(key_n^2) + eps)^(-1/2) (RMSNorm over the key)
+ *   l_{n,h}  = q_[h] . (g * khat_n)[h]              (h-th r/H slice; g = 1
+ *                                                    unless gains are set)
  *   a_{.,h}  = softmax over the sources of l_{.,h}
  *   out_[h]  = sum_n a_{n,h} s_n[h]                 (h-th d/H slice of the value)
  *
@@ -24,8 +25,19 @@
  * Residuals" Appendix E (backward paragraph, Figure 10); "Low-Rank Attention
  * Residuals" Appendix B.3 (Eq. 20-21).  Readings of open points: the RMS is
  * over the whole key and then sliced per head; eps sits inside the square
- * root; there is no norm gain; with r < d and H > 1 head h scores the h-th
- * r/H slice of the normalised key and mixes the h-th d/H slice of the value.
+ * root; with r < d and H > 1 head h scores the h-th r/H slice of the
+ * normalised key and mixes the h-th d/H slice of the value.
+ *
+ * Two options of the same read:
+ *   - a routing RMSNorm gain g_s in R^r per site multiplying the normalised
+ *     key ("Multi-Head Attention Residuals", Appendix E, Figures 9-10); it
+ *     folds into the query for the forward ("Low-Rank Attention Residuals",
+ *     Appendix B.1, Eq. 17) and its gradient is returned
+ *     (attnres_bank_set_gains);
+ *   - the full-width-RMS control: the mean of squares is taken over all d
+ *     coordinates of the source while the key stays its last r
+ *     ("Low-Rank Attention Residuals", section 4.4, Eq. 13 control; its
+ *     source gradient is Appendix B.3, Eq. 22) (attnres_config_t.norm).
  *
  * Ownership and memory
  * --------------------
@@ -47,6 +59,7 @@
  * -----------------------------------------------------------------------
  *   attnres_bank_reset
  *   attnres_bank_set_queries            (the site schedule and its queries)
+ *   attnres_bank_set_gains              (optional: per-site norm gains)
  *   for each site s = 0..S-1:           append rows until nsrc[s] are committed,
  *     attnres_bank_append ...           then
  *     attnres_route_fwd(s)
@@ -92,6 +105,12 @@ typedef enum {
 
 typedef enum { ATTNRES_F32 = 0, ATTNRES_BF16 = 1 } attnres_dtype_t;
 
+/* Width of the routing RMSNorm ("Low-Rank Attention Residuals", Eq. 13). */
+typedef enum {
+  ATTNRES_NORM_SLICE = 0, /* mean of squares over the r key coordinates (Eq. 11) */
+  ATTNRES_NORM_FULL = 1   /* over all d coordinates, key still the last r (control) */
+} attnres_norm_t;
+
 typedef struct {
   int64_t tokens;    /* T: tokens per microbatch (batch x sequence, flattened), >= 0 */
   int32_t d;         /* value width */
@@ -101,6 +120,7 @@ typedef struct {
   int32_t max_sites; /* routing sites per microbatch */
   int32_t dtype;     /* attnres_dtype_t: storage dtype */
   float eps;         /* RMSNorm epsilon, inside the square root (1e-6) */
+  int32_t norm;      /* attnres_norm_t; r == d makes both the same */
 } attnres_config_t;
 
 /* Bytes of device workspace a bank with this configuration needs (0 if the
@@ -111,7 +131,8 @@ size_t attnres_workspace_bytes(const attnres_config_t* cfg);
  * Shapes supported by this build: with c = 16 / sizeof(storage dtype)
  * elements per 16-byte chunk, d, r, d/H and r/H must be multiples of c;
  * otherwise ATTNRES_ERR_UNSUPPORTED.  H | d, H | r, 1 <= r <= d, heads >= 1,
- * max_rows >= 1, max_sites >= 1, eps > 0, else ATTNRES_ERR_INVALID.
+ * max_rows >= 1, max_sites >= 1, eps > 0, norm an attnres_norm_t, else
+ * ATTNRES_ERR_INVALID.
  * workspace_bytes must be at least attnres_workspace_bytes(cfg). */
 attnres_status_t attnres_bank_create(const attnres_config_t* cfg, void* rows, float* drows,
                                      void* dout_rows, void* workspace, size_t workspace_bytes,
@@ -132,13 +153,31 @@ attnres_status_t attnres_bank_reset(attnres_bank_t bank);
  *   queries          device [n_sites, r] storage dtype; must stay unchanged
  *                    until the backward of site 0 has run
  * Each later append scores its row against every registered query that will
- * read it, so the route itself streams the bank only to mix it. */
+ * read it, so the route itself streams the bank only to mix it.  Clears any
+ * gains of an earlier microbatch. */
 attnres_status_t attnres_bank_set_queries(attnres_bank_t bank, int32_t n_sites,
                                           const int32_t* nsrc, const int32_t* has_extra,
                                           const void* queries);
 
+/* Routing RMSNorm gains of this microbatch's sites ("Multi-Head Attention
+ * Residuals", Appendix E, Figures 9-10: the normalised key times g).  Call
+ * after attnres_bank_set_queries and before the first append.
+ *   gains   device float32 [n_sites, r]: g_s of site s, or NULL for g = 1
+ *           (clears earlier gains; dgains is then ignored)
+ *   dgains  device float32 [n_sites, r]: attnres_route_bwd(s) overwrites row
+ *           s with the gradient of g_s; required when gains is not NULL
+ * Enqueues one small kernel on `stream` that folds the gains into the
+ * queries (effective query q_s * g_s, "Low-Rank Attention Residuals",
+ * Eq. 17) into the workspace, from the current contents of `queries` and
+ * `gains`; later changes to either are not seen until the next call.  The
+ * query gradient attnres_route_bwd returns is then g_s * dL/d(q_s g_s) and
+ * the gain gradient q_s * dL/d(q_s g_s). */
+attnres_status_t attnres_bank_set_gains(attnres_bank_t bank, const float* gains, float* dgains,
+                                        attnres_stream_t stream);
+
 /* Commit the next bank row n (returned in *row_out if not NULL) and cache its
- * per-token inverse RMS over the key coordinates and its per-head logits
+ * per-token inverse RMS (over the key coordinates, or over all d with
+ * ATTNRES_NORM_FULL) and its per-head logits
  * ("key projections") against every registered query of a site that reads
  * row n.  src: device [T, d] storage dtype copied into row n, or NULL when the
  * caller already wrote row n of `rows`.  The shared bank is written once per
@@ -226,7 +265,7 @@ const char* attnres_last_error(void);
 /* Destroy the handle (the caller's buffers are untouched).  NULL is ignored. */
 void attnres_bank_destroy(attnres_bank_t bank);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2 (1 had no norm field and no gains). */
 int32_t attnres_abi_version(void);
 
 #ifdef __cplusplus

@@ -3,13 +3,16 @@
 Recipe (one numpy PCG64 stream per item, so any row, query or gradient can be
 regenerated on its own and in any order):
 
-  root = SeedSequence(seed); groups = root.spawn(5), in this order:
+  root = SeedSequence(seed); groups = root.spawn(6), in this order:
     0 scales   - one stream; c_n ~ U(0.5, 2) per bank row (all 1 if the
                  workload has no per-source scale)
     1 rows     - spawn(rows): bank row n = c_n * Z, Z ~ N(0, 1), shape [T, d]
     2 extras   - spawn(sites): transient source of site s ~ N(0, 1), [T, d]
     3 queries  - spawn(sites): q_s ~ N(0, 0.02^2), shape [r]
     4 douts    - spawn(sites): upstream gradient of site s ~ N(0, 1), [T, d]
+    5 gains    - spawn(sites): routing RMSNorm gain of site s ~ U(0.5, 1.5),
+                 shape [r], float32 (a parameter, not rounded to the storage
+                 dtype); drawn only for workloads with gains
 
 Values are drawn in float32 and then rounded to the storage dtype (bf16 with
 round-to-nearest-even), so every consumer sees exactly the same numbers.
@@ -51,12 +54,13 @@ class Inputs:
     def __init__(self, w: Workload):
         self.w = w
         root = np.random.SeedSequence(w.seed)
-        g_scale, g_rows, g_extra, g_query, g_dout = root.spawn(5)
+        g_scale, g_rows, g_extra, g_query, g_dout, g_gain = root.spawn(6)
         self._scale_seed = g_scale
         self._row_seeds = g_rows.spawn(max(w.rows, 1))
         self._extra_seeds = g_extra.spawn(max(w.sites, 1))
         self._query_seeds = g_query.spawn(max(w.sites, 1))
         self._dout_seeds = g_dout.spawn(max(w.sites, 1))
+        self._gain_seeds = g_gain.spawn(max(w.sites, 1))
         rng = np.random.Generator(np.random.PCG64(self._scale_seed))
         c = rng.uniform(0.5, 2.0, size=max(w.rows, 1))
         self.scales = c if w.source_scale else np.ones_like(c)
@@ -110,3 +114,16 @@ class Inputs:
 
     def queries(self) -> np.ndarray:
         return np.stack([self.query(s) for s in range(self.w.sites)])
+
+    def gain(self, s: int):
+        """Routing RMSNorm gain of site s (float32 [r]), or None without gains."""
+        if not self.w.gains:
+            return None
+        rng = np.random.Generator(np.random.PCG64(self._gain_seeds[s]))
+        return rng.uniform(0.5, 1.5, size=self.w.r).astype(np.float32)
+
+    def gains(self):
+        """[S, r] float32 gains of every site, or None without gains."""
+        if not self.w.gains:
+            return None
+        return np.stack([self.gain(s) for s in range(self.w.sites)])

@@ -37,6 +37,8 @@ class Workload:
     source_scale: bool  # bank row n is c_n * N(0,1) with c_n ~ U(0.5, 2)
     eps: float = 1e-6
     seed: int = 0
+    norm: str = "slice"  # "slice": RMS over the r key coordinates; "full": over all d
+    gains: bool = False  # each site has a routing RMSNorm gain g_s in R^r
 
     @property
     def sites(self) -> int:
@@ -63,9 +65,16 @@ class Workload:
         return replace(self, nsrc=self.nsrc[:sites], extra=self.extra[:sites],
                        name=f"{self.name}@S{sites}")
 
+    def with_norm(self, norm: str) -> "Workload":
+        return replace(self, norm=norm, name=f"{self.name}+{norm}rms")
+
+    def with_gains(self) -> "Workload":
+        return replace(self, gains=True, name=f"{self.name}+gain")
+
     def describe(self) -> str:
         return (f"{self.name}: T={self.tokens} d={self.d} r={self.r} H={self.heads} "
-                f"sites={self.sites} rows={self.rows} dtype={self.dtype}")
+                f"sites={self.sites} rows={self.rows} dtype={self.dtype} norm={self.norm} "
+                f"gains={int(self.gains)}")
 
 
 def full_schedule(layers: int):

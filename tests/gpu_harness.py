@@ -40,7 +40,7 @@ def run_gpu(w, inp: Inputs, tokens=None, dout_tokens=None, bank=None, backward=T
 
     S, R, T = w.sites, w.rows, w.tokens
     if bank is None:
-        bank = Bank(T, w.d, w.r, w.heads, R, S, w.dtype, w.eps)
+        bank = Bank(T, w.d, w.r, w.heads, R, S, w.dtype, w.eps, norm=w.norm)
     fill_device(bank.rows, inp, "row", range(R))
     queries = to_device(inp.queries(), w.dtype)
     if dout_tokens is None:
@@ -58,10 +58,12 @@ def run_gpu(w, inp: Inputs, tokens=None, dout_tokens=None, bank=None, backward=T
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     outs = torch.empty((S, T, w.d), dtype=tdt, device="cuda")
     dqs = torch.empty((S, w.r), dtype=torch.float32, device="cuda")
+    gains = None if inp.gains() is None else to_device(inp.gains(), "f32")
+    dgains = None if gains is None else torch.empty((S, w.r), dtype=torch.float32, device="cuda")
     dex = [torch.empty((T, w.d), dtype=torch.float32, device="cuda") if e is not None else None
            for e in extras]
     run_microbatch(bank, list(w.nsrc), list(w.extra), queries, outs, dqs, extras, dex,
-                   backward=backward)
+                   backward=backward, gains=gains, dgains=dgains)
     torch.cuda.synchronize()
     idx = None if tokens is None else torch.as_tensor(np.asarray(tokens), device="cuda")
 
@@ -80,6 +82,8 @@ def run_gpu(w, inp: Inputs, tokens=None, dout_tokens=None, bank=None, backward=T
         res["dbank"] = from_device(pick(bank.drows[:R], 1))
         res["dq"] = from_device(dqs)
         res["dextra"] = [None if t is None else from_device(pick(t, 0)) for t in dex]
+        if dgains is not None:
+            res["dgain"] = from_device(dgains)
     res["_bank"] = bank
     return res
 
@@ -99,7 +103,10 @@ def run_ref(w, inp: Inputs, tokens=None, dout_tokens=None):
             g[~m] = 0.0
         douts.append(g[sel].astype(np.float64))
     q = inp.queries().astype(np.float64)
-    return run_schedule(rows, extras, q, np.stack(douts), list(w.nsrc), w.heads, w.r, w.eps)
+    gains = inp.gains()
+    gains = None if gains is None else gains.astype(np.float64)
+    return run_schedule(rows, extras, q, np.stack(douts), list(w.nsrc), w.heads, w.r, w.eps,
+                        gains=gains, norm=w.norm)
 
 
 def compare(w, got, ref, check_dq=True, label=""):
@@ -114,6 +121,8 @@ def compare(w, got, ref, check_dq=True, label=""):
         err["dbank"] = max_rel(got["dbank"], ref["dbank"])
         if check_dq:
             err["dq"] = max_rel(got["dq"], ref["dq"])
+            if "dgain" in ref:
+                err["dgain"] = max_rel(got["dgain"], ref["dgain"])
         ex = [(a, b) for a, b in zip(got["dextra"], ref["dextra"]) if b is not None]
         if ex:
             err["dextra"] = max(max_rel(a, b) for a, b in ex)

@@ -34,7 +34,7 @@ def test_header_declarations_are_exported(lib):
     assert set(names) == set(A.EXPORTS)
     for n in names:
         assert getattr(lib, n) is not None
-    assert A.attnres_abi_version() == 1
+    assert A.attnres_abi_version() == 2
 
 
 def cfg(**kw):
@@ -61,6 +61,7 @@ def fake_bank(c):
     (dict(tokens=-1), A.ATTNRES_ERR_INVALID),
     (dict(eps=0.0), A.ATTNRES_ERR_INVALID),
     (dict(max_rows=0), A.ATTNRES_ERR_INVALID),
+    (dict(norm=2), A.ATTNRES_ERR_INVALID),
 ])
 def test_bad_config_rejected(lib, kw, status):
     c = cfg(**kw)
@@ -141,5 +142,23 @@ def test_misaligned_queries_rejected(lib):
         with pytest.raises(A.AttnResError) as e:
             A.attnres_bank_set_queries(b, [1], None, FAKE + 2)
         assert e.value.status == A.ATTNRES_ERR_INVALID
+    finally:
+        A.attnres_bank_destroy(b)
+
+
+def test_set_gains_order_and_arguments(lib):
+    b = fake_bank(cfg(r=640, norm=A.ATTNRES_NORM_FULL))
+    try:
+        with pytest.raises(A.AttnResError) as e:  # before set_queries
+            A.attnres_bank_set_gains(b, FAKE, FAKE, stream=0)
+        assert e.value.status == A.ATTNRES_ERR_ORDER
+        A.attnres_bank_set_queries(b, [1, 2], None, FAKE)
+        with pytest.raises(A.AttnResError) as e:  # gains without a gradient buffer
+            A.attnres_bank_set_gains(b, FAKE, None, stream=0)
+        assert e.value.status == A.ATTNRES_ERR_INVALID
+        with pytest.raises(A.AttnResError) as e:
+            A.attnres_bank_set_gains(b, FAKE + 4, FAKE, stream=0)
+        assert e.value.status == A.ATTNRES_ERR_INVALID
+        A.attnres_bank_set_gains(b, None, None, stream=0)  # no gains: nothing to launch
     finally:
         A.attnres_bank_destroy(b)

@@ -8,7 +8,7 @@ transient-source gradients; softmax weights within 1e-3 absolute.
 import numpy as np
 import pytest
 
-from oracle import inv_rms, key_slice
+from oracle import source_inv_rms
 from synth import Inputs, get_workload, sample_tokens
 
 from gpu_harness import compare, log, max_rel, run_gpu, run_ref
@@ -21,16 +21,34 @@ REDUCED = ["tiny", "tiny@T37", "mhar100m@T200", "mhar350m@T100", "mhar1b@T77",
            "mhar1b@T100", "lr_h1@T9", "lr_h8@T9", "lr_h8@T12"]
 
 
+# Routing RMSNorm gains and the full-width-RMS control, on every append and
+# finalize path: fp32 (vector ALU), bf16 matrix-core append (high + low query
+# parts), bf16 vector-ALU append (r/H = 24; LR with H = 1), LR keys with H = 8.
+VARIANTS = ["tiny+gain", "tiny@T37+gain", "mhar100m@T200+gain", "bf16_kk24+gain",
+            "lr_h1@T9+fullrms", "lr_h8@T9+fullrms", "lr_h8@T12+gain+fullrms",
+            "lr_h1@T9+gain+fullrms", "lr_tiny_f32+fullrms", "lr_tiny_f32+gain+fullrms"]
+
+
 def _workload(name):
-    if name == "bf16_kk24":
+    base, *opts = name.split("+")
+    if base == "bf16_kk24":
         # r/H = 24 is not a multiple of 32: exercises the vector-ALU append
         from synth import Workload, full_schedule
         nsrc, extra = full_schedule(3)
-        return Workload("bf16_kk24", 50, 192, 8, 192, nsrc, extra, "bf16", True)
-    return get_workload(name)
+        w = Workload("bf16_kk24", 50, 192, 8, 192, nsrc, extra, "bf16", True)
+    elif base == "lr_tiny_f32":
+        # fp32 block routing with keys on the last 32 of 64 coordinates
+        from synth import Workload, block_schedule
+        nsrc, extra = block_schedule(4)
+        w = Workload("lr_tiny_f32", 37, 64, 2, 32, nsrc, extra, "f32", True)
+    else:
+        w = get_workload(base)
+    for o in opts:
+        w = w.with_gains() if o == "gain" else w.with_norm("full")
+    return w
 
 
-@pytest.mark.parametrize("name", REDUCED + ["bf16_kk24"])
+@pytest.mark.parametrize("name", REDUCED + ["bf16_kk24", "lr_tiny_f32"] + VARIANTS)
 def test_schedule_matches_oracle(name):
     w = _workload(name)
     inp = Inputs(w)
@@ -38,16 +56,17 @@ def test_schedule_matches_oracle(name):
     got = run_gpu(w, inp)
     ref = run_ref(w, inp)
     compare(w, got, ref, label="full-schedule")
-    rinv_ref = np.stack([inv_rms(key_slice(inp.row(n).astype(np.float64), w.r), w.eps)
+    rinv_ref = np.stack([source_inv_rms(inp.row(n).astype(np.float64), w.r, w.eps, w.norm)
                          for n in range(w.rows)])
     assert max_rel(got["rinv"], rinv_ref) <= 1e-5
 
 
-@pytest.mark.parametrize("name", ["mhar100m", "mhar350m", "mhar1b", "lr_h1", "lr_h8"])
+@pytest.mark.parametrize("name", ["mhar100m", "mhar350m", "mhar1b", "lr_h1", "lr_h8",
+                                  "mhar1b+gain", "lr_h8+gain+fullrms"])
 def test_full_size_sampled_tokens(name):
     """Full benchmark shapes: sampled tokens against the oracle; dq through a
     second run whose upstream gradients are zero outside the sampled tokens."""
-    w = get_workload(name)
+    w = _workload(name)
     inp = Inputs(w)
     toks = sample_tokens(w.tokens, 24)
     log(f"[full-size] {w.describe()} sampled tokens={len(toks)}")
@@ -61,6 +80,10 @@ def test_full_size_sampled_tokens(name):
     err = max_rel(got2["dq"], ref2["dq"])
     log(f"  dq (masked) max-rel={err:.3e}")
     assert err <= 2e-2
+    if "dgain" in ref2:
+        errg = max_rel(got2["dgain"], ref2["dgain"])
+        log(f"  dgain (masked) max-rel={errg:.3e}")
+        assert errg <= 2e-2
 
 
 def test_deterministic_bitwise():

@@ -23,6 +23,9 @@ ATTNRES_ERR_UNSUPPORTED = 4
 ATTNRES_ERR_HIP = 5
 ATTNRES_F32 = 0
 ATTNRES_BF16 = 1
+ATTNRES_NORM_SLICE = 0
+ATTNRES_NORM_FULL = 1
+NORMS = {"slice": ATTNRES_NORM_SLICE, "full": ATTNRES_NORM_FULL}
 
 STATUS_NAMES = {0: "OK", 1: "ERR_INVALID", 2: "ERR_CAPACITY", 3: "ERR_ORDER",
                 4: "ERR_UNSUPPORTED", 5: "ERR_HIP"}
@@ -33,6 +36,7 @@ EXPORTS = (
     "attnres_bank_create",
     "attnres_bank_reset",
     "attnres_bank_set_queries",
+    "attnres_bank_set_gains",
     "attnres_bank_append",
     "attnres_route_fwd",
     "attnres_route_bwd",
@@ -60,6 +64,7 @@ class Config(ctypes.Structure):
         ("max_sites", c_int32),
         ("dtype", c_int32),
         ("eps", c_float),
+        ("norm", c_int32),
     ]
 
 
@@ -87,6 +92,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "attnres_bank_create": (i32, [cfgp, vp, vp, vp, vp, c_size_t, POINTER(vp)]),
         "attnres_bank_reset": (i32, [vp]),
         "attnres_bank_set_queries": (i32, [vp, i32, POINTER(i32), POINTER(i32), vp]),
+        "attnres_bank_set_gains": (i32, [vp, vp, vp, vp]),
         "attnres_bank_append": (i32, [vp, vp, vp, POINTER(i32)]),
         "attnres_route_fwd": (i32, [vp, i32, vp, vp, vp]),
         "attnres_route_bwd": (i32, [vp, i32, vp, vp, vp, vp, vp]),
@@ -139,9 +145,10 @@ def _stream(stream):
 # ---------------------------------------------------------------------------
 # C-named wrappers (status -> exception)
 
-def make_config(tokens, d, r, heads, max_rows, max_sites, dtype, eps=1e-6) -> Config:
+def make_config(tokens, d, r, heads, max_rows, max_sites, dtype, eps=1e-6,
+                norm=ATTNRES_NORM_SLICE) -> Config:
     return Config(int(tokens), int(d), int(r), int(heads), int(max_rows), int(max_sites),
-                  int(dtype), float(eps))
+                  int(dtype), float(eps), int(norm))
 
 
 def attnres_workspace_bytes(cfg: Config) -> int:
@@ -168,6 +175,11 @@ def attnres_bank_set_queries(bank, nsrc, has_extra, queries) -> None:
     ns = (c_int32 * n)(*[int(v) for v in nsrc])
     he = (c_int32 * n)(*[int(v) for v in has_extra]) if has_extra is not None else None
     _check(load_library().attnres_bank_set_queries(bank, n, ns, he, _ptr(queries)))
+
+
+def attnres_bank_set_gains(bank, gains, dgains, stream=None) -> None:
+    _check(load_library().attnres_bank_set_gains(bank, _ptr(gains), _ptr(dgains),
+                                                 _stream(stream)))
 
 
 def attnres_bank_append(bank, src=None, stream=None) -> int:
@@ -247,14 +259,15 @@ class Bank:
     """One bank with its caller-owned device buffers held as torch tensors."""
 
     def __init__(self, tokens, d, r, heads, max_rows, max_sites, dtype="bf16", eps=1e-6,
-                 device="cuda"):
+                 device="cuda", norm="slice"):
         import torch
         self.torch = torch
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.cdtype = ATTNRES_BF16 if dtype == "bf16" else ATTNRES_F32
         self.T, self.d, self.r, self.H = int(tokens), int(d), int(r), int(heads)
         self.max_rows, self.max_sites = int(max_rows), int(max_sites)
-        self.cfg = make_config(tokens, d, r, heads, max_rows, max_sites, self.cdtype, eps)
+        self.cfg = make_config(tokens, d, r, heads, max_rows, max_sites, self.cdtype, eps,
+                               NORMS[norm])
         self.ws_bytes = attnres_workspace_bytes(self.cfg)
         self.rows = torch.empty((max_rows, self.T, d), dtype=self.tdtype, device=device)
         self.drows = torch.empty((max_rows, self.T, d), dtype=torch.float32, device=device)
@@ -281,7 +294,14 @@ class Bank:
         self.nsrc = list(nsrc)
         self.has_extra = list(has_extra) if has_extra is not None else [0] * len(nsrc)
         self.queries = queries  # keep alive
+        self.gains = self.dgains = None
         attnres_bank_set_queries(self.handle, nsrc, has_extra, queries)
+
+    def set_gains(self, gains, dgains, stream=None):
+        """Per-site routing RMSNorm gains [n_sites, r] float32 (None: no gain)
+        and the [n_sites, r] float32 buffer their gradients are written to."""
+        self.gains, self.dgains = gains, dgains  # keep alive
+        attnres_bank_set_gains(self.handle, gains, dgains, stream)
 
     def append(self, src=None, stream=None) -> int:
         return attnres_bank_append(self.handle, src, stream)

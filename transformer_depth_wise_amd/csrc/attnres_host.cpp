@@ -13,6 +13,7 @@
 
 using attnres::FinalizeJob;
 using attnres::Geom;
+using attnres::QuerySet;
 using attnres::SiteArrays;
 
 namespace {
@@ -38,7 +39,9 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Layout {
-  size_t rinv, rinvx, proj, alpha, dl, radial, lse, dqpart, total;
+  size_t rinv, rinvx, proj, alpha, dl, radial, lse, dqpart;
+  size_t qf, q32, qhi, qlo;  // effective queries with gains ([max_sites, r] each)
+  size_t total;
   int64_t site_stride;  // floats per site of proj / alpha / dl: (max_rows + 1) * T * H
   int64_t rad_stride;   // floats per site of radial: (max_rows + 1) * T
 };
@@ -64,6 +67,11 @@ Layout make_layout(const attnres_config_t& c) {
   L.radial = take(srcs * T * c.max_sites);
   L.lse = take((size_t)c.max_sites * T * c.heads);
   L.dqpart = take((size_t)dq_parts_cap() * c.r);
+  const size_t sr = (size_t)c.max_sites * c.r;
+  L.qf = take(sr);
+  L.q32 = take(sr);
+  L.qhi = take((sr + 1) / 2);  // bf16
+  L.qlo = take((sr + 1) / 2);
   L.total = off;
   L.site_stride = (int64_t)slot;
   L.rad_stride = (int64_t)(srcs * T);
@@ -83,6 +91,9 @@ attnres_status_t check_config(const attnres_config_t* c) {
   if (c->max_rows < 1 || c->max_sites < 1)
     return fail(ATTNRES_ERR_INVALID, "max_rows and max_sites must be >= 1");
   if (!(c->eps > 0.f)) return fail(ATTNRES_ERR_INVALID, "eps must be > 0");
+  if (c->norm != ATTNRES_NORM_SLICE && c->norm != ATTNRES_NORM_FULL)
+    return fail(ATTNRES_ERR_INVALID, "norm must be ATTNRES_NORM_SLICE or ATTNRES_NORM_FULL (got %d)",
+                c->norm);
   const int pc = c->dtype == ATTNRES_F32 ? 4 : 8;
   if (c->d % pc || c->r % pc || (c->d / c->heads) % pc || (c->r / c->heads) % pc)
     return fail(ATTNRES_ERR_UNSUPPORTED,
@@ -110,6 +121,9 @@ Geom make_geom(const attnres_config_t& c, const int* cpts, int ncpts) {
   g.kvc = g.kv / g.pc;
   g.kkc = g.kk / g.pc;
   g.key_c0 = (c.d - c.r) / g.pc;
+  // with r == d both norms are the same read: keep the key-only code path
+  g.rms_full = (c.norm == ATTNRES_NORM_FULL && c.r < c.d) ? 1 : 0;
+  g.rms_w = g.rms_full ? c.d : c.r;
   g.eps = c.eps;
   double best = 2.0;
   for (int i = 0; i < ncpts; ++i) {
@@ -167,6 +181,8 @@ struct attnres_bank_s {
   std::vector<int> nsrc, has_extra;
   const void* queries;
   bool queries_set;
+  const float* gains;  // [n_sites, r] or NULL: folded into the workspace queries
+  float* dgains;
   int rows_committed;
   int fwd_next;
   int bwd_next;  // next site to run backward; -1 before the backward phase
@@ -191,6 +207,15 @@ struct attnres_bank_s {
   float* site_dl(int s) const { return f(lay.dl) + (size_t)s * lay.site_stride; }
   float* site_radial(int s) const { return f(lay.radial) + (size_t)s * lay.rad_stride; }
   float* site_lse(int s) const { return f(lay.lse) + (size_t)s * cfg.tokens * cfg.heads; }
+  QuerySet qset() const {
+    QuerySet q{queries, nullptr, nullptr, nullptr};
+    if (gains) {
+      q.qf = f(lay.qf);
+      q.qhi = reinterpret_cast<const uint16_t*>(ws + lay.qhi);
+      q.qlo = reinterpret_cast<const uint16_t*>(ws + lay.qlo);
+    }
+    return q;
+  }
 
   void clear_microbatch() {
     n_sites = 0;
@@ -198,6 +223,8 @@ struct attnres_bank_s {
     has_extra.clear();
     queries = nullptr;
     queries_set = false;
+    gains = nullptr;
+    dgains = nullptr;
     rows_committed = 0;
     fwd_next = 0;
     bwd_next = -1;
@@ -256,7 +283,7 @@ void trace_clear(attnres_bank_s* b) {
 
 extern "C" {
 
-int32_t attnres_abi_version(void) { return 1; }
+int32_t attnres_abi_version(void) { return 2; }
 
 attnres_status_t attnres_trace_enable(attnres_bank_t b, int32_t enable) {
   if (!b) return fail(ATTNRES_ERR_INVALID, "bank is NULL");
@@ -366,7 +393,34 @@ attnres_status_t attnres_bank_set_queries(attnres_bank_t b, int32_t n_sites, con
     for (int s = 0; s < n_sites; ++s) b->has_extra[s] = has_extra[s];
   b->queries = queries;
   b->queries_set = true;
+  b->gains = nullptr;
+  b->dgains = nullptr;
   b->extra_ptr.assign(n_sites, nullptr);
+  return ATTNRES_OK;
+}
+
+attnres_status_t attnres_bank_set_gains(attnres_bank_t b, const float* gains, float* dgains,
+                                        attnres_stream_t stream) {
+  if (!b) return fail(ATTNRES_ERR_INVALID, "bank is NULL");
+  if (!b->queries_set || b->rows_committed > 0 || b->fwd_next > 0 || b->bwd_next >= 0 ||
+      b->bwd_done)
+    return fail(ATTNRES_ERR_ORDER, "set_gains must follow set_queries, before the first append");
+  if (!gains) {
+    b->gains = nullptr;
+    b->dgains = nullptr;
+    return ATTNRES_OK;
+  }
+  if (!dgains) return fail(ATTNRES_ERR_INVALID, "dgains must be non-NULL when gains is set");
+  if (!aligned16(gains) || !aligned16(dgains))
+    return fail(ATTNRES_ERR_INVALID, "gains and dgains must be 16-byte aligned");
+  const int64_t count = (int64_t)b->n_sites * b->cfg.r;
+  hipError_t e = attnres::launch_fold_gains(
+      b->cfg.dtype, b->queries, gains, count, b->f(b->lay.qf), b->f(b->lay.q32),
+      reinterpret_cast<uint16_t*>(b->ws + b->lay.qhi), reinterpret_cast<uint16_t*>(b->ws + b->lay.qlo),
+      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "set_gains fold kernel");
+  b->gains = gains;
+  b->dgains = dgains;
   return ATTNRES_OK;
 }
 
@@ -391,7 +445,7 @@ attnres_status_t attnres_bank_append(attnres_bank_t b, const void* src, attnres_
   int s_lo = 0;
   while (s_lo < b->n_sites && b->nsrc[s_lo] <= n) ++s_lo;
   TraceScope ts(b, ATTNRES_KERNEL_SCORE, st);
-  hipError_t e = attnres::launch_score(b->g_main, b->cfg.dtype, dst, b->queries, s_lo, b->n_sites, n,
+  hipError_t e = attnres::launch_score(b->g_main, b->cfg.dtype, dst, b->qset(), s_lo, b->n_sites, n,
                                        b->rinv(n), b->f(b->lay.proj), b->lay.site_stride, st);
   ts.done();
   if (e != hipSuccess) return hip_fail(e, "append score kernel");
@@ -425,7 +479,7 @@ attnres_status_t attnres_route_fwd(attnres_bank_t b, int32_t site, const void* e
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (extra) {
     TraceScope ts(b, ATTNRES_KERNEL_SCORE, st);
-    hipError_t e = attnres::launch_score(b->g_main, b->cfg.dtype, extra, b->queries, site, site + 1,
+    hipError_t e = attnres::launch_score(b->g_main, b->cfg.dtype, extra, b->qset(), site, site + 1,
                                          n_rows, b->rinvx(site), b->f(b->lay.proj),
                                          b->lay.site_stride, st);
     ts.done();
@@ -484,7 +538,11 @@ attnres_status_t attnres_route_bwd(attnres_bank_t b, int32_t site, const void* e
     if (e != hipSuccess) return hip_fail(e, "route_bwd site kernel");
     // With no tokens there are no parts and the reduction writes zeros.
     TraceScope tr(b, ATTNRES_KERNEL_DQ_REDUCE, st);
-    e = attnres::launch_dq_reduce(b->f(b->lay.dqpart), c.tokens > 0 ? parts : 0, c.r, dq, st);
+    const size_t qoff = (size_t)site * c.r;
+    e = attnres::launch_dq_reduce(b->f(b->lay.dqpart), c.tokens > 0 ? parts : 0, c.r, dq,
+                                  b->gains ? b->gains + qoff : nullptr,
+                                  b->gains ? b->f(b->lay.q32) + qoff : nullptr,
+                                  b->gains ? b->dgains + qoff : nullptr, st);
     tr.done();
     if (e != hipSuccess) return hip_fail(e, "route_bwd dq reduction");
   }
@@ -522,7 +580,7 @@ attnres_status_t attnres_route_bwd(attnres_bank_t b, int32_t site, const void* e
   sa.th_stride = c.tokens * (int64_t)c.heads;
   TraceScope tf(b, ATTNRES_KERNEL_FINALIZE, st);
   hipError_t e = attnres::launch_finalize(b->g_main, c.dtype, jobs.data(), (int)jobs.size(), sa,
-                                          b->dout_rows, row_stride, b->queries, st);
+                                          b->dout_rows, row_stride, b->qset(), st);
   tf.done();
   if (e != hipSuccess) return hip_fail(e, "route_bwd finalize kernel");
   b->bwd_next = site - 1;

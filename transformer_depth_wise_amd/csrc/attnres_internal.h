@@ -28,7 +28,20 @@ struct Geom {
   int32_t cpt;   // chunks per thread of the streaming kernels
   int64_t ntiles;  // ceil(T / tt)
   int32_t wave_tokens;  // backward site pass: tokens owned by each wave (0: work-group-wide layout)
+  int32_t rms_full;  // 1: the inverse RMS is over all d coordinates (key still the last r)
+  int32_t rms_w;     // divisor of the mean of squares: d if rms_full, else r
   float eps;
+};
+
+// The queries a kernel scores with.  Without gains only `q` (storage dtype,
+// [sites, r]) is set.  With gains the effective queries q * g are read
+// instead: `qf` in float32, and for the bf16 matrix-core append `qhi` +
+// `qlo`, two bf16 arrays whose sum is q * g to about 16 significant bits.
+struct QuerySet {
+  const void* q;
+  const float* qf;
+  const uint16_t* qhi;
+  const uint16_t* qlo;
 };
 
 // Per-site saved state lives in site-major slots of the workspace:
@@ -49,9 +62,14 @@ struct SiteArrays {
   int64_t th_stride;    // floats between consecutive sites of lse = T * H
 };
 
-hipError_t launch_score(const Geom& g, int dtype, const void* x, const void* queries, int s_lo,
+hipError_t launch_score(const Geom& g, int dtype, const void* x, const QuerySet& qs, int s_lo,
                         int s_hi, int slot, float* rinv_out, float* proj,
                         int64_t site_stride, hipStream_t st);
+
+// Effective queries with gains: for every (site, k) of [sites, r],
+// qf = q * gain, q32 = q (float32), qhi = bf16(qf), qlo = bf16(qf - qhi).
+hipError_t launch_fold_gains(int dtype, const void* q, const float* gain, int64_t count,
+                             float* qf, float* q32, uint16_t* qhi, uint16_t* qlo, hipStream_t st);
 
 hipError_t launch_fwd(const Geom& g, int dtype, const void* rows, int64_t row_stride,
                       const void* extra, int n_rows, const float* proj, const float* rinv_rows,
@@ -63,7 +81,11 @@ hipError_t launch_bwd_site(const Geom& g, int dtype, const void* rows, int64_t r
                            float* dl, float* radial, float* dq_part, int parts,
                            hipStream_t st);
 
-hipError_t launch_dq_reduce(const float* dq_part, int parts, int r, float* dq, hipStream_t st);
+// dq = sum of the partial rows (fixed order).  With gains (gain, q32 and dg
+// non-NULL) the sum is the gradient of the effective query q * g: then
+// dq = gain * sum and dg = q32 * sum.
+hipError_t launch_dq_reduce(const float* dq_part, int parts, int r, float* dq, const float* gain,
+                            const float* q32, float* dg, hipStream_t st);
 
 // One finalize job: the gradient of source x (bank row or transient source)
 // gathered from the backward coefficients of sites [s0, s1).
@@ -77,7 +99,7 @@ struct FinalizeJob {
 
 hipError_t launch_finalize(const Geom& g, int dtype, const FinalizeJob* jobs, int njobs,
                            const SiteArrays& sa, const void* dout_rows, int64_t dout_stride,
-                           const void* queries, hipStream_t st);
+                           const QuerySet& qs, hipStream_t st);
 
 // Number of dq partial rows the site pass writes for this geometry.
 int bwd_site_parts(const Geom& g);

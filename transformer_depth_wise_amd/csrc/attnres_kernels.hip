@@ -83,6 +83,27 @@ struct Vec<bf16_t> {
   }
 };
 
+// One chunk (Vec<T>::N values) of a query row: storage dtype T (one 16-byte
+// word) or float32 effective queries q * g (N / 4 words).
+template <typename T, typename QT>
+struct QChunk {
+  static constexpr int W = (int)sizeof(QT) * Vec<T>::N / 16;
+  uint4 w[W];
+  __device__ __forceinline__ void load(const QT* row, int chunk) {
+    const uint4* p = reinterpret_cast<const uint4*>(row + chunk * Vec<T>::N);
+#pragma unroll
+    for (int i = 0; i < W; ++i) w[i] = p[i];
+  }
+  __device__ __forceinline__ void unpack(float* f) const {
+    if constexpr (sizeof(QT) == sizeof(T)) {
+      Vec<T>::unpack(w[0], f);
+    } else {
+#pragma unroll
+      for (int i = 0; i < W; ++i) Vec<float>::unpack(w[i], f + 4 * i);
+    }
+  }
+};
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -177,9 +198,9 @@ __device__ __forceinline__ int64_t xcd_order(int64_t b, int64_t n) {
   return x * q + (x < rem ? x : rem) + k;
 }
 
-template <typename T>
+template <typename T, typename QT>
 __global__ __launch_bounds__(kThreads) void k_score(Geom g, const T* __restrict__ x,
-                                                     const T* __restrict__ Q, int s_lo, int s_hi,
+                                                     const QT* __restrict__ Q, int s_lo, int s_hi,
                                                      int slot, float* __restrict__ rinv_out,
                                                      float* __restrict__ proj,
                                                      int64_t site_stride) {
@@ -206,12 +227,21 @@ __global__ __launch_bounds__(kThreads) void k_score(Geom g, const T* __restrict_
           ss += f[e] * f[e];
         }
       }
+      if (g.rms_full) {  // the rest of the row enters the mean of squares
+        const uint4* row = reinterpret_cast<const uint4*>(x + t * g.d);
+        for (int c = lane; c < g.key_c0; c += 64) {
+          float f[V::N];
+          V::unpack(row[c], f);
+#pragma unroll
+          for (int e = 0; e < V::N; ++e) ss += f[e] * f[e];
+        }
+      }
     } else {
       for (int i = lane; i < g.r; i += 64) kr[i] = 0.f;
     }
     ss = wave_sum(ss);
     if (lane == 0) {
-      const float ri = rsqrtf(ss / (float)g.r + g.eps);
+      const float ri = rsqrtf(ss / (float)g.rms_w + g.eps);
       srinv[tau] = ri;
       if (t < g.T) rinv_out[t] = ri;
     }
@@ -223,13 +253,15 @@ __global__ __launch_bounds__(kThreads) void k_score(Geom g, const T* __restrict_
   for (int it = tid; it < items; it += kThreads) {
     const int h = it / ns;
     const int s = s_lo + (it - h * ns);
-    const uint4* qh = reinterpret_cast<const uint4*>(Q + (int64_t)s * g.r + (int64_t)h * g.kk);
+    const QT* qh = Q + (int64_t)s * g.r + (int64_t)h * g.kk;
     float acc[kScoreTile];
 #pragma unroll
     for (int tau = 0; tau < kScoreTile; ++tau) acc[tau] = 0.f;
     for (int c = 0; c < g.kkc; ++c) {
       float qf[V::N];
-      V::unpack(qh[c], qf);
+      QChunk<T, QT> qc;
+      qc.load(qh, c);
+      qc.unpack(qf);
       const float* kb = keys + h * g.kk + c * V::N;
 #pragma unroll
       for (int tau = 0; tau < kScoreTile; ++tau) {
@@ -268,7 +300,8 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
 // per-wave sums of squares meet in LDS for the inverse RMS.  r/H = KS * 32.
 template <int KS>
 __global__ __launch_bounds__(kThreads) void k_score_mfma(Geom g, const bf16_t* __restrict__ x,
-                                                          const bf16_t* __restrict__ Q, int s_lo,
+                                                          const bf16_t* __restrict__ Q,
+                                                          const bf16_t* __restrict__ Qlo, int s_lo,
                                                           int s_hi, int slot,
                                                           float* __restrict__ rinv_out,
                                                           float* __restrict__ proj,
@@ -295,6 +328,17 @@ __global__ __launch_bounds__(kThreads) void k_score_mfma(Geom g, const bf16_t* _
   };
 
   float ss = 0.f;
+  if (g.rms_full && tok_ok) {
+    // the non-key coordinates of the token row enter the mean of squares:
+    // the 16 lanes holding this row (4 k-groups x 4 waves) take every 16th chunk
+    const uint4* rp = reinterpret_cast<const uint4*>(x + t * g.d);
+    for (int c = wave * 4 + kg; c < g.key_c0; c += 16) {
+      float f[8];
+      Vec<bf16_t>::unpack(ld_stream(rp + c), f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+    }
+  }
   uint4 a_cur[KS], a_nxt[KS];
   if (wave < g.H) fetch_a(wave, a_cur);
   for (int h = wave; h < g.H; h += kWaves) {
@@ -318,6 +362,15 @@ __global__ __launch_bounds__(kThreads) void k_score_mfma(Geom g, const bf16_t* _
       for (int ks = 0; ks < KS; ++ks)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a_cur[ks]), as_bf16x8(b[ks]), acc,
                                                       0, 0, 0);
+      if (Qlo) {  // effective queries q * g as high + low bf16 parts
+        const bf16_t* qlp = Qlo + (int64_t)(s_ok ? s : s_lo) * g.r + h * g.kk + kg * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) b[ks] = *reinterpret_cast<const uint4*>(qlp + ks * 32);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a_cur[ks]), as_bf16x8(b[ks]),
+                                                        acc, 0, 0, 0);
+      }
       if (s_ok) {
         // one 16-byte store into the token-fastest [slot][head][token] layout
         float* dst = proj + (int64_t)s * site_stride + ((int64_t)slot * g.H + h) * g.T + tq;
@@ -342,7 +395,7 @@ __global__ __launch_bounds__(kThreads) void k_score_mfma(Geom g, const bf16_t* _
     float tot = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) tot += s_ss[w][row];
-    rinv_out[t] = rsqrtf(tot / (float)g.r + g.eps);
+    rinv_out[t] = rsqrtf(tot / (float)g.rms_w + g.eps);
   }
 }
 
@@ -920,7 +973,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site_w(
 constexpr int kReduceThreads = 1024;
 __global__ __launch_bounds__(kReduceThreads) void k_dq_reduce(const float* __restrict__ part,
                                                                int parts, int r,
-                                                               float* __restrict__ dq) {
+                                                               float* __restrict__ dq,
+                                                               const float* __restrict__ gain,
+                                                               const float* __restrict__ q32,
+                                                               float* __restrict__ dg) {
   constexpr int W = kReduceThreads / 64;
   __shared__ float red[W][64];
   const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
@@ -942,7 +998,12 @@ __global__ __launch_bounds__(kReduceThreads) void k_dq_reduce(const float* __res
     float s = 0.f;
 #pragma unroll
     for (int w = 0; w < W; ++w) s += red[w][lane];
-    dq[col] = s;
+    if (gain) {  // s is the gradient of the effective query q * g
+      dq[col] = gain[col] * s;
+      dg[col] = q32[col] * s;
+    } else {
+      dq[col] = s;
+    }
   }
 }
 
@@ -962,11 +1023,11 @@ struct FinalizeArgs {
   FinalizeJob job[kMaxJobs];
 };
 
-template <typename T, int CPT>
+template <typename T, int CPT, typename QT>
 __global__ __launch_bounds__(kThreads) void k_finalize(Geom g, FinalizeArgs fa, SiteArrays sa,
                                                         int batch, const T* __restrict__ dout_rows,
                                                         int64_t dout_stride,
-                                                        const T* __restrict__ Q) {
+                                                        const QT* __restrict__ Q) {
   using V = Vec<T>;
   constexpr int N = V::N;
   extern __shared__ float sm[];
@@ -1010,14 +1071,15 @@ __global__ __launch_bounds__(kThreads) void k_finalize(Geom g, FinalizeArgs fa, 
   }
   for (int b0 = job.s0; b0 < job.s1; b0 += batch) {
     const int nb = min(batch, job.s1 - b0);
-    uint4 buf[2][CPT], qb[2][CPT];
+    uint4 buf[2][CPT];
+    QChunk<T, QT> qb[2][CPT];
     {
       const uint4* dp = dout_of(b0);
-      const uint4* qs = reinterpret_cast<const uint4*>(Q + (int64_t)b0 * g.r);
+      const QT* qs = Q + (int64_t)b0 * g.r;
 #pragma unroll
       for (int j = 0; j < CPT; ++j) {
         buf[0][j] = ld_stream(dp + qa[j]);
-        qb[0][j] = qs[ka[j]];
+        qb[0][j].load(qs, ka[j]);
       }
     }
     if ((g.H & 3) == 0 && (g.T & 3) == 0) {  // 16-byte words, each within one token
@@ -1073,11 +1135,11 @@ __global__ __launch_bounds__(kThreads) void k_finalize(Geom g, FinalizeArgs fa, 
         if (k + 1 < nb) {
           // query chunks are shared by every token of the tile: cache hits
           const uint4* dp = dout_of(s + 1);
-          const uint4* qs = reinterpret_cast<const uint4*>(Q + (int64_t)(s + 1) * g.r);
+          const QT* qs = Q + (int64_t)(s + 1) * g.r;
 #pragma unroll
           for (int j = 0; j < CPT; ++j) {
             buf[d ^ 1][j] = ld_stream(dp + qa[j]);
-            qb[d ^ 1][j] = qs[ka[j]];
+            qb[d ^ 1][j].load(qs, ka[j]);
           }
         }
 #pragma unroll
@@ -1091,7 +1153,7 @@ __global__ __launch_bounds__(kThreads) void k_finalize(Geom g, FinalizeArgs fa, 
           if (sl[j].key) {
             const float b = cQ[base + sl[j].hk];
             float qf[N];
-            V::unpack(qb[d][j], qf);
+            qb[d][j].unpack(qf);
 #pragma unroll
             for (int e = 0; e < N; ++e) acc[j][e] += b * qf[e];
           }
@@ -1102,7 +1164,7 @@ __global__ __launch_bounds__(kThreads) void k_finalize(Geom g, FinalizeArgs fa, 
   }
   if (tid < g.tt) {
     const float ri = (tid < tv) ? job.rinv[t0 + tid] : 0.f;
-    s_rad[tid] = ri * ri / (float)g.r * rad;
+    s_rad[tid] = ri * ri / (float)g.rms_w * rad;
   }
   __syncthreads();
 
@@ -1111,7 +1173,7 @@ __global__ __launch_bounds__(kThreads) void k_finalize(Geom g, FinalizeArgs fa, 
 #pragma unroll
   for (int j = 0; j < CPT; ++j) {
     if (!ok[j]) continue;
-    if (sl[j].key) {
+    if (sl[j].key || g.rms_full) {  // radial term: key coordinates, or all of them
       const float rc = s_rad[sl[j].tau];
       float f[N];
       V::unpack(xp[sl[j].q], f);
@@ -1132,8 +1194,8 @@ using FwdFn = void (*)(Geom, const T*, int64_t, const T*, int, const float*, con
 template <typename T>
 using SiteFn = void (*)(Geom, const T*, int64_t, const T*, int, const float*, const float*,
                         const float*, const float*, const T*, float*, float*, float*);
-template <typename T>
-using FinFn = void (*)(Geom, FinalizeArgs, SiteArrays, int, const T*, int64_t, const T*);
+template <typename T, typename QT>
+using FinFn = void (*)(Geom, FinalizeArgs, SiteArrays, int, const T*, int64_t, const QT*);
 
 template <typename T>
 FwdFn<T> pick_fwd(int cpt) {
@@ -1163,16 +1225,41 @@ SiteFn<T> pick_site(int cpt, bool wave_tokens) {
   }
   return nullptr;
 }
-template <typename T>
-FinFn<T> pick_fin(int cpt) {
+template <typename T, typename QT>
+FinFn<T, QT> pick_fin(int cpt) {
   switch (cpt) {
-    case 2: return k_finalize<T, 2>;
-    case 4: return k_finalize<T, 4>;
-    case 5: return k_finalize<T, 5>;
-    case 7: return k_finalize<T, 7>;
-    case 8: return k_finalize<T, 8>;
+    case 2: return k_finalize<T, 2, QT>;
+    case 4: return k_finalize<T, 4, QT>;
+    case 5: return k_finalize<T, 5, QT>;
+    case 7: return k_finalize<T, 7, QT>;
+    case 8: return k_finalize<T, 8, QT>;
   }
   return nullptr;
+}
+
+// Effective queries with gains (see launch_fold_gains).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_fold_gains(const T* __restrict__ q,
+                                                          const float* __restrict__ gain,
+                                                          int64_t count, float* __restrict__ qf,
+                                                          float* __restrict__ q32,
+                                                          bf16_t* __restrict__ qhi,
+                                                          bf16_t* __restrict__ qlo) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < count;
+       i += (int64_t)gridDim.x * kThreads) {
+    float qv;
+    if constexpr (sizeof(T) == 4) {
+      qv = q[i];
+    } else {
+      qv = __uint_as_float((uint32_t)q[i] << 16);
+    }
+    const float e = qv * gain[i];
+    const uint32_t hi = f32_to_bf16_bits(e);
+    qf[i] = e;
+    q32[i] = qv;
+    qhi[i] = (bf16_t)hi;
+    qlo[i] = (bf16_t)f32_to_bf16_bits(e - __uint_as_float(hi << 16));
+  }
 }
 
 constexpr size_t kMaxLds = 64 * 1024;
@@ -1212,7 +1299,7 @@ int bwd_site_parts(const Geom& g) {
   return (int)(g.ntiles < cap ? g.ntiles : cap);
 }
 
-hipError_t launch_score(const Geom& g, int dtype, const void* x, const void* queries, int s_lo,
+hipError_t launch_score(const Geom& g, int dtype, const void* x, const QuerySet& qs, int s_lo,
                         int s_hi, int slot, float* rinv_out, float* proj, int64_t site_stride,
                         hipStream_t st) {
   if (g.T == 0) return hipSuccess;
@@ -1220,12 +1307,14 @@ hipError_t launch_score(const Geom& g, int dtype, const void* x, const void* que
     const int ks = g.kk / 32;
     const dim3 grid((unsigned)((g.T + 15) / 16));
     const bf16_t* xb = static_cast<const bf16_t*>(x);
-    const bf16_t* qb = static_cast<const bf16_t*>(queries);
+    // with gains: high and low bf16 parts of q * g, two products per block
+    const bf16_t* qb = qs.qf ? qs.qhi : static_cast<const bf16_t*>(qs.q);
+    const bf16_t* ql = qs.qf ? qs.qlo : nullptr;
     switch (ks) {
-#define ATTNRES_SCORE_KS(K)                                                                  \
-  case K:                                                                                    \
-    hipLaunchKernelGGL(k_score_mfma<K>, grid, dim3(kThreads), 0, st, g, xb, qb, s_lo, s_hi, \
-                       slot, rinv_out, proj, site_stride);                                   \
+#define ATTNRES_SCORE_KS(K)                                                                      \
+  case K:                                                                                        \
+    hipLaunchKernelGGL(k_score_mfma<K>, grid, dim3(kThreads), 0, st, g, xb, qb, ql, s_lo, s_hi, \
+                       slot, rinv_out, proj, site_stride);                                       \
     break;
       ATTNRES_SCORE_KS(1)
       ATTNRES_SCORE_KS(2)
@@ -1243,13 +1332,32 @@ hipError_t launch_score(const Geom& g, int dtype, const void* x, const void* que
   const size_t lds = lds_score(g);
   if (lds > kMaxLds) return hipErrorInvalidConfiguration;
   if (dtype == 0)
-    hipLaunchKernelGGL(k_score<float>, grid, dim3(kThreads), lds, st, g,
-                       static_cast<const float*>(x), static_cast<const float*>(queries), s_lo, s_hi,
-                       slot, rinv_out, proj, site_stride);
+    hipLaunchKernelGGL((k_score<float, float>), grid, dim3(kThreads), lds, st, g,
+                       static_cast<const float*>(x),
+                       qs.qf ? qs.qf : static_cast<const float*>(qs.q), s_lo, s_hi, slot,
+                       rinv_out, proj, site_stride);
+  else if (qs.qf)
+    hipLaunchKernelGGL((k_score<bf16_t, float>), grid, dim3(kThreads), lds, st, g,
+                       static_cast<const bf16_t*>(x), qs.qf, s_lo, s_hi, slot, rinv_out, proj,
+                       site_stride);
   else
-    hipLaunchKernelGGL(k_score<bf16_t>, grid, dim3(kThreads), lds, st, g,
-                       static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(queries), s_lo,
+    hipLaunchKernelGGL((k_score<bf16_t, bf16_t>), grid, dim3(kThreads), lds, st, g,
+                       static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(qs.q), s_lo,
                        s_hi, slot, rinv_out, proj, site_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_fold_gains(int dtype, const void* q, const float* gain, int64_t count,
+                             float* qf, float* q32, uint16_t* qhi, uint16_t* qlo, hipStream_t st) {
+  if (count == 0) return hipSuccess;
+  int64_t blocks = (count + kThreads - 1) / kThreads;
+  if (blocks > 1024) blocks = 1024;
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_fold_gains<float>, dim3((unsigned)blocks), dim3(kThreads), 0, st,
+                       static_cast<const float*>(q), gain, count, qf, q32, qhi, qlo);
+  else
+    hipLaunchKernelGGL(k_fold_gains<bf16_t>, dim3((unsigned)blocks), dim3(kThreads), 0, st,
+                       static_cast<const bf16_t*>(q), gain, count, qf, q32, qhi, qlo);
   return hipGetLastError();
 }
 
@@ -1303,15 +1411,19 @@ hipError_t launch_bwd_site(const Geom& g, int dtype, const void* rows, int64_t r
   return hipGetLastError();
 }
 
-hipError_t launch_dq_reduce(const float* dq_part, int parts, int r, float* dq, hipStream_t st) {
+hipError_t launch_dq_reduce(const float* dq_part, int parts, int r, float* dq, const float* gain,
+                            const float* q32, float* dg, hipStream_t st) {
+  if ((gain != nullptr) != (dg != nullptr) || (gain != nullptr) != (q32 != nullptr))
+    return hipErrorInvalidValue;
   const dim3 grid((unsigned)((r + 63) / 64));
-  hipLaunchKernelGGL(k_dq_reduce, grid, dim3(kReduceThreads), 0, st, dq_part, parts, r, dq);
+  hipLaunchKernelGGL(k_dq_reduce, grid, dim3(kReduceThreads), 0, st, dq_part, parts, r, dq, gain,
+                     q32, dg);
   return hipGetLastError();
 }
 
 hipError_t launch_finalize(const Geom& g, int dtype, const FinalizeJob* jobs, int njobs,
                            const SiteArrays& sa, const void* dout_rows, int64_t dout_stride,
-                           const void* queries, hipStream_t st) {
+                           const QuerySet& qs, hipStream_t st) {
   if (g.T == 0 || njobs == 0) return hipSuccess;
   int max_sites = 1;
   for (int i = 0; i < njobs; ++i)
@@ -1326,17 +1438,22 @@ hipError_t launch_finalize(const Geom& g, int dtype, const FinalizeJob* jobs, in
     for (int i = 0; i < nj; ++i) fa.job[i] = jobs[j0 + i];
     const dim3 grid((unsigned)g.ntiles, (unsigned)nj);
     if (dtype == 0) {
-      auto fn = pick_fin<float>(g.cpt);
+      auto fn = pick_fin<float, float>(g.cpt);
       if (!fn) return hipErrorInvalidConfiguration;
       hipLaunchKernelGGL(fn, grid, dim3(kThreads), lds, st, g, fa, sa, batch,
                          static_cast<const float*>(dout_rows), dout_stride,
-                         static_cast<const float*>(queries));
+                         qs.qf ? qs.qf : static_cast<const float*>(qs.q));
+    } else if (qs.qf) {  // float32 effective queries q * g
+      auto fn = pick_fin<bf16_t, float>(g.cpt);
+      if (!fn) return hipErrorInvalidConfiguration;
+      hipLaunchKernelGGL(fn, grid, dim3(kThreads), lds, st, g, fa, sa, batch,
+                         static_cast<const bf16_t*>(dout_rows), dout_stride, qs.qf);
     } else {
-      auto fn = pick_fin<bf16_t>(g.cpt);
+      auto fn = pick_fin<bf16_t, bf16_t>(g.cpt);
       if (!fn) return hipErrorInvalidConfiguration;
       hipLaunchKernelGGL(fn, grid, dim3(kThreads), lds, st, g, fa, sa, batch,
                          static_cast<const bf16_t*>(dout_rows), dout_stride,
-                         static_cast<const bf16_t*>(queries));
+                         static_cast<const bf16_t*>(qs.q));
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
