@@ -246,9 +246,10 @@ typedef enum {
 attnres_status_t attnres_trace_enable(attnres_bank_t bank, int32_t enable);
 attnres_status_t attnres_trace_read(attnres_bank_t bank, double* ms, int64_t* launches);
 
-/* Bandwidth probes giving the practical HBM ceiling with the same 16-byte
- * vector loads as the routing kernels (grid-stride loops, whole 16-byte words
- * only; a tail under 16 bytes is ignored).  Enqueued on `stream`.
+/* Bandwidth probes giving the practical HBM ceiling with the access pattern
+ * of the routing kernels: contiguous 20 KB tiles per work-group, read with
+ * non-temporal 16-byte loads (the copy also stores non-temporally); whole
+ * 16-byte words only, a tail under 16 bytes is ignored.  Enqueued on `stream`.
  *   attnres_probe_read   reads `bytes` of src; writes attnres_probe_sink_words()
  *                        uint32 words to sink (device)
  *   attnres_probe_copy   copies `bytes` from src to dst (non-overlapping)

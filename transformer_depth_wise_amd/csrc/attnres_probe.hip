@@ -1,6 +1,9 @@
 // Bandwidth probes: the practical HBM ceiling on the same GPU, measured with
-// the same 16-byte vector loads the routing kernels use.  Grid-stride loops
-// over whole 16-byte words; a tail of fewer than 16 bytes is ignored.
+// the access pattern of the routing kernels: each work-group streams
+// contiguous 20 KB tiles (256 threads x 5 sixteen-byte words, the tile of an
+// 8-token x 1280-value bf16 row block) with non-temporal 16-byte loads, and
+// loops over tiles with the grid as stride.  Words past the last whole tile
+// are taken by a grid-stride tail; a tail of fewer than 16 bytes is ignored.
 
 #include "attnres_internal.h"
 
@@ -8,26 +11,34 @@ namespace attnres {
 namespace {
 
 constexpr int kProbeThreads = 256;
+constexpr int kProbeWords = 5;  // 16-byte words per thread per tile
+constexpr int64_t kProbeTile = (int64_t)kProbeThreads * kProbeWords;
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4_t ld_nt(const uint4* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
 
 __global__ __launch_bounds__(kProbeThreads) void k_probe_read(const uint4* __restrict__ src,
                                                                int64_t words,
                                                                uint32_t* __restrict__ sink) {
-  const int64_t stride = (int64_t)gridDim.x * kProbeThreads;
-  uint32_t a0 = 0, a1 = 0, a2 = 0, a3 = 0;
-  int64_t i = (int64_t)blockIdx.x * kProbeThreads + threadIdx.x;
-  for (; i + 3 * stride < words; i += 4 * stride) {
-    const uint4 v0 = src[i], v1 = src[i + stride], v2 = src[i + 2 * stride], v3 = src[i + 3 * stride];
-    a0 ^= v0.x ^ v0.y ^ v0.z ^ v0.w;
-    a1 ^= v1.x ^ v1.y ^ v1.z ^ v1.w;
-    a2 ^= v2.x ^ v2.y ^ v2.z ^ v2.w;
-    a3 ^= v3.x ^ v3.y ^ v3.z ^ v3.w;
+  const int64_t tiles = words / kProbeTile;
+  uint32_t a = 0;
+  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+    const uint4* p = src + tile * kProbeTile + threadIdx.x;
+    u32x4_t v[kProbeWords];
+#pragma unroll
+    for (int j = 0; j < kProbeWords; ++j) v[j] = ld_nt(p + j * kProbeThreads);
+#pragma unroll
+    for (int j = 0; j < kProbeWords; ++j) a ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
   }
-  for (; i < words; i += stride) {
-    const uint4 v = src[i];
-    a0 ^= v.x ^ v.y ^ v.z ^ v.w;
+  for (int64_t i = tiles * kProbeTile + (int64_t)blockIdx.x * kProbeThreads + threadIdx.x;
+       i < words; i += (int64_t)gridDim.x * kProbeThreads) {
+    const u32x4_t v = ld_nt(src + i);
+    a ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   // one word per work-group keeps the loads live
-  const uint32_t a = a0 ^ a1 ^ a2 ^ a3;
   __shared__ uint32_t red[kProbeThreads];
   red[threadIdx.x] = a;
   __syncthreads();
@@ -41,14 +52,19 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_read(const uint4* __res
 __global__ __launch_bounds__(kProbeThreads) void k_probe_copy(const uint4* __restrict__ src,
                                                                uint4* __restrict__ dst,
                                                                int64_t words) {
-  const int64_t stride = (int64_t)gridDim.x * kProbeThreads;
-  int64_t i = (int64_t)blockIdx.x * kProbeThreads + threadIdx.x;
-  for (; i + stride < words; i += 2 * stride) {
-    const uint4 v0 = src[i], v1 = src[i + stride];
-    dst[i] = v0;
-    dst[i + stride] = v1;
+  const int64_t tiles = words / kProbeTile;
+  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+    const int64_t base = tile * kProbeTile + threadIdx.x;
+    u32x4_t v[kProbeWords];
+#pragma unroll
+    for (int j = 0; j < kProbeWords; ++j) v[j] = ld_nt(src + base + j * kProbeThreads);
+#pragma unroll
+    for (int j = 0; j < kProbeWords; ++j)
+      __builtin_nontemporal_store(v[j], reinterpret_cast<u32x4_t*>(dst + base + j * kProbeThreads));
   }
-  for (; i < words; i += stride) dst[i] = src[i];
+  for (int64_t i = tiles * kProbeTile + (int64_t)blockIdx.x * kProbeThreads + threadIdx.x;
+       i < words; i += (int64_t)gridDim.x * kProbeThreads)
+    __builtin_nontemporal_store(ld_nt(src + i), reinterpret_cast<u32x4_t*>(dst + i));
 }
 
 }  // namespace
