@@ -4,6 +4,8 @@ tests, the smoke check and the benchmark's CPU-baseline leg."""
 
 from .attnres_oracle import (  # noqa: F401
     EPS,
+    delta_backward,
+    delta_forward,
     inv_rms,
     key_slice,
     route_backward,

@@ -51,6 +51,16 @@ Readings where the pages are open (each also listed in the design doc):
       Its source gradient is Appendix B.3, Eq. 22: the radial term has
       divisor d and reaches every coordinate.  For r = d it coincides with
       the default norm="slice".
+  R8  Delta form ("Multi-Head Attention Residuals", section 3.3,
+      identity-preserving conversion, and Appendix E, delta variant and
+      Figure 9): one self-contained read per call over a short source list,
+      a learnable null source (one d-vector shared by every token, scored as
+      source 0) followed by the block deltas, with the residual stream added
+      to the routed output: out = sum_n alpha_n s_n + partial.  Keys are the
+      full width (r = d).  The gradients of the call are returned fresh; the
+      null source's gradient is the sum over tokens of its per-token
+      gradient, and the residual stream's gradient is dout itself.  An output
+      gate on the routed term belongs to the caller.
   R5  LR with H > 1: q in R^r is split into H slices of width r/H; head h
       scores the h-th slice of the normalised r-wide key and mixes the h-th
       d/H slice of the value.  Requires H | r.  r = d gives MHAR.
@@ -219,3 +229,44 @@ def _site_sources(rows, extra, n):
     if extra is not None:
         src = np.concatenate([src, np.asarray(extra, dtype=np.float64)[None]], axis=0)
     return src
+
+
+def delta_forward(null_src, sources, q, partial, heads: int, eps: float = EPS):
+    """One delta read (R8).
+
+    null_src: [d] or None   learnable null source, the same for every token
+    sources:  [M, T, d]     block deltas
+    q:        [d]           static query of the site
+    partial:  [T, d] or None  residual stream added to the routed output
+    Returns out [T, d], alpha [N, T, H], lse [T, H] with N = M (+1 with a
+    null source, which is source 0).
+    """
+    src = _delta_sources(null_src, sources)
+    d = src.shape[-1]
+    out, alpha, lse = route_forward(src, q, heads, d, eps)
+    if partial is not None:
+        out = out + np.asarray(partial, dtype=np.float64)
+    return out, alpha, lse
+
+
+def delta_backward(null_src, sources, q, dout, heads: int, eps: float = EPS):
+    """Gradient of <dout, out> for one delta read (R8).
+
+    Returns dsources [M, T, d], dnull [d] (None without a null source) and
+    dq [d].  The residual stream's gradient is dout.
+    """
+    src = _delta_sources(null_src, sources)
+    d = src.shape[-1]
+    dsrc, dq = route_backward(src, q, heads, d, dout, eps)
+    if null_src is None:
+        return dsrc, None, dq
+    return dsrc[1:], dsrc[0].sum(axis=0), dq
+
+
+def _delta_sources(null_src, sources):
+    src = np.asarray(sources, dtype=np.float64)
+    if null_src is None:
+        return src
+    T = src.shape[1]
+    null = np.broadcast_to(np.asarray(null_src, dtype=np.float64), (1, T, src.shape[-1]))
+    return np.concatenate([null, src], axis=0)

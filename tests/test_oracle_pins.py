@@ -472,3 +472,91 @@ def test_full_rms_control_radial_dependence_outside_slice():
     _, alpha_s, _ = route_forward(src, q, H, r, norm="slice")
     assert np.abs(alpha3 - alpha).max() > 1e-3
     np.testing.assert_allclose(alpha3s, alpha_s, rtol=0, atol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# Delta form (oracle reading R8): "Multi-Head Attention Residuals", section 3.3
+# (identity-preserving conversion) and Appendix E (delta variant, Figure 9).
+DELTA_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "delta_examples.json")
+
+
+def load_delta_cases():
+    with open(DELTA_GOLDEN) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", load_delta_cases(), ids=lambda c: c["name"])
+def test_delta_worked_example_exact(case):
+    from oracle import delta_backward, delta_forward
+    q, H = num(case["q"]), case["heads"]
+    null, deltas, partial = num(case["null"]), num(case["deltas"]), num(case["partial"])
+    out, alpha, lse = delta_forward(null, deltas, q, partial, H, eps=0.0)
+    np.testing.assert_allclose(out, num(case["out"]), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(alpha, num(case["alpha"]), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, num(case["lse"]), rtol=0, atol=1e-13)
+    dd, dnull, dq = delta_backward(null, deltas, q, num(case["dout"]), H, eps=0.0)
+    np.testing.assert_allclose(dq, num(case["dq"]), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dnull, num(case["dnull"]), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dd, num(case["ddeltas"]), rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("with_null", [True, False])
+def test_delta_backward_matches_finite_differences(with_null):
+    from oracle import delta_backward, delta_forward
+    rng = np.random.default_rng(16)
+    M, T, d, H = 3, 3, 8, 2
+    null = rng.standard_normal(d) if with_null else None
+    deltas = rng.standard_normal((M, T, d)) * rng.uniform(0.5, 2.0, (M, 1, 1))
+    q = rng.standard_normal(d) * 0.8
+    partial = rng.standard_normal((T, d))
+    dout = rng.standard_normal((T, d))
+
+    def loss():
+        out, _, _ = delta_forward(null, deltas, q, partial, H)
+        return float(np.sum(dout * out))
+
+    h = 1e-6
+
+    def fd(arr, idx):
+        old = arr[idx]
+        arr[idx] = old + h
+        lp = loss()
+        arr[idx] = old - h
+        lm = loss()
+        arr[idx] = old
+        return (lp - lm) / (2 * h)
+
+    dd, dnull, dq = delta_backward(null, deltas, q, dout, H)
+    for arr, grad in ((deltas, dd), (q, dq), (partial, dout)) + (((null, dnull),) if with_null else ()):
+        g = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            g[idx] = fd(arr, idx)
+        np.testing.assert_allclose(grad, g, rtol=1e-6, atol=1e-8)
+    if not with_null:
+        assert dnull is None
+
+
+def test_delta_zero_null_is_a_zero_logit_sink():
+    # A zero null source has a zero normalised key (its RMS is sqrt(eps)), so
+    # it enters every head's softmax with logit 0 and contributes no value:
+    # out_h = sum_n e^{l_n} s_n / (1 + sum_n e^{l_n}) + partial, written here
+    # with scalar loops independently of the oracle.
+    from oracle import delta_forward
+    rng = np.random.default_rng(17)
+    M, T, d, H = 3, 2, 8, 2
+    kv = d // H
+    deltas = rng.standard_normal((M, T, d))
+    q = rng.standard_normal(d)
+    partial = rng.standard_normal((T, d))
+    out, alpha, _ = delta_forward(np.zeros(d), deltas, q, partial, H)
+    for t in range(T):
+        ss = [math.sqrt(sum(float(x) ** 2 for x in deltas[n, t]) / d + 1e-6) for n in range(M)]
+        for h in range(H):
+            w = [math.exp(sum(float(q[h * kv + k]) * float(deltas[n, t, h * kv + k]) / ss[n]
+                              for k in range(kv))) for n in range(M)]
+            z = 1.0 + sum(w)
+            assert alpha[0, t, h] == pytest.approx(1.0 / z, rel=1e-12)
+            for k in range(kv):
+                j = h * kv + k
+                ref = sum(w[n] * float(deltas[n, t, j]) for n in range(M)) / z + partial[t, j]
+                assert out[t, j] == pytest.approx(ref, rel=1e-12, abs=1e-12)
