@@ -226,6 +226,67 @@ attnres_status_t attnres_row_rinv(attnres_bank_t bank, int32_t row, const float*
  * query-gradient partial rows the site pass writes. */
 attnres_status_t attnres_bank_tiling(attnres_bank_t bank, int32_t* out5);
 
+/* ---- Delta form: one self-contained read per call -----------------------
+ * "Multi-Head Attention Residuals", section 3.3 (identity-preserving
+ * conversion) and Appendix E (delta variant; Figure 9, output line): a short
+ * source list, an optional learnable null source shared by every token
+ * (source 0) followed by n_deltas block deltas, scored by the H heads of the
+ * query against full-width RMS-normalised keys (r = d, no gain), mixed per
+ * head, and added to the residual stream:
+ *     out = sum_n alpha_n s_n + partial
+ * Unlike the bank, nothing is shared between calls: every call takes its own
+ * source list and returns fresh gradients.  An output gate on the routed term
+ * belongs to the caller.  Shapes this build handles: with c elements per
+ * 16-byte chunk, d/H must be a multiple of 4c, and 64 * cpt must be a multiple
+ * of d/c for some cpt in {1, 2, 4, 5, 8} with (64 cpt c / d) * H <= 64 (every
+ * wave owns whole tokens; e.g. d = 4096 or 1280 bf16), else
+ * ATTNRES_ERR_UNSUPPORTED.  1 <= n_deltas + (null_src != NULL) <= 16. */
+typedef struct {
+  int64_t tokens;             /* T >= 0 */
+  int32_t d;                  /* value (and key) width */
+  int32_t heads;              /* H, H | d */
+  int32_t n_deltas;           /* block deltas in the list (>= 0) */
+  int32_t dtype;              /* attnres_dtype_t: storage dtype of every [T, d] tensor */
+  float eps;                  /* RMSNorm epsilon (1e-6) */
+  const void* const* deltas;  /* host array [n_deltas] of device [T, d] pointers */
+  const void* null_src;       /* device [d] storage dtype, or NULL for no null source */
+  const void* query;          /* device [d] storage dtype */
+} attnres_delta_t;
+
+/* Device workspace bytes attnres_delta_bwd needs for this call shape (0 if the
+ * shape is invalid; see attnres_last_error). */
+size_t attnres_delta_workspace_bytes(const attnres_delta_t* call);
+
+/* Forward of one delta read.
+ *   partial  device [T, d] storage dtype residual stream added to the routed
+ *            output, or NULL (nothing added)
+ *   out      device [T, d] storage dtype (overwritten)
+ *   alpha    device float32 [n, T, H] softmax weights, n = n_deltas +
+ *            (null_src != NULL), null source first (overwritten)
+ *   lse      device float32 [T, H] log-sum-exp of the logits (overwritten)
+ * All device pointers 16-byte aligned; NULL allowed when tokens == 0. */
+attnres_status_t attnres_delta_fwd(const attnres_delta_t* call, const void* partial, void* out,
+                                   float* alpha, float* lse, attnres_stream_t stream);
+
+/* Backward of one delta read, for the loss <dout, out>.
+ *   dout       device [T, d] storage dtype
+ *   alpha      what attnres_delta_fwd wrote for the same call
+ *   lse        the forward's log-sum-exp; not read (the logits are recomputed
+ *              with the inverse RMS), may be NULL
+ *   d_deltas   host array [n_deltas] of device float32 [T, d]: gradient of
+ *              each delta (stored, not accumulated)
+ *   d_null     device float32 [d]: gradient of the null source (its
+ *              per-token gradients summed over tokens); NULL iff no null source
+ *   dq         device float32 [d]: gradient of the query
+ *   workspace  attnres_delta_workspace_bytes(call) bytes of device memory
+ * The gradient of `partial` is dout itself; nothing is written for it.
+ * Reductions over tokens run in a fixed order: results are bitwise
+ * reproducible. */
+attnres_status_t attnres_delta_bwd(const attnres_delta_t* call, const void* dout,
+                                   const float* alpha, const float* lse, float* const* d_deltas,
+                                   float* d_null, float* dq, void* workspace,
+                                   size_t workspace_bytes, attnres_stream_t stream);
+
 /* Kernel kinds reported by the launch trace. */
 typedef enum {
   ATTNRES_KERNEL_SCORE = 0,     /* append (and transient-source) scoring */

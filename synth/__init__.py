@@ -15,3 +15,4 @@ from .workloads import (  # noqa: F401
     get_workload,
 )
 from .draws import Inputs, bf16_bits, bf16_round, sample_tokens  # noqa: F401
+from .delta import DELTA_SHAPES, DeltaInputs, DeltaShape  # noqa: F401

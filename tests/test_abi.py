@@ -162,3 +162,46 @@ def test_set_gains_order_and_arguments(lib):
         A.attnres_bank_set_gains(b, None, None, stream=0)  # no gains: nothing to launch
     finally:
         A.attnres_bank_destroy(b)
+
+
+def delta_call(**kw):
+    base = dict(tokens=64, d=4096, heads=8, deltas=[FAKE] * 8, null_src=FAKE, query=FAKE,
+                dtype=A.ATTNRES_BF16)
+    base.update(kw)
+    return A.make_delta_call(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=4000), A.ATTNRES_ERR_UNSUPPORTED),           # no whole-token wave layout
+    (dict(d=512, heads=32), A.ATTNRES_ERR_UNSUPPORTED),  # d/H not a multiple of 4 chunks
+    (dict(heads=3), A.ATTNRES_ERR_INVALID),
+    (dict(deltas=[FAKE] * 16), A.ATTNRES_ERR_INVALID),   # 17 sources with the null
+    (dict(deltas=[], null_src=None), A.ATTNRES_ERR_INVALID),
+    (dict(query=FAKE + 4), A.ATTNRES_ERR_INVALID),
+    (dict(deltas=[FAKE, 0]), A.ATTNRES_ERR_INVALID),
+])
+def test_delta_bad_calls_rejected(lib, kw, status):
+    c = delta_call(**kw)
+    assert lib.attnres_delta_workspace_bytes(ctypes.byref(c)) == 0
+    with pytest.raises(A.AttnResError) as e:  # shape checks run before any launch
+        A.attnres_delta_bwd(c, FAKE, FAKE, FAKE, [FAKE] * 16, FAKE, FAKE, FAKE, 1 << 40,
+                            stream=0)
+    assert e.value.status == status
+
+
+def test_delta_workspace_and_argument_checks(lib):
+    c = delta_call()
+    n = A.attnres_delta_workspace_bytes(c)
+    assert n >= 2 * 16 * 4096 * 4  # 16 work-groups for 64 tokens: dq and null partials
+    for kw in (dict(d=1280), dict(d=64, heads=4, dtype=A.ATTNRES_F32), dict(d=2048)):
+        assert A.attnres_delta_workspace_bytes(delta_call(**kw)) > 0
+    with pytest.raises(A.AttnResError) as e:  # d_null without a null source
+        A.attnres_delta_bwd(delta_call(null_src=None), FAKE, FAKE, FAKE, [FAKE] * 8, FAKE, FAKE,
+                            FAKE, n, stream=0)
+    assert e.value.status == A.ATTNRES_ERR_INVALID
+    with pytest.raises(A.AttnResError) as e:  # workspace too small
+        A.attnres_delta_bwd(c, FAKE, FAKE, FAKE, [FAKE] * 8, FAKE, FAKE, FAKE, n - 1, stream=0)
+    assert e.value.status == A.ATTNRES_ERR_CAPACITY
+    with pytest.raises(A.AttnResError) as e:  # out missing
+        A.attnres_delta_fwd(c, None, None, FAKE, FAKE, stream=0)
+    assert e.value.status == A.ATTNRES_ERR_INVALID

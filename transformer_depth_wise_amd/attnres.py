@@ -43,6 +43,9 @@ EXPORTS = (
     "attnres_site_saved",
     "attnres_row_rinv",
     "attnres_bank_tiling",
+    "attnres_delta_workspace_bytes",
+    "attnres_delta_fwd",
+    "attnres_delta_bwd",
     "attnres_trace_enable",
     "attnres_trace_read",
     "attnres_probe_sink_words",
@@ -65,6 +68,20 @@ class Config(ctypes.Structure):
         ("dtype", c_int32),
         ("eps", c_float),
         ("norm", c_int32),
+    ]
+
+
+class DeltaCallC(ctypes.Structure):
+    _fields_ = [
+        ("tokens", c_int64),
+        ("d", c_int32),
+        ("heads", c_int32),
+        ("n_deltas", c_int32),
+        ("dtype", c_int32),
+        ("eps", c_float),
+        ("deltas", POINTER(c_void_p)),
+        ("null_src", c_void_p),
+        ("query", c_void_p),
     ]
 
 
@@ -99,6 +116,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "attnres_site_saved": (i32, [vp, i32, POINTER(vp), POINTER(vp), POINTER(i32)]),
         "attnres_row_rinv": (i32, [vp, i32, POINTER(vp)]),
         "attnres_bank_tiling": (i32, [vp, POINTER(i32)]),
+        "attnres_delta_workspace_bytes": (c_size_t, [POINTER(DeltaCallC)]),
+        "attnres_delta_fwd": (i32, [POINTER(DeltaCallC), vp, vp, vp, vp, vp]),
+        "attnres_delta_bwd": (i32, [POINTER(DeltaCallC), vp, vp, vp, POINTER(vp), vp, vp, vp,
+                                    c_size_t, vp]),
         "attnres_trace_enable": (i32, [vp, i32]),
         "attnres_trace_read": (i32, [vp, POINTER(ctypes.c_double), POINTER(c_int64)]),
         "attnres_probe_sink_words": (i32, []),
@@ -336,3 +357,77 @@ class Bank:
     def rinv(self, row):
         p = attnres_row_rinv(self.handle, row)
         return self._ws_view(p, self.T)
+
+
+# ---------------------------------------------------------------------------
+# Delta form: one self-contained read per call.
+def make_delta_call(tokens, d, heads, deltas, null_src, query, dtype, eps=1e-6):
+    """The C description of one delta read; `deltas` is a list of device
+    tensors or addresses (kept alive by the caller)."""
+    ptrs = (c_void_p * max(len(deltas), 1))(*[_ptr(x) for x in deltas])
+    call = DeltaCallC(int(tokens), int(d), int(heads), len(deltas), int(dtype), float(eps),
+                      ctypes.cast(ptrs, POINTER(c_void_p)), _ptr(null_src), _ptr(query))
+    call._ptrs = ptrs  # keep the pointer array alive with the struct
+    return call
+
+
+def attnres_delta_workspace_bytes(call) -> int:
+    n = load_library().attnres_delta_workspace_bytes(ctypes.byref(call))
+    if n == 0:
+        raise AttnResError(ATTNRES_ERR_INVALID, last_error())
+    return int(n)
+
+
+def attnres_delta_fwd(call, partial, out, alpha, lse, stream=None) -> None:
+    _check(load_library().attnres_delta_fwd(ctypes.byref(call), _ptr(partial), _ptr(out),
+                                            _ptr(alpha), _ptr(lse), _stream(stream)))
+
+
+def attnres_delta_bwd(call, dout, alpha, lse, d_deltas, d_null, dq, workspace, workspace_bytes,
+                      stream=None) -> None:
+    arr = (c_void_p * max(len(d_deltas), 1))(*[_ptr(x) for x in d_deltas])
+    _check(load_library().attnres_delta_bwd(ctypes.byref(call), _ptr(dout), _ptr(alpha),
+                                            _ptr(lse), arr, _ptr(d_null), _ptr(dq),
+                                            _ptr(workspace), int(workspace_bytes),
+                                            _stream(stream)))
+
+
+class DeltaRead:
+    """One delta read over device tensors: deltas (list of [T, d]), an optional
+    null source [d] and the query [d], all in the storage dtype."""
+
+    def __init__(self, deltas, null_src, query, heads, tokens=None, eps=1e-6):
+        import torch
+        self.torch = torch
+        self.deltas, self.null_src, self.query = list(deltas), null_src, query
+        if tokens is None:
+            if not deltas:
+                raise ValueError("tokens must be given when there are no deltas")
+            tokens = deltas[0].shape[0]
+        self.T = int(tokens)
+        self.d = int(query.shape[0])
+        self.H = int(heads)
+        self.tdtype = query.dtype
+        dt = ATTNRES_BF16 if query.dtype == torch.bfloat16 else ATTNRES_F32
+        self.call = make_delta_call(self.T, self.d, self.H, self.deltas, null_src, query, dt, eps)
+        self.n = len(self.deltas) + (1 if null_src is not None else 0)
+
+    def forward(self, partial=None, stream=None):
+        torch = self.torch
+        out = torch.empty((self.T, self.d), dtype=self.tdtype, device="cuda")
+        alpha = torch.empty((self.n, self.T, self.H), dtype=torch.float32, device="cuda")
+        lse = torch.empty((self.T, self.H), dtype=torch.float32, device="cuda")
+        attnres_delta_fwd(self.call, partial, out, alpha, lse, stream)
+        return out, alpha, lse
+
+    def backward(self, dout, alpha, lse, stream=None):
+        torch = self.torch
+        dd = [torch.empty((self.T, self.d), dtype=torch.float32, device="cuda")
+              for _ in self.deltas]
+        dn = (torch.empty(self.d, dtype=torch.float32, device="cuda")
+              if self.null_src is not None else None)
+        dq = torch.empty(self.d, dtype=torch.float32, device="cuda")
+        nbytes = attnres_delta_workspace_bytes(self.call)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        attnres_delta_bwd(self.call, dout, alpha, lse, dd, dn, dq, ws, nbytes, stream)
+        return dd, dn, dq

@@ -628,6 +628,162 @@ attnres_status_t attnres_bank_tiling(attnres_bank_t b, int32_t* out5) {
   return ATTNRES_OK;
 }
 
+// ---- delta form -------------------------------------------------------------
+
+namespace {
+
+attnres_status_t delta_geom(const attnres_delta_t* c, attnres::DeltaGeom* g) {
+  if (!c) return fail(ATTNRES_ERR_INVALID, "delta call is NULL");
+  if (c->tokens < 0) return fail(ATTNRES_ERR_INVALID, "tokens must be >= 0");
+  if (c->dtype != ATTNRES_F32 && c->dtype != ATTNRES_BF16)
+    return fail(ATTNRES_ERR_INVALID, "dtype must be ATTNRES_F32 or ATTNRES_BF16 (got %d)", c->dtype);
+  if (c->heads < 1 || c->d < 1 || c->d % c->heads)
+    return fail(ATTNRES_ERR_INVALID, "need heads >= 1 dividing d (got d=%d heads=%d)", c->d, c->heads);
+  if (!(c->eps > 0.f)) return fail(ATTNRES_ERR_INVALID, "eps must be > 0");
+  const int n = c->n_deltas + (c->null_src ? 1 : 0);
+  if (c->n_deltas < 0 || n < 1 || n > attnres::kMaxDeltaSources)
+    return fail(ATTNRES_ERR_INVALID, "need 1 <= n_deltas + null <= %d sources (got %d)",
+                attnres::kMaxDeltaSources, n);
+  const int pc = c->dtype == ATTNRES_F32 ? 4 : 8;
+  const int kv = c->d / c->heads;
+  if (kv % (4 * pc))
+    return fail(ATTNRES_ERR_UNSUPPORTED, "d/H = %d must be a multiple of %d", kv, 4 * pc);
+  const int cpr = c->d / pc;
+  static const int kCpts[] = {1, 2, 4, 5, 8};
+  int cpt = 0, tw = 0;
+  for (int x : kCpts) {
+    if ((64 * x) % cpr) continue;
+    const int t = 64 * x / cpr;
+    if (t * c->heads > 64) continue;
+    cpt = x;
+    tw = t;
+    break;
+  }
+  if (!cpt)
+    return fail(ATTNRES_ERR_UNSUPPORTED,
+                "d=%d: no wave layout owns whole tokens (64*cpt must be a multiple of %d chunks)",
+                c->d, cpr);
+  if (c->tokens > ((int64_t)1 << 31) / c->d)
+    return fail(ATTNRES_ERR_UNSUPPORTED, "tokens * d must stay below 2^31");
+  g->T = c->tokens;
+  g->d = c->d;
+  g->H = c->heads;
+  g->kv = kv;
+  g->pc = pc;
+  g->cpr = cpr;
+  g->kvc = kv / pc;
+  g->cpt = cpt;
+  g->tw = tw;
+  g->n = n;
+  g->eps = c->eps;
+  if (attnres::delta_lds_bytes(*g, true) > 160 * 1024 || attnres::delta_lds_bytes(*g, false) > 160 * 1024)
+    return fail(ATTNRES_ERR_UNSUPPORTED, "delta call needs more LDS than a work-group has");
+  if (c->tokens > 0) {
+    if (!c->query || !aligned16(c->query) || (c->null_src && !aligned16(c->null_src)))
+      return fail(ATTNRES_ERR_INVALID, "query (and null_src) must be non-NULL, 16-byte aligned");
+    if (c->n_deltas > 0 && !c->deltas) return fail(ATTNRES_ERR_INVALID, "deltas array is NULL");
+    for (int k = 0; k < c->n_deltas; ++k)
+      if (!c->deltas[k] || !aligned16(c->deltas[k]))
+        return fail(ATTNRES_ERR_INVALID, "delta %d must be non-NULL and 16-byte aligned", k);
+  }
+  return ATTNRES_OK;
+}
+
+attnres::DeltaArgs delta_args(const attnres_delta_t* c) {
+  attnres::DeltaArgs a{};
+  a.null_src = c->null_src;
+  a.query = c->query;
+  for (int k = 0; k < c->n_deltas && c->tokens > 0; ++k) a.deltas[k] = c->deltas[k];
+  return a;
+}
+
+}  // namespace
+
+// Backward workspace: dq partials and null-gradient vector partials
+// [parts][d] each, null-gradient scalar partials [parts][H + 1].
+struct DeltaWs {
+  size_t dq, nv, ns, total;
+};
+DeltaWs delta_ws(const attnres::DeltaGeom& g) {
+  const size_t parts = (size_t)attnres::delta_bwd_parts(g);
+  DeltaWs w{};
+  w.dq = 0;
+  w.nv = align256(sizeof(float) * parts * g.d);
+  w.ns = w.nv + align256(sizeof(float) * parts * g.d);
+  w.total = w.ns + align256(sizeof(float) * parts * (g.H + 1));
+  return w;
+}
+
+size_t attnres_delta_workspace_bytes(const attnres_delta_t* call) {
+  attnres::DeltaGeom g{};
+  if (delta_geom(call, &g) != ATTNRES_OK) return 0;
+  return delta_ws(g).total;
+}
+
+attnres_status_t attnres_delta_fwd(const attnres_delta_t* call, const void* partial, void* out,
+                                   float* alpha, float* lse, attnres_stream_t stream) {
+  attnres::DeltaGeom g{};
+  attnres_status_t st = delta_geom(call, &g);
+  if (st != ATTNRES_OK) return st;
+  if (g.T == 0) return ATTNRES_OK;
+  if (!out || !alpha || !lse) return fail(ATTNRES_ERR_INVALID, "out, alpha and lse must be non-NULL");
+  if (!aligned16(out) || !aligned16(alpha) || !aligned16(lse) || (partial && !aligned16(partial)))
+    return fail(ATTNRES_ERR_INVALID, "out, alpha, lse and partial must be 16-byte aligned");
+  hipError_t e = attnres::launch_delta_fwd(g, call->dtype, delta_args(call), partial, out, alpha,
+                                           lse, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTNRES_OK : hip_fail(e, "delta forward kernel");
+}
+
+attnres_status_t attnres_delta_bwd(const attnres_delta_t* call, const void* dout,
+                                   const float* alpha, const float* lse, float* const* d_deltas,
+                                   float* d_null, float* dq, void* workspace,
+                                   size_t workspace_bytes, attnres_stream_t stream) {
+  attnres::DeltaGeom g{};
+  attnres_status_t st = delta_geom(call, &g);
+  if (st != ATTNRES_OK) return st;
+  if (!dq || !aligned16(dq)) return fail(ATTNRES_ERR_INVALID, "dq must be non-NULL, 16-byte aligned");
+  if ((d_null != nullptr) != (call->null_src != nullptr))
+    return fail(ATTNRES_ERR_INVALID, "d_null must be given exactly when the call has a null source");
+  if (d_null && !aligned16(d_null)) return fail(ATTNRES_ERR_INVALID, "d_null must be 16-byte aligned");
+  const DeltaWs ws = delta_ws(g);
+  if (!workspace || !aligned16(workspace))
+    return fail(ATTNRES_ERR_INVALID, "workspace must be non-NULL and 16-byte aligned");
+  if (workspace_bytes < ws.total)
+    return fail(ATTNRES_ERR_CAPACITY, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                ws.total);
+  attnres::DeltaGrads dg{};
+  (void)lse;  // the backward recomputes the logits; lse is part of the saved state
+  if (g.T > 0) {
+    if (!dout || !alpha || !aligned16(dout) || !aligned16(alpha))
+      return fail(ATTNRES_ERR_INVALID, "dout and alpha must be non-NULL and 16-byte aligned");
+    if (call->n_deltas > 0 && !d_deltas) return fail(ATTNRES_ERR_INVALID, "d_deltas array is NULL");
+    for (int k = 0; k < call->n_deltas; ++k) {
+      if (!d_deltas[k] || !aligned16(d_deltas[k]))
+        return fail(ATTNRES_ERR_INVALID, "d_deltas[%d] must be non-NULL and 16-byte aligned", k);
+      dg.d[k] = d_deltas[k];
+    }
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int parts = g.T > 0 ? attnres::delta_bwd_parts(g) : 0;
+  char* w = static_cast<char*>(workspace);
+  float* dq_part = reinterpret_cast<float*>(w + ws.dq);
+  float* nv_part = reinterpret_cast<float*>(w + ws.nv);
+  float* ns_part = reinterpret_cast<float*>(w + ws.ns);
+  const attnres::DeltaArgs args = delta_args(call);
+  hipError_t e = attnres::launch_delta_bwd(g, call->dtype, args, dout, alpha, dg, dq_part, ns_part,
+                                           parts, s);
+  if (e != hipSuccess) return hip_fail(e, "delta backward kernel");
+  // With no tokens there are no parts and the reductions write zeros.
+  e = attnres::launch_dq_reduce(dq_part, parts, g.d, dq, nullptr, nullptr, nullptr, s);
+  if (e != hipSuccess) return hip_fail(e, "delta dq reduction");
+  if (d_null) {
+    e = attnres::launch_delta_null(g, call->dtype, args, dout, alpha, nv_part, ns_part, parts,
+                                   d_null, s);
+    if (e != hipSuccess) return hip_fail(e, "delta null-source gradient");
+  }
+  return ATTNRES_OK;
+}
+
 attnres_status_t attnres_row_rinv(attnres_bank_t b, int32_t row, const float** rinv) {
   if (!b) return fail(ATTNRES_ERR_INVALID, "bank is NULL");
   if (row < 0 || row >= b->rows_committed)

@@ -104,6 +104,39 @@ hipError_t launch_finalize(const Geom& g, int dtype, const FinalizeJob* jobs, in
 // Number of dq partial rows the site pass writes for this geometry.
 int bwd_site_parts(const Geom& g);
 
+// Delta-form read (attnres_delta.hip): one self-contained read per call.
+constexpr int kMaxDeltaSources = 16;
+struct DeltaGeom {
+  int64_t T;
+  int32_t d, H, kv, pc, cpr, kvc;
+  int32_t cpt;  // 16-byte chunks per lane
+  int32_t tw;   // tokens owned by each wave: 64 * cpt / cpr
+  int32_t n;    // sources of the call (null source first, if any)
+  float eps;
+};
+struct DeltaArgs {
+  const void* null_src;  // [d] or NULL
+  const void* query;     // [d]
+  const void* deltas[kMaxDeltaSources];
+};
+struct DeltaGrads {
+  float* d[kMaxDeltaSources];  // float32 [T, d] gradient of each delta
+};
+size_t delta_lds_bytes(const DeltaGeom& g, bool fwd);
+int delta_bwd_parts(const DeltaGeom& g);
+hipError_t launch_delta_fwd(const DeltaGeom& g, int dtype, const DeltaArgs& a, const void* partial,
+                            void* out, float* alpha, float* lse, hipStream_t st);
+// Backward: delta gradients, dq partials [parts][d] and the null source's
+// scalar partials [parts][H + 1].
+hipError_t launch_delta_bwd(const DeltaGeom& g, int dtype, const DeltaArgs& a, const void* dout,
+                            const float* alpha, const DeltaGrads& dg, float* dq_part,
+                            float* ns_part, int parts, hipStream_t st);
+// Null-source gradient: weighted dout column sums into nv_part [parts][d],
+// then the fixed-order combination with the scalar partials into dnull [d].
+hipError_t launch_delta_null(const DeltaGeom& g, int dtype, const DeltaArgs& a, const void* dout,
+                             const float* alpha0, float* nv_part, const float* ns_part, int parts,
+                             float* dnull, hipStream_t st);
+
 // Bandwidth probes (attnres_probe.hip).
 int probe_blocks();
 hipError_t launch_probe_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t st);
