@@ -217,6 +217,161 @@ def load_counters(workload: str):
     return out if stamp == source_hash() else None
 
 
+# ---------------------------------------------------------------------------
+# Delta form at the pages' 8B setting ("Multi-Head Attention Residuals",
+# section 3.3 and Appendix E, delta variant): 32 layers x 2 sublayers = 64
+# routing calls per microbatch; call i sits in block b = i // 8 (blocks of
+# four layers) at position p = i % 8 and reads the null source, the b
+# completed block deltas and, once p > 0, the running delta of block b.
+DELTA_SITES = 64
+DELTA_SITES_PER_BLOCK = 8
+
+
+def delta_schedule():
+    """Number of block deltas each call reads (the null source comes on top)."""
+    return [i // DELTA_SITES_PER_BLOCK + (1 if i % DELTA_SITES_PER_BLOCK else 0)
+            for i in range(DELTA_SITES)]
+
+
+def delta_bytes(shape, m: int):
+    """Algorithmic bytes of one delta call with m block deltas: (fwd, bwd)."""
+    T, d, H, b = shape.tokens, shape.d, shape.heads, 2 if shape.dtype == "bf16" else 4
+    n = m + 1
+    fwd = m * T * d * b + d * b + 2 * T * d * b + 4 * n * T * H + 4 * T * H  # + partial, out
+    # two passes over the deltas, dout (and once more for the null sum), alpha,
+    # float32 delta gradients
+    bwd = 2 * m * T * d * b + 2 * d * b + 2 * T * d * b + 4 * n * T * H + 4 * m * T * d
+    return fwd, bwd
+
+
+def delta_cpu_baseline(shape, tokens: int):
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import delta_backward, delta_forward
+    from synth import DeltaInputs
+
+    s = shape.with_tokens(tokens)
+    inp = DeltaInputs(s)
+    deltas = np.stack([inp.value("delta", m) for m in range(s.n_deltas)]).astype(np.float64)
+    null = inp.value("null").astype(np.float64)
+    q = inp.value("query").astype(np.float64)
+    part = inp.value("partial").astype(np.float64)
+    dout = inp.value("dout").astype(np.float64)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for m in delta_schedule():
+            delta_forward(null, deltas[:m], q, part, s.heads, s.eps)
+            delta_backward(null, deltas[:m], q, dout, s.heads, s.eps)
+        dt = time.perf_counter() - t0
+    return {
+        "value": round(dt * 1e3 * shape.tokens / tokens, 1),
+        "unit": "ms/microbatch",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{tokens} of {shape.tokens} tokens, all {DELTA_SITES} calls fwd+bwd, NumPy "
+                   f"fp64 oracle on one thread ({cpu_model()}); measured {dt:.2f} s, scaled "
+                   f"linearly in tokens"),
+    }
+
+
+def bench_delta(args):
+    import torch
+
+    from synth import DELTA_SHAPES, DeltaInputs
+    from synth.device import to_device
+    from transformer_depth_wise_amd.attnres import (ATTNRES_BF16, attnres_delta_bwd,
+                                                    attnres_delta_fwd,
+                                                    attnres_delta_workspace_bytes,
+                                                    make_delta_call)
+
+    shape = DELTA_SHAPES[args.workload]
+    torch.cuda.set_device(0)
+    inp = DeltaInputs(shape)
+    T, d, H = shape.tokens, shape.d, shape.heads
+    deltas = [to_device(inp.value("delta", m), shape.dtype) for m in range(shape.n_deltas)]
+    null = to_device(inp.value("null"), shape.dtype)
+    queries = [to_device(inp.value("query"), shape.dtype) for _ in range(DELTA_SITES)]
+    partial = to_device(inp.value("partial"), shape.dtype)
+    dout = to_device(inp.value("dout"), shape.dtype)
+    sched = delta_schedule()
+    calls = [make_delta_call(T, d, H, deltas[:m], null, queries[i], ATTNRES_BF16, shape.eps)
+             for i, m in enumerate(sched)]
+    tdt = torch.bfloat16
+    out = torch.empty((T, d), dtype=tdt, device="cuda")
+    alphas = [torch.empty((m + 1, T, H), dtype=torch.float32, device="cuda") for m in sched]
+    lses = [torch.empty((T, H), dtype=torch.float32, device="cuda") for _ in sched]
+    dds = [torch.empty((T, d), dtype=torch.float32, device="cuda") for _ in range(shape.n_deltas)]
+    dnull = torch.empty(d, dtype=torch.float32, device="cuda")
+    dq = torch.empty(d, dtype=torch.float32, device="cuda")
+    nbytes = max(attnres_delta_workspace_bytes(c) for c in calls)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    print(f"[bench] {shape.describe()}: {DELTA_SITES} calls per microbatch", file=sys.stderr,
+          flush=True)
+
+    def fwd_phase():
+        for i, c in enumerate(calls):
+            attnres_delta_fwd(c, partial, out, alphas[i], lses[i])
+
+    def bwd_phase():
+        for i in reversed(range(DELTA_SITES)):
+            attnres_delta_bwd(calls[i], dout, alphas[i], lses[i], dds[:sched[i]], dnull, dq, ws,
+                              nbytes)
+
+    for _ in range(args.warmup):
+        fwd_phase()
+        bwd_phase()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    t_f = t_b = 0.0
+    for _ in range(args.steps):
+        ev[0].record()
+        fwd_phase()
+        ev[1].record()
+        bwd_phase()
+        ev[2].record()
+        torch.cuda.synchronize()
+        t_f += ev[0].elapsed_time(ev[1])
+        t_b += ev[1].elapsed_time(ev[2])
+    ms_f, ms_b = t_f / args.steps, t_b / args.steps
+    ms = ms_f + ms_b
+    fb = [delta_bytes(shape, m) for m in sched]
+    by_f, by_b = sum(x[0] for x in fb), sum(x[1] for x in fb)
+    print(f"[bench] {args.steps} steps: {ms:.3f} ms/microbatch (fwd {ms_f:.3f}, bwd {ms_b:.3f})",
+          file=sys.stderr, flush=True)
+    kern = {"delta_fwd": {"ms_per_microbatch": round(ms_f, 3),
+                          "launches_per_microbatch": DELTA_SITES,
+                          "gbps": round(by_f / ms_f / 1e6, 1)},
+            "delta_bwd": {"ms_per_microbatch": round(ms_b, 3),
+                          "launches_per_microbatch": DELTA_SITES,
+                          "gbps": round(by_b / ms_b / 1e6, 1)}}
+    dom = max(kern, key=lambda k: kern[k]["ms_per_microbatch"])
+    a = kern[dom]["gbps"]
+    result = {
+        "metric": METRIC, "value": round(ms, 3), "unit": "ms/microbatch", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic: seeded N(0,1) block deltas x U(0.5,2), N(0,1) null source and "
+                "residual stream, N(0,0.02^2) queries, N(0,1) upstream gradients, bf16 storage",
+        "config": {"workload": shape.name, "tokens": T, "d": d, "heads": H,
+                   "calls": DELTA_SITES, "max_sources": max(sched) + 1, "storage": shape.dtype,
+                   "note": "phase time of the fwd (and bwd) launches of all calls, "
+                           "no recomputation"},
+        "achieved_gbps": round((by_f + by_b) / ms / 1e6, 1),
+        "pct_of_peak": round(100.0 * (by_f + by_b) / ms / 1e6 / HBM_PEAK_GBPS, 1),
+        "alg_bytes_per_microbatch": by_f + by_b,
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(a / HBM_PEAK_GBPS, 3), "traffic": None,
+                     "alg_bytes_per_launch": int((by_f if dom == "delta_fwd" else by_b)
+                                                 / DELTA_SITES)},
+        "kernels": kern,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = delta_cpu_baseline(shape, 16)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -245,6 +400,11 @@ def main():
               "and shards over tokens with no exchange but a dq all-reduce (see DESIGN.md); "
               "run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    from synth import DELTA_SHAPES
+    if args.workload in DELTA_SHAPES:
+        bench_delta(args)
+        return
 
     import torch
 

@@ -17,8 +17,9 @@ from gpu_harness import ALPHA_TOL, TOL, log, max_rel
 
 pytestmark = pytest.mark.gpu
 
-# Shapes spanning every compiled chunks-per-lane layout, ragged token tails,
-# with and without a null source and a residual stream.
+# Shapes spanning every compiled chunks-per-lane layout (whole tokens per
+# wave, and two waves per token for d = 2048 / 4096 bf16 and d = 2048 fp32),
+# ragged token tails, with and without a null source and a residual stream.
 CASES = [
     DeltaShape("f32_d64_h4", 37, 64, 4, 3, dtype="f32"),            # 1 chunk/lane, 4 tokens/wave
     DeltaShape("f32_d64_h4_bare", 37, 64, 4, 3, null=False, partial=False, dtype="f32"),
@@ -30,6 +31,7 @@ CASES = [
     DeltaShape("bf16_d4096_h8", 9, 4096, 8, 8),                     # the 8B shape, 8 chunks/lane
     DeltaShape("bf16_d4096_h8_one", 6, 4096, 8, 0),                 # null source only
     DeltaShape("bf16_d4096_h8_t1", 1, 4096, 8, 8),
+    DeltaShape("f32_d2048_h4_split", 11, 2048, 4, 2, dtype="f32"),  # two waves per token
 ]
 
 

@@ -28,7 +28,6 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
 constexpr int kDThreads = 256;
 constexpr int kDWaves = kDThreads / 64;
-constexpr int kMaxHeadsFinish = 64;  // heads the null-gradient finish handles
 
 __device__ __forceinline__ uint32_t to_bf16_bits(float f) {
   uint32_t u = __float_as_uint(f);
@@ -535,19 +534,17 @@ __global__ __launch_bounds__(kDThreads) void k_delta_null_vec(DeltaGeom g,
   }
 }
 
-// The null-source gradient from the partials, in a fixed order:
-//   dnull = sum_p nv[p] + rho_0^-1 q (sum_p dl[p][h]) - (rho_0^-2 / d) (sum_p c[p]) s_0,
+// The null-source gradient from the reduced sums (nv: [d], ns: [H + 1]):
+//   dnull = nv + rho_0^-1 q ns[h] - (rho_0^-2 / d) ns[H] s_0,
 // rho_0 being the null source's inverse RMS (one row for every token).
 template <typename T>
 __global__ __launch_bounds__(kDThreads) void k_delta_null_finish(DeltaGeom g, DeltaArgs a,
-                                                                 const float* __restrict__ nv_part,
-                                                                 const float* __restrict__ ns_part,
-                                                                 int parts,
+                                                                 const float* __restrict__ nv,
+                                                                 const float* __restrict__ ns,
                                                                  float* __restrict__ dnull) {
   using V = DVec<T>;
   constexpr int N = V::N;
   __shared__ float s_red[kDThreads];
-  __shared__ float s_sum[kMaxHeadsFinish + 1];
   const T* null = static_cast<const T*>(a.null_src);
   const T* qv = static_cast<const T*>(a.query);
   auto val = [&](const T* p, int i) {
@@ -561,21 +558,358 @@ __global__ __launch_bounds__(kDThreads) void k_delta_null_finish(DeltaGeom g, De
     ss += v * v;
   }
   s_red[threadIdx.x] = ss;
-  if (threadIdx.x <= g.H) {
-    float s = 0.f;
-    for (int p = 0; p < parts; ++p) s += ns_part[(int64_t)p * (g.H + 1) + threadIdx.x];
-    s_sum[threadIdx.x] = s;
-  }
   __syncthreads();
   float tot = 0.f;
   for (int i = 0; i < kDThreads; ++i) tot += s_red[i];
   const float ri = rsqrtf(tot / (float)g.d + g.eps);
-  const float rc = ri * ri / (float)g.d * s_sum[g.H];
-  for (int col = blockIdx.x * kDThreads + threadIdx.x; col < g.d; col += gridDim.x * kDThreads) {
-    float v = 0.f;
-    for (int p = 0; p < parts; ++p) v += nv_part[(int64_t)p * g.d + col];
-    const int h = col / g.kv;
-    dnull[col] = v + ri * s_sum[h] * val(qv, col) - rc * val(null, col);
+  const float rc = ri * ri / (float)g.d * ns[g.H];
+  for (int col = blockIdx.x * kDThreads + threadIdx.x; col < g.d; col += gridDim.x * kDThreads)
+    dnull[col] = nv[col] + ri * ns[col / g.kv] * val(qv, col) - rc * val(null, col);
+}
+
+// ---------------------------------------------------------------------------
+// Split layout for wide rows (d/c a multiple of 128 chunks, H even): two
+// waves share a token, wave half = 0 / 1 holding chunks [half * 64 CPT,
+// (half + 1) * 64 CPT) of the row, i.e. heads [half * H/2, (half + 1) * H/2),
+// so per-head dots stay inside one wave and each lane carries half the
+// state.  A work-group of 4 waves owns 2 tokens.  Only the full-width sum of
+// squares crosses the pair (through LDS and a work-group barrier: per source
+// in the forward, after the first pass in the backward), and in the backward
+// the radial sum.
+struct SplitLane {
+  int half, ts;  // chunk half of the row, token slot of the work-group
+};
+
+template <typename T, int CPT>
+__global__ __launch_bounds__(kDThreads) void k_delta_fwd_s(DeltaGeom g, DeltaArgs a,
+                                                           const T* __restrict__ partial,
+                                                           T* __restrict__ out,
+                                                           float* __restrict__ alpha,
+                                                           float* __restrict__ lse) {
+  using V = DVec<T>;
+  constexpr int N = V::N;
+  constexpr int SPAN = 64 * CPT;  // chunks per wave
+  extern __shared__ float sm[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = wave & 1, ts = wave >> 1;
+  const int hw = g.H >> 1;  // heads of this wave
+  const int parts = SPAN >> 2;
+  const int fw = 2 * parts + 3 * hw + g.n * hw;
+  uint4* s_q = reinterpret_cast<uint4*>(sm);
+  float* s_ss = sm + 4 * g.cpr;             // [2 token slots][2 halves] per source step
+  float* base = s_ss + 4;
+  float* w_part = base + wave * fw;
+  float* w_ssh = w_part + 2 * parts;
+  float* w_coef = w_ssh + hw;
+  float* w_logit = w_coef + 2 * hw;
+
+  for (int c = threadIdx.x; c < g.cpr; c += kDThreads) s_q[c] = static_cast<const uint4*>(a.query)[c];
+
+  const int64_t t = xcd_rank(blockIdx.x, gridDim.x) * 2 + ts;
+  const bool valid = t < g.T;
+  const int64_t tt = valid ? t : 0;  // invalid token slots read token 0, store nothing
+  const int c0 = half * SPAN;
+  const int h0 = half * hw;
+  __syncthreads();
+
+  float acc[CPT][N];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j)
+#pragma unroll
+    for (int e = 0; e < N; ++e) acc[j][e] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  auto load_row = [&](int k, uint4 (&x)[CPT]) {
+    const bool bc = a.null_src && k == 0;
+    const uint4* p = source_chunks<T>(a, k, bc ? 0 : tt, g.d);
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int c = c0 + lane + 64 * j;
+      x[j] = bc ? p[c] : ld_nt(p + c);
+    }
+  };
+  // one source: request the next, then score and fold this one in (called
+  // twice per loop iteration so both row buffers are named statically)
+  auto step = [&](int k, uint4 (&x)[CPT], uint4 (&nx)[CPT]) {
+    if (k + 1 < g.n) load_row(k + 1, nx);
+    float wss = 0.f;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int c = c0 + lane + 64 * j;
+      const float qd = quad_sum(V::dot(s_q[c], x[j]));
+      const float ss = quad_sum(V::dot(x[j], x[j]));
+      const int q = lane + 64 * j;
+      if ((q & 3) == 0) {
+        w_part[2 * (q >> 2)] = qd;
+        w_part[2 * (q >> 2) + 1] = ss;
+      }
+      wss += ss;
+    }
+    wave_fence();
+    float hd = 0.f;
+    if (lane < hw) {
+      const float* pp = w_part + 2 * ((lane * g.kvc) >> 2);
+      for (int i = 0; i < (g.kvc >> 2); ++i) hd += pp[2 * i];
+    }
+    // the wave's sum of squares: every quad leader's value once (lanes 4i)
+    float s2 = (lane & 3) == 0 ? wss : 0.f;
+#pragma unroll
+    for (int o = 32; o >= 4; o >>= 1) s2 += __shfl_xor(s2, o, 64);
+    if (lane == 0) s_ss[ts * 2 + half] = s2;
+    __syncthreads();
+    const float tot = s_ss[ts * 2] + s_ss[ts * 2 + 1];
+    if (lane < hw) {
+      const float lg = rsqrtf(tot / (float)g.d + g.eps) * hd;
+      const float mn = fmaxf(m, lg);
+      const float sc = expf(m - mn);
+      const float wt = expf(lg - mn);
+      l = l * sc + wt;
+      m = mn;
+      w_coef[2 * lane] = sc;
+      w_coef[2 * lane + 1] = wt;
+      w_logit[k * hw + lane] = lg;
+    }
+    wave_fence();
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int hl = (lane + 64 * j) / g.kvc;  // head of the chunk, within this half
+      const float sc = w_coef[2 * hl], wt = w_coef[2 * hl + 1];
+      float f[N];
+      V::unpack(x[j], f);
+#pragma unroll
+      for (int e = 0; e < N; ++e) acc[j][e] = acc[j][e] * sc + wt * f[e];
+    }
+    __syncthreads();  // s_ss and the coefficients are read before the next source
+  };
+  {
+    uint4 b0[CPT], b1[CPT];
+    load_row(0, b0);
+    for (int k = 0; k < g.n; k += 2) {
+      step(k, b0, b1);
+      if (k + 1 < g.n) step(k + 1, b1, b0);
+    }
+  }
+  float ls = 0.f;
+  if (lane < hw) {
+    ls = m + logf(l);
+    w_coef[2 * lane] = 1.f / l;
+    if (valid) lse[t * g.H + h0 + lane] = ls;
+  }
+  wave_fence();
+  if (valid) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int c = c0 + lane + 64 * j;
+      const float inv = w_coef[2 * ((lane + 64 * j) / g.kvc)];
+      float r[N];
+#pragma unroll
+      for (int e = 0; e < N; ++e) r[e] = acc[j][e] * inv;
+      if (partial) {
+        float f[N];
+        V::unpack(ld_nt(reinterpret_cast<const uint4*>(partial + t * g.d) + c), f);
+#pragma unroll
+        for (int e = 0; e < N; ++e) r[e] += f[e];
+      }
+      st_nt(reinterpret_cast<uint4*>(out + t * g.d) + c, V::pack(r));
+    }
+    if (lane < hw)
+      for (int k = 0; k < g.n; ++k)
+        alpha[((int64_t)k * g.T + t) * g.H + h0 + lane] = expf(w_logit[k * hw + lane] - ls);
+  }
+}
+
+template <typename T, int CPT>
+__global__ __launch_bounds__(kDThreads) void k_delta_bwd_s(DeltaGeom g, DeltaArgs a,
+                                                           const T* __restrict__ dout,
+                                                           const float* __restrict__ alpha,
+                                                           DeltaGrads dg,
+                                                           float* __restrict__ dq_part,
+                                                           float* __restrict__ ns_part) {
+  using V = DVec<T>;
+  constexpr int N = V::N;
+  constexpr int SPAN = 64 * CPT;
+  extern __shared__ float sm[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = wave & 1, ts = wave >> 1;
+  const int hw = g.H >> 1;
+  const int parts = SPAN >> 2;
+  const int n = g.n;
+  const int fw = 3 * parts + 5 * n * hw + 2 * n + hw;
+  uint4* s_q = reinterpret_cast<uint4*>(sm);
+  float* s_x = sm + 4 * g.cpr;               // [n][2 slots][2 halves] sums of squares, then radial halves
+  float* base = s_x + 4 * n;
+  float* w_part = base + wave * fw;          // [parts][3]
+  float* w_alpha = w_part + 3 * parts;       // [n][hw]
+  float* w_P = w_alpha + n * hw;
+  float* w_hq = w_P + n * hw;                // query dots, then logits
+  float* w_dl = w_hq + n * hw;
+  float* w_tmp = w_dl + n * hw;              // [n][hw]
+  float* w_rinv = w_tmp + n * hw;            // [n]
+  float* w_c = w_rinv + n;                   // [n]
+  float* w_S = w_c + n;                      // [hw]
+
+  for (int c = threadIdx.x; c < g.cpr; c += kDThreads) s_q[c] = static_cast<const uint4*>(a.query)[c];
+  __syncthreads();
+  const int c0 = half * SPAN;
+  const int h0 = half * hw;
+  float dqa[CPT][N];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j)
+#pragma unroll
+    for (int e = 0; e < N; ++e) dqa[j][e] = 0.f;
+  const bool has_null = a.null_src != nullptr;
+  float null_dl = 0.f, null_c = 0.f;
+
+  const int64_t ntiles = (g.T + 1) / 2;
+  for (int64_t tile = xcd_rank(blockIdx.x, gridDim.x); tile < ntiles; tile += gridDim.x) {
+    const int64_t t = tile * 2 + ts;
+    const bool valid = t < g.T;
+    const int64_t tt = valid ? t : tile * 2;
+    auto load_row = [&](int k, uint4 (&x)[CPT]) {
+      const bool bc = has_null && k == 0;
+      const uint4* p = source_chunks<T>(a, k, bc ? 0 : tt, g.d);
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        const int c = c0 + lane + 64 * j;
+        x[j] = bc ? p[c] : ld_nt(p + c);
+      }
+    };
+    uint4 dov[CPT];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j)
+      dov[j] = ld_nt(reinterpret_cast<const uint4*>(dout + tt * g.d) + c0 + lane + 64 * j);
+    for (int i = lane; i < n * hw; i += 64) {
+      const int k = i / hw, h = i - k * hw;
+      w_alpha[i] = valid ? alpha[((int64_t)k * g.T + t) * g.H + h0 + h] : 0.f;
+    }
+    float S_acc = 0.f;
+    // rows are loaded one source at a time here: a second buffer would cost
+    // more in occupancy than it gains in loads in flight
+    for (int k = 0; k < n; ++k) {
+      uint4 x[CPT];
+      load_row(k, x);
+      float wss = 0.f;
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        const int c = c0 + lane + 64 * j;
+        const float pd = quad_sum(V::dot(dov[j], x[j]));
+        const float qd = quad_sum(V::dot(s_q[c], x[j]));
+        const float ss = quad_sum(V::dot(x[j], x[j]));
+        const int q = lane + 64 * j;
+        if ((q & 3) == 0) {
+          w_part[3 * (q >> 2)] = pd;
+          w_part[3 * (q >> 2) + 1] = qd;
+        }
+        wss += ss;
+      }
+      float s2 = (lane & 3) == 0 ? wss : 0.f;
+#pragma unroll
+      for (int o = 32; o >= 4; o >>= 1) s2 += __shfl_xor(s2, o, 64);
+      if (lane == 0) s_x[(k * 2 + ts) * 2 + half] = s2;
+      wave_fence();
+      if (lane < hw) {
+        const float* pp = w_part + 3 * ((lane * g.kvc) >> 2);
+        float P = 0.f, hq = 0.f;
+        for (int i = 0; i < (g.kvc >> 2); ++i) {
+          P += pp[3 * i];
+          hq += pp[3 * i + 1];
+        }
+        w_P[k * hw + lane] = P;
+        w_hq[k * hw + lane] = hq;
+        S_acc += w_alpha[k * hw + lane] * P;
+      }
+      wave_fence();
+    }
+    __syncthreads();  // both halves' sums of squares are in s_x
+    if (lane < hw) w_S[lane] = S_acc;
+    for (int k = lane; k < n; k += 64)
+      w_rinv[k] = rsqrtf((s_x[(k * 2 + ts) * 2] + s_x[(k * 2 + ts) * 2 + 1]) / (float)g.d + g.eps);
+    wave_fence();
+    for (int i = lane; i < n * hw; i += 64) {
+      const int k = i / hw, h = i - k * hw;
+      const float lg = w_rinv[k] * w_hq[i];
+      w_hq[i] = lg;
+      const float dl = w_alpha[i] * (w_P[i] - w_S[h]);
+      w_dl[i] = dl;
+      w_tmp[i] = dl * lg;
+    }
+    wave_fence();
+    __syncthreads();  // every wave has read s_x
+    for (int k = lane; k < n; k += 64) {
+      float c = 0.f;
+      for (int h = 0; h < hw; ++h) c += w_tmp[k * hw + h];
+      s_x[(k * 2 + ts) * 2 + half] = c;
+    }
+    __syncthreads();
+    for (int k = lane; k < n; k += 64) w_c[k] = s_x[(k * 2 + ts) * 2] + s_x[(k * 2 + ts) * 2 + 1];
+    wave_fence();
+    if (has_null && valid) {
+      if (lane < hw) null_dl += w_dl[lane];
+      if (lane == 0 && half == 0) null_c += w_c[0];
+    }
+    for (int k = 0; k < n; ++k) {
+      uint4 x[CPT];
+      load_row(k, x);
+      const bool is_null = has_null && k == 0;
+      float* dst = is_null ? nullptr : dg.d[k - (has_null ? 1 : 0)];
+      const float ri = w_rinv[k];
+      const float rc = ri * ri / (float)g.d * w_c[k];
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        const int c = c0 + lane + 64 * j;
+        const int hl = (lane + 64 * j) / g.kvc;
+        const float dl = w_dl[k * hw + hl];
+        const float cq = valid ? ri * dl : 0.f;
+        float xf[N];
+        V::unpack(x[j], xf);
+#pragma unroll
+        for (int e = 0; e < N; ++e) dqa[j][e] += cq * xf[e];
+        if (is_null || !valid) continue;
+        const float al = w_alpha[k * hw + hl];
+        float df[N], qf[N], gr[N];
+        V::unpack(dov[j], df);
+        V::unpack(s_q[c], qf);
+#pragma unroll
+        for (int e = 0; e < N; ++e) gr[e] = al * df[e] + cq * qf[e] - rc * xf[e];
+        float* o = dst + t * g.d + (int64_t)c * N;
+#pragma unroll
+        for (int e = 0; e < N; e += 4)
+          st_nt(o + e, make_float4(gr[e], gr[e + 1], gr[e + 2], gr[e + 3]));
+      }
+    }
+    __syncthreads();  // the next tile reuses s_x and the wave regions
+  }
+
+  // Work-group partials in a fixed order: chunk c of the row sits in wave
+  // (slot, c / SPAN) at lane + 64 j = c % SPAN; sum the two token slots.
+  float* red = base;  // [4 waves][SPAN][N]
+  float* mine = red + (size_t)wave * SPAN * N;
+#pragma unroll
+  for (int j = 0; j < CPT; ++j)
+#pragma unroll
+    for (int e = 0; e < N; ++e) mine[(size_t)(64 * j + lane) * N + e] = dqa[j][e];
+  float* red_ns = red + (size_t)kDWaves * SPAN * N;  // [4 waves][64][2]
+  red_ns[2 * (wave * 64 + lane)] = null_dl;
+  red_ns[2 * (wave * 64 + lane) + 1] = null_c;
+  __syncthreads();
+  for (int col = threadIdx.x; col < g.d; col += kDThreads) {
+    const int c = col / N, e = col - c * N;
+    const int hf = c / SPAN, q = c - hf * SPAN;
+    float sacc = 0.f;
+    for (int s2 = 0; s2 < 2; ++s2) sacc += red[((size_t)(s2 * 2 + hf) * SPAN + q) * N + e];
+    dq_part[(int64_t)blockIdx.x * g.d + col] = sacc;
+  }
+  if (has_null && threadIdx.x <= g.H) {
+    const int h = threadIdx.x;
+    float sacc = 0.f;
+    for (int s2 = 0; s2 < 2; ++s2) {
+      if (h < g.H) {
+        const int hf = h / hw, hl = h - hf * hw;
+        sacc += red_ns[2 * ((s2 * 2 + hf) * 64 + hl)];
+      } else {
+        sacc += red_ns[2 * ((s2 * 2) * 64) + 1];
+      }
+    }
+    ns_part[(int64_t)blockIdx.x * (g.H + 1) + h] = sacc;
   }
 }
 
@@ -588,22 +922,38 @@ static hipError_t delta_launch(const DeltaGeom& g, const DeltaArgs& a, bool fwd,
                                hipStream_t st) {
   const size_t lds = delta_lds_bytes(g, fwd);
   if (fwd) {
-    const int64_t tile_tokens = (int64_t)kDWaves * g.tw;
+    const int64_t tile_tokens = g.split ? 2 : (int64_t)kDWaves * g.tw;
     const dim3 grid((unsigned)((g.T + tile_tokens - 1) / tile_tokens));
-    hipLaunchKernelGGL((k_delta_fwd<T, CPT>), grid, dim3(kDThreads), lds, st, g, a,
-                       static_cast<const T*>(p0), static_cast<T*>(p1),
-                       const_cast<float*>(alpha), lse);
+    if (g.split)
+      hipLaunchKernelGGL((k_delta_fwd_s<T, CPT>), grid, dim3(kDThreads), lds, st, g, a,
+                         static_cast<const T*>(p0), static_cast<T*>(p1),
+                         const_cast<float*>(alpha), lse);
+    else
+      hipLaunchKernelGGL((k_delta_fwd<T, CPT>), grid, dim3(kDThreads), lds, st, g, a,
+                         static_cast<const T*>(p0), static_cast<T*>(p1),
+                         const_cast<float*>(alpha), lse);
   } else {
-    hipLaunchKernelGGL((k_delta_bwd<T, CPT>), dim3((unsigned)parts), dim3(kDThreads), lds, st, g,
-                       a, static_cast<const T*>(dout), alpha, *dg, dq_part, ns_part);
+    if (g.split)
+      hipLaunchKernelGGL((k_delta_bwd_s<T, CPT>), dim3((unsigned)parts), dim3(kDThreads), lds, st,
+                         g, a, static_cast<const T*>(dout), alpha, *dg, dq_part, ns_part);
+    else
+      hipLaunchKernelGGL((k_delta_bwd<T, CPT>), dim3((unsigned)parts), dim3(kDThreads), lds, st,
+                         g, a, static_cast<const T*>(dout), alpha, *dg, dq_part, ns_part);
   }
   return hipGetLastError();
 }
 
 size_t delta_lds_bytes(const DeltaGeom& g, bool fwd) {
+  const size_t q = 4 * (size_t)g.cpr;  // query chunks (16 bytes each)
+  if (g.split) {
+    const size_t hw = (size_t)g.H / 2, span = 64 * (size_t)g.cpt, qp = span >> 2;
+    if (fwd) return sizeof(float) * (q + 4 + kDWaves * (2 * qp + 3 * hw + g.n * hw));
+    const size_t fw = 3 * qp + 5 * (size_t)g.n * hw + 2 * (size_t)g.n + hw;
+    const size_t tail = (size_t)kDWaves * span * g.pc + 2 * kDWaves * 64;
+    return sizeof(float) * (q + 4 * (size_t)g.n + (kDWaves * fw > tail ? kDWaves * fw : tail));
+  }
   const size_t pw = (size_t)g.tw * g.H;
   const size_t qparts = (64 * (size_t)g.cpt) >> 2;
-  const size_t q = 4 * (size_t)g.cpr;  // query chunks (16 bytes each)
   if (fwd) return sizeof(float) * (q + kDWaves * (2 * qparts + 3 * pw + g.n * pw));
   const size_t fw = 3 * qparts + pw + 4 * (size_t)g.n * pw + 2 * (size_t)g.n * g.tw + pw;
   const size_t tail = (size_t)kDWaves * 64 * g.cpt * g.pc + 2 * kDWaves * 64;  // end-of-kernel sums
@@ -611,7 +961,7 @@ size_t delta_lds_bytes(const DeltaGeom& g, bool fwd) {
 }
 
 int delta_bwd_parts(const DeltaGeom& g) {
-  const int64_t tile_tokens = (int64_t)kDWaves * g.tw;
+  const int64_t tile_tokens = g.split ? 2 : (int64_t)kDWaves * g.tw;
   const int64_t ntiles = (g.T + tile_tokens - 1) / tile_tokens;
   const int64_t cap = 512;
   return (int)(ntiles < cap ? (ntiles > 0 ? ntiles : 1) : cap);
@@ -656,8 +1006,7 @@ hipError_t launch_delta_bwd(const DeltaGeom& g, int dtype, const DeltaArgs& a, c
 
 hipError_t launch_delta_null(const DeltaGeom& g, int dtype, const DeltaArgs& a, const void* dout,
                              const float* alpha0, float* nv_part, const float* ns_part, int parts,
-                             float* dnull, hipStream_t st) {
-  if (g.H > kMaxHeadsFinish) return hipErrorInvalidConfiguration;
+                             float* nv_sum, float* ns_sum, float* dnull, hipStream_t st) {
   if (g.T > 0 && parts > 0) {
     const int64_t rows = (g.T + parts - 1) / parts;
     if (dtype == 0)
@@ -670,13 +1019,17 @@ hipError_t launch_delta_null(const DeltaGeom& g, int dtype, const DeltaArgs& a, 
     if (e != hipSuccess) return e;
   }
   const int p = g.T > 0 ? parts : 0;  // with no tokens every sum is empty
+  hipError_t e = launch_dq_reduce(nv_part, p, g.d, nv_sum, nullptr, nullptr, nullptr, st);
+  if (e != hipSuccess) return e;
+  e = launch_dq_reduce(ns_part, p, g.H + 1, ns_sum, nullptr, nullptr, nullptr, st);
+  if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((g.d + kDThreads - 1) / kDThreads));
   if (dtype == 0)
-    hipLaunchKernelGGL((k_delta_null_finish<float>), grid, dim3(kDThreads), 0, st, g, a, nv_part,
-                       ns_part, p, dnull);
+    hipLaunchKernelGGL((k_delta_null_finish<float>), grid, dim3(kDThreads), 0, st, g, a, nv_sum,
+                       ns_sum, dnull);
   else
-    hipLaunchKernelGGL((k_delta_null_finish<bf16_t>), grid, dim3(kDThreads), 0, st, g, a, nv_part,
-                       ns_part, p, dnull);
+    hipLaunchKernelGGL((k_delta_null_finish<bf16_t>), grid, dim3(kDThreads), 0, st, g, a, nv_sum,
+                       ns_sum, dnull);
   return hipGetLastError();
 }
 

@@ -659,6 +659,14 @@ attnres_status_t delta_geom(const attnres_delta_t* c, attnres::DeltaGeom* g) {
     tw = t;
     break;
   }
+  // Wide rows: two waves per token halve each lane's state (registers).
+  int split = 0;
+  if (cpr % 128 == 0 && (cpr / 128 == 1 || cpr / 128 == 2 || cpr / 128 == 4) &&
+      c->heads % 2 == 0 && (!cpt || cpt >= 4)) {
+    split = 1;
+    cpt = cpr / 128;
+    tw = 1;
+  }
   if (!cpt)
     return fail(ATTNRES_ERR_UNSUPPORTED,
                 "d=%d: no wave layout owns whole tokens (64*cpt must be a multiple of %d chunks)",
@@ -675,6 +683,7 @@ attnres_status_t delta_geom(const attnres_delta_t* c, attnres::DeltaGeom* g) {
   g->cpt = cpt;
   g->tw = tw;
   g->n = n;
+  g->split = split;
   g->eps = c->eps;
   if (attnres::delta_lds_bytes(*g, true) > 160 * 1024 || attnres::delta_lds_bytes(*g, false) > 160 * 1024)
     return fail(ATTNRES_ERR_UNSUPPORTED, "delta call needs more LDS than a work-group has");
@@ -700,9 +709,10 @@ attnres::DeltaArgs delta_args(const attnres_delta_t* c) {
 }  // namespace
 
 // Backward workspace: dq partials and null-gradient vector partials
-// [parts][d] each, null-gradient scalar partials [parts][H + 1].
+// [parts][d] each, null-gradient scalar partials [parts][H + 1], and the
+// reduced null sums [d] and [H + 1].
 struct DeltaWs {
-  size_t dq, nv, ns, total;
+  size_t dq, nv, ns, nv_sum, ns_sum, total;
 };
 DeltaWs delta_ws(const attnres::DeltaGeom& g) {
   const size_t parts = (size_t)attnres::delta_bwd_parts(g);
@@ -710,7 +720,9 @@ DeltaWs delta_ws(const attnres::DeltaGeom& g) {
   w.dq = 0;
   w.nv = align256(sizeof(float) * parts * g.d);
   w.ns = w.nv + align256(sizeof(float) * parts * g.d);
-  w.total = w.ns + align256(sizeof(float) * parts * (g.H + 1));
+  w.nv_sum = w.ns + align256(sizeof(float) * parts * (g.H + 1));
+  w.ns_sum = w.nv_sum + align256(sizeof(float) * g.d);
+  w.total = w.ns_sum + align256(sizeof(float) * (g.H + 1));
   return w;
 }
 
@@ -778,7 +790,8 @@ attnres_status_t attnres_delta_bwd(const attnres_delta_t* call, const void* dout
   if (e != hipSuccess) return hip_fail(e, "delta dq reduction");
   if (d_null) {
     e = attnres::launch_delta_null(g, call->dtype, args, dout, alpha, nv_part, ns_part, parts,
-                                   d_null, s);
+                                   reinterpret_cast<float*>(w + ws.nv_sum),
+                                   reinterpret_cast<float*>(w + ws.ns_sum), d_null, s);
     if (e != hipSuccess) return hip_fail(e, "delta null-source gradient");
   }
   return ATTNRES_OK;

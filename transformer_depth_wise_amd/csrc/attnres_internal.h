@@ -112,6 +112,7 @@ struct DeltaGeom {
   int32_t cpt;  // 16-byte chunks per lane
   int32_t tw;   // tokens owned by each wave: 64 * cpt / cpr
   int32_t n;    // sources of the call (null source first, if any)
+  int32_t split;  // 1: two waves share a token, each holding half its chunks (cpt = cpr / 128)
   float eps;
 };
 struct DeltaArgs {
@@ -131,11 +132,12 @@ hipError_t launch_delta_fwd(const DeltaGeom& g, int dtype, const DeltaArgs& a, c
 hipError_t launch_delta_bwd(const DeltaGeom& g, int dtype, const DeltaArgs& a, const void* dout,
                             const float* alpha, const DeltaGrads& dg, float* dq_part,
                             float* ns_part, int parts, hipStream_t st);
-// Null-source gradient: weighted dout column sums into nv_part [parts][d],
-// then the fixed-order combination with the scalar partials into dnull [d].
+// Null-source gradient: weighted dout column sums into nv_part [parts][d];
+// fixed-order sums of nv_part and the scalar partials into nv_sum [d] and
+// ns_sum [H + 1]; then their combination into dnull [d].
 hipError_t launch_delta_null(const DeltaGeom& g, int dtype, const DeltaArgs& a, const void* dout,
                              const float* alpha0, float* nv_part, const float* ns_part, int parts,
-                             float* dnull, hipStream_t st);
+                             float* nv_sum, float* ns_sum, float* dnull, hipStream_t st);
 
 // Bandwidth probes (attnres_probe.hip).
 int probe_blocks();
