@@ -133,7 +133,9 @@ __device__ __forceinline__ void st_stream(uint4* p, const uint4& v) {
 __device__ __forceinline__ void st_stream(float* p, const float4& v) {
   __builtin_nontemporal_store(f32x4_t_{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4_t_*>(p));
 }
-__device__ __forceinline__ void st_stream(float* p, float v) { __builtin_nontemporal_store(v, p); }
+// Single floats (scattered 4-byte results) stay plain stores: L2 merges
+// neighbouring ones into whole lines, which non-temporal stores do not.
+__device__ __forceinline__ void st_stream(float* p, float v) { *p = v; }
 
 // Sum over the 4 lanes of a quad (two DPP quad permutations).
 __device__ __forceinline__ float quad_sum(float v) {
