@@ -49,14 +49,15 @@ def kernel_bytes(w, parts: int):
     nsrc, extra = list(w.nsrc), list(w.extra)
     out = {"score": 0, "fwd": 0, "bwd_site": 0, "dq_reduce": 0, "finalize": 0}
     launches = {k: 0 for k in out}
+    rw = d if w.norm == "full" else r  # coordinates the append reads
     for n in range(max(nsrc)):  # append of row n: key coordinates in; rinv + projections out
         readers = sum(1 for s in range(S) if nsrc[s] > n)
-        out["score"] += T * r * b + 4 * T + 4 * readers * T * H
+        out["score"] += T * rw * b + 4 * T + 4 * readers * T * H
         launches["score"] += 1
     for s in range(S):
         N = nsrc[s] + extra[s]
         if extra[s]:
-            out["score"] += T * r * b + 4 * T + 4 * T * H
+            out["score"] += T * rw * b + 4 * T + 4 * T * H
             launches["score"] += 1
         # rows; projections + rinv in; alpha + lse + out written
         out["fwd"] += N * T * d * b + 4 * N * T * H + 4 * N * T + 4 * N * T * H + 4 * T * H + T * d * b
@@ -104,7 +105,9 @@ def cpu_baseline(name: str, tokens: int, full_tokens: int):
     q = inp.queries().astype(np.float64)
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        run_schedule(rows, extras, q, douts, list(w.nsrc), w.heads, w.r, w.eps)
+        gains = inp.gains()
+        run_schedule(rows, extras, q, douts, list(w.nsrc), w.heads, w.r, w.eps,
+                     gains=None if gains is None else gains.astype(np.float64), norm=w.norm)
         dt = time.perf_counter() - t0
     ms = dt * 1e3 * full_tokens / tokens
     return {
@@ -435,13 +438,24 @@ def main():
     dev_name = torch.cuda.get_device_name(0)
     inp = Inputs(w)
     t_gen = time.time()
-    bank = Bank(w.tokens, w.d, w.r, w.heads, w.rows, w.sites, w.dtype, w.eps)
+    bank = Bank(w.tokens, w.d, w.r, w.heads, w.rows, w.sites, w.dtype, w.eps, norm=w.norm)
     workers = min(16, len(os.sched_getaffinity(0)))
     fill_device(bank.rows, inp, "row", range(w.rows), workers)
     fill_device(bank.dout_rows, inp, "dout", range(w.sites), workers)
     queries = to_device(inp.queries(), w.dtype)
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    extras = [to_device(inp.extra(s), w.dtype) if w.extra[s] else None for s in range(w.sites)]
+    extras = [None] * w.sites
+    if any(w.extra):  # transient sources: drawn on a thread pool, like the rows
+        from concurrent.futures import ThreadPoolExecutor
+
+        def draw_extra(s):
+            extras[s] = to_device(inp.extra(s), w.dtype)
+
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(draw_extra, [s for s in range(w.sites) if w.extra[s]]))
+    gains = None if inp.gains() is None else to_device(inp.gains(), "f32")
+    dgains = None if gains is None else torch.empty((w.sites, w.r), dtype=torch.float32,
+                                                    device="cuda")
     d_extras = [torch.empty((w.tokens, w.d), dtype=torch.float32, device="cuda")
                 if w.extra[s] else None for s in range(w.sites)]
     outs = torch.empty((w.sites, w.tokens, w.d), dtype=tdt, device="cuda")
@@ -451,7 +465,8 @@ def main():
           file=sys.stderr, flush=True)
 
     def step():
-        run_microbatch(bank, list(w.nsrc), list(w.extra), queries, outs, dqs, extras, d_extras)
+        run_microbatch(bank, list(w.nsrc), list(w.extra), queries, outs, dqs, extras, d_extras,
+                       gains=gains, dgains=dgains)
 
     for _ in range(args.warmup):
         step()

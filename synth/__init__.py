@@ -13,6 +13,7 @@ from .workloads import (  # noqa: F401
     block_schedule,
     full_schedule,
     get_workload,
+    read_schedule,
 )
 from .draws import Inputs, bf16_bits, bf16_round, sample_tokens  # noqa: F401
 from .delta import DELTA_SHAPES, DeltaInputs, DeltaShape  # noqa: F401

@@ -89,6 +89,22 @@ def block_schedule(stages: int):
     return tuple(range(1, stages + 1)), (1,) * stages
 
 
+def read_schedule(reads: int, blocks: int):
+    """Block routing with one read after every sublayer ("Low-Rank Attention
+    Residuals", Appendix H, Figure 11): blocks end at sublayers
+    ceil(M j / N), j = 1..N; the read after sublayer t sees the embedding, the
+    blocks completed so far and, unless t ends a block (the partial sum was
+    just committed), the running partial sum as a transient source."""
+    ends = {-(-reads * j // blocks) for j in range(1, blocks + 1)}
+    nsrc, extra, done = [], [], 0
+    for t in range(1, reads + 1):
+        if t in ends:
+            done += 1
+        nsrc.append(1 + done)
+        extra.append(0 if t in ends else 1)
+    return tuple(nsrc), tuple(extra)
+
+
 def _full(name, tokens, d, heads, layers, dtype, scale=True):
     nsrc, extra = full_schedule(layers)
     return Workload(name, tokens, d, heads, d, nsrc, extra, dtype, scale)
@@ -112,6 +128,13 @@ WORKLOADS = {
     # 9 stages reading 2..10 sources (committed rows + transient partial).
     "lr_h1": _block("lr_h1", 8192, 7168, 1792, 1, 9),
     "lr_h8": _block("lr_h8", 8192, 7168, 1792, 8, 9),
+    # Kimi K3-shaped block routing ("Low-Rank Attention Residuals", Appendix
+    # E.1): d=7168, 93 layers in N=8 blocks, 186 active reads (one after every
+    # sublayer) over the embedding, the completed blocks and the running
+    # partial sum, at most nine sources; single head, full-width keys, the
+    # RMSNorm weight folded into the query (Eq. 28) as a per-site gain.
+    "k3": Workload("k3", 8192, 7168, 1, 7168, *read_schedule(186, 8), "bf16", False,
+                   gains=True),
 }
 
 

@@ -18,7 +18,10 @@ pytestmark = pytest.mark.gpu
 # Small token counts that the oracle finishes in seconds, each spanning
 # several tiles with a ragged tail (tile sizes: 64 / 16 / 8 / 8 / 2 tokens).
 REDUCED = ["tiny", "tiny@T37", "mhar100m@T200", "mhar350m@T100", "mhar1b@T77",
-           "mhar1b@T100", "lr_h1@T9", "lr_h8@T9", "lr_h8@T12"]
+           "mhar1b@T100", "lr_h1@T9", "lr_h8@T9", "lr_h8@T12",
+           # Kimi K3-shaped: 186 reads, d = 7168 full-width single-head keys
+           # with gains (vector-ALU append on 2-token tiles), ragged at T = 3
+           "k3@T3", "k3@T6"]
 
 
 # Routing RMSNorm gains and the full-width-RMS control, on every append and

@@ -8,8 +8,6 @@ namespace attnres {
 
 // Work-group size of every streaming kernel (4 wave64s).
 constexpr int kThreads = 256;
-// Tokens per tile of the scoring (append) kernel.
-constexpr int kScoreTile = 8;
 
 // Shape of one bank, in elements and in 16-byte chunks.
 struct Geom {

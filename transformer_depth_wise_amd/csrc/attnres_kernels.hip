@@ -198,7 +198,7 @@ __device__ __forceinline__ Slot make_slot(const Geom& g, int tid, int j) {
 // Append: inverse RMS of the key and per-head key projections against the
 // queries of sites [s_lo, s_hi), stored at source index `slot` of each site's
 // projection slot.  Vector-ALU form (fp32 rows, or r/H not a multiple of 32).
-// Grid: ceil(T / kScoreTile) work-groups; the key coordinates of a tile are
+// Grid: ceil(T / TILE) work-groups; the key coordinates of a tile are
 // staged in LDS as fp32, each thread owns (head, site) items with the site
 // index fastest, so a wave reads the same LDS words (broadcast) while its
 // lanes stream different query rows from L2.
@@ -213,7 +213,7 @@ __device__ __forceinline__ int64_t xcd_order(int64_t b, int64_t n) {
   return x * q + (x < rem ? x : rem) + k;
 }
 
-template <typename T, typename QT>
+template <typename T, typename QT, int TILE>
 __global__ __launch_bounds__(kThreads) void k_score(Geom g, const T* __restrict__ x,
                                                      const QT* __restrict__ Q, int s_lo, int s_hi,
                                                      int slot, float* __restrict__ rinv_out,
@@ -221,13 +221,13 @@ __global__ __launch_bounds__(kThreads) void k_score(Geom g, const T* __restrict_
                                                      int64_t site_stride) {
   using V = Vec<T>;
   extern __shared__ float sm[];
-  float* keys = sm;                      // [kScoreTile][r]
-  float* srinv = sm + kScoreTile * g.r;  // [kScoreTile]
+  float* keys = sm;                      // [TILE][r]
+  float* srinv = sm + TILE * g.r;  // [TILE]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t t0 = xcd_order(blockIdx.x, gridDim.x) * kScoreTile;
+  const int64_t t0 = xcd_order(blockIdx.x, gridDim.x) * TILE;
   const int kc = g.r / V::N;
 
-  for (int tau = wave; tau < kScoreTile; tau += kThreads / 64) {
+  for (int tau = wave; tau < TILE; tau += kThreads / 64) {
     const int64_t t = t0 + tau;
     float* kr = keys + tau * g.r;
     float ss = 0.f;
@@ -269,9 +269,9 @@ __global__ __launch_bounds__(kThreads) void k_score(Geom g, const T* __restrict_
     const int h = it / ns;
     const int s = s_lo + (it - h * ns);
     const QT* qh = Q + (int64_t)s * g.r + (int64_t)h * g.kk;
-    float acc[kScoreTile];
+    float acc[TILE];
 #pragma unroll
-    for (int tau = 0; tau < kScoreTile; ++tau) acc[tau] = 0.f;
+    for (int tau = 0; tau < TILE; ++tau) acc[tau] = 0.f;
     for (int c = 0; c < g.kkc; ++c) {
       float qf[V::N];
       QChunk<T, QT> qc;
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void k_score(Geom g, const T* __restrict_
       qc.unpack(qf);
       const float* kb = keys + h * g.kk + c * V::N;
 #pragma unroll
-      for (int tau = 0; tau < kScoreTile; ++tau) {
+      for (int tau = 0; tau < TILE; ++tau) {
         const float* kp = kb + tau * g.r;
 #pragma unroll
         for (int e = 0; e < V::N; ++e) acc[tau] += qf[e] * kp[e];
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(kThreads) void k_score(Geom g, const T* __restrict_
     }
     float* dst = proj + (int64_t)s * site_stride + ((int64_t)slot * g.H + h) * g.T + t0;
 #pragma unroll
-    for (int tau = 0; tau < kScoreTile; ++tau)
+    for (int tau = 0; tau < TILE; ++tau)
       if (t0 + tau < g.T) st_stream(dst + tau, acc[tau]);
   }
 }
@@ -421,6 +421,115 @@ __global__ __launch_bounds__(kThreads) void k_score_mfma(Geom g, const bf16_t* _
 // n_rows (if extra) the transient source.  The first two sources are
 // requested before the softmax prologue so that their loads overlap it; the
 // stream then keeps three sources in flight.
+// Append on the matrix cores for wide key heads (r/H > 256, a multiple of
+// 32; e.g. a single head over thousands of key coordinates).  The per-head
+// projection is the same [16 tokens x r/H] . [r/H x sites] product, but the
+// k dimension is too long to hold in registers: a work-group owns 16
+// tokens, its 4 waves take interleaved 32-wide k steps (so every key and
+// query fragment is loaded once per work-group), each wave accumulates up to
+// NB 16-site blocks, and the waves' accumulators meet in LDS per head.
+template <int NB>
+__global__ __launch_bounds__(kThreads) void k_score_wide(Geom g, const bf16_t* __restrict__ x,
+                                                          const bf16_t* __restrict__ Q,
+                                                          const bf16_t* __restrict__ Qlo, int s_lo,
+                                                          int s_hi, int slot,
+                                                          float* __restrict__ rinv_out,
+                                                          float* __restrict__ proj,
+                                                          int64_t site_stride) {
+  extern __shared__ float sm[];  // [4 waves][NB][64 lanes][4] partial sums, then [4][16] squares
+  constexpr int kWaves = kThreads / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = lane & 15, kg = lane >> 4;
+  const int64_t tw = xcd_order(blockIdx.x, gridDim.x) * 16;
+  const int64_t t = tw + row;
+  const bool tok_ok = t < g.T;
+  const bf16_t* xr = x + (tok_ok ? t : 0) * g.d + (g.d - g.r);
+  const int ns = s_hi - s_lo;
+  const int nsb = (ns + 15) / 16;  // <= NB
+  const int ksteps = g.kk / 32;
+  const int64_t tq = tw + kg * 4;
+  const bool vec = (g.T & 3) == 0 && tq + 3 < g.T;
+
+  float ss = 0.f;
+  if (g.rms_full && tok_ok) {
+    const uint4* rp = reinterpret_cast<const uint4*>(x + t * g.d);
+    for (int c = wave * 4 + kg; c < g.key_c0; c += 16) {
+      float f[8];
+      Vec<bf16_t>::unpack(ld_stream(rp + c), f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+    }
+  }
+  for (int h = 0; h < g.H; ++h) {
+    f32x4_t acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int i = wave; i < ksteps; i += kWaves) {
+      const int k0 = h * g.kk + i * 32 + kg * 8;
+      const uint4 av = tok_ok ? ld_stream(reinterpret_cast<const uint4*>(xr + k0)) : zero4();
+      float f[8];
+      Vec<bf16_t>::unpack(av, f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        if (b < nsb) {
+          const int sv = s_lo + b * 16 + row;
+          const int64_t qo = (int64_t)(sv < s_hi ? sv : s_lo) * g.r + k0;
+          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              as_bf16x8(av), as_bf16x8(*reinterpret_cast<const uint4*>(Q + qo)), acc[b], 0, 0, 0);
+          if (Qlo)
+            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                as_bf16x8(av), as_bf16x8(*reinterpret_cast<const uint4*>(Qlo + qo)), acc[b], 0,
+                0, 0);
+        }
+      }
+    }
+    float* mine = sm + (size_t)wave * NB * 64 * 4;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      if (b < nsb)
+        *reinterpret_cast<float4*>(mine + (b * 64 + lane) * 4) =
+            make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
+    __syncthreads();
+    // wave w sums and stores site blocks w, w + 4, ...; lane (kg, row) holds
+    // tokens tw + 4 kg .. + 3 of site block * 16 + row
+    for (int b = wave; b < nsb; b += kWaves) {
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int w = 0; w < kWaves; ++w) {
+        const float4 p = *reinterpret_cast<const float4*>(sm + ((size_t)(w * NB + b) * 64 + lane) * 4);
+        v.x += p.x;
+        v.y += p.y;
+        v.z += p.z;
+        v.w += p.w;
+      }
+      const int sv = s_lo + b * 16 + row;
+      if (sv < s_hi) {
+        float* dst = proj + (int64_t)sv * site_stride + ((int64_t)slot * g.H + h) * g.T + tq;
+        if (vec) {
+          st_stream(dst, v);
+        } else {
+          const float vv[4] = {v.x, v.y, v.z, v.w};
+          for (int j = 0; j < 4; ++j)
+            if (tq + j < g.T) st_stream(dst + j, vv[j]);
+        }
+      }
+    }
+    __syncthreads();  // the partial sums are read before the next head overwrites them
+  }
+  // sums of squares: the four k-groups of a token row, then the waves
+  ss += __shfl_xor(ss, 16, 64);
+  ss += __shfl_xor(ss, 32, 64);
+  if (kg == 0) sm[wave * 16 + row] = ss;
+  __syncthreads();
+  if (wave == 0 && kg == 0 && tok_ok) {
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) tot += sm[w * 16 + row];
+    st_stream(rinv_out + t, rsqrtf(tot / (float)g.rms_w + g.eps));
+  }
+}
+
 template <typename T, int CPT>
 __global__ __launch_bounds__(kThreads) void k_fwd(Geom g, const T* __restrict__ rows,
                                                    int64_t row_stride, const T* __restrict__ extra,
@@ -1289,7 +1398,17 @@ int finalize_batch(const Geom& g) {
 }  // namespace
 
 // ---------------------------------------------------------------------------
-size_t lds_score(const Geom& g) { return sizeof(float) * ((size_t)kScoreTile * g.r + kScoreTile); }
+// Tokens per tile of the vector-ALU append: the most (8, 4, 2 or 1) whose
+// fp32 key coordinates fit the LDS budget.
+int score_tile(const Geom& g) {
+  for (int t = 8; t > 1; t >>= 1)
+    if (sizeof(float) * ((size_t)t * g.r + t) <= kMaxLds) return t;
+  return 1;
+}
+size_t lds_score(const Geom& g) {
+  const size_t t = (size_t)score_tile(g);
+  return sizeof(float) * (t * g.r + t);
+}
 size_t lds_fwd(const Geom& g, int n_src) { return sizeof(float) * (size_t)n_src * g.tt * g.H; }
 size_t lds_bwd_site(const Geom& g, int n_src) {
   if (g.wave_tokens > 0) {
@@ -1344,22 +1463,56 @@ hipError_t launch_score(const Geom& g, int dtype, const void* x, const QuerySet&
     }
     return hipGetLastError();
   }
-  const dim3 grid((unsigned)((g.T + kScoreTile - 1) / kScoreTile));
+  const int nsb = (s_hi - s_lo + 15) / 16;
+  if (dtype != 0 && g.kk % 32 == 0 && g.kk > 256 && nsb <= 16) {
+    const dim3 grid((unsigned)((g.T + 15) / 16));
+    const bf16_t* xb = static_cast<const bf16_t*>(x);
+    const bf16_t* qb = qs.qf ? qs.qhi : static_cast<const bf16_t*>(qs.q);
+    const bf16_t* ql = qs.qf ? qs.qlo : nullptr;
+    const int nb = nsb <= 1 ? 1 : nsb <= 2 ? 2 : nsb <= 4 ? 4 : nsb <= 8 ? 8 : 16;
+    const size_t lds = sizeof(float) * (size_t)kThreads * 4 * nb;  // >= the 4 x 16 squares
+    switch (nb) {
+#define ATTNRES_SCORE_NB(B)                                                                    \
+  case B:                                                                                      \
+    hipLaunchKernelGGL(k_score_wide<B>, grid, dim3(kThreads), lds, st, g, xb, qb, ql, s_lo,    \
+                       s_hi, slot, rinv_out, proj, site_stride);                               \
+    break;
+      ATTNRES_SCORE_NB(1)
+      ATTNRES_SCORE_NB(2)
+      ATTNRES_SCORE_NB(4)
+      ATTNRES_SCORE_NB(8)
+      ATTNRES_SCORE_NB(16)
+#undef ATTNRES_SCORE_NB
+    }
+    return hipGetLastError();
+  }
+  const int tile = score_tile(g);
+  const dim3 grid((unsigned)((g.T + tile - 1) / tile));
   const size_t lds = lds_score(g);
   if (lds > kMaxLds) return hipErrorInvalidConfiguration;
-  if (dtype == 0)
-    hipLaunchKernelGGL((k_score<float, float>), grid, dim3(kThreads), lds, st, g,
-                       static_cast<const float*>(x),
-                       qs.qf ? qs.qf : static_cast<const float*>(qs.q), s_lo, s_hi, slot,
-                       rinv_out, proj, site_stride);
-  else if (qs.qf)
-    hipLaunchKernelGGL((k_score<bf16_t, float>), grid, dim3(kThreads), lds, st, g,
-                       static_cast<const bf16_t*>(x), qs.qf, s_lo, s_hi, slot, rinv_out, proj,
-                       site_stride);
-  else
-    hipLaunchKernelGGL((k_score<bf16_t, bf16_t>), grid, dim3(kThreads), lds, st, g,
-                       static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(qs.q), s_lo,
-                       s_hi, slot, rinv_out, proj, site_stride);
+  switch (tile) {
+#define ATTNRES_SCORE_TILE(TL)                                                                   \
+  case TL:                                                                                       \
+    if (dtype == 0)                                                                              \
+      hipLaunchKernelGGL((k_score<float, float, TL>), grid, dim3(kThreads), lds, st, g,          \
+                         static_cast<const float*>(x),                                           \
+                         qs.qf ? qs.qf : static_cast<const float*>(qs.q), s_lo, s_hi, slot,      \
+                         rinv_out, proj, site_stride);                                           \
+    else if (qs.qf)                                                                              \
+      hipLaunchKernelGGL((k_score<bf16_t, float, TL>), grid, dim3(kThreads), lds, st, g,         \
+                         static_cast<const bf16_t*>(x), qs.qf, s_lo, s_hi, slot, rinv_out, proj, \
+                         site_stride);                                                           \
+    else                                                                                         \
+      hipLaunchKernelGGL((k_score<bf16_t, bf16_t, TL>), grid, dim3(kThreads), lds, st, g,        \
+                         static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(qs.q), s_lo,  \
+                         s_hi, slot, rinv_out, proj, site_stride);                               \
+    break;
+    ATTNRES_SCORE_TILE(8)
+    ATTNRES_SCORE_TILE(4)
+    ATTNRES_SCORE_TILE(2)
+    ATTNRES_SCORE_TILE(1)
+#undef ATTNRES_SCORE_TILE
+  }
   return hipGetLastError();
 }
 
