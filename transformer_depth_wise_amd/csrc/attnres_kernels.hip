@@ -144,6 +144,25 @@ __device__ __forceinline__ float quad_sum(float v) {
   return v;
 }
 
+// log2 of the widest lane group (at most a wave) whose size divides kvc.
+__host__ __device__ inline int site_group_shift(int kvc) {
+  int sh = 0;
+  while (sh < 6 && (kvc & ((2 << sh) - 1)) == 0) ++sh;
+  return sh;
+}
+
+// Sum over aligned groups of 2^sh lanes (sh <= 6, uniform over the wave);
+// every lane of a group gets the group's sum.
+__device__ __forceinline__ float group_sum(float v, int sh) {
+  if (sh >= 2) {
+    v = quad_sum(v);
+    for (int o = 4; o < (1 << sh); o <<= 1) v += __shfl_xor(v, o, 64);
+  } else if (sh == 1) {
+    v += __shfl_xor(v, 1, 64);
+  }
+  return v;
+}
+
 // <a, b> over one 16-byte chunk with fp32 accumulation.
 template <typename T>
 __device__ __forceinline__ float dot_chunk(const uint4& a, const uint4& b);
@@ -692,6 +711,10 @@ __global__ __launch_bounds__(kThreads) void k_fwd(Geom g, const T* __restrict__ 
   }
 }
 
+// Rows per pair of barriers in the work-group-wide site pass.
+template <int CPT>
+constexpr int kSiteRowBatch = CPT <= 4 ? 4 : 2;
+
 // ---------------------------------------------------------------------------
 // Backward, site pass.  For every source n and (token, head):
 //   P_{n,h} = <dout_h, s_{n,h}>,   S_h = sum_n a_{n,h} P_{n,h}
@@ -701,9 +724,9 @@ __global__ __launch_bounds__(kThreads) void k_fwd(Geom g, const T* __restrict__ 
 //   W_t = sum_n a rho^-1 key_n  (per token, in registers),
 // so the rows are streamed once (the pages' kernel streams them twice).
 // Per row, each lane dots its 16-byte chunk with the upstream gradient; the
-// 4 lanes of a quad (4 chunks of one head) combine by DPP, quad leaders put
-// the sums in LDS and one thread per (token, head) adds its head's quads in a
-// fixed order.  After the tile the coefficients the finalize gather needs are
+// lanes of an aligned group inside one head (up to a wave) combine in
+// registers, group leaders put the sums in LDS and one thread per (row,
+// token, head) adds its head's groups in a fixed order.  After the tile the coefficients the finalize gather needs are
 // formed here: dl = a (P - S) and, per (source, token), the radial sum
 // sum_h dl_h * l_h with l = log(a) + lse (the logit).  Persistent grid of
 // `parts` work-groups, each writing one [r] partial of dq.
@@ -716,15 +739,20 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
     float* __restrict__ dq_part) {
   using V = Vec<T>;
   constexpr int N = V::N;
+  constexpr int RB = kSiteRowBatch<CPT>;  // rows per pair of barriers
   extern __shared__ float sm[];
   const int n_src = n_rows + (extra != nullptr ? 1 : 0);
   const int pairs = g.tt * g.H;
-  const bool quad = (g.kvc & 3) == 0;
+  // lanes hold consecutive chunks and a head's chunks start at a multiple
+  // of kvc, so the 2^sh lanes of an aligned group share one head when 2^sh
+  // divides kvc: their dots are summed in registers before LDS
+  const int sh = site_group_shift(g.kvc);
+  const int plen = g.tt * g.cpr;             // partial dots of one row (chunks)
   float* s_alpha = sm;                       // [n_src][tt][H]
   float* s_P = s_alpha + n_src * pairs;      // [n_src][tt][H]
   float* s_rinv = s_P + n_src * pairs;       // [n_src][tt]
-  float* s_part = s_rinv + n_src * g.tt;     // [tt * cpr] (or a quarter with quads)
-  float* s_S = s_part + g.tt * g.cpr;        // [tt][H]
+  float* s_part = s_rinv + n_src * g.tt;     // [RB][tt * cpr >> sh]
+  float* s_S = s_part + RB * (plen >> sh);   // [tt][H]
   float* s_lse = s_S + pairs;                // [tt][H]
   const int tid = threadIdx.x;
 
@@ -747,15 +775,13 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
     const int64_t t0 = tile * g.tt;
     const int tv = (int)min((int64_t)g.tt, g.T - t0);
     bool ok[CPT];
-    uint4 dov[CPT], cur[CPT];
+    uint4 dov[CPT];
     {
       const uint4* dp = reinterpret_cast<const uint4*>(dout + t0 * g.d);
-      const uint4* sp = tile_of(0, t0);
 #pragma unroll
       for (int j = 0; j < CPT; ++j) {
         ok[j] = sl[j].own && sl[j].tau < tv;
         dov[j] = ok[j] ? ld_stream(dp + sl[j].q) : zero4();
-        cur[j] = ok[j] ? ld_stream(sp + sl[j].q) : zero4();
       }
     }
     for (int i = tid; i < n_src * pairs; i += kThreads) {
@@ -774,59 +800,67 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
     for (int j = 0; j < CPT; ++j)
 #pragma unroll
       for (int e = 0; e < N; ++e) W[j][e] = 0.f;
-    float S_acc = 0.f;
     __syncthreads();
 
-    for (int n = 0; n < n_src; ++n) {
-      uint4 nxt[CPT];
-      if (n + 1 < n_src) {
-        const uint4* sp = tile_of(n + 1, t0);
+    // RB rows per step: every row's head dots need the whole work-group, so
+    // the rows of a batch share one pair of barriers (a token row spans
+    // several waves when rows are wide)
+    for (int n0 = 0; n0 < n_src; n0 += RB) {
+      uint4 cur[RB][CPT];
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) nxt[j] = ok[j] ? ld_stream(sp + sl[j].q) : zero4();
-      } else {
+      for (int r = 0; r < RB; ++r) {
+        const bool row = n0 + r < n_src;  // the last batch may be short
+        const uint4* sp = tile_of(row ? n0 + r : n0, t0);
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) nxt[j] = zero4();
+        for (int j = 0; j < CPT; ++j) cur[r][j] = ok[j] && row ? ld_stream(sp + sl[j].q) : zero4();
       }
 #pragma unroll
-      for (int j = 0; j < CPT; ++j) {
-        float part = dot_chunk<T>(dov[j], cur[j]);
-        if (quad) {
-          part = quad_sum(part);
-          if (sl[j].own && (sl[j].q & 3) == 0) s_part[sl[j].q >> 2] = part;
-        } else if (sl[j].own) {
-          s_part[sl[j].q] = part;
+      for (int r = 0; r < RB; ++r) {
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+          const float part = group_sum(dot_chunk<T>(dov[j], cur[r][j]), sh);
+          if (sl[j].own && (sl[j].q & ((1 << sh) - 1)) == 0)
+            s_part[((r * plen) >> sh) + (sl[j].q >> sh)] = part;
         }
       }
       __syncthreads();
-      if (tid < pairs) {
-        const int tau = tid / g.H, h = tid - tau * g.H;
-        const int sh = quad ? 2 : 0;
-        const float* pp = s_part + ((tau * g.cpr + h * g.kvc) >> sh);
+      // one thread per (row of the batch, token, head) adds its head's groups
+      for (int i = tid; i < RB * pairs; i += kThreads) {
+        const int r = i / pairs, p = i - r * pairs;
+        if (n0 + r >= n_src) break;
+        const int tau = p / g.H, h = p - tau * g.H;
+        const float* pp = s_part + ((r * plen + tau * g.cpr + h * g.kvc) >> sh);
         const int cnt = g.kvc >> sh;
         float P = 0.f;
         for (int c = 0; c < cnt; ++c) P += pp[c];
-        s_P[n * pairs + tid] = P;
-        S_acc += s_alpha[n * pairs + tid] * P;
+        s_P[(n0 + r) * pairs + p] = P;
       }
       __syncthreads();
 #pragma unroll
-      for (int j = 0; j < CPT; ++j) {
-        if (!sl[j].key) continue;
-        const int pi = sl[j].tau * g.H + sl[j].hk;
-        const float cw = s_alpha[n * pairs + pi] * s_rinv[n * g.tt + sl[j].tau];
-        const float cu = cw * s_P[n * pairs + pi];
-        float xv[N];
-        V::unpack(cur[j], xv);
+      for (int r = 0; r < RB; ++r) {
+        if (n0 + r >= n_src) break;
+        const int n = n0 + r;
 #pragma unroll
-        for (int e = 0; e < N; ++e) {
-          W[j][e] += cw * xv[e];
-          dq[j][e] += cu * xv[e];
+        for (int j = 0; j < CPT; ++j) {
+          if (!sl[j].key) continue;
+          const int pi = sl[j].tau * g.H + sl[j].hk;
+          const float cw = s_alpha[n * pairs + pi] * s_rinv[n * g.tt + sl[j].tau];
+          const float cu = cw * s_P[n * pairs + pi];
+          float xv[N];
+          V::unpack(cur[r][j], xv);
+#pragma unroll
+          for (int e = 0; e < N; ++e) {
+            W[j][e] += cw * xv[e];
+            dq[j][e] += cu * xv[e];
+          }
         }
       }
-#pragma unroll
-      for (int j = 0; j < CPT; ++j) cur[j] = nxt[j];
     }
-    if (tid < pairs) s_S[tid] = S_acc;
+    for (int p = tid; p < pairs; p += kThreads) {
+      float S = 0.f;
+      for (int n = 0; n < n_src; ++n) S += s_alpha[n * pairs + p] * s_P[n * pairs + p];
+      s_S[p] = S;
+    }
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
@@ -1419,7 +1453,9 @@ size_t lds_bwd_site(const Geom& g, int n_src) {
     return sizeof(float) * (a > b ? a : b);
   }
   const size_t pairs = (size_t)g.tt * g.H;
-  const size_t a = 2 * (size_t)n_src * pairs + (size_t)n_src * g.tt + (size_t)g.tt * g.cpr + 2 * pairs;
+  const size_t rb = g.cpt <= 4 ? 4 : 2;  // kSiteRowBatch
+  const size_t part = rb * (((size_t)g.tt * g.cpr) >> site_group_shift(g.kvc));
+  const size_t a = 2 * (size_t)n_src * pairs + (size_t)n_src * g.tt + part + 2 * pairs;
   const size_t b = (size_t)g.tt * g.r;
   return sizeof(float) * (a > b ? a : b);
 }
