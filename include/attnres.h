@@ -287,6 +287,71 @@ attnres_status_t attnres_delta_bwd(const attnres_delta_t* call, const void* dout
                                    float* d_null, float* dq, void* workspace,
                                    size_t workspace_bytes, attnres_stream_t stream);
 
+/* ---- Source list: one self-contained read over any shape ---------------
+ * "Low-Rank Attention Residuals", Appendix I (implementation; numerical
+ * correctness): one operator serves full routing (r = d) and sliced routing
+ * (r < d) over a list of sources chosen by the caller; the keys are the last
+ * r coordinates of each source, RMS-normalised without a gain (Eq. 11, or
+ * over all d with ATTNRES_NORM_FULL, Eq. 13 control), scored by the H heads
+ * of the query, and the softmax weights mix all d coordinates per head:
+ *     out = sum_n alpha_n s_n
+ * This is the general-shape path: d and r need no alignment (d = 513 is
+ * fine), each source has its own token stride (0 repeats one row for every
+ * token), a pointer may appear several times in the list (each entry is a
+ * separate source and gets its own gradient), and the query may be strided.
+ * Every access is one element wide; the bank above is the fast path for
+ * aligned shapes.  Nothing is kept between calls, so replays with changed
+ * inputs recompute everything.
+ * Limits: 1 <= n_sources <= 64, n_sources * (H + 1) <= 4096,
+ * r + 2 n_sources (H + 1) + H <= 16384 (else ATTNRES_ERR_UNSUPPORTED). */
+typedef struct {
+  int64_t tokens;            /* T >= 0 */
+  int32_t d;                 /* value width >= 1 */
+  int32_t r;                 /* key width, 1 <= r <= d: the last r coordinates */
+  int32_t heads;             /* H, H | d and H | r */
+  int32_t n_sources;         /* entries in the list */
+  int32_t dtype;             /* attnres_dtype_t: storage dtype of sources, query, out, dout */
+  float eps;                 /* RMSNorm epsilon (1e-6) */
+  int32_t norm;              /* attnres_norm_t */
+  const void* const* sources;     /* host array [n_sources] of device pointers; source n,
+                                     token t starts at sources[n] + t * source_strides[n]
+                                     elements and holds d elements */
+  const int64_t* source_strides;  /* host array [n_sources] of token strides in elements
+                                     (>= 0), or NULL for d */
+  const void* query;         /* device: query coordinate k at query + k * query_stride */
+  int64_t query_stride;      /* elements, >= 1 */
+} attnres_list_t;
+
+/* Device workspace bytes attnres_list_bwd needs for this call shape (0 if the
+ * shape is invalid; see attnres_last_error). */
+size_t attnres_list_workspace_bytes(const attnres_list_t* call);
+
+/* Forward of one list read.
+ *   out    device [T, d] storage dtype, contiguous (overwritten)
+ *   alpha  device float32 [n_sources, T, H] softmax weights (overwritten)
+ *   lse    device float32 [T, H] log-sum-exp of the logits (overwritten)
+ *   rinv   device float32 [n_sources, T] inverse RMS of each source (overwritten)
+ * Pointers must be aligned to their element size; NULL allowed when T == 0.
+ * out must not overlap a source. */
+attnres_status_t attnres_list_fwd(const attnres_list_t* call, void* out, float* alpha, float* lse,
+                                  float* rinv, attnres_stream_t stream);
+
+/* Backward of one list read, for the loss <dout, out>.
+ *   dout       device [T, d] storage dtype, contiguous
+ *   alpha, lse, rinv   what attnres_list_fwd wrote for the same call and inputs
+ *   d_sources  host array [n_sources] of device float32 [T, d], contiguous: the
+ *              gradient of each entry (stored, not accumulated); entries must
+ *              be distinct buffers, also when sources repeat (the gradient of
+ *              a repeated tensor is the sum of its entries' gradients)
+ *   dq         device float32 [r]: gradient of the query coordinates
+ *   workspace  attnres_list_workspace_bytes(call) bytes of device memory
+ * Reductions over tokens run in a fixed order: results are bitwise
+ * reproducible. */
+attnres_status_t attnres_list_bwd(const attnres_list_t* call, const void* dout,
+                                  const float* alpha, const float* lse, const float* rinv,
+                                  float* const* d_sources, float* dq, void* workspace,
+                                  size_t workspace_bytes, attnres_stream_t stream);
+
 /* Kernel kinds reported by the launch trace. */
 typedef enum {
   ATTNRES_KERNEL_SCORE = 0,     /* append (and transient-source) scoring */
@@ -327,7 +392,8 @@ const char* attnres_last_error(void);
 /* Destroy the handle (the caller's buffers are untouched).  NULL is ignored. */
 void attnres_bank_destroy(attnres_bank_t bank);
 
-/* ABI version of this header: 2 (1 had no norm field and no gains). */
+/* ABI version of this header: 3 (2 had no source-list read; 1 had no norm
+ * field and no gains). */
 int32_t attnres_abi_version(void);
 
 #ifdef __cplusplus

@@ -34,7 +34,7 @@ def test_header_declarations_are_exported(lib):
     assert set(names) == set(A.EXPORTS)
     for n in names:
         assert getattr(lib, n) is not None
-    assert A.attnres_abi_version() == 2
+    assert A.attnres_abi_version() == 3
 
 
 def cfg(**kw):
@@ -204,4 +204,55 @@ def test_delta_workspace_and_argument_checks(lib):
     assert e.value.status == A.ATTNRES_ERR_CAPACITY
     with pytest.raises(A.AttnResError) as e:  # out missing
         A.attnres_delta_fwd(c, None, None, FAKE, FAKE, stream=0)
+    assert e.value.status == A.ATTNRES_ERR_INVALID
+
+
+def list_call(**kw):
+    base = dict(tokens=64, d=513, r=135, heads=3, sources=[FAKE, FAKE + 2, FAKE],
+                strides=[600, 0, 513], query=FAKE, query_stride=7, dtype=A.ATTNRES_BF16)
+    base.update(kw)
+    return A.make_list_call(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(r=600), A.ATTNRES_ERR_INVALID),                 # r > d
+    (dict(heads=2), A.ATTNRES_ERR_INVALID),               # H does not divide d
+    (dict(r=136), A.ATTNRES_ERR_INVALID),                 # H does not divide r
+    (dict(sources=[], strides=None), A.ATTNRES_ERR_INVALID),
+    (dict(sources=[FAKE] * 65, strides=None), A.ATTNRES_ERR_INVALID),
+    (dict(sources=[FAKE, FAKE + 1, FAKE]), A.ATTNRES_ERR_INVALID),  # bf16 needs 2-byte alignment
+    (dict(sources=[FAKE, 0, FAKE]), A.ATTNRES_ERR_INVALID),
+    (dict(strides=[600, -1, 513]), A.ATTNRES_ERR_INVALID),
+    (dict(query_stride=0), A.ATTNRES_ERR_INVALID),
+    (dict(query=FAKE + 1), A.ATTNRES_ERR_INVALID),
+    (dict(norm=5), A.ATTNRES_ERR_INVALID),
+    (dict(d=16384, r=16384, heads=1), A.ATTNRES_ERR_UNSUPPORTED),  # dq does not fit in LDS
+    (dict(d=7168, r=1792, heads=64, sources=[FAKE] * 64, strides=None),
+     A.ATTNRES_ERR_UNSUPPORTED),  # n (H + 1) > 4096
+])
+def test_list_bad_calls_rejected(lib, kw, status):
+    c = list_call(**kw)
+    assert lib.attnres_list_workspace_bytes(ctypes.byref(c)) == 0
+    with pytest.raises(A.AttnResError) as e:  # shape checks run before any launch
+        A.attnres_list_bwd(c, FAKE, FAKE, FAKE, FAKE, [FAKE + 16 * i for i in range(65)], FAKE,
+                           FAKE, 1 << 40, stream=0)
+    assert e.value.status == status
+
+
+def test_list_workspace_and_argument_checks(lib):
+    c = list_call()
+    n = A.attnres_list_workspace_bytes(c)
+    assert n >= 64 * 135 * 4  # one dq partial row per wave, one wave per token here
+    assert A.attnres_list_workspace_bytes(list_call(tokens=0)) > 0
+    assert A.attnres_list_workspace_bytes(list_call(d=7168, r=1792, heads=8, strides=None)) > 0
+    with pytest.raises(A.AttnResError) as e:  # entries must get distinct gradient buffers
+        A.attnres_list_bwd(c, FAKE, FAKE, FAKE, FAKE, [FAKE, FAKE + 16, FAKE], FAKE, FAKE, n,
+                           stream=0)
+    assert e.value.status == A.ATTNRES_ERR_INVALID
+    with pytest.raises(A.AttnResError) as e:  # workspace too small
+        A.attnres_list_bwd(c, FAKE, FAKE, FAKE, FAKE, [FAKE, FAKE + 16, FAKE + 32], FAKE, FAKE,
+                           n - 1, stream=0)
+    assert e.value.status == A.ATTNRES_ERR_CAPACITY
+    with pytest.raises(A.AttnResError) as e:  # rinv missing
+        A.attnres_list_fwd(c, FAKE, FAKE, FAKE, None, stream=0)
     assert e.value.status == A.ATTNRES_ERR_INVALID

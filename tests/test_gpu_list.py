@@ -1,0 +1,175 @@
+"""Source-list read (one self-contained read over any shape) on the HIP path
+vs the CPU oracle ("Low-Rank Attention Residuals", Appendix I: unaligned
+width d=513 and ranks, repeated or strided sources, strided queries,
+changed-input replays), element by element on seeded inputs.
+
+Tolerances as for the bank: max-rel <= 1e-5 (fp32 storage) or 2e-2 (bf16)
+for out, lse, the inverse RMS and every gradient; softmax weights within 1e-3
+absolute.  The gradient of every list entry is compared on its own (a tensor
+listed twice gets one gradient per entry).
+"""
+
+import numpy as np
+import pytest
+
+from oracle import route_backward, route_forward, source_inv_rms
+from synth import LIST_SHAPES, ListInputs, ListShape, sample_tokens
+from synth.device import from_device, to_device
+
+from gpu_harness import ALPHA_TOL, TOL, log, max_rel
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # unaligned width and rank; strided (pads and offsets), repeated entries,
+    # strided query; query scales give logits of order 1 (q ~ 2 / sqrt(r / H))
+    ListShape("d513_r135_h3", 37, 513, 135, 3, (0, 1, 2, 0), pads=(87, 0, 5), offsets=(1, 0, 3),
+              qstride=7, qscale=0.3),
+    # RMS over all d (control) with a broadcast source (token stride 0)
+    ListShape("d513_r171_h3_full", 29, 513, 171, 3, (0, 1, 2), pads=(0, -1, 2), qstride=2,
+              qscale=0.25, norm="full"),
+    # full-width keys (r = d), fp32, one tensor listed twice
+    ListShape("d513_r513_f32", 41, 513, 513, 1, (0, 1, 1, 2, 3), offsets=(0, 1), dtype="f32",
+              qscale=0.1),
+    ListShape("d7_r3_f32", 5, 7, 3, 1, (0, 1), dtype="f32", qscale=1.0),
+    ListShape("d7_r3_f32_full", 5, 7, 3, 1, (0, 1, 0), dtype="f32", qscale=1.0, norm="full"),
+    # the low-rank shape (aligned) at a ragged token count
+    ListShape("lr_d7168_r1792_h8", 19, 7168, 1792, 8, tuple(range(10))),
+    # the most sources a call takes, over 16 tensors
+    ListShape("n64", 70, 96, 48, 4, tuple(k % 16 for k in range(64)), qscale=0.5),
+    ListShape("n1", 13, 100, 20, 2, (0,), qscale=1.0),
+    # many narrow heads
+    ListShape("h64_f32", 9, 640, 640, 64, (0, 1, 2), dtype="f32", qscale=0.6),
+    # rank wider than a wave per head, odd head width
+    ListShape("d1000_r600_h2", 33, 1000, 600, 2, (0, 1, 2, 3), pads=(3, 0, 0, 1), qstride=5,
+              qscale=0.1),
+]
+
+
+def upload(s: ListShape, inp: ListInputs):
+    """Device buffers laid out as the shape says; returns the list entries
+    (views), the query view and the buffers."""
+    import torch
+    bufs = [to_device(inp.stored_tensor(k), s.dtype) for k in range(s.tensors)]
+    views = []
+    for k, b in enumerate(bufs):
+        v = b[:, s.offset(k):s.offset(k) + s.d]
+        views.append(v.expand(s.tokens, s.d) if s.broadcast(k) else v)
+    qbuf = to_device(inp.stored_query(), s.dtype)
+    q = torch.as_strided(qbuf, (s.r,), (s.qstride,))
+    return [views[k] for k in s.entries], q, bufs, qbuf
+
+
+def run_gpu(s: ListShape, inp: ListInputs, tokens=None, dout_tokens=None, read=None, dev=None):
+    import torch
+    from transformer_depth_wise_amd.attnres import ListRead
+    if dev is None:
+        dev = upload(s, inp)
+    entries, q = dev[0], dev[1]
+    dout_np = inp.value("dout")
+    if dout_tokens is not None:
+        keep = np.zeros(s.tokens, dtype=bool)
+        keep[dout_tokens] = True
+        dout_np = dout_np.copy()
+        dout_np[~keep] = 0.0
+    dout = to_device(dout_np, s.dtype)
+    rd = read or ListRead(entries, q, s.heads, eps=s.eps, norm=s.norm, tokens=s.tokens)
+    out, alpha, lse, rinv = rd.forward()
+    ds, dq = rd.backward(dout, alpha, lse, rinv)
+    torch.cuda.synchronize()
+    idx = None if tokens is None else torch.as_tensor(np.asarray(tokens), device="cuda")
+
+    def pick(t, axis):
+        return t if idx is None else t.index_select(axis, idx)
+
+    return {"out": from_device(pick(out, 0)), "alpha": from_device(pick(alpha, 1)),
+            "lse": from_device(pick(lse, 0)), "rinv": from_device(pick(rinv, 1)),
+            "ds": [from_device(pick(x, 0)) for x in ds], "dq": from_device(dq)}
+
+
+def run_ref(s: ListShape, inp: ListInputs, tokens=None, dout_tokens=None):
+    sel = slice(None) if tokens is None else np.asarray(tokens)
+    src = inp.entry_values()[:, sel].astype(np.float64)
+    q = inp.value("query").astype(np.float64)
+    dout = inp.value("dout")
+    if dout_tokens is not None:
+        keep = np.zeros(s.tokens, dtype=bool)
+        keep[dout_tokens] = True
+        dout = dout.copy()
+        dout[~keep] = 0.0
+    dout = dout[sel].astype(np.float64)
+    out, alpha, lse = route_forward(src, q, s.heads, s.r, s.eps, norm=s.norm)
+    ds, dq = route_backward(src, q, s.heads, s.r, dout, s.eps, norm=s.norm)
+    rinv = source_inv_rms(src, s.r, s.eps, s.norm)
+    return {"out": out, "alpha": alpha, "lse": lse, "rinv": rinv, "ds": list(ds), "dq": dq}
+
+
+def compare(s, got, ref, label=""):
+    tol = TOL[s.dtype]
+    err = {"out": max_rel(got["out"], ref["out"]), "lse": max_rel(got["lse"], ref["lse"]),
+           "rinv": max_rel(got["rinv"], ref["rinv"]),
+           "alpha_abs": float(np.abs(got["alpha"] - ref["alpha"]).max()),
+           "dsources": max(max_rel(a, b) for a, b in zip(got["ds"], ref["ds"])),
+           "dq": max_rel(got["dq"], ref["dq"])}
+    log(f"  {label} {s.describe()} errors: " + ", ".join(f"{k}={v:.3e}" for k, v in err.items()))
+    for k, v in err.items():
+        limit = ALPHA_TOL if k == "alpha_abs" else tol
+        assert v <= limit, f"{k} error {v:.3e} above {limit:.1e}"
+
+
+@pytest.mark.parametrize("s", CASES, ids=lambda s: s.name)
+def test_list_matches_oracle(s):
+    inp = ListInputs(s)
+    log(f"[list] {s.describe()}")
+    compare(s, run_gpu(s, inp), run_ref(s, inp), label="list")
+
+
+def test_list_empty_tokens():
+    s = ListShape("d513_t0", 0, 513, 135, 3, (0, 1))
+    inp = ListInputs(s)
+    log(f"[list] {s.describe()}")
+    got = run_gpu(s, inp)
+    assert got["out"].shape == (0, 513)
+    assert got["ds"][0].shape == (0, 513)
+    assert not got["dq"].any()
+
+
+def test_list_changed_input_replay():
+    """One call description, run, then the sources and the query rewritten in
+    place and run again: the second run matches the oracle on the new
+    inputs (nothing is kept between calls)."""
+    s = CASES[0]
+    inp0, inp1 = ListInputs(s), ListInputs(s, generation=1)
+    log(f"[list replay] {s.describe()}")
+    from transformer_depth_wise_amd.attnres import ListRead
+    dev = upload(s, inp0)
+    entries, q, bufs, qbuf = dev
+    rd = ListRead(entries, q, s.heads, eps=s.eps, norm=s.norm, tokens=s.tokens)
+    compare(s, run_gpu(s, inp0, read=rd, dev=dev), run_ref(s, inp0), label="first")
+    for k, b in enumerate(bufs):
+        to_device(inp1.stored_tensor(k), s.dtype, out=b)
+    to_device(inp1.stored_query(), s.dtype, out=qbuf)
+    compare(s, run_gpu(s, inp1, read=rd, dev=dev), run_ref(s, inp1), label="replay")
+
+
+def test_list_deterministic_bitwise():
+    s = CASES[-1]
+    inp = ListInputs(s)
+    a, b = run_gpu(s, inp), run_gpu(s, inp)
+    for k in ("out", "alpha", "lse", "rinv", "dq"):
+        np.testing.assert_array_equal(a[k], b[k])
+    for x, y in zip(a["ds"], b["ds"]):
+        np.testing.assert_array_equal(x, y)
+
+
+@pytest.mark.parametrize("name", list(LIST_SHAPES))
+def test_list_full_size_sampled_tokens(name):
+    """The benchmarked list shapes at full size: sampled tokens against the
+    oracle; dq through upstream gradients masked to the sampled tokens."""
+    s = LIST_SHAPES[name]
+    inp = ListInputs(s)
+    toks = sample_tokens(s.tokens, 16)
+    log(f"[list full-size] {s.describe()} sampled tokens={len(toks)}")
+    got = run_gpu(s, inp, tokens=toks, dout_tokens=toks)
+    ref = run_ref(s, inp, tokens=toks, dout_tokens=toks)
+    compare(s, got, ref, label="sampled+masked")

@@ -560,3 +560,73 @@ def test_delta_zero_null_is_a_zero_logit_sink():
                 j = h * kv + k
                 ref = sum(w[n] * float(deltas[n, t, j]) for n in range(M)) / z + partial[t, j]
                 assert out[t, j] == pytest.approx(ref, rel=1e-12, abs=1e-12)
+
+
+# Source lists of any shape ("Low-Rank Attention Residuals", Appendix I,
+# numerical correctness: unaligned width d=513, repeated or strided sources).
+# The oracle's read takes any d, r with H | d and H | r; these pins check it
+# at odd widths and ranks, with an entry of the list repeated: the gradient of
+# a tensor listed twice is the sum of the gradients of its two entries.
+LIST_FD_CASES = {
+    "d13_r5_h1_slice": (13, 5, 1, "slice"),
+    "d9_r6_h3_slice": (9, 6, 3, "slice"),
+    "d9_r6_h3_full": (9, 6, 3, "full"),
+    "d7_r7_h1": (7, 7, 1, "slice"),
+}
+
+
+@pytest.mark.parametrize("kind", list(LIST_FD_CASES))
+def test_list_read_gradients_with_repeated_source(kind):
+    d, r, H, norm = LIST_FD_CASES[kind]
+    rng = np.random.default_rng(29)
+    T = 3
+    a = rng.standard_normal((T, d)) * 1.5
+    b = rng.standard_normal((T, d)) * 0.7
+    c = rng.standard_normal((T, d))
+    q = rng.standard_normal(r)
+    dout = rng.standard_normal((T, d))
+
+    def loss():
+        out, _, _ = route_forward(np.stack([a, b, a, c]), q, H, r, norm=norm)
+        return float((out * dout).sum())
+
+    ds, dq = route_backward(np.stack([a, b, a, c]), q, H, r, dout, norm=norm)
+    h = 1e-6
+
+    def fd(arr):
+        g = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + h
+            lp = loss()
+            arr[idx] = old - h
+            lm = loss()
+            arr[idx] = old
+            g[idx] = (lp - lm) / (2 * h)
+        return g
+
+    np.testing.assert_allclose(ds[0] + ds[2], fd(a), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(ds[1], fd(b), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(ds[3], fd(c), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(dq, fd(q), rtol=1e-6, atol=1e-8)
+
+
+def test_list_read_repeated_source_is_a_log2_logit_shift():
+    # Listing a source twice gives both entries the same weight; the mix is
+    # the read over the list with that source once and e^l doubled.  Written
+    # with scalar loops at d=5, r=3, H=1 (the last 3 coordinates are the key).
+    rng = np.random.default_rng(31)
+    T, d, r = 2, 5, 3
+    a, b = rng.standard_normal((T, d)), rng.standard_normal((T, d))
+    q = rng.standard_normal(r)
+    out, alpha, _ = route_forward(np.stack([a, b, a]), q, 1, r)
+    for t in range(T):
+        def logit(x):
+            ms = sum(float(v) ** 2 for v in x[t, d - r:]) / r
+            return sum(float(q[k]) * float(x[t, d - r + k]) for k in range(r)) / math.sqrt(ms + 1e-6)
+        ea, eb = 2.0 * math.exp(logit(a)), math.exp(logit(b))
+        assert alpha[0, t, 0] == pytest.approx(0.5 * ea / (ea + eb), rel=1e-12)
+        assert alpha[2, t, 0] == pytest.approx(alpha[0, t, 0], rel=1e-15)
+        for j in range(d):
+            ref = (ea * float(a[t, j]) + eb * float(b[t, j])) / (ea + eb)
+            assert out[t, j] == pytest.approx(ref, rel=1e-12, abs=1e-12)

@@ -46,6 +46,9 @@ EXPORTS = (
     "attnres_delta_workspace_bytes",
     "attnres_delta_fwd",
     "attnres_delta_bwd",
+    "attnres_list_workspace_bytes",
+    "attnres_list_fwd",
+    "attnres_list_bwd",
     "attnres_trace_enable",
     "attnres_trace_read",
     "attnres_probe_sink_words",
@@ -85,6 +88,23 @@ class DeltaCallC(ctypes.Structure):
     ]
 
 
+class ListCallC(ctypes.Structure):
+    _fields_ = [
+        ("tokens", c_int64),
+        ("d", c_int32),
+        ("r", c_int32),
+        ("heads", c_int32),
+        ("n_sources", c_int32),
+        ("dtype", c_int32),
+        ("eps", c_float),
+        ("norm", c_int32),
+        ("sources", POINTER(c_void_p)),
+        ("source_strides", POINTER(c_int64)),
+        ("query", c_void_p),
+        ("query_stride", c_int64),
+    ]
+
+
 class AttnResError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
@@ -120,6 +140,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "attnres_delta_fwd": (i32, [POINTER(DeltaCallC), vp, vp, vp, vp, vp]),
         "attnres_delta_bwd": (i32, [POINTER(DeltaCallC), vp, vp, vp, POINTER(vp), vp, vp, vp,
                                     c_size_t, vp]),
+        "attnres_list_workspace_bytes": (c_size_t, [POINTER(ListCallC)]),
+        "attnres_list_fwd": (i32, [POINTER(ListCallC), vp, vp, vp, vp, vp]),
+        "attnres_list_bwd": (i32, [POINTER(ListCallC), vp, vp, vp, vp, POINTER(vp), vp, vp,
+                                   c_size_t, vp]),
         "attnres_trace_enable": (i32, [vp, i32]),
         "attnres_trace_read": (i32, [vp, POINTER(ctypes.c_double), POINTER(c_int64)]),
         "attnres_probe_sink_words": (i32, []),
@@ -431,3 +455,91 @@ class DeltaRead:
         ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         attnres_delta_bwd(self.call, dout, alpha, lse, dd, dn, dq, ws, nbytes, stream)
         return dd, dn, dq
+
+
+# ---------------------------------------------------------------------------
+# Source list: one self-contained read over any shape.
+def make_list_call(tokens, d, r, heads, sources, strides, query, query_stride, dtype,
+                   eps=1e-6, norm="slice"):
+    """The C description of one list read.  `sources` are device tensors or
+    addresses (kept alive by the caller), `strides` their token strides in
+    elements (None: d for every source)."""
+    n = len(sources)
+    ptrs = (c_void_p * max(n, 1))(*[_ptr(x) for x in sources])
+    st = None
+    if strides is not None:
+        st = (c_int64 * max(n, 1))(*[int(x) for x in strides])
+    call = ListCallC(int(tokens), int(d), int(r), int(heads), n, int(dtype), float(eps),
+                     NORMS[norm] if isinstance(norm, str) else int(norm),
+                     ctypes.cast(ptrs, POINTER(c_void_p)),
+                     ctypes.cast(st, POINTER(c_int64)) if st is not None else None,
+                     _ptr(query), int(query_stride))
+    call._keep = (ptrs, st)  # keep the host arrays alive with the struct
+    return call
+
+
+def attnres_list_workspace_bytes(call) -> int:
+    n = load_library().attnres_list_workspace_bytes(ctypes.byref(call))
+    if n == 0:
+        raise AttnResError(ATTNRES_ERR_INVALID, last_error())
+    return int(n)
+
+
+def attnres_list_fwd(call, out, alpha, lse, rinv, stream=None) -> None:
+    _check(load_library().attnres_list_fwd(ctypes.byref(call), _ptr(out), _ptr(alpha), _ptr(lse),
+                                           _ptr(rinv), _stream(stream)))
+
+
+def attnres_list_bwd(call, dout, alpha, lse, rinv, d_sources, dq, workspace, workspace_bytes,
+                     stream=None) -> None:
+    arr = (c_void_p * max(len(d_sources), 1))(*[_ptr(x) for x in d_sources])
+    _check(load_library().attnres_list_bwd(ctypes.byref(call), _ptr(dout), _ptr(alpha),
+                                           _ptr(lse), _ptr(rinv), arr, _ptr(dq),
+                                           _ptr(workspace), int(workspace_bytes),
+                                           _stream(stream)))
+
+
+class ListRead:
+    """One list read over device tensors: `sources` is a list of [T, d] views
+    whose rows may be strided (stride(1) must be 1; a stride(0) of 0 repeats
+    one row) and may repeat, `query` a [r] view (any element stride), all in
+    the storage dtype.  Keys are the last r coordinates."""
+
+    def __init__(self, sources, query, heads, eps=1e-6, norm="slice", tokens=None):
+        import torch
+        self.torch = torch
+        self.sources = list(sources)
+        if not self.sources:
+            raise ValueError("a list read needs at least one source")
+        for x in self.sources:
+            if x.dim() != 2 or (x.numel() > 0 and x.shape[1] > 1 and x.stride(1) != 1):
+                raise ValueError("sources must be [T, d] views with unit element stride")
+        self.T = int(tokens if tokens is not None else self.sources[0].shape[0])
+        self.d = int(self.sources[0].shape[1])
+        self.r = int(query.shape[0])
+        self.H = int(heads)
+        self.tdtype = query.dtype
+        dt = ATTNRES_BF16 if query.dtype == torch.bfloat16 else ATTNRES_F32
+        strides = [x.stride(0) for x in self.sources]
+        self.call = make_list_call(self.T, self.d, self.r, self.H, self.sources, strides, query,
+                                   query.stride(0), dt, eps, norm)
+        self.n = len(self.sources)
+
+    def forward(self, stream=None):
+        torch = self.torch
+        out = torch.empty((self.T, self.d), dtype=self.tdtype, device="cuda")
+        alpha = torch.empty((self.n, self.T, self.H), dtype=torch.float32, device="cuda")
+        lse = torch.empty((self.T, self.H), dtype=torch.float32, device="cuda")
+        rinv = torch.empty((self.n, self.T), dtype=torch.float32, device="cuda")
+        attnres_list_fwd(self.call, out, alpha, lse, rinv, stream)
+        return out, alpha, lse, rinv
+
+    def backward(self, dout, alpha, lse, rinv, stream=None):
+        torch = self.torch
+        ds = [torch.empty((self.T, self.d), dtype=torch.float32, device="cuda")
+              for _ in self.sources]
+        dq = torch.empty(self.r, dtype=torch.float32, device="cuda")
+        nbytes = attnres_list_workspace_bytes(self.call)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        attnres_list_bwd(self.call, dout, alpha, lse, rinv, ds, dq, ws, nbytes, stream)
+        return ds, dq

@@ -14,7 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libattnres.so")
-SOURCES = ["attnres_kernels.hip", "attnres_delta.hip", "attnres_probe.hip", "attnres_host.cpp"]
+SOURCES = ["attnres_kernels.hip", "attnres_delta.hip", "attnres_list.hip", "attnres_probe.hip",
+           "attnres_host.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -283,7 +283,7 @@ void trace_clear(attnres_bank_s* b) {
 
 extern "C" {
 
-int32_t attnres_abi_version(void) { return 2; }
+int32_t attnres_abi_version(void) { return 3; }
 
 attnres_status_t attnres_trace_enable(attnres_bank_t b, int32_t enable) {
   if (!b) return fail(ATTNRES_ERR_INVALID, "bank is NULL");
@@ -795,6 +795,146 @@ attnres_status_t attnres_delta_bwd(const attnres_delta_t* call, const void* dout
     if (e != hipSuccess) return hip_fail(e, "delta null-source gradient");
   }
   return ATTNRES_OK;
+}
+
+// ---- source list -------------------------------------------------------------
+namespace {
+
+bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+attnres_status_t list_geom(const attnres_list_t* c, attnres::ListGeom* g) {
+  if (!c) return fail(ATTNRES_ERR_INVALID, "list call is NULL");
+  if (c->tokens < 0) return fail(ATTNRES_ERR_INVALID, "tokens must be >= 0");
+  if (c->dtype != ATTNRES_F32 && c->dtype != ATTNRES_BF16)
+    return fail(ATTNRES_ERR_INVALID, "dtype must be ATTNRES_F32 or ATTNRES_BF16 (got %d)", c->dtype);
+  if (c->d < 1 || c->r < 1 || c->r > c->d)
+    return fail(ATTNRES_ERR_INVALID, "need 1 <= r <= d (got d=%d r=%d)", c->d, c->r);
+  if (c->heads < 1 || c->d % c->heads || c->r % c->heads)
+    return fail(ATTNRES_ERR_INVALID, "need heads >= 1 dividing d and r (got d=%d r=%d heads=%d)",
+                c->d, c->r, c->heads);
+  if (!(c->eps > 0.f)) return fail(ATTNRES_ERR_INVALID, "eps must be > 0");
+  if (c->norm != ATTNRES_NORM_SLICE && c->norm != ATTNRES_NORM_FULL)
+    return fail(ATTNRES_ERR_INVALID, "norm must be ATTNRES_NORM_SLICE or ATTNRES_NORM_FULL");
+  if (c->n_sources < 1 || c->n_sources > attnres::kMaxListSources)
+    return fail(ATTNRES_ERR_INVALID, "need 1 <= n_sources <= %d (got %d)", attnres::kMaxListSources,
+                c->n_sources);
+  if ((int64_t)c->n_sources * (c->heads + 1) > 4096)
+    return fail(ATTNRES_ERR_UNSUPPORTED, "n_sources * (heads + 1) must be <= 4096");
+  if ((int64_t)c->r + 2 * (int64_t)c->n_sources * (c->heads + 1) + c->heads > 16384)
+    return fail(ATTNRES_ERR_UNSUPPORTED, "r + 2 n_sources (heads + 1) + heads must be <= 16384");
+  if (c->query_stride < 1) return fail(ATTNRES_ERR_INVALID, "query_stride must be >= 1");
+  const size_t es = c->dtype == ATTNRES_F32 ? 4 : 2;
+  if (c->tokens > 0) {
+    if (!c->sources) return fail(ATTNRES_ERR_INVALID, "sources array is NULL");
+    if (!c->query || !aligned_to(c->query, es))
+      return fail(ATTNRES_ERR_INVALID, "query must be non-NULL and aligned to its element size");
+    if ((int64_t)c->r > ((int64_t)1 << 62) / c->query_stride)
+      return fail(ATTNRES_ERR_UNSUPPORTED, "r * query_stride overflows");
+    for (int n = 0; n < c->n_sources; ++n) {
+      if (!c->sources[n] || !aligned_to(c->sources[n], es))
+        return fail(ATTNRES_ERR_INVALID, "source %d must be non-NULL and aligned to its element size",
+                    n);
+      const int64_t stride = c->source_strides ? c->source_strides[n] : c->d;
+      if (stride < 0) return fail(ATTNRES_ERR_INVALID, "source %d has a negative stride", n);
+      if (stride > 0 && c->tokens > (((int64_t)1 << 62) - c->d) / stride)
+        return fail(ATTNRES_ERR_UNSUPPORTED, "source %d: tokens * stride overflows", n);
+    }
+  }
+  if (c->tokens > ((int64_t)1 << 62) / c->d)
+    return fail(ATTNRES_ERR_UNSUPPORTED, "tokens * d overflows");
+  g->T = c->tokens;
+  g->d = c->d;
+  g->r = c->r;
+  g->H = c->heads;
+  g->kv = c->d / c->heads;
+  g->kk = c->r / c->heads;
+  g->n = c->n_sources;
+  g->k0 = c->d - c->r;
+  g->n0 = c->norm == ATTNRES_NORM_FULL ? 0 : g->k0;
+  g->w = c->d - g->n0;
+  g->qs = c->query_stride;
+  g->eps = c->eps;
+  return ATTNRES_OK;
+}
+
+attnres::ListArgs list_args(const attnres_list_t* c) {
+  attnres::ListArgs a{};
+  a.query = c->query;
+  for (int n = 0; n < c->n_sources && c->tokens > 0; ++n) {
+    a.src[n] = c->sources[n];
+    a.stride[n] = c->source_strides ? c->source_strides[n] : c->d;
+  }
+  return a;
+}
+
+size_t list_ws_bytes(const attnres::ListGeom& g) {
+  const size_t parts = (size_t)attnres::list_bwd_parts(g);
+  return align256(sizeof(float) * (parts > 0 ? parts : 1) * g.r);
+}
+
+}  // namespace
+
+size_t attnres_list_workspace_bytes(const attnres_list_t* call) {
+  attnres::ListGeom g{};
+  if (list_geom(call, &g) != ATTNRES_OK) return 0;
+  return list_ws_bytes(g);
+}
+
+attnres_status_t attnres_list_fwd(const attnres_list_t* call, void* out, float* alpha, float* lse,
+                                  float* rinv, attnres_stream_t stream) {
+  attnres::ListGeom g{};
+  attnres_status_t st = list_geom(call, &g);
+  if (st != ATTNRES_OK) return st;
+  if (g.T == 0) return ATTNRES_OK;
+  const size_t es = call->dtype == ATTNRES_F32 ? 4 : 2;
+  if (!out || !alpha || !lse || !rinv)
+    return fail(ATTNRES_ERR_INVALID, "out, alpha, lse and rinv must be non-NULL");
+  if (!aligned_to(out, es) || !aligned_to(alpha, 4) || !aligned_to(lse, 4) || !aligned_to(rinv, 4))
+    return fail(ATTNRES_ERR_INVALID, "out, alpha, lse and rinv must be aligned to their element size");
+  hipError_t e = attnres::launch_list_fwd(g, call->dtype, list_args(call), out, alpha, lse, rinv,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTNRES_OK : hip_fail(e, "list forward kernel");
+}
+
+attnres_status_t attnres_list_bwd(const attnres_list_t* call, const void* dout,
+                                  const float* alpha, const float* lse, const float* rinv,
+                                  float* const* d_sources, float* dq, void* workspace,
+                                  size_t workspace_bytes, attnres_stream_t stream) {
+  attnres::ListGeom g{};
+  attnres_status_t st = list_geom(call, &g);
+  if (st != ATTNRES_OK) return st;
+  if (!dq || !aligned_to(dq, 4)) return fail(ATTNRES_ERR_INVALID, "dq must be non-NULL, 4-byte aligned");
+  const size_t need = list_ws_bytes(g);
+  if (!workspace || !aligned16(workspace))
+    return fail(ATTNRES_ERR_INVALID, "workspace must be non-NULL and 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(ATTNRES_ERR_CAPACITY, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  attnres::ListGrads gr{};
+  if (g.T > 0) {
+    const size_t es = call->dtype == ATTNRES_F32 ? 4 : 2;
+    if (!dout || !alpha || !lse || !rinv)
+      return fail(ATTNRES_ERR_INVALID, "dout, alpha, lse and rinv must be non-NULL");
+    if (!aligned_to(dout, es) || !aligned_to(alpha, 4) || !aligned_to(lse, 4) || !aligned_to(rinv, 4))
+      return fail(ATTNRES_ERR_INVALID, "dout, alpha, lse and rinv must be aligned to their element size");
+    if (!d_sources) return fail(ATTNRES_ERR_INVALID, "d_sources array is NULL");
+    for (int n = 0; n < g.n; ++n) {
+      if (!d_sources[n] || !aligned_to(d_sources[n], 4))
+        return fail(ATTNRES_ERR_INVALID, "d_sources[%d] must be non-NULL and 4-byte aligned", n);
+      for (int m = 0; m < n; ++m)
+        if (d_sources[m] == d_sources[n])
+          return fail(ATTNRES_ERR_INVALID, "d_sources[%d] and d_sources[%d] are the same buffer", m, n);
+      gr.d[n] = d_sources[n];
+    }
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int parts = attnres::list_bwd_parts(g);
+  float* dq_part = static_cast<float*>(workspace);
+  hipError_t e = attnres::launch_list_bwd(g, call->dtype, list_args(call), dout, alpha, lse, rinv,
+                                          gr, dq_part, parts, s);
+  if (e != hipSuccess) return hip_fail(e, "list backward kernel");
+  // With no tokens there are no parts and the reduction writes zeros.
+  e = attnres::launch_dq_reduce(dq_part, parts, g.r, dq, nullptr, nullptr, nullptr, s);
+  return e == hipSuccess ? ATTNRES_OK : hip_fail(e, "list dq reduction");
 }
 
 attnres_status_t attnres_row_rinv(attnres_bank_t b, int32_t row, const float** rinv) {

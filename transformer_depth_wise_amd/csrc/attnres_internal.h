@@ -137,6 +137,43 @@ hipError_t launch_delta_null(const DeltaGeom& g, int dtype, const DeltaArgs& a, 
                              const float* alpha0, float* nv_part, const float* ns_part, int parts,
                              float* nv_sum, float* ns_sum, float* dnull, hipStream_t st);
 
+// Source-list read (attnres_list.hip): one self-contained read per call over
+// any shape, with element-wide accesses.
+constexpr int kMaxListSources = 64;
+constexpr size_t kListLdsBudget = 64 * 1024;   // backward LDS per work-group
+constexpr size_t kListPartBytes = 64u << 20;   // cap on the dq partial rows
+struct ListGeom {
+  int64_t T;
+  int32_t d, r, H, kv, kk, n;
+  int32_t k0;  // first key coordinate: d - r
+  int32_t n0;  // first coordinate of the RMS: k0 (slice) or 0 (full)
+  int32_t w;   // coordinates in the RMS: d - n0
+  int64_t qs;  // query stride in elements
+  float eps;
+};
+struct ListArgs {
+  const void* src[kMaxListSources];
+  int64_t stride[kMaxListSources];  // token stride of each source, elements
+  const void* query;
+};
+struct ListGrads {
+  float* d[kMaxListSources];  // float32 [T, d] gradient of each entry
+};
+// LDS floats per wave of the backward: dq [r], weights and dl [n][H] each,
+// inverse RMS and radial sums [n] each, lse [H].
+__host__ __device__ inline int list_bwd_wave_floats(const ListGeom& g) {
+  return g.r + 2 * g.n * g.H + 2 * g.n + g.H;
+}
+size_t list_fwd_lds_bytes(const ListGeom& g);
+int list_bwd_waves_per_group(const ListGeom& g);
+// Waves of the backward grid = dq partial rows [parts][r] (0 when T == 0).
+int list_bwd_parts(const ListGeom& g);
+hipError_t launch_list_fwd(const ListGeom& g, int dtype, const ListArgs& a, void* out,
+                           float* alpha, float* lse, float* rinv, hipStream_t st);
+hipError_t launch_list_bwd(const ListGeom& g, int dtype, const ListArgs& a, const void* dout,
+                           const float* alpha, const float* lse, const float* rinv,
+                           const ListGrads& gr, float* dq_part, int parts, hipStream_t st);
+
 // Bandwidth probes (attnres_probe.hip).
 int probe_blocks();
 hipError_t launch_probe_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t st);

@@ -1,0 +1,280 @@
+// gfx950 kernels of the source-list read ("Low-Rank Attention Residuals",
+// Appendix I, implementation): one self-contained routing read over a list
+// of sources, each given by a pointer and a token stride (a pointer may be
+// listed more than once), keys on the last r coordinates, values on all d,
+// with no alignment requirement on d, r, the strides or the query stride.
+// This is the path for the shapes the 16-byte bank kernels do not take
+// (unaligned widths and ranks, strided or repeated sources, strided
+// queries): every access is one element wide, consecutive lanes on
+// consecutive coordinates, so each wave load still covers a contiguous run.
+//
+// One wave per token, grid-stride over tokens; per-(token, head) reductions
+// are wave sums, so no work-group barrier is needed.
+//   Forward: per source, the per-head dots of the query with the key and the
+//   sum of squares over the norm coordinates; the logits l = rinv * dot; the
+//   softmax over sources per head; the mix of all d coordinates.
+//   Backward, for the loss <dout, out>:
+//     P_{n,h} = <dout_h, s_{n,h}>,  S_h = sum_n a P,  dl = a (P - S),
+//     c_n = sum_h dl_{n,h} l_{n,h}                   (l = log a + lse)
+//     ds_n[j] = a_{n,h(j)} dout[j]
+//             + [j a key coordinate]  rinv_n dl_{n,hk(j)} q[j - (d - r)]
+//             - [j a norm coordinate] rinv_n^2 / w * c_n * s_n[j]
+//     dq[k] = sum_t sum_n rinv_n dl_{n,hk} s_n[d - r + k]
+//   (the radial term is the derivative of the inverse RMS; w is the number
+//   of norm coordinates).  dq is summed per wave in LDS, written as one
+//   partial row per wave, and reduced over rows in a fixed order.
+
+#include <math.h>
+
+#include "attnres_internal.h"
+
+namespace attnres {
+namespace {
+
+typedef uint16_t bf16_t;
+
+constexpr int kLFwdThreads = 256;  // forward: 4 waves per work-group
+
+template <typename T>
+__device__ __forceinline__ float ld1(const T* p);
+template <>
+__device__ __forceinline__ float ld1<float>(const float* p) {
+  return *p;
+}
+template <>
+__device__ __forceinline__ float ld1<bf16_t>(const bf16_t* p) {
+  return __uint_as_float((uint32_t)*p << 16);
+}
+
+__device__ __forceinline__ uint32_t to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);                                  // round to nearest even
+  return u >> 16;
+}
+
+__device__ __forceinline__ void st1(float* p, float v) { *p = v; }
+__device__ __forceinline__ void st1(bf16_t* p, float v) { *p = (bf16_t)to_bf16_bits(v); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// LDS accesses of one wave execute in order; this keeps the compiler from
+// moving them across the point where lanes read what other lanes wrote.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+template <typename T>
+__device__ __forceinline__ const T* row_of(const ListArgs& a, int n, int64_t t) {
+  return static_cast<const T*>(a.src[n]) + t * a.stride[n];
+}
+
+template <typename T>
+__global__ __launch_bounds__(kLFwdThreads) void k_list_fwd(ListGeom g, ListArgs a,
+                                                           T* __restrict__ out,
+                                                           float* __restrict__ alpha,
+                                                           float* __restrict__ lse,
+                                                           float* __restrict__ rinv_out) {
+  extern __shared__ float sm[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nh = g.n * g.H;
+  float* w_a = sm + wave * (nh + g.n);  // [n][H] dots, then weights
+  float* w_r = w_a + nh;                // [n] inverse RMS
+  const T* q = static_cast<const T*>(a.query);
+  const int64_t waves = (int64_t)gridDim.x * (kLFwdThreads / 64);
+  for (int64_t t = (int64_t)blockIdx.x * (kLFwdThreads / 64) + wave; t < g.T; t += waves) {
+    for (int n = 0; n < g.n; ++n) {
+      const T* s = row_of<T>(a, n, t);
+      float ss = 0.f;
+      for (int j = g.n0 + lane; j < g.k0; j += 64) {  // norm coordinates outside the key
+        const float v = ld1(s + j);
+        ss += v * v;
+      }
+      for (int h = 0; h < g.H; ++h) {
+        const T* kh = s + g.k0 + h * g.kk;
+        const T* qh = q + (int64_t)h * g.kk * g.qs;
+        float dot = 0.f;
+        for (int k = lane; k < g.kk; k += 64) {
+          const float v = ld1(kh + k);
+          ss += v * v;
+          dot += v * ld1(qh + (int64_t)k * g.qs);
+        }
+        dot = wave_sum(dot);
+        if (lane == 0) w_a[n * g.H + h] = dot;
+      }
+      ss = wave_sum(ss);
+      if (lane == 0) w_r[n] = 1.f / sqrtf(ss / (float)g.w + g.eps);
+    }
+    wave_lds_fence();
+    for (int h = lane; h < g.H; h += 64) {  // exact softmax over sources, per head
+      float m = -INFINITY;
+      for (int n = 0; n < g.n; ++n) m = fmaxf(m, w_a[n * g.H + h] * w_r[n]);
+      float l = 0.f;
+      for (int n = 0; n < g.n; ++n) l += expf(w_a[n * g.H + h] * w_r[n] - m);
+      const float ls = m + logf(l);
+      for (int n = 0; n < g.n; ++n) {
+        const float al = expf(w_a[n * g.H + h] * w_r[n] - ls);
+        w_a[n * g.H + h] = al;
+        alpha[((int64_t)n * g.T + t) * g.H + h] = al;
+      }
+      lse[t * g.H + h] = ls;
+    }
+    for (int n = lane; n < g.n; n += 64) rinv_out[(int64_t)n * g.T + t] = w_r[n];
+    wave_lds_fence();
+    T* o = out + t * g.d;
+    for (int h = 0; h < g.H; ++h) {
+      for (int k = lane; k < g.kv; k += 64) {
+        const int j = h * g.kv + k;
+        float acc = 0.f;
+        for (int n = 0; n < g.n; ++n) acc += w_a[n * g.H + h] * ld1(row_of<T>(a, n, t) + j);
+        st1(o + j, acc);
+      }
+    }
+    wave_lds_fence();  // the next token rewrites w_a
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_list_bwd(ListGeom g, ListArgs a,
+                                                  const T* __restrict__ dout,
+                                                  const float* __restrict__ alpha,
+                                                  const float* __restrict__ lse,
+                                                  const float* __restrict__ rinv,
+                                                  ListGrads gr, float* __restrict__ dq_part) {
+  extern __shared__ float sm[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int nh = g.n * g.H;
+  float* w_dq = sm + (int64_t)wave * list_bwd_wave_floats(g);  // [r] this wave's dq
+  float* w_a = w_dq + g.r;   // [n][H] weights
+  float* w_p = w_a + nh;     // [n][H] P, then dl
+  float* w_r = w_p + nh;     // [n] inverse RMS
+  float* w_c = w_r + g.n;    // [n] radial sums
+  float* w_l = w_c + g.n;    // [H] lse
+  for (int k = lane; k < g.r; k += 64) w_dq[k] = 0.f;
+  const T* q = static_cast<const T*>(a.query);
+  const int64_t waves = (int64_t)gridDim.x * nw;
+  for (int64_t t = (int64_t)blockIdx.x * nw + wave; t < g.T; t += waves) {
+    for (int i = lane; i < nh; i += 64) {
+      const int n = i / g.H, h = i - n * g.H;
+      w_a[i] = alpha[((int64_t)n * g.T + t) * g.H + h];
+    }
+    for (int n = lane; n < g.n; n += 64) w_r[n] = rinv[(int64_t)n * g.T + t];
+    for (int h = lane; h < g.H; h += 64) w_l[h] = lse[t * g.H + h];
+    const T* go = dout + t * g.d;
+    for (int n = 0; n < g.n; ++n) {
+      const T* s = row_of<T>(a, n, t);
+      for (int h = 0; h < g.H; ++h) {
+        float p = 0.f;
+        for (int k = lane; k < g.kv; k += 64) p += ld1(go + h * g.kv + k) * ld1(s + h * g.kv + k);
+        p = wave_sum(p);
+        if (lane == 0) w_p[n * g.H + h] = p;
+      }
+    }
+    wave_lds_fence();
+    for (int h = lane; h < g.H; h += 64) {
+      float S = 0.f;
+      for (int n = 0; n < g.n; ++n) S += w_a[n * g.H + h] * w_p[n * g.H + h];
+      for (int n = 0; n < g.n; ++n) w_p[n * g.H + h] = w_a[n * g.H + h] * (w_p[n * g.H + h] - S);
+    }
+    wave_lds_fence();
+    for (int n = lane; n < g.n; n += 64) {
+      float c = 0.f;
+      for (int h = 0; h < g.H; ++h) {
+        const float al = w_a[n * g.H + h];
+        if (al > 0.f) c += w_p[n * g.H + h] * (logf(al) + w_l[h]);
+      }
+      w_c[n] = c;
+    }
+    wave_lds_fence();
+    for (int n = 0; n < g.n; ++n) {
+      const T* s = row_of<T>(a, n, t);
+      float* ds = gr.d[n] + t * g.d;
+      const float rv = w_r[n];
+      const float cr = rv * rv / (float)g.w * w_c[n];
+      for (int h = 0; h < g.H; ++h) {
+        const float al = w_a[n * g.H + h];
+        for (int k = lane; k < g.kv; k += 64) {
+          const int j = h * g.kv + k;
+          float v = al * ld1(go + j);
+          if (j >= g.n0) {
+            const float x = ld1(s + j);
+            v -= cr * x;
+            if (j >= g.k0) {
+              const int jk = j - g.k0;
+              const float b = rv * w_p[n * g.H + jk / g.kk];
+              v += b * ld1(q + (int64_t)jk * g.qs);
+              w_dq[jk] += b * x;  // coordinate jk always belongs to this lane
+            }
+          }
+          ds[j] = v;
+        }
+      }
+    }
+    wave_lds_fence();  // the next token rewrites the per-token state
+  }
+  float* dst = dq_part + ((int64_t)blockIdx.x * nw + wave) * g.r;
+  for (int k = lane; k < g.r; k += 64) dst[k] = w_dq[k];
+}
+
+}  // namespace
+
+size_t list_fwd_lds_bytes(const ListGeom& g) {
+  return sizeof(float) * (kLFwdThreads / 64) * ((size_t)g.n * g.H + g.n);
+}
+
+int list_bwd_waves_per_group(const ListGeom& g) {
+  const size_t per = sizeof(float) * (size_t)list_bwd_wave_floats(g);
+  int nw = (int)(kListLdsBudget / per);
+  return nw > 4 ? 4 : nw;
+}
+
+int list_bwd_parts(const ListGeom& g) {
+  const int nw = list_bwd_waves_per_group(g);
+  if (g.T == 0 || nw < 1) return 0;
+  // enough waves to cover the chip several times, with the partial rows
+  // within kListPartBytes
+  int64_t waves = (int64_t)(kListPartBytes / (sizeof(float) * (size_t)g.r));
+  if (waves > 4096) waves = 4096;
+  if (waves < 256) waves = 256;
+  if (waves > g.T) waves = g.T;
+  return (int)((waves + nw - 1) / nw) * nw;
+}
+
+hipError_t launch_list_fwd(const ListGeom& g, int dtype, const ListArgs& a, void* out,
+                           float* alpha, float* lse, float* rinv, hipStream_t st) {
+  if (g.T == 0) return hipSuccess;
+  const int64_t groups = (g.T + kLFwdThreads / 64 - 1) / (kLFwdThreads / 64);
+  const dim3 grid((unsigned)(groups < 4096 ? groups : 4096));
+  const size_t lds = list_fwd_lds_bytes(g);
+  if (dtype == 0)
+    hipLaunchKernelGGL((k_list_fwd<float>), grid, dim3(kLFwdThreads), lds, st, g, a,
+                       static_cast<float*>(out), alpha, lse, rinv);
+  else
+    hipLaunchKernelGGL((k_list_fwd<bf16_t>), grid, dim3(kLFwdThreads), lds, st, g, a,
+                       static_cast<bf16_t*>(out), alpha, lse, rinv);
+  return hipGetLastError();
+}
+
+hipError_t launch_list_bwd(const ListGeom& g, int dtype, const ListArgs& a, const void* dout,
+                           const float* alpha, const float* lse, const float* rinv,
+                           const ListGrads& gr, float* dq_part, int parts, hipStream_t st) {
+  if (g.T == 0 || parts == 0) return hipSuccess;
+  const int nw = list_bwd_waves_per_group(g);
+  if (nw < 1 || parts % nw) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)(parts / nw));
+  const size_t lds = sizeof(float) * (size_t)nw * list_bwd_wave_floats(g);
+  if (dtype == 0)
+    hipLaunchKernelGGL((k_list_bwd<float>), grid, dim3(64 * nw), lds, st, g, a,
+                       static_cast<const float*>(dout), alpha, lse, rinv, gr, dq_part);
+  else
+    hipLaunchKernelGGL((k_list_bwd<bf16_t>), grid, dim3(64 * nw), lds, st, g, a,
+                       static_cast<const bf16_t*>(dout), alpha, lse, rinv, gr, dq_part);
+  return hipGetLastError();
+}
+
+}  // namespace attnres
