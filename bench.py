@@ -389,6 +389,122 @@ def bench_delta(args):
     print(json.dumps(result), flush=True)
 
 
+def list_bytes(shape):
+    """Algorithmic bytes of one list read: (fwd, bwd).  Every distinct source
+    tensor is read once (a broadcast tensor is one row), whatever the number
+    of entries naming it; float32 gradients are written per entry."""
+    T, d, r, H, n = shape.tokens, shape.d, shape.r, shape.heads, shape.n
+    b = 2 if shape.dtype == "bf16" else 4
+    src = sum((1 if shape.broadcast(k) else T) * d * b for k in range(shape.tensors))
+    stats = 4 * n * T * H + 4 * T * H + 4 * n * T  # alpha, lse, inverse RMS
+    fwd = src + r * b + T * d * b + stats
+    bwd = src + r * b + T * d * b + stats + 4 * n * T * d + 4 * r
+    return fwd, bwd
+
+
+def list_cpu_baseline(shape, tokens: int):
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import route_backward, route_forward
+    from synth import ListInputs
+
+    s = shape.with_tokens(tokens)
+    inp = ListInputs(s)
+    src = inp.entry_values().astype(np.float64)
+    q = inp.value("query").astype(np.float64)
+    dout = inp.value("dout").astype(np.float64)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        route_forward(src, q, s.heads, s.r, s.eps, norm=s.norm)
+        route_backward(src, q, s.heads, s.r, dout, s.eps, norm=s.norm)
+        dt = time.perf_counter() - t0
+    return {
+        "value": round(dt * 1e3 * shape.tokens / tokens, 1),
+        "unit": "ms/read",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{tokens} of {shape.tokens} tokens, one read fwd+bwd, NumPy fp64 oracle on "
+                   f"one thread ({cpu_model()}); measured {dt:.2f} s, scaled linearly in tokens"),
+    }
+
+
+def bench_list(args):
+    import torch
+
+    from synth import LIST_SHAPES, ListInputs
+    from synth.device import to_device
+    from transformer_depth_wise_amd.attnres import ListRead
+
+    shape = LIST_SHAPES[args.workload]
+    torch.cuda.set_device(0)
+    inp = ListInputs(shape)
+    T = shape.tokens
+    bufs = [to_device(inp.stored_tensor(k), shape.dtype) for k in range(shape.tensors)]
+    views = []
+    for k, buf in enumerate(bufs):
+        v = buf[:, shape.offset(k):shape.offset(k) + shape.d]
+        views.append(v.expand(T, shape.d) if shape.broadcast(k) else v)
+    qbuf = to_device(inp.stored_query(), shape.dtype)
+    q = torch.as_strided(qbuf, (shape.r,), (shape.qstride,))
+    dout = to_device(inp.value("dout"), shape.dtype)
+    rd = ListRead([views[k] for k in shape.entries], q, shape.heads, eps=shape.eps,
+                  norm=shape.norm, tokens=T)
+    torch.cuda.synchronize()
+    print(f"[bench] {shape.describe()}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        out, alpha, lse, rinv = rd.forward()
+        rd.backward(dout, alpha, lse, rinv)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    t_f = t_b = 0.0
+    for _ in range(args.steps):
+        ev[0].record()
+        out, alpha, lse, rinv = rd.forward()
+        ev[1].record()
+        rd.backward(dout, alpha, lse, rinv)
+        ev[2].record()
+        torch.cuda.synchronize()
+        t_f += ev[0].elapsed_time(ev[1])
+        t_b += ev[1].elapsed_time(ev[2])
+    ms_f, ms_b = t_f / args.steps, t_b / args.steps
+    ms = ms_f + ms_b
+    by_f, by_b = list_bytes(shape)
+    print(f"[bench] {args.steps} steps: {ms:.3f} ms/read (fwd {ms_f:.3f}, bwd {ms_b:.3f})",
+          file=sys.stderr, flush=True)
+    kern = {"list_fwd": {"ms_per_read": round(ms_f, 3), "gbps": round(by_f / ms_f / 1e6, 1)},
+            "list_bwd": {"ms_per_read": round(ms_b, 3), "gbps": round(by_b / ms_b / 1e6, 1),
+                         "includes": "the fixed-order dq reduction"}}
+    dom = max(kern, key=lambda k: kern[k]["ms_per_read"])
+    a = kern[dom]["gbps"]
+    result = {
+        "metric": METRIC, "value": round(ms, 3), "unit": "ms/read", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic: seeded N(0,1) x U(0.5,2) source tensors, N(0,qscale^2) query, "
+                f"N(0,1) upstream gradient, {shape.dtype} storage",
+        "config": {"workload": shape.name, "tokens": T, "d": shape.d, "r": shape.r,
+                   "heads": shape.heads, "entries": shape.n, "tensors": shape.tensors,
+                   "strides": [shape.stride(k) for k in range(shape.tensors)],
+                   "query_stride": shape.qstride, "storage": shape.dtype, "norm": shape.norm},
+        "achieved_gbps": round((by_f + by_b) / ms / 1e6, 1),
+        "pct_of_peak": round(100.0 * (by_f + by_b) / ms / 1e6 / HBM_PEAK_GBPS, 1),
+        "alg_bytes_per_read": by_f + by_b,
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(a / HBM_PEAK_GBPS, 3), "traffic": None,
+                     "alg_bytes_per_launch": by_f if dom == "list_fwd" else by_b},
+        "kernels": kern,
+    }
+    if not args.no_cpu_baseline:
+        # size the sample to about 10 s of oracle time from a 64-token run
+        probe = list_cpu_baseline(shape, 64)
+        per_token_s = probe["value"] / 1e3 / shape.tokens
+        tokens = int(min(shape.tokens, max(64, 10.0 / max(per_token_s, 1e-9))))
+        result["cpu_baseline"] = probe if tokens == 64 else list_cpu_baseline(shape, tokens)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -421,9 +537,12 @@ def main():
               "run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    from synth import DELTA_SHAPES
+    from synth import DELTA_SHAPES, LIST_SHAPES
     if args.workload in DELTA_SHAPES:
         bench_delta(args)
+        return
+    if args.workload in LIST_SHAPES:
+        bench_list(args)
         return
 
     import torch
