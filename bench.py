@@ -505,6 +505,103 @@ def bench_list(args):
     print(json.dumps(result), flush=True)
 
 
+# Block routing with the partial sums kept by the bank (Figure 11 loop with the
+# sublayer outputs given): 16 distinct seeded sublayer outputs and upstream
+# gradients are cycled over the sublayers (every read still streams its own
+# rows; only the draws are shared).
+BLOCK_DRAWS = 16
+
+
+def block_accumulate_bytes(shape):
+    """Algorithmic bytes of the block sums: the first output of a block is
+    copied into its partial (read + write), later ones add (2 reads + write)."""
+    nsrc, has_partial = shape.schedule()
+    row = shape.tokens * shape.d * (2 if shape.dtype == "bf16" else 4)
+    total, first = 0, True
+    for t in range(shape.sublayers):
+        total += (2 if first else 3) * row
+        first = not has_partial[t]  # a commit ends the block
+    return total, shape.sublayers
+
+
+def blocks_cpu_baseline(shape, tokens: int):
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import run_block_routing
+    from synth import BlockInputs
+    from synth.blocks import BlockShape
+
+    s = BlockShape(shape.name, tokens, shape.d, shape.r, shape.heads, shape.sublayers,
+                   shape.blocks, shape.dtype, shape.norm, shape.qscale, shape.eps, shape.seed)
+    inp = BlockInputs(s)
+    M = s.sublayers
+    ys = np.stack([inp.y(t % BLOCK_DRAWS) for t in range(M)])
+    q = np.stack([inp.query(t) for t in range(M)])
+    douts = np.stack([inp.dout(t % BLOCK_DRAWS) for t in range(M)])
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        run_block_routing(inp.x(), ys, q, douts, s.ends(), s.heads, s.r, s.eps, norm=s.norm)
+        dt = time.perf_counter() - t0
+    return {
+        "value": round(dt * 1e3 * shape.tokens / tokens, 1),
+        "unit": "ms/microbatch",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{tokens} of {shape.tokens} tokens, all {M} reads fwd+bwd with exact block "
+                   f"sums, NumPy fp64 oracle on one thread ({cpu_model()}); measured {dt:.2f} s, "
+                   f"scaled linearly in tokens"),
+    }
+
+
+def bench_blocks(args):
+    import torch
+
+    from synth import BLOCK_SHAPES, BlockInputs, Workload
+    from synth.device import to_device
+    from transformer_depth_wise_amd.attnres import Bank
+    from transformer_depth_wise_amd.schedule import run_block_microbatch
+
+    shape = BLOCK_SHAPES[args.workload]
+    torch.cuda.set_device(0)
+    inp = BlockInputs(shape)
+    T, d, M = shape.tokens, shape.d, shape.sublayers
+    nsrc, has_partial = shape.schedule()
+    bank = Bank(T, d, shape.r, shape.heads, shape.blocks + 1, M, shape.dtype, shape.eps,
+                norm=shape.norm)
+    tdt = bank.rows.dtype
+    x = to_device(inp.x(), shape.dtype)
+    ys = [to_device(inp.y(t), shape.dtype) for t in range(min(BLOCK_DRAWS, M))]
+    for t in range(min(BLOCK_DRAWS, M)):
+        to_device(inp.dout(t), shape.dtype, out=bank.dout_rows[t])
+    for t in range(BLOCK_DRAWS, M):
+        bank.dout_rows[t].copy_(bank.dout_rows[t % BLOCK_DRAWS])
+    queries = torch.stack([to_device(inp.query(t), shape.dtype) for t in range(M)])
+    outs = torch.empty((M, T, d), dtype=tdt, device="cuda")
+    partials = [torch.empty((T, d), dtype=tdt, device="cuda") if p else None
+                for p in has_partial]
+    douts = [bank.dout_rows[t] for t in range(M)]
+    dqs = torch.empty((M, shape.r), dtype=torch.float32, device="cuda")
+    y_of = [ys[t % BLOCK_DRAWS] for t in range(M)]
+    torch.cuda.synchronize()
+    print(f"[bench] {shape.describe()}", file=sys.stderr, flush=True)
+
+    def step():
+        run_block_microbatch(bank, list(nsrc), has_partial, queries, x, y_of, outs, partials,
+                             douts, dqs)
+
+    w = Workload(shape.name, T, d, shape.heads, shape.r, nsrc, has_partial, shape.dtype, False,
+                 norm=shape.norm)
+    alg, launches = kernel_bytes(w, bank.tiling()["dq_parts"])
+    alg["accumulate"], launches["accumulate"] = block_accumulate_bytes(shape)
+    # the embedding is appended once per microbatch like any committed row
+    report(args, w, bank, step, alg, {
+        "workload": shape.name, "tokens": T, "d": d, "r": shape.r, "heads": shape.heads,
+        "sublayers": M, "blocks": shape.blocks, "storage": shape.dtype, "norm": shape.norm,
+        "block_sums": "kept by the bank (attnres_bank_accumulate)",
+    }, cpu=lambda: blocks_cpu_baseline(shape, min(args.cpu_tokens, 16)))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -537,7 +634,10 @@ def main():
               "run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    from synth import DELTA_SHAPES, LIST_SHAPES
+    from synth import BLOCK_SHAPES, DELTA_SHAPES, LIST_SHAPES
+    if args.workload in BLOCK_SHAPES:
+        bench_blocks(args)
+        return
     if args.workload in DELTA_SHAPES:
         bench_delta(args)
         return
@@ -587,6 +687,21 @@ def main():
         run_microbatch(bank, list(w.nsrc), list(w.extra), queries, outs, dqs, extras, d_extras,
                        gains=gains, dgains=dgains)
 
+    parts = bank.tiling()["dq_parts"]
+    alg, launches = kernel_bytes(w, parts)
+    report(args, w, bank, step, alg, {
+        "workload": w.name,
+        "tokens": w.tokens, "d": w.d, "r": w.r, "heads": w.heads, "sites": w.sites,
+        "sources_read": w.reads, "storage": w.dtype,
+    })
+
+
+def report(args, w, bank, step, alg, config, cpu=None):
+    """Time `step` (one microbatch), then trace it per kernel kind, and print
+    the JSON line.  `cpu` returns the CPU baseline (default: the oracle on
+    a token sample of workload w)."""
+    import torch
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -601,8 +716,6 @@ def main():
     print(f"[bench] {args.steps} steps: {ms:.3f} ms/microbatch", file=sys.stderr, flush=True)
 
     result_probe = bandwidth_probe(torch)
-    parts = bank.tiling()["dq_parts"]
-    alg, launches = kernel_bytes(w, parts)
     total_bytes = sum(alg.values())
     result = {
         "metric": METRIC,
@@ -618,11 +731,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic: seeded N(0,1) bank rows x U(0.5,2) per-row scale, N(0,0.02^2) "
                 "queries, N(0,1) upstream gradients, bf16 storage",
-        "config": {
-            "workload": w.name,
-            "tokens": w.tokens, "d": w.d, "r": w.r, "heads": w.heads, "sites": w.sites,
-            "sources_read": w.reads, "storage": w.dtype,
-        },
+        "config": config,
         "achieved_gbps": round(total_bytes / ms / 1e6, 1),
         "pct_of_peak": round(100.0 * total_bytes / ms / 1e6 / HBM_PEAK_GBPS, 1),
         "alg_bytes_per_microbatch": total_bytes,
@@ -659,7 +768,8 @@ def main():
         print(f"[bench] per-kernel: {json.dumps(kern)}", file=sys.stderr, flush=True)
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_tokens, w.tokens)
+        result["cpu_baseline"] = (cpu() if cpu is not None
+                                  else cpu_baseline(args.workload, args.cpu_tokens, w.tokens))
     print(json.dumps(result), flush=True)
 
 

@@ -148,8 +148,11 @@ attnres_status_t attnres_bank_reset(attnres_bank_t bank);
  *   n_sites          1..max_sites
  *   nsrc[n_sites]    host array: committed rows read by each site;
  *                    1 <= nsrc[s] <= max_rows and non-decreasing in s
- *   has_extra        host array [n_sites] of 0/1 (site reads one transient
- *                    source), or NULL for none
+ *   has_extra        host array [n_sites]: 0 (no transient source), 1 (the
+ *                    site reads one transient source; its gradient is stored
+ *                    into d_extra) or 2 (the transient source is a block
+ *                    partial sum; its gradient is added to d_extra, see
+ *                    attnres_bank_accumulate), or NULL for all 0
  *   queries          device [n_sites, r] storage dtype; must stay unchanged
  *                    until the backward of site 0 has run
  * Each later append scores its row against every registered query that will
@@ -186,6 +189,32 @@ attnres_status_t attnres_bank_set_gains(attnres_bank_t bank, const float* gains,
 attnres_status_t attnres_bank_append(attnres_bank_t bank, const void* src, attnres_stream_t stream,
                                      int32_t* row_out);
 
+/* Block-sum maintenance ("Low-Rank Attention Residuals", section 3, partial-
+ * block routing, and Appendix H, Figure 11): each sublayer output y adds to
+ * the running partial sum of its block; at a block end the sum becomes the
+ * next committed bank row.  The sum is formed in float32 and rounded once to
+ * the storage dtype.
+ *   y            device [T, d] storage dtype sublayer output
+ *   commit == 0  partial_out (device [T, d], caller memory) receives the new
+ *                partial sum: y alone after a commit or reset, else the
+ *                previous partial_out + y.  It may be the previous partial
+ *                (in place) or y.  The bank keeps the pointer (the caller
+ *                keeps the memory) to add the next y; a site reading the
+ *                partial passes it as `extra` to attnres_route_fwd, and it
+ *                must stay unchanged until that site's backward.
+ *   commit != 0  partial_out must be NULL; the sum is written into the next
+ *                bank row, which is committed as by attnres_bank_append
+ *                (*row_out receives its index, else -1).
+ * Backward: mark every site that reads a partial with has_extra = 2 and pass
+ * the block's row gradient (drows slot of the row the block commits into) as
+ * its d_extra.  That slot is final after the backward of the first site that
+ * reads the committed row; each partial read then adds its gradient to it, so
+ * after the backward of the site right after sublayer t it holds the gradient
+ * of that sublayer's y. */
+attnres_status_t attnres_bank_accumulate(attnres_bank_t bank, const void* y, void* partial_out,
+                                         int32_t commit, attnres_stream_t stream,
+                                         int32_t* row_out);
+
 /* Forward of site `site` (sites in increasing order, all rows it reads
  * committed).  extra: device [T, d] transient source when has_extra[site],
  * else NULL; it must stay unchanged until the backward of this site.  Writes
@@ -204,7 +233,8 @@ attnres_status_t attnres_route_fwd(attnres_bank_t bank, int32_t site, const void
  *            they must be unchanged since their own backward.
  *   dq       device float32 [r]: gradient of this site's query (overwritten)
  *   d_extra  device float32 [T, d]: gradient of the transient source
- *            (overwritten) when the site has one, else NULL
+ *            when the site has one (overwritten; added to its contents
+ *            when has_extra[site] == 2), else NULL
  * Bank-row gradients are accumulated over all sites and written once per row
  * into drows (see the call order above). */
 attnres_status_t attnres_route_bwd(attnres_bank_t bank, int32_t site, const void* extra,
@@ -359,7 +389,8 @@ typedef enum {
   ATTNRES_KERNEL_BWD_SITE = 2,  /* backward site pass */
   ATTNRES_KERNEL_DQ_REDUCE = 3, /* query-gradient reduction */
   ATTNRES_KERNEL_FINALIZE = 4,  /* bank-row and transient-source gradients */
-  ATTNRES_KERNEL_KINDS = 5
+  ATTNRES_KERNEL_ACCUMULATE = 5, /* block partial sums (attnres_bank_accumulate) */
+  ATTNRES_KERNEL_KINDS = 6
 } attnres_kernel_t;
 
 /* Launch trace.  While enabled, every kernel the bank enqueues is bracketed by

@@ -4,12 +4,14 @@ tests, the smoke check and the benchmark's CPU-baseline leg."""
 
 from .attnres_oracle import (  # noqa: F401
     EPS,
+    block_reads,
     delta_backward,
     delta_forward,
     inv_rms,
     key_slice,
     route_backward,
     route_forward,
+    run_block_routing,
     run_schedule,
     source_inv_rms,
 )

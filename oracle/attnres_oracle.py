@@ -61,6 +61,18 @@ Readings where the pages are open (each also listed in the design doc):
       null source's gradient is the sum over tokens of its per-token
       gradient, and the residual stream's gradient is dout itself.  An output
       gate on the routed term belongs to the caller.
+  R9  Block routing ("Low-Rank Attention Residuals", section 3, partial-
+      block routing, and Appendix H, Figure 11): sublayer outputs y_t add
+      up into the running partial sum of their block; a block ends after
+      sublayer ceil(M j / N) and its sum becomes a completed source; the
+      read after sublayer t sees the embedding, the completed block sums
+      and, unless t ends a block, the partial sum.  Every source is a sum of
+      its members, so the gradient of a member is the sum of the gradients
+      of the sources containing it.  A model keeps each partial sum as a
+      tensor of its storage dtype, so each sum is rounded once as it is
+      formed, b_t = round(b_{t-1} + y_t); `store` is that rounding (given by
+      the caller; identity, i.e. exact sums, by default).  The gradient
+      passes through the rounding unchanged.
   R5  LR with H > 1: q in R^r is split into H slices of width r/H; head h
       scores the h-th slice of the normalised r-wide key and mixes the h-th
       d/H slice of the value.  Requires H | r.  r = d gives MHAR.
@@ -222,6 +234,66 @@ def run_schedule(rows, extras, queries, douts, nsrc, heads: int, r: int, eps: fl
         "dextra": dextra,
         **({} if gains is None else {"dgain": dgain}),
     }
+
+
+def block_reads(M: int, ends):
+    """Members of every source of each read of block routing (R9): a list over
+    reads t = 1..M of source member tuples, -1 the embedding, i the output of
+    sublayer i + 1; completed blocks first (embedding first), partial last."""
+    blocks, partial, reads = [(-1,)], None, []
+    for t in range(1, M + 1):
+        partial = (t - 1,) if partial is None else partial + (t - 1,)
+        if t in ends:
+            blocks.append(partial)
+            partial = None
+        reads.append(list(blocks) + ([] if partial is None else [partial]))
+    return reads
+
+
+def run_block_routing(x, ys, queries, douts, ends, heads: int, r: int, eps: float = EPS,
+                      norm: str = "slice", store=None):
+    """Block routing over given sublayer outputs (R9).
+
+    x:       [T, d]     the embedding, the first source of every read
+    ys:      [M, T, d]  sublayer outputs y_1..y_M
+    queries: [M, r]     query of the read after each sublayer
+    douts:   [M, T, d]  upstream gradient of each read's output
+    ends:    sublayer numbers (1-based) that end a block
+    store:   None, or the rounding of a freshly formed partial sum to the
+             storage dtype (R9)
+    The loss is sum_t <dout_t, out_t>.  Returns a dict: out [M, T, d],
+    dx [T, d], dy [M, T, d], dq [M, r].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    ys = np.asarray(ys, dtype=np.float64)
+    M = ys.shape[0]
+    reads = block_reads(M, set(ends))
+
+    def value(members):
+        if members[0] < 0:
+            return x
+        acc = ys[members[0]]
+        for i in members[1:]:
+            acc = acc + ys[i]
+            if store is not None:
+                acc = np.asarray(store(acc), dtype=np.float64)
+        return acc
+
+    out = np.zeros((M,) + x.shape)
+    dx = np.zeros_like(x)
+    dy = np.zeros_like(ys)
+    dq = np.zeros((M, r))
+    for t, members in enumerate(reads):
+        src = np.stack([value(m) for m in members])
+        out[t] = route_forward(src, queries[t], heads, r, eps, norm=norm)[0]
+        dsrc, dq[t] = route_backward(src, queries[t], heads, r, douts[t], eps, norm=norm)
+        for k, m in enumerate(members):
+            for i in m:
+                if i < 0:
+                    dx += dsrc[k]
+                else:
+                    dy[i] += dsrc[k]
+    return {"out": out, "dx": dx, "dy": dy, "dq": dq}
 
 
 def _site_sources(rows, extra, n):

@@ -18,3 +18,4 @@ from .workloads import (  # noqa: F401
 from .draws import Inputs, bf16_bits, bf16_round, sample_tokens  # noqa: F401
 from .delta import DELTA_SHAPES, DeltaInputs, DeltaShape  # noqa: F401
 from .lists import LIST_SHAPES, ListInputs, ListShape  # noqa: F401
+from .blocks import BLOCK_SHAPES, BlockInputs, BlockShape  # noqa: F401

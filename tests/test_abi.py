@@ -256,3 +256,29 @@ def test_list_workspace_and_argument_checks(lib):
     with pytest.raises(A.AttnResError) as e:  # rinv missing
         A.attnres_list_fwd(c, FAKE, FAKE, FAKE, None, stream=0)
     assert e.value.status == A.ATTNRES_ERR_INVALID
+
+
+def test_accumulate_order_and_arguments(lib):
+    b = fake_bank(cfg())
+    try:
+        with pytest.raises(A.AttnResError) as e:  # before set_queries
+            A.attnres_bank_accumulate(b, FAKE, FAKE, stream=0)
+        assert e.value.status == A.ATTNRES_ERR_ORDER
+        with pytest.raises(A.AttnResError) as e:  # has_extra is 0, 1 or 2
+            A.attnres_bank_set_queries(b, [1, 1], [3, 0], FAKE)
+        assert e.value.status == A.ATTNRES_ERR_INVALID
+        A.attnres_bank_set_queries(b, [1, 1, 2], [2, 2, 0], FAKE)
+        with pytest.raises(A.AttnResError) as e:  # a commit writes into the bank row
+            A.attnres_bank_accumulate(b, FAKE, FAKE, commit=True, stream=0)
+        assert e.value.status == A.ATTNRES_ERR_INVALID
+        with pytest.raises(A.AttnResError) as e:  # a partial sum needs somewhere to go
+            A.attnres_bank_accumulate(b, FAKE, None, stream=0)
+        assert e.value.status == A.ATTNRES_ERR_INVALID
+        with pytest.raises(A.AttnResError) as e:
+            A.attnres_bank_accumulate(b, FAKE + 4, FAKE, stream=0)
+        assert e.value.status == A.ATTNRES_ERR_INVALID
+        with pytest.raises(A.AttnResError) as e:  # saved state counts the partial once
+            A.attnres_site_saved(b, 0)
+        assert e.value.status == A.ATTNRES_ERR_ORDER
+    finally:
+        A.attnres_bank_destroy(b)

@@ -630,3 +630,87 @@ def test_list_read_repeated_source_is_a_log2_logit_shift():
         for j in range(d):
             ref = (ea * float(a[t, j]) + eb * float(b[t, j])) / (ea + eb)
             assert out[t, j] == pytest.approx(ref, rel=1e-12, abs=1e-12)
+
+
+# Block routing ("Low-Rank Attention Residuals", section 3, partial-block
+# routing; Appendix H, Figure 11): the reads see sums of sublayer outputs.
+def _block_ends(M, N):
+    return {-(-M * j // N) for j in range(1, N + 1)}
+
+
+def test_block_reads_membership():
+    # M = 5 sublayers in N = 2 blocks end after sublayers 3 and 5
+    from oracle import block_reads
+    reads = block_reads(5, _block_ends(5, 2))
+    assert reads == [[(-1,), (0,)], [(-1,), (0, 1)], [(-1,), (0, 1, 2)],
+                     [(-1,), (0, 1, 2), (3,)], [(-1,), (0, 1, 2), (3, 4)]]
+
+
+@pytest.mark.parametrize("M,N,norm", [(5, 2, "slice"), (4, 4, "slice"), (6, 3, "full")])
+def test_block_routing_gradients_match_finite_differences(M, N, norm):
+    from oracle import run_block_routing
+    rng = np.random.default_rng(37)
+    T, d, r, H = 2, 8, 4, 2
+    x = rng.standard_normal((T, d))
+    ys = rng.standard_normal((M, T, d)) * rng.uniform(0.5, 2.0, (M, 1, 1))
+    queries = rng.standard_normal((M, r))
+    douts = rng.standard_normal((M, T, d))
+    ends = _block_ends(M, N)
+    res = run_block_routing(x, ys, queries, douts, ends, H, r, norm=norm)
+
+    def loss():
+        o = run_block_routing(x, ys, queries, douts, ends, H, r, norm=norm)["out"]
+        return float((o * douts).sum())
+
+    h = 1e-6
+    for arr, key in ((x, "dx"), (ys, "dy"), (queries, "dq")):
+        g = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + h
+            lp = loss()
+            arr[idx] = old - h
+            lm = loss()
+            arr[idx] = old
+            g[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(res[key], g, rtol=1e-6, atol=1e-8)
+
+
+def test_block_routing_with_one_sublayer_per_block_is_full_routing():
+    # N = M keeps every sublayer output as its own source (Figure 11, N=None):
+    # the reads are the full-routing schedule over rows [x, y_1, ..., y_M].
+    from oracle import run_block_routing
+    rng = np.random.default_rng(41)
+    M, T, d, r, H = 4, 3, 8, 8, 2
+    x = rng.standard_normal((T, d))
+    ys = rng.standard_normal((M, T, d))
+    queries = rng.standard_normal((M, r))
+    douts = rng.standard_normal((M, T, d))
+    res = run_block_routing(x, ys, queries, douts, _block_ends(M, M), H, r)
+    rows = np.concatenate([x[None], ys])
+    ref = run_schedule(rows, [None] * M, queries, douts, list(range(2, M + 2)), H, r)
+    np.testing.assert_allclose(res["out"], ref["out"], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(res["dx"], ref["dbank"][0], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(res["dy"], ref["dbank"][1:], rtol=1e-12, atol=1e-13)
+
+
+def test_block_routing_store_rounds_each_partial_once():
+    # with a rounding `store`, the second read of a block sees round(y1 + y2)
+    # and the third round(round(y1 + y2) + y3); an identity store gives the
+    # exact sums.  Checked on the outputs of a one-head read whose query is
+    # zero (uniform weights): out = mean of the sources.
+    from oracle import run_block_routing
+    rng = np.random.default_rng(43)
+    M, T, d = 3, 2, 4
+    x = rng.standard_normal((T, d))
+    ys = rng.standard_normal((M, T, d))
+    q = np.zeros((M, d))
+    douts = np.zeros((M, T, d))
+    store = lambda v: np.round(v * 8.0) / 8.0  # noqa: E731  (a coarse grid)
+    res = run_block_routing(x, ys, q, douts, {3}, 1, d, store=store)
+    b2 = store(ys[0] + ys[1])
+    np.testing.assert_allclose(res["out"][1], (x + b2) / 2, rtol=1e-15, atol=1e-15)
+    b3 = store(b2 + ys[2])
+    np.testing.assert_allclose(res["out"][2], (x + b3) / 2, rtol=1e-15, atol=1e-15)
+    exact = run_block_routing(x, ys, q, douts, {3}, 1, d)
+    np.testing.assert_allclose(exact["out"][2], (x + ys.sum(0)) / 2, rtol=1e-14, atol=1e-14)

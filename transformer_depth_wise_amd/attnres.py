@@ -38,6 +38,7 @@ EXPORTS = (
     "attnres_bank_set_queries",
     "attnres_bank_set_gains",
     "attnres_bank_append",
+    "attnres_bank_accumulate",
     "attnres_route_fwd",
     "attnres_route_bwd",
     "attnres_site_saved",
@@ -131,6 +132,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "attnres_bank_set_queries": (i32, [vp, i32, POINTER(i32), POINTER(i32), vp]),
         "attnres_bank_set_gains": (i32, [vp, vp, vp, vp]),
         "attnres_bank_append": (i32, [vp, vp, vp, POINTER(i32)]),
+        "attnres_bank_accumulate": (i32, [vp, vp, vp, i32, vp, POINTER(i32)]),
         "attnres_route_fwd": (i32, [vp, i32, vp, vp, vp]),
         "attnres_route_bwd": (i32, [vp, i32, vp, vp, vp, vp, vp]),
         "attnres_site_saved": (i32, [vp, i32, POINTER(vp), POINTER(vp), POINTER(i32)]),
@@ -233,6 +235,14 @@ def attnres_bank_append(bank, src=None, stream=None) -> int:
     return row.value
 
 
+def attnres_bank_accumulate(bank, y, partial_out=None, commit=False, stream=None) -> int:
+    row = c_int32(-1)
+    _check(load_library().attnres_bank_accumulate(bank, _ptr(y), _ptr(partial_out),
+                                                  1 if commit else 0, _stream(stream),
+                                                  ctypes.byref(row)))
+    return row.value
+
+
 def attnres_route_fwd(bank, site: int, extra, out, stream=None) -> None:
     _check(load_library().attnres_route_fwd(bank, int(site), _ptr(extra), _ptr(out), _stream(stream)))
 
@@ -263,7 +273,7 @@ def attnres_bank_tiling(bank):
     return dict(zip(keys, [int(v) for v in out]))
 
 
-KERNEL_KINDS = ("score", "fwd", "bwd_site", "dq_reduce", "finalize")
+KERNEL_KINDS = ("score", "fwd", "bwd_site", "dq_reduce", "finalize", "accumulate")
 
 
 def attnres_trace_enable(bank, enable: bool) -> None:
@@ -350,6 +360,9 @@ class Bank:
 
     def append(self, src=None, stream=None) -> int:
         return attnres_bank_append(self.handle, src, stream)
+
+    def accumulate(self, y, partial_out=None, commit=False, stream=None) -> int:
+        return attnres_bank_accumulate(self.handle, y, partial_out, commit, stream)
 
     def route_fwd(self, site, extra, out, stream=None):
         attnres_route_fwd(self.handle, site, extra, out, stream)

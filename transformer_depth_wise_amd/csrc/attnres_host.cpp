@@ -188,6 +188,7 @@ struct attnres_bank_s {
   int bwd_next;  // next site to run backward; -1 before the backward phase
   bool bwd_done;  // backward of site 0 has run: only reset is allowed
   std::vector<const void*> extra_ptr;
+  const void* partial;  // running block partial sum (caller memory), NULL between blocks
   // launch trace
   struct TraceRec {
     int kind;
@@ -230,6 +231,7 @@ struct attnres_bank_s {
     bwd_next = -1;
     bwd_done = false;
     extra_ptr.clear();
+    partial = nullptr;
   }
 };
 
@@ -383,8 +385,8 @@ attnres_status_t attnres_bank_set_queries(attnres_bank_t b, int32_t n_sites, con
     if (s > 0 && nsrc[s] < nsrc[s - 1])
       return fail(ATTNRES_ERR_INVALID, "nsrc must be non-decreasing (nsrc[%d]=%d < nsrc[%d]=%d)", s,
                   nsrc[s], s - 1, nsrc[s - 1]);
-    if (has_extra && has_extra[s] != 0 && has_extra[s] != 1)
-      return fail(ATTNRES_ERR_INVALID, "has_extra[%d] must be 0 or 1", s);
+    if (has_extra && (has_extra[s] < 0 || has_extra[s] > 2))
+      return fail(ATTNRES_ERR_INVALID, "has_extra[%d] must be 0, 1 or 2", s);
   }
   b->n_sites = n_sites;
   b->nsrc.assign(nsrc, nsrc + n_sites);
@@ -451,6 +453,45 @@ attnres_status_t attnres_bank_append(attnres_bank_t b, const void* src, attnres_
   if (e != hipSuccess) return hip_fail(e, "append score kernel");
   b->rows_committed = n + 1;
   if (row_out) *row_out = n;
+  return ATTNRES_OK;
+}
+
+attnres_status_t attnres_bank_accumulate(attnres_bank_t b, const void* y, void* partial_out,
+                                         int32_t commit, attnres_stream_t stream,
+                                         int32_t* row_out) {
+  if (!b) return fail(ATTNRES_ERR_INVALID, "bank is NULL");
+  if (!b->queries_set) return fail(ATTNRES_ERR_ORDER, "accumulate before set_queries");
+  if (b->bwd_next >= 0 || b->bwd_done)
+    return fail(ATTNRES_ERR_ORDER, "accumulate during or after the backward phase");
+  const bool empty = b->cfg.tokens == 0;
+  if (!empty && !y) return fail(ATTNRES_ERR_INVALID, "y is NULL");
+  if (!aligned16(y) || !aligned16(partial_out))
+    return fail(ATTNRES_ERR_INVALID, "y and partial_out must be 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t elems = b->cfg.tokens * (int64_t)b->cfg.d;
+  if (commit) {
+    if (partial_out) return fail(ATTNRES_ERR_INVALID, "partial_out must be NULL when committing");
+    if (b->rows_committed >= b->cfg.max_rows)
+      return fail(ATTNRES_ERR_CAPACITY, "bank is full (max_rows=%d)", b->cfg.max_rows);
+    char* dst = b->row_ptr(b->rows_committed);
+    if (!empty && (b->partial || y != dst)) {
+      TraceScope ts(b, ATTNRES_KERNEL_ACCUMULATE, st);
+      hipError_t e = attnres::launch_accumulate(b->cfg.dtype, b->partial, y, dst, elems, st);
+      ts.done();
+      if (e != hipSuccess) return hip_fail(e, "accumulate kernel");
+    }
+    b->partial = nullptr;
+    return attnres_bank_append(b, nullptr, stream, row_out);
+  }
+  if (!empty && !partial_out) return fail(ATTNRES_ERR_INVALID, "partial_out is NULL");
+  if (!empty && (b->partial || y != partial_out)) {
+    TraceScope ts(b, ATTNRES_KERNEL_ACCUMULATE, st);
+    hipError_t e = attnres::launch_accumulate(b->cfg.dtype, b->partial, y, partial_out, elems, st);
+    ts.done();
+    if (e != hipSuccess) return hip_fail(e, "accumulate kernel");
+  }
+  b->partial = partial_out;
+  if (row_out) *row_out = -1;
   return ATTNRES_OK;
 }
 
@@ -567,6 +608,7 @@ attnres_status_t attnres_route_bwd(attnres_bank_t b, int32_t site, const void* e
     j.slot = n_rows;
     j.s0 = site;
     j.s1 = site + 1;
+    j.accumulate = b->has_extra[site] == 2 ? 1 : 0;
     jobs.push_back(j);
   }
   SiteArrays sa{};
@@ -596,7 +638,7 @@ attnres_status_t attnres_site_saved(attnres_bank_t b, int32_t site, const float*
   if (site >= b->fwd_next) return fail(ATTNRES_ERR_ORDER, "site %d has not run forward", site);
   if (alpha) *alpha = b->site_alpha(site);
   if (lse) *lse = b->site_lse(site);
-  if (n_src) *n_src = b->nsrc[site] + b->has_extra[site];
+  if (n_src) *n_src = b->nsrc[site] + (b->has_extra[site] ? 1 : 0);
   return ATTNRES_OK;
 }
 

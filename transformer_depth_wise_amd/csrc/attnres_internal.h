@@ -64,6 +64,11 @@ hipError_t launch_score(const Geom& g, int dtype, const void* x, const QuerySet&
                         int s_hi, int slot, float* rinv_out, float* proj,
                         int64_t site_stride, hipStream_t st);
 
+// Block partial sum: out = a + b (a may be NULL: out = b) over `elems`
+// storage-dtype elements (a multiple of the 16-byte chunk), one rounding.
+hipError_t launch_accumulate(int dtype, const void* a, const void* b, void* out, int64_t elems,
+                             hipStream_t st);
+
 // Effective queries with gains: for every (site, k) of [sites, r],
 // qf = q * gain, q32 = q (float32), qhi = bf16(qf), qlo = bf16(qf - qhi).
 hipError_t launch_fold_gains(int dtype, const void* q, const float* gain, int64_t count,
@@ -93,6 +98,7 @@ struct FinalizeJob {
   float* dst;           // its gradient [T, d] float32
   int32_t slot;         // its source index inside the per-site slots
   int32_t s0, s1;       // contributing sites
+  int32_t accumulate;   // 1: add the gradient to dst instead of storing it
 };
 
 hipError_t launch_finalize(const Geom& g, int dtype, const FinalizeJob* jobs, int njobs,

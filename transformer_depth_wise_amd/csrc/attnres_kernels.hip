@@ -1339,6 +1339,16 @@ __global__ __launch_bounds__(kThreads) void k_finalize(Geom g, FinalizeArgs fa, 
       for (int e = 0; e < N; ++e) acc[j][e] -= rc * f[e];
     }
     float4* o = reinterpret_cast<float4*>(dst + (int64_t)sl[j].q * N);
+    if (job.accumulate) {  // add to what dst holds (a block partial sum's running gradient)
+#pragma unroll
+      for (int e = 0; e < N / 4; ++e) {
+        const float4 p = o[e];
+        acc[j][4 * e] += p.x;
+        acc[j][4 * e + 1] += p.y;
+        acc[j][4 * e + 2] += p.z;
+        acc[j][4 * e + 3] += p.w;
+      }
+    }
 #pragma unroll
     for (int e = 0; e < N / 4; ++e)
       st_stream(reinterpret_cast<float*>(o + e),
@@ -1394,6 +1404,30 @@ FinFn<T, QT> pick_fin(int cpt) {
     case 8: return k_finalize<T, 8, QT>;
   }
   return nullptr;
+}
+
+// Block partial sum ("Low-Rank Attention Residuals", section 3, partial-block
+// routing): out = a + b in float32, rounded once to the storage dtype, or
+// out = b when a is NULL.  Elementwise, so out may alias a or b.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_accumulate(const uint4* a, const uint4* b, uint4* out,
+                                                         int64_t chunks) {
+  using V = Vec<T>;
+  constexpr int N = V::N;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < chunks;
+       i += (int64_t)gridDim.x * kThreads) {
+    const uint4 y = b[i];
+    if (a) {
+      float x[N], z[N];
+      V::unpack(a[i], x);
+      V::unpack(y, z);
+#pragma unroll
+      for (int e = 0; e < N; ++e) x[e] += z[e];
+      out[i] = V::pack(x);
+    } else {
+      out[i] = y;
+    }
+  }
 }
 
 // Effective queries with gains (see launch_fold_gains).
@@ -1563,6 +1597,23 @@ hipError_t launch_fold_gains(int dtype, const void* q, const float* gain, int64_
   else
     hipLaunchKernelGGL(k_fold_gains<bf16_t>, dim3((unsigned)blocks), dim3(kThreads), 0, st,
                        static_cast<const bf16_t*>(q), gain, count, qf, q32, qhi, qlo);
+  return hipGetLastError();
+}
+
+hipError_t launch_accumulate(int dtype, const void* a, const void* b, void* out, int64_t elems,
+                             hipStream_t st) {
+  const int64_t chunks = elems / (dtype == 0 ? 4 : 8);
+  if (chunks == 0) return hipSuccess;
+  int64_t blocks = (chunks + kThreads - 1) / kThreads;
+  if (blocks > 2048) blocks = 2048;
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_accumulate<float>, dim3((unsigned)blocks), dim3(kThreads), 0, st,
+                       static_cast<const uint4*>(a), static_cast<const uint4*>(b),
+                       static_cast<uint4*>(out), chunks);
+  else
+    hipLaunchKernelGGL(k_accumulate<bf16_t>, dim3((unsigned)blocks), dim3(kThreads), 0, st,
+                       static_cast<const uint4*>(a), static_cast<const uint4*>(b),
+                       static_cast<uint4*>(out), chunks);
   return hipGetLastError();
 }
 

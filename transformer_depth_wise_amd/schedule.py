@@ -39,3 +39,41 @@ def run_microbatch(bank: Bank, nsrc, has_extra, queries, outs, dqs, extras=None,
     if backward:
         for s in reversed(range(S)):
             bank.route_bwd(s, extras[s], None, dqs[s], d_extras[s], stream)
+
+
+def run_block_microbatch(bank: Bank, nsrc, has_partial, queries, x, ys, outs, partials, douts=None,
+                         dqs=None, dys=None, stream=None):
+    """Block routing over sublayer outputs ("Low-Rank Attention Residuals",
+    Appendix H, Figure 11), the partial sums kept by the bank.
+
+    ``x`` [T, d] is the embedding (row 0), ``ys[t]`` the output of sublayer
+    t + 1; the read after it sees rows [0, nsrc[t]) and, when
+    ``has_partial[t]``, the block's running partial sum, accumulated into
+    ``partials[t]`` (caller memory that must outlive the backward); a read
+    without a partial follows a block end, whose sum the bank commits as the
+    next row.  ``outs[t]`` receives the read's output.  With ``douts``, the
+    backward runs too: ``dqs[t]`` gets the query gradient and ``dys[t]``
+    (float32 [T, d]) the gradient of ys[t]; the embedding's gradient is left
+    in ``bank.drows[0]``.
+    """
+    M = len(nsrc)
+    bank.reset()
+    bank.set_queries(nsrc, [2 if p else 0 for p in has_partial], queries)
+    bank.append(x, stream)
+    for t in range(M):
+        if has_partial[t]:
+            bank.accumulate(ys[t], partials[t], False, stream)
+        else:
+            bank.accumulate(ys[t], None, True, stream)
+        bank.route_fwd(t, partials[t] if has_partial[t] else None, outs[t], stream)
+    if douts is None:
+        return
+    for t in reversed(range(M)):
+        # the row the block of sublayer t + 1 commits into: the last row read
+        # after a block end, the next row while the block is open
+        row = nsrc[t] if has_partial[t] else nsrc[t] - 1
+        d_extra = bank.drows[row] if has_partial[t] else None
+        bank.route_bwd(t, partials[t] if has_partial[t] else None, douts[t], dqs[t], d_extra,
+                       stream)
+        if dys is not None:
+            dys[t].copy_(bank.drows[row])  # the gradient of ys[t], in stream order
