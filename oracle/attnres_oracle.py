@@ -45,13 +45,12 @@ Readings where the pages are open (each also listed in the design doc):
       ("Low-Rank Attention Residuals", Appendix B.1, Eq. 17).  The fused
       kernel of Figure 9 rounds the normalised key to the storage dtype
       before the gain; the oracle keeps it exact.
-  R7  norm="full" is the full-width-RMS control ("Low-Rank Attention
-      Residuals", section 4.4, Eq. 13 control): the RMS is taken over all d
-      coordinates of the source, the key is still its last r coordinates.
-      Its source gradient is Appendix B.3, Eq. 22: the radial term has
-      divisor d and reaches every coordinate.  For r = d it coincides with
-      the default norm="slice".
-  R8  Delta form ("Multi-Head Attention Residuals", section 3.3,
+  R5  LR with H > 1: q in R^r is split into H slices of width r/H; head h
+      scores the h-th slice of the normalised r-wide key and mixes the h-th
+      d/H slice of the value.  Requires H | r.  r = d gives MHAR.
+  R6  Sites read a growing prefix of the bank; the trivial one-source site
+      is included.
+  R17  Delta form ("Multi-Head Attention Residuals", section 3.3,
       identity-preserving conversion, and Appendix E, delta variant and
       Figure 9): one self-contained read per call over a short source list,
       a learnable null source (one d-vector shared by every token, scored as
@@ -61,7 +60,13 @@ Readings where the pages are open (each also listed in the design doc):
       null source's gradient is the sum over tokens of its per-token
       gradient, and the residual stream's gradient is dout itself.  An output
       gate on the routed term belongs to the caller.
-  R9  Block routing ("Low-Rank Attention Residuals", section 3, partial-
+  R19  norm="full" is the full-width-RMS control ("Low-Rank Attention
+      Residuals", section 4.4, Eq. 13 control): the RMS is taken over all d
+      coordinates of the source, the key is still its last r coordinates.
+      Its source gradient is Appendix B.3, Eq. 22: the radial term has
+      divisor d and reaches every coordinate.  For r = d it coincides with
+      the default norm="slice".
+  R20  Block routing ("Low-Rank Attention Residuals", section 3, partial-
       block routing, and Appendix H, Figure 11): sublayer outputs y_t add
       up into the running partial sum of their block; a block ends after
       sublayer ceil(M j / N) and its sum becomes a completed source; the
@@ -73,11 +78,6 @@ Readings where the pages are open (each also listed in the design doc):
       formed, b_t = round(b_{t-1} + y_t); `store` is that rounding (given by
       the caller; identity, i.e. exact sums, by default).  The gradient
       passes through the rounding unchanged.
-  R5  LR with H > 1: q in R^r is split into H slices of width r/H; head h
-      scores the h-th slice of the normalised r-wide key and mixes the h-th
-      d/H slice of the value.  Requires H | r.  r = d gives MHAR.
-  R6  Sites read a growing prefix of the bank; the trivial one-source site
-      is included.
 """
 
 from __future__ import annotations
@@ -117,7 +117,7 @@ def route_forward(sources, q, heads: int, r: int, eps: float = EPS, gain=None,
     sources: [N, T, d]  (committed rows, then a transient source if any)
     q:       [r]        static query of the site
     gain:    [r] or None  RMSNorm gain on the normalised key (R3)
-    norm:    "slice" (RMS over the key) or "full" (RMS over all d, R7)
+    norm:    "slice" (RMS over the key) or "full" (RMS over all d, R19)
     Returns out [T, d], alpha [N, T, H], lse [T, H].
     """
     src = np.asarray(sources, dtype=np.float64)
@@ -190,7 +190,7 @@ def run_schedule(rows, extras, queries, douts, nsrc, heads: int, r: int, eps: fl
     douts:   [S, T, d]   upstream gradient of each site's output
     nsrc:    S ints; site s reads rows [0, nsrc[s]) (then its extra, if any)
     gains:   None or [S, r] RMSNorm gain of each site (R3)
-    norm:    "slice" or "full" (R7)
+    norm:    "slice" or "full" (R19)
 
     The loss whose gradients are returned is sum_s <dout_s, out_s>, with every
     bank row, query and transient source an independent input.
@@ -237,7 +237,7 @@ def run_schedule(rows, extras, queries, douts, nsrc, heads: int, r: int, eps: fl
 
 
 def block_reads(M: int, ends):
-    """Members of every source of each read of block routing (R9): a list over
+    """Members of every source of each read of block routing (R20): a list over
     reads t = 1..M of source member tuples, -1 the embedding, i the output of
     sublayer i + 1; completed blocks first (embedding first), partial last."""
     blocks, partial, reads = [(-1,)], None, []
@@ -252,7 +252,7 @@ def block_reads(M: int, ends):
 
 def run_block_routing(x, ys, queries, douts, ends, heads: int, r: int, eps: float = EPS,
                       norm: str = "slice", store=None):
-    """Block routing over given sublayer outputs (R9).
+    """Block routing over given sublayer outputs (R20).
 
     x:       [T, d]     the embedding, the first source of every read
     ys:      [M, T, d]  sublayer outputs y_1..y_M
@@ -260,7 +260,7 @@ def run_block_routing(x, ys, queries, douts, ends, heads: int, r: int, eps: floa
     douts:   [M, T, d]  upstream gradient of each read's output
     ends:    sublayer numbers (1-based) that end a block
     store:   None, or the rounding of a freshly formed partial sum to the
-             storage dtype (R9)
+             storage dtype (R20)
     The loss is sum_t <dout_t, out_t>.  Returns a dict: out [M, T, d],
     dx [T, d], dy [M, T, d], dq [M, r].
     """
@@ -304,7 +304,7 @@ def _site_sources(rows, extra, n):
 
 
 def delta_forward(null_src, sources, q, partial, heads: int, eps: float = EPS):
-    """One delta read (R8).
+    """One delta read (R17).
 
     null_src: [d] or None   learnable null source, the same for every token
     sources:  [M, T, d]     block deltas
@@ -322,7 +322,7 @@ def delta_forward(null_src, sources, q, partial, heads: int, eps: float = EPS):
 
 
 def delta_backward(null_src, sources, q, dout, heads: int, eps: float = EPS):
-    """Gradient of <dout, out> for one delta read (R8).
+    """Gradient of <dout, out> for one delta read (R17).
 
     Returns dsources [M, T, d], dnull [d] (None without a null source) and
     dq [d].  The residual stream's gradient is dout.
