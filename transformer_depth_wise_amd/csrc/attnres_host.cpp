@@ -168,7 +168,9 @@ Geom make_site_geom(const attnres_config_t& c) {
 
 struct attnres_bank_s {
   attnres_config_t cfg;
-  Geom g_main;  // forward and finalize
+  Geom g_main;  // forward
+  Geom g_fin;   // finalize (no 7 or 8 chunks per thread: its fp32 accumulators and query chunks
+                // would leave one wave per SIMD)
   Geom g_site;  // backward site pass (fewer chunks per thread: more registers per chunk)
   Layout lay;
   char* rows;
@@ -336,12 +338,14 @@ attnres_status_t attnres_bank_create(const attnres_config_t* cfg, void* rows, fl
   if (workspace_bytes < lay.total)
     return fail(ATTNRES_ERR_CAPACITY, "workspace has %zu bytes, needs %zu", workspace_bytes, lay.total);
   static const int kMainCpts[] = {4, 5, 8, 7, 2};
+  static const int kFinCpts[] = {4, 5, 2};
   attnres_bank_s* b = new (std::nothrow) attnres_bank_s();
   if (!b) return fail(ATTNRES_ERR_CAPACITY, "host allocation of the handle failed");
   b->cfg = *cfg;
   b->g_main = make_geom(*cfg, kMainCpts, 5);
+  b->g_fin = make_geom(*cfg, kFinCpts, 3);
   b->g_site = make_site_geom(*cfg);
-  if (b->g_main.tt < 1 || b->g_site.tt < 1) {
+  if (b->g_main.tt < 1 || b->g_fin.tt < 1 || b->g_site.tt < 1) {
     delete b;
     return fail(ATTNRES_ERR_UNSUPPORTED, "row of %d chunks is too wide for one tile", cfg->d);
   }
@@ -621,7 +625,7 @@ attnres_status_t attnres_route_bwd(attnres_bank_t b, int32_t site, const void* e
   sa.rad_stride = b->lay.rad_stride;
   sa.th_stride = c.tokens * (int64_t)c.heads;
   TraceScope tf(b, ATTNRES_KERNEL_FINALIZE, st);
-  hipError_t e = attnres::launch_finalize(b->g_main, c.dtype, jobs.data(), (int)jobs.size(), sa,
+  hipError_t e = attnres::launch_finalize(b->g_fin, c.dtype, jobs.data(), (int)jobs.size(), sa,
                                           b->dout_rows, row_stride, b->qset(), st);
   tf.done();
   if (e != hipSuccess) return hip_fail(e, "route_bwd finalize kernel");
