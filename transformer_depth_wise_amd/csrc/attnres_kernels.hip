@@ -144,25 +144,6 @@ __device__ __forceinline__ float quad_sum(float v) {
   return v;
 }
 
-// log2 of the widest lane group (at most a wave) whose size divides kvc.
-__host__ __device__ inline int site_group_shift(int kvc) {
-  int sh = 0;
-  while (sh < 6 && (kvc & ((2 << sh) - 1)) == 0) ++sh;
-  return sh;
-}
-
-// Sum over aligned groups of 2^sh lanes (sh <= 6, uniform over the wave);
-// every lane of a group gets the group's sum.
-__device__ __forceinline__ float group_sum(float v, int sh) {
-  if (sh >= 2) {
-    v = quad_sum(v);
-    for (int o = 4; o < (1 << sh); o <<= 1) v += __shfl_xor(v, o, 64);
-  } else if (sh == 1) {
-    v += __shfl_xor(v, 1, 64);
-  }
-  return v;
-}
-
 // <a, b> over one 16-byte chunk with fp32 accumulation.
 template <typename T>
 __device__ __forceinline__ float dot_chunk(const uint4& a, const uint4& b);
@@ -724,9 +705,10 @@ constexpr int kSiteRowBatch = CPT <= 4 ? 4 : 2;
 //   W_t = sum_n a rho^-1 key_n  (per token, in registers),
 // so the rows are streamed once (the pages' kernel streams them twice).
 // Per row, each lane dots its 16-byte chunk with the upstream gradient; the
-// lanes of an aligned group inside one head (up to a wave) combine in
-// registers, group leaders put the sums in LDS and one thread per (row,
-// token, head) adds its head's groups in a fixed order.  After the tile the coefficients the finalize gather needs are
+// 4 lanes of a quad (4 chunks of one head) combine by DPP and quad leaders
+// put the sums in LDS.  Each (row, token, head) sum then gets a lane group
+// of up to a wave, which reads its head's quad sums in parallel and reduces
+// them with a fixed-order butterfly.  After the tile the coefficients the finalize gather needs are
 // formed here: dl = a (P - S) and, per (source, token), the radial sum
 // sum_h dl_h * l_h with l = log(a) + lse (the logit).  Persistent grid of
 // `parts` work-groups, each writing one [r] partial of dq.
@@ -744,9 +726,9 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
   const int n_src = n_rows + (extra != nullptr ? 1 : 0);
   const int pairs = g.tt * g.H;
   // lanes hold consecutive chunks and a head's chunks start at a multiple
-  // of kvc, so the 2^sh lanes of an aligned group share one head when 2^sh
-  // divides kvc: their dots are summed in registers before LDS
-  const int sh = site_group_shift(g.kvc);
+  // of kvc, so the 4 lanes of a quad share one head when 4 divides kvc:
+  // their dots are summed by DPP before LDS
+  const int sh = (g.kvc & 3) == 0 ? 2 : 0;
   const int plen = g.tt * g.cpr;             // partial dots of one row (chunks)
   float* s_alpha = sm;                       // [n_src][tt][H]
   float* s_P = s_alpha + n_src * pairs;      // [n_src][tt][H]
@@ -818,22 +800,32 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
       for (int r = 0; r < RB; ++r) {
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
-          const float part = group_sum(dot_chunk<T>(dov[j], cur[r][j]), sh);
+          float part = dot_chunk<T>(dov[j], cur[r][j]);
+          if (sh) part = quad_sum(part);
           if (sl[j].own && (sl[j].q & ((1 << sh) - 1)) == 0)
             s_part[((r * plen) >> sh) + (sl[j].q >> sh)] = part;
         }
       }
       __syncthreads();
-      // one thread per (row of the batch, token, head) adds its head's groups
-      for (int i = tid; i < RB * pairs; i += kThreads) {
-        const int r = i / pairs, p = i - r * pairs;
-        if (n0 + r >= n_src) break;
-        const int tau = p / g.H, h = p - tau * g.H;
-        const float* pp = s_part + ((r * plen + tau * g.cpr + h * g.kvc) >> sh);
-        const int cnt = g.kvc >> sh;
-        float P = 0.f;
-        for (int c = 0; c < cnt; ++c) P += pp[c];
-        s_P[(n0 + r) * pairs + p] = P;
+      // each (row of the batch, token, head) sum gets a lane group of G
+      // lanes (G a power of two up to a wave): strided partial sums, then a
+      // fixed-order butterfly inside the group
+      {
+        const int combos = RB * pairs, cnt = g.kvc >> sh;
+        int G = 64;
+        while (G > 1 && combos * G > kThreads) G >>= 1;
+        for (int base = 0; base < combos * G; base += kThreads) {
+          const int i = base + tid, combo = i / G, li = i - combo * G;
+          const int r = combo / pairs, p = combo - r * pairs;
+          float P = 0.f;
+          if (combo < combos) {
+            const int tau = p / g.H, h = p - tau * g.H;
+            const float* pp = s_part + ((r * plen + tau * g.cpr + h * g.kvc) >> sh);
+            for (int c = li; c < cnt; c += G) P += pp[c];
+          }
+          for (int o = 1; o < G; o <<= 1) P += __shfl_xor(P, o, 64);
+          if (li == 0 && combo < combos && n0 + r < n_src) s_P[(n0 + r) * pairs + p] = P;
+        }
       }
       __syncthreads();
 #pragma unroll
@@ -1488,7 +1480,7 @@ size_t lds_bwd_site(const Geom& g, int n_src) {
   }
   const size_t pairs = (size_t)g.tt * g.H;
   const size_t rb = g.cpt <= 4 ? 4 : 2;  // kSiteRowBatch
-  const size_t part = rb * (((size_t)g.tt * g.cpr) >> site_group_shift(g.kvc));
+  const size_t part = rb * (((size_t)g.tt * g.cpr) >> ((g.kvc & 3) == 0 ? 2 : 0));
   const size_t a = 2 * (size_t)n_src * pairs + (size_t)n_src * g.tt + part + 2 * pairs;
   const size_t b = (size_t)g.tt * g.r;
   return sizeof(float) * (a > b ? a : b);
