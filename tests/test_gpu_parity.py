@@ -44,6 +44,18 @@ def _workload(name):
         from synth import Workload, block_schedule
         nsrc, extra = block_schedule(4)
         w = Workload("lr_tiny_f32", 37, 64, 2, 32, nsrc, extra, "f32", True)
+    elif base == "lr_f32_d2048":
+        # fp32 rows of 512 chunks: the column-layout finalize in fp32, keys on
+        # the last 512 of 2048 coordinates, 4 heads, ragged token tiles
+        from synth import Workload, block_schedule
+        nsrc, extra = block_schedule(4)
+        w = Workload("lr_f32_d2048", 29, 2048, 4, 512, nsrc, extra, "f32", True)
+    elif base == "mhar_d4096":
+        # bf16 rows of 512 chunks, full routing, 8 heads: the column-layout
+        # finalize with storage-dtype queries
+        from synth import Workload, full_schedule
+        nsrc, extra = full_schedule(2)
+        w = Workload("mhar_d4096", 21, 4096, 8, 4096, nsrc, extra, "bf16", True)
     else:
         w = get_workload(base)
     for o in opts:
@@ -51,7 +63,10 @@ def _workload(name):
     return w
 
 
-@pytest.mark.parametrize("name", REDUCED + ["bf16_kk24", "lr_tiny_f32"] + VARIANTS)
+WIDE = ["lr_f32_d2048", "lr_f32_d2048+gain+fullrms", "mhar_d4096", "mhar_d4096+gain"]
+
+
+@pytest.mark.parametrize("name", REDUCED + ["bf16_kk24", "lr_tiny_f32"] + VARIANTS + WIDE)
 def test_schedule_matches_oracle(name):
     w = _workload(name)
     inp = Inputs(w)

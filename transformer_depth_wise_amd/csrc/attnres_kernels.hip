@@ -1349,6 +1349,165 @@ __global__ __launch_bounds__(kThreads) void k_finalize(Geom g, FinalizeArgs fa, 
 }
 
 // ---------------------------------------------------------------------------
+// Finalize for wide rows (at least 512 chunks, a multiple of kColBlock):
+// the same gradient as k_finalize, laid out by columns.  A work-group covers
+// kColTokens tokens x kColBlock chunk columns; thread (half, c) owns column c
+// for kColTh consecutive tokens, so each query chunk it needs is loaded once
+// per site for all of its tokens (with one-token tiles the query chunks,
+// float32 with gains, cost L2 twice the bytes of the upstream gradients).
+// Grid: (column blocks x token tiles, jobs).
+constexpr int kColBlock = 128;
+constexpr int kColTh = 4;
+constexpr int kColTokens = 2 * kColTh;
+
+template <typename T, typename QT>
+__global__ __launch_bounds__(kThreads) void k_finalize_cols(Geom g, FinalizeArgs fa,
+                                                             SiteArrays sa, int batch,
+                                                             const T* __restrict__ dout_rows,
+                                                             int64_t dout_stride,
+                                                             const QT* __restrict__ Q) {
+  using V = Vec<T>;
+  constexpr int N = V::N;
+  constexpr int TT = kColTokens;
+  extern __shared__ float sm[];
+  const int ncb = g.cpr / kColBlock;
+  const int64_t lin = xcd_order((int64_t)blockIdx.y * gridDim.x + blockIdx.x,
+                                (int64_t)gridDim.x * gridDim.y);
+  const int64_t rem = lin % gridDim.x;
+  const FinalizeJob job = fa.job[lin / gridDim.x];
+  const int64_t tile = rem / ncb;
+  const int cb = (int)(rem - tile * ncb);
+  const int pairs = TT * g.H;
+  float* cA = sm;                      // [batch][TT][H]  alpha
+  float* cQ = cA + batch * pairs;      // [batch][TT][H]  rho^-1 * dl
+  float* s_radb = cQ + batch * pairs;  // [batch][TT]     radial sums of the batch
+  float* s_rad = s_radb + batch * TT;  // [TT]
+  const int tid = threadIdx.x;
+  const int64_t t0 = tile * TT;
+  const int tv = (int)min((int64_t)TT, g.T - t0);
+  const int col = cb * kColBlock + (tid & (kColBlock - 1));
+  const int tau0 = (tid / kColBlock) * kColTh;  // first of this thread's tokens in the tile
+  const int hv = col / g.kvc;
+  const bool key = col >= g.key_c0;
+  const int kc = key ? col - g.key_c0 : 0;
+  const int hk = kc / g.kkc;
+  // chunk offsets of this thread's tokens; tokens past the end read the
+  // tile's first token (valid memory, zero weight, never stored)
+  int64_t off[kColTh];
+#pragma unroll
+  for (int i = 0; i < kColTh; ++i)
+    off[i] = (int64_t)((tau0 + i < tv) ? tau0 + i : 0) * g.cpr + col;
+
+  float acc[kColTh][N];
+#pragma unroll
+  for (int i = 0; i < kColTh; ++i)
+#pragma unroll
+    for (int e = 0; e < N; ++e) acc[i][e] = 0.f;
+  float rad = 0.f;  // thread tau < TT: sum over sites of the radial sums
+
+  auto dout_of = [&](int s) {
+    return reinterpret_cast<const uint4*>(dout_rows + (int64_t)s * dout_stride + t0 * g.d);
+  };
+  for (int b0 = job.s0; b0 < job.s1; b0 += batch) {
+    const int nb = min(batch, job.s1 - b0);
+    uint4 buf[2][kColTh];
+    QChunk<T, QT> qb[2];
+    {
+      const uint4* dp = dout_of(b0);
+#pragma unroll
+      for (int i = 0; i < kColTh; ++i) buf[0][i] = ld_stream(dp + off[i]);
+      if (key) qb[0].load(Q + (int64_t)b0 * g.r, kc);
+    }
+    for (int i = tid; i < nb * pairs; i += kThreads) {
+      const int k = i / pairs, p = i - k * pairs;
+      const int tau = p / g.H;
+      float a = 0.f, q = 0.f;
+      if (tau < tv) {
+        const int64_t idx =
+            (int64_t)(b0 + k) * sa.site_stride + ((int64_t)job.slot * g.T + t0) * g.H + p;
+        a = sa.alpha[idx];
+        q = job.rinv[t0 + tau] * sa.dl[idx];
+      }
+      cA[i] = a;
+      cQ[i] = q;
+    }
+    for (int i = tid; i < nb * TT; i += kThreads) {
+      const int k = i / TT, tau = i - k * TT;
+      s_radb[i] = tau < tv ? sa.radial[(int64_t)(b0 + k) * sa.rad_stride +
+                                       (int64_t)job.slot * g.T + t0 + tau]
+                           : 0.f;
+    }
+    __syncthreads();
+    if (tid < TT)
+      for (int k = 0; k < nb; ++k) rad += s_radb[k * TT + tid];
+    for (int i = 0; i < nb; i += 2) {
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const int k = i + d;
+        if (k >= nb) break;
+        if (k + 1 < nb) {
+          const uint4* dp = dout_of(b0 + k + 1);
+#pragma unroll
+          for (int t = 0; t < kColTh; ++t) buf[d ^ 1][t] = ld_stream(dp + off[t]);
+          if (key) qb[d ^ 1].load(Q + (int64_t)(b0 + k + 1) * g.r, kc);
+        }
+        float qf[N];
+        if (key) qb[d].unpack(qf);
+#pragma unroll
+        for (int t = 0; t < kColTh; ++t) {
+          const int base = (k * TT + tau0 + t) * g.H;
+          const float a = cA[base + hv];
+          float f[N];
+          V::unpack(buf[d][t], f);
+#pragma unroll
+          for (int e = 0; e < N; ++e) acc[t][e] += a * f[e];
+          if (key) {
+            const float b = cQ[base + hk];
+#pragma unroll
+            for (int e = 0; e < N; ++e) acc[t][e] += b * qf[e];
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (tid < TT) {
+    const float ri = (tid < tv) ? job.rinv[t0 + tid] : 0.f;
+    s_rad[tid] = ri * ri / (float)g.rms_w * rad;
+  }
+  __syncthreads();
+
+  const uint4* xp = reinterpret_cast<const uint4*>(static_cast<const T*>(job.x) + t0 * g.d);
+  float* dst = job.dst + t0 * g.d;
+#pragma unroll
+  for (int t = 0; t < kColTh; ++t) {
+    if (tau0 + t >= tv) continue;
+    if (key || g.rms_full) {  // radial term: key coordinates, or all of them
+      const float rc = s_rad[tau0 + t];
+      float f[N];
+      V::unpack(xp[off[t]], f);
+#pragma unroll
+      for (int e = 0; e < N; ++e) acc[t][e] -= rc * f[e];
+    }
+    float4* o = reinterpret_cast<float4*>(dst + off[t] * N);
+    if (job.accumulate) {  // add to what dst holds (a block partial sum's running gradient)
+#pragma unroll
+      for (int e = 0; e < N / 4; ++e) {
+        const float4 p = o[e];
+        acc[t][4 * e] += p.x;
+        acc[t][4 * e + 1] += p.y;
+        acc[t][4 * e + 2] += p.z;
+        acc[t][4 * e + 3] += p.w;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < N / 4; ++e)
+      st_stream(reinterpret_cast<float*>(o + e),
+                make_float4(acc[t][4 * e], acc[t][4 * e + 1], acc[t][4 * e + 2], acc[t][4 * e + 3]));
+  }
+}
+
+// ---------------------------------------------------------------------------
 template <typename T>
 using FwdFn = void (*)(Geom, const T*, int64_t, const T*, int, const float*, const float*,
                        const float*, float*, float*, T*);
@@ -1669,10 +1828,53 @@ hipError_t launch_dq_reduce(const float* dq_part, int parts, int r, float* dq, c
   return hipGetLastError();
 }
 
+// Wide rows take the column layout (see k_finalize_cols).
+bool finalize_by_columns(const Geom& g) { return g.cpr >= 512 && g.cpr % kColBlock == 0; }
+
+hipError_t launch_finalize_cols(const Geom& g, int dtype, const FinalizeJob* jobs, int njobs,
+                                const SiteArrays& sa, const void* dout_rows, int64_t dout_stride,
+                                const QuerySet& qs, hipStream_t st) {
+  int max_sites = 1;
+  for (int i = 0; i < njobs; ++i)
+    if (jobs[i].s1 - jobs[i].s0 > max_sites) max_sites = jobs[i].s1 - jobs[i].s0;
+  Geom gc = g;
+  gc.tt = kColTokens;
+  int batch = finalize_batch(gc);
+  if (max_sites < batch) batch = max_sites;
+  const size_t lds = sizeof(float) * (2 * (size_t)batch * kColTokens * g.H +
+                                      (size_t)batch * kColTokens + kColTokens);
+  if (lds > kMaxLds) return hipErrorInvalidConfiguration;
+  const int64_t tiles = (g.T + kColTokens - 1) / kColTokens;
+  const int64_t gx = tiles * (g.cpr / kColBlock);
+  if (gx > 0x7fffffff) return hipErrorInvalidConfiguration;
+  for (int j0 = 0; j0 < njobs; j0 += kMaxJobs) {
+    FinalizeArgs fa{};
+    const int nj = (njobs - j0 < kMaxJobs) ? njobs - j0 : kMaxJobs;
+    for (int i = 0; i < nj; ++i) fa.job[i] = jobs[j0 + i];
+    const dim3 grid((unsigned)gx, (unsigned)nj);
+    if (dtype == 0)
+      hipLaunchKernelGGL((k_finalize_cols<float, float>), grid, dim3(kThreads), lds, st, g, fa, sa,
+                         batch, static_cast<const float*>(dout_rows), dout_stride,
+                         qs.qf ? qs.qf : static_cast<const float*>(qs.q));
+    else if (qs.qf)  // float32 effective queries q * g
+      hipLaunchKernelGGL((k_finalize_cols<bf16_t, float>), grid, dim3(kThreads), lds, st, g, fa,
+                         sa, batch, static_cast<const bf16_t*>(dout_rows), dout_stride, qs.qf);
+    else
+      hipLaunchKernelGGL((k_finalize_cols<bf16_t, bf16_t>), grid, dim3(kThreads), lds, st, g, fa,
+                         sa, batch, static_cast<const bf16_t*>(dout_rows), dout_stride,
+                         static_cast<const bf16_t*>(qs.q));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_finalize(const Geom& g, int dtype, const FinalizeJob* jobs, int njobs,
                            const SiteArrays& sa, const void* dout_rows, int64_t dout_stride,
                            const QuerySet& qs, hipStream_t st) {
   if (g.T == 0 || njobs == 0) return hipSuccess;
+  if (finalize_by_columns(g))
+    return launch_finalize_cols(g, dtype, jobs, njobs, sa, dout_rows, dout_stride, qs, st);
   int max_sites = 1;
   for (int i = 0; i < njobs; ++i)
     if (jobs[i].s1 - jobs[i].s0 > max_sites) max_sites = jobs[i].s1 - jobs[i].s0;
