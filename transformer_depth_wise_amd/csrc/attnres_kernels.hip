@@ -414,30 +414,27 @@ __global__ __launch_bounds__(kThreads) void k_score_mfma(Geom g, const bf16_t* _
   }
 }
 
-// ---------------------------------------------------------------------------
-// Forward of one site: softmax over the cached logits of the tile's
-// (token, head) pairs, then out = sum_n alpha_n * s_n per head slice.
-// Grid: ceil(T / tt) work-groups.  Source n < n_rows is bank row n, source
-// n_rows (if extra) the transient source.  The first two sources are
-// requested before the softmax prologue so that their loads overlap it; the
-// stream then keeps three sources in flight.
 // Append on the matrix cores for wide key heads (r/H > 256, a multiple of
 // 32; e.g. a single head over thousands of key coordinates).  The per-head
 // projection is the same [16 tokens x r/H] . [r/H x sites] product, but the
 // k dimension is too long to hold in registers: a work-group owns 16
-// tokens, its 4 waves take interleaved 32-wide k steps (so every key and
-// query fragment is loaded once per work-group), each wave accumulates up to
-// NB 16-site blocks, and the waves' accumulators meet in LDS per head.
-template <int NB>
-__global__ __launch_bounds__(kThreads) void k_score_wide(Geom g, const bf16_t* __restrict__ x,
+// tokens, each of its WAVES waves takes a contiguous share of the 32-wide k
+// steps (so every key and query fragment is loaded once per work-group),
+// accumulates up to NB 16-site blocks, and the waves' accumulators meet in
+// LDS per head.  With few site blocks (scoring a transient source against
+// its one site) 8 waves per work-group keep more of the row in flight.
+constexpr int kScoreWideAhead = 8;
+
+template <int NB, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_score_wide(Geom g, const bf16_t* __restrict__ x,
                                                           const bf16_t* __restrict__ Q,
                                                           const bf16_t* __restrict__ Qlo, int s_lo,
                                                           int s_hi, int slot,
                                                           float* __restrict__ rinv_out,
                                                           float* __restrict__ proj,
                                                           int64_t site_stride) {
-  extern __shared__ float sm[];  // [4 waves][NB][64 lanes][4] partial sums, then [4][16] squares
-  constexpr int kWaves = kThreads / 64;
+  extern __shared__ float sm[];  // [WAVES][NB][64 lanes][4] partial sums, then [WAVES][16] squares
+  constexpr int kWaves = WAVES;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = lane & 15, kg = lane >> 4;
   const int64_t tw = xcd_order(blockIdx.x, gridDim.x) * 16;
@@ -453,7 +450,7 @@ __global__ __launch_bounds__(kThreads) void k_score_wide(Geom g, const bf16_t* _
   float ss = 0.f;
   if (g.rms_full && tok_ok) {
     const uint4* rp = reinterpret_cast<const uint4*>(x + t * g.d);
-    for (int c = wave * 4 + kg; c < g.key_c0; c += 16) {
+    for (int c = wave * 4 + kg; c < g.key_c0; c += 4 * kWaves) {
       float f[8];
       Vec<bf16_t>::unpack(ld_stream(rp + c), f);
 #pragma unroll
@@ -464,24 +461,44 @@ __global__ __launch_bounds__(kThreads) void k_score_wide(Geom g, const bf16_t* _
     f32x4_t acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int i = wave; i < ksteps; i += kWaves) {
-      const int k0 = h * g.kk + i * 32 + kg * 8;
-      const uint4 av = tok_ok ? ld_stream(reinterpret_cast<const uint4*>(xr + k0)) : zero4();
-      float f[8];
-      Vec<bf16_t>::unpack(av, f);
+    // Each wave takes a contiguous range of k-steps, kScoreWideAhead at a
+    // time requested before the first is used: a token's row is then read in
+    // runs of kScoreWideAhead * 64 bytes, and several loads per lane are in
+    // flight (one step at a time, interleaved over the waves, left one
+    // 64-byte piece per token in flight)
+    const int per = (ksteps + kWaves - 1) / kWaves;
+    const int i_end = min(ksteps, (wave + 1) * per);
+    for (int i0 = wave * per; i0 < i_end; i0 += kScoreWideAhead) {
+      uint4 av[kScoreWideAhead];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+      for (int u = 0; u < kScoreWideAhead; ++u) {
+        const int i = i0 + u;
+        av[u] = (tok_ok && i < i_end)
+                    ? ld_stream(reinterpret_cast<const uint4*>(xr + h * g.kk + i * 32 + kg * 8))
+                    : zero4();
+      }
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        if (b < nsb) {
-          const int sv = s_lo + b * 16 + row;
-          const int64_t qo = (int64_t)(sv < s_hi ? sv : s_lo) * g.r + k0;
-          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              as_bf16x8(av), as_bf16x8(*reinterpret_cast<const uint4*>(Q + qo)), acc[b], 0, 0, 0);
-          if (Qlo)
+      for (int u = 0; u < kScoreWideAhead; ++u) {
+        const int i = i0 + u;
+        if (i >= i_end) break;
+        const int k0 = h * g.kk + i * 32 + kg * 8;
+        float f[8];
+        Vec<bf16_t>::unpack(av[u], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          if (b < nsb) {
+            const int sv = s_lo + b * 16 + row;
+            const int64_t qo = (int64_t)(sv < s_hi ? sv : s_lo) * g.r + k0;
             acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                as_bf16x8(av), as_bf16x8(*reinterpret_cast<const uint4*>(Qlo + qo)), acc[b], 0,
+                as_bf16x8(av[u]), as_bf16x8(*reinterpret_cast<const uint4*>(Q + qo)), acc[b], 0,
                 0, 0);
+            if (Qlo)
+              acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  as_bf16x8(av[u]), as_bf16x8(*reinterpret_cast<const uint4*>(Qlo + qo)), acc[b],
+                  0, 0, 0);
+          }
         }
       }
     }
@@ -530,6 +547,13 @@ __global__ __launch_bounds__(kThreads) void k_score_wide(Geom g, const bf16_t* _
   }
 }
 
+// ---------------------------------------------------------------------------
+// Forward of one site: softmax over the cached logits of the tile's
+// (token, head) pairs, then out = sum_n alpha_n * s_n per head slice.
+// Grid: ceil(T / tt) work-groups.  Source n < n_rows is bank row n, source
+// n_rows (if extra) the transient source.  The first two sources are
+// requested before the softmax prologue so that their loads overlap it; the
+// stream then keeps three sources in flight.
 template <typename T, int CPT>
 __global__ __launch_bounds__(kThreads) void k_fwd(Geom g, const T* __restrict__ rows,
                                                    int64_t row_stride, const T* __restrict__ extra,
@@ -1691,12 +1715,17 @@ hipError_t launch_score(const Geom& g, int dtype, const void* x, const QuerySet&
     const bf16_t* qb = qs.qf ? qs.qhi : static_cast<const bf16_t*>(qs.q);
     const bf16_t* ql = qs.qf ? qs.qlo : nullptr;
     const int nb = nsb <= 1 ? 1 : nsb <= 2 ? 2 : nsb <= 4 ? 4 : nsb <= 8 ? 8 : 16;
-    const size_t lds = sizeof(float) * (size_t)kThreads * 4 * nb;  // >= the 4 x 16 squares
+    const int waves = nb <= 4 ? 8 : 4;
+    const size_t lds = sizeof(float) * (size_t)waves * 64 * 4 * nb;  // >= the waves x 16 squares
     switch (nb) {
 #define ATTNRES_SCORE_NB(B)                                                                    \
   case B:                                                                                      \
-    hipLaunchKernelGGL(k_score_wide<B>, grid, dim3(kThreads), lds, st, g, xb, qb, ql, s_lo,    \
-                       s_hi, slot, rinv_out, proj, site_stride);                               \
+    if (waves == 8)                                                                            \
+      hipLaunchKernelGGL((k_score_wide<B, 8>), grid, dim3(512), lds, st, g, xb, qb, ql, s_lo,  \
+                         s_hi, slot, rinv_out, proj, site_stride);                             \
+    else                                                                                       \
+      hipLaunchKernelGGL((k_score_wide<B, 4>), grid, dim3(256), lds, st, g, xb, qb, ql, s_lo,  \
+                         s_hi, slot, rinv_out, proj, site_stride);                             \
     break;
       ATTNRES_SCORE_NB(1)
       ATTNRES_SCORE_NB(2)
