@@ -122,6 +122,25 @@ def cpu_baseline(name: str, tokens: int, full_tokens: int):
     }
 
 
+# Oracle time the default CPU-baseline sample is sized to from a 16-token run
+# (larger samples run somewhat slower per token, so the run itself takes
+# about 10-20 s), and the most tokens it takes.
+CPU_TARGET_S = 8.0
+CPU_MAX_TOKENS = 1024
+
+
+def sized_cpu_baseline(args, w):
+    """The oracle baseline on args.cpu_tokens tokens, or on a sample sized to
+    about CPU_TARGET_S seconds from a 16-token run."""
+    if args.cpu_tokens is not None:
+        return cpu_baseline(args.workload, args.cpu_tokens, w.tokens)
+    probe = cpu_baseline(args.workload, 16, w.tokens)
+    per_token_s = probe["value"] / 1e3 / w.tokens
+    tokens = int(min(w.tokens, CPU_MAX_TOKENS, max(16, CPU_TARGET_S / max(per_token_s, 1e-9))))
+    tokens -= tokens % 8 if tokens > 16 else 0
+    return probe if tokens <= 16 else cpu_baseline(args.workload, tokens, w.tokens)
+
+
 PROBE_BYTES = 2 << 30  # bytes each bandwidth probe reads
 
 
@@ -599,7 +618,7 @@ def bench_blocks(args):
         "workload": shape.name, "tokens": T, "d": d, "r": shape.r, "heads": shape.heads,
         "sublayers": M, "blocks": shape.blocks, "storage": shape.dtype, "norm": shape.norm,
         "block_sums": "kept by the bank (attnres_bank_accumulate)",
-    }, cpu=lambda: blocks_cpu_baseline(shape, min(args.cpu_tokens, 16)))
+    }, cpu=lambda: blocks_cpu_baseline(shape, args.cpu_tokens or 16))
 
 
 def main():
@@ -608,7 +627,9 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mhar1b")
-    ap.add_argument("--cpu-tokens", type=int, default=64)
+    ap.add_argument("--cpu-tokens", type=int, default=None,
+                    help="token sample of the CPU oracle baseline (default: sized from a "
+                         "16-token run to about 10-20 s of oracle time)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true")
     ap.add_argument("--no-recompute", action="store_true",
@@ -768,8 +789,7 @@ def report(args, w, bank, step, alg, config, cpu=None):
         print(f"[bench] per-kernel: {json.dumps(kern)}", file=sys.stderr, flush=True)
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = (cpu() if cpu is not None
-                                  else cpu_baseline(args.workload, args.cpu_tokens, w.tokens))
+        result["cpu_baseline"] = cpu() if cpu is not None else sized_cpu_baseline(args, w)
     print(json.dumps(result), flush=True)
 
 
