@@ -43,6 +43,12 @@ CASES = [
     # rank wider than a wave per head, odd head width
     ListShape("d1000_r600_h2", 33, 1000, 600, 2, (0, 1, 2, 3), pads=(3, 0, 0, 1), qstride=5,
               qscale=0.1),
+    # 16-byte runs (every width, head, stride and offset a multiple of the
+    # chunk): strided, repeated and broadcast sources on the vector path
+    ListShape("vec_f32_d256", 33, 256, 128, 2, (0, 1, 0, 2), pads=(4, 0, 8), offsets=(4, 0, 0),
+              dtype="f32", qscale=0.3),
+    ListShape("vec_bf16_d512_full", 29, 512, 128, 4, (0, 1, 2, 1), pads=(0, -1, 16),
+              offsets=(8, 0, 0), qscale=0.3, norm="full"),
 ]
 
 

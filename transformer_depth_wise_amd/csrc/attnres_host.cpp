@@ -6,6 +6,7 @@
 #include <stdio.h>
 
 #include <string>
+#include <initializer_list>
 #include <vector>
 
 #include "../../include/attnres.h"
@@ -903,6 +904,22 @@ attnres_status_t list_geom(const attnres_list_t* c, attnres::ListGeom* g) {
   return ATTNRES_OK;
 }
 
+// 16-byte runs: widths, heads and strides multiples of the chunk, unit query
+// stride, and every pointer the kernels touch 16-byte aligned.
+bool list_vector_ok(const attnres_list_t* c, const attnres::ListGeom& g,
+                    std::initializer_list<const void*> ptrs) {
+  const int pc = c->dtype == ATTNRES_F32 ? 4 : 8;
+  if (g.d % pc || g.r % pc || g.kv % pc || g.kk % pc || c->query_stride != 1) return false;
+  if (!aligned16(c->query)) return false;
+  for (int n = 0; n < c->n_sources; ++n) {
+    const int64_t stride = c->source_strides ? c->source_strides[n] : c->d;
+    if (stride % pc || !aligned16(c->sources[n])) return false;
+  }
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return false;
+  return true;
+}
+
 attnres::ListArgs list_args(const attnres_list_t* c) {
   attnres::ListArgs a{};
   a.query = c->query;
@@ -937,6 +954,7 @@ attnres_status_t attnres_list_fwd(const attnres_list_t* call, void* out, float* 
     return fail(ATTNRES_ERR_INVALID, "out, alpha, lse and rinv must be non-NULL");
   if (!aligned_to(out, es) || !aligned_to(alpha, 4) || !aligned_to(lse, 4) || !aligned_to(rinv, 4))
     return fail(ATTNRES_ERR_INVALID, "out, alpha, lse and rinv must be aligned to their element size");
+  g.vec = list_vector_ok(call, g, {out}) ? 1 : 0;
   hipError_t e = attnres::launch_list_fwd(g, call->dtype, list_args(call), out, alpha, lse, rinv,
                                           static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTNRES_OK : hip_fail(e, "list forward kernel");
@@ -973,6 +991,11 @@ attnres_status_t attnres_list_bwd(const attnres_list_t* call, const void* dout,
     }
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (g.T > 0) {
+    g.vec = list_vector_ok(call, g, {dout}) ? 1 : 0;
+    for (int n = 0; n < g.n && g.vec; ++n)
+      if (!aligned16(d_sources[n])) g.vec = 0;
+  }
   const int parts = attnres::list_bwd_parts(g);
   float* dq_part = static_cast<float*>(workspace);
   hipError_t e = attnres::launch_list_bwd(g, call->dtype, list_args(call), dout, alpha, lse, rinv,

@@ -156,6 +156,7 @@ struct ListGeom {
   int32_t w;   // coordinates in the RMS: d - n0
   int64_t qs;  // query stride in elements
   float eps;
+  int32_t vec;  // 1: every row, head, stride and pointer allows 16-byte runs (unit query stride)
 };
 struct ListArgs {
   const void* src[kMaxListSources];

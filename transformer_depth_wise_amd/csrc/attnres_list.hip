@@ -7,6 +7,10 @@
 // (unaligned widths and ranks, strided or repeated sources, strided
 // queries): every access is one element wide, consecutive lanes on
 // consecutive coordinates, so each wave load still covers a contiguous run.
+// When every width, head, stride and pointer of a call allows it (and the
+// query is unit-stride), the same kernels move one 16-byte chunk per lane
+// instead (VW = 8 bf16 or 4 fp32 values): no run then straddles the norm or
+// key boundary or a key head.
 //
 // One wave per token, grid-stride over tokens; per-(token, head) reductions
 // are wave sums, so no work-group barrier is needed.
@@ -74,7 +78,64 @@ __device__ __forceinline__ const T* row_of(const ListArgs& a, int n, int64_t t) 
   return static_cast<const T*>(a.src[n]) + t * a.stride[n];
 }
 
-template <typename T>
+// VW consecutive elements of one lane: VW = 1 (any alignment), or one 16-byte
+// chunk (8 bf16 or 4 fp32 values) when every row, head and pointer is
+// aligned to it.
+template <typename T, int VW>
+struct Run {
+  float v[VW];
+  __device__ __forceinline__ void load(const T* p) {
+    if constexpr (VW == 1) {
+      v[0] = ld1(p);
+    } else {
+      const uint4 w = *reinterpret_cast<const uint4*>(p);
+      if constexpr (sizeof(T) == 4) {
+        v[0] = __uint_as_float(w.x);
+        v[1] = __uint_as_float(w.y);
+        v[2] = __uint_as_float(w.z);
+        v[3] = __uint_as_float(w.w);
+      } else {
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[2 * i] = __uint_as_float(u[i] << 16);
+          v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+        }
+      }
+    }
+  }
+};
+
+// Store VW values to storage dtype T.
+template <typename T, int VW>
+__device__ __forceinline__ void store_run(T* p, const float* v) {
+  if constexpr (VW == 1) {
+    st1(p, v[0]);
+  } else if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+    uint4 w;
+    w.x = to_bf16_bits(v[0]) | (to_bf16_bits(v[1]) << 16);
+    w.y = to_bf16_bits(v[2]) | (to_bf16_bits(v[3]) << 16);
+    w.z = to_bf16_bits(v[4]) | (to_bf16_bits(v[5]) << 16);
+    w.w = to_bf16_bits(v[6]) | (to_bf16_bits(v[7]) << 16);
+    *reinterpret_cast<uint4*>(p) = w;
+  }
+}
+
+// Store VW float32 values (the gradients).
+template <int VW>
+__device__ __forceinline__ void store_f32(float* p, const float* v) {
+  if constexpr (VW == 1) {
+    *p = v[0];
+  } else {
+#pragma unroll
+    for (int i = 0; i < VW / 4; ++i)
+      reinterpret_cast<float4*>(p)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+  }
+}
+
+template <typename T, int VW>
 __global__ __launch_bounds__(kLFwdThreads) void k_list_fwd(ListGeom g, ListArgs a,
                                                            T* __restrict__ out,
                                                            float* __restrict__ alpha,
@@ -91,18 +152,29 @@ __global__ __launch_bounds__(kLFwdThreads) void k_list_fwd(ListGeom g, ListArgs 
     for (int n = 0; n < g.n; ++n) {
       const T* s = row_of<T>(a, n, t);
       float ss = 0.f;
-      for (int j = g.n0 + lane; j < g.k0; j += 64) {  // norm coordinates outside the key
-        const float v = ld1(s + j);
-        ss += v * v;
+      for (int j = g.n0 + lane * VW; j < g.k0; j += 64 * VW) {  // norm coordinates outside the key
+        Run<T, VW> x;
+        x.load(s + j);
+#pragma unroll
+        for (int e = 0; e < VW; ++e) ss += x.v[e] * x.v[e];
       }
       for (int h = 0; h < g.H; ++h) {
         const T* kh = s + g.k0 + h * g.kk;
         const T* qh = q + (int64_t)h * g.kk * g.qs;
         float dot = 0.f;
-        for (int k = lane; k < g.kk; k += 64) {
-          const float v = ld1(kh + k);
-          ss += v * v;
-          dot += v * ld1(qh + (int64_t)k * g.qs);
+        for (int k = lane * VW; k < g.kk; k += 64 * VW) {
+          Run<T, VW> x, qv;
+          x.load(kh + k);
+          if constexpr (VW == 1) {
+            qv.v[0] = ld1(qh + (int64_t)k * g.qs);
+          } else {
+            qv.load(qh + k);  // unit query stride on this path
+          }
+#pragma unroll
+          for (int e = 0; e < VW; ++e) {
+            ss += x.v[e] * x.v[e];
+            dot += x.v[e] * qv.v[e];
+          }
         }
         dot = wave_sum(dot);
         if (lane == 0) w_a[n * g.H + h] = dot;
@@ -128,18 +200,26 @@ __global__ __launch_bounds__(kLFwdThreads) void k_list_fwd(ListGeom g, ListArgs 
     wave_lds_fence();
     T* o = out + t * g.d;
     for (int h = 0; h < g.H; ++h) {
-      for (int k = lane; k < g.kv; k += 64) {
+      for (int k = lane * VW; k < g.kv; k += 64 * VW) {
         const int j = h * g.kv + k;
-        float acc = 0.f;
-        for (int n = 0; n < g.n; ++n) acc += w_a[n * g.H + h] * ld1(row_of<T>(a, n, t) + j);
-        st1(o + j, acc);
+        float acc[VW];
+#pragma unroll
+        for (int e = 0; e < VW; ++e) acc[e] = 0.f;
+        for (int n = 0; n < g.n; ++n) {
+          const float al = w_a[n * g.H + h];
+          Run<T, VW> x;
+          x.load(row_of<T>(a, n, t) + j);
+#pragma unroll
+          for (int e = 0; e < VW; ++e) acc[e] += al * x.v[e];
+        }
+        store_run<T, VW>(o + j, acc);
       }
     }
     wave_lds_fence();  // the next token rewrites w_a
   }
 }
 
-template <typename T>
+template <typename T, int VW>
 __global__ __launch_bounds__(256) void k_list_bwd(ListGeom g, ListArgs a,
                                                   const T* __restrict__ dout,
                                                   const float* __restrict__ alpha,
@@ -170,7 +250,13 @@ __global__ __launch_bounds__(256) void k_list_bwd(ListGeom g, ListArgs a,
       const T* s = row_of<T>(a, n, t);
       for (int h = 0; h < g.H; ++h) {
         float p = 0.f;
-        for (int k = lane; k < g.kv; k += 64) p += ld1(go + h * g.kv + k) * ld1(s + h * g.kv + k);
+        for (int k = lane * VW; k < g.kv; k += 64 * VW) {
+          Run<T, VW> y, x;
+          y.load(go + h * g.kv + k);
+          x.load(s + h * g.kv + k);
+#pragma unroll
+          for (int e = 0; e < VW; ++e) p += y.v[e] * x.v[e];
+        }
         p = wave_sum(p);
         if (lane == 0) w_p[n * g.H + h] = p;
       }
@@ -198,25 +284,43 @@ __global__ __launch_bounds__(256) void k_list_bwd(ListGeom g, ListArgs a,
       const float cr = rv * rv / (float)g.w * w_c[n];
       for (int h = 0; h < g.H; ++h) {
         const float al = w_a[n * g.H + h];
-        for (int k = lane; k < g.kv; k += 64) {
+        for (int k = lane * VW; k < g.kv; k += 64 * VW) {
+          // a run never straddles the norm or key boundary, nor a key head:
+          // with VW > 1 every boundary is a multiple of VW
           const int j = h * g.kv + k;
-          float v = al * ld1(go + j);
+          Run<T, VW> y;
+          y.load(go + j);
+          float v[VW];
+#pragma unroll
+          for (int e = 0; e < VW; ++e) v[e] = al * y.v[e];
           if (j >= g.n0) {
-            const float x = ld1(s + j);
-            v -= cr * x;
+            Run<T, VW> x;
+            x.load(s + j);
+#pragma unroll
+            for (int e = 0; e < VW; ++e) v[e] -= cr * x.v[e];
             if (j >= g.k0) {
               const int jk = j - g.k0;
               const float b = rv * w_p[n * g.H + jk / g.kk];
-              v += b * ld1(q + (int64_t)jk * g.qs);
-              w_dq[jk] += b * x;  // coordinate jk always belongs to this lane
+              Run<T, VW> qv;
+              if constexpr (VW == 1) {
+                qv.v[0] = ld1(q + (int64_t)jk * g.qs);
+              } else {
+                qv.load(q + jk);
+              }
+#pragma unroll
+              for (int e = 0; e < VW; ++e) {
+                v[e] += b * qv.v[e];
+                w_dq[jk + e] += b * x.v[e];  // coordinates jk.. always belong to this lane
+              }
             }
           }
-          ds[j] = v;
+          store_f32<VW>(ds + j, v);
         }
       }
     }
     wave_lds_fence();  // the next token rewrites the per-token state
   }
+  wave_lds_fence();  // dq coordinates were summed by other lanes than those writing them out
   float* dst = dq_part + ((int64_t)blockIdx.x * nw + wave) * g.r;
   for (int k = lane; k < g.r; k += 64) dst[k] = w_dq[k];
 }
@@ -251,11 +355,17 @@ hipError_t launch_list_fwd(const ListGeom& g, int dtype, const ListArgs& a, void
   const int64_t groups = (g.T + kLFwdThreads / 64 - 1) / (kLFwdThreads / 64);
   const dim3 grid((unsigned)(groups < 4096 ? groups : 4096));
   const size_t lds = list_fwd_lds_bytes(g);
-  if (dtype == 0)
-    hipLaunchKernelGGL((k_list_fwd<float>), grid, dim3(kLFwdThreads), lds, st, g, a,
+  if (dtype == 0 && g.vec)
+    hipLaunchKernelGGL((k_list_fwd<float, 4>), grid, dim3(kLFwdThreads), lds, st, g, a,
                        static_cast<float*>(out), alpha, lse, rinv);
+  else if (dtype == 0)
+    hipLaunchKernelGGL((k_list_fwd<float, 1>), grid, dim3(kLFwdThreads), lds, st, g, a,
+                       static_cast<float*>(out), alpha, lse, rinv);
+  else if (g.vec)
+    hipLaunchKernelGGL((k_list_fwd<bf16_t, 8>), grid, dim3(kLFwdThreads), lds, st, g, a,
+                       static_cast<bf16_t*>(out), alpha, lse, rinv);
   else
-    hipLaunchKernelGGL((k_list_fwd<bf16_t>), grid, dim3(kLFwdThreads), lds, st, g, a,
+    hipLaunchKernelGGL((k_list_fwd<bf16_t, 1>), grid, dim3(kLFwdThreads), lds, st, g, a,
                        static_cast<bf16_t*>(out), alpha, lse, rinv);
   return hipGetLastError();
 }
@@ -268,11 +378,17 @@ hipError_t launch_list_bwd(const ListGeom& g, int dtype, const ListArgs& a, cons
   if (nw < 1 || parts % nw) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)(parts / nw));
   const size_t lds = sizeof(float) * (size_t)nw * list_bwd_wave_floats(g);
-  if (dtype == 0)
-    hipLaunchKernelGGL((k_list_bwd<float>), grid, dim3(64 * nw), lds, st, g, a,
+  if (dtype == 0 && g.vec)
+    hipLaunchKernelGGL((k_list_bwd<float, 4>), grid, dim3(64 * nw), lds, st, g, a,
                        static_cast<const float*>(dout), alpha, lse, rinv, gr, dq_part);
+  else if (dtype == 0)
+    hipLaunchKernelGGL((k_list_bwd<float, 1>), grid, dim3(64 * nw), lds, st, g, a,
+                       static_cast<const float*>(dout), alpha, lse, rinv, gr, dq_part);
+  else if (g.vec)
+    hipLaunchKernelGGL((k_list_bwd<bf16_t, 8>), grid, dim3(64 * nw), lds, st, g, a,
+                       static_cast<const bf16_t*>(dout), alpha, lse, rinv, gr, dq_part);
   else
-    hipLaunchKernelGGL((k_list_bwd<bf16_t>), grid, dim3(64 * nw), lds, st, g, a,
+    hipLaunchKernelGGL((k_list_bwd<bf16_t, 1>), grid, dim3(64 * nw), lds, st, g, a,
                        static_cast<const bf16_t*>(dout), alpha, lse, rinv, gr, dq_part);
   return hipGetLastError();
 }
