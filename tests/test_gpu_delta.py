@@ -135,3 +135,39 @@ def test_delta_deterministic_bitwise():
         np.testing.assert_array_equal(a[k], b[k])
     for x, y in zip(a["dd"], b["dd"]):
         np.testing.assert_array_equal(x, y)
+
+
+def _delta_sweep(count=12, seed=2027):
+    """Seeded delta shapes the library accepts (its whole-token wave layouts
+    and the two-waves-per-token split), checked on the host by the
+    workspace query."""
+    from transformer_depth_wise_amd import attnres as A
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        dtype = "bf16" if rng.random() < 0.7 else "f32"
+        pc = 8 if dtype == "bf16" else 4
+        heads = int(rng.choice([1, 2, 4, 8]))
+        d = heads * 4 * pc * int(rng.integers(1, 17))
+        m = int(rng.integers(0, 9))
+        null = bool(rng.random() < 0.7) or m == 0
+        s = DeltaShape(f"sweep{len(out):02d}", int(rng.choice([1, 3, 9, 16, 37])), d, heads, m,
+                       null=null, partial=bool(rng.random() < 0.6), dtype=dtype,
+                       seed=200 + len(out))
+        c = A.make_delta_call(s.tokens, d, heads, [0x10000] * m, 0x10000 if null else None,
+                              0x10000, A.ATTNRES_BF16 if dtype == "bf16" else A.ATTNRES_F32)
+        if A.load_library().attnres_delta_workspace_bytes(ctypes.byref(c)) > 0:
+            out.append(s)
+    return out
+
+
+import ctypes  # noqa: E402
+
+DELTA_SWEEP = _delta_sweep()
+
+
+@pytest.mark.parametrize("s", DELTA_SWEEP, ids=lambda s: s.name)
+def test_delta_sweep_matches_oracle(s):
+    inp = DeltaInputs(s)
+    log(f"[delta sweep] {s.describe()}")
+    compare(s, run_gpu(s, inp), run_ref(s, inp), label="delta sweep")

@@ -122,6 +122,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise ImportError(f"libattnres is not built ({path} missing); run "
                           f"`python -m transformer_depth_wise_amd.build`")
+    # The library must bind to the HIP runtime that torch (which owns the device
+    # memory and streams handed to it) uses: load torch's first when it is
+    # installed, or a runtime loaded by this library first would be shared
+    # with torch's own libraries and the device would not be found.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     vp, i32, fp = c_void_p, c_int32, POINTER(c_float)
     cfgp = POINTER(Config)
