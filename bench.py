@@ -632,6 +632,9 @@ def main():
                          "16-token run to about 10-20 s of oracle time)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="bank workloads: also capture one microbatch as a HIP graph and time "
+                         "its replays (graph_ms_per_microbatch)")
     ap.add_argument("--no-recompute", action="store_true",
                     help="delta workloads: time the backward without re-running each call's "
                          "forward (the pages' setting re-runs it)")
@@ -736,6 +739,26 @@ def report(args, w, bank, step, alg, config, cpu=None):
     ms = ev0.elapsed_time(ev1) / args.steps
     print(f"[bench] {args.steps} steps: {ms:.3f} ms/microbatch", file=sys.stderr, flush=True)
 
+    graph_ms = None
+    if getattr(args, "graph", False):
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = ev0.elapsed_time(ev1) / args.steps
+        print(f"[bench] {args.steps} graph replays: {graph_ms:.3f} ms/microbatch", file=sys.stderr,
+              flush=True)
+        del graph
+
     result_probe = bandwidth_probe(torch)
     total_bytes = sum(alg.values())
     result = {
@@ -758,6 +781,8 @@ def report(args, w, bank, step, alg, config, cpu=None):
         "alg_bytes_per_microbatch": total_bytes,
         "probe": result_probe,
     }
+    if graph_ms is not None:
+        result["graph_ms_per_microbatch"] = round(graph_ms, 3)
 
     if not args.no_trace:
         bank.trace(True)
