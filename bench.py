@@ -23,6 +23,7 @@ import platform
 import re
 import sys
 import time
+from statistics import median
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -219,6 +220,38 @@ def summarize_counters(pmc_dir: str, workload: str, copy_bytes: int, command: st
         wk = per["WRITE_SIZE"].get(kind, (0.0, 0))[0]
         lines.append(f"kernel {kind} {n} {fk:.1f} {wk:.1f} "
                      f"{fk * 1024 * scale['FETCH_SIZE']:.0f} {wk * 1024 * scale['WRITE_SIZE']:.0f}")
+    return "\n".join(lines) + "\n"
+
+
+ACTIVITY_COUNTERS = ("OccupancyPercent", "VALUBusy")
+
+
+def summarize_activity(pmc_dir: str, workload: str, command: str):
+    """Mean per dispatch, per kernel kind, of rocprofv3's derived counters
+    OccupancyPercent (wave slots in use) and VALUBusy (share of the time the
+    vector ALUs issue), each from its own run; None when a run is missing."""
+    per = {}
+    for counter in ACTIVITY_COUNTERS:
+        path = os.path.join(pmc_dir, f"pmc_{counter}", "run_counter_collection.csv")
+        if not os.path.exists(path):
+            return None
+        vals = collections.defaultdict(list)
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                kind = kind_of(row["Kernel_Name"])
+                if kind is not None and row["Counter_Name"] == counter:
+                    vals[kind].append(float(row["Counter_Value"]))
+        per[counter] = vals
+    lines = [f"# Occupancy and VALU activity per dispatch, {workload}: rocprofv3 derived "
+             f"counters {' and '.join(ACTIVITY_COUNTERS)} (percent, mean over dispatches)",
+             f"# command: {command}",
+             f"source_hash {source_hash()}",
+             "# kind dispatches occupancy_percent valu_busy_percent"]
+    for kind in sorted(per["OccupancyPercent"]):
+        occ = per["OccupancyPercent"][kind]
+        valu = per["VALUBusy"].get(kind, [])
+        lines.append(f"kernel {kind} {len(occ)} {sum(occ) / len(occ):.1f} "
+                     f"{(sum(valu) / len(valu)) if valu else float('nan'):.1f}")
     return "\n".join(lines) + "\n"
 
 
@@ -650,6 +683,13 @@ def main():
         with open(counters_path(args.workload), "w") as f:
             f.write(text)
         print(text, end="")
+        act = summarize_activity(args.counters, args.workload,
+                                 args.counters_command.replace("FETCH_SIZE, then WRITE_SIZE",
+                                                               ", ".join(ACTIVITY_COUNTERS)))
+        if act is not None:
+            with open(os.path.join(PROFILES, f"{args.workload}_occupancy_valu.txt"), "w") as f:
+                f.write(act)
+            print(act, end="")
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -730,14 +770,17 @@ def report(args, w, bank, step, alg, config, cpu=None):
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(args.steps):
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev0, ev1 = evs[0], evs[-1]
+    evs[0].record(stream)
+    for i in range(args.steps):
         step()
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
-    print(f"[bench] {args.steps} steps: {ms:.3f} ms/microbatch", file=sys.stderr, flush=True)
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    print(f"[bench] {args.steps} steps: {ms:.3f} ms/microbatch (median {median(per_step):.3f}, "
+          f"min {per_step[0]:.3f}, max {per_step[-1]:.3f})", file=sys.stderr, flush=True)
 
     graph_ms = None
     if getattr(args, "graph", False):
@@ -780,6 +823,8 @@ def report(args, w, bank, step, alg, config, cpu=None):
         "pct_of_peak": round(100.0 * total_bytes / ms / 1e6 / HBM_PEAK_GBPS, 1),
         "alg_bytes_per_microbatch": total_bytes,
         "probe": result_probe,
+        "step_ms": {"median": round(median(per_step), 3), "min": round(per_step[0], 3),
+                    "max": round(per_step[-1], 3)},
     }
     if graph_ms is not None:
         result["graph_ms_per_microbatch"] = round(graph_ms, 3)
@@ -811,6 +856,13 @@ def report(args, w, bank, step, alg, config, cpu=None):
                               "frac": round(a / HBM_PEAK_GBPS, 3), "traffic": traffic,
                               "alg_bytes_per_launch": int(alg[dom] / n_launch)}
         result["kernels"] = kern
+        # forward phase: appends, transient scoring, forwards and block sums;
+        # backward phase: site passes, dq reductions and finalizes (kernel time)
+        fwd_kinds = ("score", "fwd", "accumulate")
+        result["phase_ms"] = {
+            "fwd": round(sum(v["ms_per_microbatch"] for k, v in kern.items() if k in fwd_kinds), 3),
+            "bwd": round(sum(v["ms_per_microbatch"] for k, v in kern.items()
+                             if k not in fwd_kinds), 3)}
         print(f"[bench] per-kernel: {json.dumps(kern)}", file=sys.stderr, flush=True)
 
     if not args.no_cpu_baseline:
