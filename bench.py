@@ -665,6 +665,8 @@ def main():
                          "16-token run to about 10-20 s of oracle time)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true")
+    ap.add_argument("--overlap", action="store_true",
+                    help="bank workloads: run the appends one site ahead on a second stream")
     ap.add_argument("--graph", action="store_true",
                     help="bank workloads: also capture one microbatch as a HIP graph and time "
                          "its replays (graph_ms_per_microbatch)")
@@ -747,9 +749,11 @@ def main():
     print(f"[bench] {w.describe()} on {dev_name}; inputs ready in {time.time() - t_gen:.1f} s",
           file=sys.stderr, flush=True)
 
+    app_stream = torch.cuda.Stream() if args.overlap else None
+
     def step():
         run_microbatch(bank, list(w.nsrc), list(w.extra), queries, outs, dqs, extras, d_extras,
-                       gains=gains, dgains=dgains)
+                       gains=gains, dgains=dgains, append_stream=app_stream)
 
     parts = bank.tiling()["dq_parts"]
     alg, launches = kernel_bytes(w, parts)

@@ -27,7 +27,8 @@ def log(msg):
     print(msg, flush=True)
 
 
-def run_gpu(w, inp: Inputs, tokens=None, dout_tokens=None, bank=None, backward=True):
+def run_gpu(w, inp: Inputs, tokens=None, dout_tokens=None, bank=None, backward=True,
+            append_stream=None):
     """Run the whole schedule of workload `w` on the GPU.
 
     tokens:      token indices to read back (None: all)
@@ -63,7 +64,7 @@ def run_gpu(w, inp: Inputs, tokens=None, dout_tokens=None, bank=None, backward=T
     dex = [torch.empty((T, w.d), dtype=torch.float32, device="cuda") if e is not None else None
            for e in extras]
     run_microbatch(bank, list(w.nsrc), list(w.extra), queries, outs, dqs, extras, dex,
-                   backward=backward, gains=gains, dgains=dgains)
+                   backward=backward, gains=gains, dgains=dgains, append_stream=append_stream)
     torch.cuda.synchronize()
     idx = None if tokens is None else torch.as_tensor(np.asarray(tokens), device="cuda")
 

@@ -167,3 +167,19 @@ def test_zero_row_and_query():
     assert max_rel(bank.drows.cpu().numpy(), ref["dbank"]) <= 1e-5
     assert max_rel(dqs.cpu().numpy(), ref["dq"]) <= 1e-5
     np.testing.assert_allclose(bank.saved(2)[0].cpu().numpy(), 1.0 / 3.0, rtol=0, atol=1e-7)
+
+
+@pytest.mark.parametrize("name", ["mhar1b@T77", "lr_h8@T12+gain"])
+def test_appends_on_a_second_stream(name):
+    """Appends one site ahead on their own stream (run_microbatch's
+    append_stream) give the same results, bit for bit, as one stream."""
+    import torch
+    w = _workload(name)
+    inp = Inputs(w)
+    log(f"[two streams] {w.describe()}")
+    a = run_gpu(w, inp)
+    b = run_gpu(w, inp, bank=a["_bank"], append_stream=torch.cuda.Stream())
+    for k in ("out", "lse", "dbank", "dq"):
+        np.testing.assert_array_equal(a[k], b[k])
+    for x, y in zip(a["alpha"], b["alpha"]):
+        np.testing.assert_array_equal(x, y)

@@ -13,8 +13,8 @@ from .attnres import Bank
 
 
 def run_microbatch(bank: Bank, nsrc, has_extra, queries, outs, dqs, extras=None, d_extras=None,
-                   backward=True, stream=None, gains=None, dgains=None):
-    """Run every site forward, then (optionally) backward, on one stream.
+                   backward=True, stream=None, gains=None, dgains=None, append_stream=None):
+    """Run every site forward, then (optionally) backward.
 
     The bank rows must already be in ``bank.rows`` (each append commits the
     next row in place) and each site's upstream gradient in
@@ -22,6 +22,12 @@ def run_microbatch(bank: Bank, nsrc, has_extra, queries, outs, dqs, extras=None,
     ``dqs[s]`` its query gradient, ``d_extras[s]`` the transient-source
     gradient; bank-row gradients land in ``bank.drows``.  With ``gains``
     ([S, r] float32 routing RMSNorm gains) their gradients land in ``dgains``.
+
+    Everything runs on ``stream`` (torch's current stream when None), unless
+    ``append_stream`` is given: the appends then run one site ahead on that
+    stream, and each forward waits only for the appends of the rows it reads.
+    An append writes only the cached statistics of later sites, so it may run
+    beside the forward of the current site.
     """
     S = len(nsrc)
     extras = extras if extras is not None else [None] * S
@@ -31,11 +37,32 @@ def run_microbatch(bank: Bank, nsrc, has_extra, queries, outs, dqs, extras=None,
     if gains is not None:
         bank.set_gains(gains, dgains, stream)
     committed = 0
-    for s in range(S):
-        while committed < nsrc[s]:
-            bank.append(None, stream)
-            committed += 1
-        bank.route_fwd(s, extras[s], outs[s], stream)
+    if append_stream is None:
+        for s in range(S):
+            while committed < nsrc[s]:
+                bank.append(None, stream)
+                committed += 1
+            bank.route_fwd(s, extras[s], outs[s], stream)
+    else:
+        import torch
+        main = stream if stream is not None else torch.cuda.current_stream()
+        ready = torch.cuda.Event()
+        ready.record(main)
+        append_stream.wait_event(ready)  # rows written and gains folded before the appends
+        done = []  # done[n]: recorded on the append stream after the append of row n
+        for s in range(S):
+            target = nsrc[s + 1] if s + 1 < S else nsrc[s]  # one site ahead
+            while committed < max(target, nsrc[s]):
+                bank.append(None, append_stream)
+                ev = torch.cuda.Event()
+                ev.record(append_stream)
+                done.append(ev)
+                committed += 1
+            main.wait_event(done[nsrc[s] - 1])
+            bank.route_fwd(s, extras[s], outs[s], main)
+        end = torch.cuda.Event()
+        end.record(append_stream)
+        main.wait_event(end)
     if backward:
         for s in reversed(range(S)):
             bank.route_bwd(s, extras[s], None, dqs[s], d_extras[s], stream)
