@@ -365,7 +365,8 @@ attnres_status_t attnres_bank_create(const attnres_config_t* cfg, void* rows, fl
 void attnres_bank_destroy(attnres_bank_t bank) {
   if (!bank) return;
   trace_clear(bank);
-  for (hipEvent_t e : bank->event_pool) hipEventDestroy(e);
+  // destroy has no status to return; a failure to release an event is ignored
+  for (hipEvent_t e : bank->event_pool) (void)hipEventDestroy(e);
   delete bank;
 }
 
