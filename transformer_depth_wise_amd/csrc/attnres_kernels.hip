@@ -301,7 +301,6 @@ __global__ __launch_bounds__(kThreads) void k_score(Geom g, const T* __restrict_
 // accumulated from the same A fragments, so the row is read once.
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
-constexpr int kMfmaSiteBlocks = 8;  // 16-site blocks accumulated per pass over the row
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
   return __builtin_bit_cast(bf16x8_t, v);
