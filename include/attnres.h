@@ -132,7 +132,10 @@ size_t attnres_workspace_bytes(const attnres_config_t* cfg);
  * elements per 16-byte chunk, d, r, d/H and r/H must be multiples of c;
  * otherwise ATTNRES_ERR_UNSUPPORTED.  H | d, H | r, 1 <= r <= d, heads >= 1,
  * max_rows >= 1, max_sites >= 1, eps > 0, norm an attnres_norm_t, else
- * ATTNRES_ERR_INVALID.
+ * ATTNRES_ERR_INVALID.  A read keeps per-source state for each tile of
+ * tokens in on-chip memory, so a read of max_rows + 1 sources must fit one
+ * work-group's 160 KiB (at d = 1280, H = 8 in bf16: max_rows <= 280),
+ * else ATTNRES_ERR_UNSUPPORTED.
  * workspace_bytes must be at least attnres_workspace_bytes(cfg). */
 attnres_status_t attnres_bank_create(const attnres_config_t* cfg, void* rows, float* drows,
                                      void* dout_rows, void* workspace, size_t workspace_bytes,

@@ -71,6 +71,17 @@ def test_bad_config_rejected(lib, kw, status):
     assert e.value.status == status
 
 
+def test_source_count_bounded_by_lds(lib):
+    # d = 1280, H = 8, bf16: the backward site pass holds 36 floats per source
+    # and 112 more per wave of 2 tokens, 4 waves: 280 rows + 1 fit 160 KiB
+    b = fake_bank(cfg(max_rows=280, max_sites=4))
+    A.attnres_bank_destroy(b)
+    with pytest.raises(A.AttnResError) as e:
+        fake_bank(cfg(max_rows=281, max_sites=4))
+    assert e.value.status == A.ATTNRES_ERR_UNSUPPORTED
+    assert "LDS" in A.last_error()
+
+
 def test_workspace_size_and_capacity(lib):
     c = cfg()
     n = A.attnres_workspace_bytes(c)

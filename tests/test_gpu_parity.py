@@ -56,6 +56,12 @@ def _workload(name):
         from synth import Workload, full_schedule
         nsrc, extra = full_schedule(2)
         w = Workload("mhar_d4096", 21, 4096, 8, 4096, nsrc, extra, "bf16", True)
+    elif base == "mhar_deep":
+        # 1B width, 75 layers: 151 sites reading up to 151 sources, so a read
+        # keeps more than 64 KiB of per-source state per work-group
+        from synth import Workload, full_schedule
+        nsrc, extra = full_schedule(75)
+        w = Workload("mhar_deep", 23, 1280, 8, 1280, nsrc, extra, "bf16", True)
     else:
         w = get_workload(base)
     for o in opts:
@@ -63,7 +69,7 @@ def _workload(name):
     return w
 
 
-WIDE = ["lr_f32_d2048", "lr_f32_d2048+gain+fullrms", "mhar_d4096", "mhar_d4096+gain"]
+WIDE = ["lr_f32_d2048", "lr_f32_d2048+gain+fullrms", "mhar_d4096", "mhar_d4096+gain", "mhar_deep"]
 
 
 @pytest.mark.parametrize("name", REDUCED + ["bf16_kk24", "lr_tiny_f32"] + VARIANTS + WIDE)

@@ -43,17 +43,21 @@ struct Layout {
   size_t rinv, rinvx, proj, alpha, dl, radial, lse, dqpart;
   size_t qf, q32, qhi, qlo;  // effective queries with gains ([max_sites, r] each)
   size_t total;
-  int64_t site_stride;  // floats per site of proj / alpha / dl: (max_rows + 1) * T * H
-  int64_t rad_stride;   // floats per site of radial: (max_rows + 1) * T
+  int64_t site_stride;  // floats per site of proj / alpha: (max_rows + 1) * T * H
+  int64_t dl_stride;    // floats per site of dl: tiles * ts * (max_rows + 1) * H
+  int64_t rad_stride;   // floats per site of radial: tiles * ts * (max_rows + 1)
+  int32_t ts;           // tokens per tile of dl / radial
 };
 
 int dq_parts_cap() { return 512; }
 
-Layout make_layout(const attnres_config_t& c) {
+// ts: tokens per tile of the tile-major dl and radial arrays.
+Layout make_layout(const attnres_config_t& c, int ts) {
   Layout L{};
   const size_t T = (size_t)c.tokens;
   const size_t srcs = (size_t)c.max_rows + 1;  // bank rows + one transient source
   const size_t slot = srcs * T * (size_t)c.heads;
+  const size_t tp = ts > 0 ? (T + ts - 1) / ts * ts : T;  // T padded to whole tiles
   size_t off = 0;
   auto take = [&](size_t floats) {
     const size_t at = off;
@@ -64,8 +68,8 @@ Layout make_layout(const attnres_config_t& c) {
   L.rinvx = take((size_t)c.max_sites * T);
   L.proj = take(slot * c.max_sites);
   L.alpha = take(slot * c.max_sites);
-  L.dl = take(slot * c.max_sites);
-  L.radial = take(srcs * T * c.max_sites);
+  L.dl = take(srcs * tp * c.heads * c.max_sites);
+  L.radial = take(srcs * tp * c.max_sites);
   L.lse = take((size_t)c.max_sites * T * c.heads);
   L.dqpart = take((size_t)dq_parts_cap() * c.r);
   const size_t sr = (size_t)c.max_sites * c.r;
@@ -75,7 +79,9 @@ Layout make_layout(const attnres_config_t& c) {
   L.qlo = take((sr + 1) / 2);
   L.total = off;
   L.site_stride = (int64_t)slot;
-  L.rad_stride = (int64_t)(srcs * T);
+  L.dl_stride = (int64_t)(srcs * tp * c.heads);
+  L.rad_stride = (int64_t)(srcs * tp);
+  L.ts = ts;
   return L;
 }
 
@@ -125,6 +131,7 @@ Geom make_geom(const attnres_config_t& c, const int* cpts, int ncpts) {
   // with r == d both norms are the same read: keep the key-only code path
   g.rms_full = (c.norm == ATTNRES_NORM_FULL && c.r < c.d) ? 1 : 0;
   g.rms_w = g.rms_full ? c.d : c.r;
+  g.nslot = c.max_rows + 1;
   g.eps = c.eps;
   double best = 2.0;
   for (int i = 0; i < ncpts; ++i) {
@@ -164,6 +171,10 @@ Geom make_site_geom(const attnres_config_t& c) {
   }
   return g;
 }
+
+// Tokens per tile of the tile-major dl / radial arrays: the block that one
+// site-pass wave (wave-owned layout) or work-group writes.
+int coef_tile(const Geom& g) { return g.wave_tokens > 0 ? g.wave_tokens : g.tt; }
 
 }  // namespace
 
@@ -208,7 +219,7 @@ struct attnres_bank_s {
   float* rinvx(int s) const { return f(lay.rinvx) + (size_t)s * cfg.tokens; }
   float* site_proj(int s) const { return f(lay.proj) + (size_t)s * lay.site_stride; }
   float* site_alpha(int s) const { return f(lay.alpha) + (size_t)s * lay.site_stride; }
-  float* site_dl(int s) const { return f(lay.dl) + (size_t)s * lay.site_stride; }
+  float* site_dl(int s) const { return f(lay.dl) + (size_t)s * lay.dl_stride; }
   float* site_radial(int s) const { return f(lay.radial) + (size_t)s * lay.rad_stride; }
   float* site_lse(int s) const { return f(lay.lse) + (size_t)s * cfg.tokens * cfg.heads; }
   QuerySet qset() const {
@@ -322,7 +333,7 @@ const char* attnres_last_error(void) { return g_error.c_str(); }
 
 size_t attnres_workspace_bytes(const attnres_config_t* cfg) {
   if (check_config(cfg) != ATTNRES_OK) return 0;
-  return make_layout(*cfg).total;
+  return make_layout(*cfg, coef_tile(make_site_geom(*cfg))).total;
 }
 
 attnres_status_t attnres_bank_create(const attnres_config_t* cfg, void* rows, float* drows,
@@ -335,7 +346,7 @@ attnres_status_t attnres_bank_create(const attnres_config_t* cfg, void* rows, fl
     return fail(ATTNRES_ERR_INVALID, "rows, drows, dout_rows and workspace must be non-NULL");
   if (!aligned16(rows) || !aligned16(drows) || !aligned16(dout_rows) || !aligned16(workspace))
     return fail(ATTNRES_ERR_INVALID, "device buffers must be 16-byte aligned");
-  const Layout lay = make_layout(*cfg);
+  const Layout lay = make_layout(*cfg, coef_tile(make_site_geom(*cfg)));
   if (workspace_bytes < lay.total)
     return fail(ATTNRES_ERR_CAPACITY, "workspace has %zu bytes, needs %zu", workspace_bytes, lay.total);
   static const int kMainCpts[] = {4, 5, 8, 7, 2};
@@ -349,6 +360,17 @@ attnres_status_t attnres_bank_create(const attnres_config_t* cfg, void* rows, fl
   if (b->g_main.tt < 1 || b->g_fin.tt < 1 || b->g_site.tt < 1) {
     delete b;
     return fail(ATTNRES_ERR_UNSUPPORTED, "row of %d chunks is too wide for one tile", cfg->d);
+  }
+  {
+    const int n_src = cfg->max_rows + 1;
+    const size_t fwd = attnres::lds_fwd(b->g_main, n_src), site = attnres::lds_bwd_site(b->g_site, n_src);
+    if (fwd > attnres::kMaxLds || site > attnres::kMaxLds) {
+      delete b;
+      return fail(ATTNRES_ERR_UNSUPPORTED,
+                  "a read of max_rows + 1 = %d sources needs %zu (forward) and %zu (backward) bytes of "
+                  "LDS per work-group, above %zu",
+                  n_src, fwd, site, attnres::kMaxLds);
+    }
   }
   b->lay = lay;
   b->rows = static_cast<char*>(rows);
@@ -624,7 +646,10 @@ attnres_status_t attnres_route_bwd(attnres_bank_t b, int32_t site, const void* e
   sa.radial = b->f(b->lay.radial);
   sa.lse = b->f(b->lay.lse);
   sa.site_stride = b->lay.site_stride;
+  sa.dl_stride = b->lay.dl_stride;
   sa.rad_stride = b->lay.rad_stride;
+  sa.ts = b->lay.ts;
+  sa.nslot = c.max_rows + 1;
   sa.th_stride = c.tokens * (int64_t)c.heads;
   TraceScope tf(b, ATTNRES_KERNEL_FINALIZE, st);
   hipError_t e = attnres::launch_finalize(b->g_fin, c.dtype, jobs.data(), (int)jobs.size(), sa,

@@ -28,6 +28,7 @@ struct Geom {
   int32_t wave_tokens;  // backward site pass: tokens owned by each wave (0: work-group-wide layout)
   int32_t rms_full;  // 1: the inverse RMS is over all d coordinates (key still the last r)
   int32_t rms_w;     // divisor of the mean of squares: d if rms_full, else r
+  int32_t nslot;     // source slots per site in the backward coefficients: max_rows + 1
   float eps;
 };
 
@@ -45,20 +46,35 @@ struct QuerySet {
 // Per-site saved state lives in site-major slots of the workspace:
 //   proj          : [site][max_rows + 1][H][T]  raw per-head key projections
 //                   q_h . key_[h] (the logit is this times the inverse RMS)
-//   alpha / dl    : [site][max_rows + 1][T][H]  softmax weights, a (P - S)
-//   radial        : [site][max_rows + 1][T]     sum_h dl_h * logit_h
+//   alpha         : [site][max_rows + 1][T][H]  softmax weights
+//   dl            : [site][tile][max_rows + 1][ts][H]  a (P - S), tile-major
+//   radial        : [site][tile][max_rows + 1][ts]     sum_h dl_h * logit_h
 //   lse           : [site][T][H]
 // Source index n of a site is bank row n, index nsrc[site] its transient source.
+// dl and radial are tile-major so that the coefficients that one wave (or,
+// in the work-group-wide site pass, one work-group) of the backward site
+// pass produces for its ts tokens form one contiguous block; tokens past T
+// in the last tile are padding.
 struct SiteArrays {
   float* proj;
   float* alpha;
   float* dl;
   float* radial;
   float* lse;
-  int64_t site_stride;  // floats between consecutive sites of proj / alpha / dl
-  int64_t rad_stride;   // floats between consecutive sites of radial = (max_rows + 1) * T
+  int64_t site_stride;  // floats between consecutive sites of proj / alpha
+  int64_t dl_stride;    // floats between consecutive sites of dl
+  int64_t rad_stride;   // floats between consecutive sites of radial
   int64_t th_stride;    // floats between consecutive sites of lse = T * H
+  int32_t ts;           // tokens per tile of dl / radial
+  int32_t nslot;        // source slots per site: max_rows + 1
 };
+
+// Position of (token t, source slot) in a site's tile-major dl / radial
+// array, in units of one token's entry (H floats for dl, 1 for radial).
+__host__ __device__ inline int64_t coef_at(int64_t t, int slot, int nslot, int ts) {
+  const int64_t tile = t / ts;
+  return (tile * nslot + slot) * ts + (t - tile * ts);
+}
 
 hipError_t launch_score(const Geom& g, int dtype, const void* x, const QuerySet& qs, int s_lo,
                         int s_hi, int slot, float* rinv_out, float* proj,
@@ -187,6 +203,12 @@ hipError_t launch_probe_read(const void* src, size_t bytes, uint32_t* sink, hipS
 hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
 
 // Dynamic LDS bytes of each kernel (host-side checks before launch).
+// LDS one work-group may allocate on gfx950, and the smaller budget that
+// tile and batch sizes are chosen for (leaving room for a second work-group
+// per compute unit).  A read's forward and site-pass LDS grows with its
+// source count; a bank whose max_rows + 1 sources exceed kMaxLds is refused.
+constexpr size_t kMaxLds = 160 * 1024;
+constexpr size_t kLdsBudget = 64 * 1024;
 size_t lds_fwd(const Geom& g, int n_src);
 size_t lds_bwd_site(const Geom& g, int n_src);
 size_t lds_finalize(const Geom& g, int n_sites);

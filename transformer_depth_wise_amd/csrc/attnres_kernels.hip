@@ -889,7 +889,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
       const int n = i / g.tt, tau = i - n * g.tt;
       if (tau >= tv) continue;
       const int base = n * pairs + tau * g.H;
-      float* dst = dl_out + ((int64_t)n * g.T + t0 + tau) * g.H;
+      const int64_t at = coef_at(t0 + tau, n, g.nslot, g.tt);
+      float* dst = dl_out + at * g.H;
       float c = 0.f;
       for (int h = 0; h < g.H; ++h) {
         const float a = s_alpha[base + h];
@@ -898,7 +899,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
         c += dl * lg;
         st_stream(dst + h, dl);
       }
-      st_stream(rad_out + (int64_t)n * g.T + t0 + tau, c);
+      st_stream(rad_out + at, c);
     }
     __syncthreads();
   }
@@ -951,13 +952,15 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site_w(
   const int pw = tw * g.H;  // (token, head) pairs of this wave, <= 64
   const bool quad = (g.kvc & 3) == 0;
   const int part_len = quad ? (tw * g.cpr) >> 2 : tw * g.cpr;
-  const int fw = 2 * n_src * pw + n_src * tw + part_len + 2 * pw;
+  // per-wave floats, a multiple of 4 so that 16-byte LDS accesses stay aligned
+  const int fw = (2 * n_src * pw + 2 * n_src * tw + part_len + 2 * pw + 3) & ~3;
   float* w_alpha = sm + wave * fw;      // [n_src][tw][H]
-  float* w_P = w_alpha + n_src * pw;    // [n_src][tw][H]
+  float* w_P = w_alpha + n_src * pw;    // [n_src][tw][H]; at the tile's end dl
   float* w_rinv = w_P + n_src * pw;     // [n_src][tw]
   float* w_part = w_rinv + n_src * tw;  // quad (or chunk) partial dots
   float* w_S = w_part + part_len;       // [tw][H]
   float* w_lse = w_S + pw;              // [tw][H]
+  float* w_c = w_lse + pw;              // [n_src][tw] radial sums
 
   int tau[CPT], hv[CPT], hk[CPT], kc[CPT], q[CPT];
   bool key[CPT];
@@ -1090,33 +1093,36 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site_w(
 #pragma unroll
       for (int e = 0; e < N; ++e) dq[j][e] -= sv * W[j][e];
     }
-    // coefficients of the finalize gather, 16-byte stores when H % 4 == 0
+    // coefficients of the finalize gather: dl (over P) and the radial sums
+    // in LDS first, then stored as this wave's one contiguous block of the
+    // tile-major arrays (tiles of tw tokens: [slot][tw][H] and [slot][tw])
     for (int i = lane; i < n_src * tw; i += 64) {
       const int n = i / tw, t = i - n * tw;
       if (t >= tv) continue;
       const int base = n * pw + t * g.H;
-      float* dst = dl_out + ((int64_t)n * g.T + t0 + t) * g.H;
       float c = 0.f;
-      for (int h0 = 0; h0 < g.H; h0 += 4) {
-        float dv[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int h = h0 + u;
-          dv[u] = 0.f;
-          if (h < g.H) {
-            const float a = w_alpha[base + h];
-            dv[u] = a * (w_P[base + h] - w_S[t * g.H + h]);
-            const float lg = a > 0.f ? logf(a) + w_lse[t * g.H + h] : 0.f;
-            c += dv[u] * lg;
-          }
-        }
-        if ((g.H & 3) == 0) {
-          st_stream(dst + h0, make_float4(dv[0], dv[1], dv[2], dv[3]));
-        } else {
-          for (int u = 0; u < 4 && h0 + u < g.H; ++u) st_stream(dst + h0 + u, dv[u]);
-        }
+      for (int h = 0; h < g.H; ++h) {
+        const float a = w_alpha[base + h];
+        const float dl = a * (w_P[base + h] - w_S[t * g.H + h]);
+        const float lg = a > 0.f ? logf(a) + w_lse[t * g.H + h] : 0.f;
+        c += dl * lg;
+        w_P[base + h] = dl;
       }
-      st_stream(rad_out + (int64_t)n * g.T + t0 + t, c);
+      w_c[i] = c;
+    }
+    wave_lds_fence();
+    // Tokens t >= tv of the block are padding past T (stale values, never read);
+    // a wave with no token has no block.
+    if (tv > 0) {
+      const int64_t at = coef_at(t0, 0, g.nslot, tw);
+      float* dst = dl_out + at * g.H;
+      if ((pw & 3) == 0) {
+        for (int i = lane; i < n_src * (pw >> 2); i += 64)
+          st_stream(dst + 4 * i, *reinterpret_cast<const float4*>(w_P + 4 * i));
+      } else {
+        for (int i = lane; i < n_src * pw; i += 64) st_stream(dst + i, w_P[i]);
+      }
+      for (int i = lane; i < n_src * tw; i += 64) st_stream(rad_out + at + i, w_c[i]);
     }
     wave_lds_fence();
   }
@@ -1265,8 +1271,10 @@ __global__ __launch_bounds__(kThreads) void k_finalize(Geom g, FinalizeArgs fa, 
         if (tau < tv) {
           const int64_t idx =
               (int64_t)(b0 + k) * sa.site_stride + ((int64_t)job.slot * g.T + t0) * g.H + 4 * r;
+          const int64_t ldl = (int64_t)(b0 + k) * sa.dl_stride +
+                              coef_at(t0 + tau, job.slot, sa.nslot, sa.ts) * g.H + 4 * r - tau * g.H;
           a = *reinterpret_cast<const float4*>(sa.alpha + idx);
-          const float4 dl = *reinterpret_cast<const float4*>(sa.dl + idx);
+          const float4 dl = *reinterpret_cast<const float4*>(sa.dl + ldl);
           const float ri = job.rinv[t0 + tau];
           q = make_float4(ri * dl.x, ri * dl.y, ri * dl.z, ri * dl.w);
         }
@@ -1281,8 +1289,10 @@ __global__ __launch_bounds__(kThreads) void k_finalize(Geom g, FinalizeArgs fa, 
         if (tau < tv) {
           const int64_t idx =
               (int64_t)(b0 + k) * sa.site_stride + ((int64_t)job.slot * g.T + t0) * g.H + p;
+          const int64_t ldl = (int64_t)(b0 + k) * sa.dl_stride +
+                              coef_at(t0 + tau, job.slot, sa.nslot, sa.ts) * g.H + p - tau * g.H;
           a = sa.alpha[idx];
-          q = job.rinv[t0 + tau] * sa.dl[idx];
+          q = job.rinv[t0 + tau] * sa.dl[ldl];
         }
         cA[i] = a;
         cQ[i] = q;
@@ -1293,7 +1303,7 @@ __global__ __launch_bounds__(kThreads) void k_finalize(Geom g, FinalizeArgs fa, 
     for (int i = tid; i < nb * g.tt; i += kThreads) {
       const int k = i / g.tt, tau = i - k * g.tt;
       s_radb[i] = tau < tv ? sa.radial[(int64_t)(b0 + k) * sa.rad_stride +
-                                       (int64_t)job.slot * g.T + t0 + tau]
+                                       coef_at(t0 + tau, job.slot, sa.nslot, sa.ts)]
                            : 0.f;
     }
     __syncthreads();
@@ -1448,8 +1458,10 @@ __global__ __launch_bounds__(kThreads) void k_finalize_cols(Geom g, FinalizeArgs
       if (tau < tv) {
         const int64_t idx =
             (int64_t)(b0 + k) * sa.site_stride + ((int64_t)job.slot * g.T + t0) * g.H + p;
+        const int64_t ldl = (int64_t)(b0 + k) * sa.dl_stride +
+                            coef_at(t0 + tau, job.slot, sa.nslot, sa.ts) * g.H + p - tau * g.H;
         a = sa.alpha[idx];
-        q = job.rinv[t0 + tau] * sa.dl[idx];
+        q = job.rinv[t0 + tau] * sa.dl[ldl];
       }
       cA[i] = a;
       cQ[i] = q;
@@ -1457,7 +1469,7 @@ __global__ __launch_bounds__(kThreads) void k_finalize_cols(Geom g, FinalizeArgs
     for (int i = tid; i < nb * TT; i += kThreads) {
       const int k = i / TT, tau = i - k * TT;
       s_radb[i] = tau < tv ? sa.radial[(int64_t)(b0 + k) * sa.rad_stride +
-                                       (int64_t)job.slot * g.T + t0 + tau]
+                                       coef_at(t0 + tau, job.slot, sa.nslot, sa.ts)]
                            : 0.f;
     }
     __syncthreads();
@@ -1629,11 +1641,9 @@ __global__ __launch_bounds__(kThreads) void k_fold_gains(const T* __restrict__ q
   }
 }
 
-constexpr size_t kMaxLds = 64 * 1024;
-
 int finalize_batch(const Geom& g) {
   const int pairs = g.tt * g.H;
-  int b = (int)((kMaxLds / sizeof(float) - g.tt) / (2 * (size_t)pairs + g.tt));
+  int b = (int)((kLdsBudget / sizeof(float) - g.tt) / (2 * (size_t)pairs + g.tt));
   return b < 1 ? 1 : b;
 }
 
@@ -1644,7 +1654,7 @@ int finalize_batch(const Geom& g) {
 // fp32 key coordinates fit the LDS budget.
 int score_tile(const Geom& g) {
   for (int t = 8; t > 1; t >>= 1)
-    if (sizeof(float) * ((size_t)t * g.r + t) <= kMaxLds) return t;
+    if (sizeof(float) * ((size_t)t * g.r + t) <= kLdsBudget) return t;
   return 1;
 }
 size_t lds_score(const Geom& g) {
@@ -1656,7 +1666,7 @@ size_t lds_bwd_site(const Geom& g, int n_src) {
   if (g.wave_tokens > 0) {
     const size_t tw = g.wave_tokens, pw = tw * g.H;
     const size_t part = (g.kvc % 4 == 0) ? tw * g.cpr / 4 : tw * g.cpr;
-    const size_t fw = 2 * (size_t)n_src * pw + (size_t)n_src * tw + part + 2 * pw;
+    const size_t fw = (2 * (size_t)n_src * pw + 2 * (size_t)n_src * tw + part + 2 * pw + 3) & ~(size_t)3;
     const size_t a = 4 * fw, b = (size_t)g.tt * g.r;
     return sizeof(float) * (a > b ? a : b);
   }
