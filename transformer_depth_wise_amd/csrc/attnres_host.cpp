@@ -6,6 +6,7 @@
 #include <stdio.h>
 
 #include <string>
+#include <algorithm>
 #include <initializer_list>
 #include <vector>
 
@@ -39,8 +40,19 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Finalize look-ahead: when a backward call finalizes rows with none of them
+// holding a partial sum, the same launch also sums, for up to kFinAhead of
+// the rows below (finalized by later calls), the sites that this call's rows
+// read, and stores those sums as partials: the launch's jobs run over the
+// same sites, tile by tile on one XCD, so each upstream-gradient tile is read
+// from HBM once for all of them.  Only worth it over at least
+// kFinAheadMinSites sites (a partial costs a float32 row written and read).
+constexpr int kFinAhead = 7;
+constexpr int kFinAheadMinSites = 8;
+
 struct Layout {
   size_t rinv, rinvx, proj, alpha, dl, radial, lse, dqpart;
+  size_t part, part_rad;  // finalize partial sums: [kFinAhead][T][d], [kFinAhead][T]
   size_t qf, q32, qhi, qlo;  // effective queries with gains ([max_sites, r] each)
   size_t total;
   int64_t site_stride;  // floats per site of proj / alpha: (max_rows + 1) * T * H
@@ -72,6 +84,9 @@ Layout make_layout(const attnres_config_t& c, int ts) {
   L.radial = take(srcs * tp * c.max_sites);
   L.lse = take((size_t)c.max_sites * T * c.heads);
   L.dqpart = take((size_t)dq_parts_cap() * c.r);
+  const size_t ahead = c.max_rows > 1 ? kFinAhead : 0;
+  L.part = take(ahead * T * c.d);
+  L.part_rad = take(ahead * T);
   const size_t sr = (size_t)c.max_sites * c.r;
   L.qf = take(sr);
   L.q32 = take(sr);
@@ -203,6 +218,9 @@ struct attnres_bank_s {
   bool bwd_done;  // backward of site 0 has run: only reset is allowed
   std::vector<const void*> extra_ptr;
   const void* partial;  // running block partial sum (caller memory), NULL between blocks
+  // finalize look-ahead: per bank row, the site from which on a stored partial
+  // sum covers its gradient (-1: none) and that partial's buffer
+  std::vector<int> part_site, part_idx;
   // launch trace
   struct TraceRec {
     int kind;
@@ -222,6 +240,8 @@ struct attnres_bank_s {
   float* site_dl(int s) const { return f(lay.dl) + (size_t)s * lay.dl_stride; }
   float* site_radial(int s) const { return f(lay.radial) + (size_t)s * lay.rad_stride; }
   float* site_lse(int s) const { return f(lay.lse) + (size_t)s * cfg.tokens * cfg.heads; }
+  float* part_buf(int i) const { return f(lay.part) + (size_t)i * cfg.tokens * cfg.d; }
+  float* part_rad(int i) const { return f(lay.part_rad) + (size_t)i * cfg.tokens; }
   QuerySet qset() const {
     QuerySet q{queries, nullptr, nullptr, nullptr};
     if (gains) {
@@ -246,6 +266,8 @@ struct attnres_bank_s {
     bwd_done = false;
     extra_ptr.clear();
     partial = nullptr;
+    part_site.assign(cfg.max_rows, -1);
+    part_idx.assign(cfg.max_rows, 0);
   }
 };
 
@@ -350,7 +372,9 @@ attnres_status_t attnres_bank_create(const attnres_config_t* cfg, void* rows, fl
   if (workspace_bytes < lay.total)
     return fail(ATTNRES_ERR_CAPACITY, "workspace has %zu bytes, needs %zu", workspace_bytes, lay.total);
   static const int kMainCpts[] = {4, 5, 8, 7, 2};
-  static const int kFinCpts[] = {4, 5, 2};
+  // ties go to the first: 2 chunks per thread (more work-groups in flight) where it
+  // fits the row as well as 4 or 5
+  static const int kFinCpts[] = {2, 4, 5};
   attnres_bank_s* b = new (std::nothrow) attnres_bank_s();
   if (!b) return fail(ATTNRES_ERR_CAPACITY, "host allocation of the handle failed");
   b->cfg = *cfg;
@@ -616,8 +640,10 @@ attnres_status_t attnres_route_bwd(attnres_bank_t b, int32_t site, const void* e
     if (e != hipSuccess) return hip_fail(e, "route_bwd dq reduction");
   }
   // Rows first read by this site are final once every later site has run.
+  // A row with a stored partial sums only the sites below the partial's.
   std::vector<FinalizeJob> jobs;
   const int lo = site > 0 ? b->nsrc[site - 1] : 0;
+  bool any_partial = false;
   for (int n = lo; n < n_rows; ++n) {
     FinalizeJob j{};
     j.x = b->row_ptr(n);
@@ -626,7 +652,37 @@ attnres_status_t attnres_route_bwd(attnres_bank_t b, int32_t site, const void* e
     j.slot = n;
     j.s0 = site;
     j.s1 = b->n_sites;
+    if (b->part_site[n] >= 0) {
+      j.s1 = b->part_site[n];
+      j.in = b->part_buf(b->part_idx[n]);
+      j.in_rad = b->part_rad(b->part_idx[n]);
+      b->part_site[n] = -1;
+      any_partial = true;
+    }
     jobs.push_back(j);
+  }
+  // Look-ahead partials for the rows just below: every site from this one on
+  // reads them (nsrc is non-decreasing), and none of them holds a partial:
+  // the previous look-ahead's rows lie above this call's rows (which hold
+  // none), all finalized already.
+  const int n_ahead = std::min({kFinAhead, lo, attnres::kMaxJobs - (int)jobs.size() - (extra ? 1 : 0)});
+  if (lo < n_rows && !any_partial && c.tokens > 0 && b->n_sites - site >= kFinAheadMinSites &&
+      n_ahead > 0) {
+    for (int i = 0; i < n_ahead; ++i) {
+      const int m = lo - n_ahead + i;
+      FinalizeJob j{};
+      j.x = b->row_ptr(m);
+      j.rinv = b->rinv(m);
+      j.dst = b->part_buf(i);
+      j.dst_rad = b->part_rad(i);
+      j.slot = m;
+      j.s0 = site;
+      j.s1 = b->n_sites;
+      j.partial_out = 1;
+      jobs.push_back(j);
+      b->part_site[m] = site;
+      b->part_idx[m] = i;
+    }
   }
   if (extra) {
     FinalizeJob j{};

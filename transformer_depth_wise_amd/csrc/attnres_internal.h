@@ -111,11 +111,19 @@ hipError_t launch_dq_reduce(const float* dq_part, int parts, int r, float* dq, c
 struct FinalizeJob {
   const void* x;        // the source [T, d]
   const float* rinv;    // its inverse RMS [T]
-  float* dst;           // its gradient [T, d] float32
+  float* dst;           // its gradient [T, d] float32, or (partial_out) the partial sum
+  float* dst_rad;       // partial_out: the radial sums [T] of sites [s0, s1)
+  const float* in;      // NULL, or a partial sum [T, d] of later sites to add
+  const float* in_rad;  // with `in`: its radial sums [T]
   int32_t slot;         // its source index inside the per-site slots
   int32_t s0, s1;       // contributing sites
   int32_t accumulate;   // 1: add the gradient to dst instead of storing it
+  int32_t partial_out;  // 1: store the sums over sites [s0, s1) without the
+                        //    radial term (x is not read)
 };
+
+// Jobs per finalize launch (more are split over several launches).
+constexpr int kMaxJobs = 8;
 
 hipError_t launch_finalize(const Geom& g, int dtype, const FinalizeJob* jobs, int njobs,
                            const SiteArrays& sa, const void* dout_rows, int64_t dout_stride,

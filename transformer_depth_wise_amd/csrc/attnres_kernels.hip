@@ -550,9 +550,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_score_wide(Geom g, const bf16_t*
 // Forward of one site: softmax over the cached logits of the tile's
 // (token, head) pairs, then out = sum_n alpha_n * s_n per head slice.
 // Grid: ceil(T / tt) work-groups.  Source n < n_rows is bank row n, source
-// n_rows (if extra) the transient source.  The first two sources are
-// requested before the softmax prologue so that their loads overlap it; the
-// stream then keeps three sources in flight.
+// n_rows (if extra) the transient source.  The row loop keeps DEPTH sources
+// in flight (DEPTH - 1 prefetched ahead of the one being mixed); the first
+// DEPTH - 1 are requested before the softmax prologue so that their loads
+// overlap it.  Three in flight measured faster for tiles of up to 5 chunks
+// per thread, two above that (where the third costs occupancy).
 template <typename T, int CPT>
 __global__ __launch_bounds__(kThreads) void k_fwd(Geom g, const T* __restrict__ rows,
                                                    int64_t row_stride, const T* __restrict__ extra,
@@ -563,7 +565,7 @@ __global__ __launch_bounds__(kThreads) void k_fwd(Geom g, const T* __restrict__ 
                                                    float* __restrict__ lse, T* __restrict__ out) {
   using V = Vec<T>;
   constexpr int N = V::N;
-  constexpr int DEPTH = 2;  // sources in flight (the next one prefetched)
+  constexpr int DEPTH = CPT <= 5 ? 3 : 2;  // sources in flight
   extern __shared__ float sa[];  // [n_src][tt][H]: logits, then softmax weights
   const int n_src = n_rows + (extra != nullptr ? 1 : 0);
   const int tid = threadIdx.x;
@@ -945,6 +947,9 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site_w(
     float* __restrict__ dq_part) {
   using V = Vec<T>;
   constexpr int N = V::N;
+  // sources in flight: three measured faster with up to 4 chunks per thread;
+  // with 5 the third buffer spills registers
+  constexpr int SD = CPT <= 4 ? 3 : 2;
   extern __shared__ float sm[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n_src = n_rows + (extra != nullptr ? 1 : 0);
@@ -993,7 +998,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site_w(
     // Chunks of tokens past the end load chunk 0 at tb (valid memory); their
     // weights are zero and their results are never stored.
     int qa[CPT];
-    uint4 dov[CPT], buf[2][CPT];
+    uint4 dov[CPT], buf[SD][CPT];
     {
       const uint4* dp = reinterpret_cast<const uint4*>(dout + tb * g.d);
       const uint4* sp = tile_of(0);
@@ -1002,6 +1007,14 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site_w(
         qa[j] = tau[j] < tv ? q[j] : 0;
         dov[j] = ld_stream(dp + qa[j]);
         buf[0][j] = ld_stream(sp + qa[j]);
+      }
+#pragma unroll
+      for (int d = 1; d < SD - 1; ++d) {
+        if (d < n_src) {
+          const uint4* sd = tile_of(d);
+#pragma unroll
+          for (int j = 0; j < CPT; ++j) buf[d][j] = ld_stream(sd + qa[j]);
+        }
       }
     }
     if ((g.H & 3) == 0) {  // 16-byte words, each within one token
@@ -1036,15 +1049,15 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site_w(
     float S_acc = 0.f;
     wave_lds_fence();
 
-    for (int i = 0; i < n_src; i += 2) {
+    for (int i = 0; i < n_src; i += SD) {
 #pragma unroll
-      for (int d = 0; d < 2; ++d) {
+      for (int d = 0; d < SD; ++d) {
         const int n = i + d;
         if (n >= n_src) break;
-        if (n + 1 < n_src) {
-          const uint4* sp = tile_of(n + 1);
+        if (n + SD - 1 < n_src) {
+          const uint4* sp = tile_of(n + SD - 1);
 #pragma unroll
-          for (int j = 0; j < CPT; ++j) buf[d ^ 1][j] = ld_stream(sp + qa[j]);
+          for (int j = 0; j < CPT; ++j) buf[(d + SD - 1) % SD][j] = ld_stream(sp + qa[j]);
         }
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
@@ -1194,13 +1207,45 @@ __global__ __launch_bounds__(kReduceThreads) void k_dq_reduce(const float* __res
 //           + [j in key] ( sum_s rho^-1 dl_{s,hk} q_s[j - (d - r)]
 //                          - rho^-2 / r * (sum_s c_s) key[j] )
 // with dl = a (P - S) and c_s = sum_h dl_{s,h} l_{s,h} from the site pass.
+// The sums are linear in the sites, so a job may cover only sites [s0, s1)
+// and add a stored partial sum of the later sites (`in`, `in_rad`), or store
+// its own sums as such a partial (`partial_out`).
 // Sites are processed in batches whose coefficients fit in LDS; each batch's
 // first upstream-gradient tile is requested before its coefficients.
 // Grid: (ceil(T / tt), jobs).
-constexpr int kMaxJobs = 8;
 struct FinalizeArgs {
   FinalizeJob job[kMaxJobs];
 };
+
+// Coefficient of the radial term of token tau of the tile (thread tau):
+// rho^-2 / w times the radial sums of the job's sites plus those of a
+// stored partial.  A partial job stores its radial sums instead (and no
+// radial term is applied to it).
+__device__ __forceinline__ float finalize_radial(const Geom& g, const FinalizeJob& job, int64_t t0,
+                                                 int tau, int tv, float rad) {
+  if (tau >= tv) return 0.f;
+  if (job.in_rad) rad += job.in_rad[t0 + tau];
+  if (job.partial_out) {
+    job.dst_rad[t0 + tau] = rad;
+    return 0.f;
+  }
+  const float ri = job.rinv[t0 + tau];
+  return ri * ri / (float)g.rms_w * rad;
+}
+
+// acc += the N float32 values at p (16-byte aligned)
+template <int N>
+__device__ __forceinline__ void add_partial(float (&acc)[N], const float* p) {
+  const float4* q = reinterpret_cast<const float4*>(p);
+#pragma unroll
+  for (int e = 0; e < N / 4; ++e) {
+    const float4 v = q[e];
+    acc[4 * e] += v.x;
+    acc[4 * e + 1] += v.y;
+    acc[4 * e + 2] += v.z;
+    acc[4 * e + 3] += v.w;
+  }
+}
 
 template <typename T, int CPT, typename QT>
 __global__ __launch_bounds__(kThreads) void k_finalize(Geom g, FinalizeArgs fa, SiteArrays sa,
@@ -1210,10 +1255,12 @@ __global__ __launch_bounds__(kThreads) void k_finalize(Geom g, FinalizeArgs fa, 
   using V = Vec<T>;
   constexpr int N = V::N;
   extern __shared__ float sm[];
+  // The jobs of one token tile are consecutive work-groups of one XCD, so
+  // jobs over the same sites share the upstream-gradient reads in its L2.
   const int64_t lin = xcd_order((int64_t)blockIdx.y * gridDim.x + blockIdx.x,
                                 (int64_t)gridDim.x * gridDim.y);
-  const int64_t tile = lin % gridDim.x;
-  const FinalizeJob job = fa.job[lin / gridDim.x];
+  const int64_t tile = lin / gridDim.y;
+  const FinalizeJob job = fa.job[lin % gridDim.y];
   const int pairs = g.tt * g.H;
   float* cA = sm;                     // [batch][tt][H]  alpha
   float* cQ = cA + batch * pairs;     // [batch][tt][H]  rho^-1 * dl
@@ -1345,10 +1392,7 @@ __global__ __launch_bounds__(kThreads) void k_finalize(Geom g, FinalizeArgs fa, 
     }
     __syncthreads();
   }
-  if (tid < g.tt) {
-    const float ri = (tid < tv) ? job.rinv[t0 + tid] : 0.f;
-    s_rad[tid] = ri * ri / (float)g.rms_w * rad;
-  }
+  if (tid < g.tt) s_rad[tid] = finalize_radial(g, job, t0, tid, tv, rad);
   __syncthreads();
 
   const uint4* xp = reinterpret_cast<const uint4*>(static_cast<const T*>(job.x) + t0 * g.d);
@@ -1356,7 +1400,8 @@ __global__ __launch_bounds__(kThreads) void k_finalize(Geom g, FinalizeArgs fa, 
 #pragma unroll
   for (int j = 0; j < CPT; ++j) {
     if (!ok[j]) continue;
-    if (sl[j].key || g.rms_full) {  // radial term: key coordinates, or all of them
+    if (job.in) add_partial<N>(acc[j], job.in + t0 * g.d + (int64_t)sl[j].q * N);
+    if (!job.partial_out && (sl[j].key || g.rms_full)) {  // radial term: key coordinates, or all
       const float rc = s_rad[sl[j].tau];
       float f[N];
       V::unpack(xp[sl[j].q], f);
@@ -1404,10 +1449,11 @@ __global__ __launch_bounds__(kThreads) void k_finalize_cols(Geom g, FinalizeArgs
   constexpr int TT = kColTokens;
   extern __shared__ float sm[];
   const int ncb = g.cpr / kColBlock;
+  // jobs fastest, as in k_finalize
   const int64_t lin = xcd_order((int64_t)blockIdx.y * gridDim.x + blockIdx.x,
                                 (int64_t)gridDim.x * gridDim.y);
-  const int64_t rem = lin % gridDim.x;
-  const FinalizeJob job = fa.job[lin / gridDim.x];
+  const int64_t rem = lin / gridDim.y;
+  const FinalizeJob job = fa.job[lin % gridDim.y];
   const int64_t tile = rem / ncb;
   const int cb = (int)(rem - tile * ncb);
   const int pairs = TT * g.H;
@@ -1506,10 +1552,7 @@ __global__ __launch_bounds__(kThreads) void k_finalize_cols(Geom g, FinalizeArgs
     }
     __syncthreads();
   }
-  if (tid < TT) {
-    const float ri = (tid < tv) ? job.rinv[t0 + tid] : 0.f;
-    s_rad[tid] = ri * ri / (float)g.rms_w * rad;
-  }
+  if (tid < TT) s_rad[tid] = finalize_radial(g, job, t0, tid, tv, rad);
   __syncthreads();
 
   const uint4* xp = reinterpret_cast<const uint4*>(static_cast<const T*>(job.x) + t0 * g.d);
@@ -1517,7 +1560,8 @@ __global__ __launch_bounds__(kThreads) void k_finalize_cols(Geom g, FinalizeArgs
 #pragma unroll
   for (int t = 0; t < kColTh; ++t) {
     if (tau0 + t >= tv) continue;
-    if (key || g.rms_full) {  // radial term: key coordinates, or all of them
+    if (job.in) add_partial<N>(acc[t], job.in + t0 * g.d + off[t] * N);
+    if (!job.partial_out && (key || g.rms_full)) {  // radial term: key coordinates, or all
       const float rc = s_rad[tau0 + t];
       float f[N];
       V::unpack(xp[off[t]], f);
