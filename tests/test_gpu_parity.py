@@ -56,6 +56,14 @@ def _workload(name):
         from synth import Workload, full_schedule
         nsrc, extra = full_schedule(2)
         w = Workload("mhar_d4096", 21, 4096, 8, 4096, nsrc, extra, "bf16", True)
+    elif base == "uneven":
+        # rows first read several at a time and sites that add no row, with
+        # and without a transient source: look-ahead partial sums in the
+        # finalize meet calls that finalize several rows, some with partials
+        from synth import Workload
+        nsrc = (1, 1, 2, 4, 4, 5, 8, 9, 9, 10, 12, 12, 13, 14, 16, 16, 17, 18, 20, 21)
+        extra = (0, 1, 0, 1, 0, 0, 1, 0, 0, 1, 0, 1, 1, 0, 0, 0, 1, 0, 0, 1)
+        w = Workload("uneven", 29, 256, 4, 256, nsrc, extra, "bf16", True)
     elif base == "mhar_deep":
         # 1B width, 75 layers: 151 sites reading up to 151 sources, so a read
         # keeps more than 64 KiB of per-source state per work-group
@@ -69,7 +77,8 @@ def _workload(name):
     return w
 
 
-WIDE = ["lr_f32_d2048", "lr_f32_d2048+gain+fullrms", "mhar_d4096", "mhar_d4096+gain", "mhar_deep"]
+WIDE = ["lr_f32_d2048", "lr_f32_d2048+gain+fullrms", "mhar_d4096", "mhar_d4096+gain", "mhar_deep",
+        "uneven", "uneven+gain"]
 
 
 @pytest.mark.parametrize("name", REDUCED + ["bf16_kk24", "lr_tiny_f32"] + VARIANTS + WIDE)
