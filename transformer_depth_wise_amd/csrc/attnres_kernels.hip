@@ -306,13 +306,15 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// A work-group owns 16 tokens and its 4 waves split the heads (wave w takes
-// heads w, w+4, ...).  Per head a wave holds its A fragments (this lane's KS
-// 16-byte pieces of the key slice, from HBM), loaded one head ahead, and
-// loops over the 16-site blocks with a single accumulator per block; query
-// fragments are small and shared by every tile, so they come from L2.  The
-// per-wave sums of squares meet in LDS for the inverse RMS.  r/H = KS * 32.
-template <int KS>
+// A work-group owns 16 * TB tokens and its 4 waves split the heads (wave w
+// takes heads w, w+4, ...).  Per head a wave holds its A fragments (this
+// lane's KS 16-byte pieces of the key slice for each of its TB 16-token
+// blocks, from HBM), loaded one head ahead, and loops over the 16-site blocks
+// with one accumulator per token block: each query fragment (from L2, shared
+// by every tile) feeds TB products, so the query traffic per token falls with
+// TB.  The per-wave sums of squares meet in LDS for the inverse RMS.
+// r/H = KS * 32.
+template <int KS, int TB>
 __global__ __launch_bounds__(kThreads) void k_score_mfma(Geom g, const bf16_t* __restrict__ x,
                                                           const bf16_t* __restrict__ Q,
                                                           const bf16_t* __restrict__ Qlo, int s_lo,
@@ -320,96 +322,132 @@ __global__ __launch_bounds__(kThreads) void k_score_mfma(Geom g, const bf16_t* _
                                                           float* __restrict__ rinv_out,
                                                           float* __restrict__ proj,
                                                           int64_t site_stride) {
-  __shared__ float s_ss[kThreads / 64][16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int kWaves = kThreads / 64;
+  __shared__ float s_ss[kWaves][16 * TB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = lane & 15, kg = lane >> 4;
-  const int64_t tw = xcd_order(blockIdx.x, gridDim.x) * 16;  // first token of the work-group
-  const int64_t t = tw + row;                   // token of this lane's A row
-  const bool tok_ok = t < g.T;
-  const bf16_t* xr = x + (tok_ok ? t : 0) * g.d + (g.d - g.r);
+  const int64_t tw = xcd_order(blockIdx.x, gridDim.x) * (16 * TB);  // first token of the work-group
   const int ns = s_hi - s_lo;
   const int nsb = (ns + 15) / 16;
-  // lane (kg, row) of the accumulator holds tokens tw+4kg..+3 of site `row`
-  const int64_t tq = tw + kg * 4;
-  const bool vec = (g.T & 3) == 0 && tq + 3 < g.T;
-
-  auto fetch_a = [&](int h, uint4* a) {
-    const bf16_t* p = xr + h * g.kk + kg * 8;
+  int64_t t[TB];     // token of this lane's A row in block b
+  bool tok_ok[TB];
+  const bf16_t* xr[TB];
+  int64_t tq[TB];    // lane (kg, row) of block b's accumulator: tokens tq..tq+3 of site `row`
+  bool vec[TB];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      a[ks] = tok_ok ? ld_stream(reinterpret_cast<const uint4*>(p + ks * 32)) : zero4();
+  for (int b = 0; b < TB; ++b) {
+    t[b] = tw + 16 * b + row;
+    tok_ok[b] = t[b] < g.T;
+    xr[b] = x + (tok_ok[b] ? t[b] : 0) * g.d + (g.d - g.r);
+    tq[b] = tw + 16 * b + kg * 4;
+    vec[b] = (g.T & 3) == 0 && tq[b] + 3 < g.T;
+  }
+
+  auto fetch_a = [&](int h, uint4 (&a)[TB][KS]) {
+#pragma unroll
+    for (int b = 0; b < TB; ++b) {
+      const bf16_t* p = xr[b] + h * g.kk + kg * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        a[b][ks] = tok_ok[b] ? ld_stream(reinterpret_cast<const uint4*>(p + ks * 32)) : zero4();
+    }
   };
 
-  float ss = 0.f;
-  if (g.rms_full && tok_ok) {
-    // the non-key coordinates of the token row enter the mean of squares:
-    // the 16 lanes holding this row (4 k-groups x 4 waves) take every 16th chunk
-    const uint4* rp = reinterpret_cast<const uint4*>(x + t * g.d);
-    for (int c = wave * 4 + kg; c < g.key_c0; c += 16) {
-      float f[8];
-      Vec<bf16_t>::unpack(ld_stream(rp + c), f);
+  float ss[TB];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+  for (int b = 0; b < TB; ++b) {
+    ss[b] = 0.f;
+    if (g.rms_full && tok_ok[b]) {
+      // the non-key coordinates of the token row enter the mean of squares:
+      // the 16 lanes holding this row (4 k-groups x 4 waves) take every 16th chunk
+      const uint4* rp = reinterpret_cast<const uint4*>(x + t[b] * g.d);
+      for (int c = wave * 4 + kg; c < g.key_c0; c += 16) {
+        float f[8];
+        Vec<bf16_t>::unpack(ld_stream(rp + c), f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss[b] += f[e] * f[e];
+      }
     }
   }
-  uint4 a_cur[KS], a_nxt[KS];
+  uint4 a_cur[TB][KS], a_nxt[TB][KS];
   if (wave < g.H) fetch_a(wave, a_cur);
   for (int h = wave; h < g.H; h += kWaves) {
     if (h + kWaves < g.H) fetch_a(h + kWaves, a_nxt);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      float f[8];
-      Vec<bf16_t>::unpack(a_cur[ks], f);
+    for (int b = 0; b < TB; ++b)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
-    }
+      for (int ks = 0; ks < KS; ++ks) {
+        float f[8];
+        Vec<bf16_t>::unpack(a_cur[b][ks], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss[b] += f[e] * f[e];
+      }
     for (int sb = 0; sb < nsb; ++sb) {
       const int s = s_lo + sb * 16 + row;
       const bool s_ok = s < s_hi;
       const bf16_t* qp = Q + (int64_t)(s_ok ? s : s_lo) * g.r + h * g.kk + kg * 8;
-      uint4 b[KS];
+      uint4 bq[KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) b[ks] = *reinterpret_cast<const uint4*>(qp + ks * 32);
-      f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < KS; ++ks) bq[ks] = *reinterpret_cast<const uint4*>(qp + ks * 32);
+      f32x4_t acc[TB];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a_cur[ks]), as_bf16x8(b[ks]), acc,
-                                                      0, 0, 0);
+      for (int b = 0; b < TB; ++b) {
+        acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a_cur[b][ks]),
+                                                           as_bf16x8(bq[ks]), acc[b], 0, 0, 0);
+      }
       if (Qlo) {  // effective queries q * g as high + low bf16 parts
         const bf16_t* qlp = Qlo + (int64_t)(s_ok ? s : s_lo) * g.r + h * g.kk + kg * 8;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) b[ks] = *reinterpret_cast<const uint4*>(qlp + ks * 32);
+        for (int ks = 0; ks < KS; ++ks) bq[ks] = *reinterpret_cast<const uint4*>(qlp + ks * 32);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a_cur[ks]), as_bf16x8(b[ks]),
-                                                        acc, 0, 0, 0);
+        for (int b = 0; b < TB; ++b)
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a_cur[b][ks]),
+                                                             as_bf16x8(bq[ks]), acc[b], 0, 0, 0);
       }
       if (s_ok) {
-        // one 16-byte store into the token-fastest [slot][head][token] layout
-        float* dst = proj + (int64_t)s * site_stride + ((int64_t)slot * g.H + h) * g.T + tq;
-        if (vec) {
-          st_stream(dst, make_float4(acc[0], acc[1], acc[2], acc[3]));
-        } else {
+        // one 16-byte store per block into the token-fastest [slot][head][token] layout
+        float* base = proj + (int64_t)s * site_stride + ((int64_t)slot * g.H + h) * g.T;
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (tq + j < g.T) st_stream(dst + j, acc[j]);
+        for (int b = 0; b < TB; ++b) {
+          float* dst = base + tq[b];
+          if (vec[b]) {
+            st_stream(dst, make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]));
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (tq[b] + j < g.T) st_stream(dst + j, acc[b][j]);
+          }
         }
       }
     }
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) a_cur[ks] = a_nxt[ks];
-  }
-  // the four k-groups of this wave holding the token row, then the waves
-  ss += __shfl_xor(ss, 16, 64);
-  ss += __shfl_xor(ss, 32, 64);
-  if (kg == 0) s_ss[wave][row] = ss;
-  __syncthreads();
-  if (wave == 0 && kg == 0 && tok_ok) {
-    float tot = 0.f;
+    for (int b = 0; b < TB; ++b)
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) tot += s_ss[w][row];
-    st_stream(rinv_out + t, rsqrtf(tot / (float)g.rms_w + g.eps));
+      for (int ks = 0; ks < KS; ++ks) a_cur[b][ks] = a_nxt[b][ks];
+  }
+  // the four k-groups of this wave holding each token row, then the waves
+#pragma unroll
+  for (int b = 0; b < TB; ++b) {
+    float v = ss[b];
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    if (kg == 0) s_ss[wave][16 * b + row] = v;
+  }
+  __syncthreads();
+  if (wave == 0 && kg == 0) {
+#pragma unroll
+    for (int b = 0; b < TB; ++b) {
+      if (!tok_ok[b]) continue;
+      float tot = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) tot += s_ss[w][16 * b + row];
+      st_stream(rinv_out + t[b], rsqrtf(tot / (float)g.rms_w + g.eps));
+    }
   }
 }
 
@@ -1738,16 +1776,24 @@ hipError_t launch_score(const Geom& g, int dtype, const void* x, const QuerySet&
   if (g.T == 0) return hipSuccess;
   if (dtype != 0 && g.kk % 32 == 0 && g.kk <= 256) {
     const int ks = g.kk / 32;
-    const dim3 grid((unsigned)((g.T + 15) / 16));
+    // two 16-token blocks per work-group where that still gives every CU two
+    // (measured: 1B-shaped append 2.1 -> 1.7 ms per microbatch; with 8192
+    // tokens, one work-group per CU, it was slower)
+    const bool two = (g.T + 31) / 32 >= 512;
+    const dim3 grid((unsigned)(two ? (g.T + 31) / 32 : (g.T + 15) / 16));
     const bf16_t* xb = static_cast<const bf16_t*>(x);
     // with gains: high and low bf16 parts of q * g, two products per block
     const bf16_t* qb = qs.qf ? qs.qhi : static_cast<const bf16_t*>(qs.q);
     const bf16_t* ql = qs.qf ? qs.qlo : nullptr;
     switch (ks) {
-#define ATTNRES_SCORE_KS(K)                                                                      \
-  case K:                                                                                        \
-    hipLaunchKernelGGL(k_score_mfma<K>, grid, dim3(kThreads), 0, st, g, xb, qb, ql, s_lo, s_hi, \
-                       slot, rinv_out, proj, site_stride);                                       \
+#define ATTNRES_SCORE_KS(K)                                                                  \
+  case K:                                                                                    \
+    if (two)                                                                                 \
+      hipLaunchKernelGGL((k_score_mfma<K, 2>), grid, dim3(kThreads), 0, st, g, xb, qb, ql,   \
+                         s_lo, s_hi, slot, rinv_out, proj, site_stride);                     \
+    else                                                                                     \
+      hipLaunchKernelGGL((k_score_mfma<K, 1>), grid, dim3(kThreads), 0, st, g, xb, qb, ql,   \
+                         s_lo, s_hi, slot, rinv_out, proj, site_stride);                     \
     break;
       ATTNRES_SCORE_KS(1)
       ATTNRES_SCORE_KS(2)
