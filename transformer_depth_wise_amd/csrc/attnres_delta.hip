@@ -491,7 +491,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_bwd(DeltaGeom g, DeltaArgs 
       for (int t = 0; t < g.tw; ++t) s += red[((size_t)w * 64 * CPT + t * g.cpr + c) * N + e];
     dq_part[(int64_t)blockIdx.x * g.d + col] = s;
   }
-  if (has_null && threadIdx.x <= g.H) {
+  if (has_null && (int)threadIdx.x <= g.H) {
     const int h = threadIdx.x;  // h == H: the radial total
     float s = 0.f;
     for (int w = 0; w < kDWaves; ++w)
@@ -898,7 +898,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_bwd_s(DeltaGeom g, DeltaArg
     for (int s2 = 0; s2 < 2; ++s2) sacc += red[((size_t)(s2 * 2 + hf) * SPAN + q) * N + e];
     dq_part[(int64_t)blockIdx.x * g.d + col] = sacc;
   }
-  if (has_null && threadIdx.x <= g.H) {
+  if (has_null && (int)threadIdx.x <= g.H) {
     const int h = threadIdx.x;
     float sacc = 0.f;
     for (int s2 = 0; s2 < 2; ++s2) {
