@@ -168,6 +168,15 @@ __device__ __forceinline__ float dot_chunk<float>(const uint4& a, const uint4& b
          __uint_as_float(a.z) * __uint_as_float(b.z) + __uint_as_float(a.w) * __uint_as_float(b.w);
 }
 
+// Exchange point between the lanes of one wave through LDS.
+__device__ __forceinline__ void wave_lds_fence() {
+  // LDS operations of one wave execute in order; this only stops the
+  // compiler from moving LDS accesses across the exchange point.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
 // Position of one chunk slot of a thread inside a [tt x cpr] tile of chunks:
 // slot j of thread `tid` is chunk q = tid + j * kThreads, token q / cpr.
 struct Slot {
@@ -584,6 +593,85 @@ __global__ __launch_bounds__(64 * WAVES) void k_score_wide(Geom g, const bf16_t*
   }
 }
 
+// Append of a row that one site reads (a transient source, typically),
+// bf16 rows with wide key heads (r/H > 256): per token and head a plain dot
+// of the key slice with that site's query, and the inverse RMS.  The
+// matrix-core kernel would spend 15 of every 16 products on padding sites;
+// here one wave owns a token, its lanes take the key's 16-byte chunks
+// kScoreOneAhead at a time, the per-chunk dots meet in wave-private LDS and
+// each head's sum gets a group of lanes.  No work-group barrier, so a wave
+// past the last token simply exits.  QT: the query's type (float32 when
+// gains are folded in).  Grid: ceil(T / 4) work-groups.
+constexpr int kScoreOneAhead = 8;
+
+template <typename QT>
+__global__ __launch_bounds__(kThreads) void k_score_one(Geom g, const bf16_t* __restrict__ x,
+                                                         const QT* __restrict__ q, int site,
+                                                         int slot, float* __restrict__ rinv_out,
+                                                         float* __restrict__ proj,
+                                                         int64_t site_stride) {
+  using V = Vec<bf16_t>;
+  constexpr int N = V::N;
+  extern __shared__ float sm[];  // [waves][r / N] per-chunk dots
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nk = g.r / N;  // key chunks of a row
+  float* part = sm + (size_t)wave * nk;
+  const int64_t t = xcd_order(blockIdx.x, gridDim.x) * (kThreads / 64) + wave;
+  if (t >= g.T) return;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + t * g.d);
+  float ss = 0.f;
+  if (g.rms_full)  // the non-key coordinates enter the mean of squares
+    for (int c = lane; c < g.key_c0; c += 64) {
+      float f[N];
+      V::unpack(ld_stream(xr + c), f);
+#pragma unroll
+      for (int e = 0; e < N; ++e) ss += f[e] * f[e];
+    }
+  const uint4* xk = xr + g.key_c0;
+  for (int c0 = 0; c0 < nk; c0 += 64 * kScoreOneAhead) {
+    uint4 v[kScoreOneAhead];
+#pragma unroll
+    for (int u = 0; u < kScoreOneAhead; ++u) {
+      const int c = c0 + u * 64 + lane;
+      v[u] = c < nk ? ld_stream(xk + c) : zero4();
+    }
+#pragma unroll
+    for (int u = 0; u < kScoreOneAhead; ++u) {
+      const int c = c0 + u * 64 + lane;
+      if (c >= nk) break;
+      float f[N], qf[N];
+      V::unpack(v[u], f);
+      QChunk<bf16_t, QT> qc;
+      qc.load(q, c);
+      qc.unpack(qf);
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < N; ++e) {
+        ss += f[e] * f[e];
+        dot += f[e] * qf[e];
+      }
+      part[c] = dot;
+    }
+  }
+  wave_lds_fence();
+  // head sums: G lanes per head (G a power of two, G * H <= 64 when H <= 64)
+  int G = 64;
+  while (G > 1 && G * g.H > 64) G >>= 1;
+  const int hpp = 64 / G;  // heads per pass
+  float* dst = proj + (int64_t)site * site_stride + (int64_t)slot * g.H * g.T + t;
+  for (int h0 = 0; h0 < g.H; h0 += hpp) {
+    const int h = h0 + lane / G, li = lane % G;
+    float P = 0.f;
+    if (h < g.H)
+      for (int c = li; c < g.kkc; c += G) P += part[h * g.kkc + c];
+    for (int o = 1; o < G; o <<= 1) P += __shfl_xor(P, o, 64);
+    if (li == 0 && h < g.H) st_stream(dst + (int64_t)h * g.T, P);
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) ss += __shfl_xor(ss, o, 64);
+  if (lane == 0) st_stream(rinv_out + t, rsqrtf(ss / (float)g.rms_w + g.eps));
+}
+
 // ---------------------------------------------------------------------------
 // Forward of one site: softmax over the cached logits of the tile's
 // (token, head) pairs, then out = sum_n alpha_n * s_n per head slice.
@@ -968,14 +1056,6 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
 // inside the wave (DPP quads, then a wave-private LDS region), so the row
 // loop has no work-group barrier and the waves of a work-group stream
 // independently.  A work-group tile is 4 * tw tokens.
-__device__ __forceinline__ void wave_lds_fence() {
-  // LDS operations of one wave execute in order; this only stops the
-  // compiler from moving LDS accesses across the exchange point.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-}
-
 template <typename T, int CPT>
 __global__ __launch_bounds__(kThreads) void k_bwd_site_w(
     Geom g, const T* __restrict__ rows, int64_t row_stride, const T* __restrict__ extra,
@@ -1805,6 +1885,20 @@ hipError_t launch_score(const Geom& g, int dtype, const void* x, const QuerySet&
       ATTNRES_SCORE_KS(8)
 #undef ATTNRES_SCORE_KS
     }
+    return hipGetLastError();
+  }
+  if (dtype != 0 && g.kk > 256 && s_hi - s_lo == 1) {
+    const dim3 grid((unsigned)((g.T + kThreads / 64 - 1) / (kThreads / 64)));
+    const size_t lds = sizeof(float) * (size_t)(kThreads / 64) * (g.r / 8);
+    if (lds > kMaxLds) return hipErrorInvalidConfiguration;
+    const bf16_t* xb = static_cast<const bf16_t*>(x);
+    if (qs.qf)
+      hipLaunchKernelGGL(k_score_one<float>, grid, dim3(kThreads), lds, st, g, xb,
+                         qs.qf + (int64_t)s_lo * g.r, s_lo, slot, rinv_out, proj, site_stride);
+    else
+      hipLaunchKernelGGL(k_score_one<bf16_t>, grid, dim3(kThreads), lds, st, g, xb,
+                         static_cast<const bf16_t*>(qs.q) + (int64_t)s_lo * g.r, s_lo, slot,
+                         rinv_out, proj, site_stride);
     return hipGetLastError();
   }
   const int nsb = (s_hi - s_lo + 15) / 16;
