@@ -84,7 +84,8 @@ Layout make_layout(const attnres_config_t& c, int ts) {
   L.radial = take(srcs * tp * c.max_sites);
   L.lse = take((size_t)c.max_sites * T * c.heads);
   L.dqpart = take((size_t)dq_parts_cap() * c.r);
-  const size_t ahead = c.max_rows > 1 ? kFinAhead : 0;
+  // a look-ahead row lies below a finalized row, so at most max_rows - 1
+  const size_t ahead = std::min(kFinAhead, c.max_rows - 1);
   L.part = take(ahead * T * c.d);
   L.part_rad = take(ahead * T);
   const size_t sr = (size_t)c.max_sites * c.r;
@@ -665,7 +666,8 @@ attnres_status_t attnres_route_bwd(attnres_bank_t b, int32_t site, const void* e
   // reads them (nsrc is non-decreasing), and none of them holds a partial:
   // the previous look-ahead's rows lie above this call's rows (which hold
   // none), all finalized already.
-  const int n_ahead = std::min({kFinAhead, lo, attnres::kMaxJobs - (int)jobs.size() - (extra ? 1 : 0)});
+  const int n_ahead = std::min({kFinAhead, c.max_rows - 1, lo,
+                                attnres::kMaxJobs - (int)jobs.size() - (extra ? 1 : 0)});
   if (lo < n_rows && !any_partial && c.tokens > 0 && b->n_sites - site >= kFinAheadMinSites &&
       n_ahead > 0) {
     for (int i = 0; i < n_ahead; ++i) {
