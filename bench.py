@@ -8,7 +8,8 @@ backward in reverse order (bank-row, query and transient-source gradients).
 Inputs (bank rows, queries, upstream gradients) are seeded synthetic arrays
 already resident in HBM when the timed region starts.
 
-Prints one JSON line (see the design doc for the byte model behind the GB/s).
+Prints one JSON line.  Its GB/s figures divide each kernel's algorithmic bytes
+(`kernel_bytes`: what the kernel must move in HBM) by its measured time.
 """
 
 from __future__ import annotations
@@ -45,7 +46,9 @@ KERNEL_KIND = (("k_score", "score"), ("k_fwd", "fwd"), ("k_bwd_site", "bwd_site"
 # ---------------------------------------------------------------------------
 # Algorithmic bytes per kernel launch (what each kernel must move in HBM).
 def kernel_bytes(w, parts: int):
-    """Total algorithmic bytes per kernel kind over one microbatch."""
+    """Total algorithmic bytes per kernel kind over one microbatch: every source
+    row a site reads once per pass, the saved coefficients, the outputs and the
+    gradients, per launch."""
     b, T, d, r, H, S = w.elem_bytes, w.tokens, w.d, w.r, w.heads, w.sites
     nsrc, extra = list(w.nsrc), list(w.extra)
     out = {"score": 0, "fwd": 0, "bwd_site": 0, "dq_reduce": 0, "finalize": 0}
@@ -696,7 +699,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures the routing path on one GPU only: the kernel is per-token "
-              "and shards over tokens with no exchange but a dq all-reduce (see DESIGN.md); "
+              "and shards over tokens with no exchange but a dq all-reduce; "
               "run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

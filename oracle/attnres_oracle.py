@@ -32,7 +32,7 @@ r_n the inverse RMS.  "Low-Rank Attention Residuals", Appendix B.3 (Lemma 2,
 Eq. 20; Corollary 2.1, Eq. 21) gives the same decomposition for sliced keys,
 with the norm taken over the r key coordinates.
 
-Readings where the pages are open (each also listed in the design doc):
+Readings where the pages are open:
   R1  RMS over the full key width, then the per-head slice (Eq. 3 normalises
       the whole source; the fused kernel of Appendix E takes mean(v*v) over
       the row).  For LR keys the RMS is over the r key coordinates.

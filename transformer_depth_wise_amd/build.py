@@ -24,7 +24,8 @@ HIPCC_FLAGS = [
     "-fPIC",
     "-shared",
     "-Wall",
-    # keep the compiler from emitting packed fp32 math
+    # keep packed fp32 instructions (v_pk_*_f32) out of the generated code:
+    # scalar fp32 math only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
