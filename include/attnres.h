@@ -99,7 +99,7 @@ typedef enum {
   ATTNRES_ERR_INVALID = 1,     /* null pointer, bad shape or value, misaligned pointer */
   ATTNRES_ERR_CAPACITY = 2,    /* more rows or sites than configured, workspace too small */
   ATTNRES_ERR_ORDER = 3,       /* call out of the documented order */
-  ATTNRES_ERR_UNSUPPORTED = 4, /* shape this build does not handle (see attnres_bank_create) */
+  ATTNRES_ERR_UNSUPPORTED = 4, /* shape the library does not handle (see attnres_bank_create) */
   ATTNRES_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed */
 } attnres_status_t;
 
@@ -128,7 +128,7 @@ typedef struct {
 size_t attnres_workspace_bytes(const attnres_config_t* cfg);
 
 /* Create a bank over caller-owned device buffers (layouts above).
- * Shapes supported by this build: with c = 16 / sizeof(storage dtype)
+ * Shapes the library supports: with c = 16 / sizeof(storage dtype)
  * elements per 16-byte chunk, d, r, d/H and r/H must be multiples of c;
  * otherwise ATTNRES_ERR_UNSUPPORTED.  H | d, H | r, 1 <= r <= d, heads >= 1,
  * max_rows >= 1, max_sites >= 1, eps > 0, norm an attnres_norm_t, else
@@ -269,7 +269,7 @@ attnres_status_t attnres_bank_tiling(attnres_bank_t bank, int32_t* out5);
  *     out = sum_n alpha_n s_n + partial
  * Unlike the bank, nothing is shared between calls: every call takes its own
  * source list and returns fresh gradients.  An output gate on the routed term
- * belongs to the caller.  Shapes this build handles: with c elements per
+ * belongs to the caller.  Shapes the library handles: with c elements per
  * 16-byte chunk, d/H must be a multiple of 4c, and 64 * cpt must be a multiple
  * of d/c for some cpt in {1, 2, 4, 5, 8} with (64 cpt c / d) * H <= 64 (every
  * wave owns whole tokens; e.g. d = 4096 or 1280 bf16), else
