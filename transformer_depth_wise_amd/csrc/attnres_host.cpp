@@ -52,7 +52,7 @@ constexpr int kFinAheadMinSites = 8;
 
 struct Layout {
   size_t rinv, rinvx, proj, alpha, dl, radial, lse, dqpart;
-  size_t part, part_rad;  // finalize partial sums: [kFinAhead][T][d], [kFinAhead][T]
+  size_t part, part_rad;  // finalize partial sums: [A][T][d] and [A][T], A = min(kFinAhead, max_rows - 1)
   size_t qf, q32, qhi, qlo;  // effective queries with gains ([max_sites, r] each)
   size_t total;
   int64_t site_stride;  // floats per site of proj / alpha: (max_rows + 1) * T * H

@@ -11,7 +11,9 @@
 //               static query that will read it (queries are input-independent,
 //               "Low-Rank Attention Residuals" section 3.4), so the forward
 //               only has to mix; the logit is the projection times the inverse
-//               RMS.  k_score_mfma is the matrix-core form for bf16 rows.
+//               RMS.  k_score_mfma is the matrix-core form for bf16 rows,
+//               k_score_wide its form for key heads wider than 256, and
+//               k_score_one a plain dot for a row that one site reads.
 //   k_fwd       softmax over the cached logits, then the per-head mix of the
 //               full-width values (Eq. 3); saves alpha and log-sum-exp.
 //   k_bwd_site  one pass over the rows the site read: per-head
@@ -21,7 +23,9 @@
 //               coefficients of every site that read it: value path
 //               a * dout, key path rho^-1 dl q - (rho^-2 / r) (sum dl*l) key
 //               (Appendix E closed form; "Low-Rank Attention Residuals"
-//               Eq. 20-21).
+//               Eq. 20-21).  A launch may also store, for the rows below,
+//               partial sums over the same sites, which their own finalize
+//               adds (the sums are linear in the sites).
 //   k_dq_reduce fixed-order sum of the per-work-group query-gradient parts.
 //
 // No atomics anywhere: every reduction runs in a fixed order, so results are
