@@ -111,7 +111,7 @@ def run_ref(w, inp: Inputs, tokens=None, dout_tokens=None):
 
 
 def compare(w, got, ref, check_dq=True, label=""):
-    """Assert the benchmark spec's tolerances; return the measured errors."""
+    """Assert the parity tolerances; return the measured errors."""
     tol = TOL[w.dtype]
     err = {
         "out": max_rel(got["out"], ref["out"]),
