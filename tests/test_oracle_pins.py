@@ -182,14 +182,66 @@ def test_alpha_is_a_distribution_over_sources():
     assert np.isfinite(lse).all()
 
 
-def test_full_width_lr_equals_full_routing():
+# I5: the low-rank read with r = d is full routing.  The oracle has one code
+# path for both (the key is the last r coordinates); here full multi-head
+# routing ("Multi-Head Attention Residuals", section 2.3, Eq. 3) is written
+# again with scalar loops and no key width at all: RMS over the whole
+# source, head h scores q_h . (s / rms)_[h] and mixes s_[h].  The oracle's
+# gradients at r = d are checked against central differences of this
+# routine's <dout, out>.
+def multi_head_full_reference(sources, q, heads, eps):
+    N, T, d = sources.shape
+    kv = d // heads
+    out = np.zeros((T, d))
+    alpha = np.zeros((N, T, heads))
+    for t in range(T):
+        rms = [math.sqrt(sum(float(v) * float(v) for v in sources[n, t]) / d + eps)
+               for n in range(N)]
+        for h in range(heads):
+            cols = range(h * kv, (h + 1) * kv)
+            logits = [sum(float(q[j]) * float(sources[n, t, j]) / rms[n] for j in cols)
+                      for n in range(N)]
+            top = max(logits)
+            ex = [math.exp(v - top) for v in logits]
+            z = sum(ex)
+            for n in range(N):
+                alpha[n, t, h] = ex[n] / z
+                for j in cols:
+                    out[t, j] += alpha[n, t, h] * float(sources[n, t, j])
+    return out, alpha
+
+
+@pytest.mark.parametrize("heads", [1, 4])
+def test_full_width_lr_equals_full_routing(heads):
     rng = np.random.default_rng(6)
-    src = rng.standard_normal((4, 3, 16))
-    q = rng.standard_normal(16)
-    a = route_forward(src, q, 2, 16)
-    b = route_forward(src.copy(), q.copy(), 2, 16)
-    for x, y in zip(a, b):
-        np.testing.assert_array_equal(x, y)
+    N, T, d = 4, 3, 16
+    src = rng.standard_normal((N, T, d)) * rng.uniform(0.5, 2.0, (N, 1, 1))
+    q = rng.standard_normal(d) * 0.8
+    dout = rng.standard_normal((T, d))
+    out, alpha, _ = route_forward(src, q, heads, d)
+    ref_out, ref_alpha = multi_head_full_reference(src, q, heads, 1e-6)
+    np.testing.assert_allclose(out, ref_out, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(alpha, ref_alpha, rtol=0, atol=1e-14)
+
+    def loss(x, qq):
+        return float(np.sum(multi_head_full_reference(x, qq, heads, 1e-6)[0] * dout))
+
+    dsrc, dq = route_backward(src, q, heads, d, dout)
+    h = 1e-6
+    fd_src = np.zeros_like(src)
+    for idx in np.ndindex(src.shape):
+        a, b = src.copy(), src.copy()
+        a[idx] += h
+        b[idx] -= h
+        fd_src[idx] = (loss(a, q) - loss(b, q)) / (2 * h)
+    fd_q = np.zeros_like(q)
+    for j in range(d):
+        a, b = q.copy(), q.copy()
+        a[j] += h
+        b[j] -= h
+        fd_q[j] = (loss(src, a) - loss(src, b)) / (2 * h)
+    assert np.abs(dsrc - fd_src).max() <= 1e-6 * max(1.0, np.abs(fd_src).max())
+    assert np.abs(dq - fd_q).max() <= 1e-6 * max(1.0, np.abs(fd_q).max())
 
 
 # --------------------------------------------------------------------------
