@@ -5,7 +5,8 @@ Recipe: root = SeedSequence([seed, 7]); groups = root.spawn(6), in order:
   1 deltas   - spawn(n_deltas): delta m = c_m * N(0, 1), shape [T, d]
   2 null     - the null source ~ N(0, 1), shape [d]
   3 partial  - the residual stream ~ N(0, 1), shape [T, d]
-  4 query    - q ~ N(0, 0.02^2), shape [d]
+  4 query    - q ~ N(0, qstd^2), shape [d]; qstd = 0.02, or tau / sqrt(d/H)
+               for a sharp read whose logits spread by about tau
   5 dout     - upstream gradient ~ N(0, 1), shape [T, d]
 Drawn in float32, rounded to the storage dtype (bf16 round-to-nearest-even).
 """
@@ -31,6 +32,7 @@ class DeltaShape:
     dtype: str = "bf16"
     eps: float = 1e-6
     seed: int = 0
+    tau: float = 0.0  # > 0: sharp read, query std tau / sqrt(d/H)
 
     @property
     def sources(self) -> int:
@@ -39,9 +41,17 @@ class DeltaShape:
     def with_tokens(self, tokens: int) -> "DeltaShape":
         return replace(self, tokens=tokens, name=f"{self.name}@T{tokens}")
 
+    def with_tau(self, tau: float) -> "DeltaShape":
+        return replace(self, tau=tau, name=f"{self.name}+tau{tau:g}")
+
+    @property
+    def qstd(self) -> float:
+        return self.tau / float(np.sqrt(self.d // self.heads)) if self.tau > 0 else QUERY_STD
+
     def describe(self) -> str:
         return (f"{self.name}: T={self.tokens} d={self.d} H={self.heads} deltas={self.n_deltas} "
-                f"null={int(self.null)} partial={int(self.partial)} dtype={self.dtype}")
+                f"null={int(self.null)} partial={int(self.partial)} dtype={self.dtype} "
+                f"tau={self.tau:g}")
 
 
 class DeltaInputs:
@@ -72,7 +82,7 @@ class DeltaInputs:
         if kind == "partial":
             return self._normal(self._g[3], (s.tokens, s.d))
         if kind == "query":
-            return self._normal(self._g[4], (s.d,)) * np.float32(QUERY_STD)
+            return self._normal(self._g[4], (s.d,)) * np.float32(s.qstd)
         if kind == "dout":
             return self._normal(self._g[5], (s.tokens, s.d))
         raise KeyError(kind)

@@ -8,7 +8,9 @@ regenerated on its own and in any order):
                  workload has no per-source scale)
     1 rows     - spawn(rows): bank row n = c_n * Z, Z ~ N(0, 1), shape [T, d]
     2 extras   - spawn(sites): transient source of site s ~ N(0, 1), [T, d]
-    3 queries  - spawn(sites): q_s ~ N(0, 0.02^2), shape [r]
+    3 queries  - spawn(sites): q_s ~ N(0, 0.02^2), shape [r]; in the sharp
+                 regime q_s ~ N(0, tau_s^2 / (r/H)) (sharp_query_std), so the
+                 logits of a head spread by about tau_s
     4 douts    - spawn(sites): upstream gradient of site s ~ N(0, 1), [T, d]
     5 gains    - spawn(sites): routing RMSNorm gain of site s ~ U(0.5, 1.5),
                  shape [r], float32 (a parameter, not rounded to the storage
@@ -25,6 +27,28 @@ import numpy as np
 from .workloads import Workload
 
 QUERY_STD = 0.02
+
+# Sharp routing.  With N(0, 0.02^2) queries the logits of a head spread by
+# about 0.02 * sqrt(r/H) (0.25 at d = 1280, H = 8): near-uniform weights, as
+# an untrained router gives.  Trained routers are sharper: the effective
+# source count (entropy perplexity, "Low-Rank Attention Residuals", section
+# 4.6, Eq. 14) measured there at the final read is about 19 of 49 sources
+# under full routing and 3.6 of 9 under block routing.  A sharp workload
+# scales the query of site s so that a head's logits (sums of r/H query
+# coordinates times unit-RMS key coordinates) spread by about tau_s, cycling
+# over a ladder: (4, 8, 48) when some read has more than 16 sources, else
+# (1.5, 4, 48).  That gives mean effective source counts of about 1.5-2.5
+# over a schedule, and at tau = 48 logit gaps beyond 104, where a float32 exp
+# underflows to zero.
+SHARP_TAU_LONG = (4.0, 8.0, 48.0)
+SHARP_TAU_SHORT = (1.5, 4.0, 48.0)
+
+
+def sharp_query_std(w: Workload, site: int) -> float:
+    """Query standard deviation of site `site` of a sharp workload."""
+    most = max((n + e for n, e in zip(w.nsrc, w.extra)), default=0)
+    ladder = SHARP_TAU_LONG if most > 16 else SHARP_TAU_SHORT
+    return ladder[site % len(ladder)] / float(np.sqrt(w.r // w.heads))
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
@@ -86,7 +110,9 @@ class Inputs:
         return self._normal(self._extra_seeds[s], (w.tokens, w.d))
 
     def _query_raw(self, s: int) -> np.ndarray:
-        return self._normal(self._query_seeds[s], (self.w.r,)) * np.float32(QUERY_STD)
+        w = self.w
+        std = sharp_query_std(w, s) if w.sharp else QUERY_STD
+        return self._normal(self._query_seeds[s], (w.r,)) * np.float32(std)
 
     def _dout_raw(self, s: int) -> np.ndarray:
         w = self.w

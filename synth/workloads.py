@@ -39,6 +39,7 @@ class Workload:
     seed: int = 0
     norm: str = "slice"  # "slice": RMS over the r key coordinates; "full": over all d
     gains: bool = False  # each site has a routing RMSNorm gain g_s in R^r
+    sharp: bool = False  # queries scaled for sharp routing (draws.sharp_query_std)
 
     @property
     def sites(self) -> int:
@@ -71,10 +72,13 @@ class Workload:
     def with_gains(self) -> "Workload":
         return replace(self, gains=True, name=f"{self.name}+gain")
 
+    def with_sharp(self) -> "Workload":
+        return replace(self, sharp=True, name=f"{self.name}+sharp")
+
     def describe(self) -> str:
         return (f"{self.name}: T={self.tokens} d={self.d} r={self.r} H={self.heads} "
                 f"sites={self.sites} rows={self.rows} dtype={self.dtype} norm={self.norm} "
-                f"gains={int(self.gains)}")
+                f"gains={int(self.gains)} sharp={int(self.sharp)}")
 
 
 def full_schedule(layers: int):

@@ -10,10 +10,10 @@ import numpy as np
 import pytest
 
 from oracle import delta_backward, delta_forward
-from synth import DELTA_SHAPES, DeltaInputs, DeltaShape, sample_tokens
+from synth import DELTA_SHAPES, DeltaInputs, DeltaShape
 from synth.device import from_device, to_device
 
-from gpu_harness import ALPHA_TOL, TOL, log, max_rel
+from gpu_harness import ALPHA_TOL, log, max_rel, oracle_threads, routing_regime, tolerance
 
 pytestmark = pytest.mark.gpu
 
@@ -64,28 +64,52 @@ def run_gpu(s: DeltaShape, inp: DeltaInputs, tokens=None, dout_tokens=None):
             "dnull": None if dn is None else from_device(dn), "dq": from_device(dq)}
 
 
-def run_ref(s: DeltaShape, inp: DeltaInputs, tokens=None, dout_tokens=None):
-    sel = slice(None) if tokens is None else np.asarray(tokens)
-    t_sel = s.tokens if tokens is None else len(tokens)
-    deltas = (np.stack([inp.value("delta", m)[sel] for m in range(s.n_deltas)]).astype(np.float64)
-              if s.n_deltas else np.zeros((0, t_sel, s.d)))
+def run_ref(s: DeltaShape, inp: DeltaInputs, tokens=None, dout_tokens=None, chunk=256):
+    """The oracle on the same inputs, restricted to `tokens` (all if None).
+    Tokens are independent, so it runs over token chunks on a thread pool;
+    the query and null-source gradients (sums over tokens) are added chunk
+    by chunk in token order."""
+    from concurrent.futures import ThreadPoolExecutor
+    sel = np.arange(s.tokens) if tokens is None else np.asarray(tokens)
+    deltas = (np.stack([inp.value("delta", m)[sel] for m in range(s.n_deltas)])
+              if s.n_deltas else np.zeros((0, len(sel), s.d), dtype=np.float32))
     null = inp.value("null").astype(np.float64) if s.null else None
     q = inp.value("query").astype(np.float64)
-    partial = inp.value("partial")[sel].astype(np.float64) if s.partial else None
+    partial = inp.value("partial")[sel] if s.partial else None
     dout = inp.value("dout")
     if dout_tokens is not None:
         keep = np.zeros(s.tokens, dtype=bool)
         keep[dout_tokens] = True
         dout = dout.copy()
         dout[~keep] = 0.0
-    dout = dout[sel].astype(np.float64)
-    out, alpha, lse = delta_forward(null, deltas, q, partial, s.heads, s.eps)
-    dd, dnull, dq = delta_backward(null, deltas, q, dout, s.heads, s.eps)
-    return {"out": out, "alpha": alpha, "lse": lse, "dd": list(dd), "dnull": dnull, "dq": dq}
+    dout = dout[sel]
+
+    def one(a):
+        b = slice(a, min(a + chunk, len(sel)))
+        dl = deltas[:, b].astype(np.float64)
+        pa = None if partial is None else partial[b].astype(np.float64)
+        g = dout[b].astype(np.float64)
+        out, alpha, lse = delta_forward(null, dl, q, pa, s.heads, s.eps)
+        dd, dnull, dq = delta_backward(null, dl, q, g, s.heads, s.eps)
+        return out, alpha, lse, dd, dnull, dq
+
+    with ThreadPoolExecutor(oracle_threads()) as pool:
+        parts = list(pool.map(one, range(0, max(len(sel), 1), chunk)))
+    dq = np.zeros(s.d)
+    dnull = None if null is None else np.zeros(s.d)
+    for p in parts:
+        dq += p[5]
+        if dnull is not None:
+            dnull += p[4]
+    return {"out": np.concatenate([p[0] for p in parts]),
+            "alpha": np.concatenate([p[1] for p in parts], axis=1),
+            "lse": np.concatenate([p[2] for p in parts]),
+            "dd": [np.concatenate([p[3][m] for p in parts]) for m in range(s.n_deltas)],
+            "dnull": dnull, "dq": dq}
 
 
 def compare(s, got, ref, grads=True, label=""):
-    tol = TOL[s.dtype]
+    tol = tolerance(s.dtype, ref["lse"])
     err = {"out": max_rel(got["out"], ref["out"]), "lse": max_rel(got["lse"], ref["lse"]),
            "alpha_abs": float(np.abs(got["alpha"] - ref["alpha"]).max())}
     if grads:
@@ -94,7 +118,8 @@ def compare(s, got, ref, grads=True, label=""):
         err["dq"] = max_rel(got["dq"], ref["dq"])
         if ref["dnull"] is not None:
             err["dnull"] = max_rel(got["dnull"], ref["dnull"])
-    log(f"  {label} {s.describe()} errors: " + ", ".join(f"{k}={v:.3e}" for k, v in err.items()))
+    log(f"  {label} {s.describe()} errors: " + ", ".join(f"{k}={v:.3e}" for k, v in err.items())
+        + f" (tolerance {tol:.1e})")
     for k, v in err.items():
         limit = ALPHA_TOL if k == "alpha_abs" else tol
         assert v <= limit, f"{k} error {v:.3e} above {limit:.1e}"
@@ -114,17 +139,50 @@ def test_delta_empty_tokens():
     assert not got["dq"].any() and not got["dnull"].any()
 
 
-def test_delta_full_size_sampled_tokens():
-    """The 8B delta shape at full size: sampled tokens against the oracle;
-    dq and the null-source gradient through upstream gradients masked to the
-    sampled tokens."""
-    s = DELTA_SHAPES["delta8b"]
+# Sharp reads: the query scaled so that each head's logits spread by about
+# tau; tau = 4 concentrates a head on one to three sources, tau = 48 puts
+# logit gaps beyond float32's exp range.
+SHARP_CASES = [
+    DeltaShape("f32_d64_h4", 37, 64, 4, 3, dtype="f32").with_tau(4),
+    DeltaShape("f32_d64_h4", 37, 64, 4, 3, dtype="f32").with_tau(48),
+    DeltaShape("bf16_d1280_h8", 37, 1280, 8, 8).with_tau(4),
+    DeltaShape("bf16_d4096_h8", 9, 4096, 8, 8).with_tau(4),
+    DeltaShape("bf16_d4096_h8", 9, 4096, 8, 8).with_tau(48),
+    DeltaShape("f32_d2048_h4_split", 11, 2048, 4, 8, dtype="f32").with_tau(48),
+]
+
+
+def assert_sharp_regime(s, ref):
+    neff, under = routing_regime([ref["alpha"]])
+    log(f"  regime: mean effective sources {neff:.2f}, {under} weights below float32's range")
+    if 0 < s.tau <= 8:
+        assert 1.5 <= neff <= 4.0
+    if s.tau >= 24:
+        assert under > 0
+
+
+@pytest.mark.parametrize("s", SHARP_CASES, ids=lambda s: s.name)
+def test_delta_sharp_matches_oracle(s):
     inp = DeltaInputs(s)
-    toks = sample_tokens(s.tokens, 24)
-    log(f"[delta full-size] {s.describe()} sampled tokens={len(toks)}")
-    got = run_gpu(s, inp, tokens=toks, dout_tokens=toks)
-    ref = run_ref(s, inp, tokens=toks, dout_tokens=toks)
-    compare(s, got, ref, label="sampled+masked")
+    log(f"[delta sharp] {s.describe()}")
+    ref = run_ref(s, inp)
+    assert_sharp_regime(s, ref)
+    compare(s, run_gpu(s, inp), ref, label="delta sharp")
+
+
+@pytest.mark.parametrize("tau", [0, 4, 48])
+def test_delta_full_size_every_token(tau):
+    """The 8B delta shape at full size, every token and the whole query and
+    null-source gradients against the oracle (plain and sharp reads)."""
+    s = DELTA_SHAPES["delta8b"]
+    if tau:
+        s = s.with_tau(tau)
+    inp = DeltaInputs(s)
+    log(f"[delta full-size] {s.describe()}")
+    got = run_gpu(s, inp)
+    ref = run_ref(s, inp)
+    assert_sharp_regime(s, ref)
+    compare(s, got, ref, label="every token")
 
 
 def test_delta_deterministic_bitwise():
