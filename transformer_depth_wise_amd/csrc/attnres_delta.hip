@@ -286,11 +286,14 @@ __global__ __launch_bounds__(kDThreads) void k_delta_fwd(DeltaGeom g, DeltaArgs 
     st_nt(reinterpret_cast<uint4*>(out + t * g.d) + L.s[j].c, V::pack(r));
   }
   if (lane < pw) {
+    // normalised by the sum, as the output, not through lse (rounded at the
+    // logits' magnitude, which would scale every weight of the pair alike)
     const int t = lane / g.H;
+    const float il = 1.f / l;
     if (t < tv)
       for (int k = 0; k < g.n; ++k)
         alpha[((int64_t)k * g.T + t0 + t) * g.H + (lane - t * g.H)] =
-            expf(w_logit[k * pw + lane] - ls);
+            expf(w_logit[k * pw + lane] - m) * il;
   }
 }
 
@@ -372,7 +375,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_bwd(DeltaGeom g, DeltaArgs 
       const int k = i / pw, p = i - k * pw, t = p / g.H;
       w_alpha[i] = t < tv ? alpha[((int64_t)k * g.T + t0 + t) * g.H + (p - t * g.H)] : 0.f;
     }
-    float S_acc = 0.f;
+    float S_acc = 0.f, A_acc = 0.f;
     // ---- pass 1: P, logits, inverse RMS
     for (int k = 0; k < n; ++k) {
       uint4 x[CPT];
@@ -412,10 +415,14 @@ __global__ __launch_bounds__(kDThreads) void k_delta_bwd(DeltaGeom g, DeltaArgs 
         w_lg[k * pw + lane] = ri * hq;
         if (lane - t * g.H == 0) w_rinv[k * g.tw + t] = ri;
         S_acc += w_alpha[k * pw + lane] * P;
+        A_acc += w_alpha[k * pw + lane];
       }
       wave_fence();  // partials read before the next source overwrites them
     }
-    if (lane < pw) w_S[lane] = S_acc;
+    // S = sum a P / sum a: the common rounding error of a pair's weights
+    // cancels (with sharp routing it would otherwise dominate dl of the top
+    // source, whose exact value is a small difference)
+    if (lane < pw) w_S[lane] = A_acc > 0.f ? S_acc / A_acc : 0.f;
     wave_fence();
     for (int i = lane; i < n * pw; i += 64) {
       const int p = i - (i / pw) * pw;
@@ -711,9 +718,11 @@ __global__ __launch_bounds__(kDThreads) void k_delta_fwd_s(DeltaGeom g, DeltaArg
       }
       st_nt(reinterpret_cast<uint4*>(out + t * g.d) + c, V::pack(r));
     }
-    if (lane < hw)
+    if (lane < hw) {
+      const float il = 1.f / l;  // normalised by the sum, as in k_delta_fwd
       for (int k = 0; k < g.n; ++k)
-        alpha[((int64_t)k * g.T + t) * g.H + h0 + lane] = expf(w_logit[k * hw + lane] - ls);
+        alpha[((int64_t)k * g.T + t) * g.H + h0 + lane] = expf(w_logit[k * hw + lane] - m) * il;
+    }
   }
 }
 
@@ -781,7 +790,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_bwd_s(DeltaGeom g, DeltaArg
       const int k = i / hw, h = i - k * hw;
       w_alpha[i] = valid ? alpha[((int64_t)k * g.T + t) * g.H + h0 + h] : 0.f;
     }
-    float S_acc = 0.f;
+    float S_acc = 0.f, A_acc = 0.f;
     // rows are loaded one source at a time here: a second buffer would cost
     // more in occupancy than it gains in loads in flight
     for (int k = 0; k < n; ++k) {
@@ -816,11 +825,12 @@ __global__ __launch_bounds__(kDThreads) void k_delta_bwd_s(DeltaGeom g, DeltaArg
         w_P[k * hw + lane] = P;
         w_hq[k * hw + lane] = hq;
         S_acc += w_alpha[k * hw + lane] * P;
+        A_acc += w_alpha[k * hw + lane];
       }
       wave_fence();
     }
     __syncthreads();  // both halves' sums of squares are in s_x
-    if (lane < hw) w_S[lane] = S_acc;
+    if (lane < hw) w_S[lane] = A_acc > 0.f ? S_acc / A_acc : 0.f;  // as in k_delta_bwd
     for (int k = lane; k < n; k += 64)
       w_rinv[k] = rsqrtf((s_x[(k * 2 + ts) * 2] + s_x[(k * 2 + ts) * 2 + 1]) / (float)g.d + g.eps);
     wave_fence();

@@ -786,10 +786,14 @@ __global__ __launch_bounds__(kThreads) void k_fwd(Geom g, const T* __restrict__ 
     float l = 0.f;
     for (int n = k; n < n_src; n += sub) l += expf(sa[n * pairs + pc] - m);
     for (int o = 1; o < sub; o <<= 1) l += __shfl_xor(l, o, 64);
-    const float ls = m + logf(l);
+    const float ls = m + logf(l), il = 1.f / l;
     __syncthreads();  // every max/sum read of sa is done before it is overwritten
     if (live) {
-      for (int n = k; n < n_src; n += sub) sa[n * pairs + p] = expf(sa[n * pairs + p] - ls);
+      // exp(logit - max) / sum rather than exp(logit - lse): lse is rounded at
+      // the logits' magnitude, and with sharp routing (|logit| ~ 100) that
+      // rounding would move every weight of the pair by the same factor, so
+      // that the weights no longer sum to 1 to float32 precision
+      for (int n = k; n < n_src; n += sub) sa[n * pairs + p] = expf(sa[n * pairs + p] - m) * il;
       lse_v = ls;
     }
     lse_p = (live && k == 0 && p / g.H < tv) ? p : -1;
@@ -1004,9 +1008,12 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
       }
     }
     for (int p = tid; p < pairs; p += kThreads) {
-      float S = 0.f;
-      for (int n = 0; n < n_src; ++n) S += s_alpha[n * pairs + p] * s_P[n * pairs + p];
-      s_S[p] = S;
+      float S = 0.f, A = 0.f;
+      for (int n = 0; n < n_src; ++n) {
+        S += s_alpha[n * pairs + p] * s_P[n * pairs + p];
+        A += s_alpha[n * pairs + p];
+      }
+      s_S[p] = A > 0.f ? S / A : 0.f;  // see k_bwd_site_w
     }
     __syncthreads();
 #pragma unroll
@@ -1168,7 +1175,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site_w(
     for (int j = 0; j < CPT; ++j)
 #pragma unroll
       for (int e = 0; e < N; ++e) W[j][e] = 0.f;
-    float S_acc = 0.f;
+    float S_acc = 0.f, A_acc = 0.f;
     wave_lds_fence();
 
     for (int i = 0; i < n_src; i += SD) {
@@ -1201,6 +1208,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site_w(
           for (int c = 0; c < cnt; ++c) P += pp[c];
           w_P[n * pw + lane] = P;
           S_acc += w_alpha[n * pw + lane] * P;
+          A_acc += w_alpha[n * pw + lane];
         }
         wave_lds_fence();
 #pragma unroll
@@ -1219,7 +1227,12 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site_w(
         }
       }
     }
-    if (lane < pw) w_S[lane] = S_acc;
+    // S = sum a P / sum a: the weights carry a rounding error common to a
+    // (token, head) (their normaliser), which cancels here.  With sharp
+    // routing the top weight is about 1 and dl = a (P - S) of that source is
+    // a small difference: an unnormalised S would turn the common error into
+    // an error of order |P| in it, amplified by |q| in the key path.
+    if (lane < pw) w_S[lane] = A_acc > 0.f ? S_acc / A_acc : 0.f;
     wave_lds_fence();
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {

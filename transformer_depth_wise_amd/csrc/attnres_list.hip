@@ -215,9 +215,10 @@ __global__ __launch_bounds__(kLFwdThreads) void k_list_fwd(ListGeom g, ListArgs 
       for (int n = 0; n < g.n; ++n) m = fmaxf(m, w_a[n * g.H + h] * w_r[n]);
       float l = 0.f;
       for (int n = 0; n < g.n; ++n) l += expf(w_a[n * g.H + h] * w_r[n] - m);
-      const float ls = m + logf(l);
+      const float ls = m + logf(l), il = 1.f / l;
       for (int n = 0; n < g.n; ++n) {
-        const float al = expf(w_a[n * g.H + h] * w_r[n] - ls);
+        // normalised by the sum, not through lse (rounded at the logits' magnitude)
+        const float al = expf(w_a[n * g.H + h] * w_r[n] - m) * il;
         w_a[n * g.H + h] = al;
         alpha[((int64_t)n * g.T + t) * g.H + h] = al;
       }
@@ -306,8 +307,14 @@ __global__ __launch_bounds__(256) void k_list_bwd(ListGeom g, ListArgs a,
     }
     wave_lds_fence();
     for (int h = lane; h < g.H; h += 64) {
-      float S = 0.f;
-      for (int n = 0; n < g.n; ++n) S += w_a[n * g.H + h] * w_p[n * g.H + h];
+      // S = sum a P / sum a: the weights' common rounding error cancels (with
+      // sharp routing it would dominate dl of the top source)
+      float S = 0.f, A = 0.f;
+      for (int n = 0; n < g.n; ++n) {
+        S += w_a[n * g.H + h] * w_p[n * g.H + h];
+        A += w_a[n * g.H + h];
+      }
+      S = A > 0.f ? S / A : 0.f;
       for (int n = 0; n < g.n; ++n) w_p[n * g.H + h] = w_a[n * g.H + h] * (w_p[n * g.H + h] - S);
     }
     wave_lds_fence();
