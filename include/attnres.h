@@ -200,11 +200,16 @@ attnres_status_t attnres_bank_append(attnres_bank_t bank, const void* src, attnr
  *   y            device [T, d] storage dtype sublayer output
  *   commit == 0  partial_out (device [T, d], caller memory) receives the new
  *                partial sum: y alone after a commit or reset, else the
- *                previous partial_out + y.  It may be the previous partial
- *                (in place) or y.  The bank keeps the pointer (the caller
- *                keeps the memory) to add the next y; a site reading the
- *                partial passes it as `extra` to attnres_route_fwd, and it
- *                must stay unchanged until that site's backward.
+ *                previous partial_out + y.  It may be y.  The bank keeps the
+ *                pointer (the caller keeps the memory) to add the next y; a
+ *                site reading the partial passes it as `extra` to
+ *                attnres_route_fwd, and it must stay unchanged until that
+ *                site's backward.  partial_out may also be the buffer of an
+ *                earlier partial (in place), but only for a forward-only
+ *                microbatch: when it is the transient source of a site that
+ *                has run forward, the microbatch becomes forward-only and
+ *                every later attnres_route_bwd returns ATTNRES_ERR_ORDER
+ *                (the site's backward would read the overwritten source).
  *   commit != 0  partial_out must be NULL; the sum is written into the next
  *                bank row, which is committed as by attnres_bank_append
  *                (*row_out receives its index, else -1).

@@ -147,6 +147,35 @@ def test_call_order_is_enforced(lib):
     assert A.last_error() != ""
 
 
+def test_in_place_partial_makes_the_microbatch_forward_only(lib):
+    """Accumulating into the buffer a site read as its transient source
+    overwrites that source before the site's backward: the backward is
+    refused.  With no tokens nothing is launched, so this runs on the CPU."""
+    P, Y1, Y2, DEX = FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000
+    for in_place in (False, True):
+        b = fake_bank(cfg(tokens=0, max_rows=2, max_sites=2))
+        try:
+            A.attnres_bank_set_queries(b, [1, 1], [2, 2], FAKE)
+            A.attnres_bank_append(b, None, stream=0)
+            A.attnres_bank_accumulate(b, Y1, P, stream=0)
+            A.attnres_route_fwd(b, 0, P, FAKE, stream=0)
+            second = P if in_place else FAKE + 0x4000
+            A.attnres_bank_accumulate(b, Y2, second, stream=0)
+            A.attnres_route_fwd(b, 1, second, FAKE, stream=0)
+            if in_place:
+                with pytest.raises(A.AttnResError) as e:
+                    A.attnres_route_bwd(b, 1, second, None, FAKE, DEX, stream=0)
+                assert e.value.status == A.ATTNRES_ERR_ORDER
+                assert "forward-only" in A.last_error()
+                with pytest.raises(A.AttnResError) as e:  # and stays refused
+                    A.attnres_route_bwd(b, 1, second, None, FAKE, DEX, stream=0)
+                assert e.value.status == A.ATTNRES_ERR_ORDER
+                A.attnres_bank_reset(b)  # a new microbatch clears it
+                A.attnres_bank_set_queries(b, [1], None, FAKE)
+        finally:
+            A.attnres_bank_destroy(b)
+
+
 def test_misaligned_queries_rejected(lib):
     b = fake_bank(cfg())
     try:

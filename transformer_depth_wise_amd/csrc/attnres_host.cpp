@@ -217,6 +217,7 @@ struct attnres_bank_s {
   int fwd_next;
   int bwd_next;  // next site to run backward; -1 before the backward phase
   bool bwd_done;  // backward of site 0 has run: only reset is allowed
+  int fwd_only_site;  // >= 0: accumulate overwrote this site's transient source (no backward)
   std::vector<const void*> extra_ptr;
   const void* partial;  // running block partial sum (caller memory), NULL between blocks
   // finalize look-ahead: per bank row, the site from which on a stored partial
@@ -265,6 +266,7 @@ struct attnres_bank_s {
     fwd_next = 0;
     bwd_next = -1;
     bwd_done = false;
+    fwd_only_site = -1;
     extra_ptr.clear();
     partial = nullptr;
     part_site.assign(cfg.max_rows, -1);
@@ -544,6 +546,10 @@ attnres_status_t attnres_bank_accumulate(attnres_bank_t b, const void* y, void* 
     if (e != hipSuccess) return hip_fail(e, "accumulate kernel");
   }
   b->partial = partial_out;
+  // Writing over the transient source of a site that has run forward leaves
+  // that site without the input its backward reads: forward-only from here.
+  for (int s = 0; s < b->fwd_next && b->fwd_only_site < 0; ++s)
+    if (partial_out && b->has_extra[s] && b->extra_ptr[s] == partial_out) b->fwd_only_site = s;
   if (row_out) *row_out = -1;
   return ATTNRES_OK;
 }
@@ -599,6 +605,10 @@ attnres_status_t attnres_route_bwd(attnres_bank_t b, int32_t site, const void* e
     return fail(ATTNRES_ERR_ORDER, "route_bwd before the forward of every registered site");
   if (b->bwd_done)
     return fail(ATTNRES_ERR_ORDER, "backward phase already complete; reset for a new microbatch");
+  if (b->fwd_only_site >= 0)
+    return fail(ATTNRES_ERR_ORDER,
+                "forward-only microbatch: accumulate wrote over the transient source of site %d",
+                b->fwd_only_site);
   const int expect = b->bwd_next < 0 ? b->n_sites - 1 : b->bwd_next;
   if (site != expect)
     return fail(ATTNRES_ERR_ORDER, "route_bwd(site=%d) out of order: next backward site is %d", site,
@@ -642,7 +652,10 @@ attnres_status_t attnres_route_bwd(attnres_bank_t b, int32_t site, const void* e
   }
   // Rows first read by this site are final once every later site has run.
   // A row with a stored partial sums only the sites below the partial's.
+  // The look-ahead state changes only once the finalize launch is enqueued:
+  // consumed partials are cleared and new ones registered from these lists.
   std::vector<FinalizeJob> jobs;
+  std::vector<int> consumed, ahead_rows;
   const int lo = site > 0 ? b->nsrc[site - 1] : 0;
   bool any_partial = false;
   for (int n = lo; n < n_rows; ++n) {
@@ -657,7 +670,7 @@ attnres_status_t attnres_route_bwd(attnres_bank_t b, int32_t site, const void* e
       j.s1 = b->part_site[n];
       j.in = b->part_buf(b->part_idx[n]);
       j.in_rad = b->part_rad(b->part_idx[n]);
-      b->part_site[n] = -1;
+      consumed.push_back(n);
       any_partial = true;
     }
     jobs.push_back(j);
@@ -682,8 +695,7 @@ attnres_status_t attnres_route_bwd(attnres_bank_t b, int32_t site, const void* e
       j.s1 = b->n_sites;
       j.partial_out = 1;
       jobs.push_back(j);
-      b->part_site[m] = site;
-      b->part_idx[m] = i;
+      ahead_rows.push_back(m);
     }
   }
   if (extra) {
@@ -714,6 +726,11 @@ attnres_status_t attnres_route_bwd(attnres_bank_t b, int32_t site, const void* e
                                           b->dout_rows, row_stride, b->qset(), st);
   tf.done();
   if (e != hipSuccess) return hip_fail(e, "route_bwd finalize kernel");
+  for (int n : consumed) b->part_site[n] = -1;
+  for (size_t i = 0; i < ahead_rows.size(); ++i) {
+    b->part_site[ahead_rows[i]] = site;
+    b->part_idx[ahead_rows[i]] = (int)i;
+  }
   b->bwd_next = site - 1;
   if (site == 0) b->bwd_done = true;
   return ATTNRES_OK;
@@ -1044,19 +1061,14 @@ attnres_status_t attnres_list_fwd(const attnres_list_t* call, void* out, float* 
   return e == hipSuccess ? ATTNRES_OK : hip_fail(e, "list forward kernel");
 }
 
-attnres_status_t attnres_list_bwd(const attnres_list_t* call, const void* dout,
-                                  const float* alpha, const float* lse, const float* rinv,
-                                  float* const* d_sources, float* dq, void* workspace,
-                                  size_t workspace_bytes, attnres_stream_t stream) {
-  attnres::ListGeom g{};
-  attnres_status_t st = list_geom(call, &g);
-  if (st != ATTNRES_OK) return st;
-  if (!dq || !aligned_to(dq, 4)) return fail(ATTNRES_ERR_INVALID, "dq must be non-NULL, 4-byte aligned");
-  const size_t need = list_ws_bytes(g);
-  if (!workspace || !aligned16(workspace))
-    return fail(ATTNRES_ERR_INVALID, "workspace must be non-NULL and 16-byte aligned");
-  if (workspace_bytes < need)
-    return fail(ATTNRES_ERR_CAPACITY, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+namespace {
+
+// The list backward once its dq partial rows have a home: argument checks,
+// then the kernel and the dq reduction.
+attnres_status_t list_bwd_run(const attnres_list_t* call, attnres::ListGeom g, const void* dout,
+                              const float* alpha, const float* lse, const float* rinv,
+                              float* const* d_sources, float* dq, float* dq_part,
+                              attnres_stream_t stream) {
   attnres::ListGrads gr{};
   if (g.T > 0) {
     const size_t es = call->dtype == ATTNRES_F32 ? 4 : 2;
@@ -1081,7 +1093,6 @@ attnres_status_t attnres_list_bwd(const attnres_list_t* call, const void* dout,
       if (!aligned16(d_sources[n])) g.vec = 0;
   }
   const int parts = attnres::list_bwd_parts(g);
-  float* dq_part = static_cast<float*>(workspace);
   hipError_t e = attnres::launch_list_bwd(g, call->dtype, list_args(call), dout, alpha, lse, rinv,
                                           gr, dq_part, parts, s);
   if (e != hipSuccess) return hip_fail(e, "list backward kernel");
@@ -1089,6 +1100,26 @@ attnres_status_t attnres_list_bwd(const attnres_list_t* call, const void* dout,
   e = attnres::launch_dq_reduce(dq_part, parts, g.r, dq, nullptr, nullptr, nullptr, s);
   return e == hipSuccess ? ATTNRES_OK : hip_fail(e, "list dq reduction");
 }
+
+}  // namespace
+
+attnres_status_t attnres_list_bwd(const attnres_list_t* call, const void* dout,
+                                  const float* alpha, const float* lse, const float* rinv,
+                                  float* const* d_sources, float* dq, void* workspace,
+                                  size_t workspace_bytes, attnres_stream_t stream) {
+  attnres::ListGeom g{};
+  attnres_status_t st = list_geom(call, &g);
+  if (st != ATTNRES_OK) return st;
+  if (!dq || !aligned_to(dq, 4)) return fail(ATTNRES_ERR_INVALID, "dq must be non-NULL, 4-byte aligned");
+  const size_t need = list_ws_bytes(g);
+  if (!workspace || !aligned16(workspace))
+    return fail(ATTNRES_ERR_INVALID, "workspace must be non-NULL and 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(ATTNRES_ERR_CAPACITY, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  return list_bwd_run(call, g, dout, alpha, lse, rinv, d_sources, dq,
+                      static_cast<float*>(workspace), stream);
+}
+
 
 attnres_status_t attnres_row_rinv(attnres_bank_t b, int32_t row, const float** rinv) {
   if (!b) return fail(ATTNRES_ERR_INVALID, "bank is NULL");
