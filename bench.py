@@ -35,12 +35,21 @@ HBM_PEAK_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 # Sources whose change makes a stored counter summary stale.
 KERNEL_SOURCES = ("transformer_depth_wise_amd/csrc/attnres_kernels.hip",
+                  "transformer_depth_wise_amd/csrc/attnres_delta.hip",
+                  "transformer_depth_wise_amd/csrc/attnres_list.hip",
                   "transformer_depth_wise_amd/csrc/attnres_internal.h",
                   "transformer_depth_wise_amd/csrc/attnres_host.cpp")
-# Kernel symbol -> kernel kind reported by the library trace.
+# Kernel symbol -> kernel kind (the bank kinds are those of the library trace).
 KERNEL_KIND = (("k_score", "score"), ("k_fwd", "fwd"), ("k_bwd_site", "bwd_site"),
                ("k_dq_reduce", "dq_reduce"), ("k_finalize", "finalize"),
+               ("k_accumulate", "accumulate"), ("k_fold_gains", "fold_gains"),
+               ("k_delta_fwd", "delta_fwd"), ("k_delta_bwd", "delta_bwd"),
+               ("k_delta_null", "delta_null"), ("k_list_fwd", "list_fwd"),
+               ("k_list_bwd", "list_bwd"),
                ("k_probe_copy", "probe_copy"), ("k_probe_read", "probe_read"))
+PROBE_KINDS = ("probe_copy", "probe_read")
+# Microbatches (or list reads) one counter run covers: `--steps 1 --warmup 0`.
+COUNTER_RUN_STEPS = 1
 
 
 # ---------------------------------------------------------------------------
@@ -218,11 +227,17 @@ def summarize_counters(pmc_dir: str, workload: str, copy_bytes: int, command: st
              f"source_hash {source_hash()}",
              f"scale FETCH_SIZE {scale['FETCH_SIZE']:.6f} WRITE_SIZE {scale['WRITE_SIZE']:.6f}",
              "# kind dispatches fetch_kib write_kib fetch_bytes_calibrated write_bytes_calibrated"]
+    total = 0.0
     for kind in sorted(per["FETCH_SIZE"]):
         fk, n = per["FETCH_SIZE"][kind]
         wk = per["WRITE_SIZE"].get(kind, (0.0, 0))[0]
-        lines.append(f"kernel {kind} {n} {fk:.1f} {wk:.1f} "
-                     f"{fk * 1024 * scale['FETCH_SIZE']:.0f} {wk * 1024 * scale['WRITE_SIZE']:.0f}")
+        fb, wb = fk * 1024 * scale["FETCH_SIZE"], wk * 1024 * scale["WRITE_SIZE"]
+        lines.append(f"kernel {kind} {n} {fk:.1f} {wk:.1f} {fb:.0f} {wb:.0f}")
+        if kind not in PROBE_KINDS:
+            total += (fb + wb) * n
+    lines.append(f"# every routing kernel of the run: (fetch + write) x dispatches, over the "
+                 f"{COUNTER_RUN_STEPS} microbatch(es) the run covers")
+    lines.append(f"hbm_bytes_per_microbatch {total / COUNTER_RUN_STEPS:.0f}")
     return "\n".join(lines) + "\n"
 
 
@@ -260,7 +275,9 @@ def summarize_activity(pmc_dir: str, workload: str, command: str):
 
 def load_counters(workload: str):
     """Calibrated (fetch, write) bytes per dispatch per kernel kind from the
-    stored summary, or None when it is missing or the kernels changed since."""
+    stored summary, with "_total" the HBM bytes of one microbatch over every
+    routing kernel; None when the summary is missing or the kernels changed
+    since it was taken."""
     path = counters_path(workload)
     if not os.path.exists(path):
         return None
@@ -272,7 +289,51 @@ def load_counters(workload: str):
                 stamp = p[1]
             elif p and p[0] == "kernel":
                 out[p[1]] = (float(p[5]), float(p[6]))
+            elif p and p[0] == "hbm_bytes_per_microbatch":
+                out["_total"] = float(p[1])
     return out if stamp == source_hash() else None
+
+
+def measured_fields(workload: str, ms: float, model_bytes: int, unit: str = "microbatch"):
+    """The bench line's bandwidth figures.  `achieved_gbps` and `pct_of_peak`
+    divide the HBM bytes the counters measured (FETCH_SIZE + WRITE_SIZE of
+    every routing kernel, calibrated on the copy probe) by the step time; the
+    model figures divide the algorithmic bytes.  Without a current counter
+    summary the measured figures are null."""
+    c = load_counters(workload)
+    hbm = c.get("_total") if c else None
+    out = {f"hbm_bytes_per_{unit}": None if hbm is None else int(hbm),
+           "achieved_gbps": None if hbm is None else round(hbm / ms / 1e6, 1),
+           "pct_of_peak": None if hbm is None else round(100.0 * hbm / ms / 1e6 / HBM_PEAK_GBPS, 1),
+           "bytes_measured_by": ("rocprofv3 FETCH_SIZE + WRITE_SIZE, " + counters_path(workload)
+                                 .replace(ROOT + os.sep, "")) if hbm is not None else None,
+           f"alg_bytes_per_{unit}": model_bytes,
+           "model_gbps": round(model_bytes / ms / 1e6, 1),
+           "model_pct_of_peak": round(100.0 * model_bytes / ms / 1e6 / HBM_PEAK_GBPS, 1)}
+    return out
+
+
+def summarize_kernel_stats(stats_csv: str, workload: str, command: str, note: str) -> str:
+    """Markdown table of a rocprofv3 --kernel-trace --stats run
+    (run_kernel_stats.csv): dispatches and durations per kernel."""
+    rows = []
+    with open(stats_csv) as f:
+        for r in csv.DictReader(f):
+            rows.append((r["Name"], int(r["Calls"]), float(r["TotalDurationNs"]) / 1e3,
+                         float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                         float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    rows.sort(key=lambda x: -x[2])
+    lines = [f"# rocprofv3 kernel trace: {workload}", "",
+             "Command (from the repository root on the GPU box):", "", f"    {command}", "",
+             note, "Durations in microseconds, from `run_kernel_stats.csv`.", "",
+             "| kernel | dispatches | total us | avg us | min us | max us | share |",
+             "|---|---|---|---|---|---|---|"]
+    for name, calls, tot, avg, mn, mx, pct in rows:
+        short = name.replace("void ", "").replace("attnres::(anonymous namespace)::", "")
+        short = short.split("(")[0]
+        lines.append(f"| {short} | {calls} | {tot:.1f} | {avg:.2f} | {mn:.2f} | {mx:.2f} | "
+                     f"{pct:.1f}% |")
+    return "\n".join(lines) + "\n"
 
 
 # ---------------------------------------------------------------------------
@@ -430,9 +491,8 @@ def bench_delta(args):
                    "calls": DELTA_SITES, "max_sources": max(sched) + 1, "storage": shape.dtype,
                    "per_call_checkpointing": not args.no_recompute,
                    "baseline_ms_other_hardware": DELTA8B_PAGES_MS},
-        "achieved_gbps": round((by_f + by_b) / ms / 1e6, 1),
-        "pct_of_peak": round(100.0 * (by_f + by_b) / ms / 1e6 / HBM_PEAK_GBPS, 1),
-        "alg_bytes_per_microbatch": by_f + by_b,
+        **measured_fields(shape.name if not args.no_recompute else shape.name + "_norecompute",
+                          ms, by_f + by_b),
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(a / HBM_PEAK_GBPS, 3), "traffic": None,
                      "alg_bytes_per_launch": int((by_f if dom == "delta_fwd" else by_b)
@@ -543,9 +603,7 @@ def bench_list(args):
                    "heads": shape.heads, "entries": shape.n, "tensors": shape.tensors,
                    "strides": [shape.stride(k) for k in range(shape.tensors)],
                    "query_stride": shape.qstride, "storage": shape.dtype, "norm": shape.norm},
-        "achieved_gbps": round((by_f + by_b) / ms / 1e6, 1),
-        "pct_of_peak": round(100.0 * (by_f + by_b) / ms / 1e6 / HBM_PEAK_GBPS, 1),
-        "alg_bytes_per_read": by_f + by_b,
+        **measured_fields(shape.name, ms, by_f + by_b, unit="read"),
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(a / HBM_PEAK_GBPS, 3), "traffic": None,
                      "alg_bytes_per_launch": by_f if dom == "list_fwd" else by_b},
@@ -680,7 +738,21 @@ def main():
                     help="summarize rocprofv3 FETCH_SIZE/WRITE_SIZE runs of this bench found "
                          "in DIR/pmc_<counter>/ into profiles/ and exit (no GPU use)")
     ap.add_argument("--counters-command", default="", help="command recorded in the summary")
+    ap.add_argument("--kernel-stats", metavar="CSV",
+                    help="summarize a rocprofv3 --kernel-trace --stats run (its "
+                         "run_kernel_stats.csv) into profiles/<workload>_kernel_trace.md and "
+                         "exit (no GPU use); --counters-command is the command recorded, "
+                         "--stats-note a line about what the run covers")
+    ap.add_argument("--stats-note", default="")
     args = ap.parse_args()
+
+    if args.kernel_stats:
+        text = summarize_kernel_stats(args.kernel_stats, args.workload, args.counters_command,
+                                      args.stats_note)
+        with open(os.path.join(PROFILES, f"{args.workload}_kernel_trace.md"), "w") as f:
+            f.write(text)
+        print(text, end="")
+        return
 
     if args.counters:
         text = summarize_counters(args.counters, args.workload, PROBE_BYTES,
@@ -826,9 +898,7 @@ def report(args, w, bank, step, alg, config, cpu=None):
         "data": "synthetic: seeded N(0,1) bank rows x U(0.5,2) per-row scale, N(0,0.02^2) "
                 "queries, N(0,1) upstream gradients, bf16 storage",
         "config": config,
-        "achieved_gbps": round(total_bytes / ms / 1e6, 1),
-        "pct_of_peak": round(100.0 * total_bytes / ms / 1e6 / HBM_PEAK_GBPS, 1),
-        "alg_bytes_per_microbatch": total_bytes,
+        **measured_fields(w.name, ms, total_bytes),
         "probe": result_probe,
         "step_ms": {"median": round(median(per_step), 3), "min": round(per_step[0], 3),
                     "max": round(per_step[-1], 3)},
@@ -844,6 +914,7 @@ def report(args, w, bank, step, alg, config, cpu=None):
         tr = bank.trace_read()
         bank.trace(False)
         kern = {}
+        counters = load_counters(w.name)
         for k, (tms, cnt) in tr.items():
             if cnt == 0:
                 continue
@@ -851,10 +922,11 @@ def report(args, w, bank, step, alg, config, cpu=None):
                        "launches_per_microbatch": cnt // args.steps,
                        "avg_launch_us": round(1e3 * tms / cnt, 2),
                        "gbps": round(alg[k] * args.steps / tms / 1e6, 1)}
+            if counters is not None and k in counters:  # counter bytes per launch / launch time
+                kern[k]["hbm_gbps"] = round(sum(counters[k]) * cnt / tms / 1e6, 1)
         dom = max(kern, key=lambda k: kern[k]["ms_per_microbatch"])
         a = kern[dom]["gbps"]
         n_launch = kern[dom]["launches_per_microbatch"]
-        counters = load_counters(w.name)
         traffic = None
         if counters is not None and dom in counters:
             traffic = int(sum(counters[dom]))

@@ -71,9 +71,48 @@ def test_counter_summary_is_calibrated_on_the_copy_probe(tmp_path, monkeypatch):
     with open(bench.counters_path("toy"), "w") as f:
         f.write(text)
     assert bench.load_counters("toy")["fwd"] == (200.0 * 1024 * 2, 20.0 * 1024)
+    # the microbatch total: every routing dispatch, the probes left out
+    total = 2 * (200.0 * 1024 * 2 + 20.0 * 1024)
+    assert bench.load_counters("toy")["_total"] == total
+    m = bench.measured_fields("toy", 2.0, 1000000)
+    assert m["hbm_bytes_per_microbatch"] == int(total)
+    assert m["achieved_gbps"] == round(total / 2.0 / 1e6, 1)
+    assert m["model_gbps"] == 0.5 and m["alg_bytes_per_microbatch"] == 1000000
     with open(bench.counters_path("toy"), "w") as f:
         f.write(text.replace(bench.source_hash(), "0" * 16))
     assert bench.load_counters("toy") is None
+
+
+@pytest.mark.parametrize("name,kind", [
+    ("void attnres::(anonymous namespace)::k_fwd<unsigned short, 5, unsigned short>(...)", "fwd"),
+    ("void attnres::(anonymous namespace)::k_bwd_site_w<unsigned short, 5>(...)", "bwd_site"),
+    ("void attnres::(anonymous namespace)::k_score_mfma<5, 2>(...)", "score"),
+    ("void attnres::(anonymous namespace)::k_delta_fwd_s<unsigned short, 8>(...)", "delta_fwd"),
+    ("void attnres::(anonymous namespace)::k_delta_bwd<unsigned short, 8>(...)", "delta_bwd"),
+    ("void attnres::(anonymous namespace)::k_delta_null_vec<unsigned short>(...)", "delta_null"),
+    ("void attnres::(anonymous namespace)::k_list_bwd<unsigned short, 8>(...)", "list_bwd"),
+    ("void attnres::(anonymous namespace)::k_finalize_cols<unsigned short, 2, float>(...)",
+     "finalize"),
+])
+def test_kernel_kinds(name, kind):
+    assert bench.kind_of(name) == kind
+
+
+def test_kernel_stats_summary(tmp_path):
+    path = tmp_path / "run_kernel_stats.csv"
+    with open(path, "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Name", "Calls", "TotalDurationNs", "AverageNs",
+                                           "Percentage", "MinNs", "MaxNs", "StdDev"])
+        wr.writeheader()
+        wr.writerow({"Name": "void attnres::(anonymous namespace)::k_fwd<unsigned short, 5>(x)",
+                     "Calls": 4, "TotalDurationNs": 4000, "AverageNs": 1000, "Percentage": 80,
+                     "MinNs": 900, "MaxNs": 1100, "StdDev": 1})
+        wr.writerow({"Name": "k_probe_copy", "Calls": 1, "TotalDurationNs": 1000,
+                     "AverageNs": 1000, "Percentage": 20, "MinNs": 1000, "MaxNs": 1000,
+                     "StdDev": 0})
+    text = bench.summarize_kernel_stats(str(path), "toy", "cmd", "note")
+    assert "| k_fwd<unsigned short, 5> | 4 | 4.0 | 1.00 | 0.90 | 1.10 | 80.0% |" in text
+    assert text.index("k_fwd") < text.index("k_probe_copy")
 
 
 def test_more_than_one_gpu_is_refused():
