@@ -390,6 +390,25 @@ attnres_status_t attnres_list_bwd(const attnres_list_t* call, const void* dout,
                                   float* const* d_sources, float* dq, void* workspace,
                                   size_t workspace_bytes, attnres_stream_t stream);
 
+/* attnres_list_bwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same kernels and results, bit for bit, with the dq partial rows in a
+ * fixed per-device scratch array of 32 MiB inside the library instead of a
+ * caller workspace.  The library neither allocates nor frees anything here;
+ * each device holds its scratch until the process ends, and looks up its
+ * address on the first call on that device.
+ *   Arguments as attnres_list_bwd, without the workspace.
+ *   A shape whose attnres_list_workspace_bytes exceeds 32 MiB returns
+ *   ATTNRES_ERR_CAPACITY before any launch (e.g. r = 2048 fits at any token
+ *   count, r = 4096 up to 2048 tokens).
+ * Every call on one device shares that device's scratch, and each call
+ * rewrites every partial row it reads: calls that may overlap on one device
+ * (concurrent streams, or threads) race and give wrong query gradients. */
+attnres_status_t attnres_list_bwd_noalloc(const attnres_list_t* call, const void* dout,
+                                          const float* alpha, const float* lse, const float* rinv,
+                                          float* const* d_sources, float* dq,
+                                          attnres_stream_t stream);
+
 /* Kernel kinds reported by the launch trace. */
 typedef enum {
   ATTNRES_KERNEL_SCORE = 0,     /* append (and transient-source) scoring */

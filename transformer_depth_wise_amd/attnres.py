@@ -50,6 +50,7 @@ EXPORTS = (
     "attnres_list_workspace_bytes",
     "attnres_list_fwd",
     "attnres_list_bwd",
+    "attnres_list_bwd_noalloc",
     "attnres_trace_enable",
     "attnres_trace_read",
     "attnres_probe_sink_words",
@@ -154,6 +155,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "attnres_list_fwd": (i32, [POINTER(ListCallC), vp, vp, vp, vp, vp]),
         "attnres_list_bwd": (i32, [POINTER(ListCallC), vp, vp, vp, vp, POINTER(vp), vp, vp,
                                    c_size_t, vp]),
+        "attnres_list_bwd_noalloc": (i32, [POINTER(ListCallC), vp, vp, vp, vp, POINTER(vp), vp,
+                                         vp]),
         "attnres_trace_enable": (i32, [vp, i32]),
         "attnres_trace_read": (i32, [vp, POINTER(ctypes.c_double), POINTER(c_int64)]),
         "attnres_probe_sink_words": (i32, []),
@@ -518,6 +521,13 @@ def attnres_list_bwd(call, dout, alpha, lse, rinv, d_sources, dq, workspace, wor
                                            _ptr(lse), _ptr(rinv), arr, _ptr(dq),
                                            _ptr(workspace), int(workspace_bytes),
                                            _stream(stream)))
+
+
+def attnres_list_bwd_noalloc(call, dout, alpha, lse, rinv, d_sources, dq, stream=None) -> None:
+    arr = (c_void_p * max(len(d_sources), 1))(*[_ptr(x) for x in d_sources])
+    _check(load_library().attnres_list_bwd_noalloc(ctypes.byref(call), _ptr(dout), _ptr(alpha),
+                                                   _ptr(lse), _ptr(rinv), arr, _ptr(dq),
+                                                   _stream(stream)))
 
 
 class ListRead:

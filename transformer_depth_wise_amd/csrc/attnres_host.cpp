@@ -1120,6 +1120,26 @@ attnres_status_t attnres_list_bwd(const attnres_list_t* call, const void* dout,
                       static_cast<float*>(workspace), stream);
 }
 
+attnres_status_t attnres_list_bwd_noalloc(const attnres_list_t* call, const void* dout,
+                                          const float* alpha, const float* lse, const float* rinv,
+                                          float* const* d_sources, float* dq,
+                                          attnres_stream_t stream) {
+  attnres::ListGeom g{};
+  attnres_status_t st = list_geom(call, &g);
+  if (st != ATTNRES_OK) return st;
+  if (!dq || !aligned_to(dq, 4)) return fail(ATTNRES_ERR_INVALID, "dq must be non-NULL, 4-byte aligned");
+  const size_t need = list_ws_bytes(g);
+  if (need > attnres::kListScratchBytes)
+    return fail(ATTNRES_ERR_CAPACITY,
+                "the call needs %zu bytes of dq partial rows, above the fixed scratch of %zu bytes "
+                "(use attnres_list_bwd with a workspace)",
+                need, attnres::kListScratchBytes);
+  float* scratch = nullptr;
+  hipError_t e = attnres::list_scratch(&scratch);
+  if (e != hipSuccess) return hip_fail(e, "list scratch address");
+  return list_bwd_run(call, g, dout, alpha, lse, rinv, d_sources, dq, scratch, stream);
+}
+
 
 attnres_status_t attnres_row_rinv(attnres_bank_t b, int32_t row, const float** rinv) {
   if (!b) return fail(ATTNRES_ERR_INVALID, "bank is NULL");

@@ -204,6 +204,11 @@ hipError_t launch_list_fwd(const ListGeom& g, int dtype, const ListArgs& a, void
 hipError_t launch_list_bwd(const ListGeom& g, int dtype, const ListArgs& a, const void* dout,
                            const float* alpha, const float* lse, const float* rinv,
                            const ListGrads& gr, float* dq_part, int parts, hipStream_t st);
+// Device address of the current device's fixed list scratch (kListScratchBytes),
+// looked up once per device.
+constexpr size_t kListScratchBytes = 32u << 20;
+constexpr int kMaxDevices = 64;
+hipError_t list_scratch(float** ptr);
 
 // Bandwidth probes (attnres_probe.hip).
 int probe_blocks();

@@ -30,6 +30,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "attnres_internal.h"
 
 namespace attnres {
@@ -441,6 +443,31 @@ hipError_t launch_list_bwd(const ListGeom& g, int dtype, const ListArgs& a, cons
     hipLaunchKernelGGL((k_list_bwd<bf16_t, 1>), grid, dim3(64 * nw), lds, st, g, a,
                        static_cast<const bf16_t*>(dout), alpha, lse, rinv, gr, dq_part);
   return hipGetLastError();
+}
+
+// Fixed device scratch for the backward entry point that allocates nothing:
+// the dq partial rows [parts][r] of one call.  Each device holds its own copy
+// until the process ends; every call on a device shares it.
+static __device__ __align__(256) float scratch[kListScratchBytes / sizeof(float)];
+
+hipError_t list_scratch(float** ptr) {
+  static std::mutex mu;
+  static float* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    // the array's name is a host-side stand-in: its device address comes from
+    // the runtime, once per device with that device current
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<float*>(p);
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace attnres
