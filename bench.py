@@ -461,6 +461,7 @@ def bench_delta(args):
         t_b += ev[1].elapsed_time(ev[2])
     ms_f, ms_b = t_f / args.steps, t_b / args.steps
     ms = ms_f + ms_b
+    probe = bandwidth_probe(torch)  # also the calibration run of the HBM counters
     fb = [delta_bytes(shape, m) for m in sched]
     by_f, by_b = sum(x[0] for x in fb), sum(x[1] for x in fb)
     if not args.no_recompute:
@@ -498,6 +499,7 @@ def bench_delta(args):
                      "alg_bytes_per_launch": int((by_f if dom == "delta_fwd" else by_b)
                                                  / DELTA_SITES)},
         "kernels": kern,
+        "probe": probe,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = delta_cpu_baseline(shape, 16)
@@ -584,6 +586,7 @@ def bench_list(args):
         t_b += ev[1].elapsed_time(ev[2])
     ms_f, ms_b = t_f / args.steps, t_b / args.steps
     ms = ms_f + ms_b
+    probe = bandwidth_probe(torch)  # also the calibration run of the HBM counters
     by_f, by_b = list_bytes(shape)
     print(f"[bench] {args.steps} steps: {ms:.3f} ms/read (fwd {ms_f:.3f}, bwd {ms_b:.3f})",
           file=sys.stderr, flush=True)
@@ -608,6 +611,7 @@ def bench_list(args):
                      "unit": "GB/s", "frac": round(a / HBM_PEAK_GBPS, 3), "traffic": None,
                      "alg_bytes_per_launch": by_f if dom == "list_fwd" else by_b},
         "kernels": kern,
+        "probe": probe,
     }
     if not args.no_cpu_baseline:
         # size the sample to about 10 s of oracle time from a 64-token run
