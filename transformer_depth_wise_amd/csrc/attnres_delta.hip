@@ -16,112 +16,15 @@
 
 #include <math.h>
 
+#include "attnres_device.h"
 #include "attnres_internal.h"
 
 namespace attnres {
 namespace {
 
-typedef uint16_t bf16_t;
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
-
+using namespace dev;
 constexpr int kDThreads = 256;
 constexpr int kDWaves = kDThreads / 64;
-
-__device__ __forceinline__ uint32_t to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);                                  // round to nearest even
-  return u >> 16;
-}
-
-template <typename T>
-struct DVec;
-template <>
-struct DVec<float> {
-  static constexpr int N = 4;
-  __device__ static __forceinline__ void unpack(const uint4& v, float* x) {
-    x[0] = __uint_as_float(v.x);
-    x[1] = __uint_as_float(v.y);
-    x[2] = __uint_as_float(v.z);
-    x[3] = __uint_as_float(v.w);
-  }
-  __device__ static __forceinline__ uint4 pack(const float* x) {
-    return make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
-                      __float_as_uint(x[3]));
-  }
-  __device__ static __forceinline__ float dot(const uint4& a, const uint4& b) {
-    return __uint_as_float(a.x) * __uint_as_float(b.x) +
-           __uint_as_float(a.y) * __uint_as_float(b.y) +
-           __uint_as_float(a.z) * __uint_as_float(b.z) +
-           __uint_as_float(a.w) * __uint_as_float(b.w);
-  }
-};
-template <>
-struct DVec<bf16_t> {
-  static constexpr int N = 8;
-  __device__ static __forceinline__ void unpack(const uint4& v, float* x) {
-    x[0] = __uint_as_float(v.x << 16);
-    x[1] = __uint_as_float(v.x & 0xffff0000u);
-    x[2] = __uint_as_float(v.y << 16);
-    x[3] = __uint_as_float(v.y & 0xffff0000u);
-    x[4] = __uint_as_float(v.z << 16);
-    x[5] = __uint_as_float(v.z & 0xffff0000u);
-    x[6] = __uint_as_float(v.w << 16);
-    x[7] = __uint_as_float(v.w & 0xffff0000u);
-  }
-  __device__ static __forceinline__ uint4 pack(const float* x) {
-    return make_uint4(to_bf16_bits(x[0]) | (to_bf16_bits(x[1]) << 16),
-                      to_bf16_bits(x[2]) | (to_bf16_bits(x[3]) << 16),
-                      to_bf16_bits(x[4]) | (to_bf16_bits(x[5]) << 16),
-                      to_bf16_bits(x[6]) | (to_bf16_bits(x[7]) << 16));
-  }
-  // bf16 x bf16 products are exact in fp32; v_dot2c_f32_bf16 adds two at a time
-  __device__ static __forceinline__ float dot(const uint4& a, const uint4& b) {
-    float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x),
-                                              __builtin_bit_cast(bf16x2_t, b.x), 0.f, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.y),
-                                        __builtin_bit_cast(bf16x2_t, b.y), s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.z),
-                                        __builtin_bit_cast(bf16x2_t, b.z), s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w),
-                                        __builtin_bit_cast(bf16x2_t, b.w), s, false);
-    return s;
-  }
-};
-
-__device__ __forceinline__ uint4 ld_nt(const uint4* p) {
-  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ void st_nt(uint4* p, const uint4& v) {
-  __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(p));
-}
-__device__ __forceinline__ void st_nt(float* p, const float4& v) {
-  __builtin_nontemporal_store(f32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4_t*>(p));
-}
-
-__device__ __forceinline__ float quad_sum(float v) {
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
-  return v;
-}
-
-// Orders this wave's LDS writes before its later LDS reads (the wave-private
-// regions are touched by one wave only, so no work-group barrier is needed).
-__device__ __forceinline__ void wave_fence() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Work-groups are dispatched round-robin over the 8 XCDs; consecutive ranks
-// on one XCD get consecutive tiles.
-__device__ __forceinline__ int64_t xcd_rank(int64_t b, int64_t n) {
-  const int64_t q = n / 8, rem = n % 8, x = b % 8, k = b / 8;
-  return x * q + (x < rem ? x : rem) + k;
-}
 
 // Per-lane chunk slots: slot j of lane l is chunk l + 64 j of the wave's
 // [tw tokens x cpr chunks] block.
@@ -171,7 +74,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_fwd(DeltaGeom g, DeltaArgs 
                                                          T* __restrict__ out,
                                                          float* __restrict__ alpha,
                                                          float* __restrict__ lse) {
-  using V = DVec<T>;
+  using V = Vec<T>;
   constexpr int N = V::N;
   extern __shared__ float sm[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -188,7 +91,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_fwd(DeltaGeom g, DeltaArgs 
   for (int c = threadIdx.x; c < g.cpr; c += kDThreads) s_q[c] = static_cast<const uint4*>(a.query)[c];
   __syncthreads();
 
-  const int64_t t0 = xcd_rank(blockIdx.x, gridDim.x) * (int64_t)(kDWaves * g.tw) +
+  const int64_t t0 = xcd_order(blockIdx.x, gridDim.x) * (int64_t)(kDWaves * g.tw) +
                      (int64_t)wave * g.tw;
   const int tv = (int)max((int64_t)0, min((int64_t)g.tw, g.T - t0));
   // rows of invalid tokens load a valid token's chunks and are never stored
@@ -210,7 +113,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_fwd(DeltaGeom g, DeltaArgs 
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
       const uint4* p = source_chunks<T>(a, k, bc ? 0 : tok(j), g.d);
-      x[j] = bc ? p[L.s[j].c] : ld_nt(p + L.s[j].c);
+      x[j] = bc ? p[L.s[j].c] : ld_stream(p + L.s[j].c);
     }
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
@@ -222,7 +125,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_fwd(DeltaGeom g, DeltaArgs 
         w_part[2 * (q >> 2) + 1] = ss;
       }
     }
-    wave_fence();
+    wave_lds_fence();
     float hd = 0.f;
     if (lane < pw) {
       const int t = lane / g.H, h = lane - t * g.H;
@@ -234,7 +137,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_fwd(DeltaGeom g, DeltaArgs 
       }
       w_ssh[lane] = s2;
     }
-    wave_fence();
+    wave_lds_fence();
     if (lane < pw) {
       const int t = lane / g.H;
       float s2 = 0.f;
@@ -249,7 +152,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_fwd(DeltaGeom g, DeltaArgs 
       w_coef[2 * lane + 1] = wt;
       w_logit[k * pw + lane] = lg;
     }
-    wave_fence();
+    wave_lds_fence();
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
       const int p = L.s[j].tau * g.H + L.s[j].h;
@@ -259,7 +162,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_fwd(DeltaGeom g, DeltaArgs 
 #pragma unroll
       for (int e = 0; e < N; ++e) acc[j][e] = acc[j][e] * sc + wt * f[e];
     }
-    wave_fence();  // coefficients read before the next source overwrites them
+    wave_lds_fence();  // coefficients read before the next source overwrites them
   }
   float ls = 0.f;
   if (lane < pw) {
@@ -268,7 +171,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_fwd(DeltaGeom g, DeltaArgs 
     const int t = lane / g.H;
     if (t < tv) lse[(t0 + t) * g.H + (lane - t * g.H)] = ls;
   }
-  wave_fence();
+  wave_lds_fence();
 #pragma unroll
   for (int j = 0; j < CPT; ++j) {
     if (L.s[j].tau >= tv) continue;
@@ -279,11 +182,11 @@ __global__ __launch_bounds__(kDThreads) void k_delta_fwd(DeltaGeom g, DeltaArgs 
     for (int e = 0; e < N; ++e) r[e] = acc[j][e] * inv;
     if (partial) {
       float f[N];
-      V::unpack(ld_nt(reinterpret_cast<const uint4*>(partial + t * g.d) + L.s[j].c), f);
+      V::unpack(ld_stream(reinterpret_cast<const uint4*>(partial + t * g.d) + L.s[j].c), f);
 #pragma unroll
       for (int e = 0; e < N; ++e) r[e] += f[e];
     }
-    st_nt(reinterpret_cast<uint4*>(out + t * g.d) + L.s[j].c, V::pack(r));
+    st_stream(reinterpret_cast<uint4*>(out + t * g.d) + L.s[j].c, V::pack(r));
   }
   if (lane < pw) {
     // normalised by the sum, as the output, not through lse (rounded at the
@@ -319,7 +222,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_bwd(DeltaGeom g, DeltaArgs 
                                                          DeltaGrads dg,
                                                          float* __restrict__ dq_part,
                                                          float* __restrict__ ns_part) {
-  using V = DVec<T>;
+  using V = Vec<T>;
   constexpr int N = V::N;
   extern __shared__ float sm[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -354,7 +257,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_bwd(DeltaGeom g, DeltaArgs 
 
   const int64_t tile_tokens = (int64_t)kDWaves * g.tw;
   const int64_t ntiles = (g.T + tile_tokens - 1) / tile_tokens;
-  for (int64_t tile = xcd_rank(blockIdx.x, gridDim.x); tile < ntiles; tile += gridDim.x) {
+  for (int64_t tile = xcd_order(blockIdx.x, gridDim.x); tile < ntiles; tile += gridDim.x) {
     const int64_t t0 = tile * tile_tokens + (int64_t)wave * g.tw;
     const int tv = (int)max((int64_t)0, min((int64_t)g.tw, g.T - t0));
     const int64_t tb = tv > 0 ? t0 : tile * tile_tokens;
@@ -364,13 +267,13 @@ __global__ __launch_bounds__(kDThreads) void k_delta_bwd(DeltaGeom g, DeltaArgs 
 #pragma unroll
       for (int j = 0; j < CPT; ++j) {
         const uint4* p = source_chunks<T>(a, k, bc ? 0 : tok(j), g.d);
-        x[j] = bc ? p[L.s[j].c] : ld_nt(p + L.s[j].c);
+        x[j] = bc ? p[L.s[j].c] : ld_stream(p + L.s[j].c);
       }
     };
     uint4 dov[CPT];
 #pragma unroll
     for (int j = 0; j < CPT; ++j)
-      dov[j] = ld_nt(reinterpret_cast<const uint4*>(dout + tok(j) * g.d) + L.s[j].c);
+      dov[j] = ld_stream(reinterpret_cast<const uint4*>(dout + tok(j) * g.d) + L.s[j].c);
     for (int i = lane; i < n * pw; i += 64) {
       const int k = i / pw, p = i - k * pw, t = p / g.H;
       w_alpha[i] = t < tv ? alpha[((int64_t)k * g.T + t0 + t) * g.H + (p - t * g.H)] : 0.f;
@@ -392,7 +295,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_bwd(DeltaGeom g, DeltaArgs 
           w_part[3 * (q >> 2) + 2] = ss;
         }
       }
-      wave_fence();
+      wave_lds_fence();
       float P = 0.f, hq = 0.f;
       if (lane < pw) {
         const int t = lane / g.H, h = lane - t * g.H;
@@ -405,7 +308,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_bwd(DeltaGeom g, DeltaArgs 
         }
         w_ssh[lane] = s2;
       }
-      wave_fence();
+      wave_lds_fence();
       if (lane < pw) {
         const int t = lane / g.H;
         float s2 = 0.f;
@@ -417,25 +320,25 @@ __global__ __launch_bounds__(kDThreads) void k_delta_bwd(DeltaGeom g, DeltaArgs 
         S_acc += w_alpha[k * pw + lane] * P;
         A_acc += w_alpha[k * pw + lane];
       }
-      wave_fence();  // partials read before the next source overwrites them
+      wave_lds_fence();  // partials read before the next source overwrites them
     }
     // S = sum a P / sum a: the common rounding error of a pair's weights
     // cancels (with sharp routing it would otherwise dominate dl of the top
     // source, whose exact value is a small difference)
     if (lane < pw) w_S[lane] = A_acc > 0.f ? S_acc / A_acc : 0.f;
-    wave_fence();
+    wave_lds_fence();
     for (int i = lane; i < n * pw; i += 64) {
       const int p = i - (i / pw) * pw;
       w_dl[i] = w_alpha[i] * (w_P[i] - w_S[p]);
     }
-    wave_fence();
+    wave_lds_fence();
     for (int i = lane; i < n * g.tw; i += 64) {
       const int k = i / g.tw, t = i - k * g.tw;
       float c = 0.f;
       for (int h = 0; h < g.H; ++h) c += w_dl[k * pw + t * g.H + h] * w_lg[k * pw + t * g.H + h];
       w_c[i] = c;
     }
-    wave_fence();
+    wave_lds_fence();
     if (has_null && lane < pw) {  // the null source is source 0; invalid tokens have alpha = 0
       const int t = lane / g.H;
       null_dl += w_dl[lane];
@@ -470,10 +373,10 @@ __global__ __launch_bounds__(kDThreads) void k_delta_bwd(DeltaGeom g, DeltaArgs 
         float* o = dst + (t0 + tau) * g.d + (int64_t)L.s[j].c * N;
 #pragma unroll
         for (int e = 0; e < N; e += 4)
-          st_nt(o + e, make_float4(gr[e], gr[e + 1], gr[e + 2], gr[e + 3]));
+          st_stream(o + e, make_float4(gr[e], gr[e + 1], gr[e + 2], gr[e + 3]));
       }
     }
-    wave_fence();
+    wave_lds_fence();
   }
 
   // Work-group partials in a fixed order.  dq: slot (wave, 64 j + lane) holds
@@ -518,7 +421,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_null_vec(DeltaGeom g,
                                                               const float* __restrict__ alpha0,
                                                               int64_t rows,
                                                               float* __restrict__ nv_part) {
-  using V = DVec<T>;
+  using V = Vec<T>;
   constexpr int N = V::N;
   const int64_t nblk = (g.T + rows - 1) / rows;
   for (int c = threadIdx.x; c < g.cpr; c += kDThreads) {
@@ -531,7 +434,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_null_vec(DeltaGeom g,
       for (int64_t t = blk * rows; t < t1; ++t) {
         const float w = alpha0[t * g.H + h];
         float f[N];
-        V::unpack(ld_nt(reinterpret_cast<const uint4*>(dout + t * g.d) + c), f);
+        V::unpack(ld_stream(reinterpret_cast<const uint4*>(dout + t * g.d) + c), f);
 #pragma unroll
         for (int e = 0; e < N; ++e) acc[e] += w * f[e];
       }
@@ -549,7 +452,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_null_finish(DeltaGeom g, De
                                                                  const float* __restrict__ nv,
                                                                  const float* __restrict__ ns,
                                                                  float* __restrict__ dnull) {
-  using V = DVec<T>;
+  using V = Vec<T>;
   constexpr int N = V::N;
   __shared__ float s_red[kDThreads];
   const T* null = static_cast<const T*>(a.null_src);
@@ -593,7 +496,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_fwd_s(DeltaGeom g, DeltaArg
                                                            T* __restrict__ out,
                                                            float* __restrict__ alpha,
                                                            float* __restrict__ lse) {
-  using V = DVec<T>;
+  using V = Vec<T>;
   constexpr int N = V::N;
   constexpr int SPAN = 64 * CPT;  // chunks per wave
   extern __shared__ float sm[];
@@ -612,7 +515,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_fwd_s(DeltaGeom g, DeltaArg
 
   for (int c = threadIdx.x; c < g.cpr; c += kDThreads) s_q[c] = static_cast<const uint4*>(a.query)[c];
 
-  const int64_t t = xcd_rank(blockIdx.x, gridDim.x) * 2 + ts;
+  const int64_t t = xcd_order(blockIdx.x, gridDim.x) * 2 + ts;
   const bool valid = t < g.T;
   const int64_t tt = valid ? t : 0;  // invalid token slots read token 0, store nothing
   const int c0 = half * SPAN;
@@ -631,7 +534,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_fwd_s(DeltaGeom g, DeltaArg
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
       const int c = c0 + lane + 64 * j;
-      x[j] = bc ? p[c] : ld_nt(p + c);
+      x[j] = bc ? p[c] : ld_stream(p + c);
     }
   };
   // one source: request the next, then score and fold this one in (called
@@ -651,7 +554,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_fwd_s(DeltaGeom g, DeltaArg
       }
       wss += ss;
     }
-    wave_fence();
+    wave_lds_fence();
     float hd = 0.f;
     if (lane < hw) {
       const float* pp = w_part + 2 * ((lane * g.kvc) >> 2);
@@ -675,7 +578,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_fwd_s(DeltaGeom g, DeltaArg
       w_coef[2 * lane + 1] = wt;
       w_logit[k * hw + lane] = lg;
     }
-    wave_fence();
+    wave_lds_fence();
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
       const int hl = (lane + 64 * j) / g.kvc;  // head of the chunk, within this half
@@ -701,7 +604,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_fwd_s(DeltaGeom g, DeltaArg
     w_coef[2 * lane] = 1.f / l;
     if (valid) lse[t * g.H + h0 + lane] = ls;
   }
-  wave_fence();
+  wave_lds_fence();
   if (valid) {
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
@@ -712,11 +615,11 @@ __global__ __launch_bounds__(kDThreads) void k_delta_fwd_s(DeltaGeom g, DeltaArg
       for (int e = 0; e < N; ++e) r[e] = acc[j][e] * inv;
       if (partial) {
         float f[N];
-        V::unpack(ld_nt(reinterpret_cast<const uint4*>(partial + t * g.d) + c), f);
+        V::unpack(ld_stream(reinterpret_cast<const uint4*>(partial + t * g.d) + c), f);
 #pragma unroll
         for (int e = 0; e < N; ++e) r[e] += f[e];
       }
-      st_nt(reinterpret_cast<uint4*>(out + t * g.d) + c, V::pack(r));
+      st_stream(reinterpret_cast<uint4*>(out + t * g.d) + c, V::pack(r));
     }
     if (lane < hw) {
       const float il = 1.f / l;  // normalised by the sum, as in k_delta_fwd
@@ -733,7 +636,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_bwd_s(DeltaGeom g, DeltaArg
                                                            DeltaGrads dg,
                                                            float* __restrict__ dq_part,
                                                            float* __restrict__ ns_part) {
-  using V = DVec<T>;
+  using V = Vec<T>;
   constexpr int N = V::N;
   constexpr int SPAN = 64 * CPT;
   extern __shared__ float sm[];
@@ -769,7 +672,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_bwd_s(DeltaGeom g, DeltaArg
   float null_dl = 0.f, null_c = 0.f;
 
   const int64_t ntiles = (g.T + 1) / 2;
-  for (int64_t tile = xcd_rank(blockIdx.x, gridDim.x); tile < ntiles; tile += gridDim.x) {
+  for (int64_t tile = xcd_order(blockIdx.x, gridDim.x); tile < ntiles; tile += gridDim.x) {
     const int64_t t = tile * 2 + ts;
     const bool valid = t < g.T;
     const int64_t tt = valid ? t : tile * 2;
@@ -779,13 +682,13 @@ __global__ __launch_bounds__(kDThreads) void k_delta_bwd_s(DeltaGeom g, DeltaArg
 #pragma unroll
       for (int j = 0; j < CPT; ++j) {
         const int c = c0 + lane + 64 * j;
-        x[j] = bc ? p[c] : ld_nt(p + c);
+        x[j] = bc ? p[c] : ld_stream(p + c);
       }
     };
     uint4 dov[CPT];
 #pragma unroll
     for (int j = 0; j < CPT; ++j)
-      dov[j] = ld_nt(reinterpret_cast<const uint4*>(dout + tt * g.d) + c0 + lane + 64 * j);
+      dov[j] = ld_stream(reinterpret_cast<const uint4*>(dout + tt * g.d) + c0 + lane + 64 * j);
     for (int i = lane; i < n * hw; i += 64) {
       const int k = i / hw, h = i - k * hw;
       w_alpha[i] = valid ? alpha[((int64_t)k * g.T + t) * g.H + h0 + h] : 0.f;
@@ -814,7 +717,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_bwd_s(DeltaGeom g, DeltaArg
 #pragma unroll
       for (int o = 32; o >= 4; o >>= 1) s2 += __shfl_xor(s2, o, 64);
       if (lane == 0) s_x[(k * 2 + ts) * 2 + half] = s2;
-      wave_fence();
+      wave_lds_fence();
       if (lane < hw) {
         const float* pp = w_part + 3 * ((lane * g.kvc) >> 2);
         float P = 0.f, hq = 0.f;
@@ -827,13 +730,13 @@ __global__ __launch_bounds__(kDThreads) void k_delta_bwd_s(DeltaGeom g, DeltaArg
         S_acc += w_alpha[k * hw + lane] * P;
         A_acc += w_alpha[k * hw + lane];
       }
-      wave_fence();
+      wave_lds_fence();
     }
     __syncthreads();  // both halves' sums of squares are in s_x
     if (lane < hw) w_S[lane] = A_acc > 0.f ? S_acc / A_acc : 0.f;  // as in k_delta_bwd
     for (int k = lane; k < n; k += 64)
       w_rinv[k] = rsqrtf((s_x[(k * 2 + ts) * 2] + s_x[(k * 2 + ts) * 2 + 1]) / (float)g.d + g.eps);
-    wave_fence();
+    wave_lds_fence();
     for (int i = lane; i < n * hw; i += 64) {
       const int k = i / hw, h = i - k * hw;
       const float lg = w_rinv[k] * w_hq[i];
@@ -842,7 +745,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_bwd_s(DeltaGeom g, DeltaArg
       w_dl[i] = dl;
       w_tmp[i] = dl * lg;
     }
-    wave_fence();
+    wave_lds_fence();
     __syncthreads();  // every wave has read s_x
     for (int k = lane; k < n; k += 64) {
       float c = 0.f;
@@ -851,7 +754,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_bwd_s(DeltaGeom g, DeltaArg
     }
     __syncthreads();
     for (int k = lane; k < n; k += 64) w_c[k] = s_x[(k * 2 + ts) * 2] + s_x[(k * 2 + ts) * 2 + 1];
-    wave_fence();
+    wave_lds_fence();
     if (has_null && valid) {
       if (lane < hw) null_dl += w_dl[lane];
       if (lane == 0 && half == 0) null_c += w_c[0];
@@ -883,7 +786,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_bwd_s(DeltaGeom g, DeltaArg
         float* o = dst + t * g.d + (int64_t)c * N;
 #pragma unroll
         for (int e = 0; e < N; e += 4)
-          st_nt(o + e, make_float4(gr[e], gr[e + 1], gr[e + 2], gr[e + 3]));
+          st_stream(o + e, make_float4(gr[e], gr[e + 1], gr[e + 2], gr[e + 3]));
       }
     }
     __syncthreads();  // the next tile reuses s_x and the wave regions

@@ -33,59 +33,13 @@
 
 #include <math.h>
 
+#include "attnres_device.h"
 #include "attnres_internal.h"
 
 namespace attnres {
 namespace {
 
-typedef uint16_t bf16_t;
-
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);                                  // round to nearest even
-  return u >> 16;
-}
-
-// One 16-byte chunk of storage values <-> float32.
-template <typename T>
-struct Vec;
-
-template <>
-struct Vec<float> {
-  static constexpr int N = 4;
-  __device__ static __forceinline__ void unpack(const uint4& v, float* x) {
-    x[0] = __uint_as_float(v.x);
-    x[1] = __uint_as_float(v.y);
-    x[2] = __uint_as_float(v.z);
-    x[3] = __uint_as_float(v.w);
-  }
-  __device__ static __forceinline__ uint4 pack(const float* x) {
-    return make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
-                      __float_as_uint(x[3]));
-  }
-};
-
-template <>
-struct Vec<bf16_t> {
-  static constexpr int N = 8;
-  __device__ static __forceinline__ void unpack(const uint4& v, float* x) {
-    x[0] = __uint_as_float(v.x << 16);
-    x[1] = __uint_as_float(v.x & 0xffff0000u);
-    x[2] = __uint_as_float(v.y << 16);
-    x[3] = __uint_as_float(v.y & 0xffff0000u);
-    x[4] = __uint_as_float(v.z << 16);
-    x[5] = __uint_as_float(v.z & 0xffff0000u);
-    x[6] = __uint_as_float(v.w << 16);
-    x[7] = __uint_as_float(v.w & 0xffff0000u);
-  }
-  __device__ static __forceinline__ uint4 pack(const float* x) {
-    return make_uint4(f32_to_bf16_bits(x[0]) | (f32_to_bf16_bits(x[1]) << 16),
-                      f32_to_bf16_bits(x[2]) | (f32_to_bf16_bits(x[3]) << 16),
-                      f32_to_bf16_bits(x[4]) | (f32_to_bf16_bits(x[5]) << 16),
-                      f32_to_bf16_bits(x[6]) | (f32_to_bf16_bits(x[7]) << 16));
-  }
-};
+using namespace dev;
 
 // One chunk (Vec<T>::N values) of a query row: storage dtype T (one 16-byte
 // word) or float32 effective queries q * g (N / 4 words).
@@ -108,78 +62,7 @@ struct QChunk {
   }
 };
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
-
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
-
-// Load of streamed data (bank rows, upstream gradients) that the kernel reads
-// exactly once: non-temporal, so it does not evict reusable lines.
-__device__ __forceinline__ uint4 ld_stream(const uint4* p) {
-  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-// Stores of results no kernel of the same pass reads back (outputs, saved
-// coefficients, gradients): non-temporal as well.  Inside a saturated read
-// stream every write costs well above its bytes on this GPU; these stores
-// cost measurably less than plain ones and leave the caches to the reads.
-typedef float f32x4_t_ __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void st_stream(uint4* p, const uint4& v) {
-  __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(p));
-}
-__device__ __forceinline__ void st_stream(float* p, const float4& v) {
-  __builtin_nontemporal_store(f32x4_t_{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4_t_*>(p));
-}
-// Single floats (scattered 4-byte results) stay plain stores: L2 merges
-// neighbouring ones into whole lines, which non-temporal stores do not.
-__device__ __forceinline__ void st_stream(float* p, float v) { *p = v; }
-
-// Sum over the 4 lanes of a quad (two DPP quad permutations).
-__device__ __forceinline__ float quad_sum(float v) {
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
-  return v;
-}
-
-// <a, b> over one 16-byte chunk with fp32 accumulation.
-template <typename T>
-__device__ __forceinline__ float dot_chunk(const uint4& a, const uint4& b);
-
-template <>
-__device__ __forceinline__ float dot_chunk<bf16_t>(const uint4& a, const uint4& b) {
-  // bf16 x bf16 products are exact in fp32; v_dot2c_f32_bf16 adds two at a time
-  float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x),
-                                            __builtin_bit_cast(bf16x2_t, b.x), 0.f, false);
-  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.y),
-                                      __builtin_bit_cast(bf16x2_t, b.y), s, false);
-  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.z),
-                                      __builtin_bit_cast(bf16x2_t, b.z), s, false);
-  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w),
-                                      __builtin_bit_cast(bf16x2_t, b.w), s, false);
-  return s;
-}
-
-template <>
-__device__ __forceinline__ float dot_chunk<float>(const uint4& a, const uint4& b) {
-  return __uint_as_float(a.x) * __uint_as_float(b.x) + __uint_as_float(a.y) * __uint_as_float(b.y) +
-         __uint_as_float(a.z) * __uint_as_float(b.z) + __uint_as_float(a.w) * __uint_as_float(b.w);
-}
-
-// Exchange point between the lanes of one wave through LDS.
-__device__ __forceinline__ void wave_lds_fence() {
-  // LDS operations of one wave execute in order; this only stops the
-  // compiler from moving LDS accesses across the exchange point.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-}
 
 // Position of one chunk slot of a thread inside a [tt x cpr] tile of chunks:
 // slot j of thread `tid` is chunk q = tid + j * kThreads, token q / cpr.
@@ -215,16 +98,10 @@ __device__ __forceinline__ Slot make_slot(const Geom& g, int tid, int j) {
 // staged in LDS as fp32, each thread owns (head, site) items with the site
 // index fastest, so a wave reads the same LDS words (broadcast) while its
 // lanes stream different query rows from L2.
-// Work-groups are dispatched round-robin over the 8 XCDs, each with its own
-// L2.  Renumbering them so that each XCD's share is one contiguous range of
-// tiles lets neighbouring tiles share the 128-byte lines of the small
-// per-token arrays (inverse RMS, projections, radial sums) in one L2 instead
-// of each XCD fetching a whole line for a 32-byte run.
-__device__ __forceinline__ int64_t xcd_order(int64_t b, int64_t n) {
-  constexpr int64_t kXcds = 8;
-  const int64_t q = n / kXcds, rem = n % kXcds, x = b % kXcds, k = b / kXcds;
-  return x * q + (x < rem ? x : rem) + k;
-}
+// Work-groups are renumbered XCD by XCD (xcd_order), so that neighbouring
+// tiles share the 128-byte lines of the small per-token arrays (inverse RMS,
+// projections, radial sums) in one L2 instead of each XCD fetching a whole
+// line for a 32-byte run.
 
 template <typename T, typename QT, int TILE>
 __global__ __launch_bounds__(kThreads) void k_score(Geom g, const T* __restrict__ x,
@@ -313,7 +190,6 @@ __global__ __launch_bounds__(kThreads) void k_score(Geom g, const T* __restrict_
 // holding column (site) l%16, rows (tokens) 4*(l/16)..+3.  The inverse RMS is
 // accumulated from the same A fragments, so the row is read once.
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
   return __builtin_bit_cast(bf16x8_t, v);
@@ -423,13 +299,16 @@ __global__ __launch_bounds__(kThreads) void k_score_mfma(Geom g, const bf16_t* _
                                                              as_bf16x8(bq[ks]), acc[b], 0, 0, 0);
       }
       if (s_ok) {
-        // one 16-byte store per block into the token-fastest [slot][head][token] layout
+        // one 16-byte store per block into the token-fastest [slot][head][token]
+        // layout: a block covers 64 bytes of a (site, head) run, half a line,
+        // so these are plain stores, which L2 merges with the other half
+        // (non-temporal ones reached HBM as partial lines)
         float* base = proj + (int64_t)s * site_stride + ((int64_t)slot * g.H + h) * g.T;
 #pragma unroll
         for (int b = 0; b < TB; ++b) {
           float* dst = base + tq[b];
           if (vec[b]) {
-            st_stream(dst, make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]));
+            *reinterpret_cast<float4*>(dst) = make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
           } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
@@ -574,7 +453,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_score_wide(Geom g, const bf16_t*
       if (sv < s_hi) {
         float* dst = proj + (int64_t)sv * site_stride + ((int64_t)slot * g.H + h) * g.T + tq;
         if (vec) {
-          st_stream(dst, v);
+          *reinterpret_cast<float4*>(dst) = v;  // half a line: plain, as in k_score_mfma
         } else {
           const float vv[4] = {v.x, v.y, v.z, v.w};
           for (int j = 0; j < 4; ++j)
@@ -959,7 +838,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
       for (int r = 0; r < RB; ++r) {
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
-          float part = dot_chunk<T>(dov[j], cur[r][j]);
+          float part = Vec<T>::dot(dov[j], cur[r][j]);
           if (sh) part = quad_sum(part);
           if (sl[j].own && (sl[j].q & ((1 << sh) - 1)) == 0)
             s_part[((r * plen) >> sh) + (sl[j].q >> sh)] = part;
@@ -1190,7 +1069,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site_w(
         }
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
-          float part = dot_chunk<T>(dov[j], buf[d][j]);
+          float part = Vec<T>::dot(dov[j], buf[d][j]);
           if (quad) {
             part = quad_sum(part);
             if ((q[j] & 3) == 0) w_part[q[j] >> 2] = part;
@@ -1812,11 +1691,11 @@ __global__ __launch_bounds__(kThreads) void k_fold_gains(const T* __restrict__ q
       qv = __uint_as_float((uint32_t)q[i] << 16);
     }
     const float e = qv * gain[i];
-    const uint32_t hi = f32_to_bf16_bits(e);
+    const uint32_t hi = bf16_bits(e);
     qf[i] = e;
     q32[i] = qv;
     qhi[i] = (bf16_t)hi;
-    qlo[i] = (bf16_t)f32_to_bf16_bits(e - __uint_as_float(hi << 16));
+    qlo[i] = (bf16_t)bf16_bits(e - __uint_as_float(hi << 16));
   }
 }
 

@@ -32,12 +32,13 @@
 
 #include <mutex>
 
+#include "attnres_device.h"
 #include "attnres_internal.h"
 
 namespace attnres {
 namespace {
 
-typedef uint16_t bf16_t;
+using namespace dev;
 
 constexpr int kLFwdThreads = 256;  // forward: 4 waves per work-group
 
@@ -52,28 +53,8 @@ __device__ __forceinline__ float ld1<bf16_t>(const bf16_t* p) {
   return __uint_as_float((uint32_t)*p << 16);
 }
 
-__device__ __forceinline__ uint32_t to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);                                  // round to nearest even
-  return u >> 16;
-}
-
 __device__ __forceinline__ void st1(float* p, float v) { *p = v; }
-__device__ __forceinline__ void st1(bf16_t* p, float v) { *p = (bf16_t)to_bf16_bits(v); }
-
-__device__ __forceinline__ float wave_sum(float v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
-// LDS accesses of one wave execute in order; this keeps the compiler from
-// moving them across the point where lanes read what other lanes wrote.
-__device__ __forceinline__ void wave_lds_fence() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-}
+__device__ __forceinline__ void st1(bf16_t* p, float v) { *p = (bf16_t)bf16_bits(v); }
 
 template <typename T>
 __device__ __forceinline__ const T* row_of(const ListArgs& a, int n, int64_t t) {
@@ -124,10 +105,10 @@ __device__ __forceinline__ void store_run(T* p, const float* v) {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
   } else {
     uint4 w;
-    w.x = to_bf16_bits(v[0]) | (to_bf16_bits(v[1]) << 16);
-    w.y = to_bf16_bits(v[2]) | (to_bf16_bits(v[3]) << 16);
-    w.z = to_bf16_bits(v[4]) | (to_bf16_bits(v[5]) << 16);
-    w.w = to_bf16_bits(v[6]) | (to_bf16_bits(v[7]) << 16);
+    w.x = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
+    w.y = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
+    w.z = bf16_bits(v[4]) | (bf16_bits(v[5]) << 16);
+    w.w = bf16_bits(v[6]) | (bf16_bits(v[7]) << 16);
     *reinterpret_cast<uint4*>(p) = w;
   }
 }

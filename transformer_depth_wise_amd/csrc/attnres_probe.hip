@@ -5,20 +5,18 @@
 // loops over tiles with the grid as stride.  Words past the last whole tile
 // are taken by a grid-stride tail; a tail of fewer than 16 bytes is ignored.
 
+#include "attnres_device.h"
 #include "attnres_internal.h"
 
 namespace attnres {
 namespace {
 
+using namespace dev;
+
 constexpr int kProbeThreads = 256;
 constexpr int kProbeWords = 5;  // 16-byte words per thread per tile
 constexpr int64_t kProbeTile = (int64_t)kProbeThreads * kProbeWords;
 
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ u32x4_t ld_nt(const uint4* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-}
 
 __global__ __launch_bounds__(kProbeThreads) void k_probe_read(const uint4* __restrict__ src,
                                                                int64_t words,
@@ -27,15 +25,15 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_read(const uint4* __res
   uint32_t a = 0;
   for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
     const uint4* p = src + tile * kProbeTile + threadIdx.x;
-    u32x4_t v[kProbeWords];
+    uint4 v[kProbeWords];
 #pragma unroll
-    for (int j = 0; j < kProbeWords; ++j) v[j] = ld_nt(p + j * kProbeThreads);
+    for (int j = 0; j < kProbeWords; ++j) v[j] = ld_stream(p + j * kProbeThreads);
 #pragma unroll
     for (int j = 0; j < kProbeWords; ++j) a ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
   }
   for (int64_t i = tiles * kProbeTile + (int64_t)blockIdx.x * kProbeThreads + threadIdx.x;
        i < words; i += (int64_t)gridDim.x * kProbeThreads) {
-    const u32x4_t v = ld_nt(src + i);
+    const uint4 v = ld_stream(src + i);
     a ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   // one word per work-group keeps the loads live
@@ -55,16 +53,16 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_copy(const uint4* __res
   const int64_t tiles = words / kProbeTile;
   for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
     const int64_t base = tile * kProbeTile + threadIdx.x;
-    u32x4_t v[kProbeWords];
+    uint4 v[kProbeWords];
 #pragma unroll
-    for (int j = 0; j < kProbeWords; ++j) v[j] = ld_nt(src + base + j * kProbeThreads);
+    for (int j = 0; j < kProbeWords; ++j) v[j] = ld_stream(src + base + j * kProbeThreads);
 #pragma unroll
     for (int j = 0; j < kProbeWords; ++j)
-      __builtin_nontemporal_store(v[j], reinterpret_cast<u32x4_t*>(dst + base + j * kProbeThreads));
+      st_stream(dst + base + j * kProbeThreads, v[j]);
   }
   for (int64_t i = tiles * kProbeTile + (int64_t)blockIdx.x * kProbeThreads + threadIdx.x;
        i < words; i += (int64_t)gridDim.x * kProbeThreads)
-    __builtin_nontemporal_store(ld_nt(src + i), reinterpret_cast<u32x4_t*>(dst + i));
+    st_stream(dst + i, ld_stream(src + i));
 }
 
 }  // namespace
