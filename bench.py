@@ -34,11 +34,22 @@ METRIC = "routing ms/microbatch fwd+bwd and achieved HBM GB/s (% of peak), 1 MI3
 HBM_PEAK_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 # Sources whose change makes a stored counter summary stale.
-KERNEL_SOURCES = ("transformer_depth_wise_amd/csrc/attnres_kernels.hip",
-                  "transformer_depth_wise_amd/csrc/attnres_delta.hip",
-                  "transformer_depth_wise_amd/csrc/attnres_list.hip",
-                  "transformer_depth_wise_amd/csrc/attnres_internal.h",
-                  "transformer_depth_wise_amd/csrc/attnres_host.cpp")
+_CSRC = "transformer_depth_wise_amd/csrc/"
+# Sources every workload's kernels and launches depend on, and those of each
+# path: a counter summary is stale once one of its workload's sources changed.
+COMMON_SOURCES = tuple(_CSRC + f for f in ("attnres_internal.h", "attnres_device.h",
+                                           "attnres_host.cpp", "attnres_probe.hip"))
+PATH_SOURCES = {"bank": (_CSRC + "attnres_kernels.hip",),
+                "delta": (_CSRC + "attnres_delta.hip", _CSRC + "attnres_kernels.hip"),
+                "list": (_CSRC + "attnres_list.hip", _CSRC + "attnres_kernels.hip")}
+
+
+def path_of(workload: str) -> str:
+    if workload.startswith("delta"):
+        return "delta"
+    if workload.startswith("list"):
+        return "list"
+    return "bank"
 # Kernel symbol -> kernel kind (the bank kinds are those of the library trace).
 KERNEL_KIND = (("k_score", "score"), ("k_fwd", "fwd"), ("k_bwd_site", "bwd_site"),
                ("k_dq_reduce", "dq_reduce"), ("k_finalize", "finalize"),
@@ -184,9 +195,11 @@ def bandwidth_probe(torch, reps: int = 10):
     return out
 
 
-def source_hash() -> str:
+def source_hash(workload: str = "mhar1b") -> str:
+    """Hash of the sources the workload's kernels are built from (the delta and
+    list reads also reduce their query gradients with the bank's dq kernel)."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in COMMON_SOURCES + PATH_SOURCES[path_of(workload)]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -224,7 +237,7 @@ def summarize_counters(pmc_dir: str, workload: str, copy_bytes: int, command: st
              f"# command: {command}",
              f"# calibration: copy probe of {copy_bytes} bytes in + out reads "
              f"FETCH_SIZE x{scale['FETCH_SIZE']:.4f}, WRITE_SIZE x{scale['WRITE_SIZE']:.4f}",
-             f"source_hash {source_hash()}",
+             f"source_hash {source_hash(workload)}",
              f"scale FETCH_SIZE {scale['FETCH_SIZE']:.6f} WRITE_SIZE {scale['WRITE_SIZE']:.6f}",
              "# kind dispatches fetch_kib write_kib fetch_bytes_calibrated write_bytes_calibrated"]
     total = 0.0
@@ -263,7 +276,7 @@ def summarize_activity(pmc_dir: str, workload: str, command: str):
     lines = [f"# Occupancy and VALU activity per dispatch, {workload}: rocprofv3 derived "
              f"counters {' and '.join(ACTIVITY_COUNTERS)} (percent, mean over dispatches)",
              f"# command: {command}",
-             f"source_hash {source_hash()}",
+             f"source_hash {source_hash(workload)}",
              "# kind dispatches occupancy_percent valu_busy_percent"]
     for kind in sorted(per["OccupancyPercent"]):
         occ = per["OccupancyPercent"][kind]
@@ -291,7 +304,7 @@ def load_counters(workload: str):
                 out[p[1]] = (float(p[5]), float(p[6]))
             elif p and p[0] == "hbm_bytes_per_microbatch":
                 out["_total"] = float(p[1])
-    return out if stamp == source_hash() else None
+    return out if stamp == source_hash(workload) else None
 
 
 def measured_fields(workload: str, ms: float, model_bytes: int, unit: str = "microbatch"):

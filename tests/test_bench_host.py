@@ -79,7 +79,7 @@ def test_counter_summary_is_calibrated_on_the_copy_probe(tmp_path, monkeypatch):
     assert m["achieved_gbps"] == round(total / 2.0 / 1e6, 1)
     assert m["model_gbps"] == 0.5 and m["alg_bytes_per_microbatch"] == 1000000
     with open(bench.counters_path("toy"), "w") as f:
-        f.write(text.replace(bench.source_hash(), "0" * 16))
+        f.write(text.replace(bench.source_hash("toy"), "0" * 16))
     assert bench.load_counters("toy") is None
 
 
@@ -96,6 +96,14 @@ def test_counter_summary_is_calibrated_on_the_copy_probe(tmp_path, monkeypatch):
 ])
 def test_kernel_kinds(name, kind):
     assert bench.kind_of(name) == kind
+
+
+def test_source_hash_follows_the_workload_path():
+    assert bench.path_of("delta8b") == "delta" and bench.path_of("list_lr") == "list"
+    assert bench.path_of("mhar1b") == "bank" and bench.path_of("k3_blocks") == "bank"
+    assert bench.source_hash("mhar1b") == bench.source_hash("k3")
+    assert bench.source_hash("mhar1b") != bench.source_hash("delta8b")
+    assert bench.source_hash("list_lr") != bench.source_hash("delta8b")
 
 
 def test_kernel_stats_summary(tmp_path):
