@@ -111,58 +111,107 @@ def cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
-def cpu_baseline(name: str, tokens: int, full_tokens: int):
-    """Time the fp64 oracle on a bounded token sample of the workload, one
-    thread, and scale linearly in tokens to ms per microbatch."""
-    import numpy as np
+def oracle_cores() -> int:
+    """Host threads the CPU baseline runs the oracle on: the CPUs this process
+    may use, at most 16 (one GPU's share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def timed_token_chunks(run, tokens: int, cores: int):
+    """Wall time of run(lo, hi) over at most `cores` contiguous token chunks,
+    one thread each, with BLAS held to one thread per call.  Every formula of
+    the read is independent per token, so the chunks together do the work of
+    one oracle call over all tokens; NumPy releases the interpreter lock inside
+    its kernels, so they run in parallel.  Returns (seconds, threads used)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     from threadpoolctl import threadpool_limits
 
-    from oracle import run_schedule
-    from synth import Inputs, get_workload
-
-    w = get_workload(name).with_tokens(tokens)
-    inp = Inputs(w)
-    rows = np.stack([inp.row(n) for n in range(w.rows)]).astype(np.float64)
-    extras = [None if inp.extra(s) is None else inp.extra(s).astype(np.float64)
-              for s in range(w.sites)]
-    douts = np.stack([inp.dout(s) for s in range(w.sites)]).astype(np.float64)
-    q = inp.queries().astype(np.float64)
-    with threadpool_limits(limits=1):
+    step = -(-tokens // max(1, cores))
+    bounds = [(a, min(a + step, tokens)) for a in range(0, tokens, step)]
+    with threadpool_limits(limits=1), ThreadPoolExecutor(len(bounds)) as pool:
         t0 = time.perf_counter()
-        gains = inp.gains()
-        run_schedule(rows, extras, q, douts, list(w.nsrc), w.heads, w.r, w.eps,
-                     gains=None if gains is None else gains.astype(np.float64), norm=w.norm)
-        dt = time.perf_counter() - t0
-    ms = dt * 1e3 * full_tokens / tokens
+        for _ in pool.map(lambda b: run(*b), bounds):
+            pass
+        return time.perf_counter() - t0, len(bounds)
+
+
+# Wall time of oracle work the default CPU-baseline sample is sized to, from a
+# one-thread run on a few tokens (larger samples run somewhat slower per token,
+# so the run itself takes about 10-20 s), and the most tokens it takes.
+CPU_TARGET_S = 8.0
+CPU_MAX_TOKENS = 4096
+
+
+def oracle_baseline(prepare, full_tokens: int, unit: str, what: str, tokens=None,
+                    probe_tokens: int = 16):
+    """The fp64 oracle timed on the host's cores over a bounded token sample of
+    a workload and scaled linearly in tokens to the workload's unit.
+
+    prepare(n) draws the workload's inputs at n tokens and returns run(lo, hi),
+    the oracle over tokens [lo, hi).  Without a fixed `tokens` the sample is
+    sized to about CPU_TARGET_S seconds on all cores from a one-thread run on
+    probe_tokens tokens."""
+    cores = oracle_cores()
+    if tokens is None:
+        n = min(probe_tokens, full_tokens)
+        dt, _ = timed_token_chunks(prepare(n), n, 1)
+        per_token_s = max(dt / n, 1e-9)
+        tokens = int(min(full_tokens, CPU_MAX_TOKENS,
+                         max(n, CPU_TARGET_S * cores / per_token_s)))
+        if tokens > 16:
+            tokens -= tokens % 16
+    dt, used = timed_token_chunks(prepare(tokens), tokens, cores)
     return {
-        "value": round(ms, 1),
-        "unit": "ms/microbatch",
-        "cores": 1,
+        "value": round(dt * 1e3 * full_tokens / tokens, 1),
+        "unit": unit,
+        "cores": used,
         "kind": "oracle",
-        "sample": (f"{tokens} of {full_tokens} tokens, all {w.sites} sites fwd+bwd, NumPy fp64 "
-                   f"oracle on one thread ({cpu_model()}; "
+        "sample": (f"{tokens} of {full_tokens} tokens, {what}, NumPy fp64 oracle in {used} "
+                   f"token chunks on {used} threads ({cpu_model()}; "
                    f"{len(os.sched_getaffinity(0))} cores visible); measured {dt:.2f} s, "
                    f"scaled linearly in tokens"),
     }
 
 
-# Oracle time the default CPU-baseline sample is sized to from a 16-token run
-# (larger samples run somewhat slower per token, so the run itself takes
-# about 10-20 s), and the most tokens it takes.
-CPU_TARGET_S = 8.0
-CPU_MAX_TOKENS = 1024
+def cpu_baseline(name: str, full_tokens: int, tokens=None):
+    """The bank workload's whole microbatch (every site, forward and backward)
+    on the oracle."""
+    import numpy as np
+
+    from oracle import run_schedule
+    from synth import Inputs, get_workload
+
+    def prepare(n):
+        w = get_workload(name).with_tokens(n)
+        inp = Inputs(w)
+        rows = np.stack([inp.row(k) for k in range(w.rows)]).astype(np.float64)
+        extras = [None if inp.extra(s) is None else inp.extra(s).astype(np.float64)
+                  for s in range(w.sites)]
+        douts = np.stack([inp.dout(s) for s in range(w.sites)]).astype(np.float64)
+        q = inp.queries().astype(np.float64)
+        gains = inp.gains()
+        gains = None if gains is None else gains.astype(np.float64)
+
+        def run(lo, hi):
+            ex = [None if e is None else e[lo:hi] for e in extras]
+            run_schedule(rows[:, lo:hi], ex, q, douts[:, lo:hi], list(w.nsrc), w.heads, w.r,
+                         w.eps, gains=gains, norm=w.norm)
+        return run
+
+    sites = get_workload(name).sites
+    return oracle_baseline(prepare, full_tokens, "ms/microbatch",
+                           f"all {sites} sites fwd+bwd", tokens)
 
 
 def sized_cpu_baseline(args, w):
     """The oracle baseline on args.cpu_tokens tokens, or on a sample sized to
-    about CPU_TARGET_S seconds from a 16-token run."""
-    if args.cpu_tokens is not None:
-        return cpu_baseline(args.workload, args.cpu_tokens, w.tokens)
-    probe = cpu_baseline(args.workload, 16, w.tokens)
-    per_token_s = probe["value"] / 1e3 / w.tokens
-    tokens = int(min(w.tokens, CPU_MAX_TOKENS, max(16, CPU_TARGET_S / max(per_token_s, 1e-9))))
-    tokens -= tokens % 8 if tokens > 16 else 0
-    return probe if tokens <= 16 else cpu_baseline(args.workload, tokens, w.tokens)
+    about CPU_TARGET_S seconds of wall time."""
+    return cpu_baseline(args.workload, w.tokens, args.cpu_tokens)
 
 
 PROBE_BYTES = 2 << 30  # bytes each bandwidth probe reads
@@ -380,36 +429,30 @@ def delta_bytes(shape, m: int):
     return fwd, bwd
 
 
-def delta_cpu_baseline(shape, tokens: int):
+def delta_cpu_baseline(shape, tokens=None):
+    """Every call of the delta microbatch, forward and backward, on the oracle."""
     import numpy as np
-    from threadpoolctl import threadpool_limits
 
     from oracle import delta_backward, delta_forward
     from synth import DeltaInputs
 
-    s = shape.with_tokens(tokens)
-    inp = DeltaInputs(s)
-    deltas = np.stack([inp.value("delta", m) for m in range(s.n_deltas)]).astype(np.float64)
-    null = inp.value("null").astype(np.float64)
-    q = inp.value("query").astype(np.float64)
-    part = inp.value("partial").astype(np.float64)
-    dout = inp.value("dout").astype(np.float64)
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        for m in delta_schedule():
-            delta_forward(null, deltas[:m], q, part, s.heads, s.eps)
-            delta_backward(null, deltas[:m], q, dout, s.heads, s.eps)
-        dt = time.perf_counter() - t0
-    return {
-        "value": round(dt * 1e3 * shape.tokens / tokens, 1),
-        "unit": "ms/microbatch",
-        "cores": 1,
-        "kind": "oracle",
-        "sample": (f"{tokens} of {shape.tokens} tokens, all {DELTA_SITES} calls fwd+bwd, NumPy "
-                   f"fp64 oracle on one thread ({cpu_model()}); measured {dt:.2f} s, scaled "
-                   f"linearly in tokens"),
-    }
+    def prepare(n):
+        s = shape.with_tokens(n)
+        inp = DeltaInputs(s)
+        deltas = np.stack([inp.value("delta", m) for m in range(s.n_deltas)]).astype(np.float64)
+        null = inp.value("null").astype(np.float64)
+        q = inp.value("query").astype(np.float64)
+        part = inp.value("partial").astype(np.float64)
+        dout = inp.value("dout").astype(np.float64)
 
+        def run(lo, hi):
+            for m in delta_schedule():
+                delta_forward(null, deltas[:m, lo:hi], q, part[lo:hi], s.heads, s.eps)
+                delta_backward(null, deltas[:m, lo:hi], q, dout[lo:hi], s.heads, s.eps)
+        return run
+
+    return oracle_baseline(prepare, shape.tokens, "ms/microbatch",
+                           f"all {DELTA_SITES} calls fwd+bwd", tokens)
 
 def bench_delta(args):
     import torch
@@ -515,7 +558,7 @@ def bench_delta(args):
         "probe": probe,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = delta_cpu_baseline(shape, 16)
+        result["cpu_baseline"] = delta_cpu_baseline(shape, args.cpu_tokens)
     print(json.dumps(result), flush=True)
 
 
@@ -532,32 +575,27 @@ def list_bytes(shape):
     return fwd, bwd
 
 
-def list_cpu_baseline(shape, tokens: int):
+def list_cpu_baseline(shape, tokens=None):
+    """One source-list read, forward and backward, on the oracle."""
     import numpy as np
-    from threadpoolctl import threadpool_limits
 
     from oracle import route_backward, route_forward
     from synth import ListInputs
 
-    s = shape.with_tokens(tokens)
-    inp = ListInputs(s)
-    src = inp.entry_values().astype(np.float64)
-    q = inp.value("query").astype(np.float64)
-    dout = inp.value("dout").astype(np.float64)
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        route_forward(src, q, s.heads, s.r, s.eps, norm=s.norm)
-        route_backward(src, q, s.heads, s.r, dout, s.eps, norm=s.norm)
-        dt = time.perf_counter() - t0
-    return {
-        "value": round(dt * 1e3 * shape.tokens / tokens, 1),
-        "unit": "ms/read",
-        "cores": 1,
-        "kind": "oracle",
-        "sample": (f"{tokens} of {shape.tokens} tokens, one read fwd+bwd, NumPy fp64 oracle on "
-                   f"one thread ({cpu_model()}); measured {dt:.2f} s, scaled linearly in tokens"),
-    }
+    def prepare(n):
+        s = shape.with_tokens(n)
+        inp = ListInputs(s)
+        src = inp.entry_values().astype(np.float64)
+        q = inp.value("query").astype(np.float64)
+        dout = inp.value("dout").astype(np.float64)
 
+        def run(lo, hi):
+            route_forward(src[:, lo:hi], q, s.heads, s.r, s.eps, norm=s.norm)
+            route_backward(src[:, lo:hi], q, s.heads, s.r, dout[lo:hi], s.eps, norm=s.norm)
+        return run
+
+    return oracle_baseline(prepare, shape.tokens, "ms/read", "one read fwd+bwd", tokens,
+                           probe_tokens=64)
 
 def bench_list(args):
     import torch
@@ -627,11 +665,7 @@ def bench_list(args):
         "probe": probe,
     }
     if not args.no_cpu_baseline:
-        # size the sample to about 10 s of oracle time from a 64-token run
-        probe = list_cpu_baseline(shape, 64)
-        per_token_s = probe["value"] / 1e3 / shape.tokens
-        tokens = int(min(shape.tokens, max(64, 10.0 / max(per_token_s, 1e-9))))
-        result["cpu_baseline"] = probe if tokens == 64 else list_cpu_baseline(shape, tokens)
+        result["cpu_baseline"] = list_cpu_baseline(shape, args.cpu_tokens)
     print(json.dumps(result), flush=True)
 
 
@@ -654,35 +688,32 @@ def block_accumulate_bytes(shape):
     return total, shape.sublayers
 
 
-def blocks_cpu_baseline(shape, tokens: int):
+def blocks_cpu_baseline(shape, tokens=None):
+    """Every read of the block-routing microbatch, forward and backward with
+    exact block sums, on the oracle."""
     import numpy as np
-    from threadpoolctl import threadpool_limits
 
     from oracle import run_block_routing
     from synth import BlockInputs
     from synth.blocks import BlockShape
 
-    s = BlockShape(shape.name, tokens, shape.d, shape.r, shape.heads, shape.sublayers,
-                   shape.blocks, shape.dtype, shape.norm, shape.qscale, shape.eps, shape.seed)
-    inp = BlockInputs(s)
-    M = s.sublayers
-    ys = np.stack([inp.y(t % BLOCK_DRAWS) for t in range(M)])
-    q = np.stack([inp.query(t) for t in range(M)])
-    douts = np.stack([inp.dout(t % BLOCK_DRAWS) for t in range(M)])
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        run_block_routing(inp.x(), ys, q, douts, s.ends(), s.heads, s.r, s.eps, norm=s.norm)
-        dt = time.perf_counter() - t0
-    return {
-        "value": round(dt * 1e3 * shape.tokens / tokens, 1),
-        "unit": "ms/microbatch",
-        "cores": 1,
-        "kind": "oracle",
-        "sample": (f"{tokens} of {shape.tokens} tokens, all {M} reads fwd+bwd with exact block "
-                   f"sums, NumPy fp64 oracle on one thread ({cpu_model()}); measured {dt:.2f} s, "
-                   f"scaled linearly in tokens"),
-    }
+    def prepare(n):
+        s = BlockShape(shape.name, n, shape.d, shape.r, shape.heads, shape.sublayers,
+                       shape.blocks, shape.dtype, shape.norm, shape.qscale, shape.eps, shape.seed)
+        inp = BlockInputs(s)
+        M = s.sublayers
+        x = inp.x()
+        ys = np.stack([inp.y(t % BLOCK_DRAWS) for t in range(M)])
+        q = np.stack([inp.query(t) for t in range(M)])
+        douts = np.stack([inp.dout(t % BLOCK_DRAWS) for t in range(M)])
 
+        def run(lo, hi):
+            run_block_routing(x[lo:hi], ys[:, lo:hi], q, douts[:, lo:hi], s.ends(), s.heads,
+                              s.r, s.eps, norm=s.norm)
+        return run
+
+    return oracle_baseline(prepare, shape.tokens, "ms/microbatch",
+                           f"all {shape.sublayers} reads fwd+bwd with exact block sums", tokens)
 
 def bench_blocks(args):
     import torch
@@ -729,7 +760,7 @@ def bench_blocks(args):
         "workload": shape.name, "tokens": T, "d": d, "r": shape.r, "heads": shape.heads,
         "sublayers": M, "blocks": shape.blocks, "storage": shape.dtype, "norm": shape.norm,
         "block_sums": "kept by the bank (attnres_bank_accumulate)",
-    }, cpu=lambda: blocks_cpu_baseline(shape, args.cpu_tokens or 16))
+    }, cpu=lambda: blocks_cpu_baseline(shape, args.cpu_tokens))
 
 
 def main():

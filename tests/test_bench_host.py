@@ -128,3 +128,26 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300)
     assert p.returncode == 2
     assert "one GPU" in p.stderr
+
+
+def test_cpu_baseline_chunks_cover_every_token_once():
+    import threading
+
+    seen, lock = [], threading.Lock()
+
+    def prepare(n):
+        def run(lo, hi):
+            with lock:
+                seen.append((n, lo, hi))
+        return run
+
+    res = bench.oracle_baseline(prepare, 1000, "ms/microbatch", "toy", tokens=37)
+    chunks = sorted((lo, hi) for n, lo, hi in seen if n == 37)
+    assert chunks[0][0] == 0 and chunks[-1][1] == 37
+    assert all(a[1] == b[0] for a, b in zip(chunks, chunks[1:]))
+    assert res["cores"] == len(chunks) <= bench.oracle_cores() <= 16
+    assert res["kind"] == "oracle" and res["unit"] == "ms/microbatch"
+    # the default sample is sized from a one-thread probe on a few tokens
+    seen.clear()
+    bench.oracle_baseline(prepare, 64, "ms/read", "toy")
+    assert seen[0] == (16, 0, 16)
