@@ -1002,6 +1002,8 @@ attnres_status_t list_geom(const attnres_list_t* c, attnres::ListGeom* g) {
   g->w = c->d - g->n0;
   g->qs = c->query_stride;
   g->eps = c->eps;
+  g->lanes_log2 = 0;
+  while ((2 << g->lanes_log2) * (int64_t)g->H <= 64) ++g->lanes_log2;
   return ATTNRES_OK;
 }
 

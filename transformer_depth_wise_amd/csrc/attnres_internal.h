@@ -181,6 +181,7 @@ struct ListGeom {
   int64_t qs;  // query stride in elements
   float eps;
   int32_t vec;  // 1: every row, head, stride and pointer allows 16-byte runs (unit query stride)
+  int32_t lanes_log2;  // log2 of the lanes per head group: the largest L with L * H <= 64 (>= 1)
 };
 struct ListArgs {
   const void* src[kMaxListSources];
@@ -197,7 +198,7 @@ __host__ __device__ inline int list_bwd_wave_floats(const ListGeom& g) {
 }
 size_t list_fwd_lds_bytes(const ListGeom& g);
 int list_bwd_waves_per_group(const ListGeom& g);
-// Waves of the backward grid = dq partial rows [parts][r] (0 when T == 0).
+// Work-groups of the backward grid = dq partial rows [parts][r] (0 when T == 0).
 int list_bwd_parts(const ListGeom& g);
 hipError_t launch_list_fwd(const ListGeom& g, int dtype, const ListArgs& a, void* out,
                            float* alpha, float* lse, float* rinv, hipStream_t st);

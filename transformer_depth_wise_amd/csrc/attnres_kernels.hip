@@ -1175,8 +1175,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site_w(
 // ---------------------------------------------------------------------------
 // Sum the [parts, r] query-gradient partials in a fixed order.
 // One 1024-thread work-group per 64 columns: wave w sums rows w, w+16, ...
-// with four independent accumulators, then wave 0 adds the 16 wave sums.
+// with eight independent accumulators (their loads issued together), then
+// wave 0 adds the 16 wave sums.
 constexpr int kReduceThreads = 1024;
+constexpr int kReduceAcc = 8;
 __global__ __launch_bounds__(kReduceThreads) void k_dq_reduce(const float* __restrict__ part,
                                                                int parts, int r,
                                                                float* __restrict__ dq,
@@ -1187,18 +1189,25 @@ __global__ __launch_bounds__(kReduceThreads) void k_dq_reduce(const float* __res
   __shared__ float red[W][64];
   const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
   const int col = blockIdx.x * 64 + lane;
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  float a[kReduceAcc];
+#pragma unroll
+  for (int k = 0; k < kReduceAcc; ++k) a[k] = 0.f;
   if (col < r) {
     int i = grp;
-    for (; i + 3 * W < parts; i += 4 * W) {
-      a0 += part[(int64_t)i * r + col];
-      a1 += part[(int64_t)(i + W) * r + col];
-      a2 += part[(int64_t)(i + 2 * W) * r + col];
-      a3 += part[(int64_t)(i + 3 * W) * r + col];
+    for (; i + (kReduceAcc - 1) * W < parts; i += kReduceAcc * W) {
+      float v[kReduceAcc];
+#pragma unroll
+      for (int k = 0; k < kReduceAcc; ++k) v[k] = part[(int64_t)(i + k * W) * r + col];
+#pragma unroll
+      for (int k = 0; k < kReduceAcc; ++k) a[k] += v[k];
     }
-    for (; i < parts; i += W) a0 += part[(int64_t)i * r + col];
+    for (; i < parts; i += W) a[0] += part[(int64_t)i * r + col];
   }
-  red[grp][lane] = (a0 + a1) + (a2 + a3);
+#pragma unroll
+  for (int w = kReduceAcc / 2; w > 0; w >>= 1)
+#pragma unroll
+    for (int k = 0; k < w; ++k) a[k] += a[k + w];
+  red[grp][lane] = a[0];
   __syncthreads();
   if (grp == 0 && col < r) {
     float s = 0.f;

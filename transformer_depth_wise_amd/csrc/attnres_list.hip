@@ -13,7 +13,9 @@
 // key boundary or a key head.
 //
 // One wave per token, grid-stride over tokens; per-(token, head) reductions
-// are wave sums, so no work-group barrier is needed.
+// are sums within a lane group per head (or wave sums), so no work-group
+// barrier is needed.  Each token's upstream gradient is read once for all
+// sources, plus once more over the norm coordinates.
 //   Forward: per source, the per-head dots of the query with the key and the
 //   sum of squares over the norm coordinates; the logits l = rinv * dot; the
 //   softmax over sources per head; the mix of all d coordinates.
@@ -31,6 +33,7 @@
 #include <math.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "attnres_device.h"
 #include "attnres_internal.h"
@@ -61,40 +64,63 @@ __device__ __forceinline__ const T* row_of(const ListArgs& a, int n, int64_t t) 
   return static_cast<const T*>(a.src[n]) + t * a.stride[n];
 }
 
-// Sources are taken kGroup at a time (4 measured fastest of 2, 3, 4 and 8):
-// their loads are issued together and their wave sums interleave, instead
-// of one source's dot waiting for the previous one's reduction.  Slots past
-// the last source read the last source again (valid memory) and their
-// results are dropped.
-constexpr int kGroup = 4;
+// Loads in flight per lane: G sources (slots past the last source read the
+// last source again, valid memory, and their results are dropped) times
+// U chunks per batch (U per pass), all issued before the arithmetic that uses them.
+template <typename T, int VW>
+struct ListTile {
+  static constexpr int G = 5;
+  static constexpr int UK = VW == 1 ? 4 : 2;  // forward key pass
+  static constexpr int UM = VW == 1 ? 8 : 2;  // forward mix
+  static constexpr int UP = VW == 1 ? 4 : 2;  // backward P pass
+  static constexpr int UG = VW == 1 ? 4 : 2;  // backward gradient pass
+};
 
 // VW consecutive elements of one lane: VW = 1 (any alignment), or one 16-byte
 // chunk (8 bf16 or 4 fp32 values) when every row, head and pointer is
-// aligned to it.
+// aligned to it.  The chunk stays packed until an element is used.
+template <typename T, int VW>
+struct Run;
+
+template <typename T>
+struct Run<T, 1> {
+  uint32_t w;  // raw bits, widened at use
+  __device__ __forceinline__ void load(const T* p) {
+    if constexpr (sizeof(T) == 4) {
+      w = __float_as_uint(*reinterpret_cast<const float*>(p));
+    } else {
+      w = *p;
+    }
+  }
+  __device__ __forceinline__ float operator[](int) const {
+    return __uint_as_float(sizeof(T) == 4 ? w : w << 16);
+  }
+};
+
 template <typename T, int VW>
 struct Run {
-  float v[VW];
-  __device__ __forceinline__ void load(const T* p) {
-    if constexpr (VW == 1) {
-      v[0] = ld1(p);
+  uint4 w;
+  __device__ __forceinline__ void load(const T* p) { w = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ float operator[](int e) const {
+    constexpr int per = 4 / (int)sizeof(T) > 0 ? 4 / (int)sizeof(T) : 1;  // values per 32-bit word
+    const int k = e / per;
+    const uint32_t u = k == 0 ? w.x : (k == 1 ? w.y : (k == 2 ? w.z : w.w));
+    if constexpr (sizeof(T) == 4) {
+      return __uint_as_float(u);
     } else {
-      const uint4 w = *reinterpret_cast<const uint4*>(p);
-      if constexpr (sizeof(T) == 4) {
-        v[0] = __uint_as_float(w.x);
-        v[1] = __uint_as_float(w.y);
-        v[2] = __uint_as_float(w.z);
-        v[3] = __uint_as_float(w.w);
-      } else {
-        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[2 * i] = __uint_as_float(u[i] << 16);
-          v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
-        }
-      }
+      return __uint_as_float((e & 1) ? (u & 0xffff0000u) : (u << 16));
     }
   }
 };
+
+// p + i with the byte offset formed in 32 bits: a uniform row address plus a
+// 32-bit lane offset, which the loads and stores take as a scalar base and a
+// vector offset (every byte offset within one row is below 2^31).
+template <typename P>
+__device__ __forceinline__ P* at(P* p, int i) {
+  typedef typename std::conditional<std::is_const<P>::value, const char, char>::type B;
+  return reinterpret_cast<P*>(reinterpret_cast<B*>(p) + (uint32_t)(i * (int)sizeof(P)));
+}
 
 // Store VW values to storage dtype T.
 template <typename T, int VW>
@@ -125,71 +151,131 @@ __device__ __forceinline__ void store_f32(float* p, const float* v) {
   }
 }
 
-template <typename T, int VW>
+// Sum over the aligned group of 2^lg lanes that holds one head (butterfly:
+// every lane of the group ends with the same value).  Every lane of the wave
+// must take part.
+__device__ __forceinline__ float group_sum(float v, int lg) {
+  for (int o = 1; o < (1 << lg); o <<= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Per-lane head groups: lanes form 64 / L groups of L = 2^lanes_log2 lanes,
+// group k taking heads k, k + 64 / L, ... in turn (one pass when H <= 64).
+// Within its head a lane takes chunks sl, sl + L, ... (sl = lane mod L), so
+// every head of a source is dotted in the same pass and summed in log2 L
+// steps, instead of one wave-wide sum per head.
+struct HeadLanes {
+  int lg, L, slots, slot, sl, passes;
+  __device__ HeadLanes(const ListGeom& g, int lane) {
+    lg = g.lanes_log2;
+    L = 1 << lg;
+    slots = 64 >> lg;
+    slot = lane >> lg;
+    sl = lane & (L - 1);
+    passes = (g.H + slots - 1) / slots;
+  }
+};
+
+// Forward, one wave per token.  Key pass: G sources at a time, each lane
+// group dotting its head's key chunks (UK chunks per lane per batch).  Mix:
+// consecutive chunks over all 64 lanes, UM per lane, gathering G sources per
+// round.  Chunks past the end are clamped to a valid one and masked at use,
+// so every load of a round is issued unconditionally, before the arithmetic.
+template <typename T, int VW, int G, int UK, int UM>
 __global__ __launch_bounds__(kLFwdThreads) void k_list_fwd(ListGeom g, ListArgs a,
                                                            T* __restrict__ out,
                                                            float* __restrict__ alpha,
                                                            float* __restrict__ lse,
                                                            float* __restrict__ rinv_out) {
   extern __shared__ float sm[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index is the same for all its lanes: made uniform, the row
+  // addresses derived from it stay in scalar registers
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nh = g.n * g.H;
   float* w_a = sm + wave * (nh + g.n);  // [n][H] dots, then weights
   float* w_r = w_a + nh;                // [n] inverse RMS
   const T* q = static_cast<const T*>(a.query);
+  const HeadLanes hl(g, lane);
+  const int kkc = g.kk / VW, dc = g.d / VW, kc0 = g.k0 / VW;
+  const int kb = (kkc + hl.L * UK - 1) / (hl.L * UK);  // key batches per head, the same for all lanes
   const int64_t waves = (int64_t)gridDim.x * (kLFwdThreads / 64);
   for (int64_t t = (int64_t)blockIdx.x * (kLFwdThreads / 64) + wave; t < g.T; t += waves) {
-    for (int n0 = 0; n0 < g.n; n0 += kGroup) {
-      const T* s[kGroup];
-      float ss[kGroup];
+    for (int n0 = 0; n0 < g.n; n0 += G) {
+      const T* s[G];
+      float ss[G];
 #pragma unroll
-      for (int i = 0; i < kGroup; ++i) {
+      for (int i = 0; i < G; ++i) {
         s[i] = row_of<T>(a, min(n0 + i, g.n - 1), t);
         ss[i] = 0.f;
       }
-      for (int j = g.n0 + lane * VW; j < g.k0; j += 64 * VW) {  // norm coordinates outside the key
-        Run<T, VW> x[kGroup];
+      for (int m = 0; m < hl.passes; ++m) {
+        const int h = hl.slot + m * hl.slots;
+        const bool hv = h < g.H;
+        const int hc = hv ? h : 0;
+        const T* qh = q + (int64_t)hc * g.kk * g.qs;
+        const int kbase = g.k0 + hc * g.kk;
+        float dot[G];
 #pragma unroll
-        for (int i = 0; i < kGroup; ++i) x[i].load(s[i] + j);
+        for (int i = 0; i < G; ++i) dot[i] = 0.f;
+        for (int b = 0; b < kb; ++b) {
+          Run<T, VW> x[G][UK], qv[UK];
+          bool ok[UK];
 #pragma unroll
-        for (int i = 0; i < kGroup; ++i)
+          for (int u = 0; u < UK; ++u) {
+            const int c = hl.sl + hl.L * (b * UK + u);
+            ok[u] = hv && c < kkc;
+            const int cc = ok[u] ? c : 0;
+            if constexpr (VW == 1) {
+              qv[u].load(qh + (int64_t)cc * g.qs);
+            } else {
+              qv[u].load(qh + cc * VW);  // unit query stride on this path
+            }
 #pragma unroll
-          for (int e = 0; e < VW; ++e) ss[i] += x[i].v[e] * x[i].v[e];
-      }
-      for (int h = 0; h < g.H; ++h) {
-        const T* qh = q + (int64_t)h * g.kk * g.qs;
-        float dot[kGroup];
-#pragma unroll
-        for (int i = 0; i < kGroup; ++i) dot[i] = 0.f;
-        for (int k = lane * VW; k < g.kk; k += 64 * VW) {
-          Run<T, VW> x[kGroup], qv;
-          if constexpr (VW == 1) {
-            qv.v[0] = ld1(qh + (int64_t)k * g.qs);
-          } else {
-            qv.load(qh + k);  // unit query stride on this path
+            for (int i = 0; i < G; ++i) x[i][u].load(at(s[i], kbase + cc * VW));
           }
 #pragma unroll
-          for (int i = 0; i < kGroup; ++i) x[i].load(s[i] + g.k0 + h * g.kk + k);
+          for (int u = 0; u < UK; ++u)
 #pragma unroll
-          for (int i = 0; i < kGroup; ++i)
+            for (int i = 0; i < G; ++i)
 #pragma unroll
-            for (int e = 0; e < VW; ++e) {
-              ss[i] += x[i].v[e] * x[i].v[e];
-              dot[i] += x[i].v[e] * qv.v[e];
-            }
+              for (int e = 0; e < VW; ++e) {
+                const float xv = ok[u] ? x[i][u][e] : 0.f;
+                ss[i] += xv * xv;
+                dot[i] += xv * qv[u][e];
+              }
         }
 #pragma unroll
-        for (int i = 0; i < kGroup; ++i) dot[i] = wave_sum(dot[i]);
-        if (lane == 0)
+        for (int i = 0; i < G; ++i) dot[i] = group_sum(dot[i], hl.lg);
+        if (hl.sl == 0 && hv)
 #pragma unroll
-          for (int i = 0; i < kGroup; ++i)
+          for (int i = 0; i < G; ++i)
             if (n0 + i < g.n) w_a[(n0 + i) * g.H + h] = dot[i];
       }
+      for (int c0 = g.n0 / VW + lane; c0 < kc0; c0 += 64 * UK) {  // RMS coordinates outside the key
+        Run<T, VW> x[G][UK];
+        bool ok[UK];
 #pragma unroll
-      for (int i = 0; i < kGroup; ++i) ss[i] = wave_sum(ss[i]);
+        for (int u = 0; u < UK; ++u) {
+          ok[u] = c0 + 64 * u < kc0;
+          const int cc = ok[u] ? c0 + 64 * u : c0;
+#pragma unroll
+          for (int i = 0; i < G; ++i) x[i][u].load(at(s[i], cc * VW));
+        }
+#pragma unroll
+        for (int u = 0; u < UK; ++u)
+#pragma unroll
+          for (int i = 0; i < G; ++i)
+#pragma unroll
+            for (int e = 0; e < VW; ++e) {
+              const float xv = ok[u] ? x[i][u][e] : 0.f;
+              ss[i] += xv * xv;
+            }
+      }
+#pragma unroll
+      for (int i = 0; i < G; ++i) ss[i] = wave_sum(ss[i]);
       if (lane == 0)
 #pragma unroll
-        for (int i = 0; i < kGroup; ++i)
+        for (int i = 0; i < G; ++i)
           if (n0 + i < g.n) w_r[n0 + i] = 1.f / sqrtf(ss[i] / (float)g.w + g.eps);
     }
     wave_lds_fence();
@@ -210,32 +296,53 @@ __global__ __launch_bounds__(kLFwdThreads) void k_list_fwd(ListGeom g, ListArgs 
     for (int n = lane; n < g.n; n += 64) rinv_out[(int64_t)n * g.T + t] = w_r[n];
     wave_lds_fence();
     T* o = out + t * g.d;
-    for (int h = 0; h < g.H; ++h) {
-      for (int k = lane * VW; k < g.kv; k += 64 * VW) {
-        const int j = h * g.kv + k;
-        float acc[VW];
+    for (int c0 = lane; c0 < dc; c0 += 64 * UM) {
+      int cc[UM], hv[UM];
+      float acc[UM][VW];
 #pragma unroll
-        for (int e = 0; e < VW; ++e) acc[e] = 0.f;
-        for (int n0 = 0; n0 < g.n; n0 += kGroup) {
-          Run<T, VW> x[kGroup];
+      for (int u = 0; u < UM; ++u) {
+        cc[u] = c0 + 64 * u < dc ? c0 + 64 * u : c0;
+        hv[u] = cc[u] * VW / g.kv;
 #pragma unroll
-          for (int i = 0; i < kGroup; ++i) x[i].load(row_of<T>(a, min(n0 + i, g.n - 1), t) + j);
+        for (int e = 0; e < VW; ++e) acc[u][e] = 0.f;
+      }
+      for (int n0 = 0; n0 < g.n; n0 += G) {
+        Run<T, VW> x[G][UM];
 #pragma unroll
-          for (int i = 0; i < kGroup; ++i) {
-            if (n0 + i >= g.n) break;
-            const float al = w_a[(n0 + i) * g.H + h];
+        for (int i = 0; i < G; ++i) {
+          const T* s = row_of<T>(a, min(n0 + i, g.n - 1), t);
 #pragma unroll
-            for (int e = 0; e < VW; ++e) acc[e] += al * x[i].v[e];
+          for (int u = 0; u < UM; ++u) x[i][u].load(at(s, cc[u] * VW));
+        }
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+          if (n0 + i >= g.n) break;
+#pragma unroll
+          for (int u = 0; u < UM; ++u) {
+            const float al = w_a[(n0 + i) * g.H + hv[u]];
+#pragma unroll
+            for (int e = 0; e < VW; ++e) acc[u][e] += al * x[i][u][e];
           }
         }
-        store_run<T, VW>(o + j, acc);
       }
+#pragma unroll
+      for (int u = 0; u < UM; ++u)
+        if (c0 + 64 * u < dc) store_run<T, VW>(at(o, cc[u] * VW), acc[u]);
     }
     wave_lds_fence();  // the next token rewrites w_a
   }
 }
 
-template <typename T, int VW>
+// Backward, one wave per token.
+//   P pass: lane groups per value head; each batch of UP chunks loads the
+//   upstream gradient once and gathers all sources G at a time; P partials
+//   are summed per group and added to w_p.  Gradients of coordinates outside
+//   the RMS (a dout only) are written here.
+//   Gradient pass over the RMS coordinates [n0, d): consecutive chunks over
+//   all lanes, the upstream gradient and query chunks loaded once per batch
+//   for all sources.
+//   As in the forward, chunks past the end are clamped and masked.
+template <typename T, int VW, int G, int UP, int UG>
 __global__ __launch_bounds__(256) void k_list_bwd(ListGeom g, ListArgs a,
                                                   const T* __restrict__ dout,
                                                   const float* __restrict__ alpha,
@@ -243,7 +350,8 @@ __global__ __launch_bounds__(256) void k_list_bwd(ListGeom g, ListArgs a,
                                                   const float* __restrict__ rinv,
                                                   ListGrads gr, float* __restrict__ dq_part) {
   extern __shared__ float sm[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = blockDim.x >> 6;
   const int nh = g.n * g.H;
   float* w_dq = sm + (int64_t)wave * list_bwd_wave_floats(g);  // [r] this wave's dq
   float* w_a = w_dq + g.r;   // [n][H] weights
@@ -253,39 +361,82 @@ __global__ __launch_bounds__(256) void k_list_bwd(ListGeom g, ListArgs a,
   float* w_l = w_c + g.n;    // [H] lse
   for (int k = lane; k < g.r; k += 64) w_dq[k] = 0.f;
   const T* q = static_cast<const T*>(a.query);
+  const HeadLanes hl(g, lane);
+  const int kvc = g.kv / VW, dc = g.d / VW;
+  const int vb = (kvc + hl.L * UP - 1) / (hl.L * UP);  // value batches per head, the same for all lanes
   const int64_t waves = (int64_t)gridDim.x * nw;
   for (int64_t t = (int64_t)blockIdx.x * nw + wave; t < g.T; t += waves) {
     for (int i = lane; i < nh; i += 64) {
       const int n = i / g.H, h = i - n * g.H;
       w_a[i] = alpha[((int64_t)n * g.T + t) * g.H + h];
+      w_p[i] = 0.f;
     }
     for (int n = lane; n < g.n; n += 64) w_r[n] = rinv[(int64_t)n * g.T + t];
     for (int h = lane; h < g.H; h += 64) w_l[h] = lse[t * g.H + h];
+    wave_lds_fence();
     const T* go = dout + t * g.d;
-    for (int n0 = 0; n0 < g.n; n0 += kGroup) {
-      const T* s[kGroup];
+    for (int m = 0; m < hl.passes; ++m) {
+      const int h = hl.slot + m * hl.slots;
+      const bool hv = h < g.H;
+      const int hc = hv ? h : 0;
+      const int hb = hc * g.kv;  // first coordinate of the head
+      for (int b = 0; b < vb; ++b) {
+        Run<T, VW> y[UP];
+        bool ok[UP];
+        int cc[UP];
+        float ym[UP][VW];  // the upstream gradient, zero on masked chunks
 #pragma unroll
-      for (int i = 0; i < kGroup; ++i) s[i] = row_of<T>(a, min(n0 + i, g.n - 1), t);
-      for (int h = 0; h < g.H; ++h) {
-        float p[kGroup];
-#pragma unroll
-        for (int i = 0; i < kGroup; ++i) p[i] = 0.f;
-        for (int k = lane * VW; k < g.kv; k += 64 * VW) {
-          Run<T, VW> y, x[kGroup];
-          y.load(go + h * g.kv + k);
-#pragma unroll
-          for (int i = 0; i < kGroup; ++i) x[i].load(s[i] + h * g.kv + k);
-#pragma unroll
-          for (int i = 0; i < kGroup; ++i)
-#pragma unroll
-            for (int e = 0; e < VW; ++e) p[i] += y.v[e] * x[i].v[e];
+        for (int u = 0; u < UP; ++u) {
+          const int c = hl.sl + hl.L * (b * UP + u);
+          ok[u] = hv && c < kvc;
+          cc[u] = ok[u] ? c : 0;
+          y[u].load(at(go, hb + cc[u] * VW));
         }
 #pragma unroll
-        for (int i = 0; i < kGroup; ++i) p[i] = wave_sum(p[i]);
-        if (lane == 0)
+        for (int u = 0; u < UP; ++u)
 #pragma unroll
-          for (int i = 0; i < kGroup; ++i)
-            if (n0 + i < g.n) w_p[(n0 + i) * g.H + h] = p[i];
+          for (int e = 0; e < VW; ++e) ym[u][e] = ok[u] ? y[u][e] : 0.f;
+        for (int n0 = 0; n0 < g.n; n0 += G) {
+          Run<T, VW> x[G][UP];
+#pragma unroll
+          for (int i = 0; i < G; ++i) {
+            const T* s = row_of<T>(a, min(n0 + i, g.n - 1), t);
+#pragma unroll
+            for (int u = 0; u < UP; ++u) x[i][u].load(at(s, hb + cc[u] * VW));
+          }
+          float p[G];
+#pragma unroll
+          for (int i = 0; i < G; ++i) {
+            p[i] = 0.f;
+#pragma unroll
+            for (int u = 0; u < UP; ++u)
+#pragma unroll
+              for (int e = 0; e < VW; ++e) p[i] += ym[u][e] * x[i][u][e];
+          }
+          // outside the RMS coordinates the gradient is a dout alone
+#pragma unroll
+          for (int i = 0; i < G; ++i) {
+            if (n0 + i >= g.n) break;
+            const float al = w_a[(n0 + i) * g.H + hc];
+            float* ds = gr.d[n0 + i] + t * g.d;
+#pragma unroll
+            for (int u = 0; u < UP; ++u) {
+              const int j = hb + cc[u] * VW;
+              if (ok[u] && j < g.n0) {
+                float v[VW];
+#pragma unroll
+                for (int e = 0; e < VW; ++e) v[e] = al * ym[u][e];
+                store_f32<VW>(at(ds, j), v);
+              }
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < G; ++i) p[i] = group_sum(p[i], hl.lg);
+          if (hl.sl == 0 && hv)
+#pragma unroll
+            for (int i = 0; i < G; ++i)
+              if (n0 + i < g.n) w_p[(n0 + i) * g.H + h] += p[i];
+        }
       }
     }
     wave_lds_fence();
@@ -310,52 +461,77 @@ __global__ __launch_bounds__(256) void k_list_bwd(ListGeom g, ListArgs a,
       w_c[n] = c;
     }
     wave_lds_fence();
-    for (int n = 0; n < g.n; ++n) {
-      const T* s = row_of<T>(a, n, t);
-      float* ds = gr.d[n] + t * g.d;
-      const float rv = w_r[n];
-      const float cr = rv * rv / (float)g.w * w_c[n];
-      for (int h = 0; h < g.H; ++h) {
-        const float al = w_a[n * g.H + h];
-        for (int k = lane * VW; k < g.kv; k += 64 * VW) {
-          // a run never straddles the norm or key boundary, nor a key head:
-          // with VW > 1 every boundary is a multiple of VW
-          const int j = h * g.kv + k;
-          Run<T, VW> y;
-          y.load(go + j);
-          float v[VW];
+    for (int c0 = g.n0 / VW + lane; c0 < dc; c0 += 64 * UG) {
+      // a chunk never straddles the norm or key boundary, nor a head: with
+      // VW > 1 every boundary is a multiple of VW
+      int cc[UG], hv[UG], hk[UG];
+      bool ok[UG];
+      Run<T, VW> y[UG], qv[UG];
 #pragma unroll
-          for (int e = 0; e < VW; ++e) v[e] = al * y.v[e];
-          if (j >= g.n0) {
-            Run<T, VW> x;
-            x.load(s + j);
+      for (int u = 0; u < UG; ++u) {
+        ok[u] = c0 + 64 * u < dc;
+        cc[u] = ok[u] ? c0 + 64 * u : c0;
+        const int j = cc[u] * VW;
+        hv[u] = j / g.kv;
+        hk[u] = j >= g.k0 ? (j - g.k0) / g.kk : -1;
+        y[u].load(at(go, j));
+        const int jq = j >= g.k0 ? j - g.k0 : 0;
+        if constexpr (VW == 1) {
+          qv[u].load(q + (int64_t)jq * g.qs);
+        } else {
+          qv[u].load(q + jq);
+        }
+      }
+      for (int n0 = 0; n0 < g.n; n0 += G) {
+        Run<T, VW> x[G][UG];
 #pragma unroll
-            for (int e = 0; e < VW; ++e) v[e] -= cr * x.v[e];
-            if (j >= g.k0) {
-              const int jk = j - g.k0;
-              const float b = rv * w_p[n * g.H + jk / g.kk];
-              Run<T, VW> qv;
-              if constexpr (VW == 1) {
-                qv.v[0] = ld1(q + (int64_t)jk * g.qs);
-              } else {
-                qv.load(q + jk);
+        for (int i = 0; i < G; ++i) {
+          const T* s = row_of<T>(a, min(n0 + i, g.n - 1), t);
+#pragma unroll
+          for (int u = 0; u < UG; ++u) x[i][u].load(at(s, cc[u] * VW));
+        }
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+          const int n = n0 + i;
+          if (n >= g.n) break;
+          const float rv = w_r[n];
+          const float cr = rv * rv / (float)g.w * w_c[n];
+          float* ds = gr.d[n] + t * g.d;
+#pragma unroll
+          for (int u = 0; u < UG; ++u) {
+            if (ok[u]) {
+              const int j = cc[u] * VW;
+              const float al = w_a[n * g.H + hv[u]];
+              float v[VW];
+#pragma unroll
+              for (int e = 0; e < VW; ++e) v[e] = al * y[u][e] - cr * x[i][u][e];
+              if (hk[u] >= 0) {
+                const int jk = j - g.k0;
+                const float bb = rv * w_p[n * g.H + hk[u]];
+#pragma unroll
+                for (int e = 0; e < VW; ++e) {
+                  v[e] += bb * qv[u][e];
+                  w_dq[jk + e] += bb * x[i][u][e];  // coordinates jk.. always belong to this lane
+                }
               }
-#pragma unroll
-              for (int e = 0; e < VW; ++e) {
-                v[e] += b * qv.v[e];
-                w_dq[jk + e] += b * x.v[e];  // coordinates jk.. always belong to this lane
-              }
+              store_f32<VW>(at(ds, j), v);
             }
           }
-          store_f32<VW>(ds + j, v);
         }
       }
     }
     wave_lds_fence();  // the next token rewrites the per-token state
   }
-  wave_lds_fence();  // dq coordinates were summed by other lanes than those writing them out
-  float* dst = dq_part + ((int64_t)blockIdx.x * nw + wave) * g.r;
-  for (int k = lane; k < g.r; k += 64) dst[k] = w_dq[k];
+  // every wave of the group has finished its tokens: one dq partial row per
+  // work-group, its waves' rows added in wave order
+  __syncthreads();
+  const int stride = list_bwd_wave_floats(g);
+  float* dst = dq_part + (int64_t)blockIdx.x * g.r;
+  for (int k = threadIdx.x; k < g.r; k += blockDim.x) {
+    float acc = 0.f;
+    for (int w = 0; w < nw; ++w) acc += sm[(int64_t)w * stride + k];
+    dst[k] = acc;
+  }
 }
 
 }  // namespace
@@ -373,13 +549,13 @@ int list_bwd_waves_per_group(const ListGeom& g) {
 int list_bwd_parts(const ListGeom& g) {
   const int nw = list_bwd_waves_per_group(g);
   if (g.T == 0 || nw < 1) return 0;
-  // enough waves to cover the chip several times, with the partial rows
-  // within kListPartBytes
-  int64_t waves = (int64_t)(kListPartBytes / (sizeof(float) * (size_t)g.r));
+  // enough waves to cover the chip several times, with the partial rows (one
+  // per work-group) within kListPartBytes
+  int64_t waves = (int64_t)(kListPartBytes / (sizeof(float) * (size_t)g.r)) * nw;
   if (waves > 4096) waves = 4096;
   if (waves < 256) waves = 256;
   if (waves > g.T) waves = g.T;
-  return (int)((waves + nw - 1) / nw) * nw;
+  return (int)((waves + nw - 1) / nw);
 }
 
 hipError_t launch_list_fwd(const ListGeom& g, int dtype, const ListArgs& a, void* out,
@@ -389,16 +565,16 @@ hipError_t launch_list_fwd(const ListGeom& g, int dtype, const ListArgs& a, void
   const dim3 grid((unsigned)(groups < 4096 ? groups : 4096));
   const size_t lds = list_fwd_lds_bytes(g);
   if (dtype == 0 && g.vec)
-    hipLaunchKernelGGL((k_list_fwd<float, 4>), grid, dim3(kLFwdThreads), lds, st, g, a,
+    hipLaunchKernelGGL((k_list_fwd<float, 4, ListTile<float, 4>::G, ListTile<float, 4>::UK, ListTile<float, 4>::UM>), grid, dim3(kLFwdThreads), lds, st, g, a,
                        static_cast<float*>(out), alpha, lse, rinv);
   else if (dtype == 0)
-    hipLaunchKernelGGL((k_list_fwd<float, 1>), grid, dim3(kLFwdThreads), lds, st, g, a,
+    hipLaunchKernelGGL((k_list_fwd<float, 1, ListTile<float, 1>::G, ListTile<float, 1>::UK, ListTile<float, 1>::UM>), grid, dim3(kLFwdThreads), lds, st, g, a,
                        static_cast<float*>(out), alpha, lse, rinv);
   else if (g.vec)
-    hipLaunchKernelGGL((k_list_fwd<bf16_t, 8>), grid, dim3(kLFwdThreads), lds, st, g, a,
+    hipLaunchKernelGGL((k_list_fwd<bf16_t, 8, ListTile<bf16_t, 8>::G, ListTile<bf16_t, 8>::UK, ListTile<bf16_t, 8>::UM>), grid, dim3(kLFwdThreads), lds, st, g, a,
                        static_cast<bf16_t*>(out), alpha, lse, rinv);
   else
-    hipLaunchKernelGGL((k_list_fwd<bf16_t, 1>), grid, dim3(kLFwdThreads), lds, st, g, a,
+    hipLaunchKernelGGL((k_list_fwd<bf16_t, 1, ListTile<bf16_t, 1>::G, ListTile<bf16_t, 1>::UK, ListTile<bf16_t, 1>::UM>), grid, dim3(kLFwdThreads), lds, st, g, a,
                        static_cast<bf16_t*>(out), alpha, lse, rinv);
   return hipGetLastError();
 }
@@ -408,20 +584,20 @@ hipError_t launch_list_bwd(const ListGeom& g, int dtype, const ListArgs& a, cons
                            const ListGrads& gr, float* dq_part, int parts, hipStream_t st) {
   if (g.T == 0 || parts == 0) return hipSuccess;
   const int nw = list_bwd_waves_per_group(g);
-  if (nw < 1 || parts % nw) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)(parts / nw));
+  if (nw < 1) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)parts);
   const size_t lds = sizeof(float) * (size_t)nw * list_bwd_wave_floats(g);
   if (dtype == 0 && g.vec)
-    hipLaunchKernelGGL((k_list_bwd<float, 4>), grid, dim3(64 * nw), lds, st, g, a,
+    hipLaunchKernelGGL((k_list_bwd<float, 4, ListTile<float, 4>::G, ListTile<float, 4>::UP, ListTile<float, 4>::UG>), grid, dim3(64 * nw), lds, st, g, a,
                        static_cast<const float*>(dout), alpha, lse, rinv, gr, dq_part);
   else if (dtype == 0)
-    hipLaunchKernelGGL((k_list_bwd<float, 1>), grid, dim3(64 * nw), lds, st, g, a,
+    hipLaunchKernelGGL((k_list_bwd<float, 1, ListTile<float, 1>::G, ListTile<float, 1>::UP, ListTile<float, 1>::UG>), grid, dim3(64 * nw), lds, st, g, a,
                        static_cast<const float*>(dout), alpha, lse, rinv, gr, dq_part);
   else if (g.vec)
-    hipLaunchKernelGGL((k_list_bwd<bf16_t, 8>), grid, dim3(64 * nw), lds, st, g, a,
+    hipLaunchKernelGGL((k_list_bwd<bf16_t, 8, ListTile<bf16_t, 8>::G, ListTile<bf16_t, 8>::UP, ListTile<bf16_t, 8>::UG>), grid, dim3(64 * nw), lds, st, g, a,
                        static_cast<const bf16_t*>(dout), alpha, lse, rinv, gr, dq_part);
   else
-    hipLaunchKernelGGL((k_list_bwd<bf16_t, 1>), grid, dim3(64 * nw), lds, st, g, a,
+    hipLaunchKernelGGL((k_list_bwd<bf16_t, 1, ListTile<bf16_t, 1>::G, ListTile<bf16_t, 1>::UP, ListTile<bf16_t, 1>::UG>), grid, dim3(64 * nw), lds, st, g, a,
                        static_cast<const bf16_t*>(dout), alpha, lse, rinv, gr, dq_part);
   return hipGetLastError();
 }
