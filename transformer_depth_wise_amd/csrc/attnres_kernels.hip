@@ -760,6 +760,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
   using V = Vec<T>;
   constexpr int N = V::N;
   constexpr int RB = kSiteRowBatch<CPT>;  // rows per pair of barriers
+  constexpr int kWaves = kThreads / 64;
   extern __shared__ float sm[];
   const int n_src = n_rows + (extra != nullptr ? 1 : 0);
   const int pairs = g.tt * g.H;
@@ -768,6 +769,9 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
   // their dots are summed by DPP before LDS
   const int sh = (g.kvc & 3) == 0 ? 2 : 0;
   const int plen = g.tt * g.cpr;             // partial dots of one row (chunks)
+  // one (token, head) pair per tile whose partial-dot region holds two
+  // batches of wave sums: P takes the one-barrier path below
+  const bool single = pairs == 1 && (plen >> sh) >= 2 * kWaves;
   float* s_alpha = sm;                       // [n_src][tt][H]
   float* s_P = s_alpha + n_src * pairs;      // [n_src][tt][H]
   float* s_rinv = s_P + n_src * pairs;       // [n_src][tt]
@@ -834,38 +838,65 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
 #pragma unroll
         for (int j = 0; j < CPT; ++j) cur[r][j] = ok[j] && row ? ld_stream(sp + sl[j].q) : zero4();
       }
+      float Pr[RB];  // one-pair tiles: each row's P, the same in every thread
+      if (single) {
+        // a row's P is one dot over the whole row: each wave sums its part in
+        // registers, and after one barrier every thread adds the four wave
+        // sums itself (a double-buffered slot per batch, so no second barrier)
+        float* s_w = s_part + ((n0 / RB) & 1) * (RB * kWaves);
 #pragma unroll
-      for (int r = 0; r < RB; ++r) {
+        for (int r = 0; r < RB; ++r) {
+          float part = 0.f;
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-          float part = Vec<T>::dot(dov[j], cur[r][j]);
-          if (sh) part = quad_sum(part);
-          if (sl[j].own && (sl[j].q & ((1 << sh) - 1)) == 0)
-            s_part[((r * plen) >> sh) + (sl[j].q >> sh)] = part;
+          for (int j = 0; j < CPT; ++j) part += Vec<T>::dot(dov[j], cur[r][j]);
+          Pr[r] = wave_sum(part);
         }
-      }
-      __syncthreads();
-      // each (row of the batch, token, head) sum gets a lane group of G
-      // lanes (G a power of two up to a wave): strided partial sums, then a
-      // fixed-order butterfly inside the group
-      {
-        const int combos = RB * pairs, cnt = g.kvc >> sh;
-        int G = 64;
-        while (G > 1 && combos * G > kThreads) G >>= 1;
-        for (int base = 0; base < combos * G; base += kThreads) {
-          const int i = base + tid, combo = i / G, li = i - combo * G;
-          const int r = combo / pairs, p = combo - r * pairs;
+        if ((tid & 63) == 0)
+#pragma unroll
+          for (int r = 0; r < RB; ++r) s_w[r * kWaves + (tid >> 6)] = Pr[r];
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
           float P = 0.f;
-          if (combo < combos) {
-            const int tau = p / g.H, h = p - tau * g.H;
-            const float* pp = s_part + ((r * plen + tau * g.cpr + h * g.kvc) >> sh);
-            for (int c = li; c < cnt; c += G) P += pp[c];
-          }
-          for (int o = 1; o < G; o <<= 1) P += __shfl_xor(P, o, 64);
-          if (li == 0 && combo < combos && n0 + r < n_src) s_P[(n0 + r) * pairs + p] = P;
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) P += s_w[r * kWaves + w];
+          Pr[r] = P;
+          if (tid == 0 && n0 + r < n_src) s_P[n0 + r] = P;
         }
+      } else {
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+#pragma unroll
+          for (int j = 0; j < CPT; ++j) {
+            float part = Vec<T>::dot(dov[j], cur[r][j]);
+            if (sh) part = quad_sum(part);
+            if (sl[j].own && (sl[j].q & ((1 << sh) - 1)) == 0)
+              s_part[((r * plen) >> sh) + (sl[j].q >> sh)] = part;
+          }
+        }
+        __syncthreads();
+        // each (row of the batch, token, head) sum gets a lane group of G
+        // lanes (G a power of two up to a wave): strided partial sums, then a
+        // fixed-order butterfly inside the group
+        {
+          const int combos = RB * pairs, cnt = g.kvc >> sh;
+          int G = 64;
+          while (G > 1 && combos * G > kThreads) G >>= 1;
+          for (int base = 0; base < combos * G; base += kThreads) {
+            const int i = base + tid, combo = i / G, li = i - combo * G;
+            const int r = combo / pairs, p = combo - r * pairs;
+            float P = 0.f;
+            if (combo < combos) {
+              const int tau = p / g.H, h = p - tau * g.H;
+              const float* pp = s_part + ((r * plen + tau * g.cpr + h * g.kvc) >> sh);
+              for (int c = li; c < cnt; c += G) P += pp[c];
+            }
+            for (int o = 1; o < G; o <<= 1) P += __shfl_xor(P, o, 64);
+            if (li == 0 && combo < combos && n0 + r < n_src) s_P[(n0 + r) * pairs + p] = P;
+          }
+        }
+        __syncthreads();
       }
-      __syncthreads();
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
         if (n0 + r >= n_src) break;
@@ -875,7 +906,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
           if (!sl[j].key) continue;
           const int pi = sl[j].tau * g.H + sl[j].hk;
           const float cw = s_alpha[n * pairs + pi] * s_rinv[n * g.tt + sl[j].tau];
-          const float cu = cw * s_P[n * pairs + pi];
+          const float cu = cw * (single ? Pr[r] : s_P[n * pairs + pi]);
           float xv[N];
           V::unpack(cur[r][j], xv);
 #pragma unroll
