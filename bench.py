@@ -728,8 +728,9 @@ def bench_blocks(args):
     inp = BlockInputs(shape)
     T, d, M = shape.tokens, shape.d, shape.sublayers
     nsrc, has_partial = shape.schedule()
+    slots = 0 if args.square_state else int(sum(n + p for n, p in zip(nsrc, has_partial)))
     bank = Bank(T, d, shape.r, shape.heads, shape.blocks + 1, M, shape.dtype, shape.eps,
-                norm=shape.norm)
+                norm=shape.norm, max_slots=slots)
     tdt = bank.rows.dtype
     x = to_device(inp.x(), shape.dtype)
     ys = [to_device(inp.y(t), shape.dtype) for t in range(min(BLOCK_DRAWS, M))]
@@ -769,6 +770,9 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mhar1b")
+    ap.add_argument("--square-state", action="store_true",
+                    help="give every site max_rows + 1 slots of saved state (default: packed "
+                         "by the schedule, attnres_config_t.max_slots)")
     ap.add_argument("--cpu-tokens", type=int, default=None,
                     help="token sample of the CPU oracle baseline (default: sized from a "
                          "16-token run to about 10-20 s of oracle time)")
@@ -846,7 +850,11 @@ def main():
     dev_name = torch.cuda.get_device_name(0)
     inp = Inputs(w)
     t_gen = time.time()
-    bank = Bank(w.tokens, w.d, w.r, w.heads, w.rows, w.sites, w.dtype, w.eps, norm=w.norm)
+    # per-site saved state packed by the schedule: site s keeps nsrc[s] + extra[s] slots
+    slots = 0 if args.square_state else int(sum(n + (1 if e else 0)
+                                                for n, e in zip(w.nsrc, w.extra)))
+    bank = Bank(w.tokens, w.d, w.r, w.heads, w.rows, w.sites, w.dtype, w.eps, norm=w.norm,
+                max_slots=slots)
     workers = min(16, len(os.sched_getaffinity(0)))
     fill_device(bank.rows, inp, "row", range(w.rows), workers)
     fill_device(bank.dout_rows, inp, "dout", range(w.sites), workers)
@@ -892,6 +900,9 @@ def report(args, w, bank, step, alg, config, cpu=None):
     the JSON line.  `cpu` returns the CPU baseline (default: the oracle on
     a token sample of workload w)."""
     import torch
+
+    config = dict(config, workspace_bytes=int(bank.ws_bytes),
+                  saved_state="square" if args.square_state else "packed by the schedule")
 
     for _ in range(args.warmup):
         step()

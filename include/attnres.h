@@ -121,6 +121,13 @@ typedef struct {
   int32_t dtype;     /* attnres_dtype_t: storage dtype */
   float eps;         /* RMSNorm epsilon, inside the square root (1e-6) */
   int32_t norm;      /* attnres_norm_t; r == d makes both the same */
+  int64_t max_slots; /* 0: every site keeps max_rows + 1 source slots of saved
+                        state.  > 0: the slots of one microbatch, summed over
+                        its sites (site s uses nsrc[s] + has_extra[s] != 0),
+                        are packed in site order within this budget: a
+                        full-routing schedule needs about half the square
+                        workspace.  attnres_bank_set_queries returns
+                        ATTNRES_ERR_CAPACITY for a schedule that needs more. */
 } attnres_config_t;
 
 /* Bytes of device workspace a bank with this configuration needs (0 if the
@@ -450,8 +457,9 @@ const char* attnres_last_error(void);
 /* Destroy the handle (the caller's buffers are untouched).  NULL is ignored. */
 void attnres_bank_destroy(attnres_bank_t bank);
 
-/* ABI version of this header: 3 (2 had no source-list read; 1 had no norm
- * field and no gains). */
+/* ABI version of this header: 4 (3 had no max_slots field in
+ * attnres_config_t; 2 had no source-list read; 1 had no norm field and no
+ * gains). */
 int32_t attnres_abi_version(void);
 
 #ifdef __cplusplus

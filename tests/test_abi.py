@@ -34,7 +34,7 @@ def test_header_declarations_are_exported(lib):
     assert set(names) == set(A.EXPORTS)
     for n in names:
         assert getattr(lib, n) is not None
-    assert A.attnres_abi_version() == 3
+    assert A.attnres_abi_version() == 4
 
 
 def cfg(**kw):
@@ -93,6 +93,35 @@ def test_workspace_size_and_capacity(lib):
     with pytest.raises(A.AttnResError) as e:
         A.attnres_bank_create(c, FAKE + 8, FAKE, FAKE, FAKE, n)
     assert e.value.status == A.ATTNRES_ERR_INVALID
+
+
+def test_slot_budget_packs_the_saved_state(lib):
+    """A slot budget sizes the per-site saved state by the sources the sites
+    read (site s: nsrc[s] + has_extra[s] != 0) instead of max_rows + 1 each;
+    a schedule above the budget is refused before anything is launched."""
+    full = list(range(1, 74))  # full routing over 73 sites: 73 * 74 / 2 slots
+    need = sum(full)
+    square = A.attnres_workspace_bytes(cfg())
+    packed = A.attnres_workspace_bytes(cfg(max_slots=need))
+    per_slot = 4 * 256 * 8 * 3  # proj, alpha and dl floats of one slot (T = 256, H = 8)
+    assert square - packed >= (73 * 74 - need) * per_slot
+    assert packed < 0.55 * square
+    # a budget above the square layout changes nothing
+    assert A.attnres_workspace_bytes(cfg(max_slots=10 ** 6)) == square
+    with pytest.raises(A.AttnResError) as e:
+        A.attnres_workspace_bytes(cfg(max_slots=-1))
+    assert e.value.status == A.ATTNRES_ERR_INVALID
+    b = fake_bank(cfg(max_slots=need))
+    try:
+        A.attnres_bank_set_queries(b, full, None, FAKE)  # fits exactly
+        A.attnres_bank_reset(b)
+        with pytest.raises(A.AttnResError) as e:  # one transient source too many
+            A.attnres_bank_set_queries(b, full, [1] + [0] * 72, FAKE)
+        assert e.value.status == A.ATTNRES_ERR_CAPACITY
+        assert "max_slots" in A.last_error()
+        A.attnres_bank_set_queries(b, full[:-1], [1] * 72, FAKE)  # 72 fewer rows, 72 extras
+    finally:
+        A.attnres_bank_destroy(b)
 
 
 def test_call_order_is_enforced(lib):

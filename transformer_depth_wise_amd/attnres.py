@@ -73,6 +73,7 @@ class Config(ctypes.Structure):
         ("dtype", c_int32),
         ("eps", c_float),
         ("norm", c_int32),
+        ("max_slots", c_int64),
     ]
 
 
@@ -204,9 +205,9 @@ def _stream(stream):
 # C-named wrappers (status -> exception)
 
 def make_config(tokens, d, r, heads, max_rows, max_sites, dtype, eps=1e-6,
-                norm=ATTNRES_NORM_SLICE) -> Config:
+                norm=ATTNRES_NORM_SLICE, max_slots=0) -> Config:
     return Config(int(tokens), int(d), int(r), int(heads), int(max_rows), int(max_sites),
-                  int(dtype), float(eps), int(norm))
+                  int(dtype), float(eps), int(norm), int(max_slots))
 
 
 def attnres_workspace_bytes(cfg: Config) -> int:
@@ -325,7 +326,7 @@ class Bank:
     """One bank with its caller-owned device buffers held as torch tensors."""
 
     def __init__(self, tokens, d, r, heads, max_rows, max_sites, dtype="bf16", eps=1e-6,
-                 device="cuda", norm="slice"):
+                 device="cuda", norm="slice", max_slots=0):
         import torch
         self.torch = torch
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
@@ -333,7 +334,7 @@ class Bank:
         self.T, self.d, self.r, self.H = int(tokens), int(d), int(r), int(heads)
         self.max_rows, self.max_sites = int(max_rows), int(max_sites)
         self.cfg = make_config(tokens, d, r, heads, max_rows, max_sites, self.cdtype, eps,
-                               NORMS[norm])
+                               NORMS[norm], max_slots)
         self.ws_bytes = attnres_workspace_bytes(self.cfg)
         self.rows = torch.empty((max_rows, self.T, d), dtype=self.tdtype, device=device)
         self.drows = torch.empty((max_rows, self.T, d), dtype=torch.float32, device=device)

@@ -7,6 +7,7 @@
 
 #include <string>
 #include <algorithm>
+#include <climits>
 #include <initializer_list>
 #include <vector>
 
@@ -51,15 +52,22 @@ constexpr int kFinAhead = 7;
 constexpr int kFinAheadMinSites = 8;
 
 struct Layout {
-  size_t rinv, rinvx, proj, alpha, dl, radial, lse, dqpart;
+  size_t rinv, rinvx, proj, alpha, dl, radial, lse, dqpart, sites;
   size_t part, part_rad;  // finalize partial sums: [A][T][d] and [A][T], A = min(kFinAhead, max_rows - 1)
   size_t qf, q32, qhi, qlo;  // effective queries with gains ([max_sites, r] each)
   size_t total;
-  int64_t site_stride;  // floats per site of proj / alpha: (max_rows + 1) * T * H
-  int64_t dl_stride;    // floats per site of dl: tiles * ts * (max_rows + 1) * H
-  int64_t rad_stride;   // floats per site of radial: tiles * ts * (max_rows + 1)
-  int32_t ts;           // tokens per tile of dl / radial
+  int64_t slots;     // source slots of proj / alpha / dl / radial
+  int64_t slot_th;   // floats per slot of proj / alpha: T * H
+  int64_t slot_dl;   // floats per slot of dl: tp * H (T padded to whole tiles)
+  int64_t slot_rad;  // floats per slot of radial: tp
+  int32_t ts;        // tokens per tile of dl / radial
 };
+
+// Source slots of saved state: the slot budget, or max_rows + 1 per site.
+int64_t slot_capacity(const attnres_config_t& c) {
+  const int64_t square = (int64_t)c.max_sites * (c.max_rows + 1);
+  return c.max_slots > 0 && c.max_slots < square ? c.max_slots : square;
+}
 
 int dq_parts_cap() { return 512; }
 
@@ -67,8 +75,7 @@ int dq_parts_cap() { return 512; }
 Layout make_layout(const attnres_config_t& c, int ts) {
   Layout L{};
   const size_t T = (size_t)c.tokens;
-  const size_t srcs = (size_t)c.max_rows + 1;  // bank rows + one transient source
-  const size_t slot = srcs * T * (size_t)c.heads;
+  const size_t slots = (size_t)slot_capacity(c);
   const size_t tp = ts > 0 ? (T + ts - 1) / ts * ts : T;  // T padded to whole tiles
   size_t off = 0;
   auto take = [&](size_t floats) {
@@ -78,12 +85,13 @@ Layout make_layout(const attnres_config_t& c, int ts) {
   };
   L.rinv = take((size_t)c.max_rows * T);
   L.rinvx = take((size_t)c.max_sites * T);
-  L.proj = take(slot * c.max_sites);
-  L.alpha = take(slot * c.max_sites);
-  L.dl = take(srcs * tp * c.heads * c.max_sites);
-  L.radial = take(srcs * tp * c.max_sites);
+  L.proj = take(slots * T * c.heads);
+  L.alpha = take(slots * T * c.heads);
+  L.dl = take(slots * tp * c.heads);
+  L.radial = take(slots * tp);
   L.lse = take((size_t)c.max_sites * T * c.heads);
   L.dqpart = take((size_t)dq_parts_cap() * c.r);
+  L.sites = take(2 * (size_t)c.max_sites);  // SiteSlot [max_sites]
   // a look-ahead row lies below a finalized row, so at most max_rows - 1
   const size_t ahead = std::min(kFinAhead, c.max_rows - 1);
   L.part = take(ahead * T * c.d);
@@ -94,9 +102,10 @@ Layout make_layout(const attnres_config_t& c, int ts) {
   L.qhi = take((sr + 1) / 2);  // bf16
   L.qlo = take((sr + 1) / 2);
   L.total = off;
-  L.site_stride = (int64_t)slot;
-  L.dl_stride = (int64_t)(srcs * tp * c.heads);
-  L.rad_stride = (int64_t)(srcs * tp);
+  L.slots = (int64_t)slots;
+  L.slot_th = (int64_t)(T * c.heads);
+  L.slot_dl = (int64_t)(tp * c.heads);
+  L.slot_rad = (int64_t)tp;
   L.ts = ts;
   return L;
 }
@@ -113,6 +122,9 @@ attnres_status_t check_config(const attnres_config_t* c) {
     return fail(ATTNRES_ERR_INVALID, "heads=%d must divide d=%d and r=%d", c->heads, c->d, c->r);
   if (c->max_rows < 1 || c->max_sites < 1)
     return fail(ATTNRES_ERR_INVALID, "max_rows and max_sites must be >= 1");
+  if (c->max_slots < 0) return fail(ATTNRES_ERR_INVALID, "max_slots must be >= 0");
+  if (slot_capacity(*c) > INT32_MAX)
+    return fail(ATTNRES_ERR_UNSUPPORTED, "more than 2^31 - 1 source slots of saved state");
   if (!(c->eps > 0.f)) return fail(ATTNRES_ERR_INVALID, "eps must be > 0");
   if (c->norm != ATTNRES_NORM_SLICE && c->norm != ATTNRES_NORM_FULL)
     return fail(ATTNRES_ERR_INVALID, "norm must be ATTNRES_NORM_SLICE or ATTNRES_NORM_FULL (got %d)",
@@ -147,7 +159,7 @@ Geom make_geom(const attnres_config_t& c, const int* cpts, int ncpts) {
   // with r == d both norms are the same read: keep the key-only code path
   g.rms_full = (c.norm == ATTNRES_NORM_FULL && c.r < c.d) ? 1 : 0;
   g.rms_w = g.rms_full ? c.d : c.r;
-  g.nslot = c.max_rows + 1;
+  g.nslot = c.max_rows + 1;  // the site pass takes each site's own count
   g.eps = c.eps;
   double best = 2.0;
   for (int i = 0; i < ncpts; ++i) {
@@ -209,6 +221,8 @@ struct attnres_bank_s {
   // microbatch state
   int n_sites;
   std::vector<int> nsrc, has_extra;
+  std::vector<attnres::SiteSlot> site_tab;  // slots of each site this microbatch
+  bool sites_uploaded;  // the device copy of site_tab has been enqueued
   const void* queries;
   bool queries_set;
   const float* gains;  // [n_sites, r] or NULL: folded into the workspace queries
@@ -237,10 +251,11 @@ struct attnres_bank_s {
   char* dout_ptr(int s) const { return dout_rows + (size_t)s * cfg.tokens * cfg.d * esz; }
   float* rinv(int n) const { return f(lay.rinv) + (size_t)n * cfg.tokens; }
   float* rinvx(int s) const { return f(lay.rinvx) + (size_t)s * cfg.tokens; }
-  float* site_proj(int s) const { return f(lay.proj) + (size_t)s * lay.site_stride; }
-  float* site_alpha(int s) const { return f(lay.alpha) + (size_t)s * lay.site_stride; }
-  float* site_dl(int s) const { return f(lay.dl) + (size_t)s * lay.dl_stride; }
-  float* site_radial(int s) const { return f(lay.radial) + (size_t)s * lay.rad_stride; }
+  float* site_proj(int s) const { return f(lay.proj) + (size_t)site_tab[s].base * lay.slot_th; }
+  float* site_alpha(int s) const { return f(lay.alpha) + (size_t)site_tab[s].base * lay.slot_th; }
+  float* site_dl(int s) const { return f(lay.dl) + (size_t)site_tab[s].base * lay.slot_dl; }
+  float* site_radial(int s) const { return f(lay.radial) + (size_t)site_tab[s].base * lay.slot_rad; }
+  attnres::SiteSlot* dev_sites() const { return reinterpret_cast<attnres::SiteSlot*>(ws + lay.sites); }
   float* site_lse(int s) const { return f(lay.lse) + (size_t)s * cfg.tokens * cfg.heads; }
   float* part_buf(int i) const { return f(lay.part) + (size_t)i * cfg.tokens * cfg.d; }
   float* part_rad(int i) const { return f(lay.part_rad) + (size_t)i * cfg.tokens; }
@@ -258,6 +273,8 @@ struct attnres_bank_s {
     n_sites = 0;
     nsrc.clear();
     has_extra.clear();
+    site_tab.clear();
+    sites_uploaded = false;
     queries = nullptr;
     queries_set = false;
     gains = nullptr;
@@ -324,7 +341,7 @@ void trace_clear(attnres_bank_s* b) {
 
 extern "C" {
 
-int32_t attnres_abi_version(void) { return 3; }
+int32_t attnres_abi_version(void) { return 4; }
 
 attnres_status_t attnres_trace_enable(attnres_bank_t b, int32_t enable) {
   if (!b) return fail(ATTNRES_ERR_INVALID, "bank is NULL");
@@ -443,6 +460,23 @@ attnres_status_t attnres_bank_set_queries(attnres_bank_t b, int32_t n_sites, con
     if (has_extra && (has_extra[s] < 0 || has_extra[s] > 2))
       return fail(ATTNRES_ERR_INVALID, "has_extra[%d] must be 0, 1 or 2", s);
   }
+  // Source slots of each site's saved state: max_rows + 1 each, or with a
+  // slot budget the sources the site reads, packed in site order.
+  std::vector<attnres::SiteSlot> tab((size_t)n_sites);
+  int64_t used = 0;
+  for (int s = 0; s < n_sites; ++s) {
+    const int need = b->cfg.max_slots > 0 ? nsrc[s] + (has_extra && has_extra[s] ? 1 : 0)
+                                          : b->cfg.max_rows + 1;
+    tab[s].base = (int32_t)used;
+    tab[s].nslot = need;
+    used += need;
+  }
+  if (used > b->lay.slots)
+    return fail(ATTNRES_ERR_CAPACITY,
+                "the schedule needs %lld source slots of saved state; the bank holds %lld "
+                "(max_slots)", (long long)used, (long long)b->lay.slots);
+  b->site_tab.swap(tab);
+  b->sites_uploaded = false;
   b->n_sites = n_sites;
   b->nsrc.assign(nsrc, nsrc + n_sites);
   b->has_extra.assign(n_sites, 0);
@@ -455,6 +489,26 @@ attnres_status_t attnres_bank_set_queries(attnres_bank_t b, int32_t n_sites, con
   b->extra_ptr.assign(n_sites, nullptr);
   return ATTNRES_OK;
 }
+
+namespace {
+
+// Enqueue the device copy of this microbatch's site table, once, before the
+// first kernel that reads it.  With no tokens nothing reads it.
+attnres_status_t upload_sites(attnres_bank_s* b, hipStream_t st) {
+  if (b->sites_uploaded || b->cfg.tokens == 0) return ATTNRES_OK;
+  for (int first = 0; first < b->n_sites; first += attnres::kSiteTableChunk) {
+    attnres::SiteTableChunk c{};
+    c.first = first;
+    c.count = std::min(attnres::kSiteTableChunk, b->n_sites - first);
+    for (int i = 0; i < c.count; ++i) c.e[i] = b->site_tab[first + i];
+    hipError_t e = attnres::launch_site_table(c, b->dev_sites(), st);
+    if (e != hipSuccess) return hip_fail(e, "site table upload");
+  }
+  b->sites_uploaded = true;
+  return ATTNRES_OK;
+}
+
+}  // namespace
 
 attnres_status_t attnres_bank_set_gains(attnres_bank_t b, const float* gains, float* dgains,
                                         attnres_stream_t stream) {
@@ -501,9 +555,11 @@ attnres_status_t attnres_bank_append(attnres_bank_t b, const void* src, attnres_
   // Sites reading row n form the suffix of the schedule with nsrc > n.
   int s_lo = 0;
   while (s_lo < b->n_sites && b->nsrc[s_lo] <= n) ++s_lo;
+  attnres_status_t us = upload_sites(b, st);
+  if (us != ATTNRES_OK) return us;
   TraceScope ts(b, ATTNRES_KERNEL_SCORE, st);
   hipError_t e = attnres::launch_score(b->g_main, b->cfg.dtype, dst, b->qset(), s_lo, b->n_sites, n,
-                                       b->rinv(n), b->f(b->lay.proj), b->lay.site_stride, st);
+                                       b->rinv(n), b->f(b->lay.proj), b->dev_sites(), st);
   ts.done();
   if (e != hipSuccess) return hip_fail(e, "append score kernel");
   b->rows_committed = n + 1;
@@ -577,11 +633,13 @@ attnres_status_t attnres_route_fwd(attnres_bank_t b, int32_t site, const void* e
   if (!aligned16(out) || (extra && !aligned16(extra)))
     return fail(ATTNRES_ERR_INVALID, "out and extra must be 16-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
+  attnres_status_t us = upload_sites(b, st);
+  if (us != ATTNRES_OK) return us;
   if (extra) {
     TraceScope ts(b, ATTNRES_KERNEL_SCORE, st);
     hipError_t e = attnres::launch_score(b->g_main, b->cfg.dtype, extra, b->qset(), site, site + 1,
                                          n_rows, b->rinvx(site), b->f(b->lay.proj),
-                                         b->lay.site_stride, st);
+                                         b->dev_sites(), st);
     ts.done();
     if (e != hipSuccess) return hip_fail(e, "route_fwd score kernel (transient source)");
   }
@@ -632,10 +690,14 @@ attnres_status_t attnres_route_bwd(attnres_bank_t b, int32_t site, const void* e
   const int n_rows = b->nsrc[site];
   const int64_t row_stride = c.tokens * (int64_t)c.d;
   const int parts = attnres::bwd_site_parts(b->g_site);
+  attnres_status_t us = upload_sites(b, st);  // (route_fwd has enqueued it already)
+  if (us != ATTNRES_OK) return us;
   {
+    attnres::Geom gs = b->g_site;
+    gs.nslot = b->site_tab[site].nslot;  // this site's coefficient slots
     TraceScope ts(b, ATTNRES_KERNEL_BWD_SITE, st);
     hipError_t e = attnres::launch_bwd_site(
-        b->g_site, c.dtype, b->rows, row_stride, extra, n_rows, b->site_alpha(site),
+        gs, c.dtype, b->rows, row_stride, extra, n_rows, b->site_alpha(site),
         b->site_lse(site), b->rinv(0), extra ? b->rinvx(site) : nullptr, slot, b->site_dl(site),
         b->site_radial(site), b->f(b->lay.dqpart), parts, st);
     ts.done();
@@ -715,11 +777,11 @@ attnres_status_t attnres_route_bwd(attnres_bank_t b, int32_t site, const void* e
   sa.dl = b->f(b->lay.dl);
   sa.radial = b->f(b->lay.radial);
   sa.lse = b->f(b->lay.lse);
-  sa.site_stride = b->lay.site_stride;
-  sa.dl_stride = b->lay.dl_stride;
-  sa.rad_stride = b->lay.rad_stride;
+  sa.sites = b->dev_sites();
+  sa.slot_th = b->lay.slot_th;
+  sa.slot_dl = b->lay.slot_dl;
+  sa.slot_rad = b->lay.slot_rad;
   sa.ts = b->lay.ts;
-  sa.nslot = c.max_rows + 1;
   sa.th_stride = c.tokens * (int64_t)c.heads;
   TraceScope tf(b, ATTNRES_KERNEL_FINALIZE, st);
   hipError_t e = attnres::launch_finalize(b->g_fin, c.dtype, jobs.data(), (int)jobs.size(), sa,

@@ -28,7 +28,7 @@ struct Geom {
   int32_t wave_tokens;  // backward site pass: tokens owned by each wave (0: work-group-wide layout)
   int32_t rms_full;  // 1: the inverse RMS is over all d coordinates (key still the last r)
   int32_t rms_w;     // divisor of the mean of squares: d if rms_full, else r
-  int32_t nslot;     // source slots per site in the backward coefficients: max_rows + 1
+  int32_t nslot;     // source slots of the site the backward site pass runs for
   float eps;
 };
 
@@ -43,30 +43,39 @@ struct QuerySet {
   const uint16_t* qlo;
 };
 
-// Per-site saved state lives in site-major slots of the workspace:
-//   proj          : [site][max_rows + 1][H][T]  raw per-head key projections
-//                   q_h . key_[h] (the logit is this times the inverse RMS)
-//   alpha         : [site][max_rows + 1][T][H]  softmax weights
-//   dl            : [site][tile][max_rows + 1][ts][H]  a (P - S), tile-major
-//   radial        : [site][tile][max_rows + 1][ts]     sum_h dl_h * logit_h
+// Per-site saved state lives in site-major slots of the workspace.  Site s
+// owns nslot[s] source slots starting at slot base[s] (SiteSlot below):
+// nslot = max_rows + 1 for every site by default, or, when the bank is
+// created with a slot budget, the sources the site reads in this microbatch
+// (its rows, plus one for a transient source), packed in site order.
+//   proj          : [slot][H][T]  raw per-head key projections q_h . key_[h]
+//                   (the logit is this times the inverse RMS)
+//   alpha         : [slot][T][H]  softmax weights
+//   dl            : per site [tile][nslot][ts][H]  a (P - S), tile-major
+//   radial        : per site [tile][nslot][ts]     sum_h dl_h * logit_h
 //   lse           : [site][T][H]
-// Source index n of a site is bank row n, index nsrc[site] its transient source.
-// dl and radial are tile-major so that the coefficients that one wave (or,
-// in the work-group-wide site pass, one work-group) of the backward site
-// pass produces for its ts tokens form one contiguous block; tokens past T
-// in the last tile are padding.
+// Source index n of a site is bank row n, index nsrc[site] its transient
+// source.  dl and radial are tile-major so that the coefficients that one
+// wave (or, in the work-group-wide site pass, one work-group) of the backward
+// site pass produces for its ts tokens form one contiguous block; tokens past
+// T in the last tile are padding (a slot of dl holds tp * H floats, tp = T
+// rounded up to whole tiles).
+struct SiteSlot {
+  int32_t base;   // first slot of the site
+  int32_t nslot;  // slots of the site
+};
 struct SiteArrays {
   float* proj;
   float* alpha;
   float* dl;
   float* radial;
   float* lse;
-  int64_t site_stride;  // floats between consecutive sites of proj / alpha
-  int64_t dl_stride;    // floats between consecutive sites of dl
-  int64_t rad_stride;   // floats between consecutive sites of radial
-  int64_t th_stride;    // floats between consecutive sites of lse = T * H
-  int32_t ts;           // tokens per tile of dl / radial
-  int32_t nslot;        // source slots per site: max_rows + 1
+  const SiteSlot* sites;  // device [sites] table
+  int64_t slot_th;     // floats per slot of proj / alpha: T * H
+  int64_t slot_dl;     // floats per slot of dl: tp * H
+  int64_t slot_rad;    // floats per slot of radial: tp
+  int64_t th_stride;   // floats between consecutive sites of lse = T * H
+  int32_t ts;          // tokens per tile of dl / radial
 };
 
 // Position of (token t, source slot) in a site's tile-major dl / radial
@@ -76,9 +85,19 @@ __host__ __device__ inline int64_t coef_at(int64_t t, int slot, int nslot, int t
   return (tile * nslot + slot) * ts + (t - tile * ts);
 }
 
+// Projections of the row (or transient source) x at source slot `slot` of
+// sites [s_lo, s_hi); site s's projections start sites[s].base slots into proj.
 hipError_t launch_score(const Geom& g, int dtype, const void* x, const QuerySet& qs, int s_lo,
                         int s_hi, int slot, float* rinv_out, float* proj,
-                        int64_t site_stride, hipStream_t st);
+                        const SiteSlot* sites, hipStream_t st);
+
+// Entries [first, first + count) of the device site table, from the host.
+constexpr int kSiteTableChunk = 128;
+struct SiteTableChunk {
+  int32_t first, count;
+  SiteSlot e[kSiteTableChunk];
+};
+hipError_t launch_site_table(const SiteTableChunk& c, SiteSlot* table, hipStream_t st);
 
 // Block partial sum: out = a + b (a may be NULL: out = b) over `elems`
 // storage-dtype elements (a multiple of the 16-byte chunk), one rounding.

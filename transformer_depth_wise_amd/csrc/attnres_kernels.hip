@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void k_score(Geom g, const T* __restrict_
                                                      const QT* __restrict__ Q, int s_lo, int s_hi,
                                                      int slot, float* __restrict__ rinv_out,
                                                      float* __restrict__ proj,
-                                                     int64_t site_stride) {
+                                                     const SiteSlot* __restrict__ sites) {
   using V = Vec<T>;
   extern __shared__ float sm[];
   float* keys = sm;                      // [TILE][r]
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void k_score(Geom g, const T* __restrict_
         for (int e = 0; e < V::N; ++e) acc[tau] += qf[e] * kp[e];
       }
     }
-    float* dst = proj + (int64_t)s * site_stride + ((int64_t)slot * g.H + h) * g.T + t0;
+    float* dst = proj + ((int64_t)sites[s].base + slot) * g.H * g.T + (int64_t)h * g.T + t0;
 #pragma unroll
     for (int tau = 0; tau < TILE; ++tau)
       if (t0 + tau < g.T) st_stream(dst + tau, acc[tau]);
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(kThreads) void k_score_mfma(Geom g, const bf16_t* _
                                                           int s_hi, int slot,
                                                           float* __restrict__ rinv_out,
                                                           float* __restrict__ proj,
-                                                          int64_t site_stride) {
+                                                          const SiteSlot* __restrict__ sites) {
   constexpr int kWaves = kThreads / 64;
   __shared__ float s_ss[kWaves][16 * TB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(kThreads) void k_score_mfma(Geom g, const bf16_t* _
         // layout: a block covers 64 bytes of a (site, head) run, half a line,
         // so these are plain stores, which L2 merges with the other half
         // (non-temporal ones reached HBM as partial lines)
-        float* base = proj + (int64_t)s * site_stride + ((int64_t)slot * g.H + h) * g.T;
+        float* base = proj + ((int64_t)sites[s].base + slot) * g.H * g.T + (int64_t)h * g.T;
 #pragma unroll
         for (int b = 0; b < TB; ++b) {
           float* dst = base + tq[b];
@@ -361,7 +361,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_score_wide(Geom g, const bf16_t*
                                                           int s_hi, int slot,
                                                           float* __restrict__ rinv_out,
                                                           float* __restrict__ proj,
-                                                          int64_t site_stride) {
+                                                          const SiteSlot* __restrict__ sites) {
   extern __shared__ float sm[];  // [WAVES][NB][64 lanes][4] partial sums, then [WAVES][16] squares
   constexpr int kWaves = WAVES;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -451,7 +451,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_score_wide(Geom g, const bf16_t*
       }
       const int sv = s_lo + b * 16 + row;
       if (sv < s_hi) {
-        float* dst = proj + (int64_t)sv * site_stride + ((int64_t)slot * g.H + h) * g.T + tq;
+        float* dst = proj + ((int64_t)sites[sv].base + slot) * g.H * g.T + (int64_t)h * g.T + tq;
         if (vec) {
           *reinterpret_cast<float4*>(dst) = v;  // half a line: plain, as in k_score_mfma
         } else {
@@ -492,7 +492,7 @@ __global__ __launch_bounds__(kThreads) void k_score_one(Geom g, const bf16_t* __
                                                          const QT* __restrict__ q, int site,
                                                          int slot, float* __restrict__ rinv_out,
                                                          float* __restrict__ proj,
-                                                         int64_t site_stride) {
+                                                         const SiteSlot* __restrict__ sites) {
   using V = Vec<bf16_t>;
   constexpr int N = V::N;
   extern __shared__ float sm[];  // [waves][r / N] per-chunk dots
@@ -541,7 +541,7 @@ __global__ __launch_bounds__(kThreads) void k_score_one(Geom g, const bf16_t* __
   int G = 64;
   while (G > 1 && G * g.H > 64) G >>= 1;
   const int hpp = 64 / G;  // heads per pass
-  float* dst = proj + (int64_t)site * site_stride + (int64_t)slot * g.H * g.T + t;
+  float* dst = proj + ((int64_t)sites[site].base + slot) * g.H * g.T + t;
   for (int h0 = 0; h0 < g.H; h0 += hpp) {
     const int h = h0 + lane / G, li = lane % G;
     float P = 0.f;
@@ -1204,6 +1204,15 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site_w(
 }
 
 // ---------------------------------------------------------------------------
+// Site table upload: the entries travel in the kernel arguments, so the copy
+// is an ordinary launch on the caller's stream (and replays with a graph).
+__global__ __launch_bounds__(kSiteTableChunk) void k_site_table(SiteTableChunk c,
+                                                                SiteSlot* __restrict__ table) {
+  const int i = threadIdx.x;
+  if (i < c.count) table[c.first + i] = c.e[i];
+}
+
+// ---------------------------------------------------------------------------
 // Sum the [parts, r] query-gradient partials in a fixed order.
 // One 1024-thread work-group per 64 columns: wave w sums rows w, w+16, ...
 // with eight independent accumulators (their loads issued together), then
@@ -1370,10 +1379,11 @@ __global__ __launch_bounds__(kThreads) void k_finalize(Geom g, FinalizeArgs fa, 
         const int tau = (4 * r) / g.H;
         float4 a = make_float4(0.f, 0.f, 0.f, 0.f), q = a;
         if (tau < tv) {
+          const SiteSlot ss = sa.sites[b0 + k];
           const int64_t idx =
-              (int64_t)(b0 + k) * sa.site_stride + ((int64_t)job.slot * g.T + t0) * g.H + 4 * r;
-          const int64_t ldl = (int64_t)(b0 + k) * sa.dl_stride +
-                              coef_at(t0 + tau, job.slot, sa.nslot, sa.ts) * g.H + 4 * r - tau * g.H;
+              ss.base * sa.slot_th + ((int64_t)job.slot * g.T + t0) * g.H + 4 * r;
+          const int64_t ldl = ss.base * sa.slot_dl +
+                              coef_at(t0 + tau, job.slot, ss.nslot, sa.ts) * g.H + 4 * r - tau * g.H;
           a = *reinterpret_cast<const float4*>(sa.alpha + idx);
           const float4 dl = *reinterpret_cast<const float4*>(sa.dl + ldl);
           const float ri = job.rinv[t0 + tau];
@@ -1388,10 +1398,10 @@ __global__ __launch_bounds__(kThreads) void k_finalize(Geom g, FinalizeArgs fa, 
         const int tau = p / g.H;
         float a = 0.f, q = 0.f;
         if (tau < tv) {
-          const int64_t idx =
-              (int64_t)(b0 + k) * sa.site_stride + ((int64_t)job.slot * g.T + t0) * g.H + p;
-          const int64_t ldl = (int64_t)(b0 + k) * sa.dl_stride +
-                              coef_at(t0 + tau, job.slot, sa.nslot, sa.ts) * g.H + p - tau * g.H;
+          const SiteSlot ss = sa.sites[b0 + k];
+          const int64_t idx = ss.base * sa.slot_th + ((int64_t)job.slot * g.T + t0) * g.H + p;
+          const int64_t ldl = ss.base * sa.slot_dl +
+                              coef_at(t0 + tau, job.slot, ss.nslot, sa.ts) * g.H + p - tau * g.H;
           a = sa.alpha[idx];
           q = job.rinv[t0 + tau] * sa.dl[ldl];
         }
@@ -1403,8 +1413,9 @@ __global__ __launch_bounds__(kThreads) void k_finalize(Geom g, FinalizeArgs fa, 
     // sum per token
     for (int i = tid; i < nb * g.tt; i += kThreads) {
       const int k = i / g.tt, tau = i - k * g.tt;
-      s_radb[i] = tau < tv ? sa.radial[(int64_t)(b0 + k) * sa.rad_stride +
-                                       coef_at(t0 + tau, job.slot, sa.nslot, sa.ts)]
+      const SiteSlot ss = sa.sites[b0 + k];
+      s_radb[i] = tau < tv ? sa.radial[ss.base * sa.slot_rad +
+                                       coef_at(t0 + tau, job.slot, ss.nslot, sa.ts)]
                            : 0.f;
     }
     __syncthreads();
@@ -1556,10 +1567,10 @@ __global__ __launch_bounds__(kThreads) void k_finalize_cols(Geom g, FinalizeArgs
       const int tau = p / g.H;
       float a = 0.f, q = 0.f;
       if (tau < tv) {
-        const int64_t idx =
-            (int64_t)(b0 + k) * sa.site_stride + ((int64_t)job.slot * g.T + t0) * g.H + p;
-        const int64_t ldl = (int64_t)(b0 + k) * sa.dl_stride +
-                            coef_at(t0 + tau, job.slot, sa.nslot, sa.ts) * g.H + p - tau * g.H;
+        const SiteSlot ss = sa.sites[b0 + k];
+        const int64_t idx = ss.base * sa.slot_th + ((int64_t)job.slot * g.T + t0) * g.H + p;
+        const int64_t ldl = ss.base * sa.slot_dl +
+                            coef_at(t0 + tau, job.slot, ss.nslot, sa.ts) * g.H + p - tau * g.H;
         a = sa.alpha[idx];
         q = job.rinv[t0 + tau] * sa.dl[ldl];
       }
@@ -1568,8 +1579,9 @@ __global__ __launch_bounds__(kThreads) void k_finalize_cols(Geom g, FinalizeArgs
     }
     for (int i = tid; i < nb * TT; i += kThreads) {
       const int k = i / TT, tau = i - k * TT;
-      s_radb[i] = tau < tv ? sa.radial[(int64_t)(b0 + k) * sa.rad_stride +
-                                       coef_at(t0 + tau, job.slot, sa.nslot, sa.ts)]
+      const SiteSlot ss = sa.sites[b0 + k];
+      s_radb[i] = tau < tv ? sa.radial[ss.base * sa.slot_rad +
+                                       coef_at(t0 + tau, job.slot, ss.nslot, sa.ts)]
                            : 0.f;
     }
     __syncthreads();
@@ -1787,7 +1799,7 @@ int bwd_site_parts(const Geom& g) {
 }
 
 hipError_t launch_score(const Geom& g, int dtype, const void* x, const QuerySet& qs, int s_lo,
-                        int s_hi, int slot, float* rinv_out, float* proj, int64_t site_stride,
+                        int s_hi, int slot, float* rinv_out, float* proj, const SiteSlot* sites,
                         hipStream_t st) {
   if (g.T == 0) return hipSuccess;
   if (dtype != 0 && g.kk % 32 == 0 && g.kk <= 256) {
@@ -1806,10 +1818,10 @@ hipError_t launch_score(const Geom& g, int dtype, const void* x, const QuerySet&
   case K:                                                                                    \
     if (two)                                                                                 \
       hipLaunchKernelGGL((k_score_mfma<K, 2>), grid, dim3(kThreads), 0, st, g, xb, qb, ql,   \
-                         s_lo, s_hi, slot, rinv_out, proj, site_stride);                     \
+                         s_lo, s_hi, slot, rinv_out, proj, sites);                     \
     else                                                                                     \
       hipLaunchKernelGGL((k_score_mfma<K, 1>), grid, dim3(kThreads), 0, st, g, xb, qb, ql,   \
-                         s_lo, s_hi, slot, rinv_out, proj, site_stride);                     \
+                         s_lo, s_hi, slot, rinv_out, proj, sites);                     \
     break;
       ATTNRES_SCORE_KS(1)
       ATTNRES_SCORE_KS(2)
@@ -1830,11 +1842,11 @@ hipError_t launch_score(const Geom& g, int dtype, const void* x, const QuerySet&
     const bf16_t* xb = static_cast<const bf16_t*>(x);
     if (qs.qf)
       hipLaunchKernelGGL(k_score_one<float>, grid, dim3(kThreads), lds, st, g, xb,
-                         qs.qf + (int64_t)s_lo * g.r, s_lo, slot, rinv_out, proj, site_stride);
+                         qs.qf + (int64_t)s_lo * g.r, s_lo, slot, rinv_out, proj, sites);
     else
       hipLaunchKernelGGL(k_score_one<bf16_t>, grid, dim3(kThreads), lds, st, g, xb,
                          static_cast<const bf16_t*>(qs.q) + (int64_t)s_lo * g.r, s_lo, slot,
-                         rinv_out, proj, site_stride);
+                         rinv_out, proj, sites);
     return hipGetLastError();
   }
   const int nsb = (s_hi - s_lo + 15) / 16;
@@ -1851,10 +1863,10 @@ hipError_t launch_score(const Geom& g, int dtype, const void* x, const QuerySet&
   case B:                                                                                      \
     if (waves == 8)                                                                            \
       hipLaunchKernelGGL((k_score_wide<B, 8>), grid, dim3(512), lds, st, g, xb, qb, ql, s_lo,  \
-                         s_hi, slot, rinv_out, proj, site_stride);                             \
+                         s_hi, slot, rinv_out, proj, sites);                             \
     else                                                                                       \
       hipLaunchKernelGGL((k_score_wide<B, 4>), grid, dim3(256), lds, st, g, xb, qb, ql, s_lo,  \
-                         s_hi, slot, rinv_out, proj, site_stride);                             \
+                         s_hi, slot, rinv_out, proj, sites);                             \
     break;
       ATTNRES_SCORE_NB(1)
       ATTNRES_SCORE_NB(2)
@@ -1876,15 +1888,15 @@ hipError_t launch_score(const Geom& g, int dtype, const void* x, const QuerySet&
       hipLaunchKernelGGL((k_score<float, float, TL>), grid, dim3(kThreads), lds, st, g,          \
                          static_cast<const float*>(x),                                           \
                          qs.qf ? qs.qf : static_cast<const float*>(qs.q), s_lo, s_hi, slot,      \
-                         rinv_out, proj, site_stride);                                           \
+                         rinv_out, proj, sites);                                           \
     else if (qs.qf)                                                                              \
       hipLaunchKernelGGL((k_score<bf16_t, float, TL>), grid, dim3(kThreads), lds, st, g,         \
                          static_cast<const bf16_t*>(x), qs.qf, s_lo, s_hi, slot, rinv_out, proj, \
-                         site_stride);                                                           \
+                         sites);                                                           \
     else                                                                                         \
       hipLaunchKernelGGL((k_score<bf16_t, bf16_t, TL>), grid, dim3(kThreads), lds, st, g,        \
                          static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(qs.q), s_lo,  \
-                         s_hi, slot, rinv_out, proj, site_stride);                               \
+                         s_hi, slot, rinv_out, proj, sites);                               \
     break;
     ATTNRES_SCORE_TILE(8)
     ATTNRES_SCORE_TILE(4)
@@ -1973,6 +1985,12 @@ hipError_t launch_bwd_site(const Geom& g, int dtype, const void* rows, int64_t r
                        row_stride, static_cast<const bf16_t*>(extra), n_rows, alpha, lse, rinv_rows,
                        rinv_extra, static_cast<const bf16_t*>(dout), dl, radial, dq_part);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_site_table(const SiteTableChunk& c, SiteSlot* table, hipStream_t st) {
+  if (c.count < 1 || c.count > kSiteTableChunk || c.first < 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_site_table, dim3(1), dim3(kSiteTableChunk), 0, st, c, table);
   return hipGetLastError();
 }
 
