@@ -144,7 +144,7 @@ def timed_token_chunks(run, tokens: int, cores: int):
 # one-thread run on a few tokens (larger samples run somewhat slower per token,
 # so the run itself takes about 10-20 s), and the most tokens it takes.
 CPU_TARGET_S = 8.0
-CPU_MAX_TOKENS = 4096
+CPU_MAX_TOKENS = 16384
 
 
 def oracle_baseline(prepare, full_tokens: int, unit: str, what: str, tokens=None,
@@ -356,6 +356,31 @@ def load_counters(workload: str):
     return out if stamp == source_hash(workload) else None
 
 
+def delta_traffic(workload: str, phase: str):
+    """Measured HBM bytes of one call of a delta phase, in the unit its
+    `achieved` figure uses: the forward is one forward kernel; the backward
+    phase is every other kernel of the microbatch (its backward kernels, the
+    null-source sums, the dq reductions and, with per-call checkpointing, the
+    recomputed forward), over the calls.  None without a current summary."""
+    c = load_counters(workload)
+    if not c or "delta_fwd" not in c or "_total" not in c:
+        return None
+    fwd = sum(c["delta_fwd"])
+    if phase == "delta_fwd":
+        return int(fwd)
+    return int((c["_total"] - DELTA_SITES * fwd) / DELTA_SITES)
+
+
+def list_traffic(workload: str, phase: str):
+    """Measured HBM bytes of one list read's phase: the forward kernel, or the
+    backward kernel with its dq reduction.  None without a current summary."""
+    c = load_counters(workload)
+    if not c or phase not in c:
+        return None
+    extra = sum(c["dq_reduce"]) if phase == "list_bwd" and "dq_reduce" in c else 0.0
+    return int(sum(c[phase]) + extra)
+
+
 def measured_fields(workload: str, ms: float, model_bytes: int, unit: str = "microbatch"):
     """The bench line's bandwidth figures.  `achieved_gbps` and `pct_of_peak`
     divide the HBM bytes the counters measured (FETCH_SIZE + WRITE_SIZE of
@@ -532,6 +557,11 @@ def bench_delta(args):
                           "launches_per_microbatch": DELTA_SITES,
                           "gbps": round(by_b / ms_b / 1e6, 1),
                           "includes_recomputed_forward": not args.no_recompute}}
+    counters_name = shape.name if not args.no_recompute else shape.name + "_norecompute"
+    for phase, t_ms in (("delta_fwd", ms_f), ("delta_bwd", ms_b)):
+        tb = delta_traffic(counters_name, phase)
+        if tb is not None:  # measured bytes of the phase over its time
+            kern[phase]["hbm_gbps"] = round(tb * DELTA_SITES / t_ms / 1e6, 1)
     dom = max(kern, key=lambda k: kern[k]["ms_per_microbatch"])
     a = kern[dom]["gbps"]
     result = {
@@ -551,7 +581,9 @@ def bench_delta(args):
         **measured_fields(shape.name if not args.no_recompute else shape.name + "_norecompute",
                           ms, by_f + by_b),
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(a / HBM_PEAK_GBPS, 3), "traffic": None,
+                     "unit": "GB/s", "frac": round(a / HBM_PEAK_GBPS, 3),
+                     "traffic": delta_traffic(shape.name if not args.no_recompute
+                                              else shape.name + "_norecompute", dom),
                      "alg_bytes_per_launch": int((by_f if dom == "delta_fwd" else by_b)
                                                  / DELTA_SITES)},
         "kernels": kern,
@@ -644,6 +676,10 @@ def bench_list(args):
     kern = {"list_fwd": {"ms_per_read": round(ms_f, 3), "gbps": round(by_f / ms_f / 1e6, 1)},
             "list_bwd": {"ms_per_read": round(ms_b, 3), "gbps": round(by_b / ms_b / 1e6, 1),
                          "includes": "the fixed-order dq reduction"}}
+    for phase, t_ms in (("list_fwd", ms_f), ("list_bwd", ms_b)):
+        tb = list_traffic(shape.name, phase)
+        if tb is not None:  # measured bytes of the phase over its time
+            kern[phase]["hbm_gbps"] = round(tb / t_ms / 1e6, 1)
     dom = max(kern, key=lambda k: kern[k]["ms_per_read"])
     a = kern[dom]["gbps"]
     result = {
@@ -659,7 +695,8 @@ def bench_list(args):
                    "query_stride": shape.qstride, "storage": shape.dtype, "norm": shape.norm},
         **measured_fields(shape.name, ms, by_f + by_b, unit="read"),
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(a / HBM_PEAK_GBPS, 3), "traffic": None,
+                     "unit": "GB/s", "frac": round(a / HBM_PEAK_GBPS, 3),
+                     "traffic": list_traffic(shape.name, dom),
                      "alg_bytes_per_launch": by_f if dom == "list_fwd" else by_b},
         "kernels": kern,
         "probe": probe,

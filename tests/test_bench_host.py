@@ -83,6 +83,34 @@ def test_counter_summary_is_calibrated_on_the_copy_probe(tmp_path, monkeypatch):
     assert bench.load_counters("toy") is None
 
 
+def test_phase_traffic_of_the_delta_and_list_lines(tmp_path, monkeypatch):
+    """The roofline traffic of the delta and list lines is measured bytes in
+    the unit of their `achieved` figure: one call's backward phase holds its
+    recomputed forward, null sums and dq reductions; the list backward its dq
+    reduction."""
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    h = bench.source_hash("delta8b")
+    n = bench.DELTA_SITES
+    fwd, bwd, null, red = (100.0, 10.0), (300.0, 200.0), (5.0, 1.0), (2.0, 0.0)
+    total = 2 * n * sum(fwd) + n * sum(bwd) + 2 * n * sum(null) + 3 * n * sum(red)
+    with open(bench.counters_path("delta8b"), "w") as f:
+        f.write(f"source_hash {h}\n"
+                f"kernel delta_fwd {2 * n} 0 0 {fwd[0]} {fwd[1]}\n"
+                f"kernel delta_bwd {n} 0 0 {bwd[0]} {bwd[1]}\n"
+                f"kernel delta_null {2 * n} 0 0 {null[0]} {null[1]}\n"
+                f"kernel dq_reduce {3 * n} 0 0 {red[0]} {red[1]}\n"
+                f"hbm_bytes_per_microbatch {total}\n")
+    assert bench.delta_traffic("delta8b", "delta_fwd") == 110
+    assert bench.delta_traffic("delta8b", "delta_bwd") == 110 + 500 + 2 * 6 + 3 * 2
+    with open(bench.counters_path("list_lr"), "w") as f:
+        f.write(f"source_hash {bench.source_hash('list_lr')}\n"
+                "kernel list_fwd 1 0 0 70 7\nkernel list_bwd 1 0 0 90 40\n"
+                "kernel dq_reduce 1 0 0 3 1\nhbm_bytes_per_microbatch 211\n")
+    assert bench.list_traffic("list_lr", "list_fwd") == 77
+    assert bench.list_traffic("list_lr", "list_bwd") == 134
+    assert bench.list_traffic("list_d513", "list_bwd") is None  # no summary
+
+
 @pytest.mark.parametrize("name,kind", [
     ("void attnres::(anonymous namespace)::k_fwd<unsigned short, 5, unsigned short>(...)", "fwd"),
     ("void attnres::(anonymous namespace)::k_bwd_site_w<unsigned short, 5>(...)", "bwd_site"),
