@@ -443,14 +443,15 @@ def delta_schedule():
             for i in range(DELTA_SITES)]
 
 
-def delta_bytes(shape, m: int):
-    """Algorithmic bytes of one delta call with m block deltas: (fwd, bwd)."""
+def delta_bytes(shape, m: int, grad_bytes: int = 4):
+    """Algorithmic bytes of one delta call with m block deltas: (fwd, bwd);
+    the delta gradients are float32 (grad_bytes 4) or bf16 (2)."""
     T, d, H, b = shape.tokens, shape.d, shape.heads, 2 if shape.dtype == "bf16" else 4
     n = m + 1
     fwd = m * T * d * b + d * b + 2 * T * d * b + 4 * n * T * H + 4 * T * H  # + partial, out
     # two passes over the deltas, dout (and once more for the null sum), alpha,
-    # float32 delta gradients
-    bwd = 2 * m * T * d * b + 2 * d * b + 2 * T * d * b + 4 * n * T * H + 4 * m * T * d
+    # the delta gradients
+    bwd = 2 * m * T * d * b + 2 * d * b + 2 * T * d * b + 4 * n * T * H + grad_bytes * m * T * d
     return fwd, bwd
 
 
@@ -499,13 +500,15 @@ def bench_delta(args):
     partial = to_device(inp.value("partial"), shape.dtype)
     dout = to_device(inp.value("dout"), shape.dtype)
     sched = delta_schedule()
-    calls = [make_delta_call(T, d, H, deltas[:m], null, queries[i], ATTNRES_BF16, shape.eps)
+    gdt = ATTNRES_BF16 if args.bf16_grads else 0
+    calls = [make_delta_call(T, d, H, deltas[:m], null, queries[i], ATTNRES_BF16, shape.eps, gdt)
              for i, m in enumerate(sched)]
     tdt = torch.bfloat16
     out = torch.empty((T, d), dtype=tdt, device="cuda")
     alphas = [torch.empty((m + 1, T, H), dtype=torch.float32, device="cuda") for m in sched]
     lses = [torch.empty((T, H), dtype=torch.float32, device="cuda") for _ in sched]
-    dds = [torch.empty((T, d), dtype=torch.float32, device="cuda") for _ in range(shape.n_deltas)]
+    gtd = torch.bfloat16 if args.bf16_grads else torch.float32
+    dds = [torch.empty((T, d), dtype=gtd, device="cuda") for _ in range(shape.n_deltas)]
     dnull = torch.empty(d, dtype=torch.float32, device="cuda")
     dq = torch.empty(d, dtype=torch.float32, device="cuda")
     nbytes = max(attnres_delta_workspace_bytes(c) for c in calls)
@@ -543,7 +546,7 @@ def bench_delta(args):
     ms_f, ms_b = t_f / args.steps, t_b / args.steps
     ms = ms_f + ms_b
     probe = bandwidth_probe(torch)  # also the calibration run of the HBM counters
-    fb = [delta_bytes(shape, m) for m in sched]
+    fb = [delta_bytes(shape, m, 2 if args.bf16_grads else 4) for m in sched]
     by_f, by_b = sum(x[0] for x in fb), sum(x[1] for x in fb)
     if not args.no_recompute:
         by_b += by_f  # the backward phase runs every forward again
@@ -557,7 +560,9 @@ def bench_delta(args):
                           "launches_per_microbatch": DELTA_SITES,
                           "gbps": round(by_b / ms_b / 1e6, 1),
                           "includes_recomputed_forward": not args.no_recompute}}
-    counters_name = shape.name if not args.no_recompute else shape.name + "_norecompute"
+    # counters are taken with per-call recomputation and float32 gradients
+    counters_name = (shape.name + ("" if not args.no_recompute else "_norecompute")
+                     + ("_bf16grads" if args.bf16_grads else ""))
     for phase, t_ms in (("delta_fwd", ms_f), ("delta_bwd", ms_b)):
         tb = delta_traffic(counters_name, phase)
         if tb is not None:  # measured bytes of the phase over its time
@@ -569,21 +574,20 @@ def bench_delta(args):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
         "higher_is_better": False, "scaling": "weak",
         # the pages' number for this setting, on another machine (context)
-        "vs_baseline": (round(ms / DELTA8B_PAGES_MS, 4)
-                        if shape.name == "delta8b" and not args.no_recompute else None),
+        "vs_baseline": (round(ms / DELTA8B_PAGES_MS, 4) if shape.name == "delta8b"
+                        and not args.no_recompute and not args.bf16_grads else None),
         "dtype": "f32",
         "data": "synthetic: seeded N(0,1) block deltas x U(0.5,2), N(0,1) null source and "
                 "residual stream, N(0,0.02^2) queries, N(0,1) upstream gradients, bf16 storage",
         "config": {"workload": shape.name, "tokens": T, "d": d, "heads": H,
                    "calls": DELTA_SITES, "max_sources": max(sched) + 1, "storage": shape.dtype,
                    "per_call_checkpointing": not args.no_recompute,
+                   "gradients": "bf16" if args.bf16_grads else "f32",
                    "baseline_ms_other_hardware": DELTA8B_PAGES_MS},
-        **measured_fields(shape.name if not args.no_recompute else shape.name + "_norecompute",
-                          ms, by_f + by_b),
+        **measured_fields(counters_name, ms, by_f + by_b),
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(a / HBM_PEAK_GBPS, 3),
-                     "traffic": delta_traffic(shape.name if not args.no_recompute
-                                              else shape.name + "_norecompute", dom),
+                     "traffic": delta_traffic(counters_name, dom),
                      "alg_bytes_per_launch": int((by_f if dom == "delta_fwd" else by_b)
                                                  / DELTA_SITES)},
         "kernels": kern,
@@ -594,16 +598,17 @@ def bench_delta(args):
     print(json.dumps(result), flush=True)
 
 
-def list_bytes(shape):
+def list_bytes(shape, grad_bytes: int = 4):
     """Algorithmic bytes of one list read: (fwd, bwd).  Every distinct source
     tensor is read once (a broadcast tensor is one row), whatever the number
-    of entries naming it; float32 gradients are written per entry."""
+    of entries naming it; gradients (float32, or bf16 with grad_bytes = 2)
+    are written per entry."""
     T, d, r, H, n = shape.tokens, shape.d, shape.r, shape.heads, shape.n
     b = 2 if shape.dtype == "bf16" else 4
     src = sum((1 if shape.broadcast(k) else T) * d * b for k in range(shape.tensors))
     stats = 4 * n * T * H + 4 * T * H + 4 * n * T  # alpha, lse, inverse RMS
     fwd = src + r * b + T * d * b + stats
-    bwd = src + r * b + T * d * b + stats + 4 * n * T * d + 4 * r
+    bwd = src + r * b + T * d * b + stats + grad_bytes * n * T * d + 4 * r
     return fwd, bwd
 
 
@@ -649,7 +654,7 @@ def bench_list(args):
     q = torch.as_strided(qbuf, (shape.r,), (shape.qstride,))
     dout = to_device(inp.value("dout"), shape.dtype)
     rd = ListRead([views[k] for k in shape.entries], q, shape.heads, eps=shape.eps,
-                  norm=shape.norm, tokens=T)
+                  norm=shape.norm, tokens=T, grad_dtype="bf16" if args.bf16_grads else "f32")
     torch.cuda.synchronize()
     print(f"[bench] {shape.describe()}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -670,14 +675,16 @@ def bench_list(args):
     ms_f, ms_b = t_f / args.steps, t_b / args.steps
     ms = ms_f + ms_b
     probe = bandwidth_probe(torch)  # also the calibration run of the HBM counters
-    by_f, by_b = list_bytes(shape)
+    by_f, by_b = list_bytes(shape, 2 if args.bf16_grads else 4)
+    # counters are taken with float32 gradients
+    counters_name = shape.name + ("_bf16grads" if args.bf16_grads else "")
     print(f"[bench] {args.steps} steps: {ms:.3f} ms/read (fwd {ms_f:.3f}, bwd {ms_b:.3f})",
           file=sys.stderr, flush=True)
     kern = {"list_fwd": {"ms_per_read": round(ms_f, 3), "gbps": round(by_f / ms_f / 1e6, 1)},
             "list_bwd": {"ms_per_read": round(ms_b, 3), "gbps": round(by_b / ms_b / 1e6, 1),
                          "includes": "the fixed-order dq reduction"}}
     for phase, t_ms in (("list_fwd", ms_f), ("list_bwd", ms_b)):
-        tb = list_traffic(shape.name, phase)
+        tb = list_traffic(counters_name, phase)
         if tb is not None:  # measured bytes of the phase over its time
             kern[phase]["hbm_gbps"] = round(tb / t_ms / 1e6, 1)
     dom = max(kern, key=lambda k: kern[k]["ms_per_read"])
@@ -692,11 +699,12 @@ def bench_list(args):
         "config": {"workload": shape.name, "tokens": T, "d": shape.d, "r": shape.r,
                    "heads": shape.heads, "entries": shape.n, "tensors": shape.tensors,
                    "strides": [shape.stride(k) for k in range(shape.tensors)],
-                   "query_stride": shape.qstride, "storage": shape.dtype, "norm": shape.norm},
-        **measured_fields(shape.name, ms, by_f + by_b, unit="read"),
+                   "query_stride": shape.qstride, "storage": shape.dtype, "norm": shape.norm,
+                   "gradients": "bf16" if args.bf16_grads else "f32"},
+        **measured_fields(counters_name, ms, by_f + by_b, unit="read"),
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(a / HBM_PEAK_GBPS, 3),
-                     "traffic": list_traffic(shape.name, dom),
+                     "traffic": list_traffic(counters_name, dom),
                      "alg_bytes_per_launch": by_f if dom == "list_fwd" else by_b},
         "kernels": kern,
         "probe": probe,
@@ -807,6 +815,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mhar1b")
+    ap.add_argument("--bf16-grads", action="store_true",
+                    help="list and delta reads: write the source gradients in bf16 (grad_dtype)")
     ap.add_argument("--square-state", action="store_true",
                     help="give every site max_rows + 1 slots of saved state (default: packed "
                          "by the schedule, attnres_config_t.max_slots)")

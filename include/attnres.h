@@ -296,6 +296,9 @@ typedef struct {
   const void* const* deltas;  /* host array [n_deltas] of device [T, d] pointers */
   const void* null_src;       /* device [d] storage dtype, or NULL for no null source */
   const void* query;          /* device [d] storage dtype */
+  int32_t grad_dtype;         /* attnres_dtype_t of the delta gradients attnres_delta_bwd
+                                 writes: ATTNRES_F32 (0, the default) or ATTNRES_BF16, each
+                                 value rounded once from its float32 sum */
 } attnres_delta_t;
 
 /* Device workspace bytes attnres_delta_bwd needs for this call shape (0 if the
@@ -318,8 +321,9 @@ attnres_status_t attnres_delta_fwd(const attnres_delta_t* call, const void* part
  *   alpha      what attnres_delta_fwd wrote for the same call
  *   lse        the forward's log-sum-exp; not read (the logits are recomputed
  *              with the inverse RMS), may be NULL
- *   d_deltas   host array [n_deltas] of device float32 [T, d]: gradient of
- *              each delta (stored, not accumulated)
+ *   d_deltas   host array [n_deltas] of device [T, d] arrays of
+ *              call->grad_dtype (float32, or bf16 passed as float*): gradient
+ *              of each delta (stored, not accumulated)
  *   d_null     device float32 [d]: gradient of the null source (its
  *              per-token gradients summed over tokens); NULL iff no null source
  *   dq         device float32 [d]: gradient of the query
@@ -365,6 +369,10 @@ typedef struct {
                                      (>= 0), or NULL for d */
   const void* query;         /* device: query coordinate k at query + k * query_stride */
   int64_t query_stride;      /* elements, >= 1 */
+  int32_t grad_dtype;        /* attnres_dtype_t of the source gradients attnres_list_bwd
+                                writes: ATTNRES_F32 (0, the default) or ATTNRES_BF16, each
+                                value rounded once from its float32 sum (the pages' operator
+                                writes bf16 source gradients, Appendix I) */
 } attnres_list_t;
 
 /* Device workspace bytes attnres_list_bwd needs for this call shape (0 if the
@@ -384,10 +392,12 @@ attnres_status_t attnres_list_fwd(const attnres_list_t* call, void* out, float* 
 /* Backward of one list read, for the loss <dout, out>.
  *   dout       device [T, d] storage dtype, contiguous
  *   alpha, lse, rinv   what attnres_list_fwd wrote for the same call and inputs
- *   d_sources  host array [n_sources] of device float32 [T, d], contiguous: the
- *              gradient of each entry (stored, not accumulated); entries must
- *              be distinct buffers, also when sources repeat (the gradient of
- *              a repeated tensor is the sum of its entries' gradients)
+ *   d_sources  host array [n_sources] of device [T, d] arrays of
+ *              call->grad_dtype (float32, or bf16 passed as float*),
+ *              contiguous: the gradient of each entry (stored, not
+ *              accumulated); entries must be distinct buffers, also when
+ *              sources repeat (the gradient of a repeated tensor is the sum
+ *              of its entries' gradients)
  *   dq         device float32 [r]: gradient of the query coordinates
  *   workspace  attnres_list_workspace_bytes(call) bytes of device memory
  * Reductions over tokens run in a fixed order: results are bitwise
@@ -406,8 +416,8 @@ attnres_status_t attnres_list_bwd(const attnres_list_t* call, const void* dout,
  * address on the first call on that device.
  *   Arguments as attnres_list_bwd, without the workspace.
  *   A shape whose attnres_list_workspace_bytes exceeds 32 MiB returns
- *   ATTNRES_ERR_CAPACITY before any launch (e.g. r = 2048 fits at any token
- *   count, r = 4096 up to 2048 tokens).
+ *   ATTNRES_ERR_CAPACITY before any launch (e.g. r = 4096 fits at any token
+ *   count, r = 8192 up to 1024 tokens).
  * Every call on one device shares that device's scratch, and each call
  * rewrites every partial row it reads: calls that may overlap on one device
  * (concurrent streams, or threads) race and give wrong query gradients. */
@@ -457,7 +467,8 @@ const char* attnres_last_error(void);
 /* Destroy the handle (the caller's buffers are untouched).  NULL is ignored. */
 void attnres_bank_destroy(attnres_bank_t bank);
 
-/* ABI version of this header: 4 (3 had no max_slots field in
+/* ABI version of this header: 5 (4 had no grad_dtype fields in
+ * attnres_list_t and attnres_delta_t; 3 had no max_slots field in
  * attnres_config_t; 2 had no source-list read; 1 had no norm field and no
  * gains). */
 int32_t attnres_abi_version(void);

@@ -34,7 +34,7 @@ def test_header_declarations_are_exported(lib):
     assert set(names) == set(A.EXPORTS)
     for n in names:
         assert getattr(lib, n) is not None
-    assert A.attnres_abi_version() == 4
+    assert A.attnres_abi_version() == 5
 
 
 def cfg(**kw):

@@ -35,7 +35,7 @@ CASES = [
 ]
 
 
-def run_gpu(s: DeltaShape, inp: DeltaInputs, tokens=None, dout_tokens=None):
+def run_gpu(s: DeltaShape, inp: DeltaInputs, tokens=None, dout_tokens=None, grad_dtype="f32"):
     import torch
     from transformer_depth_wise_amd.attnres import DeltaRead
     deltas = [to_device(inp.value("delta", m), s.dtype) for m in range(s.n_deltas)]
@@ -49,7 +49,7 @@ def run_gpu(s: DeltaShape, inp: DeltaInputs, tokens=None, dout_tokens=None):
         dout_np = dout_np.copy()
         dout_np[~keep] = 0.0
     dout = to_device(dout_np, s.dtype)
-    rd = DeltaRead(deltas, null, q, s.heads, tokens=s.tokens, eps=s.eps)
+    rd = DeltaRead(deltas, null, q, s.heads, tokens=s.tokens, eps=s.eps, grad_dtype=grad_dtype)
     out, alpha, lse = rd.forward(partial)
     dd, dn, dq = rd.backward(dout, alpha, lse)
     torch.cuda.synchronize()
@@ -130,6 +130,33 @@ def test_delta_matches_oracle(s):
     inp = DeltaInputs(s)
     log(f"[delta] {s.describe()}")
     compare(s, run_gpu(s, inp), run_ref(s, inp), label="delta")
+
+
+# bf16 delta gradients (attnres_delta_t.grad_dtype): 4-value chunks (fp32
+# storage: one 8-byte store), 8-value chunks (bf16: one 16-byte store), the
+# two-waves-per-token layout and the 8B shape
+BF16_GRAD_CASES = [c for c in CASES if c.name in (
+    "f32_d64_h4", "bf16_d1280_h8", "bf16_d4096_h8", "f32_d2048_h4_split")]
+
+
+@pytest.mark.parametrize("s", BF16_GRAD_CASES, ids=lambda s: s.name)
+def test_delta_bf16_gradients(s):
+    """With grad_dtype = bf16 every delta gradient is the float32 gradient of
+    the same kernel rounded once to bf16 (nearest even), bit for bit; the null
+    source and query gradients are unchanged."""
+    import torch
+
+    inp = DeltaInputs(s)
+    log(f"[delta bf16 grads] {s.describe()}")
+    g32 = run_gpu(s, inp)
+    g16 = run_gpu(s, inp, grad_dtype="bf16")
+    for a, b in zip(g32["dd"], g16["dd"]):
+        rounded = torch.from_numpy(a).to(torch.bfloat16).to(torch.float32).numpy()
+        np.testing.assert_array_equal(b, rounded)
+    np.testing.assert_array_equal(g16["dq"], g32["dq"])
+    if g32["dnull"] is not None:
+        np.testing.assert_array_equal(g16["dnull"], g32["dnull"])
+    np.testing.assert_array_equal(g16["out"], g32["out"])
 
 
 def test_delta_empty_tokens():

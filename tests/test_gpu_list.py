@@ -160,6 +160,40 @@ def test_list_matches_oracle(s):
     compare(s, run_gpu(s, inp), run_ref(s, inp), label="list")
 
 
+# bf16 source gradients (attnres_list_t.grad_dtype): the element-wise path
+# with bf16 and fp32 storage, the 16-byte paths with fp32 storage (4 values,
+# one 8-byte store) and bf16 storage (8 values, one 16-byte store), the
+# full-width RMS and sharp routing
+BF16_GRAD_CASES = [c for c in CASES if c.name in (
+    "d513_r135_h3", "d7_r3_f32_full", "vec_f32_d256", "lr_d7168_r1792_h8", "sharp_vec_bf16_d512")]
+
+
+@pytest.mark.parametrize("s", BF16_GRAD_CASES, ids=lambda s: s.name)
+def test_list_bf16_gradients(s):
+    """With grad_dtype = bf16 every source gradient is the float32 gradient of
+    the same kernel rounded once to bf16 (nearest even), bit for bit, and the
+    query gradient is unchanged; against the oracle the gradients are within
+    bf16's own rounding."""
+    import torch
+    from transformer_depth_wise_amd.attnres import ListRead
+
+    inp = ListInputs(s)
+    log(f"[list bf16 grads] {s.describe()}")
+    dev = upload(s, inp)
+    got32 = run_gpu(s, inp, dev=dev)
+    rd = ListRead(dev[0], dev[1], s.heads, eps=s.eps, norm=s.norm, tokens=s.tokens,
+                  grad_dtype="bf16")
+    got16 = run_gpu(s, inp, read=rd, dev=dev)
+    for a, b in zip(got32["ds"], got16["ds"]):
+        rounded = torch.from_numpy(a).to(torch.bfloat16).to(torch.float32).numpy()
+        np.testing.assert_array_equal(b, rounded)
+    np.testing.assert_array_equal(got16["dq"], got32["dq"])
+    ref = run_ref(s, inp)
+    err = max(max_rel(a, b) for a, b in zip(got16["ds"], ref["ds"]))
+    log(f"  bf16 gradients vs oracle: {err:.3e}")
+    assert err <= tolerance("bf16", ref["lse"])
+
+
 def test_list_empty_tokens():
     s = ListShape("d513_t0", 0, 513, 135, 3, (0, 1))
     inp = ListInputs(s)

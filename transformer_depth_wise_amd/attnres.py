@@ -88,6 +88,7 @@ class DeltaCallC(ctypes.Structure):
         ("deltas", POINTER(c_void_p)),
         ("null_src", c_void_p),
         ("query", c_void_p),
+        ("grad_dtype", c_int32),
     ]
 
 
@@ -105,6 +106,7 @@ class ListCallC(ctypes.Structure):
         ("source_strides", POINTER(c_int64)),
         ("query", c_void_p),
         ("query_stride", c_int64),
+        ("grad_dtype", c_int32),
     ]
 
 
@@ -410,12 +412,15 @@ class Bank:
 
 # ---------------------------------------------------------------------------
 # Delta form: one self-contained read per call.
-def make_delta_call(tokens, d, heads, deltas, null_src, query, dtype, eps=1e-6):
+def make_delta_call(tokens, d, heads, deltas, null_src, query, dtype, eps=1e-6,
+                    grad_dtype=ATTNRES_F32):
     """The C description of one delta read; `deltas` is a list of device
-    tensors or addresses (kept alive by the caller)."""
+    tensors or addresses (kept alive by the caller); `grad_dtype` the dtype
+    of the delta gradients the backward writes."""
     ptrs = (c_void_p * max(len(deltas), 1))(*[_ptr(x) for x in deltas])
     call = DeltaCallC(int(tokens), int(d), int(heads), len(deltas), int(dtype), float(eps),
-                      ctypes.cast(ptrs, POINTER(c_void_p)), _ptr(null_src), _ptr(query))
+                      ctypes.cast(ptrs, POINTER(c_void_p)), _ptr(null_src), _ptr(query),
+                      int(grad_dtype))
     call._ptrs = ptrs  # keep the pointer array alive with the struct
     return call
 
@@ -445,7 +450,7 @@ class DeltaRead:
     """One delta read over device tensors: deltas (list of [T, d]), an optional
     null source [d] and the query [d], all in the storage dtype."""
 
-    def __init__(self, deltas, null_src, query, heads, tokens=None, eps=1e-6):
+    def __init__(self, deltas, null_src, query, heads, tokens=None, eps=1e-6, grad_dtype="f32"):
         import torch
         self.torch = torch
         self.deltas, self.null_src, self.query = list(deltas), null_src, query
@@ -458,7 +463,9 @@ class DeltaRead:
         self.H = int(heads)
         self.tdtype = query.dtype
         dt = ATTNRES_BF16 if query.dtype == torch.bfloat16 else ATTNRES_F32
-        self.call = make_delta_call(self.T, self.d, self.H, self.deltas, null_src, query, dt, eps)
+        self.gdtype = torch.bfloat16 if grad_dtype == "bf16" else torch.float32
+        self.call = make_delta_call(self.T, self.d, self.H, self.deltas, null_src, query, dt, eps,
+                                    ATTNRES_BF16 if grad_dtype == "bf16" else ATTNRES_F32)
         self.n = len(self.deltas) + (1 if null_src is not None else 0)
 
     def forward(self, partial=None, stream=None):
@@ -471,7 +478,7 @@ class DeltaRead:
 
     def backward(self, dout, alpha, lse, stream=None):
         torch = self.torch
-        dd = [torch.empty((self.T, self.d), dtype=torch.float32, device="cuda")
+        dd = [torch.empty((self.T, self.d), dtype=self.gdtype, device="cuda")
               for _ in self.deltas]
         dn = (torch.empty(self.d, dtype=torch.float32, device="cuda")
               if self.null_src is not None else None)
@@ -485,10 +492,11 @@ class DeltaRead:
 # ---------------------------------------------------------------------------
 # Source list: one self-contained read over any shape.
 def make_list_call(tokens, d, r, heads, sources, strides, query, query_stride, dtype,
-                   eps=1e-6, norm="slice"):
+                   eps=1e-6, norm="slice", grad_dtype=ATTNRES_F32):
     """The C description of one list read.  `sources` are device tensors or
     addresses (kept alive by the caller), `strides` their token strides in
-    elements (None: d for every source)."""
+    elements (None: d for every source); `grad_dtype` the dtype of the source
+    gradients the backward writes."""
     n = len(sources)
     ptrs = (c_void_p * max(n, 1))(*[_ptr(x) for x in sources])
     st = None
@@ -498,7 +506,7 @@ def make_list_call(tokens, d, r, heads, sources, strides, query, query_stride, d
                      NORMS[norm] if isinstance(norm, str) else int(norm),
                      ctypes.cast(ptrs, POINTER(c_void_p)),
                      ctypes.cast(st, POINTER(c_int64)) if st is not None else None,
-                     _ptr(query), int(query_stride))
+                     _ptr(query), int(query_stride), int(grad_dtype))
     call._keep = (ptrs, st)  # keep the host arrays alive with the struct
     return call
 
@@ -537,7 +545,8 @@ class ListRead:
     one row) and may repeat, `query` a [r] view (any element stride), all in
     the storage dtype.  Keys are the last r coordinates."""
 
-    def __init__(self, sources, query, heads, eps=1e-6, norm="slice", tokens=None):
+    def __init__(self, sources, query, heads, eps=1e-6, norm="slice", tokens=None,
+                 grad_dtype="f32"):
         import torch
         self.torch = torch
         self.sources = list(sources)
@@ -553,8 +562,10 @@ class ListRead:
         self.tdtype = query.dtype
         dt = ATTNRES_BF16 if query.dtype == torch.bfloat16 else ATTNRES_F32
         strides = [x.stride(0) for x in self.sources]
+        self.gdtype = torch.bfloat16 if grad_dtype == "bf16" else torch.float32
         self.call = make_list_call(self.T, self.d, self.r, self.H, self.sources, strides, query,
-                                   query.stride(0), dt, eps, norm)
+                                   query.stride(0), dt, eps, norm,
+                                   ATTNRES_BF16 if grad_dtype == "bf16" else ATTNRES_F32)
         self.n = len(self.sources)
 
     def forward(self, stream=None):
@@ -568,7 +579,7 @@ class ListRead:
 
     def backward(self, dout, alpha, lse, rinv, stream=None):
         torch = self.torch
-        ds = [torch.empty((self.T, self.d), dtype=torch.float32, device="cuda")
+        ds = [torch.empty((self.T, self.d), dtype=self.gdtype, device="cuda")
               for _ in self.sources]
         dq = torch.empty(self.r, dtype=torch.float32, device="cuda")
         nbytes = attnres_list_workspace_bytes(self.call)

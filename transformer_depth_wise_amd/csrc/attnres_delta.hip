@@ -32,6 +32,24 @@ struct DSlot {
   int tau, c, h;
 };
 
+// Store N gradient values of one chunk as GT, non-temporal: float32 (N / 4
+// 16-byte words), or bf16 rounded once (N = 8: one 16-byte word; N = 4: one
+// 8-byte word).
+template <typename GT, int N>
+__device__ __forceinline__ void st_grad(GT* o, const float* gr) {
+  if constexpr (sizeof(GT) == 4) {
+#pragma unroll
+    for (int e = 0; e < N; e += 4)
+      st_stream(o + e, make_float4(gr[e], gr[e + 1], gr[e + 2], gr[e + 3]));
+  } else if constexpr (N == 8) {
+    st_stream(reinterpret_cast<uint4*>(o), Vec<bf16_t>::pack(gr));
+  } else {
+    static_assert(N == 4, "a chunk holds 4 or 8 values");
+    *reinterpret_cast<uint2*>(o) = make_uint2(bf16_bits(gr[0]) | (bf16_bits(gr[1]) << 16),
+                                              bf16_bits(gr[2]) | (bf16_bits(gr[3]) << 16));
+  }
+}
+
 template <typename T, int CPT>
 struct DeltaLane {
   DSlot s[CPT];
@@ -215,7 +233,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_fwd(DeltaGeom g, DeltaArgs 
 // this kernel keeps the two scalar sums (per head, and total) and
 // k_delta_null_vec forms the first term.  Each work-group writes one [d]
 // partial of dq and one [H + 1] partial of the null scalars.
-template <typename T, int CPT>
+template <typename T, int CPT, typename GT>
 __global__ __launch_bounds__(kDThreads) void k_delta_bwd(DeltaGeom g, DeltaArgs a,
                                                          const T* __restrict__ dout,
                                                          const float* __restrict__ alpha,
@@ -349,7 +367,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_bwd(DeltaGeom g, DeltaArgs 
       uint4 x[CPT];
       load_row(k, x);
       const bool is_null = has_null && k == 0;
-      float* dst = is_null ? nullptr : dg.d[k - (has_null ? 1 : 0)];
+      GT* dst = is_null ? nullptr : static_cast<GT*>(dg.d[k - (has_null ? 1 : 0)]);
 #pragma unroll
       for (int j = 0; j < CPT; ++j) {
         const int tau = L.s[j].tau;
@@ -370,10 +388,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_bwd(DeltaGeom g, DeltaArgs 
         V::unpack(s_q[L.s[j].c], qf);
 #pragma unroll
         for (int e = 0; e < N; ++e) gr[e] = al * df[e] + cq * qf[e] - rc * xf[e];
-        float* o = dst + (t0 + tau) * g.d + (int64_t)L.s[j].c * N;
-#pragma unroll
-        for (int e = 0; e < N; e += 4)
-          st_stream(o + e, make_float4(gr[e], gr[e + 1], gr[e + 2], gr[e + 3]));
+        st_grad<GT, N>(dst + (t0 + tau) * g.d + (int64_t)L.s[j].c * N, gr);
       }
     }
     wave_lds_fence();
@@ -629,7 +644,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_fwd_s(DeltaGeom g, DeltaArg
   }
 }
 
-template <typename T, int CPT>
+template <typename T, int CPT, typename GT>
 __global__ __launch_bounds__(kDThreads) void k_delta_bwd_s(DeltaGeom g, DeltaArgs a,
                                                            const T* __restrict__ dout,
                                                            const float* __restrict__ alpha,
@@ -763,7 +778,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_bwd_s(DeltaGeom g, DeltaArg
       uint4 x[CPT];
       load_row(k, x);
       const bool is_null = has_null && k == 0;
-      float* dst = is_null ? nullptr : dg.d[k - (has_null ? 1 : 0)];
+      GT* dst = is_null ? nullptr : static_cast<GT*>(dg.d[k - (has_null ? 1 : 0)]);
       const float ri = w_rinv[k];
       const float rc = ri * ri / (float)g.d * w_c[k];
 #pragma unroll
@@ -783,10 +798,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_bwd_s(DeltaGeom g, DeltaArg
         V::unpack(s_q[c], qf);
 #pragma unroll
         for (int e = 0; e < N; ++e) gr[e] = al * df[e] + cq * qf[e] - rc * xf[e];
-        float* o = dst + t * g.d + (int64_t)c * N;
-#pragma unroll
-        for (int e = 0; e < N; e += 4)
-          st_stream(o + e, make_float4(gr[e], gr[e + 1], gr[e + 2], gr[e + 3]));
+        st_grad<GT, N>(dst + t * g.d + (int64_t)c * N, gr);
       }
     }
     __syncthreads();  // the next tile reuses s_x and the wave regions
@@ -846,12 +858,19 @@ static hipError_t delta_launch(const DeltaGeom& g, const DeltaArgs& a, bool fwd,
                          static_cast<const T*>(p0), static_cast<T*>(p1),
                          const_cast<float*>(alpha), lse);
   } else {
-    if (g.split)
-      hipLaunchKernelGGL((k_delta_bwd_s<T, CPT>), dim3((unsigned)parts), dim3(kDThreads), lds, st,
-                         g, a, static_cast<const T*>(dout), alpha, *dg, dq_part, ns_part);
+    const dim3 grid((unsigned)parts);
+    if (g.split && dg->bf16)
+      hipLaunchKernelGGL((k_delta_bwd_s<T, CPT, bf16_t>), grid, dim3(kDThreads), lds, st, g, a,
+                         static_cast<const T*>(dout), alpha, *dg, dq_part, ns_part);
+    else if (g.split)
+      hipLaunchKernelGGL((k_delta_bwd_s<T, CPT, float>), grid, dim3(kDThreads), lds, st, g, a,
+                         static_cast<const T*>(dout), alpha, *dg, dq_part, ns_part);
+    else if (dg->bf16)
+      hipLaunchKernelGGL((k_delta_bwd<T, CPT, bf16_t>), grid, dim3(kDThreads), lds, st, g, a,
+                         static_cast<const T*>(dout), alpha, *dg, dq_part, ns_part);
     else
-      hipLaunchKernelGGL((k_delta_bwd<T, CPT>), dim3((unsigned)parts), dim3(kDThreads), lds, st,
-                         g, a, static_cast<const T*>(dout), alpha, *dg, dq_part, ns_part);
+      hipLaunchKernelGGL((k_delta_bwd<T, CPT, float>), grid, dim3(kDThreads), lds, st, g, a,
+                         static_cast<const T*>(dout), alpha, *dg, dq_part, ns_part);
   }
   return hipGetLastError();
 }

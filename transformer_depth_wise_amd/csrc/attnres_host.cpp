@@ -341,7 +341,7 @@ void trace_clear(attnres_bank_s* b) {
 
 extern "C" {
 
-int32_t attnres_abi_version(void) { return 4; }
+int32_t attnres_abi_version(void) { return 5; }
 
 attnres_status_t attnres_trace_enable(attnres_bank_t b, int32_t enable) {
   if (!b) return fail(ATTNRES_ERR_INVALID, "bank is NULL");
@@ -850,6 +850,9 @@ attnres_status_t delta_geom(const attnres_delta_t* c, attnres::DeltaGeom* g) {
   if (c->heads < 1 || c->d < 1 || c->d % c->heads)
     return fail(ATTNRES_ERR_INVALID, "need heads >= 1 dividing d (got d=%d heads=%d)", c->d, c->heads);
   if (!(c->eps > 0.f)) return fail(ATTNRES_ERR_INVALID, "eps must be > 0");
+  if (c->grad_dtype != ATTNRES_F32 && c->grad_dtype != ATTNRES_BF16)
+    return fail(ATTNRES_ERR_INVALID, "grad_dtype must be ATTNRES_F32 or ATTNRES_BF16 (got %d)",
+                c->grad_dtype);
   const int n = c->n_deltas + (c->null_src ? 1 : 0);
   if (c->n_deltas < 0 || n < 1 || n > attnres::kMaxDeltaSources)
     return fail(ATTNRES_ERR_INVALID, "need 1 <= n_deltas + null <= %d sources (got %d)",
@@ -985,6 +988,7 @@ attnres_status_t attnres_delta_bwd(const attnres_delta_t* call, const void* dout
       dg.d[k] = d_deltas[k];
     }
   }
+  dg.bf16 = call->grad_dtype == ATTNRES_BF16 ? 1 : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int parts = g.T > 0 ? attnres::delta_bwd_parts(g) : 0;
   char* w = static_cast<char*>(workspace);
@@ -1025,6 +1029,9 @@ attnres_status_t list_geom(const attnres_list_t* c, attnres::ListGeom* g) {
   if (!(c->eps > 0.f)) return fail(ATTNRES_ERR_INVALID, "eps must be > 0");
   if (c->norm != ATTNRES_NORM_SLICE && c->norm != ATTNRES_NORM_FULL)
     return fail(ATTNRES_ERR_INVALID, "norm must be ATTNRES_NORM_SLICE or ATTNRES_NORM_FULL");
+  if (c->grad_dtype != ATTNRES_F32 && c->grad_dtype != ATTNRES_BF16)
+    return fail(ATTNRES_ERR_INVALID, "grad_dtype must be ATTNRES_F32 or ATTNRES_BF16 (got %d)",
+                c->grad_dtype);
   if (c->n_sources < 1 || c->n_sources > attnres::kMaxListSources)
     return fail(ATTNRES_ERR_INVALID, "need 1 <= n_sources <= %d (got %d)", attnres::kMaxListSources,
                 c->n_sources);
@@ -1141,15 +1148,18 @@ attnres_status_t list_bwd_run(const attnres_list_t* call, attnres::ListGeom g, c
     if (!aligned_to(dout, es) || !aligned_to(alpha, 4) || !aligned_to(lse, 4) || !aligned_to(rinv, 4))
       return fail(ATTNRES_ERR_INVALID, "dout, alpha, lse and rinv must be aligned to their element size");
     if (!d_sources) return fail(ATTNRES_ERR_INVALID, "d_sources array is NULL");
+    const size_t gs = call->grad_dtype == ATTNRES_BF16 ? 2 : 4;
     for (int n = 0; n < g.n; ++n) {
-      if (!d_sources[n] || !aligned_to(d_sources[n], 4))
-        return fail(ATTNRES_ERR_INVALID, "d_sources[%d] must be non-NULL and 4-byte aligned", n);
+      if (!d_sources[n] || !aligned_to(d_sources[n], gs))
+        return fail(ATTNRES_ERR_INVALID, "d_sources[%d] must be non-NULL and %zu-byte aligned", n,
+                    gs);
       for (int m = 0; m < n; ++m)
         if (d_sources[m] == d_sources[n])
           return fail(ATTNRES_ERR_INVALID, "d_sources[%d] and d_sources[%d] are the same buffer", m, n);
       gr.d[n] = d_sources[n];
     }
   }
+  gr.bf16 = call->grad_dtype == ATTNRES_BF16 ? 1 : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (g.T > 0) {
     g.vec = list_vector_ok(call, g, {dout}) ? 1 : 0;

@@ -168,7 +168,8 @@ struct DeltaArgs {
   const void* deltas[kMaxDeltaSources];
 };
 struct DeltaGrads {
-  float* d[kMaxDeltaSources];  // float32 [T, d] gradient of each delta
+  void* d[kMaxDeltaSources];  // [T, d] gradient of each delta: float32, or bf16 with bf16 set
+  int32_t bf16;
 };
 size_t delta_lds_bytes(const DeltaGeom& g, bool fwd);
 int delta_bwd_parts(const DeltaGeom& g);
@@ -208,7 +209,8 @@ struct ListArgs {
   const void* query;
 };
 struct ListGrads {
-  float* d[kMaxListSources];  // float32 [T, d] gradient of each entry
+  void* d[kMaxListSources];  // [T, d] gradient of each entry: float32, or bf16 with bf16 set
+  int32_t bf16;
 };
 // LDS floats per wave of the backward: dq [r], weights and dl [n][H] each,
 // inverse RMS and radial sums [n] each, lse [H].

@@ -139,15 +139,26 @@ __device__ __forceinline__ void store_run(T* p, const float* v) {
   }
 }
 
-// Store VW float32 values (the gradients).
-template <int VW>
-__device__ __forceinline__ void store_f32(float* p, const float* v) {
-  if constexpr (VW == 1) {
-    *p = v[0];
-  } else {
+// Store VW gradient values as GT: float32, or bf16 rounded once (VW = 8: one
+// 16-byte word, VW = 4: one 8-byte word, VW = 1: one element).
+template <typename GT, int VW>
+__device__ __forceinline__ void store_grad(GT* p, const float* v) {
+  if constexpr (sizeof(GT) == 4) {
+    if constexpr (VW == 1) {
+      *p = v[0];
+    } else {
 #pragma unroll
-    for (int i = 0; i < VW / 4; ++i)
-      reinterpret_cast<float4*>(p)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+      for (int i = 0; i < VW / 4; ++i)
+        reinterpret_cast<float4*>(p)[i] =
+            make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+    }
+  } else if constexpr (VW == 1) {
+    *p = (bf16_t)bf16_bits(v[0]);
+  } else if constexpr (VW == 4) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(bf16_bits(v[0]) | (bf16_bits(v[1]) << 16),
+                                              bf16_bits(v[2]) | (bf16_bits(v[3]) << 16));
+  } else {
+    *reinterpret_cast<uint4*>(p) = Vec<bf16_t>::pack(v);
   }
 }
 
@@ -342,7 +353,7 @@ __global__ __launch_bounds__(kLFwdThreads) void k_list_fwd(ListGeom g, ListArgs 
 //   all lanes, the upstream gradient and query chunks loaded once per batch
 //   for all sources.
 //   As in the forward, chunks past the end are clamped and masked.
-template <typename T, int VW, int G, int UP, int UG>
+template <typename T, typename GT, int VW, int G, int UP, int UG>
 __global__ __launch_bounds__(256) void k_list_bwd(ListGeom g, ListArgs a,
                                                   const T* __restrict__ dout,
                                                   const float* __restrict__ alpha,
@@ -418,7 +429,7 @@ __global__ __launch_bounds__(256) void k_list_bwd(ListGeom g, ListArgs a,
           for (int i = 0; i < G; ++i) {
             if (n0 + i >= g.n) break;
             const float al = w_a[(n0 + i) * g.H + hc];
-            float* ds = gr.d[n0 + i] + t * g.d;
+            GT* ds = static_cast<GT*>(gr.d[n0 + i]) + t * g.d;
 #pragma unroll
             for (int u = 0; u < UP; ++u) {
               const int j = hb + cc[u] * VW;
@@ -426,7 +437,7 @@ __global__ __launch_bounds__(256) void k_list_bwd(ListGeom g, ListArgs a,
                 float v[VW];
 #pragma unroll
                 for (int e = 0; e < VW; ++e) v[e] = al * ym[u][e];
-                store_f32<VW>(at(ds, j), v);
+                store_grad<GT, VW>(at(ds, j), v);
               }
             }
           }
@@ -496,7 +507,7 @@ __global__ __launch_bounds__(256) void k_list_bwd(ListGeom g, ListArgs a,
           if (n >= g.n) break;
           const float rv = w_r[n];
           const float cr = rv * rv / (float)g.w * w_c[n];
-          float* ds = gr.d[n] + t * g.d;
+          GT* ds = static_cast<GT*>(gr.d[n]) + t * g.d;
 #pragma unroll
           for (int u = 0; u < UG; ++u) {
             if (ok[u]) {
@@ -514,7 +525,7 @@ __global__ __launch_bounds__(256) void k_list_bwd(ListGeom g, ListArgs a,
                   w_dq[jk + e] += bb * x[i][u][e];  // coordinates jk.. always belong to this lane
                 }
               }
-              store_f32<VW>(at(ds, j), v);
+              store_grad<GT, VW>(at(ds, j), v);
             }
           }
         }
@@ -579,6 +590,23 @@ hipError_t launch_list_fwd(const ListGeom& g, int dtype, const ListArgs& a, void
   return hipGetLastError();
 }
 
+namespace {
+
+template <typename T, int VW>
+void launch_list_bwd_as(const ListGeom& g, dim3 grid, int nw, size_t lds, const ListArgs& a,
+                        const void* dout, const float* alpha, const float* lse,
+                        const float* rinv, const ListGrads& gr, float* dq_part, hipStream_t st) {
+  typedef ListTile<T, VW> Tl;
+  if (gr.bf16)
+    hipLaunchKernelGGL((k_list_bwd<T, bf16_t, VW, Tl::G, Tl::UP, Tl::UG>), grid, dim3(64 * nw),
+                       lds, st, g, a, static_cast<const T*>(dout), alpha, lse, rinv, gr, dq_part);
+  else
+    hipLaunchKernelGGL((k_list_bwd<T, float, VW, Tl::G, Tl::UP, Tl::UG>), grid, dim3(64 * nw),
+                       lds, st, g, a, static_cast<const T*>(dout), alpha, lse, rinv, gr, dq_part);
+}
+
+}  // namespace
+
 hipError_t launch_list_bwd(const ListGeom& g, int dtype, const ListArgs& a, const void* dout,
                            const float* alpha, const float* lse, const float* rinv,
                            const ListGrads& gr, float* dq_part, int parts, hipStream_t st) {
@@ -588,17 +616,13 @@ hipError_t launch_list_bwd(const ListGeom& g, int dtype, const ListArgs& a, cons
   const dim3 grid((unsigned)parts);
   const size_t lds = sizeof(float) * (size_t)nw * list_bwd_wave_floats(g);
   if (dtype == 0 && g.vec)
-    hipLaunchKernelGGL((k_list_bwd<float, 4, ListTile<float, 4>::G, ListTile<float, 4>::UP, ListTile<float, 4>::UG>), grid, dim3(64 * nw), lds, st, g, a,
-                       static_cast<const float*>(dout), alpha, lse, rinv, gr, dq_part);
+    launch_list_bwd_as<float, 4>(g, grid, nw, lds, a, dout, alpha, lse, rinv, gr, dq_part, st);
   else if (dtype == 0)
-    hipLaunchKernelGGL((k_list_bwd<float, 1, ListTile<float, 1>::G, ListTile<float, 1>::UP, ListTile<float, 1>::UG>), grid, dim3(64 * nw), lds, st, g, a,
-                       static_cast<const float*>(dout), alpha, lse, rinv, gr, dq_part);
+    launch_list_bwd_as<float, 1>(g, grid, nw, lds, a, dout, alpha, lse, rinv, gr, dq_part, st);
   else if (g.vec)
-    hipLaunchKernelGGL((k_list_bwd<bf16_t, 8, ListTile<bf16_t, 8>::G, ListTile<bf16_t, 8>::UP, ListTile<bf16_t, 8>::UG>), grid, dim3(64 * nw), lds, st, g, a,
-                       static_cast<const bf16_t*>(dout), alpha, lse, rinv, gr, dq_part);
+    launch_list_bwd_as<bf16_t, 8>(g, grid, nw, lds, a, dout, alpha, lse, rinv, gr, dq_part, st);
   else
-    hipLaunchKernelGGL((k_list_bwd<bf16_t, 1, ListTile<bf16_t, 1>::G, ListTile<bf16_t, 1>::UP, ListTile<bf16_t, 1>::UG>), grid, dim3(64 * nw), lds, st, g, a,
-                       static_cast<const bf16_t*>(dout), alpha, lse, rinv, gr, dq_part);
+    launch_list_bwd_as<bf16_t, 1>(g, grid, nw, lds, a, dout, alpha, lse, rinv, gr, dq_part, st);
   return hipGetLastError();
 }
 
