@@ -176,6 +176,35 @@ def test_call_order_is_enforced(lib):
     assert A.last_error() != ""
 
 
+def _gpu_visible() -> bool:
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="needs a host without a GPU: the launches here would "
+                                           "run kernels on fake pointers")
+def test_failed_launch_leaves_the_handle_unchanged(lib):
+    """On a host without a GPU every kernel launch fails: each call returns
+    ATTNRES_ERR_HIP and leaves the handle as it was, so the same call fails
+    the same way again and the order checks still see the old state."""
+    b = fake_bank(cfg(tokens=8, max_rows=3, max_sites=3))
+    try:
+        A.attnres_bank_set_queries(b, [1, 2], None, FAKE)
+        for _ in range(2):
+            with pytest.raises(A.AttnResError) as e:
+                A.attnres_bank_append(b, None, stream=0)
+            assert e.value.status == A.ATTNRES_ERR_HIP
+        with pytest.raises(A.AttnResError) as e:  # no row was committed
+            A.attnres_route_fwd(b, 0, None, FAKE, stream=0)
+        assert e.value.status == A.ATTNRES_ERR_ORDER
+        assert "only 0 are committed" in A.last_error()
+    finally:
+        A.attnres_bank_destroy(b)
+
+
 def test_in_place_partial_makes_the_microbatch_forward_only(lib):
     """Accumulating into the buffer a site read as its transient source
     overwrites that source before the site's backward: the backward is
