@@ -5,12 +5,14 @@
 // with no alignment requirement on d, r, the strides or the query stride.
 // This is the path for the shapes the 16-byte bank kernels do not take
 // (unaligned widths and ranks, strided or repeated sources, strided
-// queries): every access is one element wide, consecutive lanes on
-// consecutive coordinates, so each wave load still covers a contiguous run.
-// When every width, head, stride and pointer of a call allows it (and the
-// query is unit-stride), the same kernels move one 16-byte chunk per lane
-// instead (VW = 8 bf16 or 4 fp32 values): no run then straddles the norm or
-// key boundary or a key head.
+// queries): every access is one element wide, and the lanes that share a
+// head (or, in the mix and the gradient pass, all 64 lanes) take
+// consecutive coordinates, so each wave load covers contiguous runs.  When
+// every width, head, stride and pointer of a call allows it (and the query
+// is unit-stride), the same kernels move one 16-byte chunk per lane instead
+// (VW = 8 bf16 or 4 fp32 values): no run then straddles the norm or key
+// boundary or a key head.  The source gradients are written in float32, or
+// in bf16 when the call asks for it.
 //
 // One wave per token, grid-stride over tokens; per-(token, head) reductions
 // are sums within a lane group per head (or wave sums), so no work-group
@@ -27,8 +29,9 @@
 //             - [j a norm coordinate] rinv_n^2 / w * c_n * s_n[j]
 //     dq[k] = sum_t sum_n rinv_n dl_{n,hk} s_n[d - r + k]
 //   (the radial term is the derivative of the inverse RMS; w is the number
-//   of norm coordinates).  dq is summed per wave in LDS, written as one
-//   partial row per wave, and reduced over rows in a fixed order.
+//   of norm coordinates).  dq is summed per wave in LDS; the waves of a
+//   work-group add their rows in wave order into one partial row, and the
+//   partial rows are reduced in a fixed order.
 
 #include <math.h>
 
