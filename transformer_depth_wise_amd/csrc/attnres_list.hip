@@ -48,17 +48,6 @@ using namespace dev;
 
 constexpr int kLFwdThreads = 256;  // forward: 4 waves per work-group
 
-template <typename T>
-__device__ __forceinline__ float ld1(const T* p);
-template <>
-__device__ __forceinline__ float ld1<float>(const float* p) {
-  return *p;
-}
-template <>
-__device__ __forceinline__ float ld1<bf16_t>(const bf16_t* p) {
-  return __uint_as_float((uint32_t)*p << 16);
-}
-
 __device__ __forceinline__ void st1(float* p, float v) { *p = v; }
 __device__ __forceinline__ void st1(bf16_t* p, float v) { *p = (bf16_t)bf16_bits(v); }
 
