@@ -27,8 +27,11 @@ def _fill(bank, w, inp):
         to_device(inp.dout(s), w.dtype, out=bank.dout_rows[s])
 
 
-@pytest.mark.parametrize("name", ["mhar1b", "lr_h8"])
-def test_microbatch_replays_in_a_hip_graph(name):
+@pytest.mark.parametrize("name,packed", [("mhar1b", False), ("lr_h8", False),
+                                         ("mhar1b", True)])
+def test_microbatch_replays_in_a_hip_graph(name, packed):
+    """packed: the per-site saved state packed by the schedule, whose site
+    table the first append of the microbatch uploads inside the graph."""
     import torch
     from transformer_depth_wise_amd.attnres import Bank
     from transformer_depth_wise_amd.schedule import run_microbatch
@@ -38,8 +41,9 @@ def test_microbatch_replays_in_a_hip_graph(name):
         # 12 sites: the backward calls of sites 0..4 run over at least 8 sites,
         # so the finalize stores and consumes look-ahead partial sums
         w = w.with_sites(12)
-    log(f"[graph] {w.describe()}")
-    bank = Bank(w.tokens, w.d, w.r, w.heads, w.rows, w.sites, w.dtype, w.eps)
+    slots = sum(n + (1 if e else 0) for n, e in zip(w.nsrc, w.extra)) if packed else 0
+    log(f"[graph] {w.describe()} saved-state slots={slots or 'square'}")
+    bank = Bank(w.tokens, w.d, w.r, w.heads, w.rows, w.sites, w.dtype, w.eps, max_slots=slots)
     tdt = bank.rows.dtype
     inputs = [Inputs(replace(w, seed=seed)) for seed in (0, 1, 2)]
     queries = to_device(inputs[0].queries(), w.dtype)
