@@ -16,18 +16,19 @@ from gpu_harness import log
 pytestmark = pytest.mark.gpu
 
 
-def _both(s: ListShape, inp: ListInputs):
+def _both(s: ListShape, inp: ListInputs, grad_dtype="f32"):
     import torch
     from transformer_depth_wise_amd import attnres as A
 
     from test_gpu_list import upload
 
     entries, q, bufs, qbuf = upload(s, inp)
-    rd = A.ListRead(entries, q, s.heads, eps=s.eps, norm=s.norm, tokens=s.tokens)
+    rd = A.ListRead(entries, q, s.heads, eps=s.eps, norm=s.norm, tokens=s.tokens,
+                    grad_dtype=grad_dtype)
     out, alpha, lse, rinv = rd.forward()
     dout = to_device(inp.value("dout"), s.dtype)
     ds_ws, dq_ws = rd.backward(dout, alpha, lse, rinv)
-    ds_na = [torch.full((s.tokens, s.d), float("nan"), dtype=torch.float32, device="cuda")
+    ds_na = [torch.full((s.tokens, s.d), float("nan"), dtype=rd.gdtype, device="cuda")
              for _ in entries]
     dq_na = torch.full((s.r,), float("nan"), dtype=torch.float32, device="cuda")
     A.attnres_list_bwd_noalloc(rd.call, dout, alpha, lse, rinv, ds_na, dq_na)
@@ -36,14 +37,15 @@ def _both(s: ListShape, inp: ListInputs):
             [from_device(x) for x in ds_na], from_device(dq_na))
 
 
-def test_no_alloc_list_backward_matches_workspace_backward():
+@pytest.mark.parametrize("grad_dtype", ["f32", "bf16"])
+def test_no_alloc_list_backward_matches_workspace_backward(grad_dtype):
     calls = [LIST_SHAPES["list_lr"].with_tokens(1500),
              ListShape("d513_r135_h3", 37, 513, 135, 3, (0, 1, 2, 0), pads=(87, 0, 5),
                        offsets=(1, 0, 3), qstride=7, qscale=0.3)]
     for s in calls:
         inp = ListInputs(s)
-        log(f"[no-alloc] {s.describe()}")
-        ds_ws, dq_ws, ds_na, dq_na = _both(s, inp)
+        log(f"[no-alloc] {s.describe()} gradients {grad_dtype}")
+        ds_ws, dq_ws, ds_na, dq_na = _both(s, inp, grad_dtype)
         assert np.isfinite(dq_na).all()
         np.testing.assert_array_equal(dq_na, dq_ws)
         for a, b in zip(ds_na, ds_ws):
