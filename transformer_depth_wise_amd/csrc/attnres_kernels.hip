@@ -33,6 +33,8 @@
 
 #include <math.h>
 
+#include <vector>
+
 #include "attnres_device.h"
 #include "attnres_internal.h"
 
@@ -1492,6 +1494,238 @@ __global__ __launch_bounds__(kThreads) void k_finalize(Geom g, FinalizeArgs fa, 
 }
 
 // ---------------------------------------------------------------------------
+// Finalize of several jobs over the same sites [s0, s1), none adding a stored
+// partial or accumulating (the look-ahead launches: a row and the partial sums
+// of the rows below it).  One work-group per token tile computes every job:
+// each upstream-gradient chunk is loaded once and feeds the accumulators of
+// all jobs, so the work-groups in flight stream distinct tiles.  (With one
+// job per work-group the jobs of a tile share each read through L2, and the
+// distinct bytes in flight, which bound a latency-limited stream, drop by the
+// number of jobs.)  The sums run in k_finalize's order (per site the value
+// term, then the key term; the radial sums site by site), so the results are
+// the same.  Per batch of sites the coefficients of every job and the sites'
+// query rows are staged in LDS; DEPTH upstream-gradient sites are in flight.
+// Grid: ceil(T / tt) work-groups; g.cpt == C.
+template <typename T, typename QT, int C, int DEPTH>
+__global__ __launch_bounds__(kThreads) void k_finalize_multi(Geom g, FinalizeArgs fa, int nj,
+                                                              SiteArrays sa, int batch,
+                                                              const T* __restrict__ dout_rows,
+                                                              int64_t dout_stride,
+                                                              const QT* __restrict__ Q) {
+  using V = Vec<T>;
+  constexpr int N = V::N;
+  constexpr int J = kMaxJobs;
+  extern __shared__ float sm[];
+  __shared__ int s_slot[J];
+  __shared__ const float* s_rinv[J];
+  const int tid = threadIdx.x;
+  const int64_t t0 = xcd_order(blockIdx.x, gridDim.x) * g.tt;
+  const int tv = (int)min((int64_t)g.tt, g.T - t0);
+  const int cpl = g.tt * g.H * J;          // floats per site of each coefficient array
+  float* cA = sm;                          // [batch][tt][H][J]  alpha
+  float* cQ = cA + batch * cpl;            // [batch][tt][H][J]  rho^-1 * dl
+  float* cR = cQ + batch * cpl;            // [batch][J][tt]     radial sums
+  float* s_rc = cR + batch * J * g.tt;     // [J][tt]            radial coefficients
+  uint4* sq = reinterpret_cast<uint4*>(s_rc + J * g.tt);  // [batch][qwords] query rows
+  const int qwords = g.r * (int)sizeof(QT) / 16;
+  const int s0 = fa.job[0].s0, s1 = fa.job[0].s1;
+#pragma unroll
+  for (int jj = 0; jj < J; ++jj)
+    if (tid == jj) {
+      s_slot[jj] = fa.job[jj].slot;
+      s_rinv[jj] = fa.job[jj].rinv;
+    }
+
+  Slot sl[C];
+  bool ok[C];
+  int qa[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    sl[c] = make_slot(g, tid, c);
+    ok[c] = sl[c].own && sl[c].tau < tv;
+    qa[c] = ok[c] ? sl[c].q : 0;  // other slots load the tile's first chunk, never stored
+  }
+  float acc[J][C][N];
+#pragma unroll
+  for (int jj = 0; jj < J; ++jj)
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int e = 0; e < N; ++e) acc[jj][c][e] = 0.f;
+  float rad = 0.f;  // thread tid < nj * tt: job tid / tt, token tid % tt
+  auto dout_of = [&](int s) {
+    return reinterpret_cast<const uint4*>(dout_rows + (int64_t)s * dout_stride + t0 * g.d);
+  };
+  __syncthreads();  // job table
+
+  uint4 buf[DEPTH][C];
+  for (int b0 = s0; b0 < s1; b0 += batch) {
+    const int nb = min(batch, s1 - b0);
+#pragma unroll
+    for (int d = 0; d < DEPTH - 1; ++d)
+      if (d < nb) {
+        const uint4* dp = dout_of(b0 + d);
+#pragma unroll
+        for (int c = 0; c < C; ++c) buf[d][c] = ld_stream(dp + qa[c]);
+      }
+    // coefficients of every (site, job, token, head), jobs fastest in LDS
+    if ((g.H & 3) == 0) {
+      const int h4 = g.H >> 2, per = g.tt * h4, items = nj * per;
+#pragma unroll 2
+      for (int i = tid; i < nb * items; i += kThreads) {
+        const int k = i / items;
+        int rr = i - k * items;
+        const int jj = rr / per;
+        rr -= jj * per;
+        const int tau = rr / h4, h = 4 * (rr - tau * h4);
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), q = a;
+        if (tau < tv) {
+          const SiteSlot ss = sa.sites[b0 + k];
+          const int slot = s_slot[jj];
+          a = *reinterpret_cast<const float4*>(sa.alpha + ss.base * sa.slot_th +
+                                               ((int64_t)slot * g.T + t0 + tau) * g.H + h);
+          const float4 dl = *reinterpret_cast<const float4*>(
+              sa.dl + ss.base * sa.slot_dl + coef_at(t0 + tau, slot, ss.nslot, sa.ts) * g.H + h);
+          const float ri = s_rinv[jj][t0 + tau];
+          q = make_float4(ri * dl.x, ri * dl.y, ri * dl.z, ri * dl.w);
+        }
+        float* pa = cA + k * cpl + (tau * g.H + h) * J + jj;
+        float* pq = cQ + k * cpl + (tau * g.H + h) * J + jj;
+        pa[0] = a.x, pa[J] = a.y, pa[2 * J] = a.z, pa[3 * J] = a.w;
+        pq[0] = q.x, pq[J] = q.y, pq[2 * J] = q.z, pq[3 * J] = q.w;
+      }
+    } else {
+      const int per = g.tt * g.H, items = nj * per;
+      for (int i = tid; i < nb * items; i += kThreads) {
+        const int k = i / items;
+        int rr = i - k * items;
+        const int jj = rr / per;
+        rr -= jj * per;
+        const int tau = rr / g.H, h = rr - tau * g.H;
+        float a = 0.f, q = 0.f;
+        if (tau < tv) {
+          const SiteSlot ss = sa.sites[b0 + k];
+          const int slot = s_slot[jj];
+          a = sa.alpha[ss.base * sa.slot_th + ((int64_t)slot * g.T + t0 + tau) * g.H + h];
+          q = s_rinv[jj][t0 + tau] *
+              sa.dl[ss.base * sa.slot_dl + coef_at(t0 + tau, slot, ss.nslot, sa.ts) * g.H + h];
+        }
+        cA[k * cpl + (tau * g.H + h) * J + jj] = a;
+        cQ[k * cpl + (tau * g.H + h) * J + jj] = q;
+      }
+    }
+    for (int i = tid; i < nb * nj * g.tt; i += kThreads) {
+      const int k = i / (nj * g.tt);
+      const int rr = i - k * nj * g.tt, jj = rr / g.tt, tau = rr - jj * g.tt;
+      const SiteSlot ss = sa.sites[b0 + k];
+      cR[(k * J + jj) * g.tt + tau] =
+          tau < tv ? sa.radial[ss.base * sa.slot_rad +
+                               coef_at(t0 + tau, s_slot[jj], ss.nslot, sa.ts)]
+                   : 0.f;
+    }
+    {
+      const uint4* qs = reinterpret_cast<const uint4*>(Q + (int64_t)b0 * g.r);
+      for (int i = tid; i < nb * qwords; i += kThreads) sq[i] = qs[i];
+    }
+    __syncthreads();
+    if (tid < nj * g.tt) {
+      const int jj = tid / g.tt, tau = tid - jj * g.tt;
+      for (int k = 0; k < nb; ++k) rad += cR[(k * J + jj) * g.tt + tau];
+    }
+    for (int i = 0; i < nb; i += DEPTH) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        const int k = i + d;
+        if (k < nb) {
+          if (k + DEPTH - 1 < nb) {
+            const uint4* dp = dout_of(b0 + k + DEPTH - 1);
+#pragma unroll
+            for (int c = 0; c < C; ++c) buf[(d + DEPTH - 1) % DEPTH][c] = ld_stream(dp + qa[c]);
+          }
+#pragma unroll
+          for (int c = 0; c < C; ++c) {
+            const int base = k * cpl + (sl[c].tau * g.H + sl[c].hv) * J;
+            float a[J];
+#pragma unroll
+            for (int v = 0; v < J / 4; ++v) {
+              const float4 t = *reinterpret_cast<const float4*>(cA + base + 4 * v);
+              a[4 * v] = t.x, a[4 * v + 1] = t.y, a[4 * v + 2] = t.z, a[4 * v + 3] = t.w;
+            }
+            float f[N];
+            V::unpack(buf[d][c], f);
+            if (sl[c].key) {
+              const int kb = k * cpl + (sl[c].tau * g.H + sl[c].hk) * J;
+              float b[J];
+#pragma unroll
+              for (int v = 0; v < J / 4; ++v) {
+                const float4 t = *reinterpret_cast<const float4*>(cQ + kb + 4 * v);
+                b[4 * v] = t.x, b[4 * v + 1] = t.y, b[4 * v + 2] = t.z, b[4 * v + 3] = t.w;
+              }
+              QChunk<T, QT> qc;
+              qc.load(reinterpret_cast<const QT*>(sq + k * qwords), sl[c].kc);
+              float qf[N];
+              qc.unpack(qf);
+#pragma unroll
+              for (int jj = 0; jj < J; ++jj)
+#pragma unroll
+                for (int e = 0; e < N; ++e) {
+                  acc[jj][c][e] += a[jj] * f[e];
+                  acc[jj][c][e] += b[jj] * qf[e];
+                }
+            } else {
+#pragma unroll
+              for (int jj = 0; jj < J; ++jj)
+#pragma unroll
+                for (int e = 0; e < N; ++e) acc[jj][c][e] += a[jj] * f[e];
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();  // the next batch overwrites the staged coefficients
+  }
+#pragma unroll
+  for (int jj = 0; jj < J; ++jj)
+    if (jj < nj && tid >= jj * g.tt && tid < (jj + 1) * g.tt)
+      s_rc[tid] = finalize_radial(g, fa.job[jj], t0, tid - jj * g.tt, tv, rad);
+  __syncthreads();
+
+  // (typically only the first job is a finished row that reads its source)
+#pragma unroll
+  for (int jj = 0; jj < J; ++jj) {
+    const FinalizeJob& job = fa.job[jj];
+    if (jj >= nj) break;
+    if (!job.partial_out) {
+      const uint4* xp = reinterpret_cast<const uint4*>(static_cast<const T*>(job.x) + t0 * g.d);
+      uint4 xv[C];
+#pragma unroll
+      for (int c = 0; c < C; ++c) xv[c] = (sl[c].key || g.rms_full) ? xp[qa[c]] : zero4();
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        if (sl[c].key || g.rms_full) {
+          const float rc = s_rc[jj * g.tt + sl[c].tau];
+          float f[N];
+          V::unpack(xv[c], f);
+#pragma unroll
+          for (int e = 0; e < N; ++e) acc[jj][c][e] -= rc * f[e];
+        }
+      }
+    }
+    float* dst = job.dst + t0 * g.d;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      if (!ok[c]) continue;
+      float4* o = reinterpret_cast<float4*>(dst + (int64_t)sl[c].q * N);
+#pragma unroll
+      for (int e = 0; e < N / 4; ++e)
+        st_stream(reinterpret_cast<float*>(o + e),
+                  make_float4(acc[jj][c][4 * e], acc[jj][c][4 * e + 1], acc[jj][c][4 * e + 2],
+                              acc[jj][c][4 * e + 3]));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Finalize for wide rows (at least 512 chunks, a multiple of kColBlock):
 // the same gradient as k_finalize, laid out by columns.  A work-group covers
 // kColTokens tokens x kColBlock chunk columns; thread (half, c) owns column c
@@ -2053,12 +2287,104 @@ hipError_t launch_finalize_cols(const Geom& g, int dtype, const FinalizeJob* job
   return hipSuccess;
 }
 
+hipError_t launch_finalize_jobs(const Geom& g, int dtype, const FinalizeJob* jobs, int njobs,
+                                const SiteArrays& sa, const void* dout_rows, int64_t dout_stride,
+                                const QuerySet& qs, hipStream_t st);
+
+namespace {
+
+constexpr int kFinMultiC = 2;      // chunks per thread of the multi-job finalize
+constexpr int kFinMultiDepth = 3;  // upstream-gradient sites in flight
+
+// Tile of the multi-job finalize: kFinMultiC chunks per thread (tt = 0: the
+// row does not fit one tile).
+Geom multi_geom(const Geom& g) {
+  Geom m = g;
+  m.cpt = kFinMultiC;
+  int tt = kThreads * kFinMultiC / g.cpr;
+  if (tt > 64) tt = 64;
+  if (tt * g.H > kThreads) tt = kThreads / g.H;
+  if (tt * kMaxJobs > kThreads) tt = kThreads / kMaxJobs;  // a thread per (job, token) radial sum
+  m.tt = tt;
+  m.ntiles = tt > 0 ? (g.T + tt - 1) / tt : 0;
+  return m;
+}
+
+size_t multi_site_bytes(const Geom& m, int qbytes) {
+  return sizeof(float) * (2 * (size_t)m.tt * m.H * kMaxJobs + (size_t)kMaxJobs * m.tt) +
+         (size_t)m.r * qbytes;
+}
+
+// The jobs of `jobs` that the multi-job kernel takes (same sites as the first
+// of them, no stored partial, not accumulating), in their order; the rest in
+// `rest`.
+void split_multi(const FinalizeJob* jobs, int njobs, std::vector<FinalizeJob>& multi,
+                 std::vector<FinalizeJob>& rest) {
+  for (int i = 0; i < njobs; ++i) {
+    const FinalizeJob& j = jobs[i];
+    const bool fits = !j.in && !j.accumulate && (int)multi.size() < kMaxJobs &&
+                      (multi.empty() || (j.s0 == multi[0].s0 && j.s1 == multi[0].s1));
+    (fits ? multi : rest).push_back(j);
+  }
+}
+
+template <typename T, typename QT>
+hipError_t launch_multi_as(const Geom& m, const FinalizeArgs& fa, int nj, const SiteArrays& sa,
+                           int batch, size_t lds, const void* dout_rows, int64_t dout_stride,
+                           const QT* Q, hipStream_t st) {
+  hipLaunchKernelGGL((k_finalize_multi<T, QT, kFinMultiC, kFinMultiDepth>),
+                     dim3((unsigned)m.ntiles), dim3(kThreads), lds, st, m, fa, nj, sa, batch,
+                     static_cast<const T*>(dout_rows), dout_stride, Q);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_finalize(const Geom& g, int dtype, const FinalizeJob* jobs, int njobs,
                            const SiteArrays& sa, const void* dout_rows, int64_t dout_stride,
                            const QuerySet& qs, hipStream_t st) {
   if (g.T == 0 || njobs == 0) return hipSuccess;
   if (finalize_by_columns(g))
     return launch_finalize_cols(g, dtype, jobs, njobs, sa, dout_rows, dout_stride, qs, st);
+  {
+    // Several jobs over the same sites: one multi-job launch for them, the
+    // others below.
+    std::vector<FinalizeJob> multi, rest;
+    split_multi(jobs, njobs, multi, rest);
+    const Geom m = multi_geom(g);
+    const int qbytes = (dtype == 0 || qs.qf) ? 4 : 2;
+    const size_t per = m.tt > 0 ? multi_site_bytes(m, qbytes) : 0;
+    const size_t fixed = sizeof(float) * (size_t)kMaxJobs * m.tt;
+    if (multi.size() >= 2 && m.tt > 0 && fixed + per <= kLdsBudget) {
+      const int sites = multi[0].s1 - multi[0].s0;
+      int batch = (int)((kLdsBudget - fixed) / per);
+      if (batch > sites) batch = sites;
+      const size_t lds = fixed + per * (size_t)batch;
+      FinalizeArgs fa{};
+      for (size_t i = 0; i < multi.size(); ++i) fa.job[i] = multi[i];
+      const int nj = (int)multi.size();
+      hipError_t e;
+      if (dtype == 0)
+        e = launch_multi_as<float, float>(m, fa, nj, sa, batch, lds, dout_rows, dout_stride,
+                                          qs.qf ? qs.qf : static_cast<const float*>(qs.q), st);
+      else if (qs.qf)
+        e = launch_multi_as<bf16_t, float>(m, fa, nj, sa, batch, lds, dout_rows, dout_stride,
+                                           qs.qf, st);
+      else
+        e = launch_multi_as<bf16_t, bf16_t>(m, fa, nj, sa, batch, lds, dout_rows, dout_stride,
+                                            static_cast<const bf16_t*>(qs.q), st);
+      if (e != hipSuccess || rest.empty()) return e;
+      return launch_finalize_jobs(g, dtype, rest.data(), (int)rest.size(), sa, dout_rows,
+                                  dout_stride, qs, st);
+    }
+  }
+  return launch_finalize_jobs(g, dtype, jobs, njobs, sa, dout_rows, dout_stride, qs, st);
+}
+
+// One work-group per (tile, job).
+hipError_t launch_finalize_jobs(const Geom& g, int dtype, const FinalizeJob* jobs, int njobs,
+                                const SiteArrays& sa, const void* dout_rows, int64_t dout_stride,
+                                const QuerySet& qs, hipStream_t st) {
   int max_sites = 1;
   for (int i = 0; i < njobs; ++i)
     if (jobs[i].s1 - jobs[i].s0 > max_sites) max_sites = jobs[i].s1 - jobs[i].s0;
