@@ -692,14 +692,32 @@ attnres_status_t attnres_route_bwd(attnres_bank_t b, int32_t site, const void* e
   const int parts = attnres::bwd_site_parts(b->g_site);
   attnres_status_t us = upload_sites(b, st);  // (route_fwd has enqueued it already)
   if (us != ATTNRES_OK) return us;
+  // The transient source is read by this site only: where the site pass can,
+  // it forms that source's gradient itself (no finalize job, no second read
+  // of the upstream gradient and the source).
+  // (Not for a block partial sum's running gradient: adding into it there
+  // measured slower than the finalize job.)
+  const bool fuse_extra =
+      extra && c.tokens > 0 && b->has_extra[site] != 2 &&
+      attnres::site_forms_extra_grad(b->g_site) &&
+      attnres::lds_bwd_site(b->g_site, n_rows + 1, true) <= attnres::kMaxLds;
   {
     attnres::Geom gs = b->g_site;
     gs.nslot = b->site_tab[site].nslot;  // this site's coefficient slots
+    attnres::ExtraGrad xg{};
+    if (fuse_extra) {
+      const attnres::QuerySet qs = b->qset();
+      const size_t qoff = (size_t)site * c.r;
+      xg.dst = d_extra;
+      xg.q = qs.qf ? static_cast<const void*>(qs.qf + qoff)
+                   : static_cast<const void*>(static_cast<const char*>(qs.q) + qoff * b->esz);
+      xg.q_f32 = (qs.qf || c.dtype == ATTNRES_F32) ? 1 : 0;
+    }
     TraceScope ts(b, ATTNRES_KERNEL_BWD_SITE, st);
     hipError_t e = attnres::launch_bwd_site(
         gs, c.dtype, b->rows, row_stride, extra, n_rows, b->site_alpha(site),
         b->site_lse(site), b->rinv(0), extra ? b->rinvx(site) : nullptr, slot, b->site_dl(site),
-        b->site_radial(site), b->f(b->lay.dqpart), parts, st);
+        b->site_radial(site), b->f(b->lay.dqpart), parts, xg, st);
     ts.done();
     if (e != hipSuccess) return hip_fail(e, "route_bwd site kernel");
     // With no tokens there are no parts and the reduction writes zeros.
@@ -742,7 +760,7 @@ attnres_status_t attnres_route_bwd(attnres_bank_t b, int32_t site, const void* e
   // the previous look-ahead's rows lie above this call's rows (which hold
   // none), all finalized already.
   const int n_ahead = std::min({kFinAhead, c.max_rows - 1, lo,
-                                attnres::kMaxJobs - (int)jobs.size() - (extra ? 1 : 0)});
+                                attnres::kMaxJobs - (int)jobs.size() - (extra && !fuse_extra ? 1 : 0)});
   if (lo < n_rows && !any_partial && c.tokens > 0 && b->n_sites - site >= kFinAheadMinSites &&
       n_ahead > 0) {
     for (int i = 0; i < n_ahead; ++i) {
@@ -760,7 +778,7 @@ attnres_status_t attnres_route_bwd(attnres_bank_t b, int32_t site, const void* e
       ahead_rows.push_back(m);
     }
   }
-  if (extra) {
+  if (extra && !fuse_extra) {
     FinalizeJob j{};
     j.x = extra;
     j.rinv = b->rinvx(site);

@@ -113,11 +113,22 @@ hipError_t launch_fwd(const Geom& g, int dtype, const void* rows, int64_t row_st
                       const void* extra, int n_rows, const float* proj, const float* rinv_rows,
                       const float* rinv_x, float* alpha, float* lse, void* out, hipStream_t st);
 
+// Gradient of a site's transient source, formed by the site pass itself
+// where site_forms_extra_grad(g) (the work-group-wide kernel): dst [T][d]
+// float32, stored (NULL: the finalize forms it); q the site's effective
+// query [r] (float32 if q_f32, else the storage dtype).
+struct ExtraGrad {
+  float* dst;
+  const void* q;
+  int32_t q_f32;
+};
+bool site_forms_extra_grad(const Geom& g);
+
 hipError_t launch_bwd_site(const Geom& g, int dtype, const void* rows, int64_t row_stride,
                            const void* extra, int n_rows, const float* alpha, const float* lse,
                            const float* rinv_rows, const float* rinv_extra, const void* dout,
                            float* dl, float* radial, float* dq_part, int parts,
-                           hipStream_t st);
+                           const ExtraGrad& xg, hipStream_t st);
 
 // dq = sum of the partial rows (fixed order).  With gains (gain, q32 and dg
 // non-NULL) the sum is the gradient of the effective query q * g: then
@@ -245,7 +256,20 @@ hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream
 constexpr size_t kMaxLds = 160 * 1024;
 constexpr size_t kLdsBudget = 64 * 1024;
 size_t lds_fwd(const Geom& g, int n_src);
-size_t lds_bwd_site(const Geom& g, int n_src);
+// with_x: room for the transient source's tile (the site pass forming its gradient)
+size_t lds_bwd_site(const Geom& g, int n_src, bool with_x = false);
+
+// Floats of the work-group-wide site pass's LDS before the transient
+// source's tile (rounded up to 16 bytes): coefficients, partial dots of
+// kSiteRowBatch rows (4 up to 4 chunks per thread, else 2), S, lse and the
+// radial sums of the transient source.
+__host__ __device__ inline size_t site_x_offset(const Geom& g, int n_src) {
+  const size_t pairs = (size_t)g.tt * g.H;
+  const size_t rb = g.cpt <= 4 ? 4 : 2;
+  const size_t part = rb * (((size_t)g.tt * g.cpr) >> ((g.kvc & 3) == 0 ? 2 : 0));
+  const size_t a = 2 * (size_t)n_src * pairs + (size_t)n_src * g.tt + part + 2 * pairs + g.tt;
+  return (a + 3) & ~(size_t)3;
+}
 size_t lds_finalize(const Geom& g, int n_sites);
 size_t lds_score(const Geom& g);
 

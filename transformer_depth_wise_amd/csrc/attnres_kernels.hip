@@ -758,7 +758,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
     int n_rows, const float* __restrict__ alpha, const float* __restrict__ lse_site,
     const float* __restrict__ rinv_rows, const float* __restrict__ rinv_x,
     const T* __restrict__ dout, float* __restrict__ dl_out, float* __restrict__ rad_out,
-    float* __restrict__ dq_part) {
+    float* __restrict__ dq_part, ExtraGrad xg) {
   using V = Vec<T>;
   constexpr int N = V::N;
   constexpr int RB = kSiteRowBatch<CPT>;  // rows per pair of barriers
@@ -780,6 +780,9 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
   float* s_part = s_rinv + n_src * g.tt;     // [RB][tt * cpr >> sh]
   float* s_S = s_part + RB * (plen >> sh);   // [tt][H]
   float* s_lse = s_S + pairs;                // [tt][H]
+  float* s_cx = s_lse + pairs;               // [tt] radial sums of the transient source
+  // [tt * cpr] 16-byte chunks: the transient source's tile, kept for its gradient
+  uint4* s_x = reinterpret_cast<uint4*>(sm + site_x_offset(g, n_src));
   const int tid = threadIdx.x;
 
   Slot sl[CPT];
@@ -840,6 +843,13 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
 #pragma unroll
         for (int j = 0; j < CPT; ++j) cur[r][j] = ok[j] && row ? ld_stream(sp + sl[j].q) : zero4();
       }
+      if (xg.dst != nullptr)
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+          if (n0 + r == n_rows)
+#pragma unroll
+            for (int j = 0; j < CPT; ++j)
+              if (ok[j]) s_x[sl[j].q] = cur[r][j];
       float Pr[RB];  // one-pair tiles: each row's P, the same in every thread
       if (single) {
         // a row's P is one dot over the whole row: each wave sums its part in
@@ -951,6 +961,61 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
         st_stream(dst + h, dl);
       }
       st_stream(rad_out + at, c);
+      if (n == n_rows) s_cx[tau] = c;
+    }
+    if (xg.dst != nullptr) {
+      // The transient source's gradient, formed here rather than by a
+      // finalize launch (it has no later reader): the upstream-gradient chunks
+      // are still in registers and the source's tile was just read.  Same
+      // terms and order as k_finalize with one site: value term, key term,
+      // radial term over the key (or every) coordinate.
+      __syncthreads();  // s_cx
+      const int nx = n_rows;
+      float* dstp = xg.dst + t0 * g.d;
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        if (!ok[j]) continue;
+        // opaque copies: the addresses below are formed here, not hoisted out
+        // of the tile loop into registers held across the row stream
+        int q = sl[j].q, tau = sl[j].tau;
+        asm volatile("" : "+v"(q), "+v"(tau));
+        const float a = s_alpha[nx * pairs + tau * g.H + sl[j].hv];
+        float acc[N], f[N];
+        V::unpack(dov[j], f);
+#pragma unroll
+        for (int e = 0; e < N; ++e) acc[e] = a * f[e];
+        const float ri = s_rinv[nx * g.tt + tau];
+        if (sl[j].key) {
+          const int pk = tau * g.H + sl[j].hk;
+          const float b = ri * (s_alpha[nx * pairs + pk] * (s_P[nx * pairs + pk] - s_S[pk]));
+          float qf[N];
+          if (xg.q_f32) {
+            const float4* qp = reinterpret_cast<const float4*>(static_cast<const float*>(xg.q)) +
+                               sl[j].kc * (N / 4);
+#pragma unroll
+            for (int e = 0; e < N / 4; ++e) {
+              const float4 v = qp[e];
+              qf[4 * e] = v.x, qf[4 * e + 1] = v.y, qf[4 * e + 2] = v.z, qf[4 * e + 3] = v.w;
+            }
+          } else {
+            V::unpack(reinterpret_cast<const uint4*>(static_cast<const T*>(xg.q))[sl[j].kc], qf);
+          }
+#pragma unroll
+          for (int e = 0; e < N; ++e) acc[e] += b * qf[e];
+        }
+        if (sl[j].key || g.rms_full) {
+          const float rc = ri * ri / (float)g.rms_w * s_cx[tau];
+          float xv[N];
+          V::unpack(s_x[q], xv);
+#pragma unroll
+          for (int e = 0; e < N; ++e) acc[e] -= rc * xv[e];
+        }
+        float4* o = reinterpret_cast<float4*>(dstp + (int64_t)q * N);
+#pragma unroll
+        for (int e = 0; e < N / 4; ++e)
+          st_stream(reinterpret_cast<float*>(o + e),
+                    make_float4(acc[4 * e], acc[4 * e + 1], acc[4 * e + 2], acc[4 * e + 3]));
+      }
     }
     __syncthreads();
   }
@@ -985,7 +1050,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site_w(
     int n_rows, const float* __restrict__ alpha, const float* __restrict__ lse_site,
     const float* __restrict__ rinv_rows, const float* __restrict__ rinv_x,
     const T* __restrict__ dout, float* __restrict__ dl_out, float* __restrict__ rad_out,
-    float* __restrict__ dq_part) {
+    float* __restrict__ dq_part, ExtraGrad /* unused: the finalize forms it */) {
   using V = Vec<T>;
   constexpr int N = V::N;
   // sources in flight: three measured faster with up to 4 chunks per thread;
@@ -1892,7 +1957,7 @@ using FwdFn = void (*)(Geom, const T*, int64_t, const T*, int, const float*, con
                        const float*, float*, float*, T*);
 template <typename T>
 using SiteFn = void (*)(Geom, const T*, int64_t, const T*, int, const float*, const float*,
-                        const float*, const float*, const T*, float*, float*, float*);
+                        const float*, const float*, const T*, float*, float*, float*, ExtraGrad);
 template <typename T, typename QT>
 using FinFn = void (*)(Geom, FinalizeArgs, SiteArrays, int, const T*, int64_t, const QT*);
 
@@ -2007,7 +2072,7 @@ size_t lds_score(const Geom& g) {
 }
 constexpr size_t kFwdLdsFloor = 64 * 1024;  // 160 KB per CU / 64 KB = two work-groups
 size_t lds_fwd(const Geom& g, int n_src) { return sizeof(float) * (size_t)n_src * g.tt * g.H; }
-size_t lds_bwd_site(const Geom& g, int n_src) {
+size_t lds_bwd_site(const Geom& g, int n_src, bool with_x) {
   if (g.wave_tokens > 0) {
     const size_t tw = g.wave_tokens, pw = tw * g.H;
     const size_t part = (g.kvc % 4 == 0) ? tw * g.cpr / 4 : tw * g.cpr;
@@ -2015,13 +2080,11 @@ size_t lds_bwd_site(const Geom& g, int n_src) {
     const size_t a = 4 * fw, b = (size_t)g.tt * g.r;
     return sizeof(float) * (a > b ? a : b);
   }
-  const size_t pairs = (size_t)g.tt * g.H;
-  const size_t rb = g.cpt <= 4 ? 4 : 2;  // kSiteRowBatch
-  const size_t part = rb * (((size_t)g.tt * g.cpr) >> ((g.kvc & 3) == 0 ? 2 : 0));
-  const size_t a = 2 * (size_t)n_src * pairs + (size_t)n_src * g.tt + part + 2 * pairs;
+  const size_t a = site_x_offset(g, n_src) + (with_x ? 4 * (size_t)g.tt * g.cpr : 0);
   const size_t b = (size_t)g.tt * g.r;
   return sizeof(float) * (a > b ? a : b);
 }
+
 size_t lds_finalize(const Geom& g, int n_sites) {
   int b = finalize_batch(g);
   if (n_sites < b) b = n_sites < 1 ? 1 : n_sites;
@@ -2204,14 +2267,18 @@ hipError_t launch_fwd(const Geom& g, int dtype, const void* rows, int64_t row_st
   return hipGetLastError();
 }
 
+bool site_forms_extra_grad(const Geom& g) { return g.wave_tokens == 0; }
+
 hipError_t launch_bwd_site(const Geom& g, int dtype, const void* rows, int64_t row_stride,
                            const void* extra, int n_rows, const float* alpha, const float* lse,
                            const float* rinv_rows, const float* rinv_extra, const void* dout,
                            float* dl, float* radial, float* dq_part, int parts,
-                           hipStream_t st) {
+                           const ExtraGrad& xg, hipStream_t st) {
   if (g.T == 0) return hipSuccess;
+  if (xg.dst && !site_forms_extra_grad(g)) return hipErrorInvalidValue;
+  if (xg.dst && (!extra || !xg.q)) return hipErrorInvalidValue;
   const int n_src = n_rows + (extra ? 1 : 0);
-  const size_t lds = lds_bwd_site(g, n_src);
+  const size_t lds = lds_bwd_site(g, n_src, xg.dst != nullptr);
   if (lds > kMaxLds || parts < 1) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)parts);
   if (dtype == 0) {
@@ -2219,13 +2286,13 @@ hipError_t launch_bwd_site(const Geom& g, int dtype, const void* rows, int64_t r
     if (!fn) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(fn, grid, dim3(kThreads), lds, st, g, static_cast<const float*>(rows),
                        row_stride, static_cast<const float*>(extra), n_rows, alpha, lse, rinv_rows,
-                       rinv_extra, static_cast<const float*>(dout), dl, radial, dq_part);
+                       rinv_extra, static_cast<const float*>(dout), dl, radial, dq_part, xg);
   } else {
     auto fn = pick_site<bf16_t>(g.cpt, g.wave_tokens > 0);
     if (!fn) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(fn, grid, dim3(kThreads), lds, st, g, static_cast<const bf16_t*>(rows),
                        row_stride, static_cast<const bf16_t*>(extra), n_rows, alpha, lse, rinv_rows,
-                       rinv_extra, static_cast<const bf16_t*>(dout), dl, radial, dq_part);
+                       rinv_extra, static_cast<const bf16_t*>(dout), dl, radial, dq_part, xg);
   }
   return hipGetLastError();
 }
