@@ -695,10 +695,8 @@ attnres_status_t attnres_route_bwd(attnres_bank_t b, int32_t site, const void* e
   // The transient source is read by this site only: where the site pass can,
   // it forms that source's gradient itself (no finalize job, no second read
   // of the upstream gradient and the source).
-  // (Not for a block partial sum's running gradient: adding into it there
-  // measured slower than the finalize job.)
   const bool fuse_extra =
-      extra && c.tokens > 0 && b->has_extra[site] != 2 &&
+      extra && c.tokens > 0 &&
       attnres::site_forms_extra_grad(b->g_site) &&
       attnres::lds_bwd_site(b->g_site, n_rows + 1, true) <= attnres::kMaxLds;
   {
@@ -712,6 +710,7 @@ attnres_status_t attnres_route_bwd(attnres_bank_t b, int32_t site, const void* e
       xg.q = qs.qf ? static_cast<const void*>(qs.qf + qoff)
                    : static_cast<const void*>(static_cast<const char*>(qs.q) + qoff * b->esz);
       xg.q_f32 = (qs.qf || c.dtype == ATTNRES_F32) ? 1 : 0;
+      xg.accumulate = b->has_extra[site] == 2 ? 1 : 0;
     }
     TraceScope ts(b, ATTNRES_KERNEL_BWD_SITE, st);
     hipError_t e = attnres::launch_bwd_site(

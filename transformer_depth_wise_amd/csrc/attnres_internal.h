@@ -115,12 +115,14 @@ hipError_t launch_fwd(const Geom& g, int dtype, const void* rows, int64_t row_st
 
 // Gradient of a site's transient source, formed by the site pass itself
 // where site_forms_extra_grad(g) (the work-group-wide kernel): dst [T][d]
-// float32, stored (NULL: the finalize forms it); q the site's effective
+// float32 (NULL: the finalize forms it), stored, or with accumulate added
+// into (a block partial sum's running gradient); q the site's effective
 // query [r] (float32 if q_f32, else the storage dtype).
 struct ExtraGrad {
   float* dst;
   const void* q;
   int32_t q_f32;
+  int32_t accumulate;
 };
 bool site_forms_extra_grad(const Geom& g);
 

@@ -1012,9 +1012,14 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
         }
         float4* o = reinterpret_cast<float4*>(dstp + (int64_t)q * N);
 #pragma unroll
-        for (int e = 0; e < N / 4; ++e)
-          st_stream(reinterpret_cast<float*>(o + e),
-                    make_float4(acc[4 * e], acc[4 * e + 1], acc[4 * e + 2], acc[4 * e + 3]));
+        for (int e = 0; e < N / 4; ++e) {
+          float4 v = make_float4(acc[4 * e], acc[4 * e + 1], acc[4 * e + 2], acc[4 * e + 3]);
+          if (xg.accumulate) {  // a block partial sum's running gradient
+            const float4 p = o[e];
+            v.x += p.x, v.y += p.y, v.z += p.z, v.w += p.w;
+          }
+          st_stream(reinterpret_cast<float*>(o + e), v);
+        }
       }
     }
     __syncthreads();
