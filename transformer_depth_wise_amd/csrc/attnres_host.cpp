@@ -53,7 +53,7 @@ constexpr int kFinAheadMinSites = 8;
 
 struct Layout {
   size_t rinv, rinvx, proj, alpha, dl, radial, lse, dqpart, sites;
-  size_t part, part_rad;  // finalize partial sums: [A][T][d] and [A][T], A = min(kFinAhead, max_rows - 1)
+  size_t part, part_rad;  // finalize partial sums: [A][T][d] and [2][A][T], A = min(kFinAhead, max_rows - 1)
   size_t qf, q32, qhi, qlo;  // effective queries with gains ([max_sites, r] each)
   size_t total;
   int64_t slots;     // source slots of proj / alpha / dl / radial
@@ -95,7 +95,7 @@ Layout make_layout(const attnres_config_t& c, int ts) {
   // a look-ahead row lies below a finalized row, so at most max_rows - 1
   const size_t ahead = std::min(kFinAhead, c.max_rows - 1);
   L.part = take(ahead * T * c.d);
-  L.part_rad = take(ahead * T);
+  L.part_rad = take(2 * ahead * T);  // two halves: an extended partial reads one, writes the other
   const size_t sr = (size_t)c.max_sites * c.r;
   L.qf = take(sr);
   L.q32 = take(sr);
@@ -235,8 +235,9 @@ struct attnres_bank_s {
   std::vector<const void*> extra_ptr;
   const void* partial;  // running block partial sum (caller memory), NULL between blocks
   // finalize look-ahead: per bank row, the site from which on a stored partial
-  // sum covers its gradient (-1: none) and that partial's buffer
-  std::vector<int> part_site, part_idx;
+  // sum covers its gradient (-1: none), that partial's buffer and which half
+  // of the radial sums holds it
+  std::vector<int> part_site, part_idx, part_half;
   // launch trace
   struct TraceRec {
     int kind;
@@ -258,7 +259,10 @@ struct attnres_bank_s {
   attnres::SiteSlot* dev_sites() const { return reinterpret_cast<attnres::SiteSlot*>(ws + lay.sites); }
   float* site_lse(int s) const { return f(lay.lse) + (size_t)s * cfg.tokens * cfg.heads; }
   float* part_buf(int i) const { return f(lay.part) + (size_t)i * cfg.tokens * cfg.d; }
-  float* part_rad(int i) const { return f(lay.part_rad) + (size_t)i * cfg.tokens; }
+  float* part_rad(int i, int half) const {
+    const size_t ahead = (size_t)std::min(kFinAhead, cfg.max_rows - 1);
+    return f(lay.part_rad) + ((size_t)half * ahead + i) * cfg.tokens;
+  }
   QuerySet qset() const {
     QuerySet q{queries, nullptr, nullptr, nullptr};
     if (gains) {
@@ -288,6 +292,7 @@ struct attnres_bank_s {
     partial = nullptr;
     part_site.assign(cfg.max_rows, -1);
     part_idx.assign(cfg.max_rows, 0);
+    part_half.assign(cfg.max_rows, 0);
   }
 };
 
@@ -748,7 +753,7 @@ attnres_status_t attnres_route_bwd(attnres_bank_t b, int32_t site, const void* e
     if (b->part_site[n] >= 0) {
       j.s1 = b->part_site[n];
       j.in = b->part_buf(b->part_idx[n]);
-      j.in_rad = b->part_rad(b->part_idx[n]);
+      j.in_rad = b->part_rad(b->part_idx[n], b->part_half[n]);
       consumed.push_back(n);
       any_partial = true;
     }
@@ -768,7 +773,7 @@ attnres_status_t attnres_route_bwd(attnres_bank_t b, int32_t site, const void* e
       j.x = b->row_ptr(m);
       j.rinv = b->rinv(m);
       j.dst = b->part_buf(i);
-      j.dst_rad = b->part_rad(i);
+      j.dst_rad = b->part_rad(i, 0);
       j.slot = m;
       j.s0 = site;
       j.s1 = b->n_sites;
@@ -776,6 +781,37 @@ attnres_status_t attnres_route_bwd(attnres_bank_t b, int32_t site, const void* e
       jobs.push_back(j);
       ahead_rows.push_back(m);
     }
+  }
+  // Extension of stored partials: when this call's rows sum a long site range
+  // [site, s1) that ends where rows below have a partial, the same launch adds
+  // those sites to those partials (in place; the radial sums go to the other
+  // half), so each of these rows later sums only its own range.  Worth it
+  // over at least kFinAheadMinSites sites: an extension reads and writes a
+  // float32 row, a site range not read again saves a storage row per site.
+  std::vector<int> extended;
+  if (any_partial && c.tokens > 0 && !jobs.empty()) {
+    const int s1 = jobs[0].s1;
+    bool same = true;
+    for (const FinalizeJob& j : jobs) same = same && j.s1 == s1 && j.in != nullptr;
+    const int room = attnres::kMaxJobs - (int)jobs.size() - (extra && !fuse_extra ? 1 : 0);
+    if (same && s1 - site >= kFinAheadMinSites)
+      for (int k = lo - 1; k >= 0 && (int)extended.size() < room; --k) {
+        if (b->part_site[k] != s1) continue;
+        const int i = b->part_idx[k], h = b->part_half[k];
+        FinalizeJob j{};
+        j.x = b->row_ptr(k);
+        j.rinv = b->rinv(k);
+        j.dst = b->part_buf(i);
+        j.in = b->part_buf(i);
+        j.in_rad = b->part_rad(i, h);
+        j.dst_rad = b->part_rad(i, 1 - h);
+        j.slot = k;
+        j.s0 = site;
+        j.s1 = s1;
+        j.partial_out = 1;
+        jobs.push_back(j);
+        extended.push_back(k);
+      }
   }
   if (extra && !fuse_extra) {
     FinalizeJob j{};
@@ -809,6 +845,11 @@ attnres_status_t attnres_route_bwd(attnres_bank_t b, int32_t site, const void* e
   for (size_t i = 0; i < ahead_rows.size(); ++i) {
     b->part_site[ahead_rows[i]] = site;
     b->part_idx[ahead_rows[i]] = (int)i;
+    b->part_half[ahead_rows[i]] = 0;
+  }
+  for (int k : extended) {
+    b->part_site[k] = site;
+    b->part_half[k] ^= 1;
   }
   b->bwd_next = site - 1;
   if (site == 0) b->bwd_done = true;
