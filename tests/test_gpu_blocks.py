@@ -26,6 +26,12 @@ pytestmark = pytest.mark.gpu
 CASES = [
     BlockShape("lr_tiny_f32", 37, 64, 32, 2, 6, 3, dtype="f32", qscale=0.5),
     BlockShape("bf16_d256_full", 50, 256, 64, 4, 7, 3, norm="full", qscale=0.3),
+    # rows of 192 chunks take the work-group-wide site pass, which forms the
+    # partial sum's gradient itself (added into the running gradient): fp32
+    # and bf16, keys narrower than the row (value-only coordinates), both RMS
+    # widths, ragged token counts
+    BlockShape("f32_d768_wide", 29, 768, 384, 2, 6, 3, dtype="f32", norm="full", qscale=0.5),
+    BlockShape("bf16_d1536_wide", 37, 1536, 768, 4, 8, 4, qscale=0.3),
     # the low-rank block shape: d=7168, r=1792, H=8, 18 sublayers in 9 blocks
     BlockShape("lr_h8_blocks", 9, 7168, 1792, 8, 18, 9),
     # Kimi K3-shaped: 186 reads over 8 blocks, full-width keys, one head
