@@ -65,12 +65,28 @@ COUNTER_RUN_STEPS = 1
 
 # ---------------------------------------------------------------------------
 # Algorithmic bytes per kernel launch (what each kernel must move in HBM).
+def site_pass_is_wave_owned(w) -> bool:
+    """Whether the bank runs the wave-owned site pass for this shape (the
+    library's rule: some 2, 4 or 5 chunks per lane cover whole tokens, with at
+    most 64 (token, head) pairs per wave).  Otherwise the work-group-wide site
+    pass runs, and it forms each transient source's gradient itself."""
+    cpr = w.d // (8 if w.elem_bytes == 2 else 4)
+    for cpt in (4, 5, 2):
+        if (64 * cpt) % cpr:
+            continue
+        tw = 64 * cpt // cpr
+        if tw >= 1 and tw * w.heads <= 64:
+            return True
+    return False
+
+
 def kernel_bytes(w, parts: int):
     """Total algorithmic bytes per kernel kind over one microbatch: every source
     row a site reads once per pass, the saved coefficients, the outputs and the
     gradients, per launch."""
     b, T, d, r, H, S = w.elem_bytes, w.tokens, w.d, w.r, w.heads, w.sites
     nsrc, extra = list(w.nsrc), list(w.extra)
+    fused = not site_pass_is_wave_owned(w)  # transient gradients formed by the site pass
     out = {"score": 0, "fwd": 0, "bwd_site": 0, "dq_reduce": 0, "finalize": 0}
     launches = {k: 0 for k in out}
     rw = d if w.norm == "full" else r  # coordinates the append reads
@@ -92,11 +108,13 @@ def kernel_bytes(w, parts: int):
         launches["fwd"] += 1
         launches["bwd_site"] += 1
         launches["dq_reduce"] += 1
+        if extra[s] and fused:  # the transient source's gradient out, the site's query in
+            out["bwd_site"] += 4 * T * d + r * b
         lo = nsrc[s - 1] if s > 0 else 0
-        jobs = [S - s] * (nsrc[s] - lo) + ([1] if extra[s] else [])
+        jobs = [S - s] * (nsrc[s] - lo) + ([1] if extra[s] and not fused else [])
         for ns in jobs:  # one source gathered from ns sites: dout, alpha, dl, radial; key, rinv; grad
             out["finalize"] += ns * T * d * b + 8 * ns * T * H + 4 * ns * T + T * r * b + 4 * T + 4 * T * d
-        launches["finalize"] += 1
+        launches["finalize"] += 1 if jobs else 0
     return out, launches
 
 

@@ -179,3 +179,23 @@ def test_cpu_baseline_chunks_cover_every_token_once():
     seen.clear()
     bench.oracle_baseline(prepare, 64, "ms/read", "toy")
     assert seen[0] == (16, 0, 16)
+
+
+def test_transient_gradient_bytes_follow_the_site_pass(monkeypatch):
+    """The work-group-wide site pass (rows no wave covers in whole tokens)
+    forms each transient source's gradient: its bytes move from the finalize
+    to the site pass, and a site that finalizes nothing launches nothing."""
+    assert bench.site_pass_is_wave_owned(get_workload("mhar1b"))
+    assert not bench.site_pass_is_wave_owned(get_workload("k3"))
+    assert not bench.site_pass_is_wave_owned(get_workload("lr_h8"))
+    w = get_workload("k3")
+    T, d, r, H, b = w.tokens, w.d, w.r, w.heads, w.elem_bytes
+    fused, fl = bench.kernel_bytes(w, parts=512)
+    monkeypatch.setattr(bench, "site_pass_is_wave_owned", lambda w: True)
+    apart, al = bench.kernel_bytes(w, parts=512)
+    n = sum(w.extra)
+    assert fused["bwd_site"] - apart["bwd_site"] == n * (4 * T * d + r * b)
+    job = T * d * b + 8 * T * H + 4 * T + T * r * b + 4 * T + 4 * T * d  # one site's gather
+    assert apart["finalize"] - fused["finalize"] == n * job
+    rows_final = sum(1 for s in range(w.sites) if w.nsrc[s] > (w.nsrc[s - 1] if s else 0))
+    assert fl["finalize"] == rows_final and al["finalize"] == w.sites

@@ -836,11 +836,13 @@ attnres_status_t attnres_route_bwd(attnres_bank_t b, int32_t site, const void* e
   sa.slot_rad = b->lay.slot_rad;
   sa.ts = b->lay.ts;
   sa.th_stride = c.tokens * (int64_t)c.heads;
-  TraceScope tf(b, ATTNRES_KERNEL_FINALIZE, st);
-  hipError_t e = attnres::launch_finalize(b->g_fin, c.dtype, jobs.data(), (int)jobs.size(), sa,
-                                          b->dout_rows, row_stride, b->qset(), st);
-  tf.done();
-  if (e != hipSuccess) return hip_fail(e, "route_bwd finalize kernel");
+  if (!jobs.empty()) {  // (a call whose site finalizes nothing launches nothing)
+    TraceScope tf(b, ATTNRES_KERNEL_FINALIZE, st);
+    hipError_t e = attnres::launch_finalize(b->g_fin, c.dtype, jobs.data(), (int)jobs.size(), sa,
+                                            b->dout_rows, row_stride, b->qset(), st);
+    tf.done();
+    if (e != hipSuccess) return hip_fail(e, "route_bwd finalize kernel");
+  }
   for (int n : consumed) b->part_site[n] = -1;
   for (size_t i = 0; i < ahead_rows.size(); ++i) {
     b->part_site[ahead_rows[i]] = site;
