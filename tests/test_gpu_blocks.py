@@ -32,6 +32,11 @@ CASES = [
     # widths, ragged token counts
     BlockShape("f32_d768_wide", 29, 768, 384, 2, 6, 3, dtype="f32", norm="full", qscale=0.5),
     BlockShape("bf16_d1536_wide", 37, 1536, 768, 4, 8, 4, qscale=0.3),
+    # 40 reads in blocks of 8: rows first read 8 sites apart, so after the
+    # first look-ahead every finalized row's range extends the stored
+    # partials of the rows below (row finalize on both site-pass variants)
+    BlockShape("ext_bf16_d256", 21, 256, 64, 4, 40, 5, qscale=0.5),
+    BlockShape("ext_f32_d768", 13, 768, 768, 1, 40, 5, dtype="f32", qscale=0.5),
     # the low-rank block shape: d=7168, r=1792, H=8, 18 sublayers in 9 blocks
     BlockShape("lr_h8_blocks", 9, 7168, 1792, 8, 18, 9),
     # Kimi K3-shaped: 186 reads over 8 blocks, full-width keys, one head

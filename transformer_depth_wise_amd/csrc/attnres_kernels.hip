@@ -761,7 +761,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
     float* __restrict__ dq_part, ExtraGrad xg) {
   using V = Vec<T>;
   constexpr int N = V::N;
-  constexpr int RB = kSiteRowBatch<CPT>;  // rows per pair of barriers
+  constexpr int RB = kSiteRowBatch<CPT> / 2;  // rows per pair of barriers (two sets)
   constexpr int kWaves = kThreads / 64;
   extern __shared__ float sm[];
   const int n_src = n_rows + (extra != nullptr ? 1 : 0);
@@ -833,23 +833,33 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
 
     // RB rows per step: every row's head dots need the whole work-group, so
     // the rows of a batch share one pair of barriers (a token row spans
-    // several waves when rows are wide)
-    for (int n0 = 0; n0 < n_src; n0 += RB) {
-      uint4 cur[RB][CPT];
+    // several waves when rows are wide).  Two register sets of RB rows: the
+    // next batch is requested before the current one is reduced.
+    uint4 cur[2][RB][CPT];
+    auto load_rows = [&](int n0, uint4 (&cb)[RB][CPT]) {
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
         const bool row = n0 + r < n_src;  // the last batch may be short
         const uint4* sp = tile_of(row ? n0 + r : n0, t0);
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) cur[r][j] = ok[j] && row ? ld_stream(sp + sl[j].q) : zero4();
+        for (int j = 0; j < CPT; ++j) cb[r][j] = ok[j] && row ? ld_stream(sp + sl[j].q) : zero4();
       }
+    };
+    load_rows(0, cur[0]);
+    for (int n2 = 0; n2 < n_src; n2 += 2 * RB) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+      const int n0 = n2 + hb * RB;
+      if (n0 >= n_src) break;
+      if (n0 + RB < n_src) load_rows(n0 + RB, cur[hb ^ 1]);
+      uint4 (&cb)[RB][CPT] = cur[hb];
       if (xg.dst != nullptr)
 #pragma unroll
         for (int r = 0; r < RB; ++r)
           if (n0 + r == n_rows)
 #pragma unroll
             for (int j = 0; j < CPT; ++j)
-              if (ok[j]) s_x[sl[j].q] = cur[r][j];
+              if (ok[j]) s_x[sl[j].q] = cb[r][j];
       float Pr[RB];  // one-pair tiles: each row's P, the same in every thread
       if (single) {
         // a row's P is one dot over the whole row: each wave sums its part in
@@ -860,7 +870,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
         for (int r = 0; r < RB; ++r) {
           float part = 0.f;
 #pragma unroll
-          for (int j = 0; j < CPT; ++j) part += Vec<T>::dot(dov[j], cur[r][j]);
+          for (int j = 0; j < CPT; ++j) part += Vec<T>::dot(dov[j], cb[r][j]);
           Pr[r] = wave_sum(part);
         }
         if ((tid & 63) == 0)
@@ -880,7 +890,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
         for (int r = 0; r < RB; ++r) {
 #pragma unroll
           for (int j = 0; j < CPT; ++j) {
-            float part = Vec<T>::dot(dov[j], cur[r][j]);
+            float part = Vec<T>::dot(dov[j], cb[r][j]);
             if (sh) part = quad_sum(part);
             if (sl[j].own && (sl[j].q & ((1 << sh) - 1)) == 0)
               s_part[((r * plen) >> sh) + (sl[j].q >> sh)] = part;
@@ -920,7 +930,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
           const float cw = s_alpha[n * pairs + pi] * s_rinv[n * g.tt + sl[j].tau];
           const float cu = cw * (single ? Pr[r] : s_P[n * pairs + pi]);
           float xv[N];
-          V::unpack(cur[r][j], xv);
+          V::unpack(cb[r][j], xv);
 #pragma unroll
           for (int e = 0; e < N; ++e) {
             W[j][e] += cw * xv[e];
@@ -928,6 +938,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_site(
           }
         }
       }
+          }
     }
     for (int p = tid; p < pairs; p += kThreads) {
       float S = 0.f, A = 0.f;
