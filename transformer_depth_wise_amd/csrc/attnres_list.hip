@@ -63,9 +63,9 @@ template <typename T, int VW>
 struct ListTile {
   static constexpr int G = 5;
   static constexpr int UK = VW == 1 ? 4 : 2;  // forward key pass
-  static constexpr int UM = VW == 1 ? 8 : 2;  // forward mix
+  static constexpr int UM = VW == 1 ? 6 : 2;  // forward mix
   static constexpr int UP = VW == 1 ? 4 : 2;  // backward P pass
-  static constexpr int UG = VW == 1 ? 4 : 2;  // backward gradient pass
+  static constexpr int UG = VW == 1 ? 3 : 2;  // backward gradient pass
 };
 
 // VW consecutive elements of one lane: VW = 1 (any alignment), or one 16-byte
