@@ -709,11 +709,9 @@ __global__ __launch_bounds__(kDThreads) void k_delta_bwd_s(DeltaGeom g, DeltaArg
       w_alpha[i] = valid ? alpha[((int64_t)k * g.T + t) * g.H + h0 + h] : 0.f;
     }
     float S_acc = 0.f, A_acc = 0.f;
-    // rows are loaded one source at a time here: a second buffer would cost
-    // more in occupancy than it gains in loads in flight
-    for (int k = 0; k < n; ++k) {
-      uint4 x[CPT];
-      load_row(k, x);
+    // rows two at a time: the next source's row is requested before the
+    // current one is reduced
+    auto source = [&](int k, const uint4 (&x)[CPT]) {
       float wss = 0.f;
 #pragma unroll
       for (int j = 0; j < CPT; ++j) {
@@ -746,6 +744,16 @@ __global__ __launch_bounds__(kDThreads) void k_delta_bwd_s(DeltaGeom g, DeltaArg
         A_acc += w_alpha[k * hw + lane];
       }
       wave_lds_fence();
+    };
+    uint4 xa[CPT], xb[CPT];
+    load_row(0, xa);
+    for (int k = 0; k < n; k += 2) {
+      if (k + 1 < n) load_row(k + 1, xb);
+      source(k, xa);
+      if (k + 1 < n) {
+        if (k + 2 < n) load_row(k + 2, xa);
+        source(k + 1, xb);
+      }
     }
     __syncthreads();  // both halves' sums of squares are in s_x
     if (lane < hw) w_S[lane] = A_acc > 0.f ? S_acc / A_acc : 0.f;  // as in k_delta_bwd
