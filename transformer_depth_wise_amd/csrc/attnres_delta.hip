@@ -782,9 +782,7 @@ __global__ __launch_bounds__(kDThreads) void k_delta_bwd_s(DeltaGeom g, DeltaArg
       if (lane < hw) null_dl += w_dl[lane];
       if (lane == 0 && half == 0) null_c += w_c[0];
     }
-    for (int k = 0; k < n; ++k) {
-      uint4 x[CPT];
-      load_row(k, x);
+    auto grad = [&](int k, const uint4 (&x)[CPT]) {
       const bool is_null = has_null && k == 0;
       GT* dst = is_null ? nullptr : static_cast<GT*>(dg.d[k - (has_null ? 1 : 0)]);
       const float ri = w_rinv[k];
@@ -807,6 +805,24 @@ __global__ __launch_bounds__(kDThreads) void k_delta_bwd_s(DeltaGeom g, DeltaArg
 #pragma unroll
         for (int e = 0; e < N; ++e) gr[e] = al * df[e] + cq * qf[e] - rc * xf[e];
         st_grad<GT, N>(dst + t * g.d + (int64_t)c * N, gr);
+      }
+    };
+    if constexpr (sizeof(GT) == 2) {
+      // bf16 gradients: the two-row rotation of the first pass fits the
+      // registers here too (with float32 gradients it would not)
+      load_row(0, xa);
+      for (int k = 0; k < n; k += 2) {
+        if (k + 1 < n) load_row(k + 1, xb);
+        grad(k, xa);
+        if (k + 1 < n) {
+          if (k + 2 < n) load_row(k + 2, xa);
+          grad(k + 1, xb);
+        }
+      }
+    } else {
+      for (int k = 0; k < n; ++k) {
+        load_row(k, xa);
+        grad(k, xa);
       }
     }
     __syncthreads();  // the next tile reuses s_x and the wave regions
